@@ -1,0 +1,291 @@
+"""Pins for the CPU oracle: each check fixes it against something other than itself.
+
+Brute force on tiny shapes (pure Python, math.fsum), hand-worked values (tests/golden),
+closed forms of RMSNorm, invariants named by the method (unit RMS, scale invariance, padded
+rows untouched, chunked == unchunked) and a library routine (torch rms_norm in float64,
+torch's bf16 cast).  Shapes are non-square so that a transposed operand or a mean over the
+wrong axis fails.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def _bits(a):
+    return synth.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def _brute(x, W, r, w, eps, kind, conventional=False):
+    """Pure-Python loops over the definition, with exactly rounded sums."""
+    T, K = len(x), len(x[0])
+    H = len(W)
+    r_new = [[0.0] * H for _ in range(T)]
+    out = [[0.0] * H for _ in range(T)]
+    for t in range(T):
+        for h in range(H):
+            y = math.fsum(x[t][k] * W[h][k] for k in range(K))
+            if conventional:
+                y = float(torch.tensor(y, dtype=torch.float64).to(torch.float32)
+                          .to(torch.bfloat16).to(torch.float64))
+            r_new[t][h] = r[t][h] + y
+        ms = math.fsum(v * v for v in r_new[t]) / H
+        inv = 1.0 / math.sqrt(ms + eps)
+        for h in range(H):
+            g = w[h] if kind == 0 else 1.0 + w[h]
+            out[t][h] = r_new[t][h] * inv * g
+    return np.array(r_new), np.array(out)
+
+
+# ----------------------------------------------------------------------------------- golden
+def test_golden_exact_case():
+    case = json.load(open(GOLDEN))["cases"][0]
+    x, W = _bits(case["x"]), _bits(case["W"])
+    r = np.array(case["residual"], dtype=np.float32)
+    for kind, key in ((oracle.NORM_STANDARD, "norm_w_standard"),
+                      (oracle.NORM_GEMMA, "norm_w_gemma")):
+        w = np.array(case[key], dtype=np.float32)
+        for mode in ("fused", "conventional"):
+            r_new, out = oracle.proj_add_rmsnorm(x, W, r, w, case["eps"], kind, mode)
+            np.testing.assert_array_equal(r_new, np.array(case["residual_out"]))
+            np.testing.assert_allclose(out, np.array(case["out"]), rtol=0, atol=1e-15)
+
+
+def test_golden_conventional_rounding():
+    case = json.load(open(GOLDEN))["cases"][1]
+    x, W = _bits(case["x"]), _bits(case["W"])
+    r = np.array(case["residual"], dtype=np.float32)
+    w = np.ones(2, dtype=np.float32)
+    rf, _ = oracle.proj_add_rmsnorm(x, W, r, w, 1e-5, 0, "fused")
+    rc, _ = oracle.proj_add_rmsnorm(x, W, r, w, 1e-5, 0, "conventional")
+    np.testing.assert_array_equal(rf, np.array(case["residual_out_fused"]))
+    np.testing.assert_array_equal(rc, np.array(case["residual_out_conventional"]))
+
+
+def test_golden_bf16_rne_table():
+    table = json.load(open(GOLDEN))["bf16_rne"]["values"]
+    vals = np.array([v for v, _ in table], dtype=np.float64)
+    want = np.array([int(b, 16) for _, b in table], dtype=np.uint16)
+    got = oracle.bf16_bits_of(oracle.round_bf16(vals))
+    np.testing.assert_array_equal(got, want)
+    # widening the expected patterns gives back exactly the rounded values
+    np.testing.assert_array_equal(oracle.widen_bf16(want), oracle.round_bf16(vals))
+
+
+def test_round_bf16_matches_torch_cast():
+    """torch's fp32 -> bf16 cast is round-to-nearest-even; on fp32-exact inputs it must agree."""
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        rng.standard_normal(2000) * 1e-39,  # fp32 / bf16 subnormals
+                        [0.0, -0.0, 1.0, 3.0, 1e38, -3.3e38]]).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_bf16(v.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_widen_bf16_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F80, 0x3EAB, 0x4049], dtype=np.uint16)
+    want = [1.0, -2.0, 0.0, -0.0, np.inf, 0.333984375, 3.140625]
+    np.testing.assert_array_equal(oracle.widen_bf16(bits), want)
+
+
+# ----------------------------------------------------------------------------- brute force
+@pytest.mark.parametrize("T,K,H,kind,mode", [
+    (3, 5, 7, 0, "fused"), (4, 8, 3, 1, "fused"), (2, 6, 9, 0, "conventional"),
+    (5, 3, 4, 1, "conventional"), (1, 16, 16, 0, "fused")])
+def test_brute_force_tiny(T, K, H, kind, mode):
+    rng = np.random.default_rng(T * 100 + K * 10 + H)
+    x = _bits(rng.standard_normal((T, K)))
+    W = _bits(rng.standard_normal((H, K)) / np.sqrt(K))
+    r = rng.standard_normal((T, H)).astype(np.float32)
+    w = (rng.standard_normal(H) * 0.1 + (1.0 if kind == 0 else 0.0)).astype(np.float32)
+    eps = float(np.float32(1e-5))
+    r_ref, out_ref = oracle.proj_add_rmsnorm(x, W, r, w, eps, kind, mode)
+    xf = oracle.widen_bf16(x).tolist()
+    Wf = oracle.widen_bf16(W).tolist()
+    r_b, out_b = _brute(xf, Wf, r.astype(np.float64).tolist(), w.astype(np.float64).tolist(),
+                        eps, kind, conventional=(mode == "conventional"))
+    np.testing.assert_allclose(r_ref, r_b, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(out_ref, out_b, rtol=1e-12, atol=1e-13)
+
+
+def test_integer_projection_exact():
+    d = synth.integer_inputs(7, 24, 11, seed=5)
+    y = oracle.projection(oracle.widen_bf16(d["x"]), oracle.widen_bf16(d["W"]))
+    xi = oracle.widen_bf16(d["x"]).astype(np.int64)
+    Wi = oracle.widen_bf16(d["W"]).astype(np.int64)
+    want = np.array([[sum(int(xi[t, k]) * int(Wi[h, k]) for k in range(24)) for h in range(11)]
+                     for t in range(7)])
+    np.testing.assert_array_equal(y, want)
+
+
+def test_one_hot_row_selects_weight_column():
+    K, H = 6, 5
+    rng = np.random.default_rng(1)
+    W = oracle.widen_bf16(_bits(rng.standard_normal((H, K))))
+    for j in range(K):
+        x = np.zeros((1, K))
+        x[0, j] = 1.0
+        np.testing.assert_array_equal(oracle.projection(x, W)[0], W[:, j])
+
+
+# ---------------------------------------------------------------------------- RMSNorm forms
+def test_zero_weight_leaves_residual_and_normalises_it():
+    rng = np.random.default_rng(2)
+    T, K, H = 4, 8, 12
+    x = _bits(rng.standard_normal((T, K)))
+    W = np.zeros((H, K), dtype=np.uint16)
+    r = rng.standard_normal((T, H)).astype(np.float32)
+    w = np.ones(H, dtype=np.float32)
+    r_new, out = oracle.proj_add_rmsnorm(x, W, r, w, 0.0, 0)
+    np.testing.assert_array_equal(r_new, r.astype(np.float64))
+    rms = np.sqrt(np.mean(r.astype(np.float64) ** 2, axis=1, keepdims=True))
+    np.testing.assert_allclose(out, r / rms, rtol=1e-14)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 1e-2, 3.0])
+def test_unit_rms_closed_form(eps):
+    rng = np.random.default_rng(4)
+    rp = rng.standard_normal((6, 40)) * rng.uniform(0.1, 5, (6, 1))
+    out = oracle.rms_norm(rp, np.ones(40), eps)
+    ms = np.mean(rp ** 2, axis=1)
+    got = np.sqrt(np.mean(out ** 2, axis=1))
+    np.testing.assert_allclose(got, np.sqrt(ms / (ms + eps)), rtol=1e-14)
+
+
+def test_scale_invariance_up_to_eps():
+    rng = np.random.default_rng(5)
+    rp = rng.standard_normal((5, 32))
+    g = 1 + 0.1 * rng.standard_normal(32)
+    for alpha in (0.5, 3.0, 1000.0):
+        np.testing.assert_allclose(oracle.rms_norm(alpha * rp, g, 0.0), oracle.rms_norm(rp, g, 0.0),
+                                   rtol=1e-13, atol=1e-15)
+        eps = 1e-4
+        diff = np.abs(oracle.rms_norm(alpha * rp, g, eps) - oracle.rms_norm(rp, g, eps))
+        ms = np.mean(rp ** 2, axis=1, keepdims=True)
+        bound = eps / (2 * ms) * abs(1 - 1 / alpha ** 2) * np.abs(oracle.rms_norm(rp, g, 0.0))
+        assert np.all(diff <= 1.01 * bound + 1e-15)
+
+
+def test_constant_and_one_hot_rows():
+    H = 16
+    g = np.linspace(0.5, 1.5, H)
+    for c in (-3.0, 0.25, 7.0):
+        out = oracle.rms_norm(np.full((1, H), c), g, 1e-3)
+        np.testing.assert_allclose(out[0], c / math.sqrt(c * c + 1e-3) * g, rtol=1e-14)
+    for j, v in ((0, 2.0), (7, -5.0), (15, 0.5)):
+        rp = np.zeros((1, H))
+        rp[0, j] = v
+        out = oracle.rms_norm(rp, g, 1e-2)
+        want = np.zeros(H)
+        want[j] = v / math.sqrt(v * v / H + 1e-2) * g[j]
+        np.testing.assert_allclose(out[0], want, rtol=1e-14, atol=0)
+
+
+def test_matches_torch_rms_norm_float64():
+    rng = np.random.default_rng(6)
+    rp = rng.standard_normal((9, 48)) * 3
+    w = rng.standard_normal(48)
+    for eps in (1e-6, 1e-2):
+        want = torch.nn.functional.rms_norm(torch.from_numpy(rp), (48,), torch.from_numpy(w),
+                                            eps=eps).numpy()
+        np.testing.assert_allclose(oracle.rms_norm(rp, w, eps), want, rtol=1e-13, atol=1e-15)
+
+
+def test_gemma_is_standard_with_one_plus_w():
+    rng = np.random.default_rng(7)
+    T, K, H = 3, 16, 10
+    x = _bits(rng.standard_normal((T, K)))
+    W = _bits(rng.standard_normal((H, K)))
+    r = rng.standard_normal((T, H)).astype(np.float32)
+    # offsets on a 2^-10 grid, so that 1 + w is exact in fp32 as well
+    w = (np.round(0.1 * rng.standard_normal(H) * 1024) / 1024).astype(np.float32)
+    _, out_g = oracle.proj_add_rmsnorm(x, W, r, w, 1e-6, oracle.NORM_GEMMA)
+    _, out_s = oracle.proj_add_rmsnorm(x, W, r, (1.0 + w.astype(np.float64)), 1e-6,
+                                       oracle.NORM_STANDARD)
+    np.testing.assert_allclose(out_g, out_s, rtol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.norm_gain(w, 2)
+
+
+# -------------------------------------------------------------------------- microchunking
+@pytest.mark.parametrize("T,mc", [(10, 3), (10, 5), (10, 10), (10, 16), (1, 4), (17, 8)])
+@pytest.mark.parametrize("mode", ["fused", "conventional"])
+def test_chunked_equals_unchunked_and_padding_is_inert(T, mc, mode):
+    rng = np.random.default_rng(T * 31 + mc)
+    K, H = 12, 20
+    x = _bits(rng.standard_normal((T, K)))
+    W = _bits(rng.standard_normal((H, K)) / np.sqrt(K))
+    r = rng.standard_normal((T, H)).astype(np.float32)
+    w = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    r_u, out_u = oracle.proj_add_rmsnorm(x, W, r, w, 1e-5, 0, mode)
+    for pad in (np.nan, 1e30, 0.0):
+        r_c, out_c = oracle.proj_add_rmsnorm_chunked(x, W, r, w, 1e-5, 0, mc, mode, pad_value=pad)
+        np.testing.assert_array_equal(r_c, r_u)
+        np.testing.assert_array_equal(out_c, out_u)
+
+
+def test_chunked_empty():
+    r_c, out_c = oracle.proj_add_rmsnorm_chunked(np.zeros((0, 8), np.uint16),
+                                                 np.zeros((4, 8), np.uint16),
+                                                 np.zeros((0, 4), np.float32),
+                                                 np.ones(4, np.float32), 1e-5, 0, 4)
+    assert r_c.shape == (0, 4) and out_c.shape == (0, 4)
+
+
+def test_padded_k_columns_are_inert():
+    """Zero columns appended to x and W (the 64-element padding of an intermediate size)."""
+    rng = np.random.default_rng(8)
+    T, Kr, K, H = 4, 10, 64, 6
+    xr = rng.standard_normal((T, Kr))
+    Wr = rng.standard_normal((H, Kr))
+    x = np.zeros((T, K), np.uint16)
+    W = np.zeros((H, K), np.uint16)
+    x[:, :Kr] = _bits(xr)
+    W[:, :Kr] = _bits(Wr)
+    r = rng.standard_normal((T, H)).astype(np.float32)
+    w = (0.1 * rng.standard_normal(H)).astype(np.float32)
+    a = oracle.proj_add_rmsnorm(x, W, r, w, 1e-6, 1)
+    b = oracle.proj_add_rmsnorm(x[:, :Kr], W[:, :Kr], r, w, 1e-6, 1)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------------------ comparison
+def test_compare_accepts_own_rounding_and_rejects_planted_errors():
+    d = synth.make_custom(32, 64, 128, seed=9)
+    r_ref, out_ref = oracle.proj_add_rmsnorm(d["x"], d["W"], d["residual"], d["norm_w"], d["eps"])
+    out_bits = oracle.bf16_bits_of(oracle.round_bf16(out_ref))
+    r32 = r_ref.astype(np.float32)
+    assert oracle.within_tolerance(oracle.compare(r32, out_bits, r_ref, out_ref))
+    bad = out_bits.copy()
+    bad[3, 5] ^= 0x4000          # flip an exponent bit in one output element
+    assert not oracle.within_tolerance(oracle.compare(r32, bad, r_ref, out_ref))
+    r_bad = r32.copy()
+    r_bad[:, 7] += 1.0           # one column's residual off by one
+    assert not oracle.within_tolerance(oracle.compare(r_bad, out_bits, r_ref, out_ref))
+    # a transposed / misread projection: residual without y added
+    r_noy = d["residual"].astype(np.float32)
+    assert not oracle.within_tolerance(oracle.compare(r_noy, out_bits, r_ref, out_ref))
+
+
+def test_workload_inputs_statistics():
+    """The recipes produce the stated distributions (W variance 1/K, silu*mul second moment)."""
+    d = synth.make_inputs(synth.WORKLOADS["tiny"], seed=0)
+    W = oracle.widen_bf16(d["W"])
+    assert abs(W.var() * d["K"] - 1.0) < 0.02
+    assert d["x"].shape == (64, 512) and d["residual"].dtype == np.float32
+    g = synth.make_inputs(synth.WORKLOADS["gemma"], seed=0, T=8)
+    assert np.all(g["x"][:, 16360:] == 0) and np.all(g["W"][:, 16360:] == 0)
+    assert abs(float(np.mean(g["norm_w"]))) < 0.02     # Gemma offset weight centred on 0
+    dp = synth.make_inputs(synth.WORKLOADS["down_proj"], seed=0, T=64)
+    x = oracle.widen_bf16(dp["x"])
+    assert 0.3 < float(np.mean(x * x)) < 0.42          # E[(silu(a) b)^2] ~ 0.356
