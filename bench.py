@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused projection -> residual add -> RMSNorm call on one MI355X.
+
+A step is one proj_add_rmsnorm call over one batch of T tokens of a workload (all steps of
+the path: the projection of every microchunk, the slot hand-off between the two streams, the
+residual add and the RMSNorm), with inputs already resident in HBM.  The default workload is
+the Llama-3-8B-shaped o_proj prefill (T=2048, K=H=4096, bf16, standard RMSNorm), the pipeline
+run at each of its chunk sizes {256, 512}; the best one is the headline.  The conventional
+path is timed beside it.  Prints one JSON line.
+
+    python bench.py [--steps 50] [--warmup 10] [--workload o_proj] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="o_proj")
+    ap.add_argument("--microchunk", type=int, default=0, help="0: every chunk size of the workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def time_steps(call, steps: int, warmup: int, torch):
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(d, seconds: float) -> dict:
+    """The oracle, as it stands, on a bounded sample of the workload's tokens."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rows = min(d["T"], 256)
+    x, r = d["x"][:rows], d["residual"][:rows]
+    reps, t_total = 0, 0.0
+    while t_total < seconds and reps < 1000:
+        t0 = time.perf_counter()
+        oracle.proj_add_rmsnorm(x, d["W"], r, d["norm_w"], d["eps"], d["norm_kind"], "fused")
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": rows * reps / t_total, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {rows} of {d['T']} tokens, {reps} calls of the float64 oracle "
+                      f"({t_total:.1f} s); rows are independent, so tokens/s scales to the "
+                      f"full batch"}
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "inter-GPU step in this build", file=sys.stderr)
+        return 2
+    import torch
+    import projection_residual_rmsnorm_amd as pr
+    import synth
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    wl = synth.WORKLOADS[args.workload]
+    T, K, H = wl.T, wl.K, wl.H
+    log(f"workload {wl.name}: T={T} K={K} H={H} chunk sizes {wl.microchunks}")
+    d = synth.make_inputs(wl, seed=0)
+    dev = "cuda:0"
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+    W_src = torch.from_numpy(d["W"].view(np.int16)).to(dev)
+    Wp = torch.empty(K * H, dtype=torch.int16, device=dev)
+    pr.pr_prepare_weight(W_src, pr.PR_WEIGHT_OUT_IN, Wp, K, H)
+    r = torch.from_numpy(d["residual"]).to(dev)
+    w = torch.from_numpy(d["norm_w"]).to(dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    del W_src
+    torch.cuda.synchronize()
+    flops = 2.0 * T * K * H
+
+    def fused(mc):
+        return lambda: pr.proj_add_rmsnorm(x, Wp, r, w, d["eps"], T, K, H, mc, wl.norm_kind, out)
+
+    def conventional():
+        pr.proj_add_rmsnorm_unfused(x, Wp, r, w, d["eps"], T, K, H, wl.norm_kind, out)
+
+    mcs = [args.microchunk] if args.microchunk else list(wl.microchunks)
+    per_mc = {}
+    best = None
+    for mc in mcs:
+        pr.pr_profile_enable(True)
+        el = time_steps(fused(mc), args.steps, args.warmup, torch)
+        prof_all = pr.pr_profile_read()
+        pr.pr_profile_enable(False)
+        # the profile counted warm-up launches too; per-launch averages are unaffected
+        per_mc[mc] = {"tokens_per_s": T * args.steps / el, "ms_per_step": el * 1e3 / args.steps,
+                      "tflops": flops * args.steps / el / 1e12, "profile": prof_all}
+        log(f"fused mc={mc}: {per_mc[mc]['ms_per_step']:.4f} ms/step "
+            f"{per_mc[mc]['tflops']:.1f} TFLOP/s")
+        if best is None or el < per_mc[best]["ms_per_step"] * args.steps / 1e3:
+            best = mc
+    pr.pr_profile_enable(True)
+    el_c = time_steps(conventional, args.steps, args.warmup, torch)
+    prof_c = pr.pr_profile_read()
+    pr.pr_profile_enable(False)
+    conv = {"tokens_per_s": T * args.steps / el_c, "ms_per_step": el_c * 1e3 / args.steps,
+            "tflops": flops * args.steps / el_c / 1e12}
+    log(f"conventional: {conv['ms_per_step']:.4f} ms/step {conv['tflops']:.1f} TFLOP/s")
+
+    # headline: the best chunk size, re-timed as its own region with the kernel profile live
+    mc = best
+    pr.pr_profile_enable(True)
+    for _ in range(args.warmup):
+        fused(mc)()
+    torch.cuda.synchronize()
+    pr.pr_profile_read()
+    pr.pr_profile_enable(True)  # restart counters: timed region only
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fused(mc)()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    prof = pr.pr_profile_read()
+    pr.pr_profile_enable(False)
+    value = T * args.steps / el
+    ms_step = el * 1e3 / args.steps
+    tflops = flops * args.steps / el / 1e12
+
+    g_launch_s = prof["gemm_ms"] / max(prof["gemm_launches"], 1) / 1e3
+    a_launch_s = prof["addnorm_ms"] / max(prof["addnorm_launches"], 1) / 1e3
+    gemm_flops_per_launch = flops * args.steps / max(prof["gemm_launches"], 1)
+    addnorm_elems_per_launch = T * H * args.steps / max(prof["addnorm_launches"], 1)
+    split = pr.pr_select(T, K, H, mc)["split_k"]
+    addnorm_bytes_per_elem = 4 * split + 4 + 4 + 2   # slot planes + r read + r write + out
+    gemm_tflops = gemm_flops_per_launch / g_launch_s / 1e12
+    addnorm_gbs = addnorm_elems_per_launch * addnorm_bytes_per_elem / a_launch_s / 1e9
+    dom_gemm = prof["gemm_ms"] >= prof["addnorm_ms"]
+    if dom_gemm:
+        roof = {"kernel": "gemm_bf16_kernel", "bound": "mfma", "achieved": gemm_tflops,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
+                "traffic": None, "avg_launch_us": g_launch_s * 1e6,
+                "launches": prof["gemm_launches"]}
+    else:
+        roof = {"kernel": "add_rmsnorm_kernel", "bound": "hbm", "achieved": addnorm_gbs,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": addnorm_gbs / PEAK_HBM_GBS,
+                "traffic": None, "avg_launch_us": a_launch_s * 1e6,
+                "launches": prof["addnorm_launches"]}
+    kernels = {"gemm_avg_us": g_launch_s * 1e6, "gemm_tflops": gemm_tflops,
+               "addnorm_avg_us": a_launch_s * 1e6, "addnorm_gbs": addnorm_gbs,
+               "addnorm_bytes_per_elem": addnorm_bytes_per_elem, "split_k": split}
+    result = {
+        "metric": "fused proj+add+RMSNorm tokens/s; TFLOP/s as % bf16 MFMA peak (1 GPU)",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name} prefill", "T": T, "K": K, "H": H,
+                   "microchunk": mc, "norm": "gemma" if wl.norm_kind else "standard",
+                   "path": "fused microchunk pipeline", "parallelism": "none (1 GPU)"},
+        "tflops": tflops, "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "roofline": roof, "kernels": kernels,
+        "per_microchunk": {str(k): {kk: vv for kk, vv in v.items() if kk != "profile"}
+                           for k, v in per_mc.items()},
+        "conventional": conv,
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
+        result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

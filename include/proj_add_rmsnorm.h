@@ -1,0 +1,257 @@
+/*
+ * proj_add_rmsnorm.h -- C ABI of the MI355X (gfx950) projection -> residual add -> RMSNorm
+ * library.
+ *
+ * The operation is the decoder-layer region that follows a row-parallel projection (o_proj or
+ * down_proj): vLLM "TPSP Design" page, section 1 (Motivation: projection, then residual add
+ * and normalisation) and section 3 (Fusion regions; Microchunk pipeline), for one device's
+ * share with no collective.  For T tokens, projection input size K and hidden size H:
+ *
+ *     y[t,h]   = sum_k x[t,k] * W[h,k]                 (bf16 inputs, fp32 accumulation)
+ *     r[t,h]  <- r[t,h] + y[t,h]                        (fp32 residual, updated in place)
+ *     out[t,h] = r[t,h] / sqrt(mean_h r[t,:]^2 + eps) * g[h]   (fp32 math, one bf16 rounding)
+ *
+ * with g = w for standard RMSNorm (no bias, "TPSP Design" section 4 Constraints) and g = 1 + w
+ * for the Gemma form (spyre-inference "Plugin Architecture" page, custom-op table, GemmaRMSNorm
+ * row: the weight multiply is done in fp32).
+ *
+ * Conventions for every entry point below
+ *  - Tensor pointers are DEVICE pointers on the current HIP device, row-major, 16-byte aligned.
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls are
+ *    asynchronous: they return once the work is enqueued on `stream`; the caller synchronises.
+ *  - Shapes: K % 64 == 0 and H % 64 == 0 (an intermediate size that is not a multiple of 64 is
+ *    zero-padded at load, which leaves the result unchanged: "Plugin Architecture" page,
+ *    SiluAndMul row).  T >= 0; T == 0 is a successful no-op.
+ *  - Return 0 (PR_OK) or a negative PR_ERR_* code; pr_last_error() gives a message.  Invalid
+ *    arguments and HIP execution errors are returned to the caller; the library never retries
+ *    or silently re-routes them ("TPSP Design" section 3, Profiling and fallback).
+ *  - Calls on one device are sequential: the library-owned workspace (pipeline slots, the
+ *    borrowed output) is shared by all calls on that device, so concurrent calls from several
+ *    host threads or streams on one device race ("TPSP Design" section 4: shared workspace
+ *    assumes sequential invocation).
+ */
+#ifndef PROJ_ADD_RMSNORM_H
+#define PROJ_ADD_RMSNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PR_VERSION 1
+
+/* return codes */
+#define PR_OK 0
+#define PR_ERR_INVALID_ARG (-1) /* null pointer, negative size, bad enum, negative eps       */
+#define PR_ERR_SHAPE (-2)       /* K or H not a multiple of 64, sizes too large                */
+#define PR_ERR_MICROCHUNK (-3)  /* microchunk < 0 or > PR_MAX_MICROCHUNK                       */
+#define PR_ERR_UNSUPPORTED (-4) /* call outside the tuned token range, no device, not gfx950   */
+#define PR_ERR_NOMEM (-5)       /* workspace allocation failed                                 */
+#define PR_ERR_HIP (-6)         /* a HIP call or kernel launch failed                          */
+
+/* RMSNorm gain form */
+#define PR_NORM_STANDARD 0 /* g = w      */
+#define PR_NORM_GEMMA 1    /* g = 1 + w  */
+
+/* source layouts accepted by pr_prepare_weight */
+#define PR_WEIGHT_OUT_IN 0 /* nn.Linear layout W[H][K] ([out, in])                  */
+#define PR_WEIGHT_IN_OUT 1 /* pre-transposed W^T[K][H] ([in, out], K rows of H)     */
+
+/* microchunk cap in tokens ("TPSP Design" section 4 Constraints, Resources) */
+#define PR_MAX_MICROCHUNK 4096
+
+/* execution paths */
+#define PR_PATH_CONVENTIONAL 0
+#define PR_PATH_FUSED 1
+
+/*
+ * Weight preparation, once after the weights load ("TPSP Design" section 3, Profiling and
+ * fallback: projection weights are prepared after load; "Plugin Architecture" page, section
+ * Transposed linear weights: the layout change is paid once at load, not in every forward).
+ *
+ * W_src   [H][K] (PR_WEIGHT_OUT_IN) or [K][H] (PR_WEIGHT_IN_OUT) bf16, device, caller-owned.
+ * W_prep  K*H bf16, device, caller-owned, written here.  Layout: the weight transposed to
+ *         [in][out] order in groups of 8 input rows, W_prep[((k/8)*H + h)*8 + k%8] = W[h][k],
+ *         so each output column's 8 consecutive k-values form one 16-byte matrix-core operand.
+ *         This is the only weight layout proj_add_rmsnorm and proj_add_rmsnorm_unfused accept.
+ * Must not alias W_src.  Errors: PR_ERR_INVALID_ARG, PR_ERR_SHAPE, PR_ERR_HIP.
+ */
+int pr_prepare_weight(const uint16_t* W_src, int src_layout, uint16_t* W_prep, int K, int H,
+                      void* stream);
+
+/*
+ * The fused region, one device's share ("TPSP Design" sections 1 and 3).
+ *
+ * x              [T][K] bf16, read only.
+ * W              [K*H] bf16 prepared by pr_prepare_weight, read only.
+ * residual_inout [T][H] fp32, read and updated in place: r += x . W^T.
+ * norm_w         [H] fp32 (standard: gain w; Gemma: offset w, applied as 1 + w).
+ * eps            >= 0, added to the mean square inside the square root.
+ * microchunk     > 0: microchunked pipeline with chunks of this many tokens (<= 4096; a value
+ *                  >= T gives one chunk).  Chunk i+1's projection overlaps chunk i's add+norm
+ *                  on a second stream; three reusable fp32 slots guarded by readiness and
+ *                  completion events hold the projection results; the rows past T in the last
+ *                  chunk are padding and never update residual or output ("TPSP Design"
+ *                  section 3, Microchunk pipeline).
+ *                = 0: automatic: the tuned token threshold picks the pipeline (with the tuned
+ *                  chunk size) when T >= threshold, else the conventional path.  Untuned shapes
+ *                  and inconclusive tunings use the conventional path; a T above the largest
+ *                  tuned token count returns PR_ERR_UNSUPPORTED ("TPSP Design" section 3,
+ *                  Profiling and fallback; section 4, Resources).  The environment variables
+ *                  PR_MICROCHUNK_TOKENS and PR_THRESHOLD_TOKENS override the tuned values; with
+ *                  both set no tuning is needed.
+ *                < 0: PR_ERR_MICROCHUNK.
+ * norm_kind      PR_NORM_STANDARD or PR_NORM_GEMMA.
+ * out            [T][H] bf16, caller-owned, written.  NULL: the result goes to a library
+ *                workspace returned by pr_workspace_output(), borrowed until the next call on
+ *                this device ("TPSP Design" section 3: the output borrows a shared workspace
+ *                and must be consumed before the next call).  Must not alias x, W or residual.
+ * stream         ordering stream (see conventions).
+ */
+int proj_add_rmsnorm(const uint16_t* x, const uint16_t* W, float* residual_inout,
+                     const float* norm_w, float eps, int T, int K, int H, int microchunk,
+                     int norm_kind, uint16_t* out, void* stream);
+
+/*
+ * Conventional path ("TPSP Design" section 1, "Conventional TP": projection, then the residual
+ * add and norm), one device's share: one projection over all T tokens emitting y in bf16
+ * (round to nearest even) to a library workspace, then one add+RMSNorm pass.  Same arguments
+ * and ownership as proj_add_rmsnorm without `microchunk`.  Its result differs from the fused
+ * path by the bf16 rounding of y.
+ */
+int proj_add_rmsnorm_unfused(const uint16_t* x, const uint16_t* W, float* residual_inout,
+                             const float* norm_w, float eps, int T, int K, int H, int norm_kind,
+                             uint16_t* out, void* stream);
+
+/* Device pointer of the borrowed output of the last call made with out == NULL on the current
+ * device, or NULL if there was none.  Valid until the next call on that device. */
+const uint16_t* pr_workspace_output(void);
+
+/* ---------------------------------------------------------------------------------------- *
+ * Host-only helpers (no device work; usable without a GPU)
+ * ---------------------------------------------------------------------------------------- */
+
+/* Argument checks of proj_add_rmsnorm (pointers are checked for NULL and aliasing only). */
+int pr_validate(const void* x, const void* W, const void* residual_inout, const void* norm_w,
+                float eps, int T, int K, int H, int microchunk, int norm_kind, const void* out);
+
+/* Execution decision for one call. */
+typedef struct {
+  int path;       /* PR_PATH_FUSED or PR_PATH_CONVENTIONAL                          */
+  int microchunk; /* chunk tokens (fused), else T                                   */
+  int n_chunks;   /* ceil(T / microchunk) (fused), else 1                           */
+  int last_valid; /* valid rows of the last chunk                                   */
+  int gemm_bm;    /* projection tile rows                                           */
+  int gemm_bn;    /* projection tile columns                                        */
+  int split_k;    /* K partitions of the projection; partial sums are added in order */
+  int reason;     /* PR_REASON_*                                                    */
+} pr_decision;
+
+#define PR_REASON_EXPLICIT 0          /* microchunk > 0 given by the caller            */
+#define PR_REASON_ABOVE_THRESHOLD 1   /* auto: T >= tuned/override threshold          */
+#define PR_REASON_BELOW_THRESHOLD 2   /* auto: T < threshold                          */
+#define PR_REASON_UNTUNED 3           /* auto: no tuning for this shape               */
+#define PR_REASON_INCONCLUSIVE 4      /* auto: tuning found no profitable range       */
+#define PR_REASON_UNFUSED_CALL 5      /* proj_add_rmsnorm_unfused                      */
+
+/* Decision proj_add_rmsnorm would take (microchunk as in proj_add_rmsnorm; -1 = the unfused
+ * entry point).  Returns PR_OK or the error that call would return. */
+int pr_select(int T, int K, int H, int microchunk, pr_decision* d);
+
+/* Dry-run schedule of the microchunk pipeline: the ordered list of operations the library
+ * enqueues for T tokens and chunk size mc (host order).  Returns the number of operations
+ * (written up to max_ops), or a negative error. */
+typedef struct {
+  int op;     /* PR_OP_*                                       */
+  int stream; /* 0 = caller's stream, 1 = projection stream A, 2 = add/norm stream B */
+  int chunk;  /* chunk index or -1                             */
+  int slot;   /* slot / event index (chunk % 3) or -1          */
+  int rows;   /* valid rows of the chunk or 0                  */
+} pr_plan_op;
+
+#define PR_OP_RECORD_ENTRY 0 /* caller stream: record the entry event                   */
+#define PR_OP_WAIT_ENTRY 1   /* stream A or B: wait for the entry event                  */
+#define PR_OP_WAIT_DONE 2    /* stream A: wait done[slot] before overwriting the slot    */
+#define PR_OP_GEMM 3         /* stream A: projection of the chunk into slot              */
+#define PR_OP_RECORD_READY 4 /* stream A: record ready[slot]                             */
+#define PR_OP_WAIT_READY 5   /* stream B: wait ready[slot]                               */
+#define PR_OP_ADDNORM 6      /* stream B: residual add + RMSNorm of the chunk from slot  */
+#define PR_OP_RECORD_DONE 7  /* stream B: record done[slot]                              */
+#define PR_OP_JOIN 8         /* caller stream: wait done[slot] of the last chunk         */
+#define PR_NUM_SLOTS 3
+
+int pr_plan(int T, int microchunk, pr_plan_op* ops, int max_ops);
+
+/* ---------------------------------------------------------------------------------------- *
+ * Token-threshold tuning ("TPSP Design" section 3, Profiling and fallback)
+ * ---------------------------------------------------------------------------------------- */
+
+/*
+ * Threshold from measured timings, summed over shape groups (host-only).
+ * t_conv, t_fused: [ngroups][nT] median seconds (t_fused = best checked chunk size; <= 0 when
+ * no candidate passed the numerical check).  spread: [ngroups][nT] run-to-run spread
+ * (p90 - p10) of the fused timing, or NULL.  T_grid ascending.  The threshold is the smallest
+ * grid T such that at it and at every larger grid T the summed fused time beats the summed
+ * conventional time by more than max(2%, summed spread); *threshold = INT32_MAX when none
+ * (inconclusive: the conventional path is kept).
+ */
+int pr_threshold_from_timings(int ngroups, int nT, const int* T_grid, const double* t_conv,
+                              const double* t_fused, const double* spread, int* threshold);
+
+/* Install a tuning result for the shape group (K, H): fused iff T >= threshold_tokens with
+ * chunk size mc_for_T[i] for T in [T_grid[i], T_grid[i+1]); calls with T > max_tokens fail
+ * with PR_ERR_UNSUPPORTED.  threshold_tokens = INT32_MAX marks an inconclusive tuning. */
+int pr_set_tuning(int K, int H, int threshold_tokens, int max_tokens, const int* T_grid,
+                  const int* mc_for_T, int nT);
+void pr_clear_tuning(void);
+
+typedef struct {
+  int threshold_tokens; /* INT32_MAX when inconclusive                         */
+  int max_tokens;
+  int n_checked;        /* candidate configurations that passed the check      */
+  int n_rejected;       /* candidates that failed the numerical check          */
+} pr_tune_report;
+
+/*
+ * Autotune on the current device: for each group g (shape K[g] x H[g]) and each T in T_grid,
+ * time the conventional path and the pipeline for every chunk size in mc_cand (<= min(T, 4096));
+ * each candidate's result is first checked against the conventional path's result (output
+ * max |delta| <= 2e-2 and relative L2 <= 5e-3, residual relative L2 <= 1e-3) and dropped if it
+ * fails.  Timings are medians of `reps` calls on synthetic device data.  Installs the result
+ * with pr_set_tuning for every group.  timings_out (optional): [ngroups][nT][2 + nmc] seconds
+ * (conventional, best fused, then each candidate; <= 0 for skipped or rejected candidates).
+ * With PR_MICROCHUNK_TOKENS and PR_THRESHOLD_TOKENS both set, nothing is timed or checked and
+ * the override is installed.
+ */
+int pr_tune(const int* K, const int* H, int ngroups, int norm_kind, const int* T_grid, int nT,
+            const int* mc_cand, int nmc, int reps, pr_tune_report* report, double* timings_out,
+            void* stream);
+
+/* ---------------------------------------------------------------------------------------- *
+ * Kernel timing for benchmarks: while enabled, every projection and add/norm launch of the
+ * calls on the current device is bracketed by timing events on the stream it runs on (the
+ * library's pipeline streams or the caller's stream).  pr_profile_read waits for the recorded
+ * events and returns the summed durations; the counters restart at every pr_profile_enable.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  double gemm_ms;       /* summed duration of projection launches           */
+  int gemm_launches;
+  double addnorm_ms;    /* summed duration of add + RMSNorm launches        */
+  int addnorm_launches;
+} pr_profile;
+
+int pr_profile_enable(int on);
+int pr_profile_read(pr_profile* p);
+
+/* ---------------------------------------------------------------------------------------- */
+const char* pr_strerror(int code);
+const char* pr_last_error(void); /* message of the last failing call on this host thread */
+int pr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PROJ_ADD_RMSNORM_H */

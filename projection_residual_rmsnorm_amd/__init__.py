@@ -1,0 +1,248 @@
+"""Thin Python binding of the MI355X projection -> residual add -> RMSNorm library.
+
+Every function here marshals arguments and calls the C ABI declared in
+include/proj_add_rmsnorm.h (same names); all computation runs in the HIP library.  Tensors may
+be torch tensors (their device pointers are passed) or raw integer addresses.  A non-zero return
+code raises PRError with the library's message.  The library must have been built
+(``python -m projection_residual_rmsnorm_amd.build``); importing the binding without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libprojaddnorm.so")
+
+PR_OK = 0
+PR_ERR_INVALID_ARG = -1
+PR_ERR_SHAPE = -2
+PR_ERR_MICROCHUNK = -3
+PR_ERR_UNSUPPORTED = -4
+PR_ERR_NOMEM = -5
+PR_ERR_HIP = -6
+
+PR_NORM_STANDARD = 0
+PR_NORM_GEMMA = 1
+PR_WEIGHT_OUT_IN = 0
+PR_WEIGHT_IN_OUT = 1
+PR_MAX_MICROCHUNK = 4096
+PR_PATH_CONVENTIONAL = 0
+PR_PATH_FUSED = 1
+PR_NUM_SLOTS = 3
+INT32_MAX = 2**31 - 1
+
+OP_NAMES = ["RECORD_ENTRY", "WAIT_ENTRY", "WAIT_DONE", "GEMM", "RECORD_READY", "WAIT_READY",
+            "ADDNORM", "RECORD_DONE", "JOIN"]
+REASON_NAMES = ["explicit", "above_threshold", "below_threshold", "untuned", "inconclusive",
+                "unfused_call"]
+
+# C signatures of every exported entry point (the header's declarations).
+_c = ctypes
+_vp, _i, _f, _d = _c.c_void_p, _c.c_int, _c.c_float, _c.c_double
+
+
+class pr_decision(_c.Structure):
+    _fields_ = [("path", _i), ("microchunk", _i), ("n_chunks", _i), ("last_valid", _i),
+                ("gemm_bm", _i), ("gemm_bn", _i), ("split_k", _i), ("reason", _i)]
+
+
+class pr_plan_op(_c.Structure):
+    _fields_ = [("op", _i), ("stream", _i), ("chunk", _i), ("slot", _i), ("rows", _i)]
+
+
+class pr_tune_report(_c.Structure):
+    _fields_ = [("threshold_tokens", _i), ("max_tokens", _i), ("n_checked", _i),
+                ("n_rejected", _i)]
+
+
+class pr_profile(_c.Structure):
+    _fields_ = [("gemm_ms", _d), ("gemm_launches", _i), ("addnorm_ms", _d),
+                ("addnorm_launches", _i)]
+
+
+SIGNATURES = {
+    "pr_profile_enable": (_i, [_i]),
+    "pr_profile_read": (_i, [_c.POINTER(pr_profile)]),
+    "pr_prepare_weight": (_i, [_vp, _i, _vp, _i, _i, _vp]),
+    "proj_add_rmsnorm": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _i, _vp, _vp]),
+    "proj_add_rmsnorm_unfused": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp, _vp]),
+    "pr_workspace_output": (_vp, []),
+    "pr_validate": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _i, _vp]),
+    "pr_select": (_i, [_i, _i, _i, _i, _c.POINTER(pr_decision)]),
+    "pr_plan": (_i, [_i, _i, _c.POINTER(pr_plan_op), _i]),
+    "pr_threshold_from_timings": (_i, [_i, _i, _c.POINTER(_i), _c.POINTER(_d), _c.POINTER(_d),
+                                       _c.POINTER(_d), _c.POINTER(_i)]),
+    "pr_set_tuning": (_i, [_i, _i, _i, _i, _c.POINTER(_i), _c.POINTER(_i), _i]),
+    "pr_clear_tuning": (None, []),
+    "pr_tune": (_i, [_c.POINTER(_i), _c.POINTER(_i), _i, _i, _c.POINTER(_i), _i, _c.POINTER(_i),
+                     _i, _i, _c.POINTER(pr_tune_report), _c.POINTER(_d), _vp]),
+    "pr_strerror": (_c.c_char_p, [_i]),
+    "pr_last_error": (_c.c_char_p, []),
+    "pr_version": (_i, []),
+}
+
+
+class PRError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{code} ({_lib().pr_strerror(code).decode()}): {message}")
+        self.code = code
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library {LIB_PATH} is missing; build it with "
+                "`python -m projection_residual_rmsnorm_amd.build`")
+        # torch ships its own HIP runtime; importing it first makes the library bind to that one
+        # runtime (same soname) instead of loading a second copy from /opt/rocm.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def library():
+    """The loaded ctypes library (loads it on first use)."""
+    return _lib()
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream, *tensors) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    for t in tensors:
+        if t is not None and not isinstance(t, int) and getattr(t, "is_cuda", False):
+            import torch
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _check(rc: int) -> int:
+    if rc != PR_OK:
+        raise PRError(rc, _lib().pr_last_error().decode())
+    return rc
+
+
+def pr_prepare_weight(W_src, src_layout: int, W_prep, K: int, H: int, stream=None) -> None:
+    _check(_lib().pr_prepare_weight(_ptr(W_src), src_layout, _ptr(W_prep), K, H,
+                                    _stream(stream, W_src)))
+
+
+def proj_add_rmsnorm(x, W, residual_inout, norm_w, eps: float, T: int, K: int, H: int,
+                     microchunk: int, norm_kind: int = PR_NORM_STANDARD, out=None,
+                     stream=None) -> None:
+    _check(_lib().proj_add_rmsnorm(_ptr(x), _ptr(W), _ptr(residual_inout), _ptr(norm_w), eps, T,
+                                   K, H, microchunk, norm_kind, _ptr(out),
+                                   _stream(stream, x, residual_inout)))
+
+
+def proj_add_rmsnorm_unfused(x, W, residual_inout, norm_w, eps: float, T: int, K: int, H: int,
+                             norm_kind: int = PR_NORM_STANDARD, out=None, stream=None) -> None:
+    _check(_lib().proj_add_rmsnorm_unfused(_ptr(x), _ptr(W), _ptr(residual_inout), _ptr(norm_w),
+                                           eps, T, K, H, norm_kind, _ptr(out),
+                                           _stream(stream, x, residual_inout)))
+
+
+def pr_workspace_output() -> Optional[int]:
+    return _lib().pr_workspace_output()
+
+
+def pr_validate(x, W, residual_inout, norm_w, eps, T, K, H, microchunk, norm_kind, out) -> int:
+    """Returns the code (does not raise)."""
+    return _lib().pr_validate(_ptr(x), _ptr(W), _ptr(residual_inout), _ptr(norm_w), eps, T, K,
+                              H, microchunk, norm_kind, _ptr(out))
+
+
+def pr_select(T: int, K: int, H: int, microchunk: int) -> dict:
+    d = pr_decision()
+    _check(_lib().pr_select(T, K, H, microchunk, ctypes.byref(d)))
+    return {f: getattr(d, f) for f, _ in pr_decision._fields_}
+
+
+def pr_plan(T: int, microchunk: int) -> List[Tuple[str, int, int, int, int]]:
+    n = _lib().pr_plan(T, microchunk, None, 0)
+    if n < 0:
+        _check(n)
+    ops = (pr_plan_op * max(n, 1))()
+    _check(0 if _lib().pr_plan(T, microchunk, ops, n) == n else PR_ERR_INVALID_ARG)
+    return [(OP_NAMES[o.op], o.stream, o.chunk, o.slot, o.rows) for o in ops[:n]]
+
+
+def pr_threshold_from_timings(T_grid: Sequence[int], t_conv, t_fused, spread=None) -> int:
+    """t_conv / t_fused / spread: [ngroups][nT] nested sequences (seconds)."""
+    ng, nT = len(t_conv), len(T_grid)
+    flat = lambda a: (ctypes.c_double * (ng * nT))(*[float(v) for row in a for v in row])
+    thr = ctypes.c_int()
+    _check(_lib().pr_threshold_from_timings(
+        ng, nT, (ctypes.c_int * nT)(*T_grid), flat(t_conv), flat(t_fused),
+        flat(spread) if spread is not None else None, ctypes.byref(thr)))
+    return thr.value
+
+
+def pr_set_tuning(K: int, H: int, threshold_tokens: int, max_tokens: int,
+                  T_grid: Sequence[int], mc_for_T: Sequence[int]) -> None:
+    n = len(T_grid)
+    _check(_lib().pr_set_tuning(K, H, threshold_tokens, max_tokens, (ctypes.c_int * n)(*T_grid),
+                                (ctypes.c_int * n)(*mc_for_T), n))
+
+
+def pr_clear_tuning() -> None:
+    _lib().pr_clear_tuning()
+
+
+def pr_tune(Ks: Sequence[int], Hs: Sequence[int], norm_kind: int, T_grid: Sequence[int],
+            mc_cand: Sequence[int], reps: int = 10, stream=None) -> dict:
+    ng, nT, nmc = len(Ks), len(T_grid), len(mc_cand)
+    rep = pr_tune_report()
+    timings = (ctypes.c_double * (ng * nT * (2 + nmc)))()
+    _check(_lib().pr_tune((ctypes.c_int * ng)(*Ks), (ctypes.c_int * ng)(*Hs), ng, norm_kind,
+                          (ctypes.c_int * nT)(*T_grid), nT, (ctypes.c_int * nmc)(*mc_cand), nmc,
+                          reps, ctypes.byref(rep), timings, _stream(stream)))
+    t = list(timings)
+    table = [[t[(g * nT + i) * (2 + nmc):(g * nT + i + 1) * (2 + nmc)] for i in range(nT)]
+             for g in range(ng)]
+    return {"threshold_tokens": rep.threshold_tokens, "max_tokens": rep.max_tokens,
+            "n_checked": rep.n_checked, "n_rejected": rep.n_rejected, "timings": table}
+
+
+def pr_profile_enable(on: bool = True) -> None:
+    _check(_lib().pr_profile_enable(1 if on else 0))
+
+
+def pr_profile_read() -> dict:
+    p = pr_profile()
+    _check(_lib().pr_profile_read(ctypes.byref(p)))
+    return {f: getattr(p, f) for f, _ in pr_profile._fields_}
+
+
+def pr_strerror(code: int) -> str:
+    return _lib().pr_strerror(code).decode()
+
+
+def pr_last_error() -> str:
+    return _lib().pr_last_error().decode()
+
+
+def pr_version() -> int:
+    return _lib().pr_version()

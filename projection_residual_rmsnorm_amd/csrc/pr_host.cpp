@@ -1,0 +1,388 @@
+// Host-only logic of the library: argument checks, the per-call path decision, the projection
+// tile choice, the dry-run schedule of the microchunk pipeline and the token-threshold search.
+// Nothing here touches a GPU, so all of it is testable on a machine without one.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <limits>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "pr_internal.h"
+
+namespace pr {
+
+namespace {
+thread_local std::string g_last_error;
+
+struct Tuning {
+  int threshold = INT32_MAX;
+  int max_tokens = 0;
+  std::vector<int> T_grid;
+  std::vector<int> mc_for_T;
+};
+std::mutex g_tuning_mu;
+std::map<std::pair<int, int>, Tuning> g_tuning;  // keyed by (K, H)
+
+constexpr long long kMaxWeightElems = 1LL << 30;  // K*H <= 2^30 (2 GiB of bf16)
+}  // namespace
+
+bool log_enabled() {
+  const char* v = std::getenv("PR_LOG");
+  return v != nullptr && v[0] != '\0' && v[0] != '0';
+}
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  if (log_enabled()) std::fprintf(stderr, "[proj_add_rmsnorm] error %d: %s\n", code, buf);
+  return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+static int parse_env_int(const char* name, int* out) {
+  *out = 0;
+  const char* v = std::getenv(name);
+  if (v == nullptr || v[0] == '\0') return PR_OK;
+  char* end = nullptr;
+  const long x = std::strtol(v, &end, 10);
+  if (end == v || *end != '\0' || x < 0 || x > INT32_MAX)
+    return fail(PR_ERR_INVALID_ARG, "%s=\"%s\" is not a non-negative integer", name, v);
+  *out = (int)x;
+  return PR_OK;
+}
+
+int read_overrides(int* mc_override, int* threshold_override) {
+  int rc = parse_env_int("PR_MICROCHUNK_TOKENS", mc_override);
+  if (rc != PR_OK) return rc;
+  if (*mc_override > PR_MAX_MICROCHUNK)
+    return fail(PR_ERR_MICROCHUNK, "PR_MICROCHUNK_TOKENS=%d exceeds the cap of %d tokens",
+                *mc_override, PR_MAX_MICROCHUNK);
+  return parse_env_int("PR_THRESHOLD_TOKENS", threshold_override);
+}
+
+static bool env_set(const char* name) {
+  const char* v = std::getenv(name);
+  return v != nullptr && v[0] != '\0';
+}
+
+// Debug override of the projection tile: PR_FORCE_TILE="BMxBN" (an instantiated tile) and
+// PR_FORCE_SPLIT=S (S must divide K/64).  Used by tests to reach every kernel variant.
+static int apply_forced_tile(int K, GemmCfg* g) {
+  const char* t = std::getenv("PR_FORCE_TILE");
+  if (t != nullptr && t[0] != '\0') {
+    int bm = 0, bn = 0;
+    bool ok = std::sscanf(t, "%dx%d", &bm, &bn) == 2;
+    bool known = false;
+    for (int c = 0; c < kNumTileCfgs; ++c) known |= (kTileBM[c] == bm && kTileBN[c] == bn);
+    if (!ok || !known) return fail(PR_ERR_INVALID_ARG, "PR_FORCE_TILE=\"%s\" is not a tile", t);
+    g->bm = bm;
+    g->bn = bn;
+  }
+  const char* sp = std::getenv("PR_FORCE_SPLIT");
+  if (sp != nullptr && sp[0] != '\0') {
+    const int split = std::atoi(sp);
+    if (split <= 0 || K % (64 * split) != 0)
+      return fail(PR_ERR_INVALID_ARG, "PR_FORCE_SPLIT=%s must divide K/64 = %d", sp, K / 64);
+    g->split = split;
+  }
+  return PR_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Projection tile choice.  Time model per workgroup wave: the MFMA time of one tile at the
+// tile's sustained fraction of peak, times the number of rounds of 256 workgroups, plus the
+// HBM/MALL time of the extra fp32 partial planes that a K split writes and the add/norm reads.
+// ---------------------------------------------------------------------------------------------
+GemmCfg choose_gemm(int M, int N, int K, bool fp32_out) {
+  static const double kEff[kNumTileCfgs] = {1.0, 0.85, 0.6};
+  const double per_cu_flops = 2.5e15 / kNumCUs;
+  const double bw = 5.0e12;
+  GemmCfg best;
+  double best_t = std::numeric_limits<double>::infinity();
+  for (int c = 0; c < kNumTileCfgs; ++c) {
+    const int bm = kTileBM[c], bn = kTileBN[c];
+    const long long tiles = (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    for (int split = 1; split <= 16; split *= 2) {
+      if (K % (64 * split) != 0) break;
+      const long long units = tiles * split;
+      const long long rounds = (units + kNumCUs - 1) / kNumCUs;
+      const double t_mfma = (double)rounds * 2.0 * bm * bn * (double)(K / split) /
+                            (per_cu_flops * kEff[c]);
+      // bytes of y moved between projection and add/norm beyond a single bf16 (conventional)
+      // or fp32 (pipeline) plane
+      const double base_bytes = (fp32_out ? 8.0 : 4.0) * M * (double)N;
+      const double bytes = split == 1 ? base_bytes : 8.0 * split * M * (double)N;
+      const double t = t_mfma + (bytes - base_bytes) / bw;
+      if (t < best_t * 0.999) {
+        best_t = t;
+        best.bm = bm;
+        best.bn = bn;
+        best.split = split;
+      }
+    }
+  }
+  return best;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-call decision.
+// ---------------------------------------------------------------------------------------------
+int decide(int T, int K, int H, int microchunk, pr_decision* d) {
+  std::memset(d, 0, sizeof(*d));
+  int path = PR_PATH_CONVENTIONAL;
+  int mc = 0;
+  int reason = PR_REASON_UNFUSED_CALL;
+  if (microchunk > 0) {
+    path = PR_PATH_FUSED;
+    mc = microchunk;
+    reason = PR_REASON_EXPLICIT;
+  } else if (microchunk == 0) {
+    int mc_ov = 0, thr_ov = 0;
+    int rc = read_overrides(&mc_ov, &thr_ov);
+    if (rc != PR_OK) return rc;
+    const bool have_mc = env_set("PR_MICROCHUNK_TOKENS");
+    const bool have_thr = env_set("PR_THRESHOLD_TOKENS");
+    if (have_mc && mc_ov == 0)
+      return fail(PR_ERR_MICROCHUNK, "PR_MICROCHUNK_TOKENS must be in 1..%d", PR_MAX_MICROCHUNK);
+    if (have_mc && have_thr) {
+      // Both overrides: no tuning, no numerical check.
+      if (T >= thr_ov) {
+        path = PR_PATH_FUSED;
+        mc = mc_ov;
+        reason = PR_REASON_ABOVE_THRESHOLD;
+      } else {
+        reason = PR_REASON_BELOW_THRESHOLD;
+      }
+    } else {
+      Tuning tu;
+      bool found = false;
+      {
+        std::lock_guard<std::mutex> lk(g_tuning_mu);
+        auto it = g_tuning.find({K, H});
+        if (it != g_tuning.end()) {
+          tu = it->second;
+          found = true;
+        }
+      }
+      if (!found) {
+        reason = PR_REASON_UNTUNED;
+      } else if (T > tu.max_tokens) {
+        return fail(PR_ERR_UNSUPPORTED,
+                    "T=%d exceeds the largest tuned token count %d for K=%d H=%d", T,
+                    tu.max_tokens, K, H);
+      } else {
+        const int thr = have_thr ? thr_ov : tu.threshold;
+        if (!have_thr && tu.threshold == INT32_MAX) {
+          reason = PR_REASON_INCONCLUSIVE;
+        } else if (T >= thr) {
+          path = PR_PATH_FUSED;
+          reason = PR_REASON_ABOVE_THRESHOLD;
+          if (have_mc) {
+            mc = mc_ov;
+          } else {
+            int idx = 0;
+            for (size_t i = 0; i < tu.T_grid.size(); ++i)
+              if (tu.T_grid[i] <= T) idx = (int)i;
+            mc = tu.mc_for_T.empty() ? std::min(T, PR_MAX_MICROCHUNK) : tu.mc_for_T[idx];
+          }
+        } else {
+          reason = PR_REASON_BELOW_THRESHOLD;
+        }
+      }
+    }
+  }
+  d->path = path;
+  d->reason = reason;
+  GemmCfg g;
+  if (path == PR_PATH_FUSED) {
+    const int eff = std::min(mc, std::max(T, 1));
+    d->microchunk = mc;
+    d->n_chunks = T > 0 ? (T + mc - 1) / mc : 0;
+    d->last_valid = T > 0 ? T - (d->n_chunks - 1) * mc : 0;
+    g = choose_gemm(eff, H, K, true);
+  } else {
+    d->microchunk = T;
+    d->n_chunks = T > 0 ? 1 : 0;
+    d->last_valid = T;
+    g = choose_gemm(std::max(T, 1), H, K, false);
+  }
+  const int rc = apply_forced_tile(K, &g);
+  if (rc != PR_OK) return rc;
+  d->gemm_bm = g.bm;
+  d->gemm_bn = g.bn;
+  d->split_k = g.split;
+  return PR_OK;
+}
+
+}  // namespace pr
+
+using namespace pr;
+
+extern "C" {
+
+int pr_version(void) { return PR_VERSION; }
+
+const char* pr_strerror(int code) {
+  switch (code) {
+    case PR_OK:
+      return "success";
+    case PR_ERR_INVALID_ARG:
+      return "invalid argument";
+    case PR_ERR_SHAPE:
+      return "unsupported shape";
+    case PR_ERR_MICROCHUNK:
+      return "invalid microchunk";
+    case PR_ERR_UNSUPPORTED:
+      return "unsupported call";
+    case PR_ERR_NOMEM:
+      return "out of device memory";
+    case PR_ERR_HIP:
+      return "HIP error";
+    default:
+      return "unknown error";
+  }
+}
+
+const char* pr_last_error(void) { return pr::g_last_error.c_str(); }
+
+int pr_validate(const void* x, const void* W, const void* residual_inout, const void* norm_w,
+                float eps, int T, int K, int H, int microchunk, int norm_kind, const void* out) {
+  if (T < 0 || K <= 0 || H <= 0)
+    return fail(PR_ERR_INVALID_ARG, "sizes must satisfy T >= 0, K > 0, H > 0 (T=%d K=%d H=%d)",
+                T, K, H);
+  if (K % 64 != 0 || H % 64 != 0)
+    return fail(PR_ERR_SHAPE, "K=%d and H=%d must be multiples of 64 (zero-pad at load)", K, H);
+  if ((long long)K * H > kMaxWeightElems)
+    return fail(PR_ERR_SHAPE, "weight K*H=%lld exceeds %lld elements", (long long)K * H,
+                kMaxWeightElems);
+  if ((long long)T * H > (1LL << 40) || (long long)T * K > (1LL << 40))
+    return fail(PR_ERR_SHAPE, "T=%d too large", T);
+  if (microchunk < -1)
+    return fail(PR_ERR_MICROCHUNK, "microchunk=%d must be >= 0", microchunk);
+  if (microchunk > PR_MAX_MICROCHUNK)
+    return fail(PR_ERR_MICROCHUNK, "microchunk=%d exceeds the cap of %d tokens", microchunk,
+                PR_MAX_MICROCHUNK);
+  if (norm_kind != PR_NORM_STANDARD && norm_kind != PR_NORM_GEMMA)
+    return fail(PR_ERR_INVALID_ARG, "unknown norm_kind %d", norm_kind);
+  if (!(eps >= 0.0f) || std::isinf(eps))
+    return fail(PR_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (T == 0) return PR_OK;
+  if (x == nullptr || W == nullptr || residual_inout == nullptr || norm_w == nullptr)
+    return fail(PR_ERR_INVALID_ARG, "null tensor pointer");
+  if (out != nullptr && (out == x || out == W || out == residual_inout))
+    return fail(PR_ERR_INVALID_ARG, "out must not alias x, W or residual");
+  const uintptr_t a[5] = {(uintptr_t)x, (uintptr_t)W, (uintptr_t)residual_inout,
+                          (uintptr_t)norm_w, (uintptr_t)out};
+  for (uintptr_t p : a)
+    if (p % 16 != 0) return fail(PR_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  return PR_OK;
+}
+
+int pr_select(int T, int K, int H, int microchunk, pr_decision* d) {
+  if (d == nullptr) return fail(PR_ERR_INVALID_ARG, "null decision");
+  if (T < 0 || K <= 0 || H <= 0) return fail(PR_ERR_INVALID_ARG, "bad sizes");
+  if (microchunk < -1 || microchunk > PR_MAX_MICROCHUNK)
+    return fail(PR_ERR_MICROCHUNK, "microchunk=%d out of range", microchunk);
+  return decide(T, K, H, microchunk, d);
+}
+
+int pr_plan(int T, int microchunk, pr_plan_op* ops, int max_ops) {
+  if (T < 0 || microchunk <= 0 || microchunk > PR_MAX_MICROCHUNK)
+    return fail(PR_ERR_INVALID_ARG, "pr_plan needs T >= 0 and 0 < microchunk <= %d",
+                PR_MAX_MICROCHUNK);
+  if (max_ops < 0 || (max_ops > 0 && ops == nullptr))
+    return fail(PR_ERR_INVALID_ARG, "bad op buffer");
+  int n = 0;
+  auto emit = [&](int op, int stream, int chunk, int slot, int rows) {
+    if (n < max_ops) ops[n] = pr_plan_op{op, stream, chunk, slot, rows};
+    ++n;
+  };
+  if (T == 0) return 0;
+  const int nc = (T + microchunk - 1) / microchunk;
+  emit(PR_OP_RECORD_ENTRY, 0, -1, -1, 0);
+  emit(PR_OP_WAIT_ENTRY, 1, -1, -1, 0);
+  emit(PR_OP_WAIT_ENTRY, 2, -1, -1, 0);
+  for (int c = 0; c < nc; ++c) {
+    const int s = c % PR_NUM_SLOTS;
+    const int rows = std::min(microchunk, T - c * microchunk);
+    if (c >= PR_NUM_SLOTS) emit(PR_OP_WAIT_DONE, 1, c, s, 0);
+    emit(PR_OP_GEMM, 1, c, s, rows);
+    emit(PR_OP_RECORD_READY, 1, c, s, 0);
+    emit(PR_OP_WAIT_READY, 2, c, s, 0);
+    emit(PR_OP_ADDNORM, 2, c, s, rows);
+    emit(PR_OP_RECORD_DONE, 2, c, s, 0);
+  }
+  emit(PR_OP_JOIN, 0, nc - 1, (nc - 1) % PR_NUM_SLOTS, 0);
+  return n;
+}
+
+int pr_threshold_from_timings(int ngroups, int nT, const int* T_grid, const double* t_conv,
+                              const double* t_fused, const double* spread, int* threshold) {
+  if (ngroups <= 0 || nT <= 0 || T_grid == nullptr || t_conv == nullptr || t_fused == nullptr ||
+      threshold == nullptr)
+    return fail(PR_ERR_INVALID_ARG, "bad threshold inputs");
+  for (int i = 1; i < nT; ++i)
+    if (T_grid[i] <= T_grid[i - 1]) return fail(PR_ERR_INVALID_ARG, "T_grid must ascend");
+  std::vector<bool> win(nT, false);
+  for (int i = 0; i < nT; ++i) {
+    double sc = 0, sf = 0, sp = 0;
+    bool ok = true;
+    for (int g = 0; g < ngroups; ++g) {
+      const double c = t_conv[g * nT + i], f = t_fused[g * nT + i];
+      if (!(c > 0) || !(f > 0)) ok = false;
+      sc += c;
+      sf += f;
+      if (spread != nullptr) sp += std::max(0.0, spread[g * nT + i]);
+    }
+    const double margin = std::max(0.02 * sc, sp);
+    win[i] = ok && (sf + margin < sc);
+  }
+  int thr = INT32_MAX;
+  for (int i = nT - 1; i >= 0; --i) {
+    if (!win[i]) break;
+    thr = T_grid[i];
+  }
+  *threshold = thr;
+  return PR_OK;
+}
+
+int pr_set_tuning(int K, int H, int threshold_tokens, int max_tokens, const int* T_grid,
+                  const int* mc_for_T, int nT) {
+  if (K <= 0 || H <= 0 || max_tokens < 0 || threshold_tokens < 0 || nT < 0 ||
+      (nT > 0 && (T_grid == nullptr || mc_for_T == nullptr)))
+    return fail(PR_ERR_INVALID_ARG, "bad tuning arguments");
+  Tuning tu;
+  tu.threshold = threshold_tokens;
+  tu.max_tokens = max_tokens;
+  for (int i = 0; i < nT; ++i) {
+    if (i > 0 && T_grid[i] <= T_grid[i - 1])
+      return fail(PR_ERR_INVALID_ARG, "T_grid must ascend");
+    if (mc_for_T[i] <= 0 || mc_for_T[i] > PR_MAX_MICROCHUNK)
+      return fail(PR_ERR_MICROCHUNK, "tuned microchunk %d out of range", mc_for_T[i]);
+    tu.T_grid.push_back(T_grid[i]);
+    tu.mc_for_T.push_back(mc_for_T[i]);
+  }
+  std::lock_guard<std::mutex> lk(g_tuning_mu);
+  g_tuning[{K, H}] = tu;
+  return PR_OK;
+}
+
+void pr_clear_tuning(void) {
+  std::lock_guard<std::mutex> lk(g_tuning_mu);
+  g_tuning.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Internal interfaces shared by the library's translation units (not part of the C ABI).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/proj_add_rmsnorm.h"
+
+namespace pr {
+
+// MI355X: 256 compute units (8 XCDs x 32), 2.4 GHz peak engine clock.
+constexpr int kNumCUs = 256;
+constexpr int kNumXCDs = 8;
+
+// Projection tile configuration.
+struct GemmCfg {
+  int bm = 256;   // tile rows (tokens)
+  int bn = 256;   // tile columns (hidden)
+  int split = 1;  // K partitions; partial sums land in separate fp32 planes
+};
+
+// Tile configurations the library instantiates (rows x columns per workgroup).
+constexpr int kNumTileCfgs = 3;
+constexpr int kTileBM[kNumTileCfgs] = {256, 256, 128};
+constexpr int kTileBN[kNumTileCfgs] = {256, 128, 128};
+
+// Cost-model choice of tile and split for an M x N x K projection.  `fp32_out` is true when the
+// projection result is kept in fp32 (the pipeline's slot), false when it is emitted in bf16.
+GemmCfg choose_gemm(int M, int N, int K, bool fp32_out);
+
+// Error reporting: stores the message for pr_last_error() and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+bool log_enabled();
+
+// Auto-mode / explicit decision (host only); `microchunk` = -1 marks the unfused entry point.
+int decide(int T, int K, int H, int microchunk, pr_decision* d);
+
+// Environment overrides: returns PR_OK and sets the values (0 when unset) or an error for a
+// malformed value.
+int read_overrides(int* mc_override, int* threshold_override);
+
+}  // namespace pr
+
+// ---- device-side launchers (pr_kernels.hip) -----------------------------------------------
+namespace pr {
+
+// y = x . W^T for M rows.  x [M][K] bf16 (row stride K), Wp the prepared weight (K*N).
+// fp32 mode: C planes [split][M][N] at plane stride `plane_stride` elements.
+// bf16 mode (split must be 1): C is [M][N] bf16, rounded to nearest even.
+int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
+                int K, const GemmCfg& cfg, long long plane_stride, void* stream);
+
+// r <- r + y; out = RMSNorm(r) for `rows` rows of width H.
+// y: fp32 planes [nplanes][rows][H] (summed in plane order) or bf16 [rows][H] (y_bf16 != 0).
+// round_y: round the summed fp32 y to bf16 before the add (conventional semantics).
+int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_stride,
+                       int round_y, float* r, const float* w, uint16_t* out, int rows, int H,
+                       float eps, int gemma, void* stream);
+
+int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,
+                          void* stream);
+
+// Debug helpers: a bounded sleep (iters x s_sleep 127) and a NaN fill.
+int launch_delay(int iters, void* stream);
+int launch_fill_nan(float* p, size_t n, void* stream);
+// Synthetic device data for tuning: bf16 values uniform in [-scale, scale) from a counter hash.
+int launch_fill_bf16_hash(uint16_t* p, size_t n, uint32_t seed, float scale, void* stream);
+int launch_fill_f32_hash(float* p, size_t n, uint32_t seed, float scale, float offset,
+                         void* stream);
+
+}  // namespace pr

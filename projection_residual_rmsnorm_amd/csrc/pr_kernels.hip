@@ -1,0 +1,566 @@
+// gfx950 kernels of the projection -> residual add -> RMSNorm path.
+//
+//  * gemm_bf16_kernel: y = x . W^T on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16), fp32
+//    accumulation, tiles staged through LDS with direct global->LDS loads, double-buffered.
+//    The projection of the region ("TPSP Design" page, section 3, Fusion regions: o_proj and
+//    down_proj) is the dense contraction of the path, so it is the part that runs on MFMA.
+//  * add_rmsnorm_kernel: r <- r + y in fp32 (in place), then RMSNorm of the row with a
+//    wavefront reduction of the sum of squares and one bf16 rounding of the output
+//    ("TPSP Design" section 3: the fused path updates the residual and returns normalised
+//    states; "Plugin Architecture" page, GemmaRMSNorm row: fp32 weight multiply).  HBM-bound.
+//  * prepare_weight kernels: the one-time layout change of the weight after load.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pr_internal.h"
+
+namespace pr {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_cvoid_t;
+
+constexpr int kBK = 64;  // K depth of one LDS stage (8 groups of 8 bf16 = 128 bytes per row)
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays a quiet NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ void load_to_lds16(const char* gbase, uint32_t lane_off,
+                                              char* lds_dst_wave_base) {
+  // Each lane copies 16 bytes from gbase + lane_off (gbase wave-uniform) to
+  // lds_dst_wave_base + lane * 16.
+  __builtin_amdgcn_global_load_lds((global_cvoid_t*)(gbase + lane_off),
+                                   (lds_void_t*)lds_dst_wave_base, 16, 0, 0);
+}
+
+// --------------------------------------------------------------------------------------------
+// Projection.
+//
+// Operands
+//   A  = x [M][K] bf16, row stride K (the chunk's tokens).
+//   Bp = prepared weight, Bp[((k/8)*N + n)*8 + k%8] = W[n][k].
+// LDS stage layouts (bytes), chosen so that every fragment read is lane-linear (conflict-free)
+// and every direct global->LDS load writes 1 KiB contiguously:
+//   A stage: [BM/32 row blocks][8 k-groups][32 rows][16 B]
+//   B stage: [8 k-groups][BN columns][16 B]
+// A 32x32x16 MFMA takes, per lane l, A[row l%32][k 8*(l/32)..+8] and B[k 8*(l/32)..+8][col l%32]:
+// both are one 16-byte read at offset ((k-group)*32 + l%32)*16 within a 32-row/column block.
+// --------------------------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, bool ODD_STAGES>
+__global__ void __launch_bounds__(WM* WN * 64, 1)
+    gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp,
+                     float* __restrict__ Cf, uint16_t* __restrict__ Cb, int M, int N, int K,
+                     int k_split_len, long long plane_stride, int tiles_m, int tiles_n,
+                     int split) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM;  // wave tile rows
+  constexpr int WTN = BN / WN;  // wave tile columns
+  constexpr int TM = WTM / 32;
+  constexpr int TN = WTN / 32;
+  constexpr int A_BYTES = BM * kBK * 2;
+  constexpr int B_BYTES = BN * kBK * 2;
+  constexpr int A_LOADS = A_BYTES / 1024;  // wave-wide 1 KiB load instructions per stage
+  constexpr int B_LOADS = B_BYTES / 1024;
+  static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads must split evenly over waves");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
+
+  __shared__ __attribute__((aligned(1024))) char sA0[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB0[B_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sA1[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sB1[B_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+
+  // Workgroups are dealt round-robin to the 8 XCDs (linear id % 8).  Give each XCD a contiguous
+  // range of the (split, column tile, row tile) space so that tiles sharing weight columns
+  // share that XCD's L2.
+  const int total = tiles_m * tiles_n * split;
+  const int b = blockIdx.x;
+  const int q8 = total / kNumXCDs;
+  const int r8 = total % kNumXCDs;
+  const int xcd = b % kNumXCDs;
+  const int logical = xcd * q8 + (xcd < r8 ? xcd : r8) + b / kNumXCDs;
+  const int per_split = tiles_m * tiles_n;
+  const int z = logical / per_split;
+  const int t = logical % per_split;
+  const int tm = t % tiles_m;
+  const int tn = t / tiles_m;
+
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+  const int k_begin = z * k_split_len;
+  const int nk = k_split_len / kBK;
+
+  // Load assignment (NW == 4): A load i of wave w covers row block i, k-groups 2w and 2w+1
+  // (lane l: row 32i + l%32, k-group 2w + l/32); B load i of wave w covers k-group
+  // (w + 4i) / (BN/64) and the 64 columns of column group (w + 4i) % (BN/64).  Rows and columns
+  // past the matrix edge are clamped to the last valid one: their data only feeds outputs that
+  // are never stored.  Offsets are 32-bit byte offsets (the launcher keeps every operand
+  // slice below 2 GiB).
+  static_assert(NW == 4, "load assignment assumes four waves");
+  uint32_t a_off[A_LOADS / NW];
+#pragma unroll
+  for (int i = 0; i < A_LOADS / NW; ++i) {
+    int row = m0 + i * 32 + (lane & 31);
+    row = row < M ? row : M - 1;
+    a_off[i] = (uint32_t)(row * K + (2 * wave + (lane >> 5)) * 8) * 2u;
+  }
+  constexpr int CG = BN / 64;  // 64-column groups per B stage row
+  int b_col = n0 + ((wave) % CG) * 64 + lane;
+  b_col = b_col < N ? b_col : N - 1;
+  const uint32_t b_lane_off = (uint32_t)(((wave / CG) * N + b_col) * 8) * 2u;
+  const uint32_t b_step = (uint32_t)((NW / CG) * N * 8) * 2u;  // bytes between this wave's loads
+
+  auto issue_stage = [&](int kt, char* sa, char* sb) {
+    const int k0 = k_begin + kt * kBK;
+    const char* a_base = reinterpret_cast<const char*>(A + k0);
+    const char* b_base = reinterpret_cast<const char*>(Bp + (long long)(k0 / 8) * N * 8);
+#pragma unroll
+    for (int i = 0; i < A_LOADS / NW; ++i)
+      load_to_lds16(a_base, a_off[i], sa + (i * NW + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_LOADS / NW; ++i)
+      load_to_lds16(b_base, b_lane_off + i * b_step, sb + (wave + i * NW) * 1024);
+    // Keep the loads at the top of the stage so their latency hides behind its MFMAs.
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int frag_lane = ((lane >> 5) * 32 + (lane & 31)) * 16;  // byte offset within a block
+
+  auto load_frags = [&](const char* sa, const char* sb, int s, bf16x8_t* af, bf16x8_t* bfr) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rb = wm * TM + i;
+      af[i] = *reinterpret_cast<const bf16x8_t*>(sa + (rb * 8 + 2 * s) * 512 + frag_lane);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = wn * WTN + j * 32;
+      bfr[j] = *reinterpret_cast<const bf16x8_t*>(
+          sb + ((2 * s + (lane >> 5)) * BN + col + (lane & 31)) * 16);
+    }
+  };
+  auto mfmas = [&](const bf16x8_t* af, const bf16x8_t* bfr) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+  // Fragments of k-substep s+1 are read from LDS while the MFMAs of substep s run: the
+  // scheduling groups interleave one fragment read after each MFMA, so the LDS latency of the
+  // next substep hides behind the current one.
+  auto interleave = [&]() {
+#pragma unroll
+    for (int g = 0; g < TM + TN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
+  };
+  auto compute_stage = [&](const char* sa, const char* sb) {
+    bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
+    load_frags(sa, sb, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(sa, sb, 1, a1, b1);
+    mfmas(a0, b0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(sa, sb, 2, a0, b0);
+    mfmas(a1, b1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(sa, sb, 3, a1, b1);
+    mfmas(a0, b0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Two stages per loop trip so that each LDS buffer is a distinct object at every access, and
+  // a branch-free steady state (the accumulators stay in AGPRs across the back-edge); the last
+  // one (ODD_STAGES) or two stages are peeled.
+  issue_stage(0, sA0, sB0);
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue_stage(kt + 1, sA1, sB1);
+    compute_stage(sA0, sB0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue_stage(kt + 2, sA0, sB0);
+    compute_stage(sA1, sB1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if constexpr (ODD_STAGES) {
+    compute_stage(sA0, sB0);
+  } else {
+    issue_stage(kt + 1, sA1, sB1);
+    compute_stage(sA0, sB0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    compute_stage(sA1, sB1);
+  }
+
+  // Epilogue.  32x32 fp32 accumulator layout: lane l, element e holds
+  // row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+  const int row_base = m0 + wm * WTM + (lane >> 5) * 4;
+  const int col_base = n0 + wn * WTN + (lane & 31);
+  if (Cf != nullptr) {
+    float* Cz = Cf + (long long)z * plane_stride;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = col_base + j * 32;
+        if (col >= N) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = row_base + i * 32 + (e >> 2) * 8 + (e & 3);
+          if (row < M) Cz[(long long)row * N + col] = acc[i][j][e];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one 32x32 tile live in VGPRs at a time
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = col_base + j * 32;
+        if (col >= N) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = row_base + i * 32 + (e >> 2) * 8 + (e & 3);
+          if (row < M) Cb[(long long)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// Residual add + RMSNorm: one wavefront per row, the row held in registers (NV float4 per lane,
+// H = 256 * NV).  Loads of the whole row are issued before any use so that each wave keeps
+// NV * (1 + planes) 16-byte loads per lane in flight.
+// --------------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float4 round_bf16_4(float4 v) {
+  return make_float4(bf16_to_f32(f32_to_bf16_rne(v.x)), bf16_to_f32(f32_to_bf16_rne(v.y)),
+                     bf16_to_f32(f32_to_bf16_rne(v.z)), bf16_to_f32(f32_to_bf16_rne(v.w)));
+}
+
+template <int NV>
+__global__ void __launch_bounds__(256)
+    add_rmsnorm_kernel(const float* __restrict__ yf, const uint16_t* __restrict__ yb,
+                       int nplanes, long long plane_stride, int round_y, float* __restrict__ r,
+                       const float* __restrict__ w, uint16_t* __restrict__ out, int rows, int H,
+                       float eps, int gemma) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const long long base = (long long)row * H;
+  float4 v[NV];
+  float ss = 0.0f;
+  if (yb != nullptr) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = (i * 64 + lane) * 4;
+      const float4 rv = *reinterpret_cast<const float4*>(r + base + c);
+      const uint2 yv = *reinterpret_cast<const uint2*>(yb + base + c);
+      v[i] = make_float4(rv.x + bf16_to_f32(yv.x & 0xffffu), rv.y + bf16_to_f32(yv.x >> 16),
+                         rv.z + bf16_to_f32(yv.y & 0xffffu), rv.w + bf16_to_f32(yv.y >> 16));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = (i * 64 + lane) * 4;
+      const float4 rv = *reinterpret_cast<const float4*>(r + base + c);
+      float4 yv = *reinterpret_cast<const float4*>(yf + base + c);
+      for (int p = 1; p < nplanes; ++p) {
+        const float4 q = *reinterpret_cast<const float4*>(yf + p * plane_stride + base + c);
+        yv.x += q.x;
+        yv.y += q.y;
+        yv.z += q.z;
+        yv.w += q.w;
+      }
+      if (round_y) yv = round_bf16_4(yv);
+      v[i] = make_float4(rv.x + yv.x, rv.y + yv.y, rv.z + yv.z, rv.w + yv.w);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = (i * 64 + lane) * 4;
+    *reinterpret_cast<float4*>(r + base + c) = v[i];
+    ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  const float g0 = gemma ? 1.0f : 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = (i * 64 + lane) * 4;
+    const float4 g = *reinterpret_cast<const float4*>(w + c);
+    const uint32_t o0 = f32_to_bf16_rne(v[i].x * inv * (g.x + g0));
+    const uint32_t o1 = f32_to_bf16_rne(v[i].y * inv * (g.y + g0));
+    const uint32_t o2 = f32_to_bf16_rne(v[i].z * inv * (g.z + g0));
+    const uint32_t o3 = f32_to_bf16_rne(v[i].w * inv * (g.w + g0));
+    *reinterpret_cast<uint2*>(out + base + c) = make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+  }
+}
+
+// Any H that is a multiple of 64 (and rows wider than the register-resident variants): two
+// passes over the row, the second re-reading the just-written residual.
+__global__ void __launch_bounds__(256)
+    add_rmsnorm_generic_kernel(const float* __restrict__ yf, const uint16_t* __restrict__ yb,
+                               int nplanes, long long plane_stride, int round_y,
+                               float* __restrict__ r, const float* __restrict__ w,
+                               uint16_t* __restrict__ out, int rows, int H, float eps,
+                               int gemma) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const long long base = (long long)row * H;
+  float ss = 0.0f;
+  for (int c = lane; c < H; c += 64) {
+    float y;
+    if (yb != nullptr) {
+      y = bf16_to_f32(yb[base + c]);
+    } else {
+      y = yf[base + c];
+      for (int p = 1; p < nplanes; ++p) y += yf[p * plane_stride + base + c];
+      if (round_y) y = bf16_to_f32(f32_to_bf16_rne(y));
+    }
+    const float v = r[base + c] + y;
+    r[base + c] = v;
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  const float g0 = gemma ? 1.0f : 0.0f;
+  for (int c = lane; c < H; c += 64)
+    out[base + c] = (uint16_t)f32_to_bf16_rne(r[base + c] * inv * (w[c] + g0));
+}
+
+// --------------------------------------------------------------------------------------------
+// Weight preparation: dst[((k/8)*H + h)*8 + k%8] = W[h][k].
+// --------------------------------------------------------------------------------------------
+__global__ void prepare_weight_out_in_kernel(const uint16_t* __restrict__ W,
+                                             uint16_t* __restrict__ dst, int K, int H) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // (k-group, h)
+  const long long total = (long long)(K / 8) * H;
+  if (idx >= total) return;
+  const int kg = (int)(idx / H);
+  const int h = (int)(idx % H);
+  const uint4 v = *reinterpret_cast<const uint4*>(W + (long long)h * K + kg * 8);
+  *reinterpret_cast<uint4*>(dst + idx * 8) = v;
+}
+
+__global__ void prepare_weight_in_out_kernel(const uint16_t* __restrict__ Wt,
+                                             uint16_t* __restrict__ dst, int K, int H) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)(K / 8) * H;
+  if (idx >= total) return;
+  const int kg = (int)(idx / H);
+  const int h = (int)(idx % H);
+  uint32_t p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = Wt[(long long)(kg * 8 + 2 * j) * H + h];
+    const uint32_t hi = Wt[(long long)(kg * 8 + 2 * j + 1) * H + h];
+    p[j] = lo | (hi << 16);
+  }
+  *reinterpret_cast<uint4*>(dst + idx * 8) = make_uint4(p[0], p[1], p[2], p[3]);
+}
+
+// --------------------------------------------------------------------------------------------
+// Debug and tuning helpers.
+// --------------------------------------------------------------------------------------------
+__global__ void delay_kernel(int iters) {
+  for (int i = 0; i < iters; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
+__global__ void fill_nan_kernel(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = __uint_as_float(0x7fc00000u);
+}
+
+__device__ __forceinline__ uint32_t hash32(uint32_t x) {
+  // splitmix-style integer finaliser
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+__global__ void fill_bf16_hash_kernel(uint16_t* __restrict__ p, size_t n, uint32_t seed,
+                                      float scale) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const uint32_t h = hash32((uint32_t)i * 2654435761u ^ seed ^ (uint32_t)(i >> 32));
+    const float u = (float)(h >> 8) * (1.0f / 16777216.0f) * 2.0f - 1.0f;
+    p[i] = (uint16_t)f32_to_bf16_rne(u * scale);
+  }
+}
+
+__global__ void fill_f32_hash_kernel(float* __restrict__ p, size_t n, uint32_t seed, float scale,
+                                     float offset) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const uint32_t h = hash32((uint32_t)i * 2654435761u ^ seed ^ (uint32_t)(i >> 32));
+    const float u = (float)(h >> 8) * (1.0f / 16777216.0f) * 2.0f - 1.0f;
+    p[i] = u * scale + offset;
+  }
+}
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PR_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return PR_OK;
+}
+
+template <int BM, int BN>
+int launch_gemm_t(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
+                  int K, int split, long long plane_stride, hipStream_t s) {
+  constexpr int WM = 2, WN = 2;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int k_len = K / split;
+  const unsigned grid = (unsigned)(tiles_m * tiles_n * split);
+  float* cf = bf16_out ? nullptr : static_cast<float*>(C);
+  uint16_t* cb = bf16_out ? static_cast<uint16_t*>(C) : nullptr;
+  if ((k_len / kBK) % 2)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, true>), dim3(grid), dim3(WM * WN * 64), 0,
+                       s, x, Wp, cf, cb, M, N, K, k_len, plane_stride, tiles_m, tiles_n, split);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, false>), dim3(grid), dim3(WM * WN * 64),
+                       0, s, x, Wp, cf, cb, M, N, K, k_len, plane_stride, tiles_m, tiles_n, split);
+  return check_launch("gemm_bf16_kernel");
+}
+
+template <int NV>
+int launch_addnorm_t(const void* y, int y_bf16, int nplanes, long long plane_stride, int round_y,
+                     float* r, const float* w, uint16_t* out, int rows, int H, float eps,
+                     int gemma, hipStream_t s) {
+  const unsigned grid = (unsigned)((rows + 3) / 4);
+  hipLaunchKernelGGL((add_rmsnorm_kernel<NV>), dim3(grid), dim3(256), 0, s,
+                     y_bf16 ? nullptr : static_cast<const float*>(y),
+                     y_bf16 ? static_cast<const uint16_t*>(y) : nullptr, nplanes, plane_stride,
+                     round_y, r, w, out, rows, H, eps, gemma);
+  return check_launch("add_rmsnorm_kernel");
+}
+
+}  // namespace
+
+int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
+                int K, const GemmCfg& cfg, long long plane_stride, void* stream) {
+  if (M <= 0) return PR_OK;
+  if (K % (kBK * cfg.split) != 0 || N % 64 != 0 || (bf16_out && cfg.split != 1))
+    return fail(PR_ERR_SHAPE, "projection shape M=%d N=%d K=%d split=%d not supported", M, N, K,
+                cfg.split);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cfg.bm == 256 && cfg.bn == 256)
+    return launch_gemm_t<256, 256>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
+  if (cfg.bm == 256 && cfg.bn == 128)
+    return launch_gemm_t<256, 128>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
+  if (cfg.bm == 128 && cfg.bn == 128)
+    return launch_gemm_t<128, 128>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
+  return fail(PR_ERR_INVALID_ARG, "no projection tile %dx%d", cfg.bm, cfg.bn);
+}
+
+int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_stride,
+                       int round_y, float* r, const float* w, uint16_t* out, int rows, int H,
+                       float eps, int gemma, void* stream) {
+  if (rows <= 0) return PR_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (H % 256 == 0) {
+    switch (H / 256) {
+#define PR_NV_CASE(n) \
+  case n:             \
+    return launch_addnorm_t<n>(y, y_bf16, nplanes, plane_stride, round_y, r, w, out, rows, H, eps, gemma, s);
+      PR_NV_CASE(1) PR_NV_CASE(2) PR_NV_CASE(3) PR_NV_CASE(4) PR_NV_CASE(5) PR_NV_CASE(6)
+      PR_NV_CASE(7) PR_NV_CASE(8) PR_NV_CASE(10) PR_NV_CASE(12) PR_NV_CASE(14) PR_NV_CASE(16)
+      PR_NV_CASE(20) PR_NV_CASE(24) PR_NV_CASE(28) PR_NV_CASE(32)
+#undef PR_NV_CASE
+      default:
+        break;
+    }
+  }
+  const unsigned grid = (unsigned)((rows + 3) / 4);
+  hipLaunchKernelGGL(add_rmsnorm_generic_kernel, dim3(grid), dim3(256), 0, s,
+                     y_bf16 ? nullptr : static_cast<const float*>(y),
+                     y_bf16 ? static_cast<const uint16_t*>(y) : nullptr, nplanes, plane_stride,
+                     round_y, r, w, out, rows, H, eps, gemma);
+  return check_launch("add_rmsnorm_generic_kernel");
+}
+
+int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,
+                          void* stream) {
+  const long long total = (long long)(K / 8) * H;
+  if (total == 0) return PR_OK;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (src_layout == PR_WEIGHT_OUT_IN)
+    hipLaunchKernelGGL(prepare_weight_out_in_kernel, dim3(grid), dim3(256), 0, s, src, dst, K, H);
+  else
+    hipLaunchKernelGGL(prepare_weight_in_out_kernel, dim3(grid), dim3(256), 0, s, src, dst, K, H);
+  return check_launch("prepare_weight");
+}
+
+int launch_delay(int iters, void* stream) {
+  hipLaunchKernelGGL(delay_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), iters);
+  return check_launch("delay_kernel");
+}
+
+int launch_fill_nan(float* p, size_t n, void* stream) {
+  if (n == 0) return PR_OK;
+  hipLaunchKernelGGL(fill_nan_kernel, dim3(1024), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     p, n);
+  return check_launch("fill_nan_kernel");
+}
+
+int launch_fill_bf16_hash(uint16_t* p, size_t n, uint32_t seed, float scale, void* stream) {
+  if (n == 0) return PR_OK;
+  hipLaunchKernelGGL(fill_bf16_hash_kernel, dim3(2048), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), p, n, seed, scale);
+  return check_launch("fill_bf16_hash_kernel");
+}
+
+int launch_fill_f32_hash(float* p, size_t n, uint32_t seed, float scale, float offset,
+                         void* stream) {
+  if (n == 0) return PR_OK;
+  hipLaunchKernelGGL(fill_f32_hash_kernel, dim3(2048), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), p, n, seed, scale, offset);
+  return check_launch("fill_f32_hash_kernel");
+}
+
+}  // namespace pr

@@ -1,0 +1,388 @@
+// Runtime of the library: per-device resources (two streams, six slot events, the three-slot
+// workspace), the microchunk pipeline executor, the conventional path and the autotuner.
+//
+// Pipeline ("TPSP Design" page, section 3, Microchunk pipeline): chunk c's projection runs on
+// stream A into slot c % 3 and records ready[slot]; stream B waits for it, runs the residual
+// add + RMSNorm of the chunk's valid rows and records done[slot]; stream A waits done[slot]
+// before chunk c + 3 overwrites the slot.  Both streams start after the caller's stream
+// (entry event) and the caller's stream waits for the last done event, so the call is ordered
+// on the caller's stream like a single kernel and never blocks the host.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "pr_internal.h"
+
+namespace pr {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DevCtx {
+  int device = -1;
+  hipStream_t sA = nullptr;  // projection stream
+  hipStream_t sB = nullptr;  // add/norm stream
+  hipEvent_t entry = nullptr;
+  hipEvent_t ready[PR_NUM_SLOTS] = {};
+  hipEvent_t done[PR_NUM_SLOTS] = {};
+  float* slots = nullptr;  // PR_NUM_SLOTS slots of slot_elems fp32 each
+  size_t slot_elems = 0;
+  void* conv = nullptr;  // conventional path: bf16 y or fp32 partial planes
+  size_t conv_bytes = 0;
+  uint16_t* out_ws = nullptr;  // borrowed output
+  size_t out_ws_bytes = 0;
+  const uint16_t* last_borrowed = nullptr;
+  // kernel timing (pr_profile_enable)
+  std::vector<hipEvent_t> ev_pool;
+  struct Timed {
+    hipEvent_t start, stop;
+    int kind;  // 0 projection, 1 add/norm
+  };
+  std::vector<Timed> pending;
+  double ms[2] = {0, 0};
+  int launches[2] = {0, 0};
+};
+
+bool g_profile = false;
+
+std::mutex g_ctx_mu;
+DevCtx* g_ctx[kMaxDevices] = {};
+
+#define PR_HIP(call)                                                                  \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess) return fail(PR_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+#define PR_TRY(call)              \
+  do {                            \
+    int rc_ = (call);             \
+    if (rc_ != PR_OK) return rc_; \
+  } while (0)
+
+int take_event(DevCtx* c, hipEvent_t* e) {
+  if (!c->ev_pool.empty()) {
+    *e = c->ev_pool.back();
+    c->ev_pool.pop_back();
+    return PR_OK;
+  }
+  PR_HIP(hipEventCreate(e));
+  return PR_OK;
+}
+
+// Runs `launch` bracketed by timing events on stream s when profiling is on.
+template <typename F>
+int timed(DevCtx* c, int kind, hipStream_t s, F&& launch) {
+  if (!g_profile) return launch();
+  DevCtx::Timed t{nullptr, nullptr, kind};
+  PR_TRY(take_event(c, &t.start));
+  PR_TRY(take_event(c, &t.stop));
+  PR_HIP(hipEventRecord(t.start, s));
+  const int rc = launch();
+  PR_HIP(hipEventRecord(t.stop, s));
+  c->pending.push_back(t);
+  return rc;
+}
+
+int env_int(const char* name) {
+  const char* v = std::getenv(name);
+  return (v != nullptr && v[0] != '\0') ? std::atoi(v) : 0;
+}
+
+bool fault_injected() {
+  const char* v = std::getenv("PR_FAULT_INJECT");
+  return v != nullptr && std::strcmp(v, "launch") == 0;
+}
+
+int get_ctx(DevCtx** out) {
+  int dev = -1;
+  PR_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PR_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lk(g_ctx_mu);
+  if (g_ctx[dev] != nullptr) {
+    *out = g_ctx[dev];
+    return PR_OK;
+  }
+  hipDeviceProp_t prop;
+  PR_HIP(hipGetDeviceProperties(&prop, dev));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(PR_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev,
+                prop.gcnArchName);
+  DevCtx* c = new DevCtx();
+  c->device = dev;
+  // Default-priority, non-blocking streams.
+  PR_HIP(hipStreamCreateWithFlags(&c->sA, hipStreamNonBlocking));
+  PR_HIP(hipStreamCreateWithFlags(&c->sB, hipStreamNonBlocking));
+  PR_HIP(hipEventCreateWithFlags(&c->entry, hipEventDisableTiming));
+  for (int s = 0; s < PR_NUM_SLOTS; ++s) {
+    PR_HIP(hipEventCreateWithFlags(&c->ready[s], hipEventDisableTiming));
+    PR_HIP(hipEventCreateWithFlags(&c->done[s], hipEventDisableTiming));
+  }
+  g_ctx[dev] = c;
+  *out = c;
+  return PR_OK;
+}
+
+// Grow a device buffer.  Growing waits for all outstanding work on the device first, since
+// earlier calls may still be reading the old buffer.
+int grow(void** p, size_t* have, size_t need) {
+  if (need <= *have) return PR_OK;
+  if (*p != nullptr) {
+    PR_HIP(hipDeviceSynchronize());
+    PR_HIP(hipFree(*p));
+    *p = nullptr;
+    *have = 0;
+  }
+  const hipError_t e = hipMalloc(p, need);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *p = nullptr;
+    return fail(PR_ERR_NOMEM, "workspace of %zu bytes: %s", need, hipGetErrorString(e));
+  }
+  *have = need;
+  return PR_OK;
+}
+
+// Projection over M rows; launches are split by rows so that one launch's x slice stays
+// below 2^30 elements (the kernel uses 32-bit offsets).
+int gemm_rows(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N, int K,
+              const GemmCfg& cfg, long long plane_stride, hipStream_t s) {
+  if (fault_injected()) return fail(PR_ERR_HIP, "injected launch failure (PR_FAULT_INJECT)");
+  long long rows_per = ((1LL << 30) / K) / cfg.bm * cfg.bm;
+  if (rows_per <= 0) return fail(PR_ERR_SHAPE, "K=%d too large", K);
+  for (long long r0 = 0; r0 < M; r0 += rows_per) {
+    const int rows = (int)std::min<long long>(rows_per, M - r0);
+    void* Cr = bf16_out ? (void*)(static_cast<uint16_t*>(C) + r0 * N)
+                        : (void*)(static_cast<float*>(C) + r0 * N);
+    PR_TRY(launch_gemm(x + r0 * K, Wp, Cr, bf16_out, rows, N, K, cfg, plane_stride, s));
+  }
+  return PR_OK;
+}
+
+int check_common(const uint16_t* x, const uint16_t* W, float* r, const float* w, float eps,
+                 int T, int K, int H, int microchunk, int norm_kind, uint16_t* out) {
+  return pr_validate(x, W, r, w, eps, T, K, H, microchunk, norm_kind, out);
+}
+
+uint16_t* resolve_out(DevCtx* c, uint16_t* out, int T, int H, int* rc) {
+  *rc = PR_OK;
+  if (out != nullptr) return out;
+  *rc = grow(reinterpret_cast<void**>(&c->out_ws), &c->out_ws_bytes, (size_t)T * H * 2);
+  if (*rc != PR_OK) return nullptr;
+  c->last_borrowed = c->out_ws;
+  return c->out_ws;
+}
+
+int run_conventional(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const float* w,
+                     float eps, int T, int K, int H, int norm_kind, uint16_t* out,
+                     const pr_decision& d, hipStream_t s) {
+  GemmCfg g;
+  g.bm = d.gemm_bm;
+  g.bn = d.gemm_bn;
+  g.split = d.split_k;
+  const long long plane = (long long)T * H;
+  if (g.split == 1) {
+    PR_TRY(grow(&c->conv, &c->conv_bytes, (size_t)plane * 2));
+    PR_TRY(timed(c, 0, s, [&] { return gemm_rows(x, W, c->conv, true, T, H, K, g, plane, s); }));
+    PR_TRY(timed(c, 1, s, [&] {
+      return launch_add_rmsnorm(c->conv, 1, 1, plane, 0, r, w, out, T, H, eps,
+                                norm_kind == PR_NORM_GEMMA, s);
+    }));
+  } else {
+    // K split: fp32 partial planes, summed and rounded to bf16 before the add.
+    PR_TRY(grow(&c->conv, &c->conv_bytes, (size_t)plane * 4 * g.split));
+    PR_TRY(timed(c, 0, s, [&] { return gemm_rows(x, W, c->conv, false, T, H, K, g, plane, s); }));
+    PR_TRY(timed(c, 1, s, [&] {
+      return launch_add_rmsnorm(c->conv, 0, g.split, plane, 1, r, w, out, T, H, eps,
+                                norm_kind == PR_NORM_GEMMA, s);
+    }));
+  }
+  return PR_OK;
+}
+
+int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const float* w,
+                 float eps, int T, int K, int H, int norm_kind, uint16_t* out,
+                 const pr_decision& d, hipStream_t caller) {
+  const int mc = d.microchunk;
+  GemmCfg g;
+  g.bm = d.gemm_bm;
+  g.bn = d.gemm_bn;
+  g.split = d.split_k;
+  const int rows_max = std::min(mc, T);
+  const long long plane = (long long)rows_max * H;  // elements of one partial plane
+  const size_t slot_elems = (size_t)plane * g.split;
+  if (slot_elems > c->slot_elems) {
+    size_t have = c->slot_elems * PR_NUM_SLOTS * sizeof(float);
+    void* p = c->slots;
+    PR_TRY(grow(&p, &have, slot_elems * PR_NUM_SLOTS * sizeof(float)));
+    c->slots = static_cast<float*>(p);
+    c->slot_elems = slot_elems;
+  }
+  const int delay = env_int("PR_DEBUG_DELAY");
+  const bool poison = env_int("PR_DEBUG_POISON") != 0;
+  const int gemma = norm_kind == PR_NORM_GEMMA;
+
+  std::vector<pr_plan_op> ops(8 + 6 * (size_t)d.n_chunks);
+  const int n = pr_plan(T, mc, ops.data(), (int)ops.size());
+  if (n < 0) return n;
+  auto stream_of = [&](int id) { return id == 0 ? caller : (id == 1 ? c->sA : c->sB); };
+  for (int i = 0; i < n; ++i) {
+    const pr_plan_op& op = ops[i];
+    float* slot = op.slot >= 0 ? c->slots + (size_t)op.slot * c->slot_elems : nullptr;
+    const long long row0 = (long long)op.chunk * mc;
+    switch (op.op) {
+      case PR_OP_RECORD_ENTRY:
+        PR_HIP(hipEventRecord(c->entry, caller));
+        break;
+      case PR_OP_WAIT_ENTRY:
+        PR_HIP(hipStreamWaitEvent(stream_of(op.stream), c->entry, 0));
+        break;
+      case PR_OP_WAIT_DONE:
+        PR_HIP(hipStreamWaitEvent(c->sA, c->done[op.slot], 0));
+        break;
+      case PR_OP_GEMM:
+        if (delay > 0) PR_TRY(launch_delay(delay, c->sA));
+        PR_TRY(timed(c, 0, c->sA, [&] {
+          return gemm_rows(x + row0 * K, W, slot, false, op.rows, H, K, g,
+                           (long long)op.rows * H, c->sA);
+        }));
+        break;
+      case PR_OP_RECORD_READY:
+        PR_HIP(hipEventRecord(c->ready[op.slot], c->sA));
+        break;
+      case PR_OP_WAIT_READY:
+        PR_HIP(hipStreamWaitEvent(c->sB, c->ready[op.slot], 0));
+        break;
+      case PR_OP_ADDNORM:
+        if (delay > 0) PR_TRY(launch_delay(delay, c->sB));
+        PR_TRY(timed(c, 1, c->sB, [&] {
+          return launch_add_rmsnorm(slot, 0, g.split, (long long)op.rows * H, 0, r + row0 * H,
+                                    w, out + row0 * H, op.rows, H, eps, gemma, c->sB);
+        }));
+        if (poison) PR_TRY(launch_fill_nan(slot, c->slot_elems, c->sB));
+        break;
+      case PR_OP_RECORD_DONE:
+        PR_HIP(hipEventRecord(c->done[op.slot], c->sB));
+        break;
+      case PR_OP_JOIN:
+        PR_HIP(hipStreamWaitEvent(caller, c->done[op.slot], 0));
+        break;
+      default:
+        return fail(PR_ERR_INVALID_ARG, "bad plan op %d", op.op);
+    }
+  }
+  return PR_OK;
+}
+
+int run_call(const uint16_t* x, const uint16_t* W, float* r, const float* w, float eps, int T,
+             int K, int H, int microchunk, int norm_kind, uint16_t* out, void* stream) {
+  clear_error();
+  PR_TRY(check_common(x, W, r, w, eps, T, K, H, microchunk < 0 ? 0 : microchunk, norm_kind, out));
+  pr_decision d;
+  PR_TRY(decide(T, K, H, microchunk, &d));
+  if (log_enabled())
+    std::fprintf(stderr,
+                 "[proj_add_rmsnorm] T=%d K=%d H=%d path=%s mc=%d chunks=%d tile=%dx%d "
+                 "split=%d reason=%d\n",
+                 T, K, H, d.path == PR_PATH_FUSED ? "fused" : "conventional", d.microchunk,
+                 d.n_chunks, d.gemm_bm, d.gemm_bn, d.split_k, d.reason);
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  if (T == 0) return PR_OK;
+  int rc = PR_OK;
+  out = resolve_out(c, out, T, H, &rc);
+  if (rc != PR_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d.path == PR_PATH_FUSED) return run_pipeline(c, x, W, r, w, eps, T, K, H, norm_kind, out, d, s);
+  return run_conventional(c, x, W, r, w, eps, T, K, H, norm_kind, out, d, s);
+}
+
+}  // namespace
+}  // namespace pr
+
+using namespace pr;
+
+extern "C" {
+
+int pr_prepare_weight(const uint16_t* W_src, int src_layout, uint16_t* W_prep, int K, int H,
+                      void* stream) {
+  clear_error();
+  if (W_src == nullptr || W_prep == nullptr) return fail(PR_ERR_INVALID_ARG, "null weight");
+  if (W_src == W_prep) return fail(PR_ERR_INVALID_ARG, "W_prep must not alias W_src");
+  if (src_layout != PR_WEIGHT_OUT_IN && src_layout != PR_WEIGHT_IN_OUT)
+    return fail(PR_ERR_INVALID_ARG, "unknown weight layout %d", src_layout);
+  if (K <= 0 || H <= 0 || K % 64 != 0 || H % 64 != 0)
+    return fail(PR_ERR_SHAPE, "K=%d and H=%d must be positive multiples of 64", K, H);
+  if ((long long)K * H > (1LL << 30)) return fail(PR_ERR_SHAPE, "weight too large");
+  if ((uintptr_t)W_src % 16 != 0 || (uintptr_t)W_prep % 16 != 0)
+    return fail(PR_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  (void)c;
+  return launch_prepare_weight(W_src, src_layout, W_prep, K, H, stream);
+}
+
+int proj_add_rmsnorm(const uint16_t* x, const uint16_t* W, float* residual_inout,
+                     const float* norm_w, float eps, int T, int K, int H, int microchunk,
+                     int norm_kind, uint16_t* out, void* stream) {
+  if (microchunk < 0) {
+    clear_error();
+    return fail(PR_ERR_MICROCHUNK, "microchunk=%d must be >= 0", microchunk);
+  }
+  return run_call(x, W, residual_inout, norm_w, eps, T, K, H, microchunk, norm_kind, out, stream);
+}
+
+int proj_add_rmsnorm_unfused(const uint16_t* x, const uint16_t* W, float* residual_inout,
+                             const float* norm_w, float eps, int T, int K, int H, int norm_kind,
+                             uint16_t* out, void* stream) {
+  return run_call(x, W, residual_inout, norm_w, eps, T, K, H, -1, norm_kind, out, stream);
+}
+
+int pr_profile_enable(int on) {
+  clear_error();
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  PR_TRY(pr_profile_read(nullptr));  // drain what is pending
+  c->ms[0] = c->ms[1] = 0;
+  c->launches[0] = c->launches[1] = 0;
+  g_profile = on != 0;
+  return PR_OK;
+}
+
+int pr_profile_read(pr_profile* p) {
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  for (const DevCtx::Timed& t : c->pending) {
+    PR_HIP(hipEventSynchronize(t.stop));
+    float ms = 0;
+    PR_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
+    c->ms[t.kind] += ms;
+    c->launches[t.kind] += 1;
+    c->ev_pool.push_back(t.start);
+    c->ev_pool.push_back(t.stop);
+  }
+  c->pending.clear();
+  if (p != nullptr) {
+    p->gemm_ms = c->ms[0];
+    p->gemm_launches = c->launches[0];
+    p->addnorm_ms = c->ms[1];
+    p->addnorm_launches = c->launches[1];
+  }
+  return PR_OK;
+}
+
+const uint16_t* pr_workspace_output(void) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_ctx_mu);
+  return g_ctx[dev] != nullptr ? g_ctx[dev]->last_borrowed : nullptr;
+}
+
+}  // extern "C"

@@ -1,0 +1,263 @@
+// Autotuner ("TPSP Design" page, section 3, Profiling and fallback): after the weights load,
+// each shape group (o_proj-like, down_proj-like) is profiled on synthetic device data; every
+// chunk-size candidate is numerically checked against the conventional path before it is
+// timed, and the token threshold compares the sum over groups of conventional and best fused
+// timings (pr_threshold_from_timings).  With both overrides set nothing is profiled.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "pr_internal.h"
+
+namespace pr {
+namespace {
+
+#define PR_HIP(call)                                                                  \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess) return fail(PR_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+#define PR_TRY(call)              \
+  do {                            \
+    int rc_ = (call);             \
+    if (rc_ != PR_OK) return rc_; \
+  } while (0)
+
+struct DevBuf {
+  void* p = nullptr;
+  ~DevBuf() {
+    if (p != nullptr) (void)hipFree(p);
+  }
+  int alloc(size_t bytes) {
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      p = nullptr;
+      return fail(PR_ERR_NOMEM, "tuning buffer of %zu bytes", bytes);
+    }
+    return PR_OK;
+  }
+};
+
+float bf16f(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Candidate check against the conventional result on sampled rows.  The two paths differ by the
+// bf16 rounding of y in the conventional one, so the residual may differ per element by half a
+// bf16 ulp of y (2^-8 |y|, with y = r_new - r_old) plus fp32 rounding.
+bool candidate_ok(const std::vector<uint16_t>& out_f, const std::vector<uint16_t>& out_c,
+                  const std::vector<float>& r_f, const std::vector<float>& r_c,
+                  const std::vector<float>& r_old) {
+  double d2 = 0, n2 = 0, dmax = 0;
+  for (size_t i = 0; i < out_f.size(); ++i) {
+    const double a = bf16f(out_f[i]), b = bf16f(out_c[i]);
+    if (!std::isfinite(a)) return false;
+    d2 += (a - b) * (a - b);
+    n2 += b * b;
+    dmax = std::max(dmax, std::fabs(a - b));
+  }
+  if (dmax > 2e-2 || d2 > 25e-6 * std::max(n2, 1e-30)) return false;
+  for (size_t i = 0; i < r_f.size(); ++i) {
+    if (!std::isfinite(r_f[i])) return false;
+    const double y = std::fabs((double)r_f[i] - r_old[i]);
+    const double bound = std::ldexp(y, -8) + 1e-5 * (1.0 + std::fabs((double)r_f[i]));
+    if (std::fabs((double)r_f[i] - r_c[i]) > bound) return false;
+  }
+  return true;
+}
+
+struct Stats {
+  double median = -1, p10 = 0, p90 = 0;
+};
+
+template <typename F>
+int time_calls(F&& call, int reps, hipStream_t s, Stats* st) {
+  hipEvent_t e0, e1;
+  PR_HIP(hipEventCreate(&e0));
+  PR_HIP(hipEventCreate(&e1));
+  std::vector<double> t;
+  int rc = PR_OK;
+  for (int i = 0; i < 2 && rc == PR_OK; ++i) rc = call();  // warm-up
+  for (int i = 0; i < reps && rc == PR_OK; ++i) {
+    (void)hipEventRecord(e0, s);
+    rc = call();
+    (void)hipEventRecord(e1, s);
+    if (rc != PR_OK) break;
+    if (hipEventSynchronize(e1) != hipSuccess) {
+      rc = fail(PR_ERR_HIP, "timing sync failed");
+      break;
+    }
+    float ms = 0;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    t.push_back(ms * 1e-3);
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (rc != PR_OK) return rc;
+  std::sort(t.begin(), t.end());
+  st->median = t[t.size() / 2];
+  st->p10 = t[t.size() / 10];
+  st->p90 = t[(t.size() * 9) / 10 < t.size() ? (t.size() * 9) / 10 : t.size() - 1];
+  return PR_OK;
+}
+
+}  // namespace
+}  // namespace pr
+
+using namespace pr;
+
+extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
+                       const int* T_grid, int nT, const int* mc_cand, int nmc, int reps,
+                       pr_tune_report* report, double* timings_out, void* stream) {
+  clear_error();
+  if (Ks == nullptr || Hs == nullptr || ngroups <= 0 || T_grid == nullptr || nT <= 0 ||
+      mc_cand == nullptr || nmc <= 0 || reps <= 0)
+    return fail(PR_ERR_INVALID_ARG, "bad tuning arguments");
+  if (norm_kind != PR_NORM_STANDARD && norm_kind != PR_NORM_GEMMA)
+    return fail(PR_ERR_INVALID_ARG, "unknown norm_kind %d", norm_kind);
+  for (int i = 0; i < nT; ++i)
+    if (T_grid[i] <= 0 || (i > 0 && T_grid[i] <= T_grid[i - 1]))
+      return fail(PR_ERR_INVALID_ARG, "T_grid must be positive and ascending");
+  for (int j = 0; j < nmc; ++j)
+    if (mc_cand[j] <= 0 || mc_cand[j] > PR_MAX_MICROCHUNK)
+      return fail(PR_ERR_MICROCHUNK, "candidate microchunk %d out of range", mc_cand[j]);
+  int mc_ov = 0, thr_ov = 0;
+  PR_TRY(read_overrides(&mc_ov, &thr_ov));
+  const char* ev_mc = std::getenv("PR_MICROCHUNK_TOKENS");
+  const char* ev_thr = std::getenv("PR_THRESHOLD_TOKENS");
+  const bool have_mc = ev_mc != nullptr && ev_mc[0] != '\0';
+  const bool have_thr = ev_thr != nullptr && ev_thr[0] != '\0';
+  pr_tune_report rep_local = {INT32_MAX, T_grid[nT - 1], 0, 0};
+  if (have_mc && have_thr) {
+    // Both overrides: no scan and no numerical check; install them for every group.
+    std::vector<int> mcs(nT, mc_ov);
+    for (int g = 0; g < ngroups; ++g)
+      PR_TRY(pr_set_tuning(Ks[g], Hs[g], thr_ov, T_grid[nT - 1], T_grid, mcs.data(), nT));
+    rep_local.threshold_tokens = thr_ov;
+    if (report != nullptr) *report = rep_local;
+    return PR_OK;
+  }
+  std::vector<int> cands(mc_cand, mc_cand + nmc);
+  if (have_mc) cands.assign(1, mc_ov);
+  const int ncols = 2 + nmc;
+  std::vector<double> t_conv(ngroups * nT, -1), t_fused(ngroups * nT, -1),
+      spread(ngroups * nT, 0);
+  std::vector<std::vector<int>> best_mc(ngroups, std::vector<int>(nT, cands[0]));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int Tmax = T_grid[nT - 1];
+  const int gemma = norm_kind == PR_NORM_GEMMA;
+
+  for (int g = 0; g < ngroups; ++g) {
+    const int K = Ks[g], H = Hs[g];
+    if (K <= 0 || H <= 0 || K % 64 || H % 64) return fail(PR_ERR_SHAPE, "group %d shape", g);
+    DevBuf x, Wsrc, Wp, r0, r, w, out;
+    PR_TRY(x.alloc((size_t)Tmax * K * 2));
+    PR_TRY(Wsrc.alloc((size_t)K * H * 2));
+    PR_TRY(Wp.alloc((size_t)K * H * 2));
+    PR_TRY(r0.alloc((size_t)Tmax * H * 4));
+    PR_TRY(r.alloc((size_t)Tmax * H * 4));
+    PR_TRY(w.alloc((size_t)H * 4));
+    PR_TRY(out.alloc((size_t)Tmax * H * 2));
+    // Uniform draws scaled to the variances of the workloads: x, r ~ var 1; W ~ var 1/K.
+    const float u1 = std::sqrt(3.0f);
+    PR_TRY(launch_fill_bf16_hash((uint16_t*)x.p, (size_t)Tmax * K, 11u + g, u1, s));
+    PR_TRY(launch_fill_bf16_hash((uint16_t*)Wsrc.p, (size_t)K * H, 23u + g, u1 / std::sqrt((float)K), s));
+    PR_TRY(launch_fill_f32_hash((float*)r0.p, (size_t)Tmax * H, 37u + g, u1, 0.0f, s));
+    PR_TRY(launch_fill_f32_hash((float*)w.p, (size_t)H, 41u + g, 0.17f, gemma ? 0.0f : 1.0f, s));
+    PR_TRY(pr_prepare_weight((const uint16_t*)Wsrc.p, PR_WEIGHT_OUT_IN, (uint16_t*)Wp.p, K, H, s));
+    PR_HIP(hipStreamSynchronize(s));
+
+    for (int i = 0; i < nT; ++i) {
+      const int T = T_grid[i];
+      const size_t rows_chk = (size_t)std::min(T, 256);
+      // rows checked: the first rows_chk and the last rows_chk (covers the padded tail chunk)
+      const size_t tail0 = (size_t)T - rows_chk;
+      auto fetch = [&](std::vector<uint16_t>& o, std::vector<float>& rr) -> int {
+        o.resize(2 * rows_chk * H);
+        rr.resize(2 * rows_chk * H);
+        PR_HIP(hipMemcpyAsync(o.data(), out.p, rows_chk * H * 2, hipMemcpyDeviceToHost, s));
+        PR_HIP(hipMemcpyAsync(o.data() + rows_chk * H, (uint16_t*)out.p + tail0 * H,
+                              rows_chk * H * 2, hipMemcpyDeviceToHost, s));
+        PR_HIP(hipMemcpyAsync(rr.data(), r.p, rows_chk * H * 4, hipMemcpyDeviceToHost, s));
+        PR_HIP(hipMemcpyAsync(rr.data() + rows_chk * H, (float*)r.p + tail0 * H,
+                              rows_chk * H * 4, hipMemcpyDeviceToHost, s));
+        PR_HIP(hipStreamSynchronize(s));
+        return PR_OK;
+      };
+      auto reset_r = [&]() -> int {
+        PR_HIP(hipMemcpyAsync(r.p, r0.p, (size_t)T * H * 4, hipMemcpyDeviceToDevice, s));
+        return PR_OK;
+      };
+      std::vector<float> r_old(2 * rows_chk * H);
+      PR_HIP(hipMemcpyAsync(r_old.data(), r0.p, rows_chk * H * 4, hipMemcpyDeviceToHost, s));
+      PR_HIP(hipMemcpyAsync(r_old.data() + rows_chk * H, (float*)r0.p + tail0 * H,
+                            rows_chk * H * 4, hipMemcpyDeviceToHost, s));
+      auto conv_call = [&]() {
+        return proj_add_rmsnorm_unfused((const uint16_t*)x.p, (const uint16_t*)Wp.p, (float*)r.p,
+                                        (const float*)w.p, 1e-5f, T, K, H, norm_kind,
+                                        (uint16_t*)out.p, s);
+      };
+      std::vector<uint16_t> out_c, out_f;
+      std::vector<float> r_c, r_f;
+      PR_TRY(reset_r());
+      PR_TRY(conv_call());
+      PR_TRY(fetch(out_c, r_c));
+      Stats sc;
+      PR_TRY(time_calls(conv_call, reps, s, &sc));
+      t_conv[g * nT + i] = sc.median;
+      if (timings_out != nullptr) timings_out[(g * nT + i) * ncols + 0] = sc.median;
+      double best = -1, best_spread = 0;
+      for (int j = 0; j < nmc; ++j)
+        if (timings_out != nullptr) timings_out[(g * nT + i) * ncols + 2 + j] = -1;
+      for (size_t j = 0; j < cands.size(); ++j) {
+        const int mc = cands[j];
+        if (mc > std::min(T, PR_MAX_MICROCHUNK)) continue;
+        auto fused_call = [&]() {
+          return proj_add_rmsnorm((const uint16_t*)x.p, (const uint16_t*)Wp.p, (float*)r.p,
+                                  (const float*)w.p, 1e-5f, T, K, H, mc, norm_kind,
+                                  (uint16_t*)out.p, s);
+        };
+        PR_TRY(reset_r());
+        PR_TRY(fused_call());
+        PR_TRY(fetch(out_f, r_f));
+        if (!candidate_ok(out_f, out_c, r_f, r_c, r_old)) {
+          ++rep_local.n_rejected;
+          continue;
+        }
+        ++rep_local.n_checked;
+        Stats sf;
+        PR_TRY(time_calls(fused_call, reps, s, &sf));
+        if (timings_out != nullptr) {
+          for (int jj = 0; jj < nmc; ++jj)
+            if (mc_cand[jj] == mc) timings_out[(g * nT + i) * ncols + 2 + jj] = sf.median;
+        }
+        if (best < 0 || sf.median < best) {
+          best = sf.median;
+          best_spread = sf.p90 - sf.p10;
+          best_mc[g][i] = mc;
+        }
+      }
+      t_fused[g * nT + i] = best;
+      spread[g * nT + i] = best_spread;
+      if (timings_out != nullptr) timings_out[(g * nT + i) * ncols + 1] = best;
+    }
+  }
+  int thr = INT32_MAX;
+  PR_TRY(pr_threshold_from_timings(ngroups, nT, T_grid, t_conv.data(), t_fused.data(),
+                                   spread.data(), &thr));
+  for (int g = 0; g < ngroups; ++g)
+    PR_TRY(pr_set_tuning(Ks[g], Hs[g], thr, Tmax, T_grid, best_mc[g].data(), nT));
+  rep_local.threshold_tokens = thr;
+  if (report != nullptr) *report = rep_local;
+  return PR_OK;
+}

@@ -1,0 +1,80 @@
+"""Helpers shared by the GPU tests: device copies of seeded inputs and calls through the C ABI."""
+import numpy as np
+import torch
+
+import projection_residual_rmsnorm_amd as pr
+
+DEV = "cuda:0"
+
+
+def i16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+class _DevArray:
+    """Exposes a raw device pointer to torch through the CUDA array interface."""
+
+    def __init__(self, ptr, shape):
+        self.__cuda_array_interface__ = {"shape": shape, "typestr": "<i2", "data": (ptr, False),
+                                         "version": 2, "strides": None}
+
+
+def borrowed(ptr: int, T: int, H: int) -> np.ndarray:
+    """Copy of the library's borrowed output workspace (bf16 bits [T, H])."""
+    t = torch.as_tensor(_DevArray(ptr, (T, H)), device=DEV)
+    return bits(t.clone())
+
+
+class Device:
+    """Device copies of one input set: x, the prepared weight, residual, norm weight."""
+
+    def __init__(self, d: dict, extra_rows: int = 0, pad_x_nan: bool = False,
+                 weight_layout: int = pr.PR_WEIGHT_OUT_IN):
+        self.d = d
+        self.T, self.K, self.H = d["T"], d["K"], d["H"]
+        x = d["x"]
+        if extra_rows:
+            fill = 0x7FC0 if pad_x_nan else 0
+            x = np.concatenate([x, np.full((extra_rows, self.K), fill, np.uint16)])
+        self.x = i16(x)
+        W = d["W"] if weight_layout == pr.PR_WEIGHT_OUT_IN else np.ascontiguousarray(d["W"].T)
+        W_src = i16(W)
+        self.Wp = torch.empty(self.K * self.H, dtype=torch.int16, device=DEV)
+        pr.pr_prepare_weight(W_src, weight_layout, self.Wp, self.K, self.H)
+        self.w = f32(d["norm_w"])
+        self.extra = extra_rows
+        self.reset()
+
+    def reset(self, sentinel: float = 12345.0):
+        r = self.d["residual"]
+        if self.extra:
+            r = np.concatenate([r, np.full((self.extra, self.H), sentinel, np.float32)])
+        self.r = f32(r)
+        # sentinel output bit pattern (bf16 0x7BAD, about 1.8e36)
+        self.out = torch.full((self.T + self.extra, self.H), 0x7BAD, dtype=torch.int16,
+                              device=DEV)
+
+    def run(self, microchunk=None, out="own", stream=None):
+        """microchunk=None: conventional entry point; else proj_add_rmsnorm(microchunk)."""
+        o = self.out if out == "own" else None
+        d = self.d
+        if microchunk is None:
+            pr.proj_add_rmsnorm_unfused(self.x, self.Wp, self.r, self.w, d["eps"], self.T, self.K,
+                                        self.H, d["norm_kind"], o, stream)
+        else:
+            pr.proj_add_rmsnorm(self.x, self.Wp, self.r, self.w, d["eps"], self.T, self.K, self.H,
+                                microchunk, d["norm_kind"], o, stream)
+        torch.cuda.synchronize()
+        if o is None:
+            ptr = pr.pr_workspace_output()
+            assert ptr is not None
+            return self.r[:self.T].cpu().numpy(), borrowed(ptr, self.T, self.H)
+        return self.r[:self.T].cpu().numpy(), bits(self.out[:self.T])

@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
+
+Tolerances: bf16 output max |delta| <= 2e-2 and relative L2 <= 5e-3; fp32 residual relative
+L2 <= 1e-3 (oracle.within_tolerance).  The fused path is compared with the oracle's fused
+mode (unrounded projection), the conventional path with its conventional mode (projection
+rounded to bf16).  Integer-valued inputs pin the projection bitwise.  Full-size workloads are
+checked on sampled rows (rows are independent, so a row subset is an exact check of those
+rows), always including the last chunk's rows.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import projection_residual_rmsnorm_amd as pr
+import synth
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpu_util import DEV, Device, bits, f32, i16
+
+
+@pytest.fixture(autouse=True)
+def _env(monkeypatch):
+    for k in ("PR_MICROCHUNK_TOKENS", "PR_THRESHOLD_TOKENS", "PR_FORCE_TILE", "PR_FORCE_SPLIT",
+              "PR_DEBUG_POISON", "PR_DEBUG_DELAY", "PR_FAULT_INJECT"):
+        monkeypatch.delenv(k, raising=False)
+    pr.pr_clear_tuning()
+    yield
+    pr.pr_clear_tuning()
+
+
+def _check(d, r_dev, out_bits, mode, rows=None):
+    x, r = d["x"], d["residual"]
+    if rows is not None:
+        x, r = x[rows], r[rows]
+        r_dev, out_bits = r_dev[rows], out_bits[rows]
+    r_ref, out_ref = oracle.proj_add_rmsnorm(x, d["W"], r, d["norm_w"], d["eps"], d["norm_kind"],
+                                             mode)
+    err = oracle.compare(r_dev, out_bits, r_ref, out_ref)
+    assert oracle.within_tolerance(err), err
+    return err
+
+
+TILES = [("256x256", 1), ("256x128", 1), ("128x128", 1), ("256x256", 2), ("128x128", 4),
+         ("256x128", 8)]
+
+
+# ------------------------------------------------------------------------ bitwise projection
+@pytest.mark.parametrize("tile,split", TILES)
+def test_integer_projection_is_exact(monkeypatch, tile, split):
+    """Small integers: every partial sum is exact in fp32, so the residual must match bitwise.
+
+    T=300 spans two 256-row tiles with a ragged tail; H=768 spans 3-6 column tiles."""
+    monkeypatch.setenv("PR_FORCE_TILE", tile)
+    monkeypatch.setenv("PR_FORCE_SPLIT", str(split))
+    d = synth.integer_inputs(300, 1024, 768, seed=3)
+    dev = Device(d)
+    for mc, mode in ((None, "conventional"), (128, "fused"), (300, "fused"), (77, "fused")):
+        dev.reset()
+        r_dev, out_bits = dev.run(mc)
+        r_ref, out_ref = oracle.proj_add_rmsnorm(d["x"], d["W"], d["residual"], d["norm_w"],
+                                                 d["eps"], 0, mode)
+        np.testing.assert_array_equal(r_dev.astype(np.float64), r_ref)
+        err = oracle.compare(r_dev, out_bits, r_ref, out_ref)
+        assert oracle.within_tolerance(err), (mc, err)
+
+
+# ------------------------------------------------------------------------- random parity
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("T,K,H", [(300, 512, 768), (64, 512, 512), (1, 256, 320),
+                                   (513, 1024, 256)])
+def test_random_parity_small(T, K, H, kind):
+    d = synth.make_custom(T, K, H, seed=T + K, norm_kind=kind, eps=1e-5)
+    dev = Device(d)
+    for mc in (None, 16, 128, 256, 4096):
+        dev.reset()
+        r_dev, out_bits = dev.run(mc)
+        _check(d, r_dev, out_bits, "conventional" if mc is None else "fused")
+
+
+def test_borrowed_output_workspace():
+    d = synth.make_custom(200, 512, 512, seed=1)
+    dev = Device(d)
+    for mc in (None, 64):
+        dev.reset()
+        r_dev, out_bits = dev.run(mc, out=None)
+        _check(d, r_dev, out_bits, "conventional" if mc is None else "fused")
+
+
+# ------------------------------------------------------------------------- padded rows
+@pytest.mark.parametrize("T,mc", [(300, 128), (3000 // 8, 64), (70, 16)])
+def test_padded_rows_untouched(T, mc):
+    """Rows past T (allocated, sentinel-filled, NaN in x) are never written or read into
+    valid rows."""
+    d = synth.make_custom(T, 512, 384, seed=5)
+    dev = Device(d, extra_rows=mc, pad_x_nan=True)
+    for m in (None, mc):
+        dev.reset(sentinel=12345.0)
+        r_dev, out_bits = dev.run(m)
+        _check(d, r_dev, out_bits, "conventional" if m is None else "fused")
+        r_all = dev.r.cpu().numpy()
+        out_all = bits(dev.out)
+        assert np.all(r_all[T:] == 12345.0)
+        assert np.all(out_all[T:] == 0x7BAD)
+
+
+# ---------------------------------------------------------------- chunked == unchunked
+@pytest.mark.parametrize("tile,split", [("256x256", 1), ("128x128", 2)])
+def test_microchunked_equals_unchunked_bitwise(monkeypatch, tile, split):
+    monkeypatch.setenv("PR_FORCE_TILE", tile)
+    monkeypatch.setenv("PR_FORCE_SPLIT", str(split))
+    d = synth.make_custom(1000, 1024, 512, seed=7)
+    dev = Device(d)
+    dev.reset()
+    r1, o1 = dev.run(1000)
+    for mc in (100, 256, 333, 512):
+        dev.reset()
+        r2, o2 = dev.run(mc)
+        np.testing.assert_array_equal(r1, r2)
+        np.testing.assert_array_equal(o1, o2)
+
+
+def test_deterministic_and_stream_ordered():
+    d = synth.make_custom(700, 1024, 1024, seed=8)
+    dev = Device(d)
+    s = torch.cuda.Stream()
+    results = []
+    for _ in range(2):
+        dev.reset()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            r, o = dev.run(128, stream=s)
+        results.append((r, o))
+    np.testing.assert_array_equal(results[0][0], results[1][0])
+    np.testing.assert_array_equal(results[0][1], results[1][1])
+    _check(d, results[0][0], results[0][1], "fused")
+
+
+# ------------------------------------------------------------------ race detection aids
+@pytest.mark.parametrize("var,val", [("PR_DEBUG_POISON", "1"), ("PR_DEBUG_DELAY", "20")])
+def test_poison_and_delay_do_not_change_results(monkeypatch, var, val):
+    """Slots are NaN-filled after use / streams are delayed: results must stay bitwise equal,
+    so no chunk reads a slot before its projection landed or after it was reused."""
+    d = synth.make_custom(1100, 512, 512, seed=9)
+    dev = Device(d)
+    dev.reset()
+    r1, o1 = dev.run(128)
+    monkeypatch.setenv(var, val)
+    dev.reset()
+    r2, o2 = dev.run(128)
+    np.testing.assert_array_equal(r1, r2)
+    np.testing.assert_array_equal(o1, o2)
+
+
+def test_fault_injection_propagates(monkeypatch):
+    d = synth.make_custom(64, 512, 512, seed=10)
+    dev = Device(d)
+    monkeypatch.setenv("PR_FAULT_INJECT", "launch")
+    for mc in (None, 16):
+        with pytest.raises(pr.PRError) as e:
+            dev.run(mc)
+        assert e.value.code == pr.PR_ERR_HIP
+    monkeypatch.delenv("PR_FAULT_INJECT")
+    dev.reset()
+    r_dev, out_bits = dev.run(16)
+    _check(d, r_dev, out_bits, "fused")
+
+
+def test_invalid_arguments_raise():
+    d = synth.make_custom(64, 512, 512, seed=11)
+    dev = Device(d)
+    with pytest.raises(pr.PRError) as e:
+        pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 64, 500, 512, 16)
+    assert e.value.code == pr.PR_ERR_SHAPE
+    with pytest.raises(pr.PRError) as e:
+        pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 64, 512, 512, 5000)
+    assert e.value.code == pr.PR_ERR_MICROCHUNK
+    with pytest.raises(pr.PRError) as e:
+        pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 64, 512, 512, -1)
+    assert e.value.code == pr.PR_ERR_MICROCHUNK
+    pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 0, 512, 512, 16)  # T == 0: no-op
+
+
+# --------------------------------------------------------------------- weight preparation
+def test_prepared_weight_layout_and_sources():
+    K, H = 128, 192
+    rng = np.random.default_rng(12)
+    W = synth.f32_to_bf16_bits(rng.standard_normal((H, K)).astype(np.float32))
+    Wp1 = torch.empty(K * H, dtype=torch.int16, device=DEV)
+    Wp2 = torch.empty(K * H, dtype=torch.int16, device=DEV)
+    pr.pr_prepare_weight(i16(W), pr.PR_WEIGHT_OUT_IN, Wp1, K, H)
+    pr.pr_prepare_weight(i16(np.ascontiguousarray(W.T)), pr.PR_WEIGHT_IN_OUT, Wp2, K, H)
+    torch.cuda.synchronize()
+    want = W.reshape(H, K // 8, 8).transpose(1, 0, 2).reshape(-1)  # [(k/8)][h][k%8]
+    np.testing.assert_array_equal(bits(Wp1), want)
+    np.testing.assert_array_equal(bits(Wp2), want)
+
+
+def test_pretransposed_source_gives_same_result():
+    d = synth.make_custom(256, 512, 512, seed=13)
+    a = Device(d, weight_layout=pr.PR_WEIGHT_OUT_IN)
+    b = Device(d, weight_layout=pr.PR_WEIGHT_IN_OUT)
+    ra, oa = a.run(128)
+    rb, ob = b.run(128)
+    np.testing.assert_array_equal(ra, rb)
+    np.testing.assert_array_equal(oa, ob)
+
+
+# ------------------------------------------------------------------------ automatic mode
+def test_auto_mode_overrides_and_tuning(monkeypatch):
+    d = synth.make_custom(512, 512, 512, seed=14)
+    dev = Device(d)
+    dev.reset()
+    r0, o0 = dev.run(0)          # untuned: conventional
+    _check(d, r0, o0, "conventional")
+    monkeypatch.setenv("PR_MICROCHUNK_TOKENS", "128")
+    monkeypatch.setenv("PR_THRESHOLD_TOKENS", "256")
+    dev.reset()
+    r1, o1 = dev.run(0)          # both overrides: fused
+    _check(d, r1, o1, "fused")
+    dev.reset()
+    r2, o2 = dev.run(128)
+    np.testing.assert_array_equal(r1, r2)
+    monkeypatch.delenv("PR_MICROCHUNK_TOKENS")
+    monkeypatch.delenv("PR_THRESHOLD_TOKENS")
+    rep = pr.pr_tune([512], [512], 0, [128, 512], [64, 128, 256], reps=3)
+    assert rep["n_checked"] >= 3 and rep["n_rejected"] == 0
+    assert rep["max_tokens"] == 512
+    for row in rep["timings"][0]:
+        assert row[0] > 0 and row[1] > 0
+    sel = pr.pr_select(512, 512, 512, 0)
+    thr = rep["threshold_tokens"]
+    assert sel["path"] == (pr.PR_PATH_FUSED if 512 >= thr else pr.PR_PATH_CONVENTIONAL)
+    with pytest.raises(pr.PRError) as e:
+        dev.run(0) if False else pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 600,
+                                                     512, 512, 0)
+    assert e.value.code == pr.PR_ERR_UNSUPPORTED
+
+
+# -------------------------------------------------------------------- full-size workloads
+def _sample_rows(T, mc, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    last = (T - 1) // mc * mc if mc else 0
+    rows = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    rows |= {0, T - 1, last, min(T - 1, last + 1)}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["tiny", "o_proj", "down_proj", "gemma", "sweep_T128",
+                                  "sweep_T2048"])
+def test_workload_parity_full_size(name):
+    wl = synth.WORKLOADS[name]
+    print(f"workload {name}: T={wl.T} K={wl.K} H={wl.H}", flush=True)
+    d = synth.make_inputs(wl, seed=0)
+    dev = Device(d)
+    for mc in (None,) + wl.microchunks:
+        dev.reset()
+        r_dev, out_bits = dev.run(mc)
+        rows = _sample_rows(wl.T, mc or wl.T, seed=hash(name) % 1000)
+        err = _check(d, r_dev, out_bits, "conventional" if mc is None else "fused", rows)
+        print(name, mc, err, flush=True)
+        assert np.all(np.isfinite(r_dev))

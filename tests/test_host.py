@@ -1,0 +1,259 @@
+"""CPU tests of the C ABI's host side: the library loads, exports every declared entry point,
+validates arguments, decides the path per call, plans a race-free pipeline schedule, and
+computes the token threshold.  No GPU is touched (only host-only entry points are called)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import projection_residual_rmsnorm_amd as pr
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include",
+                      "proj_add_rmsnorm.h")
+A = 1 << 20  # a fake, 16-byte aligned address for pointer arguments
+
+
+@pytest.fixture(autouse=True)
+def _clean_env(monkeypatch):
+    for k in ("PR_MICROCHUNK_TOKENS", "PR_THRESHOLD_TOKENS", "PR_LOG"):
+        monkeypatch.delenv(k, raising=False)
+    pr.pr_clear_tuning()
+    yield
+    pr.pr_clear_tuning()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(
+        r"^(?:int|void|const char\s*\*|const uint16_t\s*\*)\s*(\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "proj_add_rmsnorm" in names and "pr_tune" in names and len(names) >= 14
+    lib = pr.library()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in pr.SIGNATURES, f"binding lacks {n}"
+    assert pr.pr_version() == 1
+    assert pr.pr_strerror(pr.PR_ERR_SHAPE) == "unsupported shape"
+
+
+def test_validate():
+    ok = dict(x=A, W=A * 2, residual_inout=A * 3, norm_w=A * 4, eps=1e-5, T=64, K=512, H=512,
+              microchunk=16, norm_kind=0, out=A * 5)
+    assert pr.pr_validate(**ok) == 0
+    bad = [
+        (dict(K=100), pr.PR_ERR_SHAPE), (dict(H=96), pr.PR_ERR_SHAPE),
+        (dict(T=-1), pr.PR_ERR_INVALID_ARG), (dict(K=0), pr.PR_ERR_INVALID_ARG),
+        (dict(microchunk=4097), pr.PR_ERR_MICROCHUNK), (dict(microchunk=-5), pr.PR_ERR_MICROCHUNK),
+        (dict(norm_kind=2), pr.PR_ERR_INVALID_ARG), (dict(eps=-1.0), pr.PR_ERR_INVALID_ARG),
+        (dict(eps=float("nan")), pr.PR_ERR_INVALID_ARG), (dict(x=None), pr.PR_ERR_INVALID_ARG),
+        (dict(out=A), pr.PR_ERR_INVALID_ARG), (dict(out=A * 3), pr.PR_ERR_INVALID_ARG),
+        (dict(x=A + 2), pr.PR_ERR_INVALID_ARG), (dict(K=1 << 16, H=1 << 16), pr.PR_ERR_SHAPE),
+    ]
+    for change, code in bad:
+        args = dict(ok, **change)
+        assert pr.pr_validate(**args) == code, change
+    # T == 0 is a no-op: null pointers are accepted
+    assert pr.pr_validate(None, None, None, None, 1e-5, 0, 512, 512, 16, 0, None) == 0
+    # microchunk >= T is allowed (one chunk); out == NULL borrows the workspace
+    assert pr.pr_validate(**dict(ok, microchunk=4096, out=None)) == 0
+
+
+def test_select_explicit_and_unfused():
+    d = pr.pr_select(3000, 16384, 3072, 256)
+    assert d["path"] == pr.PR_PATH_FUSED and d["microchunk"] == 256
+    assert d["n_chunks"] == 12 and d["last_valid"] == 184 and d["reason"] == 0
+    d = pr.pr_select(3000, 16384, 3072, 1024)
+    assert d["n_chunks"] == 3 and d["last_valid"] == 952
+    d = pr.pr_select(64, 512, 512, 4096)  # microchunk >= T: one chunk
+    assert d["n_chunks"] == 1 and d["last_valid"] == 64
+    d = pr.pr_select(2048, 4096, 4096, -1)
+    assert d["path"] == pr.PR_PATH_CONVENTIONAL and d["reason"] == 5
+    with pytest.raises(pr.PRError):
+        pr.pr_select(10, 64, 64, 5000)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 512, 512), (512, 4096, 4096), (2048, 4096, 4096),
+                                   (4096, 4096, 14336), (3000, 3072, 16384), (128, 8192, 8192),
+                                   (32768, 8192, 8192), (184, 3072, 16384)])
+def test_tile_choice_is_valid(M, N, K):
+    for mc in (-1, min(M, 4096)):
+        d = pr.pr_select(M, K, N, mc if mc > 0 else -1)
+        assert (d["gemm_bm"], d["gemm_bn"]) in ((256, 256), (256, 128), (128, 128))
+        assert K % (64 * d["split_k"]) == 0 and d["split_k"] >= 1
+
+
+def test_auto_untuned_and_overrides(monkeypatch):
+    d = pr.pr_select(2048, 4096, 4096, 0)
+    assert d["path"] == pr.PR_PATH_CONVENTIONAL and pr.REASON_NAMES[d["reason"]] == "untuned"
+    monkeypatch.setenv("PR_MICROCHUNK_TOKENS", "512")
+    monkeypatch.setenv("PR_THRESHOLD_TOKENS", "1024")
+    d = pr.pr_select(2048, 4096, 4096, 0)
+    assert d["path"] == pr.PR_PATH_FUSED and d["microchunk"] == 512
+    d = pr.pr_select(1000, 4096, 4096, 0)
+    assert d["path"] == pr.PR_PATH_CONVENTIONAL and d["reason"] == 2
+    monkeypatch.setenv("PR_MICROCHUNK_TOKENS", "9000")
+    with pytest.raises(pr.PRError) as e:
+        pr.pr_select(2048, 4096, 4096, 0)
+    assert e.value.code == pr.PR_ERR_MICROCHUNK
+    monkeypatch.setenv("PR_MICROCHUNK_TOKENS", "abc")
+    with pytest.raises(pr.PRError):
+        pr.pr_select(2048, 4096, 4096, 0)
+
+
+def test_auto_tuned(monkeypatch):
+    pr.pr_set_tuning(4096, 4096, 2048, 32768, [128, 512, 2048, 8192, 32768],
+                     [128, 512, 512, 1024, 2048])
+    d = pr.pr_select(1024, 4096, 4096, 0)
+    assert d["path"] == pr.PR_PATH_CONVENTIONAL and d["reason"] == 2
+    d = pr.pr_select(2048, 4096, 4096, 0)
+    assert d["path"] == pr.PR_PATH_FUSED and d["microchunk"] == 512
+    d = pr.pr_select(9000, 4096, 4096, 0)  # between grid points: lower grid point's choice
+    assert d["microchunk"] == 1024
+    with pytest.raises(pr.PRError) as e:  # above the profiled token maximum
+        pr.pr_select(40000, 4096, 4096, 0)
+    assert e.value.code == pr.PR_ERR_UNSUPPORTED
+    # an explicit microchunk ignores the tuning entirely
+    assert pr.pr_select(40000, 4096, 4096, 256)["path"] == pr.PR_PATH_FUSED
+    # a single override replaces its tuned value
+    monkeypatch.setenv("PR_THRESHOLD_TOKENS", "100")
+    assert pr.pr_select(1024, 4096, 4096, 0)["path"] == pr.PR_PATH_FUSED
+    monkeypatch.delenv("PR_THRESHOLD_TOKENS")
+    monkeypatch.setenv("PR_MICROCHUNK_TOKENS", "256")
+    assert pr.pr_select(8192, 4096, 4096, 0)["microchunk"] == 256
+    monkeypatch.delenv("PR_MICROCHUNK_TOKENS")
+    # inconclusive tuning keeps the conventional path
+    pr.pr_set_tuning(8192, 8192, pr.INT32_MAX, 32768, [128], [128])
+    d = pr.pr_select(4096, 8192, 8192, 0)
+    assert d["path"] == pr.PR_PATH_CONVENTIONAL and pr.REASON_NAMES[d["reason"]] == "inconclusive"
+    with pytest.raises(pr.PRError):
+        pr.pr_set_tuning(64, 64, 1, 10, [4, 2], [1, 1])  # grid must ascend
+
+
+def _simulate(ops):
+    """Vector-clock happens-before over the planned enqueue order.
+
+    Streams execute in order; a record snapshots the stream's clock into the event; a wait
+    joins the most recent record of that event at enqueue time (HIP semantics).  Returns the
+    clock of every GEMM / ADDNORM op keyed by (kind, chunk) and of the final join.
+    """
+    clocks = {0: {}, 1: {}, 2: {}}
+    events = {}
+    stamps = {}
+    counter = [0]
+
+    def tick(s, label):
+        counter[0] += 1
+        c = dict(clocks[s])
+        c[label] = counter[0]
+        clocks[s] = c
+        return c
+
+    for name, stream, chunk, slot, rows in ops:
+        if name == "RECORD_ENTRY":
+            events["entry"] = dict(tick(0, ("caller_pre",)))
+        elif name == "WAIT_ENTRY":
+            clocks[stream] = {**clocks[stream], **events["entry"]}
+        elif name in ("GEMM", "ADDNORM"):
+            stamps[(name, chunk)] = (tick(stream, (name, chunk)), slot, rows)
+        elif name == "RECORD_READY":
+            events[("ready", slot)] = dict(clocks[stream])
+        elif name == "RECORD_DONE":
+            events[("done", slot)] = dict(clocks[stream])
+        elif name == "WAIT_READY":
+            clocks[stream] = {**clocks[stream], **events[("ready", slot)]}
+        elif name == "WAIT_DONE":
+            clocks[stream] = {**clocks[stream], **events[("done", slot)]}
+        elif name == "JOIN":
+            clocks[0] = {**clocks[0], **events[("done", slot)]}
+            stamps["join"] = (dict(clocks[0]), -1, 0)
+    return stamps
+
+
+def _hb(stamps, a, b):
+    """a happens before b."""
+    return a in stamps[b][0] if isinstance(a, tuple) and len(a) == 2 else False
+
+
+@pytest.mark.parametrize("T,mc", [(64, 16), (3000, 256), (3000, 1024), (2048, 512), (7, 7),
+                                  (1, 4096), (10, 3), (4096, 4096)])
+def test_plan_is_race_free(T, mc):
+    ops = pr.pr_plan(T, mc)
+    nc = -(-T // mc)
+    gemms = [o for o in ops if o[0] == "GEMM"]
+    norms = [o for o in ops if o[0] == "ADDNORM"]
+    assert len(gemms) == nc and len(norms) == nc
+    assert sum(o[4] for o in norms) == T                 # valid rows only, each once
+    assert all(o[4] == mc for o in norms[:-1]) and norms[-1][4] == T - (nc - 1) * mc
+    assert {o[3] for o in ops if o[3] >= 0} <= {0, 1, 2}  # three reusable slots
+    st = _simulate(ops)
+    for c in range(nc):
+        assert ("GEMM", c) in st[("ADDNORM", c)][0]          # slot written before it is read
+        if c + 3 < nc:                                        # slot reused only after its read
+            assert ("ADDNORM", c) in st[("GEMM", c + 3)][0]
+        assert ("ADDNORM", c) in st["join"][0]               # caller waits for every chunk
+        assert ("caller_pre",) in st[("GEMM", c)][0]         # nothing starts before entry
+        assert st[("GEMM", c)][1] == c % 3
+    # overlap is possible: GEMM(c+1) does not depend on ADDNORM(c)
+    for c in range(nc - 1):
+        assert ("ADDNORM", c) not in st[("GEMM", c + 1)][0]
+
+
+def test_plan_detects_a_missing_wait():
+    """The simulator itself catches a schedule without the slot-reuse wait."""
+    ops = [o for o in pr.pr_plan(3000, 256) if o[0] != "WAIT_DONE"]
+    st = _simulate(ops)
+    assert not all(("ADDNORM", c) in st[("GEMM", c + 3)][0] for c in range(9))
+
+
+def test_plan_edge_cases():
+    assert pr.pr_plan(0, 16) == []
+    with pytest.raises(pr.PRError):
+        pr.pr_plan(10, 0)
+    with pytest.raises(pr.PRError):
+        pr.pr_plan(10, 4097)
+
+
+def test_threshold_from_timings():
+    T = [128, 512, 2048, 8192, 32768]
+    conv = [[1.0, 2.0, 4.0, 8.0, 16.0]]
+    # fused wins from 2048 upward by more than 2 %
+    fused = [[1.5, 2.5, 3.5, 7.0, 14.0]]
+    assert pr.pr_threshold_from_timings(T, conv, fused) == 2048
+    # a win inside the noise margin does not count
+    fused2 = [[1.5, 2.5, 3.95, 7.0, 14.0]]
+    assert pr.pr_threshold_from_timings(T, conv, fused2) == 8192
+    # large spread suppresses a small win
+    assert pr.pr_threshold_from_timings(T, conv, fused, spread=[[0, 0, 0, 0, 3.0]]) \
+        == pr.INT32_MAX
+    # a loss at the top of the grid: no range where fused keeps winning -> inconclusive
+    fused3 = [[0.5, 0.5, 0.5, 0.5, 20.0]]
+    assert pr.pr_threshold_from_timings(T, conv, fused3) == pr.INT32_MAX
+    # groups are summed: one group's loss can outweigh the other's win
+    conv2 = [[1, 1, 1, 1, 1], [1, 1, 1, 1, 1]]
+    fused4 = [[0.5, 0.5, 0.5, 0.5, 0.5], [2, 2, 1.6, 1.6, 1.6]]
+    assert pr.pr_threshold_from_timings(T, conv2, fused4) == pr.INT32_MAX
+    fused5 = [[0.5, 0.5, 0.5, 0.5, 0.5], [2, 2, 1.2, 1.2, 1.0]]
+    assert pr.pr_threshold_from_timings(T, conv2, fused5) == 2048
+    # a rejected candidate (no fused time) is never profitable
+    assert pr.pr_threshold_from_timings([1, 2], [[1, 1]], [[0.1, -1]]) == pr.INT32_MAX
+    with pytest.raises(pr.PRError):
+        pr.pr_threshold_from_timings([2, 1], [[1, 1]], [[1, 1]])
+
+
+def test_calls_without_gpu_fail_cleanly():
+    """On a machine without a GPU the device entry points report an error, never crash."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc = pr.library().proj_add_rmsnorm(A, A * 2, A * 3, A * 4, 1e-5, 64, 512, 512, 16, 0,
+                                       A * 5, None)
+    assert rc in (pr.PR_ERR_HIP, pr.PR_ERR_UNSUPPORTED)
+    assert pr.pr_last_error() != ""
+    # a T == 0 call is a no-op that still needs a device context
+    rc = pr.library().proj_add_rmsnorm(None, None, None, None, 1e-5, 0, 512, 512, 16, 0, None,
+                                       None)
+    assert rc in (0, pr.PR_ERR_HIP, pr.PR_ERR_UNSUPPORTED)
