@@ -147,6 +147,7 @@ typedef struct {
   int gemm_bm;    /* projection tile rows                                           */
   int gemm_bn;    /* projection tile columns                                        */
   int split_k;    /* K partitions of the projection; partial sums are added in order */
+  int gemm_waves; /* waves per projection workgroup (4 or 8)                         */
   int reason;     /* PR_REASON_*                                                    */
 } pr_decision;
 

@@ -91,6 +91,13 @@ static int apply_forced_tile(int K, GemmCfg* g) {
     g->bm = bm;
     g->bn = bn;
   }
+  const char* wv = std::getenv("PR_FORCE_WAVES");
+  if (wv != nullptr && wv[0] != '\0') {
+    const int waves = std::atoi(wv);
+    if (waves != 4 && waves != 8)
+      return fail(PR_ERR_INVALID_ARG, "PR_FORCE_WAVES=%s must be 4 or 8", wv);
+    g->waves = waves;
+  }
   const char* sp = std::getenv("PR_FORCE_SPLIT");
   if (sp != nullptr && sp[0] != '\0') {
     const int split = std::atoi(sp);
@@ -224,6 +231,7 @@ int decide(int T, int K, int H, int microchunk, pr_decision* d) {
   d->gemm_bm = g.bm;
   d->gemm_bn = g.bn;
   d->split_k = g.split;
+  d->gemm_waves = g.waves;
   return PR_OK;
 }
 

@@ -18,6 +18,7 @@ struct GemmCfg {
   int bm = 256;   // tile rows (tokens)
   int bn = 256;   // tile columns (hidden)
   int split = 1;  // K partitions; partial sums land in separate fp32 planes
+  int waves = 4;  // waves per workgroup: 4 (one per SIMD) or 8 (two per SIMD)
 };
 
 // Tile configurations the library instantiates (rows x columns per workgroup).

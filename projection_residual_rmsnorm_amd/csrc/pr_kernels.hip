@@ -23,7 +23,13 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void global_cvoid_t;
 
-constexpr int kBK = 64;  // K depth of one LDS stage (8 groups of 8 bf16 = 128 bytes per row)
+constexpr int kBK = 32;  // K depth of one LDS stage (4 groups of 8 bf16 = 64 bytes per row)
+
+// s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+// The builtin (unlike inline asm) is understood by the compiler's own wait insertion, which
+// then knows which direct-to-LDS loads have landed.
+#define PR_VMCNT(n) (0x0F70 | ((n)&15) | ((((n) >> 4) & 3) << 14))
+#define PR_LGKMCNT0 0xC07F
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -36,9 +42,19 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_floa
 __device__ __forceinline__ void load_to_lds16(const char* gbase, uint32_t lane_off,
                                               char* lds_dst_wave_base) {
   // Each lane copies 16 bytes from gbase + lane_off (gbase wave-uniform) to
-  // lds_dst_wave_base + lane * 16.
-  __builtin_amdgcn_global_load_lds((global_cvoid_t*)(gbase + lane_off),
+  // lds_dst_wave_base + lane * 16.  The sum is formed in the global address space so that the
+  // load uses the scalar-base + 32-bit vector-offset form.
+  const __attribute__((address_space(1))) char* g =
+      (const __attribute__((address_space(1))) char*)gbase;
+  __builtin_amdgcn_global_load_lds((global_cvoid_t*)(g + lane_off),
                                    (lds_void_t*)lds_dst_wave_base, 16, 0, 0);
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for every outstanding global
+// load, i.e. drain the prefetch ring).  Callers wait for what they need first.
+__device__ __forceinline__ void barrier_no_fence() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // --------------------------------------------------------------------------------------------
@@ -49,42 +65,60 @@ __device__ __forceinline__ void load_to_lds16(const char* gbase, uint32_t lane_o
 //   Bp = prepared weight, Bp[((k/8)*N + n)*8 + k%8] = W[n][k].
 // LDS stage layouts (bytes), chosen so that every fragment read is lane-linear (conflict-free)
 // and every direct global->LDS load writes 1 KiB contiguously:
-//   A stage: [BM/32 row blocks][8 k-groups][32 rows][16 B]
-//   B stage: [8 k-groups][BN columns][16 B]
+//   A stage: [BM/32 row blocks][4 k-groups][32 rows][16 B]
+//   B stage: [4 k-groups][BN columns][16 B]
 // A 32x32x16 MFMA takes, per lane l, A[row l%32][k 8*(l/32)..+8] and B[k 8*(l/32)..+8][col l%32]:
 // both are one 16-byte read at offset ((k-group)*32 + l%32)*16 within a 32-row/column block.
+//
+// Pipeline: NB stage buffers in a ring, stages issued NB-1 ahead.  Each stage step runs the
+// MFMAs of its first k-substep while reading the second substep's fragments, waits for the
+// next stage to land (own loads) and meets the other waves at one barrier, then runs the
+// second substep's MFMAs while reading the next stage's first fragments.  A buffer is refilled
+// one step after the barrier that follows its last read.  K per split is a multiple of
+// 32 * NB, so every loop trip runs all NB steps.
 // --------------------------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, bool ODD_STAGES>
+template <int BM, int BN, int NB, int WM, int WN>
 __global__ void __launch_bounds__(WM* WN * 64, 1)
     gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp,
                      float* __restrict__ Cf, uint16_t* __restrict__ Cb, int M, int N, int K,
                      int k_split_len, long long plane_stride, int tiles_m, int tiles_n,
                      int split) {
-  constexpr int NW = WM * WN;
+  constexpr int NW = WM * WN;  // waves per workgroup (4: one per SIMD, 8: two per SIMD)
   constexpr int WTM = BM / WM;  // wave tile rows
   constexpr int WTN = BN / WN;  // wave tile columns
   constexpr int TM = WTM / 32;
   constexpr int TN = WTN / 32;
   constexpr int A_BYTES = BM * kBK * 2;
   constexpr int B_BYTES = BN * kBK * 2;
-  constexpr int A_LOADS = A_BYTES / 1024;  // wave-wide 1 KiB load instructions per stage
-  constexpr int B_LOADS = B_BYTES / 1024;
-  static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads must split evenly over waves");
+  constexpr int A_LPW = A_BYTES / 1024 / NW;  // 1 KiB loads per wave per stage
+  constexpr int B_LPW = B_BYTES / 1024 / NW;
+  constexpr int LPW = A_LPW + B_LPW;
+  constexpr int P = NB - 1;  // stages in flight ahead of the one being computed
+  constexpr int CG = BN / 64;
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "load split");
+  static_assert(NW % CG == 0, "B loads: waves must cover whole k-groups");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
+  static_assert(NB >= 2 && NB <= 4 && NB * (A_BYTES + B_BYTES) <= 160 * 1024, "LDS budget");
+  static_assert(LPW * (P - 1) < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) char sA0[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB0[B_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sA1[A_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sB1[B_BYTES];
+  // One LDS object per ring buffer: the compiler tracks direct-to-LDS loads per object, so a
+  // fragment read from one buffer does not wait for loads still landing in another.
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  __shared__ __attribute__((aligned(1024))) char sb0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sb1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char sb2[NB > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char sb3[NB > 3 ? STAGE : 16];
+  auto smem = [&](int u) -> char* { return u == 0 ? sb0 : (u == 1 ? sb1 : (u == 2 ? sb2 : sb3)); };
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int wm = wave / WN;
   const int wn = wave % WN;
 
-  // Workgroups are dealt round-robin to the 8 XCDs (linear id % 8).  Give each XCD a contiguous
-  // range of the (split, column tile, row tile) space so that tiles sharing weight columns
-  // share that XCD's L2.
+  // Tile order.  Workgroups are dealt round-robin to the 8 XCDs (linear id % 8); each XCD
+  // gets a contiguous range of the logical order, and the logical order walks groups of 8 tile
+  // rows column by column, so the ~32 workgroups an XCD runs at once cover an 8 x 4 patch of
+  // tiles and share their x rows and weight columns in that XCD's L2.
   const int total = tiles_m * tiles_n * split;
   const int b = blockIdx.x;
   const int q8 = total / kNumXCDs;
@@ -94,46 +128,50 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
   const int per_split = tiles_m * tiles_n;
   const int z = logical / per_split;
   const int t = logical % per_split;
-  const int tm = t % tiles_m;
-  const int tn = t / tiles_m;
+  constexpr int GROUP_M = 8;
+  const int group = t / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int in_group = t % (GROUP_M * tiles_n);
+  const int tm = first_m + in_group % gm;
+  const int tn = in_group / gm;
 
   const int m0 = tm * BM;
   const int n0 = tn * BN;
   const int k_begin = z * k_split_len;
   const int nk = k_split_len / kBK;
 
-  // Load assignment (NW == 4): A load i of wave w covers row block i, k-groups 2w and 2w+1
-  // (lane l: row 32i + l%32, k-group 2w + l/32); B load i of wave w covers k-group
-  // (w + 4i) / (BN/64) and the 64 columns of column group (w + 4i) % (BN/64).  Rows and columns
-  // past the matrix edge are clamped to the last valid one: their data only feeds outputs that
-  // are never stored.  Offsets are 32-bit byte offsets (the launcher keeps every operand
-  // slice below 2 GiB).
-  static_assert(NW == 4, "load assignment assumes four waves");
-  uint32_t a_off[A_LOADS / NW];
+  // Load assignment: A load i of wave w fills LDS kilobyte q = w + NW*i of the stage, i.e. row
+  // block q/2 and k-groups 2(q%2), 2(q%2)+1 (lane l: row 32(q/2) + l%32, k-group 2(q%2) + l/32).
+  // B load i of wave w fills kilobyte q = w + NW*i: k-group q / CG, 64-column group q % CG.
+  // Rows and columns past the matrix edge are clamped to the last valid one: their data only
+  // feeds outputs that are never stored.  Offsets are 32-bit byte offsets (the launcher keeps
+  // every operand slice below 2 GiB).
+  uint32_t a_off[A_LPW];
 #pragma unroll
-  for (int i = 0; i < A_LOADS / NW; ++i) {
-    int row = m0 + i * 32 + (lane & 31);
+  for (int i = 0; i < A_LPW; ++i) {
+    const int q = wave + NW * i;
+    int row = m0 + (q >> 1) * 32 + (lane & 31);
     row = row < M ? row : M - 1;
-    a_off[i] = (uint32_t)(row * K + (2 * wave + (lane >> 5)) * 8) * 2u;
+    a_off[i] = (uint32_t)(row * K + (2 * (q & 1) + (lane >> 5)) * 8) * 2u;
   }
-  constexpr int CG = BN / 64;  // 64-column groups per B stage row
-  int b_col = n0 + ((wave) % CG) * 64 + lane;
+  int b_col = n0 + (wave % CG) * 64 + lane;
   b_col = b_col < N ? b_col : N - 1;
   const uint32_t b_lane_off = (uint32_t)(((wave / CG) * N + b_col) * 8) * 2u;
-  const uint32_t b_step = (uint32_t)((NW / CG) * N * 8) * 2u;  // bytes between this wave's loads
+  const uint32_t b_step = (uint32_t)((NW / CG) * N * 8) * 2u;
 
-  auto issue_stage = [&](int kt, char* sa, char* sb) {
-    const int k0 = k_begin + kt * kBK;
-    const char* a_base = reinterpret_cast<const char*>(A + k0);
-    const char* b_base = reinterpret_cast<const char*>(Bp + (long long)(k0 / 8) * N * 8);
+  // Stage bases advance by a fixed number of bytes per stage (scalar arithmetic only).
+  const char* a_base0 = reinterpret_cast<const char*>(A + k_begin);
+  const char* b_base0 = reinterpret_cast<const char*>(Bp + (long long)(k_begin / 8) * N * 8);
+  const long long b_stage_bytes = (long long)(kBK / 8) * N * 16;
+  auto issue_stage = [&](int kt, char* buf) {
+    const char* a_base = a_base0 + kt * (kBK * 2);
+    const char* b_base = b_base0 + kt * b_stage_bytes;
 #pragma unroll
-    for (int i = 0; i < A_LOADS / NW; ++i)
-      load_to_lds16(a_base, a_off[i], sa + (i * NW + wave) * 1024);
+    for (int i = 0; i < A_LPW; ++i) load_to_lds16(a_base, a_off[i], buf + (wave + NW * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < B_LOADS / NW; ++i)
-      load_to_lds16(b_base, b_lane_off + i * b_step, sb + (wave + i * NW) * 1024);
-    // Keep the loads at the top of the stage so their latency hides behind its MFMAs.
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < B_LPW; ++i)
+      load_to_lds16(b_base, b_lane_off + i * b_step, buf + A_BYTES + (wave + NW * i) * 1024);
   };
 
   f32x16_t acc[TM][TN];
@@ -144,19 +182,17 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int frag_lane = ((lane >> 5) * 32 + (lane & 31)) * 16;  // byte offset within a block
-
-  auto load_frags = [&](const char* sa, const char* sb, int s, bf16x8_t* af, bf16x8_t* bfr) {
+  auto load_frags = [&](const char* buf, int s, bf16x8_t* af, bf16x8_t* bfr) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int rb = wm * TM + i;
-      af[i] = *reinterpret_cast<const bf16x8_t*>(sa + (rb * 8 + 2 * s) * 512 + frag_lane);
+      af[i] = *reinterpret_cast<const bf16x8_t*>(buf + (rb * 4 + 2 * s) * 512 + lane * 16);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = wn * WTN + j * 32;
       bfr[j] = *reinterpret_cast<const bf16x8_t*>(
-          sb + ((2 * s + (lane >> 5)) * BN + col + (lane & 31)) * 16);
+          buf + A_BYTES + ((2 * s + (lane >> 5)) * BN + col + (lane & 31)) * 16);
     }
   };
   auto mfmas = [&](const bf16x8_t* af, const bf16x8_t* bfr) {
@@ -166,62 +202,48 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
-  // Fragments of k-substep s+1 are read from LDS while the MFMAs of substep s run: the
-  // scheduling groups interleave one fragment read after each MFMA, so the LDS latency of the
-  // next substep hides behind the current one.
+  // One LDS fragment read after each of the first TM+TN MFMAs, then the rest of the MFMAs.
   auto interleave = [&]() {
 #pragma unroll
     for (int g = 0; g < TM + TN; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
   };
-  auto compute_stage = [&](const char* sa, const char* sb) {
-    bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
-    load_frags(sa, sb, 0, a0, b0);
+
+  bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+
+  // Prologue: stages 0 .. P-1 in flight, wait for stage 0, read its first fragments.
+#pragma unroll
+  for (int p = 0; p < P; ++p) issue_stage(p, smem(p));
+  __builtin_amdgcn_s_waitcnt(PR_VMCNT(LPW * (P - 1)));
+  barrier_no_fence();
+  load_frags(smem(0), 0, fa0, fb0);
+
+  // The refill is issued in every step so that the count of loads in flight is the same in
+  // every step; past the last stage it re-reads the last stage (an L2 hit) into the buffer
+  // being refilled, which is never read again.
+  auto step = [&](int kt, char* cur, char* next, char* refill) {
+    issue_stage(min(kt + P, nk - 1), refill);
     __builtin_amdgcn_sched_barrier(0);
-    load_frags(sa, sb, 1, a1, b1);
-    mfmas(a0, b0);
+    load_frags(cur, 1, fa1, fb1);
+    mfmas(fa0, fb0);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
-    load_frags(sa, sb, 2, a0, b0);
-    mfmas(a1, b1);
+    __builtin_amdgcn_s_waitcnt(PR_VMCNT(LPW * (P - 1)));  // stage kt+1 landed
+    __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);
+    barrier_no_fence();
+    load_frags(next, 0, fa0, fb0);
+    mfmas(fa1, fb1);
     interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(sa, sb, 3, a1, b1);
-    mfmas(a0, b0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(a1, b1);
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Two stages per loop trip so that each LDS buffer is a distinct object at every access, and
-  // a branch-free steady state (the accumulators stay in AGPRs across the back-edge); the last
-  // one (ODD_STAGES) or two stages are peeled.
-  issue_stage(0, sA0, sB0);
-  int kt = 0;
-  for (; kt + 2 < nk; kt += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    issue_stage(kt + 1, sA1, sB1);
-    compute_stage(sA0, sB0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    issue_stage(kt + 2, sA0, sB0);
-    compute_stage(sA1, sB1);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if constexpr (ODD_STAGES) {
-    compute_stage(sA0, sB0);
-  } else {
-    issue_stage(kt + 1, sA1, sB1);
-    compute_stage(sA0, sB0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    compute_stage(sA1, sB1);
+  for (int kt = 0; kt < nk; kt += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      step(kt + u, smem(u), smem((u + 1) % NB), smem((u + P) % NB));
   }
 
   // Epilogue.  32x32 fp32 accumulator layout: lane l, element e holds
@@ -448,23 +470,28 @@ int check_launch(const char* what) {
   return PR_OK;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NB, int WM, int WN>
 int launch_gemm_t(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
                   int K, int split, long long plane_stride, hipStream_t s) {
-  constexpr int WM = 2, WN = 2;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
   const int k_len = K / split;
   const unsigned grid = (unsigned)(tiles_m * tiles_n * split);
   float* cf = bf16_out ? nullptr : static_cast<float*>(C);
   uint16_t* cb = bf16_out ? static_cast<uint16_t*>(C) : nullptr;
-  if ((k_len / kBK) % 2)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, true>), dim3(grid), dim3(WM * WN * 64), 0,
-                       s, x, Wp, cf, cb, M, N, K, k_len, plane_stride, tiles_m, tiles_n, split);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, false>), dim3(grid), dim3(WM * WN * 64),
-                       0, s, x, Wp, cf, cb, M, N, K, k_len, plane_stride, tiles_m, tiles_n, split);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NB, WM, WN>), dim3(grid), dim3(WM * WN * 64), 0, s,
+                     x, Wp, cf, cb, M, N, K, k_len, plane_stride, tiles_m, tiles_n, split);
   return check_launch("gemm_bf16_kernel");
+}
+
+template <int BM, int BN, int WM, int WN>
+int launch_gemm_nb(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
+                   int K, int split, long long plane_stride, hipStream_t s) {
+  // Ring depth: 4 stage buffers when K per split is a multiple of 4 stages, else 2 (K per split
+  // is always a multiple of 64, i.e. of 2 stages).
+  if ((K / split) % (4 * kBK) == 0)
+    return launch_gemm_t<BM, BN, 4, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s);
+  return launch_gemm_t<BM, BN, 2, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s);
 }
 
 template <int NV>
@@ -484,16 +511,20 @@ int launch_addnorm_t(const void* y, int y_bf16, int nplanes, long long plane_str
 int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
                 int K, const GemmCfg& cfg, long long plane_stride, void* stream) {
   if (M <= 0) return PR_OK;
-  if (K % (kBK * cfg.split) != 0 || N % 64 != 0 || (bf16_out && cfg.split != 1))
+  if (K % (2 * kBK * cfg.split) != 0 || N % 64 != 0 || (bf16_out && cfg.split != 1))
     return fail(PR_ERR_SHAPE, "projection shape M=%d N=%d K=%d split=%d not supported", M, N, K,
                 cfg.split);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool eight = cfg.waves == 8;
   if (cfg.bm == 256 && cfg.bn == 256)
-    return launch_gemm_t<256, 256>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
+    return eight ? launch_gemm_nb<256, 256, 2, 4>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s)
+                 : launch_gemm_nb<256, 256, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
   if (cfg.bm == 256 && cfg.bn == 128)
-    return launch_gemm_t<256, 128>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
+    return eight ? launch_gemm_nb<256, 128, 4, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s)
+                 : launch_gemm_nb<256, 128, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
   if (cfg.bm == 128 && cfg.bn == 128)
-    return launch_gemm_t<128, 128>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
+    return eight ? launch_gemm_nb<128, 128, 2, 4>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s)
+                 : launch_gemm_nb<128, 128, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
   return fail(PR_ERR_INVALID_ARG, "no projection tile %dx%d", cfg.bm, cfg.bn);
 }
 
