@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--microchunk", type=int, default=0, help="0: every chunk size of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_o_proj.json"),
+                    help="measured HBM bytes per projection launch (from the counter runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -103,6 +107,10 @@ def main() -> int:
     out = torch.empty((T, H), dtype=torch.int16, device=dev)
     del W_src
     torch.cuda.synchronize()
+    # All timed work runs on one dedicated stream (the legacy null stream adds host-side
+    # synchronisation to every event record on it).
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
     flops = 2.0 * T * K * H
 
     def fused(mc):
@@ -113,46 +121,37 @@ def main() -> int:
 
     mcs = [args.microchunk] if args.microchunk else list(wl.microchunks)
     per_mc = {}
-    best = None
     for mc in mcs:
-        pr.pr_profile_enable(True)
         el = time_steps(fused(mc), args.steps, args.warmup, torch)
-        prof_all = pr.pr_profile_read()
-        pr.pr_profile_enable(False)
-        # the profile counted warm-up launches too; per-launch averages are unaffected
         per_mc[mc] = {"tokens_per_s": T * args.steps / el, "ms_per_step": el * 1e3 / args.steps,
-                      "tflops": flops * args.steps / el / 1e12, "profile": prof_all}
+                      "tflops": flops * args.steps / el / 1e12}
         log(f"fused mc={mc}: {per_mc[mc]['ms_per_step']:.4f} ms/step "
             f"{per_mc[mc]['tflops']:.1f} TFLOP/s")
-        if best is None or el < per_mc[best]["ms_per_step"] * args.steps / 1e3:
-            best = mc
-    pr.pr_profile_enable(True)
+    best = min(per_mc, key=lambda m: per_mc[m]["ms_per_step"])
     el_c = time_steps(conventional, args.steps, args.warmup, torch)
-    prof_c = pr.pr_profile_read()
-    pr.pr_profile_enable(False)
     conv = {"tokens_per_s": T * args.steps / el_c, "ms_per_step": el_c * 1e3 / args.steps,
             "tflops": flops * args.steps / el_c / 1e12}
     log(f"conventional: {conv['ms_per_step']:.4f} ms/step {conv['tflops']:.1f} TFLOP/s")
 
-    # headline: the best chunk size, re-timed as its own region with the kernel profile live
+    # Headline: the best chunk size, timed as its own region (barrier-free single process:
+    # synchronize on both sides).
     mc = best
+    el = time_steps(fused(mc), args.steps, args.warmup, torch)
+    value = T * args.steps / el
+    ms_step = el * 1e3 / args.steps
+    tflops = flops * args.steps / el / 1e12
+
+    # Kernel durations: the same steps again with the library's timing events bracketing every
+    # projection and add/norm launch on the stream it runs on.
     pr.pr_profile_enable(True)
-    for _ in range(args.warmup):
-        fused(mc)()
-    torch.cuda.synchronize()
-    pr.pr_profile_read()
-    pr.pr_profile_enable(True)  # restart counters: timed region only
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         fused(mc)()
     torch.cuda.synchronize()
-    el = time.perf_counter() - t0
+    el_prof = time.perf_counter() - t0
     prof = pr.pr_profile_read()
     pr.pr_profile_enable(False)
-    value = T * args.steps / el
-    ms_step = el * 1e3 / args.steps
-    tflops = flops * args.steps / el / 1e12
 
     g_launch_s = prof["gemm_ms"] / max(prof["gemm_launches"], 1) / 1e3
     a_launch_s = prof["addnorm_ms"] / max(prof["addnorm_launches"], 1) / 1e3
@@ -162,17 +161,22 @@ def main() -> int:
     addnorm_bytes_per_elem = 4 * split + 4 + 4 + 2   # slot planes + r read + r write + out
     gemm_tflops = gemm_flops_per_launch / g_launch_s / 1e12
     addnorm_gbs = addnorm_elems_per_launch * addnorm_bytes_per_elem / a_launch_s / 1e9
-    dom_gemm = prof["gemm_ms"] >= prof["addnorm_ms"]
-    if dom_gemm:
-        roof = {"kernel": "gemm_bf16_kernel", "bound": "mfma", "achieved": gemm_tflops,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
-                "traffic": None, "avg_launch_us": g_launch_s * 1e6,
-                "launches": prof["gemm_launches"]}
-    else:
-        roof = {"kernel": "add_rmsnorm_kernel", "bound": "hbm", "achieved": addnorm_gbs,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": addnorm_gbs / PEAK_HBM_GBS,
-                "traffic": None, "avg_launch_us": a_launch_s * 1e6,
-                "launches": prof["addnorm_launches"]}
+    # Measured HBM bytes per projection launch, from the committed counter runs; null unless
+    # they were taken on this exact kernel source and this workload / chunk size.
+    traffic = None
+    if args.traffic_file and os.path.exists(args.traffic_file):
+        from projection_residual_rmsnorm_amd.profiling import source_digest
+        with open(args.traffic_file) as f:
+            tr = json.load(f)
+        src = os.path.join(ROOT, "projection_residual_rmsnorm_amd", "csrc", "pr_kernels.hip")
+        if (tr.get("kernel_source_sha256") == source_digest(src)
+                and tr.get("config") == f"{wl.name}:mc={mc}"):
+            traffic = tr.get("gemm_bytes_per_launch")
+    roof = {"kernel": "gemm_bf16_kernel", "bound": "mfma", "achieved": gemm_tflops,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic, "avg_launch_us": g_launch_s * 1e6,
+            "launches": prof["gemm_launches"], "flops_per_launch": gemm_flops_per_launch,
+            "timed_pass_ms_per_step": el_prof * 1e3 / args.steps}
     kernels = {"gemm_avg_us": g_launch_s * 1e6, "gemm_tflops": gemm_tflops,
                "addnorm_avg_us": a_launch_s * 1e6, "addnorm_gbs": addnorm_gbs,
                "addnorm_bytes_per_elem": addnorm_bytes_per_elem, "split_k": split}
@@ -186,10 +190,16 @@ def main() -> int:
                    "path": "fused microchunk pipeline", "parallelism": "none (1 GPU)"},
         "tflops": tflops, "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "roofline": roof, "kernels": kernels,
-        "per_microchunk": {str(k): {kk: vv for kk, vv in v.items() if kk != "profile"}
-                           for k, v in per_mc.items()},
+        "per_microchunk": {str(k): v for k, v in per_mc.items()},
         "conventional": conv,
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log(f"timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
         result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)

@@ -163,8 +163,12 @@ typedef struct {
 int pr_select(int T, int K, int H, int microchunk, pr_decision* d);
 
 /* Dry-run schedule of the microchunk pipeline: the ordered list of operations the library
- * enqueues for T tokens and chunk size mc (host order).  Returns the number of operations
- * (written up to max_ops), or a negative error. */
+ * enqueues for T tokens and chunk size mc (host order).  Stream B needs no entry wait of its
+ * own (its first operation waits for chunk 0's projection, which waited for the entry);
+ * done[slot] is recorded only where a later operation waits for it (slot reuse three chunks
+ * on, and the join); a record that directly follows the launch it marks is signalled by that
+ * launch itself.  Returns the number of operations (written up to max_ops), or a negative
+ * error. */
 typedef struct {
   int op;     /* PR_OP_*                                       */
   int stream; /* 0 = caller's stream, 1 = projection stream A, 2 = add/norm stream B */
@@ -174,7 +178,7 @@ typedef struct {
 } pr_plan_op;
 
 #define PR_OP_RECORD_ENTRY 0 /* caller stream: record the entry event                   */
-#define PR_OP_WAIT_ENTRY 1   /* stream A or B: wait for the entry event                  */
+#define PR_OP_WAIT_ENTRY 1   /* stream A: wait for the entry event                       */
 #define PR_OP_WAIT_DONE 2    /* stream A: wait done[slot] before overwriting the slot    */
 #define PR_OP_GEMM 3         /* stream A: projection of the chunk into slot              */
 #define PR_OP_RECORD_READY 4 /* stream A: record ready[slot]                             */
@@ -182,6 +186,7 @@ typedef struct {
 #define PR_OP_ADDNORM 6      /* stream B: residual add + RMSNorm of the chunk from slot  */
 #define PR_OP_RECORD_DONE 7  /* stream B: record done[slot]                              */
 #define PR_OP_JOIN 8         /* caller stream: wait done[slot] of the last chunk         */
+#define PR_OP_WAIT_PREV 9    /* stream A: wait for the previous call's last add/norm     */
 #define PR_NUM_SLOTS 3
 
 int pr_plan(int T, int microchunk, pr_plan_op* ops, int max_ops);

@@ -114,10 +114,13 @@ static int apply_forced_tile(int K, GemmCfg* g) {
 // HBM/MALL time of the extra fp32 partial planes that a K split writes and the add/norm reads.
 // ---------------------------------------------------------------------------------------------
 GemmCfg choose_gemm(int M, int N, int K, bool fp32_out) {
-  static const double kEff[kNumTileCfgs] = {1.0, 0.85, 0.6};
-  const double per_cu_flops = 2.5e15 / kNumCUs;
+  // Sustained fraction of the 256x256 tile's rate per tile shape (measured with two waves per
+  // SIMD), and a fixed per-workgroup cost of about three K-stages (prologue + epilogue).
+  static const double kEff[kNumTileCfgs] = {1.0, 0.8, 0.65};
+  const double per_cu_flops = 1.2e15 / kNumCUs;  // sustained 256x256 rate per CU
   const double bw = 5.0e12;
   GemmCfg best;
+  best.waves = 8;
   double best_t = std::numeric_limits<double>::infinity();
   for (int c = 0; c < kNumTileCfgs; ++c) {
     const int bm = kTileBM[c], bn = kTileBN[c];
@@ -126,7 +129,7 @@ GemmCfg choose_gemm(int M, int N, int K, bool fp32_out) {
       if (K % (64 * split) != 0) break;
       const long long units = tiles * split;
       const long long rounds = (units + kNumCUs - 1) / kNumCUs;
-      const double t_mfma = (double)rounds * 2.0 * bm * bn * (double)(K / split) /
+      const double t_mfma = (double)rounds * 2.0 * bm * bn * (double)(K / split + 96) /
                             (per_cu_flops * kEff[c]);
       // bytes of y moved between projection and add/norm beyond a single bf16 (conventional)
       // or fp32 (pipeline) plane
@@ -322,7 +325,7 @@ int pr_plan(int T, int microchunk, pr_plan_op* ops, int max_ops) {
   const int nc = (T + microchunk - 1) / microchunk;
   emit(PR_OP_RECORD_ENTRY, 0, -1, -1, 0);
   emit(PR_OP_WAIT_ENTRY, 1, -1, -1, 0);
-  emit(PR_OP_WAIT_ENTRY, 2, -1, -1, 0);
+  emit(PR_OP_WAIT_PREV, 1, -1, -1, 0);
   for (int c = 0; c < nc; ++c) {
     const int s = c % PR_NUM_SLOTS;
     const int rows = std::min(microchunk, T - c * microchunk);
@@ -331,7 +334,7 @@ int pr_plan(int T, int microchunk, pr_plan_op* ops, int max_ops) {
     emit(PR_OP_RECORD_READY, 1, c, s, 0);
     emit(PR_OP_WAIT_READY, 2, c, s, 0);
     emit(PR_OP_ADDNORM, 2, c, s, rows);
-    emit(PR_OP_RECORD_DONE, 2, c, s, 0);
+    if (c + PR_NUM_SLOTS < nc || c == nc - 1) emit(PR_OP_RECORD_DONE, 2, c, s, 0);
   }
   emit(PR_OP_JOIN, 0, nc - 1, (nc - 1) % PR_NUM_SLOTS, 0);
   return n;

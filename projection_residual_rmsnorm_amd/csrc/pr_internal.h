@@ -50,15 +50,20 @@ namespace pr {
 // y = x . W^T for M rows.  x [M][K] bf16 (row stride K), Wp the prepared weight (K*N).
 // fp32 mode: C planes [split][M][N] at plane stride `plane_stride` elements.
 // bf16 mode (split must be 1): C is [M][N] bf16, rounded to nearest even.
+// done_event (a hipEvent_t or NULL) is signalled when the launch completes; start_timing /
+// stop_timing (hipEvent_t or NULL) take the dispatch's own start and end times.
 int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
-                int K, const GemmCfg& cfg, long long plane_stride, void* stream);
+                int K, const GemmCfg& cfg, long long plane_stride, void* stream,
+                void* done_event = nullptr, void* start_timing = nullptr,
+                void* stop_timing = nullptr);
 
 // r <- r + y; out = RMSNorm(r) for `rows` rows of width H.
 // y: fp32 planes [nplanes][rows][H] (summed in plane order) or bf16 [rows][H] (y_bf16 != 0).
 // round_y: round the summed fp32 y to bf16 before the add (conventional semantics).
 int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_stride,
                        int round_y, float* r, const float* w, uint16_t* out, int rows, int H,
-                       float eps, int gemma, void* stream);
+                       float eps, int gemma, void* stream, void* done_event = nullptr,
+                       void* start_timing = nullptr, void* stop_timing = nullptr);
 
 int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,
                           void* stream);

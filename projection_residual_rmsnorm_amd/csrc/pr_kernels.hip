@@ -9,9 +9,11 @@
 //    ("TPSP Design" section 3: the fused path updates the residual and returns normalised
 //    states; "Plugin Architecture" page, GemmaRMSNorm row: fp32 weight multiply).  HBM-bound.
 //  * prepare_weight kernels: the one-time layout change of the weight after load.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 
 #include "pr_internal.h"
 
@@ -247,38 +249,49 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
   }
 
   // Epilogue.  32x32 fp32 accumulator layout: lane l, element e holds
-  // row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-  const int row_base = m0 + wm * WTM + (lane >> 5) * 4;
-  const int col_base = n0 + wn * WTN + (lane & 31);
-  if (Cf != nullptr) {
-    float* Cz = Cf + (long long)z * plane_stride;
+  // row 8*(e/4) + 4*(l/32) + e%4, column l%32.  Each wave passes its tile through its own LDS
+  // region 16 rows at a time (row stride padded by 4 floats) and writes it back with 16-byte,
+  // row-contiguous stores.  The regions live in the first two stage buffers.
+  __syncthreads();  // every wave is past its last fragment read of the stage buffers
+  constexpr int EP_LD = WTN + 4;            // floats per staged row
+  constexpr int EP_BYTES = 16 * EP_LD * 4;  // one 16-row slice of a wave tile
+  constexpr int EP_PER_BUF = STAGE / EP_BYTES;
+  static_assert(NW <= 2 * EP_PER_BUF, "epilogue staging must fit in two stage buffers");
+  float* ep = reinterpret_cast<float*>((wave < EP_PER_BUF ? sb0 : sb1) +
+                                       (wave % EP_PER_BUF) * EP_BYTES);
+  constexpr int LPR = WTN / 4;  // lanes per staged row (4 floats each)
+  constexpr int RPI = 64 / LPR; // rows per read instruction
+  const int rcol = (lane % LPR) * 4;
+  const int col = n0 + wn * WTN + rcol;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = col_base + j * 32;
-        if (col >= N) continue;
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = row_base + i * 32 + (e >> 2) * 8 + (e & 3);
-          if (row < M) Cz[(long long)row * N + col] = acc[i][j][e];
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 8 * h; e < 8 * h + 8; ++e)
+          ep[(((e >> 2) - 2 * h) * 8 + (lane >> 5) * 4 + (e & 3)) * EP_LD + j * 32 + (lane & 31)] =
+              acc[i][j][e];
+      __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);
+#pragma unroll
+      for (int rr = 0; rr < 16 / RPI; ++rr) {
+        const int r_in = rr * RPI + lane / LPR;
+        const float4 v = *reinterpret_cast<const float4*>(ep + r_in * EP_LD + rcol);
+        const int row = m0 + wm * WTM + i * 32 + h * 16 + r_in;
+        if (row < M && col < N) {
+          if (Cf != nullptr) {
+            *reinterpret_cast<float4*>(Cf + (long long)z * plane_stride + (long long)row * N +
+                                       col) = v;
+          } else {
+            const uint32_t lo = f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16);
+            const uint32_t hi = f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16);
+            *reinterpret_cast<uint2*>(Cb + (long long)row * N + col) = make_uint2(lo, hi);
+          }
         }
-        __builtin_amdgcn_sched_barrier(0);  // one 32x32 tile live in VGPRs at a time
       }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = col_base + j * 32;
-        if (col >= N) continue;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = row_base + i * 32 + (e >> 2) * 8 + (e & 3);
-          if (row < M) Cb[(long long)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);  // reads done before the next slice overwrites
+    }
   }
 }
 
@@ -298,62 +311,82 @@ __device__ __forceinline__ float4 round_bf16_4(float4 v) {
                      bf16_to_f32(f32_to_bf16_rne(v.z)), bf16_to_f32(f32_to_bf16_rne(v.w)));
 }
 
-template <int NV>
-__global__ void __launch_bounds__(256)
+// Rows are split over WPR waves (WPR = 1, 2, 4, 8): wave w of a row holds the columns
+// [w*H/WPR, (w+1)*H/WPR) as NV float4 per lane (H = 256 * NV * WPR).  The wave partial sums of
+// squares meet in LDS and are added in wave order, so the result does not depend on timing.
+template <int NV, int WPR>
+__global__ void __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR)
     add_rmsnorm_kernel(const float* __restrict__ yf, const uint16_t* __restrict__ yb,
                        int nplanes, long long plane_stride, int round_y, float* __restrict__ r,
                        const float* __restrict__ w, uint16_t* __restrict__ out, int rows, int H,
                        float eps, int gemma) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int RPB = WPR <= 4 ? 4 / WPR : 1;  // rows per workgroup
+  __shared__ float part[RPB][WPR];
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const long long base = (long long)row * H;
+  const int row_in = wave / WPR;
+  const int wr = wave % WPR;
+  const int row = blockIdx.x * RPB + row_in;
+  const bool live = row < rows;
+  const long long base = (long long)(live ? row : 0) * H + wr * (H / WPR);
   float4 v[NV];
   float ss = 0.0f;
-  if (yb != nullptr) {
+  if (live) {
+    if (yb != nullptr) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int c = (i * 64 + lane) * 4;
-      const float4 rv = *reinterpret_cast<const float4*>(r + base + c);
-      const uint2 yv = *reinterpret_cast<const uint2*>(yb + base + c);
-      v[i] = make_float4(rv.x + bf16_to_f32(yv.x & 0xffffu), rv.y + bf16_to_f32(yv.x >> 16),
-                         rv.z + bf16_to_f32(yv.y & 0xffffu), rv.w + bf16_to_f32(yv.y >> 16));
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int c = (i * 64 + lane) * 4;
-      const float4 rv = *reinterpret_cast<const float4*>(r + base + c);
-      float4 yv = *reinterpret_cast<const float4*>(yf + base + c);
-      for (int p = 1; p < nplanes; ++p) {
-        const float4 q = *reinterpret_cast<const float4*>(yf + p * plane_stride + base + c);
-        yv.x += q.x;
-        yv.y += q.y;
-        yv.z += q.z;
-        yv.w += q.w;
+      for (int i = 0; i < NV; ++i) {
+        const int c = (i * 64 + lane) * 4;
+        const float4 rv = *reinterpret_cast<const float4*>(r + base + c);
+        const uint2 yv = *reinterpret_cast<const uint2*>(yb + base + c);
+        v[i] = make_float4(rv.x + bf16_to_f32(yv.x & 0xffffu), rv.y + bf16_to_f32(yv.x >> 16),
+                           rv.z + bf16_to_f32(yv.y & 0xffffu), rv.w + bf16_to_f32(yv.y >> 16));
       }
-      if (round_y) yv = round_bf16_4(yv);
-      v[i] = make_float4(rv.x + yv.x, rv.y + yv.y, rv.z + yv.z, rv.w + yv.w);
-    }
-  }
+    } else {
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c = (i * 64 + lane) * 4;
-    *reinterpret_cast<float4*>(r + base + c) = v[i];
-    ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+      for (int i = 0; i < NV; ++i) {
+        const int c = (i * 64 + lane) * 4;
+        const float4 rv = *reinterpret_cast<const float4*>(r + base + c);
+        float4 yv = *reinterpret_cast<const float4*>(yf + base + c);
+        for (int p = 1; p < nplanes; ++p) {
+          const float4 q = *reinterpret_cast<const float4*>(yf + p * plane_stride + base + c);
+          yv.x += q.x;
+          yv.y += q.y;
+          yv.z += q.z;
+          yv.w += q.w;
+        }
+        if (round_y) yv = round_bf16_4(yv);
+        v[i] = make_float4(rv.x + yv.x, rv.y + yv.y, rv.z + yv.z, rv.w + yv.w);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = (i * 64 + lane) * 4;
+      *reinterpret_cast<float4*>(r + base + c) = v[i];
+      ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    }
+    ss = wave_sum(ss);
   }
-  ss = wave_sum(ss);
+  if (WPR > 1) {
+    if (lane == 0) part[row_in][wr] = ss;
+    __syncthreads();
+    ss = 0.0f;
+#pragma unroll
+    for (int q = 0; q < WPR; ++q) ss += part[row_in][q];
+  }
+  if (!live) return;
   const float inv = 1.0f / sqrtf(ss / (float)H + eps);
   const float g0 = gemma ? 1.0f : 0.0f;
+  const float* wc = w + wr * (H / WPR);
+  uint16_t* oc = out + base;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = (i * 64 + lane) * 4;
-    const float4 g = *reinterpret_cast<const float4*>(w + c);
+    const float4 g = *reinterpret_cast<const float4*>(wc + c);
     const uint32_t o0 = f32_to_bf16_rne(v[i].x * inv * (g.x + g0));
     const uint32_t o1 = f32_to_bf16_rne(v[i].y * inv * (g.y + g0));
     const uint32_t o2 = f32_to_bf16_rne(v[i].z * inv * (g.z + g0));
     const uint32_t o3 = f32_to_bf16_rne(v[i].w * inv * (g.w + g0));
-    *reinterpret_cast<uint2*>(out + base + c) = make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+    *reinterpret_cast<uint2*>(oc + c) = make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
   }
 }
 
@@ -470,46 +503,91 @@ int check_launch(const char* what) {
   return PR_OK;
 }
 
+// Completion event of a launch: an event record right after it on the same stream.
+int record_after(int rc, hipEvent_t done, hipStream_t s) {
+  if (rc != PR_OK || done == nullptr) return rc;
+  const hipError_t e = hipEventRecord(done, s);
+  if (e != hipSuccess) return fail(PR_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  return PR_OK;
+}
+
+// The extended launch signals the event from the dispatch itself, which costs the host less
+// than a separate record; PR_EXT_LAUNCH=0 selects launch + record.
+bool ext_launch_events() {
+  const char* v = std::getenv("PR_EXT_LAUNCH");
+  return v == nullptr || v[0] != '0';
+}
+
 template <int BM, int BN, int NB, int WM, int WN>
 int launch_gemm_t(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
-                  int K, int split, long long plane_stride, hipStream_t s) {
+                  int K, int split, long long plane_stride, hipStream_t s, hipEvent_t done,
+                  hipEvent_t t0, hipEvent_t t1) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
   const int k_len = K / split;
   const unsigned grid = (unsigned)(tiles_m * tiles_n * split);
   float* cf = bf16_out ? nullptr : static_cast<float*>(C);
   uint16_t* cb = bf16_out ? static_cast<uint16_t*>(C) : nullptr;
+  if (t0 != nullptr) {
+    // Timed launch: the dispatch records its own start and end; the completion event follows.
+    hipExtLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NB, WM, WN>), dim3(grid), dim3(WM * WN * 64),
+                          0, s, t0, t1, 0, x, Wp, cf, cb, M, N, K, k_len, plane_stride, tiles_m,
+                          tiles_n, split);
+    return record_after(check_launch("gemm_bf16_kernel"), done, s);
+  }
+  if (done != nullptr && ext_launch_events()) {
+    // The completion event is signalled by the dispatch itself.
+    hipExtLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NB, WM, WN>), dim3(grid), dim3(WM * WN * 64),
+                          0, s, nullptr, done, 0, x, Wp, cf, cb, M, N, K, k_len, plane_stride,
+                          tiles_m, tiles_n, split);
+    return check_launch("gemm_bf16_kernel");
+  }
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NB, WM, WN>), dim3(grid), dim3(WM * WN * 64), 0, s,
                      x, Wp, cf, cb, M, N, K, k_len, plane_stride, tiles_m, tiles_n, split);
-  return check_launch("gemm_bf16_kernel");
+  return record_after(check_launch("gemm_bf16_kernel"), done, s);
 }
 
 template <int BM, int BN, int WM, int WN>
 int launch_gemm_nb(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
-                   int K, int split, long long plane_stride, hipStream_t s) {
+                   int K, int split, long long plane_stride, hipStream_t s, hipEvent_t done,
+                   hipEvent_t t0, hipEvent_t t1) {
   // Ring depth: 4 stage buffers when K per split is a multiple of 4 stages, else 2 (K per split
   // is always a multiple of 64, i.e. of 2 stages).
   if ((K / split) % (4 * kBK) == 0)
-    return launch_gemm_t<BM, BN, 4, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s);
-  return launch_gemm_t<BM, BN, 2, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s);
+    return launch_gemm_t<BM, BN, 4, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s, done, t0, t1);
+  return launch_gemm_t<BM, BN, 2, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s, done, t0, t1);
 }
 
-template <int NV>
+template <int NV, int WPR>
 int launch_addnorm_t(const void* y, int y_bf16, int nplanes, long long plane_stride, int round_y,
                      float* r, const float* w, uint16_t* out, int rows, int H, float eps,
-                     int gemma, hipStream_t s) {
-  const unsigned grid = (unsigned)((rows + 3) / 4);
-  hipLaunchKernelGGL((add_rmsnorm_kernel<NV>), dim3(grid), dim3(256), 0, s,
+                     int gemma, hipStream_t s, hipEvent_t done, hipEvent_t t0, hipEvent_t t1) {
+  constexpr int RPB = WPR <= 4 ? 4 / WPR : 1;
+  const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
+  if (t0 != nullptr || (done != nullptr && ext_launch_events())) {
+    hipExtLaunchKernelGGL((add_rmsnorm_kernel<NV, WPR>), dim3(grid), dim3(64 * WPR * RPB), 0, s,
+                          t0, t0 != nullptr ? t1 : done, 0,
+                          y_bf16 ? nullptr : static_cast<const float*>(y),
+                          y_bf16 ? static_cast<const uint16_t*>(y) : nullptr, nplanes,
+                          plane_stride, round_y, r, w, out, rows, H, eps, gemma);
+    return t0 != nullptr ? record_after(check_launch("add_rmsnorm_kernel"), done, s)
+                         : check_launch("add_rmsnorm_kernel");
+  }
+  hipLaunchKernelGGL((add_rmsnorm_kernel<NV, WPR>), dim3(grid), dim3(64 * WPR * RPB), 0, s,
                      y_bf16 ? nullptr : static_cast<const float*>(y),
                      y_bf16 ? static_cast<const uint16_t*>(y) : nullptr, nplanes, plane_stride,
                      round_y, r, w, out, rows, H, eps, gemma);
-  return check_launch("add_rmsnorm_kernel");
+  return record_after(check_launch("add_rmsnorm_kernel"), done, s);
 }
 
 }  // namespace
 
 int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
-                int K, const GemmCfg& cfg, long long plane_stride, void* stream) {
+                int K, const GemmCfg& cfg, long long plane_stride, void* stream, void* done_event,
+                void* start_timing, void* stop_timing) {
+  hipEvent_t done = static_cast<hipEvent_t>(done_event);
+  hipEvent_t t0 = static_cast<hipEvent_t>(start_timing);
+  hipEvent_t t1 = static_cast<hipEvent_t>(stop_timing);
   if (M <= 0) return PR_OK;
   if (K % (2 * kBK * cfg.split) != 0 || N % 64 != 0 || (bf16_out && cfg.split != 1))
     return fail(PR_ERR_SHAPE, "projection shape M=%d N=%d K=%d split=%d not supported", M, N, K,
@@ -517,41 +595,56 @@ int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool eight = cfg.waves == 8;
   if (cfg.bm == 256 && cfg.bn == 256)
-    return eight ? launch_gemm_nb<256, 256, 2, 4>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s)
-                 : launch_gemm_nb<256, 256, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
+    return eight ? launch_gemm_nb<256, 256, 2, 4>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1)
+                 : launch_gemm_nb<256, 256, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1);
   if (cfg.bm == 256 && cfg.bn == 128)
-    return eight ? launch_gemm_nb<256, 128, 4, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s)
-                 : launch_gemm_nb<256, 128, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
+    return eight ? launch_gemm_nb<256, 128, 4, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1)
+                 : launch_gemm_nb<256, 128, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1);
   if (cfg.bm == 128 && cfg.bn == 128)
-    return eight ? launch_gemm_nb<128, 128, 2, 4>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s)
-                 : launch_gemm_nb<128, 128, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s);
+    return eight ? launch_gemm_nb<128, 128, 2, 4>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1)
+                 : launch_gemm_nb<128, 128, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1);
   return fail(PR_ERR_INVALID_ARG, "no projection tile %dx%d", cfg.bm, cfg.bn);
 }
 
 int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_stride,
                        int round_y, float* r, const float* w, uint16_t* out, int rows, int H,
-                       float eps, int gemma, void* stream) {
+                       float eps, int gemma, void* stream, void* done_event, void* start_timing,
+                       void* stop_timing) {
   if (rows <= 0) return PR_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t done = static_cast<hipEvent_t>(done_event);
+  hipEvent_t t0 = static_cast<hipEvent_t>(start_timing);
+  hipEvent_t t1 = static_cast<hipEvent_t>(stop_timing);
+  // Waves per row: as many as keep >= 1 float4 per lane, until the launch has >= 2048 waves.
   if (H % 256 == 0) {
-    switch (H / 256) {
-#define PR_NV_CASE(n) \
-  case n:             \
-    return launch_addnorm_t<n>(y, y_bf16, nplanes, plane_stride, round_y, r, w, out, rows, H, eps, gemma, s);
-      PR_NV_CASE(1) PR_NV_CASE(2) PR_NV_CASE(3) PR_NV_CASE(4) PR_NV_CASE(5) PR_NV_CASE(6)
-      PR_NV_CASE(7) PR_NV_CASE(8) PR_NV_CASE(10) PR_NV_CASE(12) PR_NV_CASE(14) PR_NV_CASE(16)
-      PR_NV_CASE(20) PR_NV_CASE(24) PR_NV_CASE(28) PR_NV_CASE(32)
-#undef PR_NV_CASE
-      default:
-        break;
-    }
+    const int n4 = H / 256;  // float4 per lane for one wave per row
+    int wpr = 1;
+    while (wpr < 8 && n4 % (2 * wpr) == 0 && (long long)rows * wpr < 2048) wpr *= 2;
+    const int nv = n4 / wpr;
+#define PR_AN(NV_, W_)                                                                        \
+  if (nv == NV_ && wpr == W_)                                                                 \
+    return launch_addnorm_t<NV_, W_>(y, y_bf16, nplanes, plane_stride, round_y, r, w, out, rows, \
+                                     H, eps, gemma, s, done, t0, t1);
+#define PR_AN_ALL(NV_) PR_AN(NV_, 1) PR_AN(NV_, 2) PR_AN(NV_, 4) PR_AN(NV_, 8)
+    PR_AN_ALL(1) PR_AN_ALL(2) PR_AN_ALL(3) PR_AN_ALL(4) PR_AN_ALL(5) PR_AN_ALL(6) PR_AN_ALL(7)
+    PR_AN_ALL(8) PR_AN_ALL(10) PR_AN_ALL(12) PR_AN_ALL(14) PR_AN_ALL(16) PR_AN_ALL(20)
+    PR_AN_ALL(24) PR_AN_ALL(28) PR_AN_ALL(32)
+#undef PR_AN_ALL
+#undef PR_AN
   }
   const unsigned grid = (unsigned)((rows + 3) / 4);
+  if (t0 != nullptr) {
+    hipExtLaunchKernelGGL(add_rmsnorm_generic_kernel, dim3(grid), dim3(256), 0, s, t0, t1, 0,
+                          y_bf16 ? nullptr : static_cast<const float*>(y),
+                          y_bf16 ? static_cast<const uint16_t*>(y) : nullptr, nplanes,
+                          plane_stride, round_y, r, w, out, rows, H, eps, gemma);
+    return record_after(check_launch("add_rmsnorm_generic_kernel"), done, s);
+  }
   hipLaunchKernelGGL(add_rmsnorm_generic_kernel, dim3(grid), dim3(256), 0, s,
                      y_bf16 ? nullptr : static_cast<const float*>(y),
                      y_bf16 ? static_cast<const uint16_t*>(y) : nullptr, nplanes, plane_stride,
                      round_y, r, w, out, rows, H, eps, gemma);
-  return check_launch("add_rmsnorm_generic_kernel");
+  return record_after(check_launch("add_rmsnorm_generic_kernel"), done, s);
 }
 
 int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,

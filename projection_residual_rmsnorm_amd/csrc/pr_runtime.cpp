@@ -39,6 +39,7 @@ struct DevCtx {
   uint16_t* out_ws = nullptr;  // borrowed output
   size_t out_ws_bytes = 0;
   const uint16_t* last_borrowed = nullptr;
+  int prev_done_slot = -1;  // slot whose done event closes the previous pipeline call
   // kernel timing (pr_profile_enable)
   std::vector<hipEvent_t> ev_pool;
   struct Timed {
@@ -77,16 +78,15 @@ int take_event(DevCtx* c, hipEvent_t* e) {
   return PR_OK;
 }
 
-// Runs `launch` bracketed by timing events on stream s when profiling is on.
+// Runs launch(start, stop): with profiling on, the dispatch records its own start and end
+// into two timing events (extended launch), else both are NULL.
 template <typename F>
-int timed(DevCtx* c, int kind, hipStream_t s, F&& launch) {
-  if (!g_profile) return launch();
+int timed(DevCtx* c, int kind, F&& launch) {
+  if (!g_profile) return launch(nullptr, nullptr);
   DevCtx::Timed t{nullptr, nullptr, kind};
   PR_TRY(take_event(c, &t.start));
   PR_TRY(take_event(c, &t.stop));
-  PR_HIP(hipEventRecord(t.start, s));
-  const int rc = launch();
-  PR_HIP(hipEventRecord(t.stop, s));
+  const int rc = launch(t.start, t.stop);
   c->pending.push_back(t);
   return rc;
 }
@@ -120,10 +120,13 @@ int get_ctx(DevCtx** out) {
   // Default-priority, non-blocking streams.
   PR_HIP(hipStreamCreateWithFlags(&c->sA, hipStreamNonBlocking));
   PR_HIP(hipStreamCreateWithFlags(&c->sB, hipStreamNonBlocking));
-  PR_HIP(hipEventCreateWithFlags(&c->entry, hipEventDisableTiming));
+  // Default-flag events throughout: the dispatches signal ready/done themselves (extended
+  // launch), and a stream wait on such an event is much cheaper on the host than on an event
+  // created with hipEventDisableTiming.
+  PR_HIP(hipEventCreate(&c->entry));
   for (int s = 0; s < PR_NUM_SLOTS; ++s) {
-    PR_HIP(hipEventCreateWithFlags(&c->ready[s], hipEventDisableTiming));
-    PR_HIP(hipEventCreateWithFlags(&c->done[s], hipEventDisableTiming));
+    PR_HIP(hipEventCreate(&c->ready[s]));
+    PR_HIP(hipEventCreate(&c->done[s]));
   }
   g_ctx[dev] = c;
   *out = c;
@@ -153,7 +156,8 @@ int grow(void** p, size_t* have, size_t need) {
 // Projection over M rows; launches are split by rows so that one launch's x slice stays
 // below 2^30 elements (the kernel uses 32-bit offsets).
 int gemm_rows(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N, int K,
-              const GemmCfg& cfg, long long plane_stride, hipStream_t s) {
+              const GemmCfg& cfg, long long plane_stride, hipStream_t s,
+              hipEvent_t done = nullptr, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr) {
   if (fault_injected()) return fail(PR_ERR_HIP, "injected launch failure (PR_FAULT_INJECT)");
   long long rows_per = ((1LL << 30) / K) / cfg.bm * cfg.bm;
   if (rows_per <= 0) return fail(PR_ERR_SHAPE, "K=%d too large", K);
@@ -161,7 +165,12 @@ int gemm_rows(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int
     const int rows = (int)std::min<long long>(rows_per, M - r0);
     void* Cr = bf16_out ? (void*)(static_cast<uint16_t*>(C) + r0 * N)
                         : (void*)(static_cast<float*>(C) + r0 * N);
-    PR_TRY(launch_gemm(x + r0 * K, Wp, Cr, bf16_out, rows, N, K, cfg, plane_stride, s));
+    const bool first = r0 == 0, last = r0 + rows_per >= M;
+    // timing spans the first launch's start to the last launch's end
+    PR_TRY(launch_gemm(x + r0 * K, Wp, Cr, bf16_out, rows, N, K, cfg, plane_stride, s,
+                       last ? done : nullptr, t0 != nullptr && first ? t0 : nullptr,
+                       t0 != nullptr && first ? (last ? t1 : nullptr) : nullptr));
+    if (t0 != nullptr && last && !first) PR_HIP(hipEventRecord(t1, s));
   }
   return PR_OK;
 }
@@ -191,18 +200,22 @@ int run_conventional(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, 
   const long long plane = (long long)T * H;
   if (g.split == 1) {
     PR_TRY(grow(&c->conv, &c->conv_bytes, (size_t)plane * 2));
-    PR_TRY(timed(c, 0, s, [&] { return gemm_rows(x, W, c->conv, true, T, H, K, g, plane, s); }));
-    PR_TRY(timed(c, 1, s, [&] {
+    PR_TRY(timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
+      return gemm_rows(x, W, c->conv, true, T, H, K, g, plane, s, nullptr, t0, t1);
+    }));
+    PR_TRY(timed(c, 1, [&](hipEvent_t t0, hipEvent_t t1) {
       return launch_add_rmsnorm(c->conv, 1, 1, plane, 0, r, w, out, T, H, eps,
-                                norm_kind == PR_NORM_GEMMA, s);
+                                norm_kind == PR_NORM_GEMMA, s, nullptr, t0, t1);
     }));
   } else {
     // K split: fp32 partial planes, summed and rounded to bf16 before the add.
     PR_TRY(grow(&c->conv, &c->conv_bytes, (size_t)plane * 4 * g.split));
-    PR_TRY(timed(c, 0, s, [&] { return gemm_rows(x, W, c->conv, false, T, H, K, g, plane, s); }));
-    PR_TRY(timed(c, 1, s, [&] {
+    PR_TRY(timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
+      return gemm_rows(x, W, c->conv, false, T, H, K, g, plane, s, nullptr, t0, t1);
+    }));
+    PR_TRY(timed(c, 1, [&](hipEvent_t t0, hipEvent_t t1) {
       return launch_add_rmsnorm(c->conv, 0, g.split, plane, 1, r, w, out, T, H, eps,
-                                norm_kind == PR_NORM_GEMMA, s);
+                                norm_kind == PR_NORM_GEMMA, s, nullptr, t0, t1);
     }));
   }
   return PR_OK;
@@ -239,6 +252,11 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
     const pr_plan_op& op = ops[i];
     float* slot = op.slot >= 0 ? c->slots + (size_t)op.slot * c->slot_elems : nullptr;
     const long long row0 = (long long)op.chunk * mc;
+    // A record that directly follows the launch it marks is signalled by the launch.
+    const bool fuse_next = i + 1 < n && ops[i + 1].stream == op.stream &&
+                           ((op.op == PR_OP_GEMM && ops[i + 1].op == PR_OP_RECORD_READY) ||
+                            (op.op == PR_OP_ADDNORM && ops[i + 1].op == PR_OP_RECORD_DONE &&
+                             !poison));
     switch (op.op) {
       case PR_OP_RECORD_ENTRY:
         PR_HIP(hipEventRecord(c->entry, caller));
@@ -246,15 +264,23 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
       case PR_OP_WAIT_ENTRY:
         PR_HIP(hipStreamWaitEvent(stream_of(op.stream), c->entry, 0));
         break;
+      case PR_OP_WAIT_PREV:
+        // The previous call's last add/norm may still be reading a slot (the caller may have
+        // switched streams); the stream is in order, so its last done event covers it all.
+        if (c->prev_done_slot >= 0)
+          PR_HIP(hipStreamWaitEvent(c->sA, c->done[c->prev_done_slot], 0));
+        break;
       case PR_OP_WAIT_DONE:
         PR_HIP(hipStreamWaitEvent(c->sA, c->done[op.slot], 0));
         break;
       case PR_OP_GEMM:
         if (delay > 0) PR_TRY(launch_delay(delay, c->sA));
-        PR_TRY(timed(c, 0, c->sA, [&] {
+        PR_TRY(timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
           return gemm_rows(x + row0 * K, W, slot, false, op.rows, H, K, g,
-                           (long long)op.rows * H, c->sA);
+                           (long long)op.rows * H, c->sA, fuse_next ? c->ready[op.slot] : nullptr,
+                           t0, t1);
         }));
+        if (fuse_next) ++i;
         break;
       case PR_OP_RECORD_READY:
         PR_HIP(hipEventRecord(c->ready[op.slot], c->sA));
@@ -264,10 +290,12 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
         break;
       case PR_OP_ADDNORM:
         if (delay > 0) PR_TRY(launch_delay(delay, c->sB));
-        PR_TRY(timed(c, 1, c->sB, [&] {
+        PR_TRY(timed(c, 1, [&](hipEvent_t t0, hipEvent_t t1) {
           return launch_add_rmsnorm(slot, 0, g.split, (long long)op.rows * H, 0, r + row0 * H,
-                                    w, out + row0 * H, op.rows, H, eps, gemma, c->sB);
+                                    w, out + row0 * H, op.rows, H, eps, gemma, c->sB,
+                                    fuse_next ? c->done[op.slot] : nullptr, t0, t1);
         }));
+        if (fuse_next) ++i;
         if (poison) PR_TRY(launch_fill_nan(slot, c->slot_elems, c->sB));
         break;
       case PR_OP_RECORD_DONE:
@@ -275,6 +303,7 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
         break;
       case PR_OP_JOIN:
         PR_HIP(hipStreamWaitEvent(caller, c->done[op.slot], 0));
+        c->prev_done_slot = op.slot;
         break;
       default:
         return fail(PR_ERR_INVALID_ARG, "bad plan op %d", op.op);

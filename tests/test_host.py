@@ -157,6 +157,8 @@ def _simulate(ops):
             events["entry"] = dict(tick(0, ("caller_pre",)))
         elif name == "WAIT_ENTRY":
             clocks[stream] = {**clocks[stream], **events["entry"]}
+        elif name == "WAIT_PREV":
+            pass  # orders against the previous call only
         elif name in ("GEMM", "ADDNORM"):
             stamps[(name, chunk)] = (tick(stream, (name, chunk)), slot, rows)
         elif name == "RECORD_READY":
@@ -196,6 +198,7 @@ def test_plan_is_race_free(T, mc):
             assert ("ADDNORM", c) in st[("GEMM", c + 3)][0]
         assert ("ADDNORM", c) in st["join"][0]               # caller waits for every chunk
         assert ("caller_pre",) in st[("GEMM", c)][0]         # nothing starts before entry
+        assert ("caller_pre",) in st[("ADDNORM", c)][0]
         assert st[("GEMM", c)][1] == c % 3
     # overlap is possible: GEMM(c+1) does not depend on ADDNORM(c)
     for c in range(nc - 1):
@@ -205,6 +208,7 @@ def test_plan_is_race_free(T, mc):
 def test_plan_detects_a_missing_wait():
     """The simulator itself catches a schedule without the slot-reuse wait."""
     ops = [o for o in pr.pr_plan(3000, 256) if o[0] != "WAIT_DONE"]
+    assert sum(o[0] == "RECORD_DONE" for o in pr.pr_plan(3000, 256)) == 10  # 9 reused + last
     st = _simulate(ops)
     assert not all(("ADDNORM", c) in st[("GEMM", c + 3)][0] for c in range(9))
 
