@@ -163,30 +163,32 @@ typedef struct {
 int pr_select(int T, int K, int H, int microchunk, pr_decision* d);
 
 /* Dry-run schedule of the microchunk pipeline: the ordered list of operations the library
- * enqueues for T tokens and chunk size mc (host order).  Stream B needs no entry wait of its
- * own (its first operation waits for chunk 0's projection, which waited for the entry);
- * done[slot] is recorded only where a later operation waits for it (slot reuse three chunks
- * on, and the join); a record that directly follows the launch it marks is signalled by that
- * launch itself.  Returns the number of operations (written up to max_ops), or a negative
+ * enqueues for T tokens and chunk size mc (host order).  Chunks alternate between the caller's
+ * stream (even chunks) and a library stream (odd chunks); a chunk's projection and its add/norm
+ * are consecutive on one stream, so chunk c+1's projection on the other stream overlaps chunk
+ * c's add/norm.  Slot c % 3 is reused by chunk c+3, which runs on the other stream and waits
+ * for done[slot]; done[slot] is recorded only where something waits for it, and a record that
+ * follows the launch it marks is signalled by that launch.  The library stream starts after
+ * the caller's prior work (entry event) and the caller's stream waits for the library stream's
+ * last chunk (join).  Returns the number of operations (written up to max_ops), or a negative
  * error. */
 typedef struct {
-  int op;     /* PR_OP_*                                       */
-  int stream; /* 0 = caller's stream, 1 = projection stream A, 2 = add/norm stream B */
-  int chunk;  /* chunk index or -1                             */
-  int slot;   /* slot / event index (chunk % 3) or -1          */
-  int rows;   /* valid rows of the chunk or 0                  */
+  int op;     /* PR_OP_*                                  */
+  int stream; /* 0 = caller's stream, 1 = library stream  */
+  int chunk;  /* chunk index or -1                        */
+  int slot;   /* slot / event index (chunk % 3) or -1     */
+  int rows;   /* valid rows of the chunk or 0             */
 } pr_plan_op;
 
-#define PR_OP_RECORD_ENTRY 0 /* caller stream: record the entry event                   */
-#define PR_OP_WAIT_ENTRY 1   /* stream A: wait for the entry event                       */
-#define PR_OP_WAIT_DONE 2    /* stream A: wait done[slot] before overwriting the slot    */
-#define PR_OP_GEMM 3         /* stream A: projection of the chunk into slot              */
-#define PR_OP_RECORD_READY 4 /* stream A: record ready[slot]                             */
-#define PR_OP_WAIT_READY 5   /* stream B: wait ready[slot]                               */
-#define PR_OP_ADDNORM 6      /* stream B: residual add + RMSNorm of the chunk from slot  */
-#define PR_OP_RECORD_DONE 7  /* stream B: record done[slot]                              */
-#define PR_OP_JOIN 8         /* caller stream: wait done[slot] of the last chunk         */
-#define PR_OP_WAIT_PREV 9    /* stream A: wait for the previous call's last add/norm     */
+#define PR_OP_RECORD_ENTRY 0 /* caller stream: record the entry event                      */
+#define PR_OP_WAIT_ENTRY 1   /* library stream: wait for the entry event                    */
+#define PR_OP_WAIT_DONE 2    /* wait done[slot] (chunk c-3, other stream) before reusing it */
+#define PR_OP_GEMM 3         /* projection of the chunk into slot                           */
+#define PR_OP_ADDNORM 4      /* residual add + RMSNorm of the chunk from slot               */
+#define PR_OP_RECORD_DONE 5  /* record done[slot] after the chunk's add/norm               */
+#define PR_OP_JOIN 6         /* caller stream: wait done[slot] of the library stream's last */
+#define PR_OP_WAIT_PREV 7    /* caller stream: wait for the previous call's last chunks when
+                                that call was made on a different caller stream            */
 #define PR_NUM_SLOTS 3
 
 int pr_plan(int T, int microchunk, pr_plan_op* ops, int max_ops);

@@ -33,8 +33,8 @@ PR_PATH_FUSED = 1
 PR_NUM_SLOTS = 3
 INT32_MAX = 2**31 - 1
 
-OP_NAMES = ["RECORD_ENTRY", "WAIT_ENTRY", "WAIT_DONE", "GEMM", "RECORD_READY", "WAIT_READY",
-            "ADDNORM", "RECORD_DONE", "JOIN", "WAIT_PREV"]
+OP_NAMES = ["RECORD_ENTRY", "WAIT_ENTRY", "WAIT_DONE", "GEMM", "ADDNORM", "RECORD_DONE", "JOIN",
+            "WAIT_PREV"]
 REASON_NAMES = ["explicit", "above_threshold", "below_threshold", "untuned", "inconclusive",
                 "unfused_call"]
 

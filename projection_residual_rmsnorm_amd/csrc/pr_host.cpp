@@ -323,20 +323,31 @@ int pr_plan(int T, int microchunk, pr_plan_op* ops, int max_ops) {
   };
   if (T == 0) return 0;
   const int nc = (T + microchunk - 1) / microchunk;
-  emit(PR_OP_RECORD_ENTRY, 0, -1, -1, 0);
-  emit(PR_OP_WAIT_ENTRY, 1, -1, -1, 0);
-  emit(PR_OP_WAIT_PREV, 1, -1, -1, 0);
+  // Even chunks run on the caller's stream (0), odd chunks on the library stream (1); each
+  // chunk's projection and add/norm are consecutive on one stream, so chunk c+1's projection
+  // on the other stream overlaps chunk c's add/norm.  Slot c % 3 is reused by chunk c + 3,
+  // which always runs on the other stream and waits for done[slot].
+  auto stream_of = [](int c) { return c % 2 == 0 ? 0 : 1; };
+  const int last_even = (nc - 1) % 2 == 0 ? nc - 1 : nc - 2;               // caller stream
+  const int last_odd = nc >= 2 ? ((nc - 1) % 2 == 1 ? nc - 1 : nc - 2) : -1;  // library stream
+  emit(PR_OP_WAIT_PREV, 0, -1, -1, 0);
+  if (nc >= 2) {
+    emit(PR_OP_RECORD_ENTRY, 0, -1, -1, 0);
+    emit(PR_OP_WAIT_ENTRY, 1, -1, -1, 0);
+  }
   for (int c = 0; c < nc; ++c) {
+    const int st = stream_of(c);
     const int s = c % PR_NUM_SLOTS;
     const int rows = std::min(microchunk, T - c * microchunk);
-    if (c >= PR_NUM_SLOTS) emit(PR_OP_WAIT_DONE, 1, c, s, 0);
-    emit(PR_OP_GEMM, 1, c, s, rows);
-    emit(PR_OP_RECORD_READY, 1, c, s, 0);
-    emit(PR_OP_WAIT_READY, 2, c, s, 0);
-    emit(PR_OP_ADDNORM, 2, c, s, rows);
-    if (c + PR_NUM_SLOTS < nc || c == nc - 1) emit(PR_OP_RECORD_DONE, 2, c, s, 0);
+    if (c >= PR_NUM_SLOTS) emit(PR_OP_WAIT_DONE, st, c, s, 0);
+    emit(PR_OP_GEMM, st, c, s, rows);
+    emit(PR_OP_ADDNORM, st, c, s, rows);
+    // done[slot]: waited for by chunk c + 3, by the join (the library stream's last chunk) and
+    // by a next call made from another stream (the last chunk on each stream).
+    if (c + PR_NUM_SLOTS < nc || c == last_even || c == last_odd)
+      emit(PR_OP_RECORD_DONE, st, c, s, 0);
   }
-  emit(PR_OP_JOIN, 0, nc - 1, (nc - 1) % PR_NUM_SLOTS, 0);
+  if (last_odd >= 0) emit(PR_OP_JOIN, 0, last_odd, last_odd % PR_NUM_SLOTS, 0);
   return n;
 }
 

@@ -1,12 +1,13 @@
 // Runtime of the library: per-device resources (two streams, six slot events, the three-slot
 // workspace), the microchunk pipeline executor, the conventional path and the autotuner.
 //
-// Pipeline ("TPSP Design" page, section 3, Microchunk pipeline): chunk c's projection runs on
-// stream A into slot c % 3 and records ready[slot]; stream B waits for it, runs the residual
-// add + RMSNorm of the chunk's valid rows and records done[slot]; stream A waits done[slot]
-// before chunk c + 3 overwrites the slot.  Both streams start after the caller's stream
-// (entry event) and the caller's stream waits for the last done event, so the call is ordered
-// on the caller's stream like a single kernel and never blocks the host.
+// Pipeline ("TPSP Design" page, section 3, Microchunk pipeline): chunks alternate between the
+// caller's stream and one library stream.  On its stream, chunk c's projection writes slot
+// c % 3 and the chunk's residual add + RMSNorm follows it directly, while chunk c+1's
+// projection runs on the other stream.  Chunk c+3 reuses the slot from the other stream and
+// waits for done[slot] first.  The library stream starts after the caller's prior work (entry
+// event) and the caller's stream waits for the library stream's last chunk, so the call is
+// ordered on the caller's stream like a single kernel and never blocks the host.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -27,10 +28,8 @@ constexpr int kMaxDevices = 64;
 
 struct DevCtx {
   int device = -1;
-  hipStream_t sA = nullptr;  // projection stream
-  hipStream_t sB = nullptr;  // add/norm stream
+  hipStream_t sL = nullptr;  // library stream (odd chunks)
   hipEvent_t entry = nullptr;
-  hipEvent_t ready[PR_NUM_SLOTS] = {};
   hipEvent_t done[PR_NUM_SLOTS] = {};
   float* slots = nullptr;  // PR_NUM_SLOTS slots of slot_elems fp32 each
   size_t slot_elems = 0;
@@ -39,7 +38,10 @@ struct DevCtx {
   uint16_t* out_ws = nullptr;  // borrowed output
   size_t out_ws_bytes = 0;
   const uint16_t* last_borrowed = nullptr;
-  int prev_done_slot = -1;  // slot whose done event closes the previous pipeline call
+  // the previous pipeline call: its caller stream and the done slots of its last chunk on
+  // each stream (-1 if none)
+  hipStream_t prev_caller = nullptr;
+  int prev_done_slots[2] = {-1, -1};
   // kernel timing (pr_profile_enable)
   std::vector<hipEvent_t> ev_pool;
   struct Timed {
@@ -118,16 +120,12 @@ int get_ctx(DevCtx** out) {
   DevCtx* c = new DevCtx();
   c->device = dev;
   // Default-priority, non-blocking streams.
-  PR_HIP(hipStreamCreateWithFlags(&c->sA, hipStreamNonBlocking));
-  PR_HIP(hipStreamCreateWithFlags(&c->sB, hipStreamNonBlocking));
-  // Default-flag events throughout: the dispatches signal ready/done themselves (extended
-  // launch), and a stream wait on such an event is much cheaper on the host than on an event
-  // created with hipEventDisableTiming.
+  PR_HIP(hipStreamCreateWithFlags(&c->sL, hipStreamNonBlocking));
+  // Default-flag events throughout: the dispatches signal done themselves (extended launch),
+  // and a stream wait on such an event is much cheaper on the host than on an event created
+  // with hipEventDisableTiming.
   PR_HIP(hipEventCreate(&c->entry));
-  for (int s = 0; s < PR_NUM_SLOTS; ++s) {
-    PR_HIP(hipEventCreate(&c->ready[s]));
-    PR_HIP(hipEventCreate(&c->done[s]));
-  }
+  for (int s = 0; s < PR_NUM_SLOTS; ++s) PR_HIP(hipEventCreate(&c->done[s]));
   g_ctx[dev] = c;
   *out = c;
   return PR_OK;
@@ -247,68 +245,69 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
   std::vector<pr_plan_op> ops(8 + 6 * (size_t)d.n_chunks);
   const int n = pr_plan(T, mc, ops.data(), (int)ops.size());
   if (n < 0) return n;
-  auto stream_of = [&](int id) { return id == 0 ? caller : (id == 1 ? c->sA : c->sB); };
+  auto stream_of = [&](int id) { return id == 0 ? caller : c->sL; };
+  int last_slot[2] = {-1, -1};
   for (int i = 0; i < n; ++i) {
     const pr_plan_op& op = ops[i];
     float* slot = op.slot >= 0 ? c->slots + (size_t)op.slot * c->slot_elems : nullptr;
     const long long row0 = (long long)op.chunk * mc;
-    // A record that directly follows the launch it marks is signalled by the launch.
-    const bool fuse_next = i + 1 < n && ops[i + 1].stream == op.stream &&
-                           ((op.op == PR_OP_GEMM && ops[i + 1].op == PR_OP_RECORD_READY) ||
-                            (op.op == PR_OP_ADDNORM && ops[i + 1].op == PR_OP_RECORD_DONE &&
-                             !poison));
+    hipStream_t st = stream_of(op.stream);
+    // A done record that directly follows the add/norm it marks is signalled by the launch.
+    const bool fuse_next = op.op == PR_OP_ADDNORM && i + 1 < n &&
+                           ops[i + 1].op == PR_OP_RECORD_DONE && ops[i + 1].stream == op.stream &&
+                           !poison;
     switch (op.op) {
+      case PR_OP_WAIT_PREV:
+        // In order on one caller stream (and joined), the previous call needs no wait; a call
+        // from another stream waits for the previous call's last chunk on each stream.
+        if (c->prev_caller != caller)
+          for (int k = 0; k < 2; ++k)
+            if (c->prev_done_slots[k] >= 0)
+              PR_HIP(hipStreamWaitEvent(caller, c->done[c->prev_done_slots[k]], 0));
+        break;
       case PR_OP_RECORD_ENTRY:
         PR_HIP(hipEventRecord(c->entry, caller));
         break;
       case PR_OP_WAIT_ENTRY:
-        PR_HIP(hipStreamWaitEvent(stream_of(op.stream), c->entry, 0));
-        break;
-      case PR_OP_WAIT_PREV:
-        // The previous call's last add/norm may still be reading a slot (the caller may have
-        // switched streams); the stream is in order, so its last done event covers it all.
-        if (c->prev_done_slot >= 0)
-          PR_HIP(hipStreamWaitEvent(c->sA, c->done[c->prev_done_slot], 0));
+        PR_HIP(hipStreamWaitEvent(st, c->entry, 0));
         break;
       case PR_OP_WAIT_DONE:
-        PR_HIP(hipStreamWaitEvent(c->sA, c->done[op.slot], 0));
+        PR_HIP(hipStreamWaitEvent(st, c->done[op.slot], 0));
         break;
       case PR_OP_GEMM:
-        if (delay > 0) PR_TRY(launch_delay(delay, c->sA));
+        if (delay > 0) PR_TRY(launch_delay(delay, st));
         PR_TRY(timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
           return gemm_rows(x + row0 * K, W, slot, false, op.rows, H, K, g,
-                           (long long)op.rows * H, c->sA, fuse_next ? c->ready[op.slot] : nullptr,
-                           t0, t1);
+                           (long long)op.rows * H, st, nullptr, t0, t1);
         }));
-        if (fuse_next) ++i;
-        break;
-      case PR_OP_RECORD_READY:
-        PR_HIP(hipEventRecord(c->ready[op.slot], c->sA));
-        break;
-      case PR_OP_WAIT_READY:
-        PR_HIP(hipStreamWaitEvent(c->sB, c->ready[op.slot], 0));
         break;
       case PR_OP_ADDNORM:
-        if (delay > 0) PR_TRY(launch_delay(delay, c->sB));
+        if (delay > 0) PR_TRY(launch_delay(delay, st));
         PR_TRY(timed(c, 1, [&](hipEvent_t t0, hipEvent_t t1) {
           return launch_add_rmsnorm(slot, 0, g.split, (long long)op.rows * H, 0, r + row0 * H,
-                                    w, out + row0 * H, op.rows, H, eps, gemma, c->sB,
+                                    w, out + row0 * H, op.rows, H, eps, gemma, st,
                                     fuse_next ? c->done[op.slot] : nullptr, t0, t1);
         }));
-        if (fuse_next) ++i;
-        if (poison) PR_TRY(launch_fill_nan(slot, c->slot_elems, c->sB));
+        if (poison) PR_TRY(launch_fill_nan(slot, c->slot_elems, st));
+        if (fuse_next) {
+          last_slot[op.stream] = op.slot;
+          ++i;
+        }
         break;
       case PR_OP_RECORD_DONE:
-        PR_HIP(hipEventRecord(c->done[op.slot], c->sB));
+        PR_HIP(hipEventRecord(c->done[op.slot], st));
+        last_slot[op.stream] = op.slot;
         break;
       case PR_OP_JOIN:
         PR_HIP(hipStreamWaitEvent(caller, c->done[op.slot], 0));
-        c->prev_done_slot = op.slot;
         break;
       default:
         return fail(PR_ERR_INVALID_ARG, "bad plan op %d", op.op);
     }
   }
+  c->prev_caller = caller;
+  c->prev_done_slots[0] = last_slot[0];
+  c->prev_done_slots[1] = last_slot[1];
   return PR_OK;
 }
 

@@ -133,55 +133,61 @@ def test_auto_tuned(monkeypatch):
         pr.pr_set_tuning(64, 64, 1, 10, [4, 2], [1, 1])  # grid must ascend
 
 
-def _simulate(ops):
-    """Vector-clock happens-before over the planned enqueue order.
+def _simulate(calls):
+    """Vector-clock happens-before over the planned enqueue order of one or more calls.
 
-    Streams execute in order; a record snapshots the stream's clock into the event; a wait
-    joins the most recent record of that event at enqueue time (HIP semantics).  Returns the
-    clock of every GEMM / ADDNORM op keyed by (kind, chunk) and of the final join.
+    `calls` is a list of (plan, caller_stream_name).  Streams execute in order; a record
+    snapshots the stream's clock into the event; a wait joins the most recent record of that
+    event at enqueue time (HIP semantics).  WAIT_PREV, for a call on a different caller stream,
+    joins the previous call's last done record on each stream.  Returns per call the clock of
+    every GEMM / ADDNORM, keyed by (kind, chunk), and the caller's clock after the call.
     """
-    clocks = {0: {}, 1: {}, 2: {}}
+    clocks = {}
     events = {}
-    stamps = {}
     counter = [0]
+    out = []
+    prev = None  # (caller name, {stream id: last done event key})
 
     def tick(s, label):
         counter[0] += 1
-        c = dict(clocks[s])
+        c = dict(clocks.get(s, {}))
         c[label] = counter[0]
         clocks[s] = c
         return c
 
-    for name, stream, chunk, slot, rows in ops:
-        if name == "RECORD_ENTRY":
-            events["entry"] = dict(tick(0, ("caller_pre",)))
-        elif name == "WAIT_ENTRY":
-            clocks[stream] = {**clocks[stream], **events["entry"]}
-        elif name == "WAIT_PREV":
-            pass  # orders against the previous call only
-        elif name in ("GEMM", "ADDNORM"):
-            stamps[(name, chunk)] = (tick(stream, (name, chunk)), slot, rows)
-        elif name == "RECORD_READY":
-            events[("ready", slot)] = dict(clocks[stream])
-        elif name == "RECORD_DONE":
-            events[("done", slot)] = dict(clocks[stream])
-        elif name == "WAIT_READY":
-            clocks[stream] = {**clocks[stream], **events[("ready", slot)]}
-        elif name == "WAIT_DONE":
-            clocks[stream] = {**clocks[stream], **events[("done", slot)]}
-        elif name == "JOIN":
-            clocks[0] = {**clocks[0], **events[("done", slot)]}
-            stamps["join"] = (dict(clocks[0]), -1, 0)
-    return stamps
-
-
-def _hb(stamps, a, b):
-    """a happens before b."""
-    return a in stamps[b][0] if isinstance(a, tuple) and len(a) == 2 else False
+    for k, (ops, caller) in enumerate(calls):
+        names = {0: caller, 1: "library"}
+        tick(caller, ("caller_pre", k))
+        stamps = {}
+        last_done = {}
+        for name, stream, chunk, slot, rows in ops:
+            sn = names[stream]
+            if name == "WAIT_PREV":
+                if prev is not None and prev[0] != caller:
+                    for ev in prev[1].values():
+                        clocks[caller] = {**clocks.get(caller, {}), **events[ev]}
+            elif name == "RECORD_ENTRY":
+                events["entry"] = dict(clocks.get(sn, {}))
+            elif name == "WAIT_ENTRY":
+                clocks[sn] = {**clocks.get(sn, {}), **events["entry"]}
+            elif name in ("GEMM", "ADDNORM"):
+                stamps[(name, chunk)] = (tick(sn, (name, chunk, k)), slot, rows, stream)
+            elif name == "RECORD_DONE":
+                events[("done", slot)] = dict(clocks.get(sn, {}))
+                last_done[stream] = ("done", slot)
+            elif name == "WAIT_DONE":
+                clocks[sn] = {**clocks.get(sn, {}), **events[("done", slot)]}
+            elif name == "JOIN":
+                clocks[sn] = {**clocks.get(sn, {}), **events[("done", slot)]}
+            else:
+                raise AssertionError(name)
+        out.append((stamps, dict(clocks.get(caller, {}))))
+        prev = (caller, last_done)
+    return out
 
 
 @pytest.mark.parametrize("T,mc", [(64, 16), (3000, 256), (3000, 1024), (2048, 512), (7, 7),
-                                  (1, 4096), (10, 3), (4096, 4096)])
+                                  (1, 4096), (10, 3), (4096, 4096), (5000, 512)])
 def test_plan_is_race_free(T, mc):
     ops = pr.pr_plan(T, mc)
     nc = -(-T // mc)
@@ -191,26 +197,42 @@ def test_plan_is_race_free(T, mc):
     assert sum(o[4] for o in norms) == T                 # valid rows only, each once
     assert all(o[4] == mc for o in norms[:-1]) and norms[-1][4] == T - (nc - 1) * mc
     assert {o[3] for o in ops if o[3] >= 0} <= {0, 1, 2}  # three reusable slots
-    st = _simulate(ops)
+    (st, caller_end), = _simulate([(ops, "caller")])
     for c in range(nc):
-        assert ("GEMM", c) in st[("ADDNORM", c)][0]          # slot written before it is read
-        if c + 3 < nc:                                        # slot reused only after its read
-            assert ("ADDNORM", c) in st[("GEMM", c + 3)][0]
-        assert ("ADDNORM", c) in st["join"][0]               # caller waits for every chunk
-        assert ("caller_pre",) in st[("GEMM", c)][0]         # nothing starts before entry
-        assert ("caller_pre",) in st[("ADDNORM", c)][0]
+        g, a = ("GEMM", c, 0), ("ADDNORM", c, 0)
+        assert g in st[("ADDNORM", c)][0]                    # slot written before it is read
+        if c + 3 < nc:                                       # slot reused only after its read
+            assert a in st[("GEMM", c + 3)][0]
+        assert a in caller_end                               # caller waits for every chunk
+        assert ("caller_pre", 0) in st[("GEMM", c)][0]       # nothing starts before entry
         assert st[("GEMM", c)][1] == c % 3
-    # overlap is possible: GEMM(c+1) does not depend on ADDNORM(c)
+    # overlap is possible: chunk c+1's projection does not wait for chunk c's add/norm
     for c in range(nc - 1):
-        assert ("ADDNORM", c) not in st[("GEMM", c + 1)][0]
+        assert ("ADDNORM", c, 0) not in st[("GEMM", c + 1)][0]
+
+
+@pytest.mark.parametrize("T1,mc1,T2,mc2", [(2048, 512, 2048, 512), (3000, 256, 700, 128),
+                                           (10, 3, 7, 2), (512, 512, 2048, 256)])
+@pytest.mark.parametrize("same_stream", [True, False])
+def test_consecutive_calls_are_ordered(T1, mc1, T2, mc2, same_stream):
+    """A second call, on the same or on another caller stream, starts each chunk only after
+    every chunk of the first call has finished (they share slots, rows and the residual)."""
+    first, second = pr.pr_plan(T1, mc1), pr.pr_plan(T2, mc2)
+    (st1, end1), (st2, _) = _simulate([(first, "s1"), (second, "s1" if same_stream else "s2")])
+    nc1, nc2 = -(-T1 // mc1), -(-T2 // mc2)
+    for c2 in range(nc2):
+        for c1 in range(nc1):
+            assert ("ADDNORM", c1, 0) in st2[("GEMM", c2)][0], (c1, c2)
 
 
 def test_plan_detects_a_missing_wait():
     """The simulator itself catches a schedule without the slot-reuse wait."""
-    ops = [o for o in pr.pr_plan(3000, 256) if o[0] != "WAIT_DONE"]
-    assert sum(o[0] == "RECORD_DONE" for o in pr.pr_plan(3000, 256)) == 10  # 9 reused + last
-    st = _simulate(ops)
-    assert not all(("ADDNORM", c) in st[("GEMM", c + 3)][0] for c in range(9))
+    full = pr.pr_plan(3000, 256)
+    ops = [o for o in full if o[0] != "WAIT_DONE"]
+    (st, _), = _simulate([(ops, "caller")])
+    assert not all(("ADDNORM", c, 0) in st[("GEMM", c + 3)][0] for c in range(9))
+    # done records: 9 for reuse (chunks 0..8), plus the last chunk on each stream (10, 11)
+    assert sum(o[0] == "RECORD_DONE" for o in full) == 11
 
 
 def test_plan_edge_cases():
