@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_o_proj.json"),
                     help="measured HBM bytes per projection launch (from the counter runs)")
+    ap.add_argument("--tune-sweep", action="store_true",
+                    help="run the token-threshold search on the K=H=8192 sweep and print it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -81,6 +83,32 @@ def cpu_baseline(d, seconds: float) -> dict:
                       f"full batch"}
 
 
+def tune_sweep(pr, torch, args) -> int:
+    """Token-threshold search over the long-prefill sweep (K = H = 8192): every chunk size is
+    checked against the conventional path, then timed; prints the table and the crossover."""
+    import synth
+    grid = list(synth.SWEEP_T)
+    mcs = [512, 1024, 2048]
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    t0 = time.perf_counter()
+    rep = pr.pr_tune([8192], [8192], pr.PR_NORM_STANDARD, grid, mcs, reps=max(args.steps // 5, 5))
+    rows = []
+    for i, T in enumerate(grid):
+        t = rep["timings"][0][i]
+        rows.append({"T": T, "conventional_ms": t[0] * 1e3,
+                     "best_fused_ms": t[1] * 1e3 if t[1] > 0 else None,
+                     "fused_ms": {str(m): (t[2 + j] * 1e3 if t[2 + j] > 0 else None)
+                                  for j, m in enumerate(mcs)}})
+    thr = rep["threshold_tokens"]
+    print(json.dumps({"tune_sweep": {"K": 8192, "H": 8192, "T_grid": grid, "microchunks": mcs,
+                                     "rows": rows, "n_checked": rep["n_checked"],
+                                     "n_rejected": rep["n_rejected"],
+                                     "threshold_tokens": None if thr == pr.INT32_MAX else thr,
+                                     "seconds": time.perf_counter() - t0}}), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -93,6 +121,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.tune_sweep:
+        return tune_sweep(pr, torch, args)
     wl = synth.WORKLOADS[args.workload]
     T, K, H = wl.T, wl.K, wl.H
     log(f"workload {wl.name}: T={T} K={K} H={H} chunk sizes {wl.microchunks}")

@@ -52,21 +52,24 @@ float bf16f(uint16_t b) {
   return f;
 }
 
-// Candidate check against the conventional result on sampled rows.  The two paths differ by the
-// bf16 rounding of y in the conventional one, so the residual may differ per element by half a
-// bf16 ulp of y (2^-8 |y|, with y = r_new - r_old) plus fp32 rounding.
+// Candidate check against the conventional result on sampled rows.  The two paths differ by
+// the bf16 rounding of y in the conventional one, and both outputs are rounded to bf16, so one
+// output element may differ by one bf16 ulp (2^-7 relative) on top of the 2e-2 absolute bound
+// (relative L2 <= 5e-3 as for the oracle comparison); the residual may differ per element by
+// half a bf16 ulp of y (2^-8 |y|, with y = r_new - r_old) plus fp32 rounding.
 bool candidate_ok(const std::vector<uint16_t>& out_f, const std::vector<uint16_t>& out_c,
                   const std::vector<float>& r_f, const std::vector<float>& r_c,
                   const std::vector<float>& r_old) {
-  double d2 = 0, n2 = 0, dmax = 0;
+  double d2 = 0, n2 = 0;
   for (size_t i = 0; i < out_f.size(); ++i) {
     const double a = bf16f(out_f[i]), b = bf16f(out_c[i]);
     if (!std::isfinite(a)) return false;
     d2 += (a - b) * (a - b);
     n2 += b * b;
-    dmax = std::max(dmax, std::fabs(a - b));
+    if (std::fabs(a - b) > 2e-2 + std::ldexp(std::max(std::fabs(a), std::fabs(b)), -7))
+      return false;
   }
-  if (dmax > 2e-2 || d2 > 25e-6 * std::max(n2, 1e-30)) return false;
+  if (d2 > 25e-6 * std::max(n2, 1e-30)) return false;
   for (size_t i = 0; i < r_f.size(); ++i) {
     if (!std::isfinite(r_f[i])) return false;
     const double y = std::fabs((double)r_f[i] - r_old[i]);

@@ -241,6 +241,14 @@ def test_auto_mode_overrides_and_tuning(monkeypatch):
     assert e.value.code == pr.PR_ERR_UNSUPPORTED
 
 
+def test_tuner_accepts_large_hidden_sizes():
+    """At H = 8192 two correct bf16 outputs differ by an ulp at |out| >= 4 (0.031 > 2e-2):
+    the candidate check must still accept the pipeline (every candidate checked, none
+    rejected)."""
+    rep = pr.pr_tune([1024], [8192], 0, [512, 1024], [256, 512], reps=2)
+    assert rep["n_rejected"] == 0 and rep["n_checked"] == 4, rep
+
+
 # -------------------------------------------------------------------- full-size workloads
 def _sample_rows(T, mc, n=48, seed=0):
     rng = np.random.default_rng(seed)
