@@ -65,12 +65,16 @@ __device__ __forceinline__ void barrier_no_fence() {
 // Operands
 //   A  = x [M][K] bf16, row stride K (the chunk's tokens).
 //   Bp = prepared weight, Bp[((k/8)*N + n)*8 + k%8] = W[n][k].
-// LDS stage layouts (bytes), chosen so that every fragment read is lane-linear (conflict-free)
-// and every direct global->LDS load writes 1 KiB contiguously:
-//   A stage: [BM/32 row blocks][4 k-groups][32 rows][16 B]
-//   B stage: [4 k-groups][BN columns][16 B]
-// A 32x32x16 MFMA takes, per lane l, A[row l%32][k 8*(l/32)..+8] and B[k 8*(l/32)..+8][col l%32]:
-// both are one 16-byte read at offset ((k-group)*32 + l%32)*16 within a 32-row/column block.
+// LDS stage layouts (bytes).  Every direct global->LDS load writes 1 KiB contiguously (lane
+// l at offset 16 l), so the global side chooses which 16 bytes land where:
+//   A stage: [BM rows][4 slots][16 B], row r's slot p holding k-group p ^ f(r) with
+//            f(r) = ((r >> 1) ^ (r >> 3)) & 3.  One load fills 16 rows (64 B of each row, a
+//            coalesced read); the swizzle spreads the 32 rows of a fragment read over all
+//            banks both for 8-lane (32-bank) and for 16-lane (64-bank) LDS passes.
+//   B stage: [4 k-groups][BN columns][16 B] (lane-linear on both sides: the prepared weight
+//            already has this layout).
+// A 32x32x16 MFMA takes, per lane l, A[row l%32][k 8*(l/32)..+8] and B[k 8*(l/32)..+8][col l%32],
+// one 16-byte read each.
 //
 // Pipeline: NB stage buffers in a ring, stages issued NB-1 ahead.  Each stage step runs the
 // MFMAs of its first k-substep while reading the second substep's fragments, waits for the
@@ -143,8 +147,8 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
   const int k_begin = z * k_split_len;
   const int nk = k_split_len / kBK;
 
-  // Load assignment: A load i of wave w fills LDS kilobyte q = w + NW*i of the stage, i.e. row
-  // block q/2 and k-groups 2(q%2), 2(q%2)+1 (lane l: row 32(q/2) + l%32, k-group 2(q%2) + l/32).
+  // Load assignment: A load i of wave w fills LDS kilobyte q = w + NW*i of the stage, rows
+  // 16q .. 16q+15 (lane l: tile row 16q + l/4, slot l%4, i.e. k-group (l%4) ^ f(row)).
   // B load i of wave w fills kilobyte q = w + NW*i: k-group q / CG, 64-column group q % CG.
   // Rows and columns past the matrix edge are clamped to the last valid one: their data only
   // feeds outputs that are never stored.  Offsets are 32-bit byte offsets (the launcher keeps
@@ -153,9 +157,11 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
 #pragma unroll
   for (int i = 0; i < A_LPW; ++i) {
     const int q = wave + NW * i;
-    int row = m0 + (q >> 1) * 32 + (lane & 31);
+    const int trow = q * 16 + (lane >> 2);
+    const int kg = (lane & 3) ^ (((trow >> 1) ^ (trow >> 3)) & 3);
+    int row = m0 + trow;
     row = row < M ? row : M - 1;
-    a_off[i] = (uint32_t)(row * K + (2 * (q & 1) + (lane >> 5)) * 8) * 2u;
+    a_off[i] = (uint32_t)(row * K + kg * 8) * 2u;
   }
   int b_col = n0 + (wave % CG) * 64 + lane;
   b_col = b_col < N ? b_col : N - 1;
@@ -184,11 +190,17 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // A fragment read: lane l reads tile row 32 rb + l%32, k-group 2s + l/32, i.e. slot
+  // (2s + l/32) ^ f(row); f(row) depends only on l%32 (32 rb is a multiple of 16).
+  const int a_r = lane & 31;
+  const int a_f = ((a_r >> 1) ^ (a_r >> 3)) & 3;
+  const int a_lane0 = a_r * 64 + (((lane >> 5)) ^ a_f) * 16;      // substep 0
+  const int a_lane1 = a_r * 64 + ((2 + (lane >> 5)) ^ a_f) * 16;  // substep 1
   auto load_frags = [&](const char* buf, int s, bf16x8_t* af, bf16x8_t* bfr) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int rb = wm * TM + i;
-      af[i] = *reinterpret_cast<const bf16x8_t*>(buf + (rb * 4 + 2 * s) * 512 + lane * 16);
+      af[i] = *reinterpret_cast<const bf16x8_t*>(buf + rb * 2048 + (s == 0 ? a_lane0 : a_lane1));
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
