@@ -78,7 +78,8 @@ static bool env_set(const char* name) {
   return v != nullptr && v[0] != '\0';
 }
 
-// Debug override of the projection tile: PR_FORCE_TILE="BMxBN" (an instantiated tile) and
+// Debug override of the projection tile: PR_FORCE_TILE="BMxBN" (an instantiated tile),
+// PR_FORCE_WAVES=4|8, PR_FORCE_STAGES=N (an instantiated ring depth of the tile) and
 // PR_FORCE_SPLIT=S (S must divide K/64).  Used by tests to reach every kernel variant.
 static int apply_forced_tile(int K, GemmCfg* g) {
   const char* t = std::getenv("PR_FORCE_TILE");
@@ -97,6 +98,13 @@ static int apply_forced_tile(int K, GemmCfg* g) {
     if (waves != 4 && waves != 8)
       return fail(PR_ERR_INVALID_ARG, "PR_FORCE_WAVES=%s must be 4 or 8", wv);
     g->waves = waves;
+  }
+  const char* st = std::getenv("PR_FORCE_STAGES");
+  if (st != nullptr && st[0] != '\0') {
+    const int stages = std::atoi(st);
+    if (stages < 2 || stages > 8)
+      return fail(PR_ERR_INVALID_ARG, "PR_FORCE_STAGES=%s must be in 2..8", st);
+    g->stages = stages;
   }
   const char* sp = std::getenv("PR_FORCE_SPLIT");
   if (sp != nullptr && sp[0] != '\0') {

@@ -19,6 +19,7 @@ struct GemmCfg {
   int bn = 256;   // tile columns (hidden)
   int split = 1;  // K partitions; partial sums land in separate fp32 planes
   int waves = 4;  // waves per workgroup: 4 (one per SIMD) or 8 (two per SIMD)
+  int stages = 0; // LDS ring depth; 0 = the deepest the tile fits in LDS
 };
 
 // Tile configurations the library instantiates (rows x columns per workgroup).

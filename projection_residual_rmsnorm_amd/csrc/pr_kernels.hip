@@ -80,9 +80,23 @@ __device__ __forceinline__ void barrier_no_fence() {
 // MFMAs of its first k-substep while reading the second substep's fragments, waits for the
 // next stage to land (own loads) and meets the other waves at one barrier, then runs the
 // second substep's MFMAs while reading the next stage's first fragments.  A buffer is refilled
-// one step after the barrier that follows its last read.  K per split is a multiple of
-// 32 * NB, so every loop trip runs all NB steps.
+// one step after the barrier that follows its last read.  The loop runs whole trips of NB
+// steps and then the remaining (K per split / 32) mod NB steps.
+//
+// Loads are latency-bound rather than bandwidth-bound: a stage is usable only once its
+// slowest load (an L2 miss) has landed, so the bytes a CU keeps in flight, (NB - 1) stages,
+// set its load rate.  NB is therefore as deep as the 160 KiB of LDS allows.
 // --------------------------------------------------------------------------------------------
+
+// One LDS object per ring buffer (instantiated only for the buffers a kernel uses): the
+// compiler tracks direct-to-LDS loads per object, so a fragment read from one buffer does not
+// wait for loads still landing in another.
+template <int I, int BYTES, int BM, int BN, int NB, int WM, int WN>
+__device__ __forceinline__ char* ring_buffer() {
+  __shared__ __attribute__((aligned(1024))) char buf[BYTES];
+  return buf;
+}
+
 template <int BM, int BN, int NB, int WM, int WN>
 __global__ void __launch_bounds__(WM* WN * 64, 1)
     gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp,
@@ -104,17 +118,22 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "load split");
   static_assert(NW % CG == 0, "B loads: waves must cover whole k-groups");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
-  static_assert(NB >= 2 && NB <= 4 && NB * (A_BYTES + B_BYTES) <= 160 * 1024, "LDS budget");
+  static_assert(NB >= 2 && NB <= 8 && NB * (A_BYTES + B_BYTES) <= 160 * 1024, "LDS budget");
   static_assert(LPW * (P - 1) < 64, "vmcnt range");
 
-  // One LDS object per ring buffer: the compiler tracks direct-to-LDS loads per object, so a
-  // fragment read from one buffer does not wait for loads still landing in another.
   constexpr int STAGE = A_BYTES + B_BYTES;
-  __shared__ __attribute__((aligned(1024))) char sb0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char sb1[STAGE];
-  __shared__ __attribute__((aligned(1024))) char sb2[NB > 2 ? STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char sb3[NB > 3 ? STAGE : 16];
-  auto smem = [&](int u) -> char* { return u == 0 ? sb0 : (u == 1 ? sb1 : (u == 2 ? sb2 : sb3)); };
+  char* const sb0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
+  char* const sb1 = ring_buffer<1, STAGE, BM, BN, NB, WM, WN>();
+  // u is a compile-time constant at every call (unrolled loops), so this folds to one object.
+  auto smem = [&](int u) -> char* {
+    if constexpr (NB > 2) if (u == 2) return ring_buffer<2, STAGE, BM, BN, NB, WM, WN>();
+    if constexpr (NB > 3) if (u == 3) return ring_buffer<3, STAGE, BM, BN, NB, WM, WN>();
+    if constexpr (NB > 4) if (u == 4) return ring_buffer<4, STAGE, BM, BN, NB, WM, WN>();
+    if constexpr (NB > 5) if (u == 5) return ring_buffer<5, STAGE, BM, BN, NB, WM, WN>();
+    if constexpr (NB > 6) if (u == 6) return ring_buffer<6, STAGE, BM, BN, NB, WM, WN>();
+    if constexpr (NB > 7) if (u == 7) return ring_buffer<7, STAGE, BM, BN, NB, WM, WN>();
+    return u == 0 ? sb0 : sb1;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -230,7 +249,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
 
   // Prologue: stages 0 .. P-1 in flight, wait for stage 0, read its first fragments.
 #pragma unroll
-  for (int p = 0; p < P; ++p) issue_stage(p, smem(p));
+  for (int p = 0; p < P; ++p) issue_stage(min(p, nk - 1), smem(p));
   __builtin_amdgcn_s_waitcnt(PR_VMCNT(LPW * (P - 1)));
   barrier_no_fence();
   load_frags(smem(0), 0, fa0, fb0);
@@ -254,11 +273,17 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  for (int kt = 0; kt < nk; kt += NB) {
+  int kt = 0;
+  for (; kt + NB <= nk; kt += NB) {
 #pragma unroll
     for (int u = 0; u < NB; ++u)
       step(kt + u, smem(u), smem((u + 1) % NB), smem((u + P) % NB));
   }
+  // Remaining steps: the ring position continues at buffer 0 (kt is a multiple of NB).
+  const int rem = nk - kt;
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u)
+    if (u < rem) step(kt + u, smem(u), smem((u + 1) % NB), smem((u + P) % NB));
 
   // Epilogue.  32x32 fp32 accumulator layout: lane l, element e holds
   // row 8*(e/4) + 4*(l/32) + e%4, column l%32.  Each wave passes its tile through its own LDS
@@ -561,13 +586,21 @@ int launch_gemm_t(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out,
 
 template <int BM, int BN, int WM, int WN>
 int launch_gemm_nb(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
-                   int K, int split, long long plane_stride, hipStream_t s, hipEvent_t done,
-                   hipEvent_t t0, hipEvent_t t1) {
-  // Ring depth: 4 stage buffers when K per split is a multiple of 4 stages, else 2 (K per split
-  // is always a multiple of 64, i.e. of 2 stages).
-  if ((K / split) % (4 * kBK) == 0)
+                   int K, int split, int stages, long long plane_stride, hipStream_t s,
+                   hipEvent_t done, hipEvent_t t0, hipEvent_t t1) {
+  // Ring depth: the deepest that fits in LDS by default (stages = 0); tests and tuning may ask
+  // for 4 or for another instantiated depth.
+  constexpr int STAGE = (BM + BN) * kBK * 2;
+  constexpr int DEEP = (160 * 1024) / STAGE > 8 ? 8 : (160 * 1024) / STAGE;
+  constexpr int MID = (DEEP + 4) / 2;
+  if (stages == 0 || stages == DEEP)
+    return launch_gemm_t<BM, BN, DEEP, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s, done, t0, t1);
+  if (stages == 4)
     return launch_gemm_t<BM, BN, 4, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s, done, t0, t1);
-  return launch_gemm_t<BM, BN, 2, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s, done, t0, t1);
+  if (stages == MID)
+    return launch_gemm_t<BM, BN, MID, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s, done, t0, t1);
+  return fail(PR_ERR_INVALID_ARG, "projection tile %dx%d has no %d-stage variant (4, %d, %d)", BM,
+              BN, stages, MID, DEEP);
 }
 
 template <int NV, int WPR>
@@ -607,14 +640,14 @@ int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool eight = cfg.waves == 8;
   if (cfg.bm == 256 && cfg.bn == 256)
-    return eight ? launch_gemm_nb<256, 256, 2, 4>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1)
-                 : launch_gemm_nb<256, 256, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1);
+    return eight ? launch_gemm_nb<256, 256, 2, 4>(x, Wp, C, bf16_out, M, N, K, cfg.split, cfg.stages, plane_stride, s, done, t0, t1)
+                 : launch_gemm_nb<256, 256, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, cfg.stages, plane_stride, s, done, t0, t1);
   if (cfg.bm == 256 && cfg.bn == 128)
-    return eight ? launch_gemm_nb<256, 128, 4, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1)
-                 : launch_gemm_nb<256, 128, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1);
+    return eight ? launch_gemm_nb<256, 128, 4, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, cfg.stages, plane_stride, s, done, t0, t1)
+                 : launch_gemm_nb<256, 128, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, cfg.stages, plane_stride, s, done, t0, t1);
   if (cfg.bm == 128 && cfg.bn == 128)
-    return eight ? launch_gemm_nb<128, 128, 2, 4>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1)
-                 : launch_gemm_nb<128, 128, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, plane_stride, s, done, t0, t1);
+    return eight ? launch_gemm_nb<128, 128, 2, 4>(x, Wp, C, bf16_out, M, N, K, cfg.split, cfg.stages, plane_stride, s, done, t0, t1)
+                 : launch_gemm_nb<128, 128, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, cfg.stages, plane_stride, s, done, t0, t1);
   return fail(PR_ERR_INVALID_ARG, "no projection tile %dx%d", cfg.bm, cfg.bn);
 }
 

@@ -26,7 +26,8 @@ if torch.cuda.is_available():
 @pytest.fixture(autouse=True)
 def _env(monkeypatch):
     for k in ("PR_MICROCHUNK_TOKENS", "PR_THRESHOLD_TOKENS", "PR_FORCE_TILE", "PR_FORCE_SPLIT",
-              "PR_DEBUG_POISON", "PR_DEBUG_DELAY", "PR_FAULT_INJECT"):
+              "PR_FORCE_WAVES", "PR_FORCE_STAGES", "PR_DEBUG_POISON", "PR_DEBUG_DELAY",
+              "PR_FAULT_INJECT"):
         monkeypatch.delenv(k, raising=False)
     pr.pr_clear_tuning()
     yield
@@ -45,18 +46,28 @@ def _check(d, r_dev, out_bits, mode, rows=None):
     return err
 
 
-TILES = [("256x256", 1), ("256x128", 1), ("128x128", 1), ("256x256", 2), ("128x128", 4),
-         ("256x128", 8)]
+# (tile, K split, waves per workgroup, LDS ring depth; 0 = the tile's deepest).  Together these
+# reach every instantiated kernel: 256x256 at depths 5 and 4, 256x128 at 6, 5, 4 and 128x128 at
+# 8, 6, 4, each with 4 and 8 waves.  K = 1024 gives 32 k-steps per split of 1, so most depths
+# end in a partial ring trip; split 8 leaves fewer k-steps than stages.
+TILES = [("256x256", 1, 8, 0), ("256x256", 1, 4, 0), ("256x256", 2, 8, 4), ("256x256", 1, 4, 4),
+         ("256x128", 1, 8, 0), ("256x128", 8, 4, 0), ("256x128", 1, 8, 5), ("256x128", 2, 4, 5),
+         ("256x128", 1, 8, 4), ("256x128", 1, 4, 4),
+         ("128x128", 1, 8, 0), ("128x128", 4, 4, 0), ("128x128", 2, 8, 0), ("128x128", 1, 8, 6),
+         ("128x128", 1, 4, 6), ("128x128", 1, 4, 4), ("128x128", 2, 8, 4)]
 
 
 # ------------------------------------------------------------------------ bitwise projection
-@pytest.mark.parametrize("tile,split", TILES)
-def test_integer_projection_is_exact(monkeypatch, tile, split):
+@pytest.mark.parametrize("tile,split,waves,stages", TILES)
+def test_integer_projection_is_exact(monkeypatch, tile, split, waves, stages):
     """Small integers: every partial sum is exact in fp32, so the residual must match bitwise.
 
     T=300 spans two 256-row tiles with a ragged tail; H=768 spans 3-6 column tiles."""
     monkeypatch.setenv("PR_FORCE_TILE", tile)
     monkeypatch.setenv("PR_FORCE_SPLIT", str(split))
+    monkeypatch.setenv("PR_FORCE_WAVES", str(waves))
+    if stages:
+        monkeypatch.setenv("PR_FORCE_STAGES", str(stages))
     d = synth.integer_inputs(300, 1024, 768, seed=3)
     dev = Device(d)
     for mc, mode in ((None, "conventional"), (128, "fused"), (300, "fused"), (77, "fused")):
