@@ -166,8 +166,10 @@ int pr_select(int T, int K, int H, int microchunk, pr_decision* d);
  * enqueues for T tokens and chunk size mc (host order).  Chunks alternate between the caller's
  * stream (even chunks) and a library stream (odd chunks); a chunk's projection and its add/norm
  * are consecutive on one stream, so chunk c+1's projection on the other stream overlaps chunk
- * c's add/norm.  Slot c % 3 is reused by chunk c+3, which runs on the other stream and waits
- * for done[slot]; done[slot] is recorded only where something waits for it, and a record that
+ * c's add/norm.  On the host, chunk c+1's projection is enqueued before chunk c's add/norm so
+ * that it reaches its stream while chunk c's projection still runs.  Slot c % 3 is reused by
+ * chunk c+3, which runs on the other stream and waits for done[slot]; done[slot] is recorded
+ * only where something waits for it, and a record that
  * follows the launch it marks is signalled by that launch.  The library stream starts after
  * the caller's prior work (entry event) and the caller's stream waits for the library stream's
  * last chunk (join).  Returns the number of operations (written up to max_ops), or a negative

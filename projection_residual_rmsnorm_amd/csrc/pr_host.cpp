@@ -343,18 +343,26 @@ int pr_plan(int T, int microchunk, pr_plan_op* ops, int max_ops) {
     emit(PR_OP_RECORD_ENTRY, 0, -1, -1, 0);
     emit(PR_OP_WAIT_ENTRY, 1, -1, -1, 0);
   }
-  for (int c = 0; c < nc; ++c) {
-    const int st = stream_of(c);
-    const int s = c % PR_NUM_SLOTS;
-    const int rows = std::min(microchunk, T - c * microchunk);
-    if (c >= PR_NUM_SLOTS) emit(PR_OP_WAIT_DONE, st, c, s, 0);
-    emit(PR_OP_GEMM, st, c, s, rows);
-    emit(PR_OP_ADDNORM, st, c, s, rows);
+  auto rows_of = [&](int c) { return std::min(microchunk, T - c * microchunk); };
+  auto addnorm = [&](int c) {
+    emit(PR_OP_ADDNORM, stream_of(c), c, c % PR_NUM_SLOTS, rows_of(c));
     // done[slot]: waited for by chunk c + 3, by the join (the library stream's last chunk) and
     // by a next call made from another stream (the last chunk on each stream).
     if (c + PR_NUM_SLOTS < nc || c == last_even || c == last_odd)
-      emit(PR_OP_RECORD_DONE, st, c, s, 0);
+      emit(PR_OP_RECORD_DONE, stream_of(c), c, c % PR_NUM_SLOTS, 0);
+  };
+  // Host order: chunk c's projection is enqueued before chunk c-1's add/norm, so that it
+  // reaches the other stream while chunk c-1's projection still runs.  Each stream's own
+  // order (projection, add/norm, projection, ...) is unchanged, and done[slot] of chunk c-3
+  // is recorded (with that chunk's add/norm, two iterations earlier) before chunk c waits
+  // for it.
+  for (int c = 0; c < nc; ++c) {
+    const int s = c % PR_NUM_SLOTS;
+    if (c >= PR_NUM_SLOTS) emit(PR_OP_WAIT_DONE, stream_of(c), c, s, 0);
+    emit(PR_OP_GEMM, stream_of(c), c, s, rows_of(c));
+    if (c >= 1) addnorm(c - 1);
   }
+  addnorm(nc - 1);
   if (last_odd >= 0) emit(PR_OP_JOIN, 0, last_odd, last_odd % PR_NUM_SLOTS, 0);
   return n;
 }

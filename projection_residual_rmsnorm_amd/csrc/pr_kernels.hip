@@ -588,12 +588,16 @@ template <int BM, int BN, int WM, int WN>
 int launch_gemm_nb(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, int M, int N,
                    int K, int split, int stages, long long plane_stride, hipStream_t s,
                    hipEvent_t done, hipEvent_t t0, hipEvent_t t1) {
-  // Ring depth: the deepest that fits in LDS by default (stages = 0); tests and tuning may ask
-  // for 4 or for another instantiated depth.
+  // Ring depth.  The 256x256 tile's loads stall on latency with 4 stages, so it takes the
+  // deepest ring that fits (5 x 32 KiB).  The smaller tiles run as fast with 4 stages as with
+  // deeper rings, and at 4 stages (64 KiB) two 128x128 workgroups fit on one CU, which lets
+  // the projections of consecutive chunks share the CUs.  Tests and tuning may ask for
+  // another instantiated depth.
   constexpr int STAGE = (BM + BN) * kBK * 2;
   constexpr int DEEP = (160 * 1024) / STAGE > 8 ? 8 : (160 * 1024) / STAGE;
   constexpr int MID = (DEEP + 4) / 2;
-  if (stages == 0 || stages == DEEP)
+  if (stages == 0) stages = (BM == 256 && BN == 256) ? DEEP : 4;
+  if (stages == DEEP)
     return launch_gemm_t<BM, BN, DEEP, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s, done, t0, t1);
   if (stages == 4)
     return launch_gemm_t<BM, BN, 4, WM, WN>(x, Wp, C, bf16_out, M, N, K, split, plane_stride, s, done, t0, t1);
