@@ -16,7 +16,8 @@ A = 1 << 20  # a fake, 16-byte aligned address for pointer arguments
 
 @pytest.fixture(autouse=True)
 def _clean_env(monkeypatch):
-    for k in ("PR_MICROCHUNK_TOKENS", "PR_THRESHOLD_TOKENS", "PR_LOG"):
+    for k in ("PR_MICROCHUNK_TOKENS", "PR_THRESHOLD_TOKENS", "PR_LOG", "PR_FORCE_TILE",
+              "PR_FORCE_SPLIT", "PR_FORCE_WAVES", "PR_FORCE_STAGES"):
         monkeypatch.delenv(k, raising=False)
     pr.pr_clear_tuning()
     yield
@@ -84,6 +85,27 @@ def test_tile_choice_is_valid(M, N, K):
         d = pr.pr_select(M, K, N, mc if mc > 0 else -1)
         assert (d["gemm_bm"], d["gemm_bn"]) in ((256, 256), (256, 128), (128, 128))
         assert K % (64 * d["split_k"]) == 0 and d["split_k"] >= 1
+
+
+def test_forced_projection_config(monkeypatch):
+    """Debug overrides of the projection configuration are validated on the host."""
+    monkeypatch.setenv("PR_FORCE_TILE", "128x128")
+    monkeypatch.setenv("PR_FORCE_SPLIT", "2")
+    monkeypatch.setenv("PR_FORCE_WAVES", "4")
+    d = pr.pr_select(512, 4096, 4096, 512)
+    assert (d["gemm_bm"], d["gemm_bn"], d["split_k"], d["gemm_waves"]) == (128, 128, 2, 4)
+    for name, bad in (("PR_FORCE_TILE", "64x64"), ("PR_FORCE_SPLIT", "3"),
+                      ("PR_FORCE_WAVES", "6"), ("PR_FORCE_STAGES", "1"),
+                      ("PR_FORCE_STAGES", "9")):
+        monkeypatch.setenv(name, bad)
+        with pytest.raises(pr.PRError):
+            pr.pr_select(512, 4096, 4096, 512)
+        monkeypatch.delenv(name)
+        if name != "PR_FORCE_STAGES":
+            monkeypatch.setenv(name, {"PR_FORCE_TILE": "128x128", "PR_FORCE_SPLIT": "2",
+                                      "PR_FORCE_WAVES": "4"}[name])
+    monkeypatch.setenv("PR_FORCE_STAGES", "6")  # an instantiated depth of the 128x128 tile
+    assert pr.pr_select(512, 4096, 4096, 512)["gemm_bm"] == 128
 
 
 def test_auto_untuned_and_overrides(monkeypatch):
