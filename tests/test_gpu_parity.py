@@ -119,6 +119,28 @@ def test_padded_rows_untouched(T, mc):
         assert np.all(out_all[T:] == 0x7BAD)
 
 
+# --------------------------------------------------------------- zero-padded K is inert
+@pytest.mark.parametrize("tile", ["256x256", "128x128"])
+def test_zero_padded_k_is_bitwise_inert(monkeypatch, tile):
+    """K = 448 real columns zero-padded to 512: with the K split pinned to 1, the padded run
+    adds two k-stages of exact zeros to the same accumulation, so residual and output match
+    the unpadded run bitwise (fused and conventional), and both match the oracle."""
+    monkeypatch.setenv("PR_FORCE_TILE", tile)
+    monkeypatch.setenv("PR_FORCE_SPLIT", "1")
+    d = synth.make_custom(300, 512, 384, seed=12, norm_kind=1, eps=1e-6, K_real=448)
+    cut = dict(d, x=np.ascontiguousarray(d["x"][:, :448]),
+               W=np.ascontiguousarray(d["W"][:, :448]), K=448)
+    pad_dev, cut_dev = Device(d), Device(cut)
+    for mc in (None, 128):
+        pad_dev.reset()
+        cut_dev.reset()
+        r1, o1 = pad_dev.run(mc)
+        r2, o2 = cut_dev.run(mc)
+        np.testing.assert_array_equal(r1, r2)
+        np.testing.assert_array_equal(o1, o2)
+        _check(cut, r2, o2, "conventional" if mc is None else "fused")
+
+
 # ---------------------------------------------------------------- chunked == unchunked
 @pytest.mark.parametrize("tile,split", [("256x256", 1), ("128x128", 2)])
 def test_microchunked_equals_unchunked_bitwise(monkeypatch, tile, split):

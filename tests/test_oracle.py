@@ -289,3 +289,4 @@ def test_workload_inputs_statistics():
     dp = synth.make_inputs(synth.WORKLOADS["down_proj"], seed=0, T=64)
     x = oracle.widen_bf16(dp["x"])
     assert 0.3 < float(np.mean(x * x)) < 0.42          # E[(silu(a) b)^2] ~ 0.356
+
