@@ -108,7 +108,9 @@ int pr_prepare_weight(const uint16_t* W_src, int src_layout, uint16_t* W_prep, i
  * out            [T][H] bf16, caller-owned, written.  NULL: the result goes to a library
  *                workspace returned by pr_workspace_output(), borrowed until the next call on
  *                this device ("TPSP Design" section 3: the output borrows a shared workspace
- *                and must be consumed before the next call).  Must not alias x, W or residual.
+ *                and must be consumed before the next call).  Must not overlap x, W, the
+ *                residual or norm_w; the residual must not overlap x, W or norm_w (byte ranges
+ *                of the dense extents above; PR_ERR_INVALID_ARG otherwise).
  * stream         ordering stream (see conventions).
  */
 int proj_add_rmsnorm(const uint16_t* x, const uint16_t* W, float* residual_inout,
@@ -134,7 +136,8 @@ const uint16_t* pr_workspace_output(void);
  * Host-only helpers (no device work; usable without a GPU)
  * ---------------------------------------------------------------------------------------- */
 
-/* Argument checks of proj_add_rmsnorm (pointers are checked for NULL and aliasing only). */
+/* Argument checks of proj_add_rmsnorm (pointers are checked for NULL, alignment and overlap of
+ * the written buffers with the others; nothing is dereferenced). */
 int pr_validate(const void* x, const void* W, const void* residual_inout, const void* norm_w,
                 float eps, int T, int K, int H, int microchunk, int norm_kind, const void* out);
 

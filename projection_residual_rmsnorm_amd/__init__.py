@@ -121,11 +121,20 @@ def library():
     return _lib()
 
 
-def _ptr(t) -> Optional[int]:
+def _ptr(t, nbytes: int = 0, name: str = "buffer") -> Optional[int]:
+    """Device address of a tensor (or a raw integer address, passed through unchecked).
+
+    A tensor must be contiguous and hold at least `nbytes` bytes: the library reads and writes
+    the dense row-major extent the shape arguments describe."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes; the call needs "
+                         f"{nbytes}")
     return t.data_ptr()
 
 
@@ -146,22 +155,30 @@ def _check(rc: int) -> int:
 
 
 def pr_prepare_weight(W_src, src_layout: int, W_prep, K: int, H: int, stream=None) -> None:
-    _check(_lib().pr_prepare_weight(_ptr(W_src), src_layout, _ptr(W_prep), K, H,
-                                    _stream(stream, W_src)))
+    n = 2 * max(K, 0) * max(H, 0)
+    _check(_lib().pr_prepare_weight(_ptr(W_src, n, "W_src"), src_layout,
+                                    _ptr(W_prep, n, "W_prep"), K, H, _stream(stream, W_src)))
+
+
+def _call_ptrs(x, W, residual_inout, norm_w, out, T: int, K: int, H: int):
+    T, K, H = max(T, 0), max(K, 0), max(H, 0)
+    return (_ptr(x, 2 * T * K, "x"), _ptr(W, 2 * K * H, "W"),
+            _ptr(residual_inout, 4 * T * H, "residual_inout"), _ptr(norm_w, 4 * H, "norm_w"),
+            _ptr(out, 2 * T * H, "out"))
 
 
 def proj_add_rmsnorm(x, W, residual_inout, norm_w, eps: float, T: int, K: int, H: int,
                      microchunk: int, norm_kind: int = PR_NORM_STANDARD, out=None,
                      stream=None) -> None:
-    _check(_lib().proj_add_rmsnorm(_ptr(x), _ptr(W), _ptr(residual_inout), _ptr(norm_w), eps, T,
-                                   K, H, microchunk, norm_kind, _ptr(out),
+    px, pw, pr_, pn, po = _call_ptrs(x, W, residual_inout, norm_w, out, T, K, H)
+    _check(_lib().proj_add_rmsnorm(px, pw, pr_, pn, eps, T, K, H, microchunk, norm_kind, po,
                                    _stream(stream, x, residual_inout)))
 
 
 def proj_add_rmsnorm_unfused(x, W, residual_inout, norm_w, eps: float, T: int, K: int, H: int,
                              norm_kind: int = PR_NORM_STANDARD, out=None, stream=None) -> None:
-    _check(_lib().proj_add_rmsnorm_unfused(_ptr(x), _ptr(W), _ptr(residual_inout), _ptr(norm_w),
-                                           eps, T, K, H, norm_kind, _ptr(out),
+    px, pw, pr_, pn, po = _call_ptrs(x, W, residual_inout, norm_w, out, T, K, H)
+    _check(_lib().proj_add_rmsnorm_unfused(px, pw, pr_, pn, eps, T, K, H, norm_kind, po,
                                            _stream(stream, x, residual_inout)))
 
 

@@ -301,8 +301,27 @@ int pr_validate(const void* x, const void* W, const void* residual_inout, const 
   if (T == 0) return PR_OK;
   if (x == nullptr || W == nullptr || residual_inout == nullptr || norm_w == nullptr)
     return fail(PR_ERR_INVALID_ARG, "null tensor pointer");
-  if (out != nullptr && (out == x || out == W || out == residual_inout))
-    return fail(PR_ERR_INVALID_ARG, "out must not alias x, W or residual");
+  // Written buffers must not overlap anything else the call touches: the residual is updated
+  // in place while later chunks still read x, and out is written while x, W, the residual and
+  // the norm weight are read.  Extents are the dense row-major sizes the shape arguments give.
+  struct Range {
+    uintptr_t lo, hi;
+    const char* name;
+  };
+  auto range = [](const void* p, unsigned long long bytes, const char* name) {
+    return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes, name};
+  };
+  const Range rx = range(x, 2ULL * T * K, "x"), rw = range(W, 2ULL * K * H, "W"),
+              rr = range(residual_inout, 4ULL * T * H, "residual"),
+              rn = range(norm_w, 4ULL * H, "norm_w");
+  auto overlap = [](const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; };
+  for (const Range& o : {rx, rw, rn})
+    if (overlap(rr, o)) return fail(PR_ERR_INVALID_ARG, "residual overlaps %s", o.name);
+  if (out != nullptr) {
+    const Range ro = range(out, 2ULL * T * H, "out");
+    for (const Range& o : {rx, rw, rr, rn})
+      if (overlap(ro, o)) return fail(PR_ERR_INVALID_ARG, "out overlaps %s", o.name);
+  }
   const uintptr_t a[5] = {(uintptr_t)x, (uintptr_t)W, (uintptr_t)residual_inout,
                           (uintptr_t)norm_w, (uintptr_t)out};
   for (uintptr_t p : a)

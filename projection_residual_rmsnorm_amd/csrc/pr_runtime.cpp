@@ -1,5 +1,6 @@
-// Runtime of the library: per-device resources (two streams, six slot events, the three-slot
-// workspace), the microchunk pipeline executor, the conventional path and the autotuner.
+// Runtime of the library: per-device resources (one library stream, an entry event, three slot
+// done events, the three-slot workspace), the microchunk pipeline executor and the
+// conventional path.
 //
 // Pipeline ("TPSP Design" page, section 3, Microchunk pipeline): chunks alternate between the
 // caller's stream and one library stream.  On its stream, chunk c's projection writes slot
@@ -16,6 +17,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
+#include <memory>
 #include <mutex>
 #include <vector>
 
@@ -53,7 +56,7 @@ struct DevCtx {
   int launches[2] = {0, 0};
 };
 
-bool g_profile = false;
+std::atomic<bool> g_profile{false};
 
 std::mutex g_ctx_mu;
 DevCtx* g_ctx[kMaxDevices] = {};
@@ -84,13 +87,21 @@ int take_event(DevCtx* c, hipEvent_t* e) {
 // into two timing events (extended launch), else both are NULL.
 template <typename F>
 int timed(DevCtx* c, int kind, F&& launch) {
-  if (!g_profile) return launch(nullptr, nullptr);
+  if (!g_profile.load(std::memory_order_relaxed)) return launch(nullptr, nullptr);
   DevCtx::Timed t{nullptr, nullptr, kind};
   PR_TRY(take_event(c, &t.start));
-  PR_TRY(take_event(c, &t.stop));
+  if (const int rc = take_event(c, &t.stop); rc != PR_OK) {
+    c->ev_pool.push_back(t.start);
+    return rc;
+  }
   const int rc = launch(t.start, t.stop);
+  if (rc != PR_OK) {  // nothing was recorded into the pair
+    c->ev_pool.push_back(t.start);
+    c->ev_pool.push_back(t.stop);
+    return rc;
+  }
   c->pending.push_back(t);
-  return rc;
+  return PR_OK;
 }
 
 int env_int(const char* name) {
@@ -117,17 +128,25 @@ int get_ctx(DevCtx** out) {
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(PR_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev,
                 prop.gcnArchName);
-  DevCtx* c = new DevCtx();
+  std::unique_ptr<DevCtx> c(new DevCtx());
   c->device = dev;
-  // Default-priority, non-blocking streams.
-  PR_HIP(hipStreamCreateWithFlags(&c->sL, hipStreamNonBlocking));
-  // Default-flag events throughout: the dispatches signal done themselves (extended launch),
-  // and a stream wait on such an event is much cheaper on the host than on an event created
-  // with hipEventDisableTiming.
-  PR_HIP(hipEventCreate(&c->entry));
-  for (int s = 0; s < PR_NUM_SLOTS; ++s) PR_HIP(hipEventCreate(&c->done[s]));
-  g_ctx[dev] = c;
-  *out = c;
+  // A default-priority, non-blocking stream.  Default-flag events throughout: the dispatches
+  // signal done themselves (extended launch), and a stream wait on such an event is much
+  // cheaper on the host than on an event created with hipEventDisableTiming.
+  hipError_t e = hipStreamCreateWithFlags(&c->sL, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreate(&c->entry);
+  for (int s = 0; s < PR_NUM_SLOTS && e == hipSuccess; ++s) e = hipEventCreate(&c->done[s]);
+  if (e != hipSuccess) {
+    // release what was created; the context is not kept
+    for (int s = 0; s < PR_NUM_SLOTS; ++s)
+      if (c->done[s] != nullptr) (void)hipEventDestroy(c->done[s]);
+    if (c->entry != nullptr) (void)hipEventDestroy(c->entry);
+    if (c->sL != nullptr) (void)hipStreamDestroy(c->sL);
+    return fail(PR_ERR_HIP, "creating the library stream and events on device %d: %s", dev,
+                hipGetErrorString(e));
+  }
+  g_ctx[dev] = c.release();
+  *out = g_ctx[dev];
   return PR_OK;
 }
 
@@ -382,23 +401,33 @@ int pr_profile_enable(int on) {
   PR_TRY(pr_profile_read(nullptr));  // drain what is pending
   c->ms[0] = c->ms[1] = 0;
   c->launches[0] = c->launches[1] = 0;
-  g_profile = on != 0;
+  g_profile.store(on != 0);
   return PR_OK;
 }
 
 int pr_profile_read(pr_profile* p) {
+  clear_error();
   DevCtx* c = nullptr;
   PR_TRY(get_ctx(&c));
+  // Every pending pair is consumed (and its events returned to the pool) even if one fails,
+  // so that one bad read does not leave the queue in a state every later read fails on.
+  hipError_t first_err = hipSuccess;
   for (const DevCtx::Timed& t : c->pending) {
-    PR_HIP(hipEventSynchronize(t.stop));
     float ms = 0;
-    PR_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
-    c->ms[t.kind] += ms;
-    c->launches[t.kind] += 1;
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e == hipSuccess) {
+      c->ms[t.kind] += ms;
+      c->launches[t.kind] += 1;
+    } else if (first_err == hipSuccess) {
+      first_err = e;
+    }
     c->ev_pool.push_back(t.start);
     c->ev_pool.push_back(t.stop);
   }
   c->pending.clear();
+  if (first_err != hipSuccess)
+    return fail(PR_ERR_HIP, "reading kernel timing events: %s", hipGetErrorString(first_err));
   if (p != nullptr) {
     p->gemm_ms = c->ms[0];
     p->gemm_launches = c->launches[0];

@@ -87,7 +87,10 @@ template <typename F>
 int time_calls(F&& call, int reps, hipStream_t s, Stats* st) {
   hipEvent_t e0, e1;
   PR_HIP(hipEventCreate(&e0));
-  PR_HIP(hipEventCreate(&e1));
+  if (const hipError_t e = hipEventCreate(&e1); e != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return fail(PR_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+  }
   std::vector<double> t;
   int rc = PR_OK;
   for (int i = 0; i < 2 && rc == PR_OK; ++i) rc = call();  // warm-up

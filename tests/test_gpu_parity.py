@@ -268,9 +268,11 @@ def test_auto_mode_overrides_and_tuning(monkeypatch):
     sel = pr.pr_select(512, 512, 512, 0)
     thr = rep["threshold_tokens"]
     assert sel["path"] == (pr.PR_PATH_FUSED if 512 >= thr else pr.PR_PATH_CONVENTIONAL)
+    # T above the largest tuned token count is refused before anything runs
+    x600 = torch.zeros((600, 512), dtype=torch.int16, device=DEV)
+    r600 = torch.zeros((600, 512), dtype=torch.float32, device=DEV)
     with pytest.raises(pr.PRError) as e:
-        dev.run(0) if False else pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 600,
-                                                     512, 512, 0)
+        pr.proj_add_rmsnorm(x600, dev.Wp, r600, dev.w, 1e-5, 600, 512, 512, 0)
     assert e.value.code == pr.PR_ERR_UNSUPPORTED
 
 

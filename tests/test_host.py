@@ -53,6 +53,12 @@ def test_validate():
         (dict(eps=float("nan")), pr.PR_ERR_INVALID_ARG), (dict(x=None), pr.PR_ERR_INVALID_ARG),
         (dict(out=A), pr.PR_ERR_INVALID_ARG), (dict(out=A * 3), pr.PR_ERR_INVALID_ARG),
         (dict(x=A + 2), pr.PR_ERR_INVALID_ARG), (dict(K=1 << 16, H=1 << 16), pr.PR_ERR_SHAPE),
+        # partial overlaps (16-byte aligned): out inside the residual, residual inside x,
+        # residual reaching into the weight, out covering the norm weight
+        (dict(out=A * 3 + 64), pr.PR_ERR_INVALID_ARG),
+        (dict(residual_inout=A + 1024), pr.PR_ERR_INVALID_ARG),
+        (dict(residual_inout=A * 2 - 1024), pr.PR_ERR_INVALID_ARG),
+        (dict(out=A * 4 - 1024), pr.PR_ERR_INVALID_ARG),
     ]
     for change, code in bad:
         args = dict(ok, **change)
@@ -305,3 +311,22 @@ def test_calls_without_gpu_fail_cleanly():
     rc = pr.library().proj_add_rmsnorm(None, None, None, None, 1e-5, 0, 512, 512, 16, 0, None,
                                        None)
     assert rc in (0, pr.PR_ERR_HIP, pr.PR_ERR_UNSUPPORTED)
+
+
+def test_binding_rejects_strided_or_short_tensors():
+    """The binding hands the library raw addresses: tensors must be contiguous and hold the
+    extent the shape arguments describe (checked before the library is reached)."""
+    import torch
+    T, K, H = 8, 64, 64
+    x = torch.zeros((T, K), dtype=torch.int16)
+    W = torch.zeros(K * H, dtype=torch.int16)
+    r = torch.zeros((T, H), dtype=torch.float32)
+    w = torch.zeros(H, dtype=torch.float32)
+    with pytest.raises(ValueError, match="contiguous"):
+        pr.proj_add_rmsnorm(x.t(), W, r, w, 1e-5, T, K, H, 4)
+    with pytest.raises(ValueError, match="residual_inout"):
+        pr.proj_add_rmsnorm(x, W, r[: T - 1], w, 1e-5, T, K, H, 4)
+    with pytest.raises(ValueError, match="W"):
+        pr.proj_add_rmsnorm_unfused(x, W[:-1], r, w, 1e-5, T, K, H)
+    with pytest.raises(ValueError, match="W_prep"):
+        pr.pr_prepare_weight(W, pr.PR_WEIGHT_OUT_IN, W[: K * H // 2], K, H)
