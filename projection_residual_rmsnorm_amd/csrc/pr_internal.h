@@ -61,10 +61,12 @@ int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, i
 // r <- r + y; out = RMSNorm(r) for `rows` rows of width H.
 // y: fp32 planes [nplanes][rows][H] (summed in plane order) or bf16 [rows][H] (y_bf16 != 0).
 // round_y: round the summed fp32 y to bf16 before the add (conventional semantics).
+// max_wgs > 0 caps the workgroups (CUs) the launch occupies; the result does not depend on it.
 int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_stride,
                        int round_y, float* r, const float* w, uint16_t* out, int rows, int H,
-                       float eps, int gemma, void* stream, void* done_event = nullptr,
-                       void* start_timing = nullptr, void* stop_timing = nullptr);
+                       float eps, int gemma, int max_wgs, void* stream,
+                       void* done_event = nullptr, void* start_timing = nullptr,
+                       void* stop_timing = nullptr);
 
 int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,
                           void* stream);

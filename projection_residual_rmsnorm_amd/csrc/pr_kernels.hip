@@ -349,115 +349,175 @@ __device__ __forceinline__ float4 round_bf16_4(float4 v) {
 }
 
 // Rows are split over WPR waves (WPR = 1, 2, 4, 8): wave w of a row holds the columns
-// [w*H/WPR, (w+1)*H/WPR) as NV float4 per lane (H = 256 * NV * WPR).  The wave partial sums of
-// squares meet in LDS and are added in wave order, so the result does not depend on timing.
-template <int NV, int WPR>
+// [w*H/WPR, (w+1)*H/WPR) as NV float4 per lane (H = 256 * NV * WPR).  The sum of squares is
+// taken over S fixed segments of the row (S = 8, 4, 2 or 1, set by H alone): each segment's
+// partial is accumulated per lane in column order and reduced across the wave, and the S
+// partials are added in segment order.  That order does not depend on WPR, on how many rows
+// the launch has or on timing, so a row's result is the same in a microchunk and in the whole
+// batch.  A workgroup handles RPB rows at a time and strides over row groups by the grid size,
+// so the launch may use fewer workgroups (CUs) than there are row groups.
+template <int NV, int WPR, bool YB>
 __global__ void __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR)
     add_rmsnorm_kernel(const float* __restrict__ yf, const uint16_t* __restrict__ yb,
                        int nplanes, long long plane_stride, int round_y, float* __restrict__ r,
                        const float* __restrict__ w, uint16_t* __restrict__ out, int rows, int H,
                        float eps, int gemma) {
-  constexpr int RPB = WPR <= 4 ? 4 / WPR : 1;  // rows per workgroup
-  __shared__ float part[RPB][WPR];
+  constexpr int RPB = WPR <= 4 ? 4 / WPR : 1;  // rows per workgroup per iteration
+  constexpr int N4 = NV * WPR;                   // float4 per lane over the whole row
+  constexpr int S = N4 % 8 == 0 ? 8 : (N4 % 4 == 0 ? 4 : (N4 % 2 == 0 ? 2 : 1));
+  static_assert(S % WPR == 0, "each wave holds whole segments");
+  constexpr int SW = S / WPR;  // segments held by one wave
+  constexpr int PER = NV / SW;  // float4 per lane per segment
+  // Segment partials, double-buffered by iteration parity: a wave reuses a buffer two
+  // iterations later, after every wave has passed the barrier of the iteration in between
+  // (and so has finished reading it).
+  __shared__ float part[2][RPB][S];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int row_in = wave / WPR;
   const int wr = wave % WPR;
-  const int row = blockIdx.x * RPB + row_in;
-  const bool live = row < rows;
-  const long long base = (long long)(live ? row : 0) * H + wr * (H / WPR);
-  float4 v[NV];
-  float ss = 0.0f;
-  if (live) {
-    if (yb != nullptr) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int c = (i * 64 + lane) * 4;
-        const float4 rv = *reinterpret_cast<const float4*>(r + base + c);
-        const uint2 yv = *reinterpret_cast<const uint2*>(yb + base + c);
-        v[i] = make_float4(rv.x + bf16_to_f32(yv.x & 0xffffu), rv.y + bf16_to_f32(yv.x >> 16),
-                           rv.z + bf16_to_f32(yv.y & 0xffffu), rv.w + bf16_to_f32(yv.y >> 16));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int c = (i * 64 + lane) * 4;
-        const float4 rv = *reinterpret_cast<const float4*>(r + base + c);
-        float4 yv = *reinterpret_cast<const float4*>(yf + base + c);
-        for (int p = 1; p < nplanes; ++p) {
-          const float4 q = *reinterpret_cast<const float4*>(yf + p * plane_stride + base + c);
-          yv.x += q.x;
-          yv.y += q.y;
-          yv.z += q.z;
-          yv.w += q.w;
-        }
-        if (round_y) yv = round_bf16_4(yv);
-        v[i] = make_float4(rv.x + yv.x, rv.y + yv.y, rv.z + yv.z, rv.w + yv.w);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int c = (i * 64 + lane) * 4;
-      *reinterpret_cast<float4*>(r + base + c) = v[i];
-      ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
-    }
-    ss = wave_sum(ss);
-  }
-  if (WPR > 1) {
-    if (lane == 0) part[row_in][wr] = ss;
-    __syncthreads();
-    ss = 0.0f;
-#pragma unroll
-    for (int q = 0; q < WPR; ++q) ss += part[row_in][q];
-  }
-  if (!live) return;
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
   const float g0 = gemma ? 1.0f : 0.0f;
   const float* wc = w + wr * (H / WPR);
-  uint16_t* oc = out + base;
+  int parity = 0;
+  // The loop bound depends only on blockIdx, so every wave of a workgroup takes the same trips
+  // (the barrier below is uniform).
+  for (int group = blockIdx.x; group * RPB < rows; group += gridDim.x, parity ^= 1) {
+    // Keeps the norm-weight loads inside the loop: hoisted out of it they would hold NV more
+    // float4 per lane for the whole kernel (most workgroups run one trip).
+    asm volatile("" ::: "memory");
+    const int row = group * RPB + row_in;
+    const bool live = row < rows;
+    const long long base = (long long)(live ? row : 0) * H + wr * (H / WPR);
+    float4 v[NV];
+    float seg[SW];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c = (i * 64 + lane) * 4;
-    const float4 g = *reinterpret_cast<const float4*>(wc + c);
-    const uint32_t o0 = f32_to_bf16_rne(v[i].x * inv * (g.x + g0));
-    const uint32_t o1 = f32_to_bf16_rne(v[i].y * inv * (g.y + g0));
-    const uint32_t o2 = f32_to_bf16_rne(v[i].z * inv * (g.z + g0));
-    const uint32_t o3 = f32_to_bf16_rne(v[i].w * inv * (g.w + g0));
-    *reinterpret_cast<uint2*>(oc + c) = make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+    for (int j = 0; j < SW; ++j) seg[j] = 0.0f;
+    if (live) {
+      // Loads go out in batches of NV independent 16-byte loads per lane (the residual, then
+      // the first plane or the bf16 y, then each further plane), so each wave keeps a whole
+      // batch in flight rather than one load at a time.
+      float4 rv[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        rv[i] = *reinterpret_cast<const float4*>(r + base + (i * 64 + lane) * 4);
+      if constexpr (YB) {
+        (void)yf;
+        (void)nplanes;
+        (void)plane_stride;
+        (void)round_y;
+        uint2 yv[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          yv[i] = *reinterpret_cast<const uint2*>(yb + base + (i * 64 + lane) * 4);
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          v[i] = make_float4(rv[i].x + bf16_to_f32(yv[i].x & 0xffffu),
+                             rv[i].y + bf16_to_f32(yv[i].x >> 16),
+                             rv[i].z + bf16_to_f32(yv[i].y & 0xffffu),
+                             rv[i].w + bf16_to_f32(yv[i].y >> 16));
+      } else {
+        (void)yb;
+        // y = plane 0 + plane 1 + ... in plane order, then r + y.
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          v[i] = *reinterpret_cast<const float4*>(yf + base + (i * 64 + lane) * 4);
+        for (int p = 1; p < nplanes; ++p) {
+          float4 q[NV];
+#pragma unroll
+          for (int i = 0; i < NV; ++i)
+            q[i] = *reinterpret_cast<const float4*>(yf + p * plane_stride + base +
+                                                    (i * 64 + lane) * 4);
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            v[i].x += q[i].x;
+            v[i].y += q[i].y;
+            v[i].z += q[i].z;
+            v[i].w += q[i].w;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          if (round_y) v[i] = round_bf16_4(v[i]);
+          v[i] = make_float4(rv[i].x + v[i].x, rv[i].y + v[i].y, rv[i].z + v[i].z,
+                             rv[i].w + v[i].w);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = (i * 64 + lane) * 4;
+        *reinterpret_cast<float4*>(r + base + c) = v[i];
+      }
+#pragma unroll
+      for (int j = 0; j < SW; ++j) {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = j * PER; i < (j + 1) * PER; ++i)
+          a += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+        seg[j] = wave_sum(a);
+      }
+    }
+    float ss = 0.0f;
+    if (WPR > 1) {
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < SW; ++j) part[parity][row_in][wr * SW + j] = seg[j];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < S; ++q) ss += part[parity][row_in][q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < S; ++q) ss += seg[q];
+    }
+    if (live) {
+      const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+      uint16_t* oc = out + base;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = (i * 64 + lane) * 4;
+        const float4 g = *reinterpret_cast<const float4*>(wc + c);
+        const uint32_t o0 = f32_to_bf16_rne(v[i].x * inv * (g.x + g0));
+        const uint32_t o1 = f32_to_bf16_rne(v[i].y * inv * (g.y + g0));
+        const uint32_t o2 = f32_to_bf16_rne(v[i].z * inv * (g.z + g0));
+        const uint32_t o3 = f32_to_bf16_rne(v[i].w * inv * (g.w + g0));
+        *reinterpret_cast<uint2*>(oc + c) = make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+      }
+    }
   }
 }
 
-// Any H that is a multiple of 64 (and rows wider than the register-resident variants): two
-// passes over the row, the second re-reading the just-written residual.
+// Any H that is a multiple of 64 (and rows wider than the register-resident variants): one
+// wave per row, two passes over the row, the second re-reading the just-written residual.
+// Waves stride over rows by the grid size.
 __global__ void __launch_bounds__(256)
     add_rmsnorm_generic_kernel(const float* __restrict__ yf, const uint16_t* __restrict__ yb,
                                int nplanes, long long plane_stride, int round_y,
                                float* __restrict__ r, const float* __restrict__ w,
                                uint16_t* __restrict__ out, int rows, int H, float eps,
                                int gemma) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const long long base = (long long)row * H;
-  float ss = 0.0f;
-  for (int c = lane; c < H; c += 64) {
-    float y;
-    if (yb != nullptr) {
-      y = bf16_to_f32(yb[base + c]);
-    } else {
-      y = yf[base + c];
-      for (int p = 1; p < nplanes; ++p) y += yf[p * plane_stride + base + c];
-      if (round_y) y = bf16_to_f32(f32_to_bf16_rne(y));
-    }
-    const float v = r[base + c] + y;
-    r[base + c] = v;
-    ss += v * v;
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
   const float g0 = gemma ? 1.0f : 0.0f;
-  for (int c = lane; c < H; c += 64)
-    out[base + c] = (uint16_t)f32_to_bf16_rne(r[base + c] * inv * (w[c] + g0));
+  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
+    const long long base = (long long)row * H;
+    float ss = 0.0f;
+    for (int c = lane; c < H; c += 64) {
+      float y;
+      if (yb != nullptr) {
+        y = bf16_to_f32(yb[base + c]);
+      } else {
+        y = yf[base + c];
+        for (int p = 1; p < nplanes; ++p) y += yf[p * plane_stride + base + c];
+        if (round_y) y = bf16_to_f32(f32_to_bf16_rne(y));
+      }
+      const float v = r[base + c] + y;
+      r[base + c] = v;
+      ss += v * v;
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int c = lane; c < H; c += 64)
+      out[base + c] = (uint16_t)f32_to_bf16_rne(r[base + c] * inv * (w[c] + g0));
+  }
 }
 
 // --------------------------------------------------------------------------------------------
@@ -607,14 +667,17 @@ int launch_gemm_nb(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out
               BN, stages, MID, DEEP);
 }
 
-template <int NV, int WPR>
+template <int NV, int WPR, bool YB>
 int launch_addnorm_t(const void* y, int y_bf16, int nplanes, long long plane_stride, int round_y,
                      float* r, const float* w, uint16_t* out, int rows, int H, float eps,
-                     int gemma, hipStream_t s, hipEvent_t done, hipEvent_t t0, hipEvent_t t1) {
+                     int gemma, int max_wgs, hipStream_t s, hipEvent_t done, hipEvent_t t0,
+                     hipEvent_t t1) {
   constexpr int RPB = WPR <= 4 ? 4 / WPR : 1;
-  const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
+  int groups = (rows + RPB - 1) / RPB;
+  if (max_wgs > 0 && groups > max_wgs) groups = max_wgs;
+  const unsigned grid = (unsigned)groups;
   if (t0 != nullptr || (done != nullptr && ext_launch_events())) {
-    hipExtLaunchKernelGGL((add_rmsnorm_kernel<NV, WPR>), dim3(grid), dim3(64 * WPR * RPB), 0, s,
+    hipExtLaunchKernelGGL((add_rmsnorm_kernel<NV, WPR, YB>), dim3(grid), dim3(64 * WPR * RPB), 0, s,
                           t0, t0 != nullptr ? t1 : done, 0,
                           y_bf16 ? nullptr : static_cast<const float*>(y),
                           y_bf16 ? static_cast<const uint16_t*>(y) : nullptr, nplanes,
@@ -622,7 +685,7 @@ int launch_addnorm_t(const void* y, int y_bf16, int nplanes, long long plane_str
     return t0 != nullptr ? record_after(check_launch("add_rmsnorm_kernel"), done, s)
                          : check_launch("add_rmsnorm_kernel");
   }
-  hipLaunchKernelGGL((add_rmsnorm_kernel<NV, WPR>), dim3(grid), dim3(64 * WPR * RPB), 0, s,
+  hipLaunchKernelGGL((add_rmsnorm_kernel<NV, WPR, YB>), dim3(grid), dim3(64 * WPR * RPB), 0, s,
                      y_bf16 ? nullptr : static_cast<const float*>(y),
                      y_bf16 ? static_cast<const uint16_t*>(y) : nullptr, nplanes, plane_stride,
                      round_y, r, w, out, rows, H, eps, gemma);
@@ -657,31 +720,51 @@ int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, i
 
 int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_stride,
                        int round_y, float* r, const float* w, uint16_t* out, int rows, int H,
-                       float eps, int gemma, void* stream, void* done_event, void* start_timing,
-                       void* stop_timing) {
+                       float eps, int gemma, int max_wgs, void* stream, void* done_event,
+                       void* start_timing, void* stop_timing) {
   if (rows <= 0) return PR_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t done = static_cast<hipEvent_t>(done_event);
   hipEvent_t t0 = static_cast<hipEvent_t>(start_timing);
   hipEvent_t t1 = static_cast<hipEvent_t>(stop_timing);
-  // Waves per row: as many as keep >= 1 float4 per lane, until the launch has >= 2048 waves.
+  // Waves per row: the fewest that give an instantiated row share of at most 8 float4 per lane
+  // (when the segment count allows), then more (within the segment count and instantiated
+  // shares) until the launch has >= 2048 waves.  Whether the
+  // register-resident kernel is used at all depends on H only, and its result does not depend
+  // on the waves per row, so every row count gives the same result for a given H.
   if (H % 256 == 0) {
+    // At most 16 float4 per lane: the residual, the running y and one plane batch stay in
+    // registers together.
+    auto inst = [](int nv) {
+      return (nv >= 1 && nv <= 8) || nv == 10 || nv == 12 || nv == 14 || nv == 16;
+    };
     const int n4 = H / 256;  // float4 per lane for one wave per row
+    const int segs = n4 % 8 == 0 ? 8 : (n4 % 4 == 0 ? 4 : (n4 % 2 == 0 ? 2 : 1));
+    // At most 8 float4 per lane where the segments allow it (16 per lane takes the whole
+    // register file and leaves one wave per SIMD).
     int wpr = 1;
-    while (wpr < 8 && n4 % (2 * wpr) == 0 && (long long)rows * wpr < 2048) wpr *= 2;
+    while (wpr < segs && (!inst(n4 / wpr) || n4 / wpr > 8)) wpr *= 2;
+    while (inst(n4 / wpr) && 2 * wpr <= segs && inst(n4 / (2 * wpr)) &&
+           (long long)rows * wpr < 2048)
+      wpr *= 2;
     const int nv = n4 / wpr;
 #define PR_AN(NV_, W_)                                                                        \
-  if (nv == NV_ && wpr == W_)                                                                 \
-    return launch_addnorm_t<NV_, W_>(y, y_bf16, nplanes, plane_stride, round_y, r, w, out, rows, \
-                                     H, eps, gemma, s, done, t0, t1);
+  if (nv == NV_ && wpr == W_ && n4 == NV_ * W_)                                               \
+    return y_bf16 ? launch_addnorm_t<NV_, W_, true>(y, y_bf16, nplanes, plane_stride, round_y, r, \
+                                                    w, out, rows, H, eps, gemma, max_wgs, s,   \
+                                                    done, t0, t1)                              \
+                  : launch_addnorm_t<NV_, W_, false>(y, y_bf16, nplanes, plane_stride, round_y,  \
+                                                     r, w, out, rows, H, eps, gemma, max_wgs, \
+                                                     s, done, t0, t1);
 #define PR_AN_ALL(NV_) PR_AN(NV_, 1) PR_AN(NV_, 2) PR_AN(NV_, 4) PR_AN(NV_, 8)
     PR_AN_ALL(1) PR_AN_ALL(2) PR_AN_ALL(3) PR_AN_ALL(4) PR_AN_ALL(5) PR_AN_ALL(6) PR_AN_ALL(7)
-    PR_AN_ALL(8) PR_AN_ALL(10) PR_AN_ALL(12) PR_AN_ALL(14) PR_AN_ALL(16) PR_AN_ALL(20)
-    PR_AN_ALL(24) PR_AN_ALL(28) PR_AN_ALL(32)
+    PR_AN_ALL(8) PR_AN_ALL(10) PR_AN_ALL(12) PR_AN_ALL(14) PR_AN_ALL(16)
 #undef PR_AN_ALL
 #undef PR_AN
   }
-  const unsigned grid = (unsigned)((rows + 3) / 4);
+  int groups = (rows + 3) / 4;
+  if (max_wgs > 0 && groups > max_wgs) groups = max_wgs;
+  const unsigned grid = (unsigned)groups;
   if (t0 != nullptr) {
     hipExtLaunchKernelGGL(add_rmsnorm_generic_kernel, dim3(grid), dim3(256), 0, s, t0, t1, 0,
                           y_bf16 ? nullptr : static_cast<const float*>(y),

@@ -222,7 +222,7 @@ int run_conventional(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, 
     }));
     PR_TRY(timed(c, 1, [&](hipEvent_t t0, hipEvent_t t1) {
       return launch_add_rmsnorm(c->conv, 1, 1, plane, 0, r, w, out, T, H, eps,
-                                norm_kind == PR_NORM_GEMMA, s, nullptr, t0, t1);
+                                norm_kind == PR_NORM_GEMMA, 0, s, nullptr, t0, t1);
     }));
   } else {
     // K split: fp32 partial planes, summed and rounded to bf16 before the add.
@@ -232,7 +232,7 @@ int run_conventional(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, 
     }));
     PR_TRY(timed(c, 1, [&](hipEvent_t t0, hipEvent_t t1) {
       return launch_add_rmsnorm(c->conv, 0, g.split, plane, 1, r, w, out, T, H, eps,
-                                norm_kind == PR_NORM_GEMMA, s, nullptr, t0, t1);
+                                norm_kind == PR_NORM_GEMMA, 0, s, nullptr, t0, t1);
     }));
   }
   return PR_OK;
@@ -257,6 +257,7 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
     c->slots = static_cast<float*>(p);
     c->slot_elems = slot_elems;
   }
+  const int an_wgs = env_int("PR_FORCE_ADDNORM_WGS");
   const int delay = env_int("PR_DEBUG_DELAY");
   const bool poison = env_int("PR_DEBUG_POISON") != 0;
   const int gemma = norm_kind == PR_NORM_GEMMA;
@@ -304,7 +305,7 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
         if (delay > 0) PR_TRY(launch_delay(delay, st));
         PR_TRY(timed(c, 1, [&](hipEvent_t t0, hipEvent_t t1) {
           return launch_add_rmsnorm(slot, 0, g.split, (long long)op.rows * H, 0, r + row0 * H,
-                                    w, out + row0 * H, op.rows, H, eps, gemma, st,
+                                    w, out + row0 * H, op.rows, H, eps, gemma, an_wgs, st,
                                     fuse_next ? c->done[op.slot] : nullptr, t0, t1);
         }));
         if (poison) PR_TRY(launch_fill_nan(slot, c->slot_elems, st));

@@ -26,7 +26,8 @@ if torch.cuda.is_available():
 @pytest.fixture(autouse=True)
 def _env(monkeypatch):
     for k in ("PR_MICROCHUNK_TOKENS", "PR_THRESHOLD_TOKENS", "PR_FORCE_TILE", "PR_FORCE_SPLIT",
-              "PR_FORCE_WAVES", "PR_FORCE_STAGES", "PR_DEBUG_POISON", "PR_DEBUG_DELAY",
+              "PR_FORCE_WAVES", "PR_FORCE_STAGES", "PR_FORCE_ADDNORM_WGS", "PR_DEBUG_POISON",
+              "PR_DEBUG_DELAY",
               "PR_FAULT_INJECT"):
         monkeypatch.delenv(k, raising=False)
     pr.pr_clear_tuning()
@@ -119,6 +120,25 @@ def test_padded_rows_untouched(T, mc):
         assert np.all(out_all[T:] == 0x7BAD)
 
 
+# ------------------------------------------------------- add/norm workgroup cap is inert
+@pytest.mark.parametrize("T,K,H", [(700, 512, 4096), (301, 512, 320)])
+def test_addnorm_workgroup_cap_is_bitwise_inert(monkeypatch, T, K, H):
+    """The pipeline's add/norm may run on fewer workgroups than row groups (each strides over
+    row groups); results are bitwise those of the uncapped launch, for the register-resident
+    kernel (H = 4096) and the generic one (H = 320), including a partial last row group."""
+    d = synth.make_custom(T, K, H, seed=15)
+    dev = Device(d)
+    dev.reset()
+    r1, o1 = dev.run(128)
+    for cap in ("1", "7", "64"):
+        monkeypatch.setenv("PR_FORCE_ADDNORM_WGS", cap)
+        dev.reset()
+        r2, o2 = dev.run(128)
+        np.testing.assert_array_equal(r1, r2)
+        np.testing.assert_array_equal(o1, o2)
+    _check(d, r1, o1, "fused")
+
+
 # --------------------------------------------------------------- zero-padded K is inert
 @pytest.mark.parametrize("tile", ["256x256", "128x128"])
 def test_zero_padded_k_is_bitwise_inert(monkeypatch, tile):
@@ -142,14 +162,18 @@ def test_zero_padded_k_is_bitwise_inert(monkeypatch, tile):
 
 
 # ---------------------------------------------------------------- chunked == unchunked
-@pytest.mark.parametrize("tile,split", [("256x256", 1), ("128x128", 2)])
-def test_microchunked_equals_unchunked_bitwise(monkeypatch, tile, split):
+@pytest.mark.parametrize("tile,split,T,K,H", [("256x256", 1, 1000, 1024, 512),
+                                               ("128x128", 2, 1000, 1024, 512),
+                                               ("256x128", 1, 1100, 512, 4096)])
+def test_microchunked_equals_unchunked_bitwise(monkeypatch, tile, split, T, K, H):
+    """With the projection configuration pinned, every row's arithmetic is the same whatever
+    the chunk size (the add/norm's row split depends on H only)."""
     monkeypatch.setenv("PR_FORCE_TILE", tile)
     monkeypatch.setenv("PR_FORCE_SPLIT", str(split))
-    d = synth.make_custom(1000, 1024, 512, seed=7)
+    d = synth.make_custom(T, K, H, seed=7)
     dev = Device(d)
     dev.reset()
-    r1, o1 = dev.run(1000)
+    r1, o1 = dev.run(T)
     for mc in (100, 256, 333, 512):
         dev.reset()
         r2, o2 = dev.run(mc)
