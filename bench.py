@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--workload", default="o_proj")
     ap.add_argument("--microchunk", type=int, default=0, help="0: every chunk size of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="skip the load-time tuning (chunk projections use the time model)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_o_proj.json"),
                     help="measured HBM bytes per projection launch (from the counter runs)")
@@ -58,6 +60,12 @@ def time_steps(call, steps: int, warmup: int, torch):
         call()
     torch.cuda.synchronize()
     return time.perf_counter() - t0
+
+
+def traffic_label(workload: str, mc: int, chunk_cfgs: dict) -> str:
+    """Label of a traffic measurement: workload, chunk size and the chunk projection
+    configuration it ran with (counters taken under another configuration do not apply)."""
+    return f"{workload}:mc={mc}:{chunk_cfgs.get(str(mc), 'model')}"
 
 
 def cpu_baseline(d, seconds: float) -> dict:
@@ -150,6 +158,19 @@ def main() -> int:
         pr.proj_add_rmsnorm_unfused(x, Wp, r, w, d["eps"], T, K, H, wl.norm_kind, out)
 
     mcs = [args.microchunk] if args.microchunk else list(wl.microchunks)
+    # The library's load-time tuning for this shape group (untimed): it picks the projection
+    # configuration of each chunk size (checked against the conventional path) and a token
+    # threshold for auto mode.  Explicit-chunk calls below use the tuned configurations.
+    chunk_cfgs = {}
+    if not args.no_tune:
+        t_tune = time.perf_counter()
+        rep = pr.pr_tune([K], [H], wl.norm_kind, [T], mcs, reps=5, stream=stream)
+        for m in mcs:
+            c = pr.pr_select(T, K, H, m)
+            chunk_cfgs[str(m)] = (f"{c['gemm_bm']}x{c['gemm_bn']} split {c['split_k']} "
+                                  f"{c['gemm_waves']} waves")
+        log(f"tuned in {time.perf_counter() - t_tune:.1f} s: {chunk_cfgs} "
+            f"(checked {rep['n_checked']}, rejected {rep['n_rejected']})")
     per_mc = {}
     for mc in mcs:
         el = time_steps(fused(mc), args.steps, args.warmup, torch)
@@ -200,7 +221,7 @@ def main() -> int:
             tr = json.load(f)
         src = os.path.join(ROOT, "projection_residual_rmsnorm_amd", "csrc", "pr_kernels.hip")
         if (tr.get("kernel_source_sha256") == source_digest(src)
-                and tr.get("config") == f"{wl.name}:mc={mc}"):
+                and tr.get("config") == traffic_label(wl.name, mc, chunk_cfgs)):
             traffic = tr.get("gemm_bytes_per_launch")
     roof = {"kernel": "gemm_bf16_kernel", "bound": "mfma", "achieved": gemm_tflops,
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
@@ -221,6 +242,7 @@ def main() -> int:
         "tflops": tflops, "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "roofline": roof, "kernels": kernels,
         "per_microchunk": {str(k): v for k, v in per_mc.items()},
+        "chunk_configs": chunk_cfgs,
         "conventional": conv,
     }
     if args.copy_calibration:

@@ -152,6 +152,7 @@ typedef struct {
   int split_k;    /* K partitions of the projection; partial sums are added in order */
   int gemm_waves; /* waves per projection workgroup (4 or 8)                         */
   int reason;     /* PR_REASON_*                                                    */
+  int gemm_stages; /* LDS ring depth of the projection (0 = the tile's default)      */
 } pr_decision;
 
 #define PR_REASON_EXPLICIT 0          /* microchunk > 0 given by the caller            */
@@ -219,6 +220,20 @@ int pr_threshold_from_timings(int ngroups, int nT, const int* T_grid, const doub
  * with PR_ERR_UNSUPPORTED.  threshold_tokens = INT32_MAX marks an inconclusive tuning. */
 int pr_set_tuning(int K, int H, int threshold_tokens, int max_tokens, const int* T_grid,
                   const int* mc_for_T, int nT);
+
+/* Install the projection configuration used for the chunks of every fused call of the shape
+ * group (K, H) with this microchunk (explicit or auto): tile tile_m x tile_n (256x256, 256x128
+ * or 128x128), split_k K partitions (split_k divides K/64), waves 4 or 8 per workgroup.  This
+ * is the MI355X form of the SM-count targets the "TPSP Design" page tunes per group next to
+ * the chunk size (section 3, Profiling and fallback): the tile and K split fix how many CUs a
+ * chunk's projection occupies while the neighbouring chunk's projection and add/norm share the
+ * GPU.  pr_tune installs these; without one, a time model chooses.  The result changes only
+ * by summation order (within the parity tolerance).  Errors: PR_ERR_SHAPE, PR_ERR_MICROCHUNK,
+ * PR_ERR_INVALID_ARG. */
+int pr_set_chunk_config(int K, int H, int microchunk, int tile_m, int tile_n, int split_k,
+                        int waves);
+
+/* Remove every installed tuning result and chunk configuration. */
 void pr_clear_tuning(void);
 
 typedef struct {
@@ -234,8 +249,12 @@ typedef struct {
  * each candidate's result is first checked against the conventional path's result and dropped
  * if it fails: output relative L2 <= 5e-3 and per element |delta| <= 2e-2 + one bf16 ulp (both
  * outputs are rounded); residual per element within half a bf16 ulp of y plus fp32 rounding
- * (the paths differ exactly by the bf16 rounding of y).  Timings are medians of `reps` calls on synthetic device data.  Installs the result
- * with pr_set_tuning for every group.  timings_out (optional): [ngroups][nT][2 + nmc] seconds
+ * (the paths differ exactly by the bf16 rounding of y).  Timings are medians of `reps` calls
+ * on synthetic device data.  Before that, for each group and chunk size, the projection
+ * configurations the time model ranks within 1.5x of its best (up to 6) are timed in the
+ * pipeline at T = min(max T_grid, 4 x chunk size) and the fastest that passes the same check is
+ * installed with pr_set_chunk_config (skipped when a PR_FORCE_* override is set).  Installs the
+ * result with pr_set_tuning for every group.  timings_out (optional): [ngroups][nT][2 + nmc] seconds
  * (conventional, best fused, then each candidate; <= 0 for skipped or rejected candidates).
  * With PR_MICROCHUNK_TOKENS and PR_THRESHOLD_TOKENS both set, nothing is timed or checked and
  * the override is installed.

@@ -46,7 +46,7 @@ _vp, _i, _f, _d = _c.c_void_p, _c.c_int, _c.c_float, _c.c_double
 class pr_decision(_c.Structure):
     _fields_ = [("path", _i), ("microchunk", _i), ("n_chunks", _i), ("last_valid", _i),
                 ("gemm_bm", _i), ("gemm_bn", _i), ("split_k", _i), ("gemm_waves", _i),
-                ("reason", _i)]
+                ("reason", _i), ("gemm_stages", _i)]
 
 
 class pr_plan_op(_c.Structure):
@@ -76,6 +76,7 @@ SIGNATURES = {
     "pr_threshold_from_timings": (_i, [_i, _i, _c.POINTER(_i), _c.POINTER(_d), _c.POINTER(_d),
                                        _c.POINTER(_d), _c.POINTER(_i)]),
     "pr_set_tuning": (_i, [_i, _i, _i, _i, _c.POINTER(_i), _c.POINTER(_i), _i]),
+    "pr_set_chunk_config": (_i, [_i, _i, _i, _i, _i, _i, _i]),
     "pr_clear_tuning": (None, []),
     "pr_tune": (_i, [_c.POINTER(_i), _c.POINTER(_i), _i, _i, _c.POINTER(_i), _i, _c.POINTER(_i),
                      _i, _i, _c.POINTER(pr_tune_report), _c.POINTER(_d), _vp]),
@@ -223,6 +224,11 @@ def pr_set_tuning(K: int, H: int, threshold_tokens: int, max_tokens: int,
     n = len(T_grid)
     _check(_lib().pr_set_tuning(K, H, threshold_tokens, max_tokens, (ctypes.c_int * n)(*T_grid),
                                 (ctypes.c_int * n)(*mc_for_T), n))
+
+
+def pr_set_chunk_config(K: int, H: int, microchunk: int, tile_m: int, tile_n: int, split_k: int,
+                        waves: int) -> None:
+    _check(_lib().pr_set_chunk_config(K, H, microchunk, tile_m, tile_n, split_k, waves))
 
 
 def pr_clear_tuning() -> None:

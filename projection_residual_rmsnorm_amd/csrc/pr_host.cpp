@@ -10,6 +10,7 @@
 #include <cstring>
 #include <limits>
 #include <map>
+#include <tuple>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -30,6 +31,8 @@ struct Tuning {
 };
 std::mutex g_tuning_mu;
 std::map<std::pair<int, int>, Tuning> g_tuning;  // keyed by (K, H)
+// Tuned projection configuration of the chunks, keyed by (K, H, microchunk).
+std::map<std::tuple<int, int, int>, GemmCfg> g_chunk_cfg;
 
 constexpr long long kMaxWeightElems = 1LL << 30;  // K*H <= 2^30 (2 GiB of bf16)
 }  // namespace
@@ -117,37 +120,50 @@ static int apply_forced_tile(int K, GemmCfg* g) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Projection tile choice.  Time model per workgroup wave: the MFMA time of one tile at the
-// tile's sustained fraction of peak, times the number of rounds of 256 workgroups, plus the
-// HBM/MALL time of the extra fp32 partial planes that a K split writes and the add/norm reads.
+// Projection tile choice: a time model fitted to measured projection times on MI355X (random
+// bf16 data; the fit is within a few percent on shapes from 256 x 4096 x 4096 to 32768 x 8192
+// x 8192).  Under sustained MFMA load the chip is power-limited, so it delivers about R flop/s
+// in total however many CUs are busy, while a CU whose neighbours idle runs up to a per-tile
+// ceiling r_max (clock headroom, its own load path).  A round of `active` workgroups (one per
+// CU) therefore runs each CU at min(r_max, eff * R / active).  The last, partial round is timed
+// at its own size.  Output writes (bf16 y or `split` fp32 planes) cost bytes / BW_W, and the
+// add/norm's read of the planes bytes / BW_R.
 // ---------------------------------------------------------------------------------------------
+namespace {
+constexpr double kChipRate = 1.3e15;                           // R, flop/s
+constexpr double kTileEff[kNumTileCfgs] = {1.0, 0.85, 0.7};    // 256x256, 256x128, 128x128
+constexpr double kTileRmax[kNumTileCfgs] = {7.0e12, 4.5e12, 3.5e12};  // per CU, flop/s
+constexpr double kFixedK = 64;   // per-workgroup fixed cost in K-elements (prologue, epilogue)
+constexpr double kWriteBW = 6.0e12;
+constexpr double kReadBW = 5.5e12;
+}  // namespace
+
+double model_gemm_time(int M, int N, int K, int c, int split, bool fp32_out) {
+  const int bm = kTileBM[c], bn = kTileBN[c];
+  const long long units = (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn) * split;
+  const long long full = units / kNumCUs, rem = units % kNumCUs;
+  const double tile_flops = 2.0 * bm * bn * ((double)K / split + kFixedK);
+  auto round_t = [&](long long active) {
+    return tile_flops / std::min(kTileRmax[c], kTileEff[c] * kChipRate / (double)active);
+  };
+  double t = (double)full * round_t(kNumCUs) + (rem > 0 ? round_t(rem) : 0.0);
+  const bool planes = fp32_out || split > 1;
+  const double y_bytes = (planes ? 4.0 * split : 2.0) * M * (double)N;
+  return t + y_bytes / kWriteBW + y_bytes / kReadBW;
+}
+
 GemmCfg choose_gemm(int M, int N, int K, bool fp32_out) {
-  // Sustained fraction of the 256x256 tile's rate per tile shape (measured with two waves per
-  // SIMD), and a fixed per-workgroup cost of about three K-stages (prologue + epilogue).
-  static const double kEff[kNumTileCfgs] = {1.0, 0.8, 0.65};
-  const double per_cu_flops = 1.2e15 / kNumCUs;  // sustained 256x256 rate per CU
-  const double bw = 5.0e12;
   GemmCfg best;
   best.waves = 8;
   double best_t = std::numeric_limits<double>::infinity();
   for (int c = 0; c < kNumTileCfgs; ++c) {
-    const int bm = kTileBM[c], bn = kTileBN[c];
-    const long long tiles = (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     for (int split = 1; split <= 16; split *= 2) {
       if (K % (64 * split) != 0) break;
-      const long long units = tiles * split;
-      const long long rounds = (units + kNumCUs - 1) / kNumCUs;
-      const double t_mfma = (double)rounds * 2.0 * bm * bn * (double)(K / split + 96) /
-                            (per_cu_flops * kEff[c]);
-      // bytes of y moved between projection and add/norm beyond a single bf16 (conventional)
-      // or fp32 (pipeline) plane
-      const double base_bytes = (fp32_out ? 8.0 : 4.0) * M * (double)N;
-      const double bytes = split == 1 ? base_bytes : 8.0 * split * M * (double)N;
-      const double t = t_mfma + (bytes - base_bytes) / bw;
+      const double t = model_gemm_time(M, N, K, c, split, fp32_out);
       if (t < best_t * 0.999) {
         best_t = t;
-        best.bm = bm;
-        best.bn = bn;
+        best.bm = kTileBM[c];
+        best.bn = kTileBN[c];
         best.split = split;
       }
     }
@@ -230,7 +246,16 @@ int decide(int T, int K, int H, int microchunk, pr_decision* d) {
     d->microchunk = mc;
     d->n_chunks = T > 0 ? (T + mc - 1) / mc : 0;
     d->last_valid = T > 0 ? T - (d->n_chunks - 1) * mc : 0;
-    g = choose_gemm(eff, H, K, true);
+    bool tuned = false;
+    {
+      std::lock_guard<std::mutex> lk(g_tuning_mu);
+      auto it = g_chunk_cfg.find({K, H, mc});
+      if (it != g_chunk_cfg.end()) {
+        g = it->second;
+        tuned = true;
+      }
+    }
+    if (!tuned) g = choose_gemm(eff, H, K, true);
   } else {
     d->microchunk = T;
     d->n_chunks = T > 0 ? 1 : 0;
@@ -243,6 +268,7 @@ int decide(int T, int K, int H, int microchunk, pr_decision* d) {
   d->gemm_bn = g.bn;
   d->split_k = g.split;
   d->gemm_waves = g.waves;
+  d->gemm_stages = g.stages;
   return PR_OK;
 }
 
@@ -437,9 +463,32 @@ int pr_set_tuning(int K, int H, int threshold_tokens, int max_tokens, const int*
   return PR_OK;
 }
 
+int pr_set_chunk_config(int K, int H, int microchunk, int tile_m, int tile_n, int split_k,
+                        int waves) {
+  if (K <= 0 || H <= 0 || K % 64 != 0 || H % 64 != 0)
+    return fail(PR_ERR_SHAPE, "K=%d and H=%d must be positive multiples of 64", K, H);
+  if (microchunk <= 0 || microchunk > PR_MAX_MICROCHUNK)
+    return fail(PR_ERR_MICROCHUNK, "microchunk=%d out of range", microchunk);
+  bool known = false;
+  for (int c = 0; c < kNumTileCfgs; ++c) known |= (kTileBM[c] == tile_m && kTileBN[c] == tile_n);
+  if (!known) return fail(PR_ERR_INVALID_ARG, "no projection tile %dx%d", tile_m, tile_n);
+  if (split_k <= 0 || K % (64 * split_k) != 0)
+    return fail(PR_ERR_INVALID_ARG, "split_k=%d must divide K/64 = %d", split_k, K / 64);
+  if (waves != 4 && waves != 8) return fail(PR_ERR_INVALID_ARG, "waves=%d must be 4 or 8", waves);
+  GemmCfg g;
+  g.bm = tile_m;
+  g.bn = tile_n;
+  g.split = split_k;
+  g.waves = waves;
+  std::lock_guard<std::mutex> lk(g_tuning_mu);
+  g_chunk_cfg[{K, H, microchunk}] = g;
+  return PR_OK;
+}
+
 void pr_clear_tuning(void) {
   std::lock_guard<std::mutex> lk(g_tuning_mu);
   g_tuning.clear();
+  g_chunk_cfg.clear();
 }
 
 }  // extern "C"

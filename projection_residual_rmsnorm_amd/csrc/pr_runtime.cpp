@@ -214,6 +214,7 @@ int run_conventional(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, 
   g.bn = d.gemm_bn;
   g.split = d.split_k;
   g.waves = d.gemm_waves;
+  g.stages = d.gemm_stages;
   const long long plane = (long long)T * H;
   if (g.split == 1) {
     PR_TRY(grow(&c->conv, &c->conv_bytes, (size_t)plane * 2));
@@ -247,6 +248,7 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
   g.bn = d.gemm_bn;
   g.split = d.split_k;
   g.waves = d.gemm_waves;
+  g.stages = d.gemm_stages;
   const int rows_max = std::min(mc, T);
   const long long plane = (long long)rows_max * H;  // elements of one partial plane
   const size_t slot_elems = (size_t)plane * g.split;

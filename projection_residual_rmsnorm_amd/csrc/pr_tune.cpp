@@ -155,6 +155,12 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
   }
   std::vector<int> cands(mc_cand, mc_cand + nmc);
   if (have_mc) cands.assign(1, mc_ov);
+  auto env_on = [](const char* n) {
+    const char* v = std::getenv(n);
+    return v != nullptr && v[0] != '\0';
+  };
+  const bool forced_cfg = env_on("PR_FORCE_TILE") || env_on("PR_FORCE_SPLIT") ||
+                          env_on("PR_FORCE_WAVES") || env_on("PR_FORCE_STAGES");
   const int ncols = 2 + nmc;
   std::vector<double> t_conv(ngroups * nT, -1), t_fused(ngroups * nT, -1),
       spread(ngroups * nT, 0);
@@ -183,41 +189,99 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
     PR_TRY(pr_prepare_weight((const uint16_t*)Wsrc.p, PR_WEIGHT_OUT_IN, (uint16_t*)Wp.p, K, H, s));
     PR_HIP(hipStreamSynchronize(s));
 
-    for (int i = 0; i < nT; ++i) {
-      const int T = T_grid[i];
-      const size_t rows_chk = (size_t)std::min(T, 256);
-      // rows checked: the first rows_chk and the last rows_chk (covers the padded tail chunk)
-      const size_t tail0 = (size_t)T - rows_chk;
-      auto fetch = [&](std::vector<uint16_t>& o, std::vector<float>& rr) -> int {
-        o.resize(2 * rows_chk * H);
-        rr.resize(2 * rows_chk * H);
-        PR_HIP(hipMemcpyAsync(o.data(), out.p, rows_chk * H * 2, hipMemcpyDeviceToHost, s));
-        PR_HIP(hipMemcpyAsync(o.data() + rows_chk * H, (uint16_t*)out.p + tail0 * H,
-                              rows_chk * H * 2, hipMemcpyDeviceToHost, s));
-        PR_HIP(hipMemcpyAsync(rr.data(), r.p, rows_chk * H * 4, hipMemcpyDeviceToHost, s));
-        PR_HIP(hipMemcpyAsync(rr.data() + rows_chk * H, (float*)r.p + tail0 * H,
-                              rows_chk * H * 4, hipMemcpyDeviceToHost, s));
-        PR_HIP(hipStreamSynchronize(s));
-        return PR_OK;
-      };
-      auto reset_r = [&]() -> int {
-        PR_HIP(hipMemcpyAsync(r.p, r0.p, (size_t)T * H * 4, hipMemcpyDeviceToDevice, s));
-        return PR_OK;
-      };
-      std::vector<float> r_old(2 * rows_chk * H);
+    // Rows checked at a token count T: the first min(T, 256) and the last as many (covers the
+    // padded tail chunk).
+    auto rows_chk_of = [](int T) { return (size_t)std::min(T, 256); };
+    auto fetch = [&](int T, std::vector<uint16_t>& o, std::vector<float>& rr) -> int {
+      const size_t rows_chk = rows_chk_of(T), tail0 = (size_t)T - rows_chk;
+      o.resize(2 * rows_chk * H);
+      rr.resize(2 * rows_chk * H);
+      PR_HIP(hipMemcpyAsync(o.data(), out.p, rows_chk * H * 2, hipMemcpyDeviceToHost, s));
+      PR_HIP(hipMemcpyAsync(o.data() + rows_chk * H, (uint16_t*)out.p + tail0 * H,
+                            rows_chk * H * 2, hipMemcpyDeviceToHost, s));
+      PR_HIP(hipMemcpyAsync(rr.data(), r.p, rows_chk * H * 4, hipMemcpyDeviceToHost, s));
+      PR_HIP(hipMemcpyAsync(rr.data() + rows_chk * H, (float*)r.p + tail0 * H,
+                            rows_chk * H * 4, hipMemcpyDeviceToHost, s));
+      PR_HIP(hipStreamSynchronize(s));
+      return PR_OK;
+    };
+    auto reset_r = [&](int T) -> int {
+      PR_HIP(hipMemcpyAsync(r.p, r0.p, (size_t)T * H * 4, hipMemcpyDeviceToDevice, s));
+      return PR_OK;
+    };
+    auto old_rows = [&](int T, std::vector<float>& r_old) -> int {
+      const size_t rows_chk = rows_chk_of(T), tail0 = (size_t)T - rows_chk;
+      r_old.resize(2 * rows_chk * H);
       PR_HIP(hipMemcpyAsync(r_old.data(), r0.p, rows_chk * H * 4, hipMemcpyDeviceToHost, s));
       PR_HIP(hipMemcpyAsync(r_old.data() + rows_chk * H, (float*)r0.p + tail0 * H,
                             rows_chk * H * 4, hipMemcpyDeviceToHost, s));
-      auto conv_call = [&]() {
-        return proj_add_rmsnorm_unfused((const uint16_t*)x.p, (const uint16_t*)Wp.p, (float*)r.p,
-                                        (const float*)w.p, 1e-5f, T, K, H, norm_kind,
-                                        (uint16_t*)out.p, s);
-      };
+      PR_HIP(hipStreamSynchronize(s));
+      return PR_OK;
+    };
+    auto conv_call_at = [&](int T) {
+      return proj_add_rmsnorm_unfused((const uint16_t*)x.p, (const uint16_t*)Wp.p, (float*)r.p,
+                                      (const float*)w.p, 1e-5f, T, K, H, norm_kind,
+                                      (uint16_t*)out.p, s);
+    };
+    auto fused_call_at = [&](int T, int mc) {
+      return proj_add_rmsnorm((const uint16_t*)x.p, (const uint16_t*)Wp.p, (float*)r.p,
+                              (const float*)w.p, 1e-5f, T, K, H, mc, norm_kind, (uint16_t*)out.p,
+                              s);
+    };
+
+    // Chunk projection configuration per chunk size (the CU footprint of a chunk's
+    // projection): the model's best candidates, timed in the pipeline, checked like any
+    // candidate.  The fastest that passes is installed for the group.
+    if (!forced_cfg) {
+      for (const int mc : cands) {
+        if (mc > std::min(Tmax, PR_MAX_MICROCHUNK)) continue;
+        const int Tc = std::min(Tmax, 4 * mc);
+        struct Cand {
+          double t;
+          int c, split;
+        };
+        std::vector<Cand> cs;
+        for (int c = 0; c < kNumTileCfgs; ++c)
+          for (int split = 1; split <= 16 && K % (64 * split) == 0; split *= 2)
+            cs.push_back({model_gemm_time(std::min(mc, Tc), H, K, c, split, true), c, split});
+        std::sort(cs.begin(), cs.end(), [](const Cand& a, const Cand& b) { return a.t < b.t; });
+        std::vector<uint16_t> out_ref, out_try;
+        std::vector<float> r_ref, r_try, r_before;
+        PR_TRY(old_rows(Tc, r_before));
+        PR_TRY(reset_r(Tc));
+        PR_TRY(conv_call_at(Tc));
+        PR_TRY(fetch(Tc, out_ref, r_ref));
+        double best_t = -1;
+        int best_k = -1;
+        for (size_t k = 0; k < cs.size() && k < 6 && cs[k].t <= 1.5 * cs[0].t; ++k) {
+          PR_TRY(pr_set_chunk_config(K, H, mc, kTileBM[cs[k].c], kTileBN[cs[k].c], cs[k].split,
+                                     8));
+          PR_TRY(reset_r(Tc));
+          PR_TRY(fused_call_at(Tc, mc));
+          PR_TRY(fetch(Tc, out_try, r_try));
+          if (!candidate_ok(out_try, out_ref, r_try, r_ref, r_before)) continue;
+          Stats st;
+          PR_TRY(time_calls([&]() { return fused_call_at(Tc, mc); }, reps, s, &st));
+          if (best_t < 0 || st.median < best_t) {
+            best_t = st.median;
+            best_k = (int)k;
+          }
+        }
+        const Cand& pick = cs[best_k >= 0 ? best_k : 0];
+        PR_TRY(pr_set_chunk_config(K, H, mc, kTileBM[pick.c], kTileBN[pick.c], pick.split, 8));
+      }
+    }
+
+    for (int i = 0; i < nT; ++i) {
+      const int T = T_grid[i];
+      std::vector<float> r_old;
+      PR_TRY(old_rows(T, r_old));
+      auto conv_call = [&]() { return conv_call_at(T); };
       std::vector<uint16_t> out_c, out_f;
       std::vector<float> r_c, r_f;
-      PR_TRY(reset_r());
+      PR_TRY(reset_r(T));
       PR_TRY(conv_call());
-      PR_TRY(fetch(out_c, r_c));
+      PR_TRY(fetch(T, out_c, r_c));
       Stats sc;
       PR_TRY(time_calls(conv_call, reps, s, &sc));
       t_conv[g * nT + i] = sc.median;
@@ -228,14 +292,10 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
       for (size_t j = 0; j < cands.size(); ++j) {
         const int mc = cands[j];
         if (mc > std::min(T, PR_MAX_MICROCHUNK)) continue;
-        auto fused_call = [&]() {
-          return proj_add_rmsnorm((const uint16_t*)x.p, (const uint16_t*)Wp.p, (float*)r.p,
-                                  (const float*)w.p, 1e-5f, T, K, H, mc, norm_kind,
-                                  (uint16_t*)out.p, s);
-        };
-        PR_TRY(reset_r());
+        auto fused_call = [&]() { return fused_call_at(T, mc); };
+        PR_TRY(reset_r(T));
         PR_TRY(fused_call());
-        PR_TRY(fetch(out_f, r_f));
+        PR_TRY(fetch(T, out_f, r_f));
         if (!candidate_ok(out_f, out_c, r_f, r_c, r_old)) {
           ++rep_local.n_rejected;
           continue;

@@ -139,6 +139,26 @@ def test_addnorm_workgroup_cap_is_bitwise_inert(monkeypatch, T, K, H):
     _check(d, r1, o1, "fused")
 
 
+# ------------------------------------------------------------ installed chunk configuration
+def test_installed_chunk_config_matches_forced(monkeypatch):
+    """A chunk configuration installed for (K, H, microchunk) runs exactly that configuration:
+    bitwise equal to the same configuration forced through the debug overrides."""
+    d = synth.make_custom(600, 1024, 768, seed=16)
+    dev = Device(d)
+    pr.pr_set_chunk_config(1024, 768, 256, 256, 128, 2, 4)
+    dev.reset()
+    r1, o1 = dev.run(256)
+    pr.pr_clear_tuning()
+    monkeypatch.setenv("PR_FORCE_TILE", "256x128")
+    monkeypatch.setenv("PR_FORCE_SPLIT", "2")
+    monkeypatch.setenv("PR_FORCE_WAVES", "4")
+    dev.reset()
+    r2, o2 = dev.run(256)
+    np.testing.assert_array_equal(r1, r2)
+    np.testing.assert_array_equal(o1, o2)
+    _check(d, r1, o1, "fused")
+
+
 # --------------------------------------------------------------- zero-padded K is inert
 @pytest.mark.parametrize("tile", ["256x256", "128x128"])
 def test_zero_padded_k_is_bitwise_inert(monkeypatch, tile):
@@ -289,6 +309,10 @@ def test_auto_mode_overrides_and_tuning(monkeypatch):
     assert rep["max_tokens"] == 512
     for row in rep["timings"][0]:
         assert row[0] > 0 and row[1] > 0
+    for mc in (64, 128, 256):  # a chunk configuration was tuned and installed per chunk size
+        cfg = pr.pr_select(512, 512, 512, mc)
+        assert (cfg["gemm_bm"], cfg["gemm_bn"]) in ((256, 256), (256, 128), (128, 128))
+        assert 512 % (64 * cfg["split_k"]) == 0 and cfg["gemm_waves"] in (4, 8)
     sel = pr.pr_select(512, 512, 512, 0)
     thr = rep["threshold_tokens"]
     assert sel["path"] == (pr.PR_PATH_FUSED if 512 >= thr else pr.PR_PATH_CONVENTIONAL)

@@ -111,7 +111,34 @@ def test_forced_projection_config(monkeypatch):
             monkeypatch.setenv(name, {"PR_FORCE_TILE": "128x128", "PR_FORCE_SPLIT": "2",
                                       "PR_FORCE_WAVES": "4"}[name])
     monkeypatch.setenv("PR_FORCE_STAGES", "6")  # an instantiated depth of the 128x128 tile
-    assert pr.pr_select(512, 4096, 4096, 512)["gemm_bm"] == 128
+    d = pr.pr_select(512, 4096, 4096, 512)
+    assert d["gemm_bm"] == 128 and d["gemm_stages"] == 6
+
+
+def test_chunk_config_table(monkeypatch):
+    """A tuned chunk configuration applies to fused calls of its group and chunk size only;
+    clearing the tuning removes it; forced overrides still win."""
+    base = pr.pr_select(2048, 4096, 4096, 512)
+    pr.pr_set_chunk_config(4096, 4096, 512, 256, 256, 4, 4)
+    d = pr.pr_select(2048, 4096, 4096, 512)
+    assert (d["gemm_bm"], d["gemm_bn"], d["split_k"], d["gemm_waves"]) == (256, 256, 4, 4)
+    assert pr.pr_select(2048, 4096, 4096, 256)["gemm_waves"] == 8  # another chunk size: model
+    conv = pr.pr_select(2048, 4096, 4096, -1)        # conventional: the model
+    assert conv["gemm_waves"] == 8
+    assert pr.pr_select(2048, 4096, 8192, 512)["gemm_waves"] == 8   # another group
+    monkeypatch.setenv("PR_FORCE_WAVES", "8")
+    assert pr.pr_select(2048, 4096, 4096, 512)["gemm_waves"] == 8
+    monkeypatch.delenv("PR_FORCE_WAVES")
+    pr.pr_clear_tuning()
+    assert pr.pr_select(2048, 4096, 4096, 512) == base
+    for args, code in (((4096, 4096, 512, 64, 64, 1, 8), pr.PR_ERR_INVALID_ARG),
+                       ((4096, 4096, 512, 256, 256, 3, 8), pr.PR_ERR_INVALID_ARG),
+                       ((4096, 4096, 512, 256, 256, 1, 6), pr.PR_ERR_INVALID_ARG),
+                       ((4096, 4096, 5000, 256, 256, 1, 8), pr.PR_ERR_MICROCHUNK),
+                       ((4000, 4096, 512, 256, 256, 1, 8), pr.PR_ERR_SHAPE)):
+        with pytest.raises(pr.PRError) as e:
+            pr.pr_set_chunk_config(*args)
+        assert e.value.code == code, args
 
 
 def test_auto_untuned_and_overrides(monkeypatch):
