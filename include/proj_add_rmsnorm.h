@@ -253,7 +253,8 @@ typedef struct {
  * on synthetic device data.  Before that, for each group and chunk size, the projection
  * configurations the time model ranks within 1.5x of its best (up to 6) are timed in the
  * pipeline at T = min(max T_grid, 4 x chunk size) and the fastest that passes the same check is
- * installed with pr_set_chunk_config (skipped when a PR_FORCE_* override is set).  Installs the
+ * installed with pr_set_chunk_config, the model's first choice standing unless beaten by more
+ * than 3% (skipped when a PR_FORCE_* override is set).  Installs the
  * result with pr_set_tuning for every group.  timings_out (optional): [ngroups][nT][2 + nmc] seconds
  * (conventional, best fused, then each candidate; <= 0 for skipped or rejected candidates).
  * With PR_MICROCHUNK_TOKENS and PR_THRESHOLD_TOKENS both set, nothing is timed or checked and

@@ -41,18 +41,23 @@ def stats_summary(path: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-def _counter(path: str, counter: str) -> Dict[str, List[float]]:
+def _counter(path: str, counter: str, grid: int = 0) -> Dict[str, List[float]]:
+    """Counter values per kernel; with grid > 0, only dispatches of that grid size (threads) for
+    kernels other than the calibration copies (one kernel can serve several launch shapes)."""
     out: Dict[str, List[float]] = {}
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
-        out.setdefault(short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        name = short_name(r["Kernel_Name"])
+        if grid and not name.startswith("__amd_rocclr") and int(r["Grid_Size"]) != grid:
+            continue
+        out.setdefault(name, []).append(float(r["Counter_Value"]))
     return out
 
 
-def traffic(fetch_csv: str, write_csv: str, kernel: str) -> dict:
-    fetch = _counter(fetch_csv, "FETCH_SIZE")
-    write = _counter(write_csv, "WRITE_SIZE")
+def traffic(fetch_csv: str, write_csv: str, kernel: str, grid: int = 0) -> dict:
+    fetch = _counter(fetch_csv, "FETCH_SIZE", grid)
+    write = _counter(write_csv, "WRITE_SIZE", grid)
     big = lambda vals: [v for v in vals if v * 1024 > COPY_BYTES / 4]
     copy_f = big(fetch.get("__amd_rocclr_copyBuffer", []))
     copy_w = big(write.get("__amd_rocclr_copyBuffer", []))
@@ -66,7 +71,7 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str) -> dict:
         raise SystemExit(f"kernel {kernel!r} not found in the counter files")
     fetched = statistics.mean(kf) * 1024 * f_factor
     written = statistics.mean(kw) * 1024 * w_factor
-    return {"kernel": kernel, "dispatches": len(kf),
+    return {"kernel": kernel, "grid_size": grid, "dispatches": len(kf),
             "fetch_size_kib_mean": statistics.mean(kf), "write_size_kib_mean": statistics.mean(kw),
             "copy_fetch_size_kib": statistics.median(copy_f),
             "copy_write_size_kib": statistics.median(copy_w),
@@ -95,12 +100,14 @@ def main() -> None:
     t.add_argument("--command", required=True)
     t.add_argument("--config", required=True, help="workload label, e.g. o_proj:mc=512")
     t.add_argument("--source", required=True, help="kernel source the counters were taken on")
+    t.add_argument("--grid", type=int, default=0,
+                   help="only dispatches of this grid size (threads), e.g. one chunk's launch")
     a = ap.parse_args()
     if a.cmd == "stats":
         with open(a.out, "w") as f:
             f.write(stats_summary(a.csv, a.command))
     else:
-        res = traffic(a.fetch_csv, a.write_csv, a.kernel)
+        res = traffic(a.fetch_csv, a.write_csv, a.kernel, a.grid)
         res["commands"] = a.command
         res["config"] = a.config
         res["kernel_source_sha256"] = source_digest(a.source)
