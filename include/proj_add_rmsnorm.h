@@ -250,9 +250,9 @@ typedef struct {
  * if it fails: output relative L2 <= 5e-3 and per element |delta| <= 2e-2 + one bf16 ulp (both
  * outputs are rounded); residual per element within half a bf16 ulp of y plus fp32 rounding
  * (the paths differ exactly by the bf16 rounding of y).  Timings are medians of `reps` calls
- * on synthetic device data.  Before that, for each group and chunk size, the projection
- * configurations the time model ranks within 1.5x of its best (up to 6) are timed in the
- * pipeline at T = min(max T_grid, 4 x chunk size) and the fastest that passes the same check is
+ * on synthetic device data.  Before that, for each group and chunk size, the tile/split choices
+ * the time model ranks within 1.5x of its best (up to 4), each with 8 and 4 waves, are timed in
+ * the pipeline at T = min(max T_grid, 4 x chunk size) and the fastest that passes the same check is
  * installed with pr_set_chunk_config, the model's first choice standing unless beaten by more
  * than 3% (skipped when a PR_FORCE_* override is set).  Installs the
  * result with pr_set_tuning for every group.  timings_out (optional): [ngroups][nT][2 + nmc] seconds

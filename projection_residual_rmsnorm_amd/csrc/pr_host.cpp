@@ -138,15 +138,16 @@ constexpr double kWriteBW = 6.0e12;
 constexpr double kReadBW = 5.5e12;
 }  // namespace
 
-double model_gemm_time(int M, int N, int K, int c, int split, bool fp32_out) {
+double model_gemm_time(int M, int N, int K, int c, int split, bool fp32_out, int cus) {
   const int bm = kTileBM[c], bn = kTileBN[c];
   const long long units = (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn) * split;
-  const long long full = units / kNumCUs, rem = units % kNumCUs;
+  const long long full = units / cus, rem = units % cus;
   const double tile_flops = 2.0 * bm * bn * ((double)K / split + kFixedK);
+  const double chip = kChipRate * cus / kNumCUs;  // the share of the chip's rate
   auto round_t = [&](long long active) {
-    return tile_flops / std::min(kTileRmax[c], kTileEff[c] * kChipRate / (double)active);
+    return tile_flops / std::min(kTileRmax[c], kTileEff[c] * chip / (double)active);
   };
-  double t = (double)full * round_t(kNumCUs) + (rem > 0 ? round_t(rem) : 0.0);
+  double t = (double)full * round_t(cus) + (rem > 0 ? round_t(rem) : 0.0);
   const bool planes = fp32_out || split > 1;
   const double y_bytes = (planes ? 4.0 * split : 2.0) * M * (double)N;
   return t + y_bytes / kWriteBW + y_bytes / kReadBW;
@@ -159,7 +160,7 @@ GemmCfg choose_gemm(int M, int N, int K, bool fp32_out) {
   for (int c = 0; c < kNumTileCfgs; ++c) {
     for (int split = 1; split <= 16; split *= 2) {
       if (K % (64 * split) != 0) break;
-      const double t = model_gemm_time(M, N, K, c, split, fp32_out);
+      const double t = model_gemm_time(M, N, K, c, split, fp32_out, kNumCUs);
       if (t < best_t * 0.999) {
         best_t = t;
         best.bm = kTileBM[c];

@@ -31,8 +31,9 @@ constexpr int kTileBN[kNumTileCfgs] = {256, 128, 128};
 // projection result is kept in fp32 (the pipeline's slot), false when it is emitted in bf16.
 GemmCfg choose_gemm(int M, int N, int K, bool fp32_out);
 // Modelled time (seconds) of the projection of M x N x K with tile configuration c (index into
-// kTileBM/kTileBN) and K split, including the add/norm's read of its output.
-double model_gemm_time(int M, int N, int K, int c, int split, bool fp32_out);
+// kTileBM/kTileBN) and K split, including the add/norm's read of its output, when it has `cus`
+// CUs and that share of the chip's power to itself (kNumCUs: alone on the GPU).
+double model_gemm_time(int M, int N, int K, int c, int split, bool fp32_out, int cus);
 
 // Error reporting: stores the message for pr_last_error() and returns `code`.
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
