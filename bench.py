@@ -1,12 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of the fused projection -> residual add -> RMSNorm call on one MI355X.
 
-A step is one proj_add_rmsnorm call over one batch of T tokens of a workload (all steps of
-the path: the projection of every microchunk, the slot hand-off between the two streams, the
-residual add and the RMSNorm), with inputs already resident in HBM.  The default workload is
-the Llama-3-8B-shaped o_proj prefill (T=2048, K=H=4096, bf16, standard RMSNorm), the pipeline
-run at each of its chunk sizes {256, 512}; the best one is the headline.  The conventional
-path is timed beside it.  Prints one JSON line.
+A step is one fused call over one batch of T tokens of a workload (all steps of the path:
+the projection of every row block, the hand-off of its result, the residual add and the
+RMSNorm), with inputs already resident in HBM.  The default workload is the Llama-3-8B-shaped
+o_proj prefill (T=2048, K=H=4096, bf16, standard RMSNorm).  The fused forms are the
+microchunk pipeline at each of the workload's chunk sizes ({256, 512} for o_proj) and the
+single launch; the fastest is the headline.  The conventional path is timed beside them.
+Prints one JSON line.
 
     python bench.py [--steps 50] [--warmup 10] [--workload o_proj] [--no-cpu-baseline]
 """
@@ -62,10 +63,12 @@ def time_steps(call, steps: int, warmup: int, torch):
     return time.perf_counter() - t0
 
 
-def traffic_label(workload: str, mc: int, chunk_cfgs: dict) -> str:
-    """Label of a traffic measurement: workload, chunk size and the chunk projection
-    configuration it ran with (counters taken under another configuration do not apply)."""
-    return f"{workload}:mc={mc}:{chunk_cfgs.get(str(mc), 'model')}"
+def traffic_label(workload: str, mc, chunk_cfgs: dict) -> str:
+    """Label of a traffic measurement: workload, fused form (chunk size or "single") and the
+    projection configuration it ran with (counters taken under another configuration do not
+    apply)."""
+    key = "mc=single" if mc == "single" else f"mc={mc}"
+    return f"{workload}:{key}:{chunk_cfgs.get(str(mc), 'model')}"
 
 
 def cpu_baseline(d, seconds: float) -> dict:
@@ -107,7 +110,8 @@ def tune_sweep(pr, torch, args) -> int:
         rows.append({"T": T, "conventional_ms": t[0] * 1e3,
                      "best_fused_ms": t[1] * 1e3 if t[1] > 0 else None,
                      "fused_ms": {str(m): (t[2 + j] * 1e3 if t[2 + j] > 0 else None)
-                                  for j, m in enumerate(mcs)}})
+                                  for j, m in enumerate(mcs)},
+                     "single_launch_ms": t[2 + len(mcs)] * 1e3 if t[2 + len(mcs)] > 0 else None})
     thr = rep["threshold_tokens"]
     print(json.dumps({"tune_sweep": {"K": 8192, "H": 8192, "T_grid": grid, "microchunks": mcs,
                                      "rows": rows, "n_checked": rep["n_checked"],
@@ -152,6 +156,9 @@ def main() -> int:
     flops = 2.0 * T * K * H
 
     def fused(mc):
+        if mc == "single":
+            return lambda: pr.proj_add_rmsnorm_single_launch(x, Wp, r, w, d["eps"], T, K, H,
+                                                             wl.norm_kind, out)
         return lambda: pr.proj_add_rmsnorm(x, Wp, r, w, d["eps"], T, K, H, mc, wl.norm_kind, out)
 
     def conventional():
@@ -165,26 +172,29 @@ def main() -> int:
     if not args.no_tune:
         t_tune = time.perf_counter()
         rep = pr.pr_tune([K], [H], wl.norm_kind, [T], mcs, reps=5, stream=stream)
-        for m in mcs:
+        for m in mcs + [pr.PR_SINGLE_LAUNCH]:
             c = pr.pr_select(T, K, H, m)
-            chunk_cfgs[str(m)] = (f"{c['gemm_bm']}x{c['gemm_bn']} split {c['split_k']} "
-                                  f"{c['gemm_waves']} waves")
+            chunk_cfgs["single" if m == pr.PR_SINGLE_LAUNCH else str(m)] = (
+                f"{c['gemm_bm']}x{c['gemm_bn']} split {c['split_k']} {c['gemm_waves']} waves")
         log(f"tuned in {time.perf_counter() - t_tune:.1f} s: {chunk_cfgs} "
             f"(checked {rep['n_checked']}, rejected {rep['n_rejected']})")
     per_mc = {}
-    for mc in mcs:
+    forms = mcs + (["single"] if not args.microchunk else [])
+    for mc in forms:
         el = time_steps(fused(mc), args.steps, args.warmup, torch)
         per_mc[mc] = {"tokens_per_s": T * args.steps / el, "ms_per_step": el * 1e3 / args.steps,
                       "tflops": flops * args.steps / el / 1e12}
-        log(f"fused mc={mc}: {per_mc[mc]['ms_per_step']:.4f} ms/step "
-            f"{per_mc[mc]['tflops']:.1f} TFLOP/s")
+        log(f"fused {'single launch' if mc == 'single' else f'mc={mc}'}: "
+            f"{per_mc[mc]['ms_per_step']:.4f} ms/step {per_mc[mc]['tflops']:.1f} TFLOP/s")
+    if "single" in per_mc and pr.pr_device_status(stream) != 0:
+        raise SystemExit("single-launch status bits set: a row wait gave up")
     best = min(per_mc, key=lambda m: per_mc[m]["ms_per_step"])
     el_c = time_steps(conventional, args.steps, args.warmup, torch)
     conv = {"tokens_per_s": T * args.steps / el_c, "ms_per_step": el_c * 1e3 / args.steps,
             "tflops": flops * args.steps / el_c / 1e12}
     log(f"conventional: {conv['ms_per_step']:.4f} ms/step {conv['tflops']:.1f} TFLOP/s")
 
-    # Headline: the best chunk size, timed as its own region (barrier-free single process:
+    # Headline: the fastest fused form, timed as its own region (barrier-free single process:
     # synchronize on both sides).
     mc = best
     el = time_steps(fused(mc), args.steps, args.warmup, torch)
@@ -204,14 +214,22 @@ def main() -> int:
     prof = pr.pr_profile_read()
     pr.pr_profile_enable(False)
 
+    single = mc == "single"
+    if single and pr.pr_device_status(stream) != 0:
+        raise SystemExit("single-launch status bits set: a row wait gave up")
     g_launch_s = prof["gemm_ms"] / max(prof["gemm_launches"], 1) / 1e3
-    a_launch_s = prof["addnorm_ms"] / max(prof["addnorm_launches"], 1) / 1e3
     gemm_flops_per_launch = flops * args.steps / max(prof["gemm_launches"], 1)
-    addnorm_elems_per_launch = T * H * args.steps / max(prof["addnorm_launches"], 1)
-    split = pr.pr_select(T, K, H, mc)["split_k"]
-    addnorm_bytes_per_elem = 4 * split + 4 + 4 + 2   # slot planes + r read + r write + out
     gemm_tflops = gemm_flops_per_launch / g_launch_s / 1e12
-    addnorm_gbs = addnorm_elems_per_launch * addnorm_bytes_per_elem / a_launch_s / 1e9
+    split = pr.pr_select(T, K, H, pr.PR_SINGLE_LAUNCH if single else mc)["split_k"]
+    if single:
+        # One kernel per call: its HBM bytes beyond the projection are the residual read and
+        # write and the output write (10 B per element).
+        a_launch_s, addnorm_bytes_per_elem, addnorm_gbs = None, 10, None
+    else:
+        a_launch_s = prof["addnorm_ms"] / max(prof["addnorm_launches"], 1) / 1e3
+        addnorm_elems_per_launch = T * H * args.steps / max(prof["addnorm_launches"], 1)
+        addnorm_bytes_per_elem = 4 * split + 4 + 4 + 2   # slot planes + r read + r write + out
+        addnorm_gbs = addnorm_elems_per_launch * addnorm_bytes_per_elem / a_launch_s / 1e9
     # Measured HBM bytes per projection launch, from the committed counter runs; null unless
     # they were taken on this exact kernel source and this workload / chunk size.
     traffic = None
@@ -223,13 +241,15 @@ def main() -> int:
         if (tr.get("kernel_source_sha256") == source_digest(src)
                 and tr.get("config") == traffic_label(wl.name, mc, chunk_cfgs)):
             traffic = tr.get("gemm_bytes_per_launch")
-    roof = {"kernel": "gemm_bf16_kernel", "bound": "mfma", "achieved": gemm_tflops,
+    roof = {"kernel": "gemm_add_rmsnorm_kernel" if single else "gemm_bf16_kernel",
+            "bound": "mfma", "achieved": gemm_tflops,
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,
             "traffic": traffic, "avg_launch_us": g_launch_s * 1e6,
             "launches": prof["gemm_launches"], "flops_per_launch": gemm_flops_per_launch,
             "timed_pass_ms_per_step": el_prof * 1e3 / args.steps}
     kernels = {"gemm_avg_us": g_launch_s * 1e6, "gemm_tflops": gemm_tflops,
-               "addnorm_avg_us": a_launch_s * 1e6, "addnorm_gbs": addnorm_gbs,
+               "addnorm_avg_us": None if a_launch_s is None else a_launch_s * 1e6,
+               "addnorm_gbs": addnorm_gbs,
                "addnorm_bytes_per_elem": addnorm_bytes_per_elem, "split_k": split}
     result = {
         "metric": "fused proj+add+RMSNorm tokens/s; TFLOP/s as % bf16 MFMA peak (1 GPU)",
@@ -237,8 +257,10 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{wl.name} prefill", "T": T, "K": K, "H": H,
-                   "microchunk": mc, "norm": "gemma" if wl.norm_kind else "standard",
-                   "path": "fused microchunk pipeline", "parallelism": "none (1 GPU)"},
+                   "microchunk": None if single else mc,
+                   "norm": "gemma" if wl.norm_kind else "standard",
+                   "path": "fused single launch" if single else "fused microchunk pipeline",
+                   "parallelism": "none (1 GPU)"},
         "tflops": tflops, "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "roofline": roof, "kernels": kernels,
         "per_microchunk": {str(k): v for k, v in per_mc.items()},

@@ -66,6 +66,10 @@ extern "C" {
 /* execution paths */
 #define PR_PATH_CONVENTIONAL 0
 #define PR_PATH_FUSED 1
+#define PR_PATH_SINGLE 2 /* projection, add and norm in one launch */
+
+/* Chunk value that stands for the single-launch fused path (pr_select, pr_set_tuning). */
+#define PR_SINGLE_LAUNCH (-2)
 
 /*
  * Weight preparation, once after the weights load ("TPSP Design" section 3, Profiling and
@@ -128,6 +132,37 @@ int proj_add_rmsnorm_unfused(const uint16_t* x, const uint16_t* W, float* residu
                              const float* norm_w, float eps, int T, int K, int H, int norm_kind,
                              uint16_t* out, void* stream);
 
+/*
+ * Single-launch fused path: the projection, residual add and RMSNorm of all T tokens in one
+ * kernel launch.  It is the pipeline of proj_add_rmsnorm with its hand-offs moved into the
+ * kernel ("TPSP Design" section 3, Microchunk pipeline: reusable slots guarded by readiness
+ * and completion events): a chunk is one tile row of tokens, its slot is the tile's
+ * accumulators, and its events are a per-tile-row completion counter in device memory.  Each
+ * tile adds the residual to its fp32 projection result (the fused semantics: y is not
+ * rounded), publishes per-token partial sums of squares, waits until every tile of its row has
+ * published and then writes its part of the output.  The launch is cooperative (all its
+ * workgroups are resident at once), so every wait ends; a wait that exceeds its poll limit
+ * gives up, leaves its tile's output unwritten and sets a status bit read by
+ * pr_device_status.
+ *
+ * Same arguments and ownership as proj_add_rmsnorm_unfused.  Requires H = tile columns * n
+ * with n <= 64 for one of the tiles the library instantiates (256 or 128 columns), else
+ * PR_ERR_SHAPE.  The result agrees with the fused pipeline within rounding (the sum of squares
+ * is taken in another order).  Uses a device workspace of T * ceil4(H / 128) floats and
+ * 2 + T / 128 counters, shared by all calls on the device.
+ */
+int proj_add_rmsnorm_single_launch(const uint16_t* x, const uint16_t* W, float* residual_inout,
+                                   const float* norm_w, float eps, int T, int K, int H,
+                                   int norm_kind, uint16_t* out, void* stream);
+
+/*
+ * Status bits that single-launch calls on the current device collected since the last read:
+ * bit 0 = a tile's wait for its row gave up (its output rows are not written).  Waits for the
+ * calls enqueued on `stream` to finish, stores the bits in *status (0 when none) and clears
+ * them.  Errors: PR_ERR_INVALID_ARG (status NULL), PR_ERR_HIP.
+ */
+int pr_device_status(void* stream, unsigned* status);
+
 /* Device pointer of the borrowed output of the last call made with out == NULL on the current
  * device, or NULL if there was none.  Valid until the next call on that device. */
 const uint16_t* pr_workspace_output(void);
@@ -143,7 +178,7 @@ int pr_validate(const void* x, const void* W, const void* residual_inout, const 
 
 /* Execution decision for one call. */
 typedef struct {
-  int path;       /* PR_PATH_FUSED or PR_PATH_CONVENTIONAL                          */
+  int path;       /* PR_PATH_FUSED, PR_PATH_CONVENTIONAL or PR_PATH_SINGLE          */
   int microchunk; /* chunk tokens (fused), else T                                   */
   int n_chunks;   /* ceil(T / microchunk) (fused), else 1                           */
   int last_valid; /* valid rows of the last chunk                                   */
@@ -161,9 +196,11 @@ typedef struct {
 #define PR_REASON_UNTUNED 3           /* auto: no tuning for this shape               */
 #define PR_REASON_INCONCLUSIVE 4      /* auto: tuning found no profitable range       */
 #define PR_REASON_UNFUSED_CALL 5      /* proj_add_rmsnorm_unfused                      */
+#define PR_REASON_SINGLE_CALL 6       /* proj_add_rmsnorm_single_launch                */
 
 /* Decision proj_add_rmsnorm would take (microchunk as in proj_add_rmsnorm; -1 = the unfused
- * entry point).  Returns PR_OK or the error that call would return. */
+ * entry point, PR_SINGLE_LAUNCH = the single-launch entry point).  Returns PR_OK or the error
+ * that call would return. */
 int pr_select(int T, int K, int H, int microchunk, pr_decision* d);
 
 /* Dry-run schedule of the microchunk pipeline: the ordered list of operations the library
@@ -216,8 +253,9 @@ int pr_threshold_from_timings(int ngroups, int nT, const int* T_grid, const doub
                               const double* t_fused, const double* spread, int* threshold);
 
 /* Install a tuning result for the shape group (K, H): fused iff T >= threshold_tokens with
- * chunk size mc_for_T[i] for T in [T_grid[i], T_grid[i+1]); calls with T > max_tokens fail
- * with PR_ERR_UNSUPPORTED.  threshold_tokens = INT32_MAX marks an inconclusive tuning. */
+ * chunk size mc_for_T[i] for T in [T_grid[i], T_grid[i+1]) (PR_SINGLE_LAUNCH: the
+ * single-launch path); calls with T > max_tokens fail with PR_ERR_UNSUPPORTED.
+ * threshold_tokens = INT32_MAX marks an inconclusive tuning. */
 int pr_set_tuning(int K, int H, int threshold_tokens, int max_tokens, const int* T_grid,
                   const int* mc_for_T, int nT);
 
@@ -245,20 +283,25 @@ typedef struct {
 
 /*
  * Autotune on the current device: for each group g (shape K[g] x H[g]) and each T in T_grid,
- * time the conventional path and the pipeline for every chunk size in mc_cand (<= min(T, 4096));
- * each candidate's result is first checked against the conventional path's result and dropped
- * if it fails: output relative L2 <= 5e-3 and per element |delta| <= 2e-2 + one bf16 ulp (both
- * outputs are rounded); residual per element within half a bf16 ulp of y plus fp32 rounding
- * (the paths differ exactly by the bf16 rounding of y).  Timings are medians of `reps` calls
- * on synthetic device data.  Before that, for each group and chunk size, the tile/split choices
- * the time model ranks within 1.5x of its best (up to 4), each with 8 and 4 waves, are timed in
- * the pipeline at T = min(max T_grid, 4 x chunk size) and the fastest that passes the same check is
- * installed with pr_set_chunk_config, the model's first choice standing unless beaten by more
- * than 3% (skipped when a PR_FORCE_* override is set).  Installs the
- * result with pr_set_tuning for every group.  timings_out (optional): [ngroups][nT][2 + nmc] seconds
- * (conventional, best fused, then each candidate; <= 0 for skipped or rejected candidates).
- * With PR_MICROCHUNK_TOKENS and PR_THRESHOLD_TOKENS both set, nothing is timed or checked and
- * the override is installed.
+ * time the conventional path, the pipeline for every chunk size in mc_cand (<= min(T, 4096))
+ * and the single-launch path (when H allows it); the fused candidates are the pipeline chunk
+ * sizes and the single launch, and the best of them is the fused time at T.  Each candidate's
+ * result is first checked against the conventional path's result and dropped if it fails:
+ * output relative L2 <= 5e-3 and per element |delta| <= 2e-2 + one bf16 ulp (both outputs are
+ * rounded); residual per element within half a bf16 ulp of y plus fp32 rounding (the paths
+ * differ exactly by the bf16 rounding of y).  Timings are medians of `reps` calls on synthetic
+ * device data.  Before that, for each group and chunk size, the projection configurations of
+ * the chunks are chosen: the time model's three best tile/split choices for a chunk alone on
+ * the GPU and its three best with half the GPU (the other stream's chunk runs alongside), each
+ * with 8 and 4 waves, are checked and timed round-robin in the pipeline at
+ * T = min(max T_grid, 4 x chunk size), and the fastest that passes is installed with
+ * pr_set_chunk_config, the model's first choice standing unless beaten by more than 3%
+ * (skipped when a PR_FORCE_* override is set).  Installs the result with pr_set_tuning for
+ * every group (chunk value PR_SINGLE_LAUNCH where the single launch is the fastest fused
+ * candidate).  timings_out (optional): [ngroups][nT][3 + nmc] seconds: conventional, best
+ * fused, each chunk size in mc_cand order, then the single launch; <= 0 for skipped or
+ * rejected candidates.  With PR_MICROCHUNK_TOKENS and PR_THRESHOLD_TOKENS both set, nothing is
+ * timed or checked and the override is installed.
  */
 int pr_tune(const int* K, const int* H, int ngroups, int norm_kind, const int* T_grid, int nT,
             const int* mc_cand, int nmc, int reps, pr_tune_report* report, double* timings_out,

@@ -30,13 +30,16 @@ PR_WEIGHT_IN_OUT = 1
 PR_MAX_MICROCHUNK = 4096
 PR_PATH_CONVENTIONAL = 0
 PR_PATH_FUSED = 1
+PR_PATH_SINGLE = 2
+PR_SELECT_UNFUSED = -1  # pr_select: the decision of proj_add_rmsnorm_unfused
+PR_SINGLE_LAUNCH = -2   # chunk value of the single-launch path (pr_select, pr_set_tuning)
 PR_NUM_SLOTS = 3
 INT32_MAX = 2**31 - 1
 
 OP_NAMES = ["RECORD_ENTRY", "WAIT_ENTRY", "WAIT_DONE", "GEMM", "ADDNORM", "RECORD_DONE", "JOIN",
             "WAIT_PREV"]
 REASON_NAMES = ["explicit", "above_threshold", "below_threshold", "untuned", "inconclusive",
-                "unfused_call"]
+                "unfused_call", "single_call"]
 
 # C signatures of every exported entry point (the header's declarations).
 _c = ctypes
@@ -69,6 +72,8 @@ SIGNATURES = {
     "pr_prepare_weight": (_i, [_vp, _i, _vp, _i, _i, _vp]),
     "proj_add_rmsnorm": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _i, _vp, _vp]),
     "proj_add_rmsnorm_unfused": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp, _vp]),
+    "proj_add_rmsnorm_single_launch": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp, _vp]),
+    "pr_device_status": (_i, [_vp, _c.POINTER(_c.c_uint)]),
     "pr_workspace_output": (_vp, []),
     "pr_validate": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _i, _vp]),
     "pr_select": (_i, [_i, _i, _i, _i, _c.POINTER(pr_decision)]),
@@ -183,6 +188,21 @@ def proj_add_rmsnorm_unfused(x, W, residual_inout, norm_w, eps: float, T: int, K
                                            _stream(stream, x, residual_inout)))
 
 
+def proj_add_rmsnorm_single_launch(x, W, residual_inout, norm_w, eps: float, T: int, K: int,
+                                   H: int, norm_kind: int = PR_NORM_STANDARD, out=None,
+                                   stream=None) -> None:
+    px, pw, pr_, pn, po = _call_ptrs(x, W, residual_inout, norm_w, out, T, K, H)
+    _check(_lib().proj_add_rmsnorm_single_launch(px, pw, pr_, pn, eps, T, K, H, norm_kind, po,
+                                                 _stream(stream, x, residual_inout)))
+
+
+def pr_device_status(stream=None) -> int:
+    """Status bits of single-launch calls since the last read (waits for `stream`)."""
+    v = ctypes.c_uint(0)
+    _check(_lib().pr_device_status(_stream(stream), ctypes.byref(v)))
+    return v.value
+
+
 def pr_workspace_output() -> Optional[int]:
     return _lib().pr_workspace_output()
 
@@ -239,13 +259,13 @@ def pr_tune(Ks: Sequence[int], Hs: Sequence[int], norm_kind: int, T_grid: Sequen
             mc_cand: Sequence[int], reps: int = 10, stream=None) -> dict:
     ng, nT, nmc = len(Ks), len(T_grid), len(mc_cand)
     rep = pr_tune_report()
-    timings = (ctypes.c_double * (ng * nT * (2 + nmc)))()
+    nc = 3 + nmc  # conventional, best fused, each chunk size, single launch
+    timings = (ctypes.c_double * (ng * nT * nc))()
     _check(_lib().pr_tune((ctypes.c_int * ng)(*Ks), (ctypes.c_int * ng)(*Hs), ng, norm_kind,
                           (ctypes.c_int * nT)(*T_grid), nT, (ctypes.c_int * nmc)(*mc_cand), nmc,
                           reps, ctypes.byref(rep), timings, _stream(stream)))
     t = list(timings)
-    table = [[t[(g * nT + i) * (2 + nmc):(g * nT + i + 1) * (2 + nmc)] for i in range(nT)]
-             for g in range(ng)]
+    table = [[t[(g * nT + i) * nc:(g * nT + i + 1) * nc] for i in range(nT)] for g in range(ng)]
     return {"threshold_tokens": rep.threshold_tokens, "max_tokens": rep.max_tokens,
             "n_checked": rep.n_checked, "n_rejected": rep.n_rejected, "timings": table}
 

@@ -172,6 +172,30 @@ GemmCfg choose_gemm(int M, int N, int K, bool fp32_out) {
   return best;
 }
 
+// Tile of the single-launch path: the modelled fastest tile whose columns divide H into at most
+// 64 tile columns (the kernel's row-partial limit); bm = 0 if there is none.  A 256 x 128 tile
+// grid that fits in one round runs with 4 waves per workgroup (measured on 2048 x 4096 x 4096:
+// 7% faster than 8 waves; with several rounds 8 waves were as fast or faster).
+GemmCfg choose_single(int M, int N, int K) {
+  GemmCfg best;
+  best.bm = best.bn = 0;
+  best.waves = 8;
+  double best_t = std::numeric_limits<double>::infinity();
+  for (int c = 0; c < kNumTileCfgs; ++c) {
+    if (N % kTileBN[c] != 0 || N / kTileBN[c] > 64) continue;
+    const double t = model_gemm_time(M, N, K, c, 1, false, kNumCUs);
+    if (t < best_t * 0.999) {
+      best_t = t;
+      best.bm = kTileBM[c];
+      best.bn = kTileBN[c];
+    }
+  }
+  if (best.bm == 256 && best.bn == 128 &&
+      (long long)((M + 255) / 256) * (N / 128) <= kNumCUs)
+    best.waves = 4;
+  return best;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Per-call decision.
 // ---------------------------------------------------------------------------------------------
@@ -180,7 +204,10 @@ int decide(int T, int K, int H, int microchunk, pr_decision* d) {
   int path = PR_PATH_CONVENTIONAL;
   int mc = 0;
   int reason = PR_REASON_UNFUSED_CALL;
-  if (microchunk > 0) {
+  if (microchunk == PR_SINGLE_LAUNCH) {
+    path = PR_PATH_SINGLE;
+    reason = PR_REASON_SINGLE_CALL;
+  } else if (microchunk > 0) {
     path = PR_PATH_FUSED;
     mc = microchunk;
     reason = PR_REASON_EXPLICIT;
@@ -232,6 +259,7 @@ int decide(int T, int K, int H, int microchunk, pr_decision* d) {
             for (size_t i = 0; i < tu.T_grid.size(); ++i)
               if (tu.T_grid[i] <= T) idx = (int)i;
             mc = tu.mc_for_T.empty() ? std::min(T, PR_MAX_MICROCHUNK) : tu.mc_for_T[idx];
+            if (mc == PR_SINGLE_LAUNCH) path = PR_PATH_SINGLE;
           }
         } else {
           reason = PR_REASON_BELOW_THRESHOLD;
@@ -257,6 +285,14 @@ int decide(int T, int K, int H, int microchunk, pr_decision* d) {
       }
     }
     if (!tuned) g = choose_gemm(eff, H, K, true);
+  } else if (path == PR_PATH_SINGLE) {
+    d->microchunk = T;
+    d->n_chunks = T > 0 ? 1 : 0;
+    d->last_valid = T;
+    g = choose_single(std::max(T, 1), H, K);
+    if (g.bm == 0)
+      return fail(PR_ERR_SHAPE, "single launch: H=%d is not a multiple of 128 with at most 64 "
+                  "tile columns", H);
   } else {
     d->microchunk = T;
     d->n_chunks = T > 0 ? 1 : 0;
@@ -359,7 +395,7 @@ int pr_validate(const void* x, const void* W, const void* residual_inout, const 
 int pr_select(int T, int K, int H, int microchunk, pr_decision* d) {
   if (d == nullptr) return fail(PR_ERR_INVALID_ARG, "null decision");
   if (T < 0 || K <= 0 || H <= 0) return fail(PR_ERR_INVALID_ARG, "bad sizes");
-  if (microchunk < -1 || microchunk > PR_MAX_MICROCHUNK)
+  if (microchunk < PR_SINGLE_LAUNCH || microchunk > PR_MAX_MICROCHUNK)
     return fail(PR_ERR_MICROCHUNK, "microchunk=%d out of range", microchunk);
   return decide(T, K, H, microchunk, d);
 }
@@ -454,7 +490,8 @@ int pr_set_tuning(int K, int H, int threshold_tokens, int max_tokens, const int*
   for (int i = 0; i < nT; ++i) {
     if (i > 0 && T_grid[i] <= T_grid[i - 1])
       return fail(PR_ERR_INVALID_ARG, "T_grid must ascend");
-    if (mc_for_T[i] <= 0 || mc_for_T[i] > PR_MAX_MICROCHUNK)
+    if ((mc_for_T[i] <= 0 && mc_for_T[i] != PR_SINGLE_LAUNCH) ||
+        mc_for_T[i] > PR_MAX_MICROCHUNK)
       return fail(PR_ERR_MICROCHUNK, "tuned microchunk %d out of range", mc_for_T[i]);
     tu.T_grid.push_back(T_grid[i]);
     tu.mc_for_T.push_back(mc_for_T[i]);

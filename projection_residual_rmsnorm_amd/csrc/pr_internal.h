@@ -72,6 +72,20 @@ int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_s
                        void* done_event = nullptr, void* start_timing = nullptr,
                        void* stop_timing = nullptr);
 
+// Projection, residual add and RMSNorm of M rows in one launch (tile cfg.bm x cfg.bn, split 1,
+// 8 waves; N % cfg.bn == 0, N / cfg.bn <= 64).  slots: (N / cfg.bn) * M 64-bit row-partial
+// slots; a slot holding `epoch` in its high word is taken as written by this launch, so epoch
+// must differ from every value the slots held before (start from a zeroed buffer, epoch >= 1).
+// The row reads look for read_epoch (= epoch; any other value makes every wait give up).
+// sync: 2 + ceil(M / cfg.bm) words, zero before the launch and zero again after it, except
+// word 0, which collects status bits (bit 0: a wait gave up after spin_limit polls).
+int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
+                            uint16_t* out, unsigned long long* slots, unsigned* sync, int M,
+                            int N, int K, const GemmCfg& cfg, float eps, int gemma,
+                            unsigned epoch, unsigned read_epoch, unsigned spin_limit,
+                            void* stream, void* start_timing = nullptr,
+                            void* stop_timing = nullptr);
+
 int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,
                           void* stream);
 

@@ -97,12 +97,40 @@ __device__ __forceinline__ char* ring_buffer() {
   return buf;
 }
 
+// Tile order.  Workgroups are dealt round-robin to the 8 XCDs (linear id % 8); each XCD gets a
+// contiguous range of the logical order, and the logical order walks groups of 8 tile rows
+// column by column, so the ~32 workgroups an XCD runs at once cover an 8 x 4 patch of tiles
+// and share their x rows and weight columns in that XCD's L2.
+__device__ __forceinline__ int xcd_logical(int b, int total) {
+  const int q8 = total / kNumXCDs;
+  const int r8 = total % kNumXCDs;
+  const int xcd = b % kNumXCDs;
+  return xcd * q8 + (xcd < r8 ? xcd : r8) + b / kNumXCDs;
+}
+
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int* tm, int* tn) {
+  constexpr int GROUP_M = 8;
+  const int group = t / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int in_group = t % (GROUP_M * tiles_n);
+  *tm = first_m + in_group % gm;
+  *tn = in_group / gm;
+}
+
+template <int TM, int TN>
+struct TileAcc {
+  f32x16_t v[TM][TN];
+};
+
+// Main loop of one output tile: the product of A[m0 .. m0+BM)[k_begin .. k_begin + 32 nk) and
+// the weight columns [n0 .. n0+BN) over the same K range, in the 32x32 MFMA accumulator
+// layout.  Returns with each wave past its own last fragment read: callers that reuse the
+// ring's LDS synchronize first.
 template <int BM, int BN, int NB, int WM, int WN>
-__global__ void __launch_bounds__(WM* WN * 64, 1)
-    gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp,
-                     float* __restrict__ Cf, uint16_t* __restrict__ Cb, int M, int N, int K,
-                     int k_split_len, long long plane_stride, int tiles_m, int tiles_n,
-                     int split) {
+__device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp, int M, int N, int K, int m0,
+    int n0, int k_begin, int nk) {
   constexpr int NW = WM * WN;  // waves per workgroup (4: one per SIMD, 8: two per SIMD)
   constexpr int WTM = BM / WM;  // wave tile rows
   constexpr int WTN = BN / WN;  // wave tile columns
@@ -139,32 +167,6 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int wm = wave / WN;
   const int wn = wave % WN;
-
-  // Tile order.  Workgroups are dealt round-robin to the 8 XCDs (linear id % 8); each XCD
-  // gets a contiguous range of the logical order, and the logical order walks groups of 8 tile
-  // rows column by column, so the ~32 workgroups an XCD runs at once cover an 8 x 4 patch of
-  // tiles and share their x rows and weight columns in that XCD's L2.
-  const int total = tiles_m * tiles_n * split;
-  const int b = blockIdx.x;
-  const int q8 = total / kNumXCDs;
-  const int r8 = total % kNumXCDs;
-  const int xcd = b % kNumXCDs;
-  const int logical = xcd * q8 + (xcd < r8 ? xcd : r8) + b / kNumXCDs;
-  const int per_split = tiles_m * tiles_n;
-  const int z = logical / per_split;
-  const int t = logical % per_split;
-  constexpr int GROUP_M = 8;
-  const int group = t / (GROUP_M * tiles_n);
-  const int first_m = group * GROUP_M;
-  const int gm = min(tiles_m - first_m, GROUP_M);
-  const int in_group = t % (GROUP_M * tiles_n);
-  const int tm = first_m + in_group % gm;
-  const int tn = in_group / gm;
-
-  const int m0 = tm * BM;
-  const int n0 = tn * BN;
-  const int k_begin = z * k_split_len;
-  const int nk = k_split_len / kBK;
 
   // Load assignment: A load i of wave w fills LDS kilobyte q = w + NW*i of the stage, rows
   // 16q .. 16q+15 (lane l: tile row 16q + l/4, slot l%4, i.e. k-group (l%4) ^ f(row)).
@@ -284,6 +286,45 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
 #pragma unroll
   for (int u = 0; u < NB - 1; ++u)
     if (u < rem) step(kt + u, smem(u), smem((u + 1) % NB), smem((u + P) % NB));
+  TileAcc<TM, TN> res;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) res.v[i][j] = acc[i][j];
+  return res;
+}
+
+template <int BM, int BN, int NB, int WM, int WN>
+__global__ void __launch_bounds__(WM* WN * 64, 1)
+    gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp,
+                     float* __restrict__ Cf, uint16_t* __restrict__ Cb, int M, int N, int K,
+                     int k_split_len, long long plane_stride, int tiles_m, int tiles_n,
+                     int split) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM;
+  constexpr int WTN = BN / WN;
+  constexpr int TM = WTM / 32;
+  constexpr int TN = WTN / 32;
+  constexpr int STAGE = (BM + BN) * kBK * 2;
+  char* const sb0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
+  char* const sb1 = ring_buffer<1, STAGE, BM, BN, NB, WM, WN>();
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+
+  const int total = tiles_m * tiles_n * split;
+  const int logical = xcd_logical(blockIdx.x, total);
+  const int per_split = tiles_m * tiles_n;
+  const int z = logical / per_split;
+  int tm, tn;
+  tile_coords(logical % per_split, tiles_m, tiles_n, &tm, &tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+
+  const TileAcc<TM, TN> tacc = tile_mainloop<BM, BN, NB, WM, WN>(
+      A, Bp, M, N, K, m0, n0, z * k_split_len, k_split_len / kBK);
+  const auto& acc = tacc.v;
 
   // Epilogue.  32x32 fp32 accumulator layout: lane l, element e holds
   // row 8*(e/4) + 4*(l/32) + e%4, column l%32.  Each wave passes its tile through its own LDS
@@ -329,6 +370,301 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
       }
       __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);  // reads done before the next slice overwrites
     }
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// Single-launch projection + residual add + RMSNorm.
+//
+// The microchunk pipeline's hand-offs ("TPSP Design" page, section 3: chunk results pass
+// through reusable slots guarded by readiness and completion events) become in-kernel ones:
+// the chunk is one tile row (BM tokens), the slot is the tile's own accumulators, and the
+// events are device-memory words.  Each workgroup
+//   1. loads its tile's residual into registers (tiles where it fits in 64 registers per lane)
+//      and runs the projection main loop of its BM x BN tile,
+//   2. forms r + y in fp32 (the fused mode's unrounded y), writes it as the updated residual
+//      and takes, per token, the sum of squares over its BN columns (lane partials in column
+//      order, reduced over the lanes of a row, then over the waves of the tile in wave order),
+//   3. publishes each token's partial in a 64-bit slot {call epoch, value} and adds one to its
+//      tile row's counter,
+//   4. waits (one lane, bounded) until the counter shows every tile of the row, reads the
+//      row's slots in tile-column order (re-reading any slot that does not yet carry this
+//      call's epoch, read_epoch, bounded) and forms 1/sqrt(sum/H + eps),
+//   5. writes the bf16 output of its tile.
+// Slots and counters are written and read with device-scope atomic stores, loads and adds, so
+// no cache-wide fence is needed: a slot's epoch says whether its value is this call's.  r + y
+// stays in registers from step 2 to step 5, so HBM traffic beyond the projection is the
+// method's minimum: read r, write r, write out.
+//
+// Rounds: round q covers tile rows [q R, q R + R) with R * tiles_n workgroups, and the grid is
+// never larger than the workgroups the GPU holds at once.  A wait only involves tiles of the
+// same round, and a tile reaches step 3 without waiting on anything, so the waits end once
+// the launch's workgroups have been placed (which needs only CU slots that other kernels
+// free by finishing).  A wait that exceeds spin_limit polls gives up (status bit 0 is set and
+// the tile writes no output), so every workgroup exits in any case.  read_epoch equals epoch;
+// a test of the give-up path passes one that no slot carries.
+// sync: [0] status bits, [1] workgroups finished, [2 ..] per tile row counters.  All are zero
+// before the launch; the last workgroup to finish sets [1 ..] back to zero.
+// slots: tiles_n columns of M 64-bit slots (slot of row t and tile column q at q * M + t, so
+// the slot accesses of a wave are contiguous).
+// --------------------------------------------------------------------------------------------
+// Sum over each group of LANES consecutive lanes (8 or 16, within one 16-lane DPP row); every
+// lane of the group gets the same value (each step adds a lane and its partner, which is
+// commutative, so the partners' results are bitwise equal).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int LANES>
+__device__ __forceinline__ float lane_group_sum(float q) {
+  static_assert(LANES == 8 || LANES == 16, "DPP row reduction over 8 or 16 lanes");
+  q += dpp_mov<0xB1>(q);   // quad_perm [1,0,3,2]: partner lane ^ 1
+  q += dpp_mov<0x4E>(q);   // quad_perm [2,3,0,1]: partner lane ^ 2
+  q += dpp_mov<0x141>(q);  // row_half_mirror: the other quad of the 8
+  if constexpr (LANES == 16) q += dpp_mov<0x140>(q);  // row_mirror: the other half-row
+  return q;
+}
+
+template <int BM, int BN, int NB, int WM, int WN>
+__global__ void __launch_bounds__(WM* WN * 64, 1)
+    gemm_add_rmsnorm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp,
+                            float* __restrict__ R, const float* __restrict__ w,
+                            uint16_t* __restrict__ out, unsigned long long* __restrict__ slots,
+                            unsigned* __restrict__ sync, int M, int N, int K, int tiles_m,
+                            int tiles_n, int rows_per_round, float eps, int gemma,
+                            unsigned epoch, unsigned read_epoch, unsigned spin_limit) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM;
+  constexpr int WTN = BN / WN;
+  constexpr int TM = WTM / 32;
+  constexpr int TN = WTN / 32;
+  constexpr int STAGE = (BM + BN) * kBK * 2;
+  static_assert(NB >= 3, "the norm epilogue uses the third ring buffer");
+  static_assert((BM * WN + BM + 1) * 4 <= STAGE, "row partials fit in one stage buffer");
+  char* const sb0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
+  char* const sb1 = ring_buffer<1, STAGE, BM, BN, NB, WM, WN>();
+  float* const sred = reinterpret_cast<float*>(ring_buffer<2, STAGE, BM, BN, NB, WM, WN>());
+  float* const sinv = sred + BM * WN;
+  int* const sflag = reinterpret_cast<int*>(sinv + BM);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const float g0 = gemma ? 1.0f : 0.0f;
+
+  constexpr int EP_LD = WTN + 4;
+  constexpr int EP_BYTES = 16 * EP_LD * 4;
+  constexpr int EP_PER_BUF = STAGE / EP_BYTES;
+  static_assert(NW <= 2 * EP_PER_BUF, "epilogue staging must fit in two stage buffers");
+  constexpr int LPR = WTN / 4;   // lanes per staged row (8 or 16: one DPP row or half-row)
+  constexpr int RPI = 64 / LPR;  // rows per staged read
+  constexpr int NR = 16 / RPI;   // staged reads per 16-row slice
+  constexpr int KEEP = TM * 2 * NR;               // float4 of r + y per lane
+  // Residual loaded before the main loop when it fits: 64 registers per lane with two waves
+  // per SIMD (256 registers each), 128 with one wave per SIMD (512).
+  constexpr bool PREFETCH = KEEP <= (NW == 4 ? 32 : 16);
+  constexpr int TPR = NW * 64 / BM;               // threads per row for the slot reads
+  static_assert(TPR >= 1 && TPR <= WN, "slot-read partials reuse the row-partial buffer");
+
+  for (int round = 0; round * rows_per_round < tiles_m; ++round) {
+    const int rows_here = min(rows_per_round, tiles_m - round * rows_per_round);
+    const int count = rows_here * tiles_n;
+    if ((int)blockIdx.x >= count) continue;  // uniform over the workgroup
+    int tm, tn;
+    tile_coords(xcd_logical(blockIdx.x, count), rows_here, tiles_n, &tm, &tn);
+    tm += round * rows_per_round;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+
+    // Lane position in the staged layout: row lrow + RPI * rr of each 16-row slice, columns
+    // rcol .. rcol+3 of the wave's WTN (lane id l).
+    auto rcol_of = [](int l) { return (l % LPR) * 4; };
+    auto row_of = [&](int l, int i, int h, int rr) {
+      return wm * WTM + i * 32 + h * 16 + rr * RPI + l / LPR;
+    };
+
+    // The residual, loaded before the main loop so that its read overlaps the MFMA work (tiles
+    // whose share fits in 64 registers per lane), else one 16-row slice ahead in the epilogue.
+    float4 keep[KEEP];
+    if constexpr (PREFETCH) {
+      const int pcol = n0 + wn * WTN + rcol_of(lane);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int rr = 0; rr < NR; ++rr) {
+            const int row = min(m0 + row_of(lane, i, h, rr), M - 1);
+            keep[(i * 2 + h) * NR + rr] =
+                *reinterpret_cast<const float4*>(R + (long long)row * N + pcol);
+          }
+    }
+
+    const TileAcc<TM, TN> tacc =
+        tile_mainloop<BM, BN, NB, WM, WN>(A, Bp, M, N, K, m0, n0, 0, K / kBK);
+    const auto& acc = tacc.v;
+    // The ring's trailing refills (direct-to-LDS loads) have landed and every wave is past its
+    // last fragment read before the stage buffers are reused below.
+    __builtin_amdgcn_s_waitcnt(PR_VMCNT(0));
+    __syncthreads();
+
+    // The epilogue's per-lane offsets are formed here, from an opaque copy of the lane id, so
+    // that they are not hoisted out of the round loop and kept live across the main loop.
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int rcol = rcol_of(el);
+    const int lrow = el / LPR;
+    const int col = n0 + wn * WTN + rcol;
+    float* ep = reinterpret_cast<float*>((wave < EP_PER_BUF ? sb0 : sb1) +
+                                         (wave % EP_PER_BUF) * EP_BYTES);
+    auto load_slice = [&](int sl) {
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) {
+        const int row = min(m0 + row_of(el, sl >> 1, sl & 1, rr), M - 1);
+        keep[sl * NR + rr] = *reinterpret_cast<const float4*>(R + (long long)row * N + col);
+      }
+    };
+    if constexpr (!PREFETCH) load_slice(0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (!PREFETCH)
+          if (i * 2 + h + 1 < TM * 2) load_slice(i * 2 + h + 1);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 8 * h; e < 8 * h + 8; ++e)
+            ep[(((e >> 2) - 2 * h) * 8 + (el >> 5) * 4 + (e & 3)) * EP_LD + j * 32 +
+               (el & 31)] = acc[i][j][e];
+        __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);
+#pragma unroll
+        for (int rr = 0; rr < NR; ++rr) {
+          const int trow = row_of(el, i, h, rr);
+          const int r_in = rr * RPI + lrow;
+          const int row = min(m0 + trow, M - 1);  // rows past M are computed, never stored
+          const float4 y = *reinterpret_cast<const float4*>(ep + r_in * EP_LD + rcol);
+          const float4 rv = keep[(i * 2 + h) * NR + rr];
+          const float4 v = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
+          if (m0 + trow < M) *reinterpret_cast<float4*>(R + (long long)row * N + col) = v;
+          keep[(i * 2 + h) * NR + rr] = v;
+          const float q = lane_group_sum<LPR>(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
+          if (el % LPR == 0) sred[trow * WN + wn] = q;
+        }
+        __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);  // reads done before the next slice
+      }
+    }
+    __syncthreads();
+    const unsigned long long tag = (unsigned long long)epoch << 32;
+    if (threadIdx.x < BM) {
+      float p = 0.0f;
+#pragma unroll
+      for (int q = 0; q < WN; ++q) p += sred[threadIdx.x * WN + q];
+      const int row = m0 + threadIdx.x;
+      if (row < M)
+        __hip_atomic_store(slots + (long long)tn * M + row, tag | __float_as_uint(p),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned* cnt = sync + 2 + tm;
+      __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned polls = 0;
+      while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                 (unsigned)tiles_n &&
+             polls++ < spin_limit)
+        __builtin_amdgcn_s_sleep(1);
+      *sflag = 1;
+    }
+    __syncthreads();
+    {
+      // The row's slots in tile-column order: TPR threads per row each add a contiguous run
+      // of ceil(tiles_n / TPR) slots (up to 16 loads in flight per batch), then the runs are
+      // added in order.
+      const int trow = threadIdx.x % BM;
+      const int part = threadIdx.x / BM;
+      const int row = m0 + trow;
+      const int per = (tiles_n + TPR - 1) / TPR;
+      const int q_begin = min(part * per, tiles_n), q_end = min(q_begin + per, tiles_n);
+      float ss = 0.0f;
+      if (row < M) {
+        const unsigned long long* ps = slots + row;  // slot q at ps[q * M]
+        unsigned polls = 0;  // one budget for the whole run
+        for (int q0 = q_begin; q0 < q_end; q0 += 16) {
+          unsigned long long sv[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            sv[u] = q0 + u < q_end ? __hip_atomic_load(ps + (long long)(q0 + u) * M,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                   : (unsigned long long)read_epoch << 32;
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            while ((sv[u] >> 32) != read_epoch) {
+              if (polls++ >= spin_limit) {
+                *sflag = 0;  // the tile gives up
+                break;
+              }
+              __builtin_amdgcn_s_sleep(1);
+              sv[u] = __hip_atomic_load(ps + (long long)(q0 + u) * M, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (q0 + u < q_end) ss += __uint_as_float((unsigned)sv[u]);
+          }
+        }
+      }
+      sred[trow * TPR + part] = ss;
+    }
+    __syncthreads();
+    if (threadIdx.x < BM && m0 + threadIdx.x < M) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int q = 0; q < TPR; ++q) ss += sred[threadIdx.x * TPR + q];
+      sinv[threadIdx.x] = 1.0f / sqrtf(ss / (float)N + eps);
+    }
+    __syncthreads();
+    if (*sflag == 0) {
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_or(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const float4 g = *reinterpret_cast<const float4*>(w + col);
+      const float gx = g.x + g0, gy = g.y + g0, gz = g.z + g0, gw = g.w + g0;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int rr = 0; rr < NR; ++rr) {
+            const int trow = row_of(el, i, h, rr);
+            const int row = m0 + trow;
+            if (row < M) {
+              const float4 v = keep[(i * 2 + h) * NR + rr];
+              const float inv = sinv[trow];
+              const uint32_t o0 = f32_to_bf16_rne(v.x * inv * gx);
+              const uint32_t o1 = f32_to_bf16_rne(v.y * inv * gy);
+              const uint32_t o2 = f32_to_bf16_rne(v.z * inv * gz);
+              const uint32_t o3 = f32_to_bf16_rne(v.w * inv * gw);
+              *reinterpret_cast<uint2*>(out + (long long)row * N + col) =
+                  make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+            }
+          }
+    }
+    __syncthreads();  // LDS is refilled by the next tile's prologue
+  }
+
+  // The last workgroup to finish returns the counters to zero for the next launch (every
+  // other workgroup is past its last counter read by then).
+  if (threadIdx.x == 0) {
+    const unsigned prev =
+        __hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sflag = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (*sflag) {
+    for (int i = threadIdx.x; i < tiles_m; i += blockDim.x)
+      __hip_atomic_store(sync + 2 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -594,6 +930,12 @@ __global__ void fill_f32_hash_kernel(float* __restrict__ p, size_t n, uint32_t s
   }
 }
 
+#define PR_TRY_K(call)            \
+  do {                            \
+    const int rc_ = (call);       \
+    if (rc_ != PR_OK) return rc_; \
+  } while (0)
+
 int check_launch(const char* what) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PR_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
@@ -667,6 +1009,48 @@ int launch_gemm_nb(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out
               BN, stages, MID, DEEP);
 }
 
+// Workgroups of one instantiation that the device holds at once (cooperative-launch limit).
+template <typename Kern>
+int resident_workgroups(Kern kern, int threads, int* out) {
+  int dev = 0, per_cu = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                     threads, 0);
+  if (e != hipSuccess) return fail(PR_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+  *out = per_cu * cus;
+  return PR_OK;
+}
+
+template <int BM, int BN, int NB, int WM, int WN>
+int launch_single_t(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
+                    uint16_t* out, unsigned long long* slots, unsigned* sync, int M, int N,
+                    int K, float eps, int gemma, unsigned epoch, unsigned read_epoch,
+                    unsigned spin_limit, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  auto kern = gemm_add_rmsnorm_kernel<BM, BN, NB, WM, WN>;
+  constexpr int threads = WM * WN * 64;
+  static int resident = 0;  // per instantiation; the library runs on one kind of device
+  if (resident == 0) PR_TRY_K(resident_workgroups(kern, threads, &resident));
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = N / BN;
+  const int rows_per_round = resident / tiles_n < tiles_m ? resident / tiles_n : tiles_m;
+  if (rows_per_round < 1)
+    return fail(PR_ERR_UNSUPPORTED, "single launch: %d tiles per row exceed the %d resident "
+                "workgroups", tiles_n, resident);
+  const unsigned grid = (unsigned)(rows_per_round * tiles_n);
+  if (t0 != nullptr) {
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, t0, t1, 0, x, Wp, r, w, out,
+                          slots, sync, M, N, K, tiles_m, tiles_n, rows_per_round, eps, gemma,
+                          epoch, read_epoch, spin_limit);
+  } else {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, Wp, r, w, out, slots, sync, M,
+                       N, K, tiles_m, tiles_n, rows_per_round, eps, gemma, epoch, read_epoch,
+                       spin_limit);
+  }
+  return check_launch("gemm_add_rmsnorm_kernel");
+}
+
 template <int NV, int WPR, bool YB>
 int launch_addnorm_t(const void* y, int y_bf16, int nplanes, long long plane_stride, int round_y,
                      float* r, const float* w, uint16_t* out, int rows, int H, float eps,
@@ -716,6 +1100,34 @@ int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, i
     return eight ? launch_gemm_nb<128, 128, 2, 4>(x, Wp, C, bf16_out, M, N, K, cfg.split, cfg.stages, plane_stride, s, done, t0, t1)
                  : launch_gemm_nb<128, 128, 2, 2>(x, Wp, C, bf16_out, M, N, K, cfg.split, cfg.stages, plane_stride, s, done, t0, t1);
   return fail(PR_ERR_INVALID_ARG, "no projection tile %dx%d", cfg.bm, cfg.bn);
+}
+
+int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
+                            uint16_t* out, unsigned long long* slots, unsigned* sync, int M,
+                            int N, int K, const GemmCfg& cfg, float eps, int gemma,
+                            unsigned epoch, unsigned read_epoch, unsigned spin_limit,
+                            void* stream, void* start_timing, void* stop_timing) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t t0 = static_cast<hipEvent_t>(start_timing);
+  hipEvent_t t1 = static_cast<hipEvent_t>(stop_timing);
+  if (M <= 0) return PR_OK;
+  if (K % (2 * kBK) != 0 || N % cfg.bn != 0 || N / cfg.bn > 64 || cfg.split != 1 ||
+      (cfg.waves != 8 && !(cfg.waves == 4 && cfg.bm == 256 && cfg.bn == 128)))
+    return fail(PR_ERR_SHAPE, "single launch: N=%d K=%d with tile %dx%d split %d, %d waves not "
+                "supported", N, K, cfg.bm, cfg.bn, cfg.split, cfg.waves);
+  if (cfg.bm == 256 && cfg.bn == 256)
+    return launch_single_t<256, 256, 5, 2, 4>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
+                                              epoch, read_epoch, spin_limit, s, t0, t1);
+  if (cfg.bm == 256 && cfg.bn == 128 && cfg.waves == 4)
+    return launch_single_t<256, 128, 4, 2, 2>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
+                                              epoch, read_epoch, spin_limit, s, t0, t1);
+  if (cfg.bm == 256 && cfg.bn == 128)
+    return launch_single_t<256, 128, 4, 4, 2>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
+                                              epoch, read_epoch, spin_limit, s, t0, t1);
+  if (cfg.bm == 128 && cfg.bn == 128)
+    return launch_single_t<128, 128, 4, 2, 4>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
+                                              epoch, read_epoch, spin_limit, s, t0, t1);
+  return fail(PR_ERR_INVALID_ARG, "single launch: no tile %dx%d", cfg.bm, cfg.bn);
 }
 
 int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_stride,

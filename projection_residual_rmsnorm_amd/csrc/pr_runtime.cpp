@@ -40,6 +40,13 @@ struct DevCtx {
   size_t conv_bytes = 0;
   uint16_t* out_ws = nullptr;  // borrowed output
   size_t out_ws_bytes = 0;
+  // single-launch path: row-partial slots (epoch-tagged), the status / completion words (zero
+  // between calls) and the epoch of the last launch
+  void* row_slots = nullptr;
+  size_t row_slots_bytes = 0;
+  unsigned* sync = nullptr;
+  size_t sync_bytes = 0;
+  unsigned epoch = 0;
   const uint16_t* last_borrowed = nullptr;
   // the previous pipeline call: its caller stream and the done slots of its last chunk on
   // each stream (-1 if none)
@@ -112,6 +119,13 @@ int env_int(const char* name) {
 bool fault_injected() {
   const char* v = std::getenv("PR_FAULT_INJECT");
   return v != nullptr && std::strcmp(v, "launch") == 0;
+}
+
+// PR_FAULT_INJECT=wait: single-launch row reads look for an epoch no slot carries, so every
+// tile's bounded wait gives up (tests of the status report).
+bool wait_fault_injected() {
+  const char* v = std::getenv("PR_FAULT_INJECT");
+  return v != nullptr && std::strcmp(v, "wait") == 0;
 }
 
 int get_ctx(DevCtx** out) {
@@ -333,6 +347,66 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
   return PR_OK;
 }
 
+// Polls of a single-launch tile's wait before it gives up (each poll is a device-scope load
+// and a short sleep, about a microsecond): about two seconds.  PR_SPIN_LIMIT overrides it
+// (tests use small values to reach the give-up path).
+unsigned spin_limit() {
+  const char* v = std::getenv("PR_SPIN_LIMIT");
+  if (v != nullptr && v[0] != '\0') return (unsigned)std::strtoul(v, nullptr, 10);
+  return 1u << 21;
+}
+
+int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const float* w,
+               float eps, int T, int K, int H, int norm_kind, uint16_t* out,
+               const pr_decision& d, hipStream_t s) {
+  GemmCfg g;
+  g.bm = d.gemm_bm;
+  g.bn = d.gemm_bn;
+  g.split = d.split_k;
+  g.waves = d.gemm_waves;
+  g.stages = d.gemm_stages;
+  if (fault_injected()) return fail(PR_ERR_HIP, "injected launch failure (PR_FAULT_INJECT)");
+  // Launches cover at most 2^30 elements of x each (32-bit offsets in the kernel), in whole
+  // tile rows; each launch is independent (rows do not interact).
+  const long long rows_per = ((1LL << 30) / K) / g.bm * g.bm;
+  if (rows_per <= 0) return fail(PR_ERR_SHAPE, "K=%d too large", K);
+  const int rows_max = (int)std::min<long long>(rows_per, T);
+  const size_t slots_need = (size_t)rows_max * (H / g.bn) * sizeof(unsigned long long);
+  if (slots_need > c->row_slots_bytes) {
+    PR_TRY(grow(&c->row_slots, &c->row_slots_bytes, slots_need));
+    PR_HIP(hipMemset(c->row_slots, 0, c->row_slots_bytes));  // holds no epoch >= 1
+    c->epoch = 0;
+  }
+  const size_t sync_need = (size_t)(2 + (rows_max + g.bm - 1) / g.bm) * sizeof(unsigned);
+  if (sync_need > c->sync_bytes) {
+    void* p = c->sync;
+    size_t have = c->sync_bytes;
+    PR_TRY(grow(&p, &have, sync_need));
+    c->sync = static_cast<unsigned*>(p);
+    c->sync_bytes = have;
+    PR_HIP(hipMemset(c->sync, 0, have));  // the kernels keep it zero from here on
+  }
+  const unsigned limit = spin_limit();
+  const int gemma = norm_kind == PR_NORM_GEMMA;
+  for (long long r0 = 0; r0 < T; r0 += rows_per) {
+    const int rows = (int)std::min<long long>(rows_per, T - r0);
+    if (++c->epoch == 0) {
+      // After 2^32 - 1 launches the slots are cleared once so that epochs stay unique.
+      PR_HIP(hipStreamSynchronize(s));
+      PR_HIP(hipMemset(c->row_slots, 0, c->row_slots_bytes));
+      c->epoch = 1;
+    }
+    const unsigned epoch = c->epoch;
+    const unsigned read_epoch = wait_fault_injected() ? epoch ^ 0x80000000u : epoch;
+    PR_TRY(timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
+      return launch_gemm_add_rmsnorm(x + r0 * K, W, r + r0 * H, w, out + r0 * H,
+                                     static_cast<unsigned long long*>(c->row_slots), c->sync, rows,
+                                     H, K, g, eps, gemma, epoch, read_epoch, limit, s, t0, t1);
+    }));
+  }
+  return PR_OK;
+}
+
 int run_call(const uint16_t* x, const uint16_t* W, float* r, const float* w, float eps, int T,
              int K, int H, int microchunk, int norm_kind, uint16_t* out, void* stream) {
   clear_error();
@@ -343,7 +417,10 @@ int run_call(const uint16_t* x, const uint16_t* W, float* r, const float* w, flo
     std::fprintf(stderr,
                  "[proj_add_rmsnorm] T=%d K=%d H=%d path=%s mc=%d chunks=%d tile=%dx%d "
                  "split=%d reason=%d\n",
-                 T, K, H, d.path == PR_PATH_FUSED ? "fused" : "conventional", d.microchunk,
+                 T, K, H,
+                 d.path == PR_PATH_FUSED ? "fused"
+                                         : (d.path == PR_PATH_SINGLE ? "single" : "conventional"),
+                 d.microchunk,
                  d.n_chunks, d.gemm_bm, d.gemm_bn, d.split_k, d.reason);
   DevCtx* c = nullptr;
   PR_TRY(get_ctx(&c));
@@ -353,6 +430,7 @@ int run_call(const uint16_t* x, const uint16_t* W, float* r, const float* w, flo
   if (rc != PR_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.path == PR_PATH_FUSED) return run_pipeline(c, x, W, r, w, eps, T, K, H, norm_kind, out, d, s);
+  if (d.path == PR_PATH_SINGLE) return run_single(c, x, W, r, w, eps, T, K, H, norm_kind, out, d, s);
   return run_conventional(c, x, W, r, w, eps, T, K, H, norm_kind, out, d, s);
 }
 
@@ -395,6 +473,28 @@ int proj_add_rmsnorm_unfused(const uint16_t* x, const uint16_t* W, float* residu
                              const float* norm_w, float eps, int T, int K, int H, int norm_kind,
                              uint16_t* out, void* stream) {
   return run_call(x, W, residual_inout, norm_w, eps, T, K, H, -1, norm_kind, out, stream);
+}
+
+int proj_add_rmsnorm_single_launch(const uint16_t* x, const uint16_t* W, float* residual_inout,
+                                   const float* norm_w, float eps, int T, int K, int H,
+                                   int norm_kind, uint16_t* out, void* stream) {
+  return run_call(x, W, residual_inout, norm_w, eps, T, K, H, PR_SINGLE_LAUNCH, norm_kind, out,
+                  stream);
+}
+
+int pr_device_status(void* stream, unsigned* status) {
+  clear_error();
+  if (status == nullptr) return fail(PR_ERR_INVALID_ARG, "null status");
+  *status = 0;
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  PR_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  if (c->sync == nullptr) return PR_OK;
+  unsigned v = 0;
+  PR_HIP(hipMemcpy(&v, c->sync, sizeof(v), hipMemcpyDeviceToHost));
+  if (v != 0) PR_HIP(hipMemset(c->sync, 0, sizeof(unsigned)));
+  *status = v;
+  return PR_OK;
 }
 
 int pr_profile_enable(int on) {

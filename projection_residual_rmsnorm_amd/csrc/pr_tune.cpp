@@ -1,8 +1,9 @@
 // Autotuner ("TPSP Design" page, section 3, Profiling and fallback): after the weights load,
 // each shape group (o_proj-like, down_proj-like) is profiled on synthetic device data; every
-// chunk-size candidate is numerically checked against the conventional path before it is
-// timed, and the token threshold compares the sum over groups of conventional and best fused
-// timings (pr_threshold_from_timings).  With both overrides set nothing is profiled.
+// fused candidate (each chunk size of the pipeline, and the single launch) is numerically
+// checked against the conventional path before it is timed, and the token threshold compares
+// the sum over groups of conventional and best fused timings (pr_threshold_from_timings).
+// With both overrides set nothing is profiled.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -161,7 +162,7 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
   };
   const bool forced_cfg = env_on("PR_FORCE_TILE") || env_on("PR_FORCE_SPLIT") ||
                           env_on("PR_FORCE_WAVES") || env_on("PR_FORCE_STAGES");
-  const int ncols = 2 + nmc;
+  const int ncols = 3 + nmc;
   std::vector<double> t_conv(ngroups * nT, -1), t_fused(ngroups * nT, -1),
       spread(ngroups * nT, 0);
   std::vector<std::vector<int>> best_mc(ngroups, std::vector<int>(nT, cands[0]));
@@ -224,10 +225,18 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
                                       (uint16_t*)out.p, s);
     };
     auto fused_call_at = [&](int T, int mc) {
+      if (mc == PR_SINGLE_LAUNCH)
+        return proj_add_rmsnorm_single_launch((const uint16_t*)x.p, (const uint16_t*)Wp.p,
+                                              (float*)r.p, (const float*)w.p, 1e-5f, T, K, H,
+                                              norm_kind, (uint16_t*)out.p, s);
       return proj_add_rmsnorm((const uint16_t*)x.p, (const uint16_t*)Wp.p, (float*)r.p,
                               (const float*)w.p, 1e-5f, T, K, H, mc, norm_kind, (uint16_t*)out.p,
                               s);
     };
+    // The single launch is a fused candidate where some tile's columns divide H.
+    pr_decision single_d;
+    const bool single_ok = pr_select(1, K, H, PR_SINGLE_LAUNCH, &single_d) == PR_OK;
+    clear_error();
 
     // Chunk projection configuration per chunk size (the CU footprint of a chunk's
     // projection): the model's best candidates, timed in the pipeline, checked like any
@@ -350,10 +359,12 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
       t_conv[g * nT + i] = sc.median;
       if (timings_out != nullptr) timings_out[(g * nT + i) * ncols + 0] = sc.median;
       double best = -1, best_spread = 0;
-      for (int j = 0; j < nmc; ++j)
+      for (int j = 0; j < nmc + 1; ++j)
         if (timings_out != nullptr) timings_out[(g * nT + i) * ncols + 2 + j] = -1;
-      for (size_t j = 0; j < cands.size(); ++j) {
-        const int mc = cands[j];
+      std::vector<int> fused_cands = cands;
+      if (single_ok && !have_mc) fused_cands.push_back(PR_SINGLE_LAUNCH);
+      for (size_t j = 0; j < fused_cands.size(); ++j) {
+        const int mc = fused_cands[j];
         if (mc > std::min(T, PR_MAX_MICROCHUNK)) continue;
         auto fused_call = [&]() { return fused_call_at(T, mc); };
         PR_TRY(reset_r(T));
@@ -369,6 +380,7 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
         if (timings_out != nullptr) {
           for (int jj = 0; jj < nmc; ++jj)
             if (mc_cand[jj] == mc) timings_out[(g * nT + i) * ncols + 2 + jj] = sf.median;
+          if (mc == PR_SINGLE_LAUNCH) timings_out[(g * nT + i) * ncols + 2 + nmc] = sf.median;
         }
         if (best < 0 || sf.median < best) {
           best = sf.median;

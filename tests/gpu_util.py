@@ -63,12 +63,18 @@ class Device:
                               device=DEV)
 
     def run(self, microchunk=None, out="own", stream=None):
-        """microchunk=None: conventional entry point; else proj_add_rmsnorm(microchunk)."""
+        """microchunk=None: conventional entry point; "single": the single-launch entry point
+        (its status bits must stay clear); else proj_add_rmsnorm(microchunk)."""
         o = self.out if out == "own" else None
         d = self.d
         if microchunk is None:
             pr.proj_add_rmsnorm_unfused(self.x, self.Wp, self.r, self.w, d["eps"], self.T, self.K,
                                         self.H, d["norm_kind"], o, stream)
+        elif microchunk == "single":
+            pr.proj_add_rmsnorm_single_launch(self.x, self.Wp, self.r, self.w, d["eps"], self.T,
+                                              self.K, self.H, d["norm_kind"], o, stream)
+            status = pr.pr_device_status(stream or torch.cuda.current_stream())
+            assert status == 0, f"single-launch status bits {status:#x}"
         else:
             pr.proj_add_rmsnorm(self.x, self.Wp, self.r, self.w, d["eps"], self.T, self.K, self.H,
                                 microchunk, d["norm_kind"], o, stream)

@@ -27,7 +27,7 @@ if torch.cuda.is_available():
 def _env(monkeypatch):
     for k in ("PR_MICROCHUNK_TOKENS", "PR_THRESHOLD_TOKENS", "PR_FORCE_TILE", "PR_FORCE_SPLIT",
               "PR_FORCE_WAVES", "PR_FORCE_STAGES", "PR_FORCE_ADDNORM_WGS", "PR_DEBUG_POISON",
-              "PR_DEBUG_DELAY",
+              "PR_DEBUG_DELAY", "PR_SPIN_LIMIT",
               "PR_FAULT_INJECT"):
         monkeypatch.delenv(k, raising=False)
     pr.pr_clear_tuning()
@@ -92,6 +92,132 @@ def test_random_parity_small(T, K, H, kind):
         dev.reset()
         r_dev, out_bits = dev.run(mc)
         _check(d, r_dev, out_bits, "conventional" if mc is None else "fused")
+
+
+# ------------------------------------------------------------- single-launch fused path
+# (tile, waves per workgroup) of every single-launch instantiation
+SINGLE_CFGS = [("256x256", 8), ("256x128", 8), ("256x128", 4), ("128x128", 8)]
+
+
+def _mode(mc):
+    return "conventional" if mc is None else "fused"
+
+
+@pytest.mark.parametrize("tile,waves", SINGLE_CFGS)
+def test_single_launch_integer_projection_is_exact(monkeypatch, tile, waves):
+    """Small integers: the fp32 residual is exact, so it must match bitwise.  T=300 leaves a
+    ragged last tile row; H=768 is 3 or 6 tile columns."""
+    monkeypatch.setenv("PR_FORCE_TILE", tile)
+    monkeypatch.setenv("PR_FORCE_WAVES", str(waves))
+    d = synth.integer_inputs(300, 1024, 768, seed=3)
+    dev = Device(d)
+    r_dev, out_bits = dev.run("single")
+    r_ref, out_ref = oracle.proj_add_rmsnorm(d["x"], d["W"], d["residual"], d["norm_w"],
+                                             d["eps"], 0, "fused")
+    np.testing.assert_array_equal(r_dev.astype(np.float64), r_ref)
+    err = oracle.compare(r_dev, out_bits, r_ref, out_ref)
+    assert oracle.within_tolerance(err), err
+
+
+@pytest.mark.parametrize("tile,waves", SINGLE_CFGS)
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("T,K,H", [(300, 512, 768), (64, 512, 512), (1, 256, 512),
+                                   (513, 1024, 256)])
+def test_single_launch_random_parity_small(monkeypatch, tile, waves, kind, T, K, H):
+    if H % int(tile.split("x")[1]):
+        pytest.skip("tile columns do not divide H")
+    monkeypatch.setenv("PR_FORCE_TILE", tile)
+    monkeypatch.setenv("PR_FORCE_WAVES", str(waves))
+    d = synth.make_custom(T, K, H, seed=T + K, norm_kind=kind, eps=1e-5)
+    dev = Device(d)
+    r_dev, out_bits = dev.run("single")
+    _check(d, r_dev, out_bits, "fused")
+
+
+@pytest.mark.parametrize("tile,waves,T,H", [("256x128", 8, 4096, 4096), ("256x128", 4, 4096, 4096),
+                                            ("128x128", 8, 8192, 2048), ("256x256", 8, 4100, 8192)])
+def test_single_launch_several_rounds(monkeypatch, tile, waves, T, H):
+    """More tiles than resident workgroups: the launch runs several rounds of whole tile rows
+    (256x128: 512 tiles in 2 rounds; 128x128: 1024 tiles in 2; 256x256: 17 x 32 tiles, the
+    last round one ragged tile row)."""
+    monkeypatch.setenv("PR_FORCE_TILE", tile)
+    monkeypatch.setenv("PR_FORCE_WAVES", str(waves))
+    print(f"single launch {tile} T={T} H={H}", flush=True)
+    d = synth.make_custom(T, 256, H, seed=11)
+    dev = Device(d)
+    r_dev, out_bits = dev.run("single")
+    rows = _sample_rows(T, 256, n=96, seed=2)
+    _check(d, r_dev, out_bits, "fused", rows)
+
+
+def test_single_launch_padded_rows_untouched():
+    T = 300
+    d = synth.make_custom(T, 512, 384, seed=5)
+    dev = Device(d, extra_rows=212, pad_x_nan=True)
+    dev.reset(sentinel=12345.0)
+    r_dev, out_bits = dev.run("single")
+    _check(d, r_dev, out_bits, "fused")
+    assert np.all(dev.r.cpu().numpy()[T:] == 12345.0)
+    assert np.all(bits(dev.out)[T:] == 0x7BAD)
+
+
+def test_single_launch_back_to_back_calls():
+    """The completion counters return to zero at the end of every launch: calls of different
+    sizes in a row (on one stream, no host synchronisation between them) are all correct."""
+    cases = [synth.make_custom(T, 512, 1024, seed=T) for T in (1000, 300, 1000, 17)]
+    devs = [Device(d) for d in cases]
+    for dev in devs:
+        dev.reset()
+    for dev in devs:
+        d = dev.d
+        pr.proj_add_rmsnorm_single_launch(dev.x, dev.Wp, dev.r, dev.w, d["eps"], dev.T, dev.K,
+                                          dev.H, d["norm_kind"], dev.out)
+    assert pr.pr_device_status(torch.cuda.current_stream()) == 0
+    for dev in devs:
+        _check(dev.d, dev.r[:dev.T].cpu().numpy(), bits(dev.out[:dev.T]), "fused")
+
+
+def test_single_launch_agrees_with_pipeline():
+    """Same fused semantics as the microchunk pipeline: the residuals agree to fp32 rounding of
+    the projection's summation order, the outputs within one bf16 step."""
+    d = synth.make_custom(700, 1024, 2048, seed=9)
+    dev = Device(d)
+    r_s, o_s = dev.run("single")
+    dev.reset()
+    r_p, o_p = dev.run(256)
+    assert np.max(np.abs(r_s - r_p)) <= 1e-5 * np.max(np.abs(r_p))
+    a = o_s.astype(np.uint32) << 16
+    b = o_p.astype(np.uint32) << 16
+    diff = np.abs(a.view(np.float32) - b.view(np.float32))
+    assert np.max(diff) <= 2 ** -7 * np.max(np.abs(b.view(np.float32)))
+
+
+def test_single_launch_wait_limit_reports(monkeypatch):
+    """Row reads that look for an epoch no slot carries (set from the host) give up after 64
+    polls each; the kernel ends, the status bit reports it and reading clears it.  A later
+    call without the fault is correct."""
+    monkeypatch.setenv("PR_FAULT_INJECT", "wait")
+    monkeypatch.setenv("PR_SPIN_LIMIT", "64")
+    d = synth.make_custom(600, 256, 1024, seed=4)
+    dev = Device(d)
+    pr.proj_add_rmsnorm_single_launch(dev.x, dev.Wp, dev.r, dev.w, d["eps"], dev.T, dev.K, dev.H,
+                                      d["norm_kind"], dev.out)
+    assert pr.pr_device_status(torch.cuda.current_stream()) & 1
+    assert pr.pr_device_status(torch.cuda.current_stream()) == 0
+    assert np.all(bits(dev.out) == 0x7BAD)  # no tile wrote output
+    monkeypatch.delenv("PR_FAULT_INJECT")
+    monkeypatch.delenv("PR_SPIN_LIMIT")
+    dev.reset()
+    r_dev, out_bits = dev.run("single")
+    _check(d, r_dev, out_bits, "fused")
+
+
+def test_single_launch_rejects_unsupported_width():
+    d = synth.make_custom(64, 256, 320, seed=1)
+    dev = Device(d)
+    with pytest.raises(pr.PRError) as e:
+        dev.run("single")
+    assert e.value.code == pr.PR_ERR_SHAPE
 
 
 def test_borrowed_output_workspace():
@@ -305,17 +431,25 @@ def test_auto_mode_overrides_and_tuning(monkeypatch):
     monkeypatch.delenv("PR_MICROCHUNK_TOKENS")
     monkeypatch.delenv("PR_THRESHOLD_TOKENS")
     rep = pr.pr_tune([512], [512], 0, [128, 512], [64, 128, 256], reps=3)
-    assert rep["n_checked"] >= 3 and rep["n_rejected"] == 0
+    # T=128: chunks 64 and 128 and the single launch; T=512: three chunk sizes and the single
+    assert rep["n_checked"] == 7 and rep["n_rejected"] == 0
     assert rep["max_tokens"] == 512
-    for row in rep["timings"][0]:
-        assert row[0] > 0 and row[1] > 0
+    for row in rep["timings"][0]:  # conventional, best fused, chunks 64/128/256, single
+        assert len(row) == 6 and row[0] > 0 and row[1] > 0 and row[5] > 0
+        assert row[1] == min(v for v in row[2:] if v > 0)
     for mc in (64, 128, 256):  # a chunk configuration was tuned and installed per chunk size
         cfg = pr.pr_select(512, 512, 512, mc)
         assert (cfg["gemm_bm"], cfg["gemm_bn"]) in ((256, 256), (256, 128), (128, 128))
         assert 512 % (64 * cfg["split_k"]) == 0 and cfg["gemm_waves"] in (4, 8)
     sel = pr.pr_select(512, 512, 512, 0)
     thr = rep["threshold_tokens"]
-    assert sel["path"] == (pr.PR_PATH_FUSED if 512 >= thr else pr.PR_PATH_CONVENTIONAL)
+    if 512 >= thr:
+        assert sel["path"] in (pr.PR_PATH_FUSED, pr.PR_PATH_SINGLE)
+    else:
+        assert sel["path"] == pr.PR_PATH_CONVENTIONAL
+    dev.reset()
+    r3, o3 = dev.run(0)          # tuned auto mode, whichever path it chose
+    _check(d, r3, o3, "conventional" if sel["path"] == pr.PR_PATH_CONVENTIONAL else "fused")
     # T above the largest tuned token count is refused before anything runs
     x600 = torch.zeros((600, 512), dtype=torch.int16, device=DEV)
     r600 = torch.zeros((600, 512), dtype=torch.float32, device=DEV)
@@ -326,10 +460,10 @@ def test_auto_mode_overrides_and_tuning(monkeypatch):
 
 def test_tuner_accepts_large_hidden_sizes():
     """At H = 8192 two correct bf16 outputs differ by an ulp at |out| >= 4 (0.031 > 2e-2):
-    the candidate check must still accept the pipeline (every candidate checked, none
-    rejected)."""
+    the candidate check must still accept the fused candidates (every one checked, none
+    rejected: two chunk sizes and the single launch at each of the two token counts)."""
     rep = pr.pr_tune([1024], [8192], 0, [512, 1024], [256, 512], reps=2)
-    assert rep["n_rejected"] == 0 and rep["n_checked"] == 4, rep
+    assert rep["n_rejected"] == 0 and rep["n_checked"] == 6, rep
 
 
 # -------------------------------------------------------------------- full-size workloads
@@ -348,10 +482,10 @@ def test_workload_parity_full_size(name):
     print(f"workload {name}: T={wl.T} K={wl.K} H={wl.H}", flush=True)
     d = synth.make_inputs(wl, seed=0)
     dev = Device(d)
-    for mc in (None,) + wl.microchunks:
+    for mc in (None,) + wl.microchunks + ("single",):
         dev.reset()
         r_dev, out_bits = dev.run(mc)
-        rows = _sample_rows(wl.T, mc or wl.T, seed=hash(name) % 1000)
+        rows = _sample_rows(wl.T, mc if isinstance(mc, int) else wl.T, seed=hash(name) % 1000)
         err = _check(d, r_dev, out_bits, "conventional" if mc is None else "fused", rows)
         print(name, mc, err, flush=True)
         assert np.all(np.isfinite(r_dev))

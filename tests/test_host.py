@@ -141,6 +141,26 @@ def test_chunk_config_table(monkeypatch):
         assert e.value.code == code, args
 
 
+def test_select_single_launch():
+    d = pr.pr_select(2048, 4096, 4096, pr.PR_SINGLE_LAUNCH)
+    assert d["path"] == pr.PR_PATH_SINGLE and d["reason"] == 6
+    assert (d["microchunk"], d["n_chunks"], d["last_valid"]) == (2048, 1, 2048)
+    assert d["split_k"] == 1 and 4096 % d["gemm_bn"] == 0
+    # one round of 256 x 128 tiles (8 x 32 = 256 workgroups) runs with 4 waves
+    assert (d["gemm_bm"], d["gemm_bn"], d["gemm_waves"]) == (256, 128, 4)
+    for T, K, H in [(4096, 14336, 4096), (3000, 16384, 3072), (32768, 8192, 8192), (1, 512, 512)]:
+        d = pr.pr_select(T, K, H, pr.PR_SINGLE_LAUNCH)
+        assert d["path"] == pr.PR_PATH_SINGLE
+        assert H % d["gemm_bn"] == 0 and H // d["gemm_bn"] <= 64
+        assert d["gemm_waves"] in (4, 8)
+    with pytest.raises(pr.PRError) as e:  # no tile's columns divide H = 320
+        pr.pr_select(64, 256, 320, pr.PR_SINGLE_LAUNCH)
+    assert e.value.code == pr.PR_ERR_SHAPE
+    with pytest.raises(pr.PRError) as e:
+        pr.pr_select(64, 256, 256, -3)
+    assert e.value.code == pr.PR_ERR_MICROCHUNK
+
+
 def test_auto_untuned_and_overrides(monkeypatch):
     d = pr.pr_select(2048, 4096, 4096, 0)
     assert d["path"] == pr.PR_PATH_CONVENTIONAL and pr.REASON_NAMES[d["reason"]] == "untuned"
@@ -181,6 +201,14 @@ def test_auto_tuned(monkeypatch):
     assert pr.pr_select(8192, 4096, 4096, 0)["microchunk"] == 256
     monkeypatch.delenv("PR_MICROCHUNK_TOKENS")
     # inconclusive tuning keeps the conventional path
+    # the single launch as the tuned fused form of a grid range
+    pr.pr_set_tuning(4096, 4096, 512, 32768, [128, 512, 2048], [128, 256, pr.PR_SINGLE_LAUNCH])
+    assert pr.pr_select(1024, 4096, 4096, 0)["microchunk"] == 256
+    d = pr.pr_select(2048, 4096, 4096, 0)
+    assert d["path"] == pr.PR_PATH_SINGLE and d["reason"] == 1  # above threshold
+    assert pr.pr_select(256, 4096, 4096, 0)["path"] == pr.PR_PATH_CONVENTIONAL
+    with pytest.raises(pr.PRError):
+        pr.pr_set_tuning(64, 64, 1, 10, [4], [-3])
     pr.pr_set_tuning(8192, 8192, pr.INT32_MAX, 32768, [128], [128])
     d = pr.pr_select(4096, 8192, 8192, 0)
     assert d["path"] == pr.PR_PATH_CONVENTIONAL and pr.REASON_NAMES[d["reason"]] == "inconclusive"
