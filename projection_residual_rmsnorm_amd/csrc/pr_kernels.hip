@@ -472,7 +472,16 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
     const int count = rows_here * tiles_n;
     if ((int)blockIdx.x >= count) continue;  // uniform over the workgroup
     int tm, tn;
-    tile_coords(xcd_logical(blockIdx.x, count), rows_here, tiles_n, &tm, &tn);
+    if (rows_here % kNumXCDs == 0) {
+      // Whole tile rows per XCD (workgroup b runs on XCD b % 8): a row's tiles finish
+      // together, and an XCD that runs slower delays only its own rows.
+      const int per_xcd = rows_here / kNumXCDs;
+      const int j = blockIdx.x / kNumXCDs;
+      tm = (blockIdx.x % kNumXCDs) * per_xcd + j / tiles_n;
+      tn = j % tiles_n;
+    } else {
+      tile_coords(xcd_logical(blockIdx.x, count), rows_here, tiles_n, &tm, &tn);
+    }
     tm += round * rows_per_round;
     const int m0 = tm * BM;
     const int n0 = tn * BN;
