@@ -39,12 +39,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="o_proj")
     ap.add_argument("--microchunk", type=int, default=0, help="0: every chunk size of the workload")
+    ap.add_argument("--only-single", action="store_true",
+                    help="time only the single-launch fused form (profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tune", action="store_true",
                     help="skip the load-time tuning (chunk projections use the time model)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic_o_proj.json"),
-                    help="measured HBM bytes per projection launch (from the counter runs)")
+    ap.add_argument("--traffic-dir", default=os.path.join(ROOT, "profiles"),
+                    help="directory of traffic_*.json counter summaries (measured HBM bytes per "
+                         "launch of the headline kernel)")
     ap.add_argument("--tune-sweep", action="store_true",
                     help="run the token-threshold search on the K=H=8192 sweep and print it")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -179,7 +182,10 @@ def main() -> int:
         log(f"tuned in {time.perf_counter() - t_tune:.1f} s: {chunk_cfgs} "
             f"(checked {rep['n_checked']}, rejected {rep['n_rejected']})")
     per_mc = {}
-    forms = mcs + (["single"] if not args.microchunk else [])
+    if args.only_single:
+        forms = ["single"]
+    else:
+        forms = mcs + (["single"] if not args.microchunk else [])
     for mc in forms:
         el = time_steps(fused(mc), args.steps, args.warmup, torch)
         per_mc[mc] = {"tokens_per_s": T * args.steps / el, "ms_per_step": el * 1e3 / args.steps,
@@ -233,14 +239,16 @@ def main() -> int:
     # Measured HBM bytes per projection launch, from the committed counter runs; null unless
     # they were taken on this exact kernel source and this workload / chunk size.
     traffic = None
-    if args.traffic_file and os.path.exists(args.traffic_file):
+    if args.traffic_dir and os.path.isdir(args.traffic_dir):
+        import glob
         from projection_residual_rmsnorm_amd.profiling import source_digest
-        with open(args.traffic_file) as f:
-            tr = json.load(f)
         src = os.path.join(ROOT, "projection_residual_rmsnorm_amd", "csrc", "pr_kernels.hip")
-        if (tr.get("kernel_source_sha256") == source_digest(src)
-                and tr.get("config") == traffic_label(wl.name, mc, chunk_cfgs)):
-            traffic = tr.get("gemm_bytes_per_launch")
+        digest, label = source_digest(src), traffic_label(wl.name, mc, chunk_cfgs)
+        for path in sorted(glob.glob(os.path.join(args.traffic_dir, "traffic_*.json"))):
+            with open(path) as f:
+                tr = json.load(f)
+            if tr.get("kernel_source_sha256") == digest and tr.get("config") == label:
+                traffic = tr.get("gemm_bytes_per_launch")
     roof = {"kernel": "gemm_add_rmsnorm_kernel" if single else "gemm_bf16_kernel",
             "bound": "mfma", "achieved": gemm_tflops,
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / PEAK_BF16_TFLOPS,

@@ -22,6 +22,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void global_cvoid_t;
 
@@ -556,7 +557,10 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
           const float4 y = *reinterpret_cast<const float4*>(ep + r_in * EP_LD + rcol);
           const float4 rv = keep[(i * 2 + h) * NR + rr];
           const float4 v = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
-          if (m0 + trow < M) *reinterpret_cast<float4*>(R + (long long)row * N + col) = v;
+          // Streaming stores: the updated residual and the output are not read again here.
+          if (m0 + trow < M)
+            __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
+                                        reinterpret_cast<f32x4_t*>(R + (long long)row * N + col));
           keep[(i * 2 + h) * NR + rr] = v;
           const float q = lane_group_sum<LPR>(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
           if (el % LPR == 0) sred[trow * WN + wn] = q;
@@ -653,8 +657,10 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
               const uint32_t o1 = f32_to_bf16_rne(v.y * inv * gy);
               const uint32_t o2 = f32_to_bf16_rne(v.z * inv * gz);
               const uint32_t o3 = f32_to_bf16_rne(v.w * inv * gw);
-              *reinterpret_cast<uint2*>(out + (long long)row * N + col) =
-                  make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+              __builtin_nontemporal_store(
+                  (unsigned long long)(o0 | (o1 << 16)) |
+                      ((unsigned long long)(o2 | (o3 << 16)) << 32),
+                  reinterpret_cast<unsigned long long*>(out + (long long)row * N + col));
             }
           }
     }

@@ -24,7 +24,8 @@ COPY_BYTES = 1 << 30
 
 
 def short_name(name: str) -> str:
-    m = re.search(r"(gemm_bf16_kernel<[^>]*>|add_rmsnorm\w*<[^>]*>|add_rmsnorm_generic_kernel|"
+    m = re.search(r"(gemm_add_rmsnorm_kernel<[^>]*>|gemm_bf16_kernel<[^>]*>|"
+                  r"(?<!gemm_)add_rmsnorm\w*<[^>]*>|add_rmsnorm_generic_kernel|"
                   r"prepare_weight\w*|__amd_rocclr_\w+|fill_\w+|delay_kernel)", name)
     return m.group(1) if m else name[:60]
 
