@@ -137,19 +137,22 @@ int proj_add_rmsnorm_unfused(const uint16_t* x, const uint16_t* W, float* residu
  * kernel launch.  It is the pipeline of proj_add_rmsnorm with its hand-offs moved into the
  * kernel ("TPSP Design" section 3, Microchunk pipeline: reusable slots guarded by readiness
  * and completion events): a chunk is one tile row of tokens, its slot is the tile's
- * accumulators, and its events are a per-tile-row completion counter in device memory.  Each
- * tile adds the residual to its fp32 projection result (the fused semantics: y is not
- * rounded), publishes per-token partial sums of squares, waits until every tile of its row has
- * published and then writes its part of the output.  The launch is cooperative (all its
- * workgroups are resident at once), so every wait ends; a wait that exceeds its poll limit
- * gives up, leaves its tile's output unwritten and sets a status bit read by
- * pr_device_status.
+ * accumulators, and its events are a per-tile-row completion counter and epoch-tagged partial
+ * slots in device memory.  Each tile adds the residual to its fp32 projection result (the
+ * fused semantics: y is not rounded), publishes per-token partial sums of squares, waits until
+ * every tile of its row has published and then writes its part of the output.  The grid never
+ * exceeds the workgroups the device holds at once and a wait only involves tiles of the same
+ * round, so every wait ends once the launch's workgroups are placed.  A wait that nevertheless
+ * exceeds its poll limit (about two seconds) gives up: that tile's rows of the call are then
+ * invalid (output not written, residual update possibly missing) and a status bit read by
+ * pr_device_status is set.
  *
  * Same arguments and ownership as proj_add_rmsnorm_unfused.  Requires H = tile columns * n
  * with n <= 64 for one of the tiles the library instantiates (256 or 128 columns), else
  * PR_ERR_SHAPE.  The result agrees with the fused pipeline within rounding (the sum of squares
- * is taken in another order).  Uses a device workspace of T * ceil4(H / 128) floats and
- * 2 + T / 128 counters, shared by all calls on the device.
+ * is taken in another order).  Uses a device workspace of T * H / 128 64-bit slots and
+ * 2 + T / 128 counters, shared by all calls on the device (calls on one device are
+ * sequential, as for every entry point).
  */
 int proj_add_rmsnorm_single_launch(const uint16_t* x, const uint16_t* W, float* residual_inout,
                                    const float* norm_w, float eps, int T, int K, int H,

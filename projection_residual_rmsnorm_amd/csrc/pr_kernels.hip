@@ -384,8 +384,9 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
 //   1. loads its tile's residual into registers (tiles where it fits in 64 registers per lane)
 //      and runs the projection main loop of its BM x BN tile,
 //   2. forms r + y in fp32 (the fused mode's unrounded y), writes it as the updated residual
-//      and takes, per token, the sum of squares over its BN columns (lane partials in column
-//      order, reduced over the lanes of a row, then over the waves of the tile in wave order),
+//      (here or, for tiles whose residual was not prefetched, in step 5) and takes, per token,
+//      the sum of squares over its BN columns (lane partials in column order, reduced over the
+//      lanes of a row, then over the waves of the tile in wave order),
 //   3. publishes each token's partial in a 64-bit slot {call epoch, value} and adds one to its
 //      tile row's counter,
 //   4. waits (one lane, bounded) until the counter shows every tile of the row, reads the
@@ -558,9 +559,13 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
           const float4 rv = keep[(i * 2 + h) * NR + rr];
           const float4 v = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
           // Streaming stores: the updated residual and the output are not read again here.
-          if (m0 + trow < M)
-            __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
-                                        reinterpret_cast<f32x4_t*>(R + (long long)row * N + col));
+          // Without the prefetch the residual loads of the next slice would queue behind these
+          // stores (one counter covers loads and stores), so those tiles store it with the
+          // output instead.
+          if constexpr (PREFETCH)
+            if (m0 + trow < M)
+              __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
+                                          reinterpret_cast<f32x4_t*>(R + (long long)row * N + col));
           keep[(i * 2 + h) * NR + rr] = v;
           const float q = lane_group_sum<LPR>(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
           if (el % LPR == 0) sred[trow * WN + wn] = q;
@@ -652,6 +657,9 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
             const int row = m0 + trow;
             if (row < M) {
               const float4 v = keep[(i * 2 + h) * NR + rr];
+              if constexpr (!PREFETCH)
+                __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
+                                            reinterpret_cast<f32x4_t*>(R + (long long)row * N + col));
               const float inv = sinv[trow];
               const uint32_t o0 = f32_to_bf16_rne(v.x * inv * gx);
               const uint32_t o1 = f32_to_bf16_rne(v.y * inv * gy);
