@@ -99,10 +99,6 @@ def test_random_parity_small(T, K, H, kind):
 SINGLE_CFGS = [("256x256", 8), ("256x128", 8), ("256x128", 4), ("128x128", 8)]
 
 
-def _mode(mc):
-    return "conventional" if mc is None else "fused"
-
-
 @pytest.mark.parametrize("tile,waves", SINGLE_CFGS)
 def test_single_launch_integer_projection_is_exact(monkeypatch, tile, waves):
     """Small integers: the fp32 residual is exact, so it must match bitwise.  T=300 leaves a
@@ -148,6 +144,22 @@ def test_single_launch_several_rounds(monkeypatch, tile, waves, T, H):
     r_dev, out_bits = dev.run("single")
     rows = _sample_rows(T, 256, n=96, seed=2)
     _check(d, r_dev, out_bits, "fused", rows)
+
+
+def test_single_launch_largest_workload():
+    """The largest configuration (K=H=8192, T=32768): 128 tile rows in 16 rounds of whole tile
+    rows per XCD; sampled rows against the oracle, conventional path beside it."""
+    wl = synth.WORKLOADS["sweep_T32768"]
+    print(f"single launch T={wl.T} K={wl.K} H={wl.H}", flush=True)
+    d = synth.make_inputs(wl, seed=0)
+    dev = Device(d)
+    rows = _sample_rows(wl.T, 256, n=64, seed=5)
+    for mc in ("single", None):
+        dev.reset()
+        r_dev, out_bits = dev.run(mc)
+        err = _check(d, r_dev, out_bits, "conventional" if mc is None else "fused", rows)
+        print(mc, err, flush=True)
+        assert np.all(np.isfinite(r_dev[rows]))
 
 
 def test_single_launch_padded_rows_untouched():
