@@ -381,8 +381,9 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
 // through reusable slots guarded by readiness and completion events) become in-kernel ones:
 // the chunk is one tile row (BM tokens), the slot is the tile's own accumulators, and the
 // events are device-memory words.  Each workgroup
-//   1. loads its tile's residual into registers (tiles where it fits in 64 registers per lane)
-//      and runs the projection main loop of its BM x BN tile,
+//   1. loads its tile's residual into registers (tiles where it fits: 64 registers per lane
+//      with two waves per SIMD, 128 with one) and runs the projection main loop of its BM x BN
+//      tile,
 //   2. forms r + y in fp32 (the fused mode's unrounded y), writes it as the updated residual
 //      (here or, for tiles whose residual was not prefetched, in step 5) and takes, per token,
 //      the sum of squares over its BN columns (lane partials in column order, reduced over the
@@ -495,8 +496,8 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
       return wm * WTM + i * 32 + h * 16 + rr * RPI + l / LPR;
     };
 
-    // The residual, loaded before the main loop so that its read overlaps the MFMA work (tiles
-    // whose share fits in 64 registers per lane), else one 16-row slice ahead in the epilogue.
+    // The residual, loaded before the main loop so that its read overlaps the MFMA work (when
+    // PREFETCH), else one 16-row slice ahead in the epilogue.
     float4 keep[KEEP];
     if constexpr (PREFETCH) {
       const int pcol = n0 + wn * WTN + rcol_of(lane);

@@ -374,7 +374,10 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
   const size_t slots_need = (size_t)rows_max * (H / g.bn) * sizeof(unsigned long long);
   if (slots_need > c->row_slots_bytes) {
     PR_TRY(grow(&c->row_slots, &c->row_slots_bytes, slots_need));
-    PR_HIP(hipMemset(c->row_slots, 0, c->row_slots_bytes));  // holds no epoch >= 1
+    // Zeroed (no slot holds an epoch >= 1) and complete before any kernel reads it: the fill
+    // runs on the null stream, which does not order work on a non-blocking caller stream.
+    PR_HIP(hipMemset(c->row_slots, 0, c->row_slots_bytes));
+    PR_HIP(hipDeviceSynchronize());
     c->epoch = 0;
   }
   const size_t sync_need = (size_t)(2 + (rows_max + g.bm - 1) / g.bm) * sizeof(unsigned);
@@ -385,6 +388,7 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
     c->sync = static_cast<unsigned*>(p);
     c->sync_bytes = have;
     PR_HIP(hipMemset(c->sync, 0, have));  // the kernels keep it zero from here on
+    PR_HIP(hipDeviceSynchronize());
   }
   const unsigned limit = spin_limit();
   const int gemma = norm_kind == PR_NORM_GEMMA;
@@ -392,8 +396,9 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
     const int rows = (int)std::min<long long>(rows_per, T - r0);
     if (++c->epoch == 0) {
       // After 2^32 - 1 launches the slots are cleared once so that epochs stay unique.
-      PR_HIP(hipStreamSynchronize(s));
+      PR_HIP(hipDeviceSynchronize());
       PR_HIP(hipMemset(c->row_slots, 0, c->row_slots_bytes));
+      PR_HIP(hipDeviceSynchronize());
       c->epoch = 1;
     }
     const unsigned epoch = c->epoch;
@@ -492,7 +497,10 @@ int pr_device_status(void* stream, unsigned* status) {
   if (c->sync == nullptr) return PR_OK;
   unsigned v = 0;
   PR_HIP(hipMemcpy(&v, c->sync, sizeof(v), hipMemcpyDeviceToHost));
-  if (v != 0) PR_HIP(hipMemset(c->sync, 0, sizeof(unsigned)));
+  if (v != 0) {
+    PR_HIP(hipMemset(c->sync, 0, sizeof(unsigned)));
+    PR_HIP(hipDeviceSynchronize());
+  }
   *status = v;
   return PR_OK;
 }
