@@ -81,9 +81,35 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, grid: int = 0) -> dict:
             "gemm_bytes_per_launch": fetched + written}
 
 
+def _code_only(text: str) -> str:
+    """The source without comments, whitespace runs collapsed (string and character literals
+    are kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def source_digest(path: str) -> str:
-    """sha256 of a kernel source file: counter readings are void once the kernel changes."""
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    """sha256 of a kernel source file's code (comments and whitespace do not count): counter
+    readings are void once the kernels' code changes."""
+    return hashlib.sha256(_code_only(open(path).read()).encode()).hexdigest()
 
 
 def main() -> None:

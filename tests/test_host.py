@@ -385,3 +385,15 @@ def test_binding_rejects_strided_or_short_tensors():
         pr.proj_add_rmsnorm_unfused(x, W[:-1], r, w, 1e-5, T, K, H)
     with pytest.raises(ValueError, match="W_prep"):
         pr.pr_prepare_weight(W, pr.PR_WEIGHT_OUT_IN, W[: K * H // 2], K, H)
+
+
+def test_traffic_digest_ignores_comments_only(tmp_path):
+    """Counter summaries stay valid across comment edits of the kernel source and are void
+    after any code change."""
+    from projection_residual_rmsnorm_amd.profiling import source_digest
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text('int f(int x) {  // add one\n  return x + 1; /* done */ }\nconst char* s = "//";\n')
+    b.write_text('// header\nint f(int x) {\n  return x + 1;\n}\nconst char* s = "//";\n')
+    c.write_text('int f(int x) { return x + 2; }\nconst char* s = "//";\n')
+    assert source_digest(str(a)) == source_digest(str(b))
+    assert source_digest(str(a)) != source_digest(str(c))
