@@ -292,8 +292,10 @@ typedef struct {
  * result is first checked against the conventional path's result and dropped if it fails:
  * output relative L2 <= 5e-3 and per element |delta| <= 2e-2 + one bf16 ulp (both outputs are
  * rounded); residual per element within half a bf16 ulp of y plus fp32 rounding (the paths
- * differ exactly by the bf16 rounding of y).  Timings are medians of `reps` calls on synthetic
- * device data.  Before that, for each group and chunk size, the projection configurations of
+ * differ exactly by the bf16 rounding of y).  At each T the conventional path and the candidates
+ * that pass are timed round-robin (one call each per round, max(reps, 5) rounds after a
+ * warm-up round; the chip's clock drifts with its power state, so back-to-back series would
+ * favour whichever ran first) and each is represented by its median, on synthetic device data.  Before that, for each group and chunk size, the projection configurations of
  * the chunks are chosen: the time model's three best tile/split choices for a chunk alone on
  * the GPU and its three best with half the GPU (the other stream's chunk runs alongside), each
  * with 8 and 4 waves, are checked and timed round-robin in the pipeline at

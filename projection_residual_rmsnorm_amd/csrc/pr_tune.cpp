@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <vector>
 
 #include "pr_internal.h"
@@ -84,37 +85,45 @@ struct Stats {
   double median = -1, p10 = 0, p90 = 0;
 };
 
-template <typename F>
-int time_calls(F&& call, int reps, hipStream_t s, Stats* st) {
+// Times every call of `calls` round-robin: each round runs each call once, bracketed by
+// events on `s`; the first round warms up.  The chip's clock drifts with its power state, so
+// timing one candidate after another would favour whichever ran first.
+int time_round_robin(const std::vector<std::function<int()>>& calls, int rounds, hipStream_t s,
+                     std::vector<Stats>* st) {
   hipEvent_t e0, e1;
   PR_HIP(hipEventCreate(&e0));
   if (const hipError_t e = hipEventCreate(&e1); e != hipSuccess) {
     (void)hipEventDestroy(e0);
     return fail(PR_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
   }
-  std::vector<double> t;
+  std::vector<std::vector<double>> t(calls.size());
   int rc = PR_OK;
-  for (int i = 0; i < 2 && rc == PR_OK; ++i) rc = call();  // warm-up
-  for (int i = 0; i < reps && rc == PR_OK; ++i) {
-    (void)hipEventRecord(e0, s);
-    rc = call();
-    (void)hipEventRecord(e1, s);
-    if (rc != PR_OK) break;
-    if (hipEventSynchronize(e1) != hipSuccess) {
-      rc = fail(PR_ERR_HIP, "timing sync failed");
-      break;
+  for (int round = 0; round < rounds + 1 && rc == PR_OK; ++round) {
+    for (size_t k = 0; k < calls.size() && rc == PR_OK; ++k) {
+      (void)hipEventRecord(e0, s);
+      rc = calls[k]();
+      (void)hipEventRecord(e1, s);
+      if (rc != PR_OK) break;
+      if (hipEventSynchronize(e1) != hipSuccess) {
+        rc = fail(PR_ERR_HIP, "timing sync failed");
+        break;
+      }
+      float ms = 0;
+      (void)hipEventElapsedTime(&ms, e0, e1);
+      if (round > 0) t[k].push_back(ms * 1e-3);
     }
-    float ms = 0;
-    (void)hipEventElapsedTime(&ms, e0, e1);
-    t.push_back(ms * 1e-3);
   }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   if (rc != PR_OK) return rc;
-  std::sort(t.begin(), t.end());
-  st->median = t[t.size() / 2];
-  st->p10 = t[t.size() / 10];
-  st->p90 = t[(t.size() * 9) / 10 < t.size() ? (t.size() * 9) / 10 : t.size() - 1];
+  st->assign(calls.size(), Stats());
+  for (size_t k = 0; k < calls.size(); ++k) {
+    std::vector<double>& v = t[k];
+    std::sort(v.begin(), v.end());
+    (*st)[k].median = v[v.size() / 2];
+    (*st)[k].p10 = v[v.size() / 10];
+    (*st)[k].p90 = v[std::min(v.size() - 1, (v.size() * 9) / 10)];
+  }
   return PR_OK;
 }
 
@@ -293,42 +302,20 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
           PR_TRY(fetch(Tc, out_try, r_try));
           if (candidate_ok(out_try, out_ref, r_try, r_ref, r_before)) passed.push_back(k);
         }
-        std::vector<std::vector<double>> samples(cs.size());
-        const int rounds = std::max(reps, 7);
-        hipEvent_t e0, e1;
-        PR_HIP(hipEventCreate(&e0));
-        if (const hipError_t e = hipEventCreate(&e1); e != hipSuccess) {
-          (void)hipEventDestroy(e0);
-          return fail(PR_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
-        }
-        int trc = PR_OK;
-        for (int round = 0; round < rounds + 1 && trc == PR_OK; ++round) {
-          for (size_t k : passed) {
-            trc = pr_set_chunk_config(K, H, mc, kTileBM[cs[k].c], kTileBN[cs[k].c], cs[k].split,
-                                      cs[k].waves);
-            if (trc != PR_OK) break;
-            (void)hipEventRecord(e0, s);
-            trc = fused_call_at(Tc, mc);
-            (void)hipEventRecord(e1, s);
-            if (trc != PR_OK) break;
-            if (hipEventSynchronize(e1) != hipSuccess) {
-              trc = fail(PR_ERR_HIP, "timing sync failed");
-              break;
-            }
-            float ms = 0;
-            (void)hipEventElapsedTime(&ms, e0, e1);
-            if (round > 0) samples[k].push_back(ms * 1e-3);  // round 0 warms up
-          }
-        }
-        (void)hipEventDestroy(e0);
-        (void)hipEventDestroy(e1);
-        if (trc != PR_OK) return trc;
+        std::vector<std::function<int()>> calls;
+        for (size_t k : passed)
+          calls.push_back([&, k, mc, Tc]() {
+            const int rc = pr_set_chunk_config(K, H, mc, kTileBM[cs[k].c], kTileBN[cs[k].c],
+                                               cs[k].split, cs[k].waves);
+            return rc != PR_OK ? rc : fused_call_at(Tc, mc);
+          });
+        std::vector<Stats> st;
+        if (!calls.empty()) PR_TRY(time_round_robin(calls, std::max(reps, 7), s, &st));
         double best_t = -1, first_t = -1;
         int best_k = -1;
-        for (size_t k : passed) {
-          std::vector<double>& v = samples[k];
-          std::sort(v.begin(), v.end());
-          const double med = v[v.size() / 2];
+        for (size_t n = 0; n < passed.size(); ++n) {
+          const size_t k = passed[n];
+          const double med = st[n].median;
           if (k == 0) first_t = med;
           if (best_t < 0 || med < best_t) {
             best_t = med;
@@ -348,35 +335,43 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
       const int T = T_grid[i];
       std::vector<float> r_old;
       PR_TRY(old_rows(T, r_old));
-      auto conv_call = [&]() { return conv_call_at(T); };
       std::vector<uint16_t> out_c, out_f;
       std::vector<float> r_c, r_f;
       PR_TRY(reset_r(T));
-      PR_TRY(conv_call());
+      PR_TRY(conv_call_at(T));
       PR_TRY(fetch(T, out_c, r_c));
-      Stats sc;
-      PR_TRY(time_calls(conv_call, reps, s, &sc));
-      t_conv[g * nT + i] = sc.median;
-      if (timings_out != nullptr) timings_out[(g * nT + i) * ncols + 0] = sc.median;
-      double best = -1, best_spread = 0;
       for (int j = 0; j < nmc + 1; ++j)
         if (timings_out != nullptr) timings_out[(g * nT + i) * ncols + 2 + j] = -1;
-      std::vector<int> fused_cands = cands;
+      // Fused candidates at T: every chunk size that fits and the single launch; each is
+      // checked against the conventional result, then all that pass are timed round-robin
+      // with the conventional path.
+      std::vector<int> fused_cands;
+      for (const int mc : cands)
+        if (mc <= std::min(T, PR_MAX_MICROCHUNK)) fused_cands.push_back(mc);
       if (single_ok && !have_mc) fused_cands.push_back(PR_SINGLE_LAUNCH);
-      for (size_t j = 0; j < fused_cands.size(); ++j) {
-        const int mc = fused_cands[j];
-        if (mc > std::min(T, PR_MAX_MICROCHUNK)) continue;
-        auto fused_call = [&]() { return fused_call_at(T, mc); };
+      std::vector<int> passed;
+      for (const int mc : fused_cands) {
         PR_TRY(reset_r(T));
-        PR_TRY(fused_call());
+        PR_TRY(fused_call_at(T, mc));
         PR_TRY(fetch(T, out_f, r_f));
         if (!candidate_ok(out_f, out_c, r_f, r_c, r_old)) {
           ++rep_local.n_rejected;
           continue;
         }
         ++rep_local.n_checked;
-        Stats sf;
-        PR_TRY(time_calls(fused_call, reps, s, &sf));
+        passed.push_back(mc);
+      }
+      std::vector<std::function<int()>> calls;
+      calls.push_back([&, T]() { return conv_call_at(T); });
+      for (const int mc : passed) calls.push_back([&, T, mc]() { return fused_call_at(T, mc); });
+      std::vector<Stats> st;
+      PR_TRY(time_round_robin(calls, std::max(reps, 5), s, &st));
+      t_conv[g * nT + i] = st[0].median;
+      if (timings_out != nullptr) timings_out[(g * nT + i) * ncols + 0] = st[0].median;
+      double best = -1, best_spread = 0;
+      for (size_t k = 0; k < passed.size(); ++k) {
+        const int mc = passed[k];
+        const Stats& sf = st[k + 1];
         if (timings_out != nullptr) {
           for (int jj = 0; jj < nmc; ++jj)
             if (mc_cand[jj] == mc) timings_out[(g * nT + i) * ncols + 2 + jj] = sf.median;
