@@ -191,6 +191,9 @@ typedef struct {
   int gemm_waves; /* waves per projection workgroup (4 or 8)                         */
   int reason;     /* PR_REASON_*                                                    */
   int gemm_stages; /* LDS ring depth of the projection (0 = the tile's default)      */
+  int gemm_kgroups; /* K groups inside a projection workgroup (1, or 2 for the single
+                       launch's 256x128 tile with 8 waves: two groups of 4 waves each
+                       computing the tile over alternate 32-deep halves of K)          */
 } pr_decision;
 
 #define PR_REASON_EXPLICIT 0          /* microchunk > 0 given by the caller            */

@@ -49,7 +49,7 @@ _vp, _i, _f, _d = _c.c_void_p, _c.c_int, _c.c_float, _c.c_double
 class pr_decision(_c.Structure):
     _fields_ = [("path", _i), ("microchunk", _i), ("n_chunks", _i), ("last_valid", _i),
                 ("gemm_bm", _i), ("gemm_bn", _i), ("split_k", _i), ("gemm_waves", _i),
-                ("reason", _i), ("gemm_stages", _i)]
+                ("reason", _i), ("gemm_stages", _i), ("gemm_kgroups", _i)]
 
 
 class pr_plan_op(_c.Structure):

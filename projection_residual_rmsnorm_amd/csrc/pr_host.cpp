@@ -109,6 +109,12 @@ static int apply_forced_tile(int K, GemmCfg* g) {
       return fail(PR_ERR_INVALID_ARG, "PR_FORCE_STAGES=%s must be in 2..8", st);
     g->stages = stages;
   }
+  const char* kgv = std::getenv("PR_FORCE_KGROUPS");
+  if (kgv != nullptr && kgv[0] != '\0') {
+    const int kg = std::atoi(kgv);
+    if (kg != 1 && kg != 2) return fail(PR_ERR_INVALID_ARG, "PR_FORCE_KGROUPS=%s must be 1 or 2", kgv);
+    g->kgroups = kg;
+  }
   const char* sp = std::getenv("PR_FORCE_SPLIT");
   if (sp != nullptr && sp[0] != '\0') {
     const int split = std::atoi(sp);
@@ -306,6 +312,7 @@ int decide(int T, int K, int H, int microchunk, pr_decision* d) {
   d->split_k = g.split;
   d->gemm_waves = g.waves;
   d->gemm_stages = g.stages;
+  d->gemm_kgroups = g.kgroups;
   return PR_OK;
 }
 

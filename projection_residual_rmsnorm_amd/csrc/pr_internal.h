@@ -20,6 +20,7 @@ struct GemmCfg {
   int split = 1;  // K partitions; partial sums land in separate fp32 planes
   int waves = 4;  // waves per workgroup: 4 (one per SIMD) or 8 (two per SIMD)
   int stages = 0; // LDS ring depth; 0 = the deepest the tile fits in LDS
+  int kgroups = 1; // K groups inside the workgroup (single launch, 256x128 with 8 waves: 2)
 };
 
 // Tile configurations the library instantiates (rows x columns per workgroup).

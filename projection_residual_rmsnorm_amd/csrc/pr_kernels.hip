@@ -124,33 +124,42 @@ struct TileAcc {
   f32x16_t v[TM][TN];
 };
 
-// Main loop of one output tile: the product of A[m0 .. m0+BM)[k_begin .. k_begin + 32 nk) and
-// the weight columns [n0 .. n0+BN) over the same K range, in the 32x32 MFMA accumulator
+// Main loop of one output tile: the product of A[m0 .. m0+BM)[k_begin .. k_begin + 32 KG nk)
+// and the weight columns [n0 .. n0+BN) over the same K range, in the 32x32 MFMA accumulator
 // layout.  Returns with each wave past its own last fragment read: callers that reuse the
 // ring's LDS synchronize first.
-template <int BM, int BN, int NB, int WM, int WN>
+//
+// KG > 1 splits K inside the workgroup: the waves form KG groups of WM x WN waves, a stage
+// holds KG consecutive 32-deep halves of K, and group g computes the whole BM x BN tile over
+// half g of every stage.  Each wave then holds a partial sum over 1/KG of K (the caller adds
+// the groups' partials); with KG = 2 and 4-wave groups every SIMD runs two waves while each
+// wave keeps the large wave tile.
+template <int BM, int BN, int NB, int WM, int WN, int KG = 1>
 __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp, int M, int N, int K, int m0,
     int n0, int k_begin, int nk) {
-  constexpr int NW = WM * WN;  // waves per workgroup (4: one per SIMD, 8: two per SIMD)
+  constexpr int GW = WM * WN;  // waves per group
+  constexpr int NW = GW * KG;  // waves per workgroup (4: one per SIMD, 8: two per SIMD)
   constexpr int WTM = BM / WM;  // wave tile rows
   constexpr int WTN = BN / WN;  // wave tile columns
   constexpr int TM = WTM / 32;
   constexpr int TN = WTN / 32;
   constexpr int A_BYTES = BM * kBK * 2;
   constexpr int B_BYTES = BN * kBK * 2;
-  constexpr int A_LPW = A_BYTES / 1024 / NW;  // 1 KiB loads per wave per stage
+  constexpr int A_LPW = A_BYTES / 1024 / NW;  // 1 KiB loads per wave per 32-deep half
   constexpr int B_LPW = B_BYTES / 1024 / NW;
-  constexpr int LPW = A_LPW + B_LPW;
+  constexpr int LPW = KG * (A_LPW + B_LPW);   // per stage
   constexpr int P = NB - 1;  // stages in flight ahead of the one being computed
   constexpr int CG = BN / 64;
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "load split");
   static_assert(NW % CG == 0, "B loads: waves must cover whole k-groups");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
-  static_assert(NB >= 2 && NB <= 8 && NB * (A_BYTES + B_BYTES) <= 160 * 1024, "LDS budget");
+  static_assert(NB >= 2 && NB <= 8 && NB * KG * (A_BYTES + B_BYTES) <= 160 * 1024, "LDS budget");
   static_assert(LPW * (P - 1) < 64, "vmcnt range");
+  static_assert(KG == 1 || KG == 2, "one or two K groups");
 
-  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int HALF = A_BYTES + B_BYTES;  // one 32-deep half of a stage
+  constexpr int STAGE = KG * HALF;
   char* const sb0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
   char* const sb1 = ring_buffer<1, STAGE, BM, BN, NB, WM, WN>();
   // u is a compile-time constant at every call (unrolled loops), so this folds to one object.
@@ -166,10 +175,11 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int wm = wave / WN;
+  const int kgrp = KG == 1 ? 0 : wave / GW;  // K group
+  const int wm = (KG == 1 ? wave : wave % GW) / WN;
   const int wn = wave % WN;
 
-  // Load assignment: A load i of wave w fills LDS kilobyte q = w + NW*i of the stage, rows
+  // Load assignment (per half): A load i of wave w fills LDS kilobyte q = w + NW*i, rows
   // 16q .. 16q+15 (lane l: tile row 16q + l/4, slot l%4, i.e. k-group (l%4) ^ f(row)).
   // B load i of wave w fills kilobyte q = w + NW*i: k-group q / CG, 64-column group q % CG.
   // Rows and columns past the matrix edge are clamped to the last valid one: their data only
@@ -190,18 +200,22 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   const uint32_t b_lane_off = (uint32_t)(((wave / CG) * N + b_col) * 8) * 2u;
   const uint32_t b_step = (uint32_t)((NW / CG) * N * 8) * 2u;
 
-  // Stage bases advance by a fixed number of bytes per stage (scalar arithmetic only).
+  // Stage bases advance by a fixed number of bytes per half (scalar arithmetic only).
   const char* a_base0 = reinterpret_cast<const char*>(A + k_begin);
   const char* b_base0 = reinterpret_cast<const char*>(Bp + (long long)(k_begin / 8) * N * 8);
-  const long long b_stage_bytes = (long long)(kBK / 8) * N * 16;
+  const long long b_half_bytes = (long long)(kBK / 8) * N * 16;
   auto issue_stage = [&](int kt, char* buf) {
-    const char* a_base = a_base0 + kt * (kBK * 2);
-    const char* b_base = b_base0 + kt * b_stage_bytes;
 #pragma unroll
-    for (int i = 0; i < A_LPW; ++i) load_to_lds16(a_base, a_off[i], buf + (wave + NW * i) * 1024);
+    for (int h = 0; h < KG; ++h) {
+      const char* a_base = a_base0 + (kt * KG + h) * (kBK * 2);
+      const char* b_base = b_base0 + (kt * KG + h) * b_half_bytes;
+      char* hb = buf + h * HALF;
 #pragma unroll
-    for (int i = 0; i < B_LPW; ++i)
-      load_to_lds16(b_base, b_lane_off + i * b_step, buf + A_BYTES + (wave + NW * i) * 1024);
+      for (int i = 0; i < A_LPW; ++i) load_to_lds16(a_base, a_off[i], hb + (wave + NW * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < B_LPW; ++i)
+        load_to_lds16(b_base, b_lane_off + i * b_step, hb + A_BYTES + (wave + NW * i) * 1024);
+    }
   };
 
   f32x16_t acc[TM][TN];
@@ -218,7 +232,8 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   const int a_f = ((a_r >> 1) ^ (a_r >> 3)) & 3;
   const int a_lane0 = a_r * 64 + (((lane >> 5)) ^ a_f) * 16;      // substep 0
   const int a_lane1 = a_r * 64 + ((2 + (lane >> 5)) ^ a_f) * 16;  // substep 1
-  auto load_frags = [&](const char* buf, int s, bf16x8_t* af, bf16x8_t* bfr) {
+  auto load_frags = [&](const char* stage, int s, bf16x8_t* af, bf16x8_t* bfr) {
+    const char* buf = KG == 1 ? stage : stage + kgrp * HALF;  // this group's half
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int rb = wm * TM + i;
@@ -429,20 +444,26 @@ __device__ __forceinline__ float lane_group_sum(float q) {
   return q;
 }
 
-template <int BM, int BN, int NB, int WM, int WN>
-__global__ void __launch_bounds__(WM* WN * 64, 1)
+template <int BM, int BN, int NB, int WM, int WN, int KG>
+__global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     gemm_add_rmsnorm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp,
                             float* __restrict__ R, const float* __restrict__ w,
                             uint16_t* __restrict__ out, unsigned long long* __restrict__ slots,
                             unsigned* __restrict__ sync, int M, int N, int K, int tiles_m,
                             int tiles_n, int rows_per_round, float eps, int gemma,
                             unsigned epoch, unsigned read_epoch, unsigned spin_limit) {
-  constexpr int NW = WM * WN;
-  constexpr int WTM = BM / WM;
+  // Main loop: KG groups of WM x WN waves (wave tiles BM/WM x BN/WN, TM x TN MFMA blocks).
+  // Epilogue: after the groups' partials are combined, EWM x WN waves, each owning a
+  // BM/EWM x BN/WN tile (ETM x TN blocks).
+  constexpr int GW = WM * WN;
+  constexpr int NW = GW * KG;
+  constexpr int TM = BM / WM / 32;
+  constexpr int EWM = WM * KG;
+  constexpr int WTM = BM / EWM;  // epilogue wave tile rows
   constexpr int WTN = BN / WN;
-  constexpr int TM = WTM / 32;
+  constexpr int ETM = WTM / 32;
   constexpr int TN = WTN / 32;
-  constexpr int STAGE = (BM + BN) * kBK * 2;
+  constexpr int STAGE = KG * (BM + BN) * kBK * 2;
   static_assert(NB >= 3, "the norm epilogue uses the third ring buffer");
   static_assert((BM * WN + BM + 1) * 4 <= STAGE, "row partials fit in one stage buffer");
   char* const sb0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
@@ -452,7 +473,8 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
   int* const sflag = reinterpret_cast<int*>(sinv + BM);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / WN;
+  const int kgrp = KG == 1 ? 0 : wave / GW;  // K group of the main loop
+  const int wm = ((KG == 1 ? wave : wave % GW) / WN) * KG + kgrp;  // epilogue row block
   const int wn = wave % WN;
   const float g0 = gemma ? 1.0f : 0.0f;
 
@@ -463,12 +485,13 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
   constexpr int LPR = WTN / 4;   // lanes per staged row (8 or 16: one DPP row or half-row)
   constexpr int RPI = 64 / LPR;  // rows per staged read
   constexpr int NR = 16 / RPI;   // staged reads per 16-row slice
-  constexpr int KEEP = TM * 2 * NR;               // float4 of r + y per lane
+  constexpr int KEEP = ETM * 2 * NR;              // float4 of r + y per lane
   // Residual loaded before the main loop when it fits: 64 registers per lane with two waves
   // per SIMD (256 registers each), 128 with one wave per SIMD (512).
-  constexpr bool PREFETCH = KEEP <= (NW == 4 ? 32 : 16);
+  constexpr bool PREFETCH = KG == 1 && KEEP <= (NW == 4 ? 32 : 16);
   constexpr int TPR = NW * 64 / BM;               // threads per row for the slot reads
   static_assert(TPR >= 1 && TPR <= WN, "slot-read partials reuse the row-partial buffer");
+  static_assert(KG == 1 || TM % 2 == 0, "K groups hand over half of their rows");
 
   for (int round = 0; round * rows_per_round < tiles_m; ++round) {
     const int rows_here = min(rows_per_round, tiles_m - round * rows_per_round);
@@ -502,7 +525,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
     if constexpr (PREFETCH) {
       const int pcol = n0 + wn * WTN + rcol_of(lane);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < ETM; ++i)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -513,13 +536,63 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
           }
     }
 
-    const TileAcc<TM, TN> tacc =
-        tile_mainloop<BM, BN, NB, WM, WN>(A, Bp, M, N, K, m0, n0, 0, K / kBK);
-    const auto& acc = tacc.v;
+    const TileAcc<TM, TN> part_acc =
+        tile_mainloop<BM, BN, NB, WM, WN, KG>(A, Bp, M, N, K, m0, n0, 0, K / (kBK * KG));
     // The ring's trailing refills (direct-to-LDS loads) have landed and every wave is past its
     // last fragment read before the stage buffers are reused below.
     __builtin_amdgcn_s_waitcnt(PR_VMCNT(0));
     __syncthreads();
+    TileAcc<ETM, TN> tacc;
+    if constexpr (KG == 1) {
+      tacc = part_acc;
+    } else {
+      // Waves w and w + GW computed the same wave tile over the two halves of K.  Each hands
+      // the other half of its rows to its partner through LDS (one 16-byte store per lane and
+      // block element group) and adds the partner's half to the rows it keeps: group 0 keeps
+      // the upper half, group 1 the lower.  The two-term sum is the same in either order.
+      constexpr int RB = ETM * TN * 16 * 64 * 4;  // bytes handed over per wave
+      constexpr int PER = STAGE / RB;             // regions per ring buffer
+      static_assert(PER >= 1 && NB * PER >= NW, "hand-over regions fit in the ring");
+      auto region = [&](int w) -> float4* {
+        char* b = w / PER == 0 ? sb0
+                               : (w / PER == 1 ? sb1
+                                               : ring_buffer<2, STAGE, BM, BN, NB, WM, WN>());
+        return reinterpret_cast<float4*>(b + (w % PER) * RB);
+      };
+      static_assert(NW <= 3 * PER, "hand-over regions use the first three ring buffers");
+      float4* mine = region(wave);
+      const float4* theirs = region(wave < GW ? wave + GW : wave - GW);
+      auto hand_over = [&](int i0) {
+#pragma unroll
+        for (int i = 0; i < ETM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+              mine[((i * TN + j) * 4 + e4) * 64 + lane] =
+                  make_float4(part_acc.v[i0 + i][j][4 * e4], part_acc.v[i0 + i][j][4 * e4 + 1],
+                              part_acc.v[i0 + i][j][4 * e4 + 2], part_acc.v[i0 + i][j][4 * e4 + 3]);
+      };
+      auto combine = [&](int i0) {
+#pragma unroll
+        for (int i = 0; i < ETM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const float4 o = theirs[((i * TN + j) * 4 + e4) * 64 + lane];
+              tacc.v[i][j][4 * e4] = part_acc.v[i0 + i][j][4 * e4] + o.x;
+              tacc.v[i][j][4 * e4 + 1] = part_acc.v[i0 + i][j][4 * e4 + 1] + o.y;
+              tacc.v[i][j][4 * e4 + 2] = part_acc.v[i0 + i][j][4 * e4 + 2] + o.z;
+              tacc.v[i][j][4 * e4 + 3] = part_acc.v[i0 + i][j][4 * e4 + 3] + o.w;
+            }
+      };
+      if (kgrp == 0) hand_over(ETM); else hand_over(0);
+      __syncthreads();
+      if (kgrp == 0) combine(0); else combine(ETM);
+      __syncthreads();  // hand-over regions read before the epilogue reuses the buffers
+    }
+    const auto& acc = tacc.v;
 
     // The epilogue's per-lane offsets are formed here, from an opaque copy of the lane id, so
     // that they are not hoisted out of the round loop and kept live across the main loop.
@@ -539,11 +612,11 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
     };
     if constexpr (!PREFETCH) load_slice(0);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < ETM; ++i) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         if constexpr (!PREFETCH)
-          if (i * 2 + h + 1 < TM * 2) load_slice(i * 2 + h + 1);
+          if (i * 2 + h + 1 < ETM * 2) load_slice(i * 2 + h + 1);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -649,7 +722,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
       const float4 g = *reinterpret_cast<const float4*>(w + col);
       const float gx = g.x + g0, gy = g.y + g0, gz = g.z + g0, gw = g.w + g0;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < ETM; ++i)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -1047,13 +1120,13 @@ int resident_workgroups(Kern kern, int threads, int* out) {
   return PR_OK;
 }
 
-template <int BM, int BN, int NB, int WM, int WN>
+template <int BM, int BN, int NB, int WM, int WN, int KG>
 int launch_single_t(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
                     uint16_t* out, unsigned long long* slots, unsigned* sync, int M, int N,
                     int K, float eps, int gemma, unsigned epoch, unsigned read_epoch,
                     unsigned spin_limit, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  auto kern = gemm_add_rmsnorm_kernel<BM, BN, NB, WM, WN>;
-  constexpr int threads = WM * WN * 64;
+  auto kern = gemm_add_rmsnorm_kernel<BM, BN, NB, WM, WN, KG>;
+  constexpr int threads = WM * WN * KG * 64;
   static int resident = 0;  // per instantiation; the library runs on one kind of device
   if (resident == 0) PR_TRY_K(resident_workgroups(kern, threads, &resident));
   const int tiles_m = (M + BM - 1) / BM;
@@ -1109,7 +1182,8 @@ int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, i
   hipEvent_t t0 = static_cast<hipEvent_t>(start_timing);
   hipEvent_t t1 = static_cast<hipEvent_t>(stop_timing);
   if (M <= 0) return PR_OK;
-  if (K % (2 * kBK * cfg.split) != 0 || N % 64 != 0 || (bf16_out && cfg.split != 1))
+  if (K % (2 * kBK * cfg.split) != 0 || N % 64 != 0 || (bf16_out && cfg.split != 1) ||
+      cfg.kgroups != 1)
     return fail(PR_ERR_SHAPE, "projection shape M=%d N=%d K=%d split=%d not supported", M, N, K,
                 cfg.split);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1135,21 +1209,26 @@ int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, con
   hipEvent_t t0 = static_cast<hipEvent_t>(start_timing);
   hipEvent_t t1 = static_cast<hipEvent_t>(stop_timing);
   if (M <= 0) return PR_OK;
+  const bool r256x128 = cfg.bm == 256 && cfg.bn == 128;
   if (K % (2 * kBK) != 0 || N % cfg.bn != 0 || N / cfg.bn > 64 || cfg.split != 1 ||
-      (cfg.waves != 8 && !(cfg.waves == 4 && cfg.bm == 256 && cfg.bn == 128)))
-    return fail(PR_ERR_SHAPE, "single launch: N=%d K=%d with tile %dx%d split %d, %d waves not "
-                "supported", N, K, cfg.bm, cfg.bn, cfg.split, cfg.waves);
+      (cfg.waves != 8 && !(cfg.waves == 4 && r256x128)) ||
+      (cfg.kgroups != 1 && !(cfg.kgroups == 2 && cfg.waves == 8 && r256x128)))
+    return fail(PR_ERR_SHAPE, "single launch: N=%d K=%d with tile %dx%d split %d, %d waves, %d K "
+                "groups not supported", N, K, cfg.bm, cfg.bn, cfg.split, cfg.waves, cfg.kgroups);
   if (cfg.bm == 256 && cfg.bn == 256)
-    return launch_single_t<256, 256, 5, 2, 4>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
+    return launch_single_t<256, 256, 5, 2, 4, 1>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
                                               epoch, read_epoch, spin_limit, s, t0, t1);
+  if (r256x128 && cfg.kgroups == 2)
+    return launch_single_t<256, 128, 3, 2, 2, 2>(x, Wp, r, w, out, slots, sync, M, N, K, eps,
+                                                 gemma, epoch, read_epoch, spin_limit, s, t0, t1);
   if (cfg.bm == 256 && cfg.bn == 128 && cfg.waves == 4)
-    return launch_single_t<256, 128, 4, 2, 2>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
+    return launch_single_t<256, 128, 4, 2, 2, 1>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
                                               epoch, read_epoch, spin_limit, s, t0, t1);
   if (cfg.bm == 256 && cfg.bn == 128)
-    return launch_single_t<256, 128, 4, 4, 2>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
+    return launch_single_t<256, 128, 4, 4, 2, 1>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
                                               epoch, read_epoch, spin_limit, s, t0, t1);
   if (cfg.bm == 128 && cfg.bn == 128)
-    return launch_single_t<128, 128, 4, 2, 4>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
+    return launch_single_t<128, 128, 4, 2, 4, 1>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
                                               epoch, read_epoch, spin_limit, s, t0, t1);
   return fail(PR_ERR_INVALID_ARG, "single launch: no tile %dx%d", cfg.bm, cfg.bn);
 }

@@ -229,6 +229,7 @@ int run_conventional(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, 
   g.split = d.split_k;
   g.waves = d.gemm_waves;
   g.stages = d.gemm_stages;
+  g.kgroups = d.gemm_kgroups;
   const long long plane = (long long)T * H;
   if (g.split == 1) {
     PR_TRY(grow(&c->conv, &c->conv_bytes, (size_t)plane * 2));
@@ -263,6 +264,7 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
   g.split = d.split_k;
   g.waves = d.gemm_waves;
   g.stages = d.gemm_stages;
+  g.kgroups = d.gemm_kgroups;
   const int rows_max = std::min(mc, T);
   const long long plane = (long long)rows_max * H;  // elements of one partial plane
   const size_t slot_elems = (size_t)plane * g.split;
@@ -365,6 +367,7 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
   g.split = d.split_k;
   g.waves = d.gemm_waves;
   g.stages = d.gemm_stages;
+  g.kgroups = d.gemm_kgroups;
   if (fault_injected()) return fail(PR_ERR_HIP, "injected launch failure (PR_FAULT_INJECT)");
   // Launches cover at most 2^30 elements of x each (32-bit offsets in the kernel), in whole
   // tile rows; each launch is independent (rows do not interact).

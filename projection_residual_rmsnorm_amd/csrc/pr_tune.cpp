@@ -170,7 +170,8 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
     return v != nullptr && v[0] != '\0';
   };
   const bool forced_cfg = env_on("PR_FORCE_TILE") || env_on("PR_FORCE_SPLIT") ||
-                          env_on("PR_FORCE_WAVES") || env_on("PR_FORCE_STAGES");
+                          env_on("PR_FORCE_WAVES") || env_on("PR_FORCE_STAGES") ||
+                          env_on("PR_FORCE_KGROUPS");
   const int ncols = 3 + nmc;
   std::vector<double> t_conv(ngroups * nT, -1), t_fused(ngroups * nT, -1),
       spread(ngroups * nT, 0);

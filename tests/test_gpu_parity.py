@@ -26,7 +26,8 @@ if torch.cuda.is_available():
 @pytest.fixture(autouse=True)
 def _env(monkeypatch):
     for k in ("PR_MICROCHUNK_TOKENS", "PR_THRESHOLD_TOKENS", "PR_FORCE_TILE", "PR_FORCE_SPLIT",
-              "PR_FORCE_WAVES", "PR_FORCE_STAGES", "PR_FORCE_ADDNORM_WGS", "PR_DEBUG_POISON",
+              "PR_FORCE_WAVES", "PR_FORCE_STAGES", "PR_FORCE_KGROUPS", "PR_FORCE_ADDNORM_WGS",
+              "PR_DEBUG_POISON",
               "PR_DEBUG_DELAY", "PR_SPIN_LIMIT",
               "PR_FAULT_INJECT"):
         monkeypatch.delenv(k, raising=False)
@@ -95,16 +96,18 @@ def test_random_parity_small(T, K, H, kind):
 
 
 # ------------------------------------------------------------- single-launch fused path
-# (tile, waves per workgroup) of every single-launch instantiation
-SINGLE_CFGS = [("256x256", 8), ("256x128", 8), ("256x128", 4), ("128x128", 8)]
+# (tile, waves per workgroup, K groups) of every single-launch instantiation
+SINGLE_CFGS = [("256x256", 8, 1), ("256x128", 8, 1), ("256x128", 4, 1), ("256x128", 8, 2),
+               ("128x128", 8, 1)]
 
 
-@pytest.mark.parametrize("tile,waves", SINGLE_CFGS)
-def test_single_launch_integer_projection_is_exact(monkeypatch, tile, waves):
+@pytest.mark.parametrize("tile,waves,kgroups", SINGLE_CFGS)
+def test_single_launch_integer_projection_is_exact(monkeypatch, tile, waves, kgroups):
     """Small integers: the fp32 residual is exact, so it must match bitwise.  T=300 leaves a
     ragged last tile row; H=768 is 3 or 6 tile columns."""
     monkeypatch.setenv("PR_FORCE_TILE", tile)
     monkeypatch.setenv("PR_FORCE_WAVES", str(waves))
+    monkeypatch.setenv("PR_FORCE_KGROUPS", str(kgroups))
     d = synth.integer_inputs(300, 1024, 768, seed=3)
     dev = Device(d)
     r_dev, out_bits = dev.run("single")
@@ -115,30 +118,35 @@ def test_single_launch_integer_projection_is_exact(monkeypatch, tile, waves):
     assert oracle.within_tolerance(err), err
 
 
-@pytest.mark.parametrize("tile,waves", SINGLE_CFGS)
+@pytest.mark.parametrize("tile,waves,kgroups", SINGLE_CFGS)
 @pytest.mark.parametrize("kind", [0, 1])
 @pytest.mark.parametrize("T,K,H", [(300, 512, 768), (64, 512, 512), (1, 256, 512),
                                    (513, 1024, 256)])
-def test_single_launch_random_parity_small(monkeypatch, tile, waves, kind, T, K, H):
+def test_single_launch_random_parity_small(monkeypatch, tile, waves, kgroups, kind, T, K, H):
     if H % int(tile.split("x")[1]):
         pytest.skip("tile columns do not divide H")
     monkeypatch.setenv("PR_FORCE_TILE", tile)
     monkeypatch.setenv("PR_FORCE_WAVES", str(waves))
+    monkeypatch.setenv("PR_FORCE_KGROUPS", str(kgroups))
     d = synth.make_custom(T, K, H, seed=T + K, norm_kind=kind, eps=1e-5)
     dev = Device(d)
     r_dev, out_bits = dev.run("single")
     _check(d, r_dev, out_bits, "fused")
 
 
-@pytest.mark.parametrize("tile,waves,T,H", [("256x128", 8, 4096, 4096), ("256x128", 4, 4096, 4096),
-                                            ("128x128", 8, 8192, 2048), ("256x256", 8, 4100, 8192)])
-def test_single_launch_several_rounds(monkeypatch, tile, waves, T, H):
+@pytest.mark.parametrize("tile,waves,kgroups,T,H", [("256x128", 8, 1, 4096, 4096),
+                                                    ("256x128", 4, 1, 4096, 4096),
+                                                    ("256x128", 8, 2, 4096, 4096),
+                                                    ("128x128", 8, 1, 8192, 2048),
+                                                    ("256x256", 8, 1, 4100, 8192)])
+def test_single_launch_several_rounds(monkeypatch, tile, waves, kgroups, T, H):
     """More tiles than resident workgroups: the launch runs several rounds of whole tile rows
     (256x128: 512 tiles in 2 rounds; 128x128: 1024 tiles in 2; 256x256: 17 x 32 tiles, the
     last round one ragged tile row)."""
     monkeypatch.setenv("PR_FORCE_TILE", tile)
     monkeypatch.setenv("PR_FORCE_WAVES", str(waves))
-    print(f"single launch {tile} T={T} H={H}", flush=True)
+    monkeypatch.setenv("PR_FORCE_KGROUPS", str(kgroups))
+    print(f"single launch {tile} {waves} waves {kgroups} K groups T={T} H={H}", flush=True)
     d = synth.make_custom(T, 256, H, seed=11)
     dev = Device(d)
     r_dev, out_bits = dev.run("single")

@@ -17,7 +17,7 @@ A = 1 << 20  # a fake, 16-byte aligned address for pointer arguments
 @pytest.fixture(autouse=True)
 def _clean_env(monkeypatch):
     for k in ("PR_MICROCHUNK_TOKENS", "PR_THRESHOLD_TOKENS", "PR_LOG", "PR_FORCE_TILE",
-              "PR_FORCE_SPLIT", "PR_FORCE_WAVES", "PR_FORCE_STAGES"):
+              "PR_FORCE_SPLIT", "PR_FORCE_WAVES", "PR_FORCE_STAGES", "PR_FORCE_KGROUPS"):
         monkeypatch.delenv(k, raising=False)
     pr.pr_clear_tuning()
     yield
