@@ -498,13 +498,17 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     const int count = rows_here * tiles_n;
     if ((int)blockIdx.x >= count) continue;  // uniform over the workgroup
     int tm, tn;
-    if (rows_here % kNumXCDs == 0) {
-      // Whole tile rows per XCD (workgroup b runs on XCD b % 8): a row's tiles finish
-      // together, and an XCD that runs slower delays only its own rows.
-      const int per_xcd = rows_here / kNumXCDs;
-      const int j = blockIdx.x / kNumXCDs;
-      tm = (blockIdx.x % kNumXCDs) * per_xcd + j / tiles_n;
-      tn = j % tiles_n;
+    constexpr int XG = 2;  // XCDs per tile row
+    if ((rows_here * XG) % kNumXCDs == 0 && tiles_n % XG == 0) {
+      // Each pair of XCDs computes whole tile rows, each XCD half of every row's columns
+      // (workgroup b runs on XCD b % 8): a row's tiles finish together, an XCD that runs
+      // slower delays only its pair's rows, and each XCD reads half of the weight.
+      const int xcd = blockIdx.x % kNumXCDs;
+      const int rows_g = rows_here * XG / kNumXCDs;  // tile rows of this XCD pair
+      const int cols_x = tiles_n / XG;               // column tiles per XCD
+      const int j = blockIdx.x / kNumXCDs;            // 0 .. rows_g * cols_x - 1
+      tm = (xcd / XG) * rows_g + j / cols_x;
+      tn = (xcd % XG) * cols_x + j % cols_x;
     } else {
       tile_coords(xcd_logical(blockIdx.x, count), rows_here, tiles_n, &tm, &tn);
     }
