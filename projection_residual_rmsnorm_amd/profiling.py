@@ -6,6 +6,9 @@
         <write counter_collection.csv> --kernel "<kernel name prefix>" --out <traffic.json> \
         --command "<commands>"
 
+    python -m projection_residual_rmsnorm_amd.profiling counters <counter_collection.csv> <out.md> \
+        --kernel "<kernel name prefix>" [--kernel ...] [--grid N] --command "<command>"
+
 `traffic` calibrates FETCH_SIZE and WRITE_SIZE (KiB per dispatch) against the plain 1 GiB
 device copies that `bench.py --copy-calibration` runs in the same process: the factor that
 turns each counter into bytes is (1 GiB) / (the counter's reading for one such copy).
@@ -81,6 +84,93 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, grid: int = 0) -> dict:
             "gemm_bytes_per_launch": fetched + written}
 
 
+CU_COUNT = 256
+SIMDS_PER_CU = 4
+MOP_FLOPS = 512  # SQ_INSTS_VALU_MFMA_MOPS_*: one count per 512 floating-point operations
+
+
+def counter_table(path: str, kernels: List[str], grid: int = 0) -> Dict[str, dict]:
+    """Per kernel (name prefix), the mean of every collected counter over its dispatches, and
+    the dispatch duration when the file has timestamps (a run with --kernel-trace)."""
+    per: Dict[str, Dict[int, dict]] = {}
+    for r in csv.DictReader(open(path)):
+        name = short_name(r["Kernel_Name"])
+        k = next((k for k in kernels if name.startswith(k)), None)
+        if k is None or (grid and int(r["Grid_Size"]) != grid):
+            continue
+        d = per.setdefault(k, {}).setdefault(int(r["Dispatch_Id"]), {"name": name})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            d["duration_ns"] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {}
+    for k, disp in per.items():
+        names = sorted({c for d in disp.values() for c in d if c != "name"})
+        out[k] = {"kernel": sorted({d["name"] for d in disp.values()}),
+                  "dispatches": len(disp),
+                  "mean": {c: statistics.mean(d[c] for d in disp.values() if c in d)
+                           for c in names}}
+    return out
+
+
+NAMEPLATE_GHZ = 2.4
+XCDS = 8
+
+
+def derived(mean: Dict[str, float]) -> Dict[str, float]:
+    """Ratios the counters support.
+
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs (one 32x32x16 bf16 MFMA keeps a SIMD
+    busy 32 cycles, so the sum equals flops / 1024).  GRBM_GUI_ACTIVE is summed over the 8
+    XCDs (it reads about 8 x the shader clock x the dispatch time) and spans the counter
+    window, which is a few microseconds longer than the dispatch.
+      mfma_util_nameplate: busy cycles / (SIMDs x duration x 2.4 GHz), the fraction of the
+        dense bf16 peak;
+      mfma_util_active: busy cycles / (SIMDs x GRBM_GUI_ACTIVE / 8), against the cycles the
+        GPU clock actually ran;
+      lds_bank_conflict_frac: conflict cycles / LDS-active cycles;
+      lds_active_frac: LDS-active cycles per CU / (GRBM_GUI_ACTIVE / 8)."""
+    out = {}
+    simds = CU_COUNT * SIMDS_PER_CU
+    busy, active = mean.get("SQ_VALU_MFMA_BUSY_CYCLES"), mean.get("GRBM_GUI_ACTIVE")
+    dur = mean.get("duration_ns")
+    if dur:
+        out["duration_us"] = dur / 1e3
+    if active and dur:
+        out["gui_active_per_xcd_GHz"] = active / XCDS / dur
+    if busy is not None and dur:
+        out["mfma_util_nameplate"] = busy / (simds * dur * NAMEPLATE_GHZ)
+    if busy is not None and active:
+        out["mfma_util_active"] = busy / (simds * active / XCDS)
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:
+        out["mfma_bf16_flops"] = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * MOP_FLOPS
+        if dur:
+            out["mfma_bf16_TFLOPs"] = out["mfma_bf16_flops"] / dur / 1e3
+    if "SQ_LDS_BANK_CONFLICT" in mean and mean.get("SQ_LDS_IDX_ACTIVE"):
+        out["lds_bank_conflict_frac"] = mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_LDS_IDX_ACTIVE"]
+        if active:
+            out["lds_active_frac"] = mean["SQ_LDS_IDX_ACTIVE"] / CU_COUNT / (active / XCDS)
+    return out
+
+
+def counters_summary(path: str, kernels: List[str], grid: int, command: str) -> str:
+    tab = counter_table(path, kernels, grid)
+    lines = ["# rocprofv3 counters per dispatch", "", "Command:", "", "```", command, "```", ""]
+    for k in kernels:
+        if k not in tab:
+            lines += [f"`{k}`: no dispatches in the file", ""]
+            continue
+        t = tab[k]
+        lines += [f"## `{', '.join(t['kernel'])}` ({t['dispatches']} dispatches)", "",
+                  "| counter | mean per dispatch |", "|---|---|"]
+        lines += [f"| {c} | {v:.6g} |" for c, v in t["mean"].items()]
+        dv = derived(t["mean"])
+        if dv:
+            lines += ["", "| derived | value |", "|---|---|"]
+            lines += [f"| {c} | {v:.4g} |" for c, v in dv.items()]
+        lines.append("")
+    return "\n".join(lines)
+
+
 def _code_only(text: str) -> str:
     """The source without comments, whitespace runs collapsed (string and character literals
     are kept as written)."""
@@ -129,8 +219,17 @@ def main() -> None:
     t.add_argument("--source", required=True, help="kernel source the counters were taken on")
     t.add_argument("--grid", type=int, default=0,
                    help="only dispatches of this grid size (threads), e.g. one chunk's launch")
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("out")
+    c.add_argument("--kernel", action="append", required=True)
+    c.add_argument("--grid", type=int, default=0)
+    c.add_argument("--command", required=True)
     a = ap.parse_args()
-    if a.cmd == "stats":
+    if a.cmd == "counters":
+        with open(a.out, "w") as f:
+            f.write(counters_summary(a.csv, a.kernel, a.grid, a.command))
+    elif a.cmd == "stats":
         with open(a.out, "w") as f:
             f.write(stats_summary(a.csv, a.command))
     else:

@@ -397,3 +397,35 @@ def test_traffic_digest_ignores_comments_only(tmp_path):
     c.write_text('int f(int x) { return x + 2; }\nconst char* s = "//";\n')
     assert source_digest(str(a)) == source_digest(str(b))
     assert source_digest(str(a)) != source_digest(str(c))
+
+
+def test_counter_summary_derivations(tmp_path):
+    """Per-dispatch means and the derived MFMA / LDS ratios of a counter file (rocprofv3's
+    counter_collection.csv layout: one row per dispatch and counter)."""
+    from projection_residual_rmsnorm_amd.profiling import counter_table, derived
+    path = tmp_path / "c.csv"
+    cols = ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value",
+            "Start_Timestamp", "End_Timestamp"]
+    lines = [",".join(cols)]
+    # two dispatches of one kernel, 100 us each; busy = half of 1024 SIMDs x 100 us x 2.4 GHz
+    for disp in (1, 2):
+        for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 1024 * 100e3 * 2.4),
+                     ("GRBM_GUI_ACTIVE", 8 * 100e3 * 2.0),
+                     ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e6),
+                     ("SQ_LDS_IDX_ACTIVE", 256 * 1000.0), ("SQ_LDS_BANK_CONFLICT", 256 * 250.0)):
+            lines.append(f'{disp},65536,"void pr::gemm_add_rmsnorm_kernel<256, 128, 4, 2, 2, 1>(x)",'
+                         f'{c},{v},1000,{1000 + 100_000}')
+    lines.append('3,256,"void pr::fill_nan_kernel(x)",GRBM_GUI_ACTIVE,5,0,10')
+    path.write_text("\n".join(lines) + "\n")
+    tab = counter_table(str(path), ["gemm_add_rmsnorm_kernel"])
+    t = tab["gemm_add_rmsnorm_kernel"]
+    assert t["dispatches"] == 2
+    dv = derived(t["mean"])
+    assert abs(dv["duration_us"] - 100.0) < 1e-9
+    assert abs(dv["mfma_util_nameplate"] - 0.5) < 1e-9
+    assert abs(dv["mfma_util_active"] - 0.6) < 1e-9      # the clock ran at 2.0 of 2.4 GHz
+    assert abs(dv["gui_active_per_xcd_GHz"] - 2.0) < 1e-9
+    assert dv["mfma_bf16_flops"] == 512e6
+    assert abs(dv["lds_bank_conflict_frac"] - 0.25) < 1e-12
+    assert abs(dv["lds_active_frac"] - 1000.0 / 200e3) < 1e-12
+    assert counter_table(str(path), ["gemm_add_rmsnorm_kernel"], grid=256) == {}
