@@ -153,6 +153,13 @@ int proj_add_rmsnorm_unfused(const uint16_t* x, const uint16_t* W, float* residu
  * is taken in another order).  Uses a device workspace of T * H / 128 64-bit slots and
  * 2 + T / 128 counters, shared by all calls on the device (calls on one device are
  * sequential, as for every entry point).
+ *
+ * A second form splits the K range of each 256 x 256 tile over a pair of workgroups, which
+ * swap partial sums before the residual add (reached with the debug overrides
+ * PR_FORCE_TILE=256x256 PR_FORCE_WAVES=8 PR_FORCE_SPLIT=2; never chosen by default, as it
+ * measured slower).  It needs H a multiple of 256 and adds 64 MiB of exchange regions and
+ * 4 * ceil(T / 256) * H / 256 64-bit words to the workspace; its results agree with the first
+ * form within rounding.
  */
 int proj_add_rmsnorm_single_launch(const uint16_t* x, const uint16_t* W, float* residual_inout,
                                    const float* norm_w, float eps, int T, int K, int H,

@@ -83,7 +83,8 @@ static bool env_set(const char* name) {
 
 // Debug override of the projection tile: PR_FORCE_TILE="BMxBN" (an instantiated tile),
 // PR_FORCE_WAVES=4|8, PR_FORCE_STAGES=N (an instantiated ring depth of the tile) and
-// PR_FORCE_SPLIT=S (S must divide K/64).  Used by tests to reach every kernel variant.
+// PR_FORCE_SPLIT=S (S must divide K/64; for the single launch 1, or 2 for the pair form with
+// the 256x256 tile and 8 waves).  Used by tests to reach every kernel variant.
 static int apply_forced_tile(int K, GemmCfg* g) {
   const char* t = std::getenv("PR_FORCE_TILE");
   if (t != nullptr && t[0] != '\0') {

@@ -73,19 +73,26 @@ int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_s
                        void* done_event = nullptr, void* start_timing = nullptr,
                        void* stop_timing = nullptr);
 
-// Projection, residual add and RMSNorm of M rows in one launch (tile cfg.bm x cfg.bn, split 1,
-// 8 waves; N % cfg.bn == 0, N / cfg.bn <= 64).  slots: (N / cfg.bn) * M 64-bit row-partial
-// slots; a slot holding `epoch` in its high word is taken as written by this launch, so epoch
-// must differ from every value the slots held before (start from a zeroed buffer, epoch >= 1).
-// The row reads look for read_epoch (= epoch; any other value makes every wait give up).
-// sync: 2 + ceil(M / cfg.bm) words, zero before the launch and zero again after it, except
-// word 0, which collects status bits (bit 0: a wait gave up after spin_limit polls).
+// Projection, residual add and RMSNorm of M rows in one launch (tile cfg.bm x cfg.bn, 8 waves
+// or the 4-wave 256x128 form; N % cfg.bn == 0, N / cfg.bn <= 64).  slots: (N / cfg.bn) * M
+// 64-bit row-partial slots; a slot holding `epoch` in its high word is taken as written by
+// this launch, so epoch must differ from every value the slots held before (start from a
+// zeroed buffer, epoch >= 1).  The row reads look for read_epoch (= epoch; any other value
+// makes every wait give up).  sync: 2 + ceil(M / cfg.bm) words (split 2: 2 + 2 ceil(M / 256)),
+// zero before the launch and zero again after it, except word 0, which collects status bits
+// (bit 0: a wait gave up after spin_limit polls).
+// cfg.split == 2 selects the pair form (256x256, 8 waves, K halves on two workgroups):
+// pair_words holds 4 * ceil(M / 256) * (N / 256) 64-bit words with the same epoch rule as the
+// slots, and xbuf xbuf_words 64-bit words of exchange regions (16384 per workgroup of a round,
+// twice that when the launch takes several rounds).
 int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
                             uint16_t* out, unsigned long long* slots, unsigned* sync, int M,
                             int N, int K, const GemmCfg& cfg, float eps, int gemma,
                             unsigned epoch, unsigned read_epoch, unsigned spin_limit,
                             void* stream, void* start_timing = nullptr,
-                            void* stop_timing = nullptr);
+                            void* stop_timing = nullptr,
+                            unsigned long long* pair_words = nullptr,
+                            unsigned long long* xbuf = nullptr, size_t xbuf_words = 0);
 
 int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,
                           void* stream);

@@ -23,6 +23,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void global_cvoid_t;
 
@@ -770,6 +771,410 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
 }
 
 // --------------------------------------------------------------------------------------------
+// Single launch with the K range of each 256 x 256 tile split over a pair of workgroups.
+//
+// When a shape has fewer 256 x 256 tiles than the GPU has CUs, a workgroup pair shares each
+// tile: workgroup h (0 or 1) runs the main loop over K half h, so every CU works on a large
+// tile (fewer operand bytes per flop than a 256 x 128 tile over the whole K).  The pair then
+// swaps partial sums: h keeps tile rows [128 h, 128 h + 128) and hands the other 128 rows'
+// partial to its partner through an exchange region, announced by an epoch-tagged ready word
+// stored after the writes have completed.  The pair normally sits on one XCD (workgroups b
+// and b ^ 8); each workgroup publishes its XCD id when its round starts, and a writer that
+// finds its partner's id (with this launch's epoch) equal to its own writes the region with
+// plain stores, which land in the XCD's shared L2, and says so in its ready word; the reader
+// then drops its own L1 copy of any earlier round's region and reads with plain loads from
+// that L2.  Otherwise both sides use device-scope accesses, which reach the memory-side
+// coherence point, so the exchange is correct wherever the pair runs.  Each workgroup adds
+// the two partials of its rows
+// (a two-term fp32 sum, the same in either order) and runs the residual add and RMSNorm of
+// its 128 x 256 block with the row-partial slot protocol of gemm_add_rmsnorm_kernel: its block
+// row has tiles_n column tiles, one slot per row and column tile, and one counter per
+// 128-row block.
+//
+// The four waves that hand their rows over load the residual of the kept rows into LDS (ring
+// buffers 0..3, 32 rows of 1 KiB each) while the exchange completes; the four waves that keep
+// their rows add the partner's partial, form r + y in place in LDS and the row sums; all eight
+// waves then write the residual, wait for the row block and write the output from LDS.
+//
+// Exchange regions: `xbuf` holds 128 KiB per workgroup and round parity (the region a
+// workgroup writes in round q is rewritten in round q + 2 only after the partner's round q + 1
+// ready word, i.e. after the partner finished reading it).  pwords: four 64-bit words per tile
+// of the launch, per half h the XCD-id word [4 t + 2 h] and the ready word [4 t + 2 h + 1],
+// each {epoch of the launch that wrote it, value}.
+// --------------------------------------------------------------------------------------------
+template <int NB>
+__global__ void __launch_bounds__(512, 1)
+    gemm_add_rmsnorm_pair_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp,
+                                 float* __restrict__ R, const float* __restrict__ w,
+                                 uint16_t* __restrict__ out, unsigned long long* __restrict__ slots,
+                                 unsigned* __restrict__ sync,
+                                 unsigned long long* __restrict__ pwords,
+                                 unsigned long long* __restrict__ xbuf, int M, int N, int K,
+                                 int tiles_m, int tiles_n, int rows_per_round, float eps,
+                                 int gemma, unsigned epoch, unsigned read_epoch,
+                                 unsigned spin_limit) {
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
+  constexpr int TM = 4, TN = 2;       // 128 x 64 wave tiles
+  constexpr int HB = 128;             // rows kept per workgroup
+  constexpr int STAGE = (BM + BN) * kBK * 2;  // 32 KiB
+  constexpr int XW = TM * TN * 8 * 64;        // 64-bit exchange words per wave (32 KiB)
+  static_assert(NB == 5 && STAGE == 32 * 1024, "residual in buffers 0..3, staging in 4");
+  constexpr int EP_LD = 64 + 4;
+  constexpr int EP_BYTES = 16 * EP_LD * 4;
+  static_assert(4 * EP_BYTES + (HB * WN + HB + 3) * 4 <= STAGE, "staging fits in buffer 4");
+  // Residual buffers 0..3 (separate LDS objects), chosen by a wave-uniform index.
+  auto rbuf = [](int u) -> char* {
+    char* const b0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
+    char* const b1 = ring_buffer<1, STAGE, BM, BN, NB, WM, WN>();
+    char* const b2 = ring_buffer<2, STAGE, BM, BN, NB, WM, WN>();
+    char* const b3 = ring_buffer<3, STAGE, BM, BN, NB, WM, WN>();
+    return u == 0 ? b0 : (u == 1 ? b1 : (u == 2 ? b2 : b3));
+  };
+  char* const sb4 = ring_buffer<4, STAGE, BM, BN, NB, WM, WN>();
+  float* const sred = reinterpret_cast<float*>(sb4 + 4 * EP_BYTES);
+  float* const sinv = sred + HB * WN;
+  int* const sflag = reinterpret_cast<int*>(sinv + HB);
+  int* const smode = sflag + 1;  // this workgroup writes its hand-over with plain stores
+  int* const spart = sflag + 2;  // the partner wrote its hand-over with plain stores
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const float g0 = gemma ? 1.0f : 0.0f;
+
+  for (int round = 0; round * rows_per_round < tiles_m; ++round) {
+    const int rows_here = min(rows_per_round, tiles_m - round * rows_per_round);
+    const int tiles = rows_here * tiles_n;
+    const int count = 2 * tiles;
+    if ((int)blockIdx.x >= count) continue;  // uniform over the workgroup
+    // Pairs: workgroups b and b ^ 8 (same XCD, b % 8) within each group of 16, else b and
+    // b ^ 1.  q numbers the tiles so that q % 8 is the pair's XCD.
+    const int b = blockIdx.x;
+    const int full = count / 16 * 16;
+    int h, q, partner;
+    if (b < full) {
+      h = (b >> 3) & 1;
+      q = (b >> 4) * 8 + (b & 7);
+      partner = b ^ 8;
+    } else {
+      h = b & 1;
+      q = b >> 1;
+      partner = b ^ 1;
+    }
+    int tm, tn;
+    if (full == count && (rows_here * 2) % kNumXCDs == 0 && tiles_n % 2 == 0) {
+      // Each pair of XCDs computes whole tile rows, each XCD half of every row's columns.
+      const int xcd = q % kNumXCDs;
+      const int rows_g = rows_here * 2 / kNumXCDs;
+      const int cols_x = tiles_n / 2;
+      const int j = q / kNumXCDs;
+      tm = (xcd / 2) * rows_g + j / cols_x;
+      tn = (xcd % 2) * cols_x + j % cols_x;
+    } else {
+      tile_coords(xcd_logical(q, tiles), rows_here, tiles_n, &tm, &tn);
+    }
+    tm += round * rows_per_round;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int own0 = m0 + h * HB;  // first row this workgroup normalises
+    const int tile_id = tm * tiles_n + tn;
+    unsigned long long* const my_words = pwords + tile_id * 4 + h * 2;
+    const unsigned long long* const partner_words = pwords + tile_id * 4 + (1 - h) * 2;
+    unsigned xcc = 0;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    xcc &= 0xff;
+    const unsigned long long tag = (unsigned long long)epoch << 32;
+    if (threadIdx.x == 0)
+      __hip_atomic_store(my_words, tag | xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    TileAcc<TM, TN> acc = tile_mainloop<BM, BN, NB, WM, WN>(A, Bp, M, N, K, m0, n0, h * (K / 2),
+                                                            K / 2 / kBK);
+    // Plain hand-over only if the partner's id word is this launch's and names this XCD.
+    unsigned long long pid = 0;
+    if (threadIdx.x == 0)
+      pid = __hip_atomic_load(partner_words, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(PR_VMCNT(0));
+    __syncthreads();  // the ring is free
+    if (threadIdx.x == 0) *smode = pid == (tag | xcc);
+    __syncthreads();
+    const bool plain = *smode != 0;
+    // Lane-dependent epilogue offsets come from an opaque copy of the lane id, so that they are
+    // formed here rather than hoisted out of the round loop and kept live across the main loop.
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    int et = threadIdx.x;
+    asm volatile("" : "+v"(et));
+
+    unsigned long long* const xmine = xbuf + (size_t)((round & 1) * gridDim.x + b) * (4 * XW);
+    const unsigned long long* const xpart =
+        xbuf + (size_t)((round & 1) * gridDim.x + partner) * (4 * XW);
+    if (wm != h) {
+      // Fetch 32 rows of the kept rows' residual into ring buffer wn, then hand over this
+      // wave's rows (the partner keeps them): 16-byte plain stores (same XCD) or 8-byte
+      // device-scope stores, each in its own layout.
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        int row = own0 + wn * 32 + k;
+        row = row < M ? row : M - 1;  // rows past M are computed, never stored
+        load_to_lds16(reinterpret_cast<const char*>(R + (long long)row * N + n0),
+                      (uint32_t)el * 16u, rbuf(wn) + k * 1024);
+      }
+      if (plain) {
+        float4* xw = reinterpret_cast<float4*>(xmine + wn * XW);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+              xw[((i * TN + j) * 4 + e4) * 64 + el] =
+                  make_float4(acc.v[i][j][4 * e4], acc.v[i][j][4 * e4 + 1],
+                              acc.v[i][j][4 * e4 + 2], acc.v[i][j][4 * e4 + 3]);
+      } else {
+        unsigned long long* xw = xmine + wn * XW;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+              const unsigned long long v =
+                  (unsigned long long)__float_as_uint(acc.v[i][j][2 * e2]) |
+                  ((unsigned long long)__float_as_uint(acc.v[i][j][2 * e2 + 1]) << 32);
+              __hip_atomic_store(xw + ((i * TN + j) * 8 + e2) * 64 + el, v, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+            }
+      }
+      __builtin_amdgcn_s_waitcnt(PR_VMCNT(0));  // hand-over written, residual landed
+    }
+    __syncthreads();
+    if (et == 0) {
+      __hip_atomic_store(my_words + 1, tag | (plain ? 1u : 0u), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      unsigned polls = 0;
+      int ok = 1;
+      unsigned long long v;
+      while (((v = __hip_atomic_load(partner_words + 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT)) >> 32) != read_epoch) {
+        if (polls++ >= spin_limit) {
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      *sflag = ok;
+      *spart = (int)(v & 1);
+    }
+    __syncthreads();
+    if (*sflag == 0) {
+      // The partner never announced its half: this block writes nothing (its row block's
+      // waits give up in turn).
+      if (et == 0)
+        __hip_atomic_fetch_or(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      continue;
+    }
+
+    const int lrow = el / 16;        // staged layout: 16 lanes per row, 4 floats each
+    const int rcol = (el % 16) * 4;
+    if (wm == h && *spart) {
+      // The partner's partial of the kept rows, from this XCD's L2: 16-byte loads after
+      // dropping any L1 copy of the region (it may hold an earlier round's contents).
+      asm volatile("buffer_inv sc0" ::: "memory");
+      const float4* xp = reinterpret_cast<const float4*>(xpart + wn * XW);
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        float4 pv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) pv[u] = xp[(part * 16 + u) * 64 + el];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int idx = part * 16 + u;  // (i * TN + j) * 4 + e4
+          const int i = idx / (TN * 4), j = (idx / 4) % TN, e4 = idx % 4;
+          acc.v[i][j][4 * e4] += pv[u].x;
+          acc.v[i][j][4 * e4 + 1] += pv[u].y;
+          acc.v[i][j][4 * e4 + 2] += pv[u].z;
+          acc.v[i][j][4 * e4 + 3] += pv[u].w;
+        }
+      }
+    } else if (wm == h) {
+      // The partner's partial through the memory-side coherence point (batches of 16 loads).
+      const unsigned long long* xp = xpart + wn * XW;
+#pragma unroll
+      for (int part = 0; part < 4; ++part) {
+        unsigned long long pv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          pv[u] = __hip_atomic_load(xp + (part * 16 + u) * 64 + el, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int idx = part * 16 + u;  // (i * TN + j) * 8 + e2
+          const int i = idx / (TN * 8), j = (idx / 8) % TN, e2 = idx % 8;
+          acc.v[i][j][2 * e2] += __uint_as_float((unsigned)pv[u]);
+          acc.v[i][j][2 * e2 + 1] += __uint_as_float((unsigned)(pv[u] >> 32));
+        }
+      }
+    }
+    if (wm == h) {
+      // r + y in place in LDS, and per-row sums of squares of this wave's 64 columns.
+      float* ep = reinterpret_cast<float*>(sb4 + wn * EP_BYTES);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 8 * hh; e < 8 * hh + 8; ++e)
+              ep[(((e >> 2) - 2 * hh) * 8 + (el >> 5) * 4 + (e & 3)) * EP_LD + j * 32 +
+                 (el & 31)] = acc.v[i][j][e];
+          __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int r_in = rr * 4 + lrow;
+            const int trow = i * 32 + hh * 16 + r_in;  // row within the kept 128 (buffer i)
+            const float4 y = *reinterpret_cast<const float4*>(ep + r_in * EP_LD + rcol);
+            float4* rp = reinterpret_cast<float4*>(rbuf(i) + (trow % 32) * 1024 +
+                                                   (wn * 64 + rcol) * 4);
+            const float4 rv = *rp;
+            const float4 v = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
+            *rp = v;
+            const float sq = lane_group_sum<16>(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
+            if (el % 16 == 0) sred[trow * WN + wn] = sq;
+          }
+          __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);  // reads done before the next slice
+        }
+      }
+    }
+    __syncthreads();
+    if (et < HB) {
+      float p = 0.0f;
+#pragma unroll
+      for (int c = 0; c < WN; ++c) p += sred[et * WN + c];
+      const int row = own0 + et;
+      if (row < M)
+        __hip_atomic_store(slots + (long long)tn * M + row, tag | __float_as_uint(p),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    unsigned* const cnt = sync + 2 + tm * 2 + h;
+    if (et == 0)
+      __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The updated residual: 16 rows of 1 KiB per wave, from LDS.
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int trow = wave * 16 + k;
+      const int row = own0 + trow;
+      const float4 v = *reinterpret_cast<const float4*>(rbuf(trow / 32) + (trow % 32) * 1024 +
+                                                        el * 16);
+      if (row < M)
+        __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<f32x4_t*>(R + (long long)row * N + n0 +
+                                                               el * 4));
+    }
+    if (et == 0) {
+      unsigned polls = 0;
+      while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                 (unsigned)tiles_n &&
+             polls++ < spin_limit)
+        __builtin_amdgcn_s_sleep(1);
+      *sflag = 1;
+    }
+    __syncthreads();
+    {
+      // The row block's slots in tile-column order: four threads per row, each a contiguous
+      // run of ceil(tiles_n / 4) slots, then the runs in order.
+      const int trow = et % HB;
+      const int part = et / HB;
+      const int row = own0 + trow;
+      const int per = (tiles_n + 3) / 4;
+      const int c_begin = min(part * per, tiles_n), c_end = min(c_begin + per, tiles_n);
+      float ss = 0.0f;
+      if (row < M) {
+        const unsigned long long* ps = slots + row;
+        unsigned polls = 0;
+        unsigned long long sv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          sv[u] = c_begin + u < c_end ? __hip_atomic_load(ps + (long long)(c_begin + u) * M,
+                                                          __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT)
+                                      : (unsigned long long)read_epoch << 32;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          while ((sv[u] >> 32) != read_epoch) {
+            if (polls++ >= spin_limit) {
+              *sflag = 0;  // the block gives up
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            sv[u] = __hip_atomic_load(ps + (long long)(c_begin + u) * M, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if (c_begin + u < c_end) ss += __uint_as_float((unsigned)sv[u]);
+        }
+      }
+      sred[trow * 4 + part] = ss;  // the publish reads of sred are two barriers back
+    }
+    __syncthreads();
+    if (et < HB && own0 + et < M) {
+      const float ss = ((sred[et * 4] + sred[et * 4 + 1]) +
+                        sred[et * 4 + 2]) + sred[et * 4 + 3];
+      sinv[et] = 1.0f / sqrtf(ss / (float)N + eps);
+    }
+    __syncthreads();
+    if (*sflag == 0) {
+      if (et == 0)
+        __hip_atomic_fetch_or(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      // Output: 16 rows per wave, two rows per instruction, 8 columns (16 bytes) per lane.
+      const int c8 = (el & 31) * 8;
+      const float4 ga = *reinterpret_cast<const float4*>(w + n0 + c8);
+      const float4 gb = *reinterpret_cast<const float4*>(w + n0 + c8 + 4);
+      const float gx[8] = {ga.x + g0, ga.y + g0, ga.z + g0, ga.w + g0,
+                           gb.x + g0, gb.y + g0, gb.z + g0, gb.w + g0};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int trow = wave * 16 + k * 2 + (el >> 5);
+        const int row = own0 + trow;
+        if (row < M) {
+          const float* src =
+              reinterpret_cast<const float*>(rbuf(trow / 32) + (trow % 32) * 1024) + c8;
+          const float4 va = *reinterpret_cast<const float4*>(src);
+          const float4 vb = *reinterpret_cast<const float4*>(src + 4);
+          const float inv = sinv[trow];
+          const float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+          uint32_t o[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            o[t] = f32_to_bf16_rne(v[2 * t] * inv * gx[2 * t]) |
+                   (f32_to_bf16_rne(v[2 * t + 1] * inv * gx[2 * t + 1]) << 16);
+          __builtin_nontemporal_store(
+              u32x4_t{o[0], o[1], o[2], o[3]},
+              reinterpret_cast<u32x4_t*>(out + (long long)row * N + n0 + c8));
+        }
+      }
+    }
+    __syncthreads();  // LDS is refilled by the next tile's prologue
+  }
+
+  // The last workgroup to finish returns the counters to zero for the next launch.
+  if (threadIdx.x == 0) {
+    const unsigned prev =
+        __hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sflag = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (*sflag) {
+    for (int i = threadIdx.x; i < 2 * tiles_m; i += blockDim.x)
+      __hip_atomic_store(sync + 2 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// --------------------------------------------------------------------------------------------
 // Residual add + RMSNorm: one wavefront per row, the row held in registers (NV float4 per lane,
 // H = 256 * NV).  Loads of the whole row are issued before any use so that each wave keeps
 // NV * (1 + planes) 16-byte loads per lane in flight.
@@ -1152,6 +1557,41 @@ int launch_single_t(const uint16_t* x, const uint16_t* Wp, float* r, const float
   return check_launch("gemm_add_rmsnorm_kernel");
 }
 
+// Pair form (256 x 256 tiles, 8 waves, K split over two workgroups).  Rounds cover whole tile
+// rows; every pair and row block of a round is resident at once.
+int launch_pair(const uint16_t* x, const uint16_t* Wp, float* r, const float* w, uint16_t* out,
+                unsigned long long* slots, unsigned* sync, unsigned long long* pwords,
+                unsigned long long* xbuf, size_t xbuf_words, int M, int N, int K, float eps,
+                int gemma, unsigned epoch, unsigned read_epoch, unsigned spin_limit,
+                hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  auto kern = gemm_add_rmsnorm_pair_kernel<5>;
+  constexpr int threads = 512;
+  static int resident = 0;
+  if (resident == 0) PR_TRY_K(resident_workgroups(kern, threads, &resident));
+  const int tiles_m = (M + 255) / 256;
+  const int tiles_n = N / 256;
+  const int rows_per_round =
+      resident / (2 * tiles_n) < tiles_m ? resident / (2 * tiles_n) : tiles_m;
+  if (rows_per_round < 1)
+    return fail(PR_ERR_UNSUPPORTED, "single launch (pairs): %d workgroups per tile row exceed "
+                "the %d resident workgroups", 2 * tiles_n, resident);
+  const unsigned grid = (unsigned)(2 * rows_per_round * tiles_n);
+  const size_t parities = rows_per_round < tiles_m ? 2 : 1;
+  if (xbuf == nullptr || pwords == nullptr || parities * grid * 16384u > xbuf_words)
+    return fail(PR_ERR_INVALID_ARG, "single launch (pairs): exchange buffer of %zu words is "
+                "smaller than %zu", xbuf_words, parities * grid * 16384u);
+  if (t0 != nullptr) {
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, t0, t1, 0, x, Wp, r, w, out,
+                          slots, sync, pwords, xbuf, M, N, K, tiles_m, tiles_n, rows_per_round,
+                          eps, gemma, epoch, read_epoch, spin_limit);
+  } else {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, Wp, r, w, out, slots, sync,
+                       pwords, xbuf, M, N, K, tiles_m, tiles_n, rows_per_round, eps, gemma, epoch,
+                       read_epoch, spin_limit);
+  }
+  return check_launch("gemm_add_rmsnorm_pair_kernel");
+}
+
 template <int NV, int WPR, bool YB>
 int launch_addnorm_t(const void* y, int y_bf16, int nplanes, long long plane_stride, int round_y,
                      float* r, const float* w, uint16_t* out, int rows, int H, float eps,
@@ -1208,11 +1648,22 @@ int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, con
                             uint16_t* out, unsigned long long* slots, unsigned* sync, int M,
                             int N, int K, const GemmCfg& cfg, float eps, int gemma,
                             unsigned epoch, unsigned read_epoch, unsigned spin_limit,
-                            void* stream, void* start_timing, void* stop_timing) {
+                            void* stream, void* start_timing, void* stop_timing,
+                            unsigned long long* pair_words, unsigned long long* xbuf,
+                            size_t xbuf_words) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t t0 = static_cast<hipEvent_t>(start_timing);
   hipEvent_t t1 = static_cast<hipEvent_t>(stop_timing);
   if (M <= 0) return PR_OK;
+  if (cfg.split == 2) {
+    if (cfg.bm != 256 || cfg.bn != 256 || cfg.waves != 8 || cfg.kgroups != 1 ||
+        K % (2 * kBK) != 0 || N % 256 != 0 || N / 256 > 64)
+      return fail(PR_ERR_SHAPE, "single launch (pairs): N=%d K=%d with tile %dx%d, %d waves, %d "
+                  "K groups not supported (256x256, 8 waves, N a multiple of 256)", N, K, cfg.bm,
+                  cfg.bn, cfg.waves, cfg.kgroups);
+    return launch_pair(x, Wp, r, w, out, slots, sync, pair_words, xbuf, xbuf_words, M, N, K, eps,
+                       gemma, epoch, read_epoch, spin_limit, s, t0, t1);
+  }
   const bool r256x128 = cfg.bm == 256 && cfg.bn == 128;
   if (K % (2 * kBK) != 0 || N % cfg.bn != 0 || N / cfg.bn > 64 || cfg.split != 1 ||
       (cfg.waves != 8 && !(cfg.waves == 4 && r256x128)) ||

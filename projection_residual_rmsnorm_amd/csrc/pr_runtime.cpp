@@ -46,6 +46,12 @@ struct DevCtx {
   size_t row_slots_bytes = 0;
   unsigned* sync = nullptr;
   size_t sync_bytes = 0;
+  // pair form: per-tile XCD-id and ready words (epoch-tagged like the slots) and the exchange
+  // regions
+  void* pair_flags = nullptr;
+  size_t pair_flags_bytes = 0;
+  void* xbuf = nullptr;
+  size_t xbuf_bytes = 0;
   unsigned epoch = 0;
   const uint16_t* last_borrowed = nullptr;
   // the previous pipeline call: its caller stream and the done slots of its last chunk on
@@ -374,16 +380,30 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
   const long long rows_per = ((1LL << 30) / K) / g.bm * g.bm;
   if (rows_per <= 0) return fail(PR_ERR_SHAPE, "K=%d too large", K);
   const int rows_max = (int)std::min<long long>(rows_per, T);
+  const bool pairs = g.split == 2;
   const size_t slots_need = (size_t)rows_max * (H / g.bn) * sizeof(unsigned long long);
-  if (slots_need > c->row_slots_bytes) {
+  const size_t flags_need =
+      pairs ? (size_t)4 * ((rows_max + 255) / 256) * (H / 256) * sizeof(unsigned long long) : 0;
+  // Epoch-tagged buffers (row slots, pair flags): a grown buffer restarts the epochs, so every
+  // such buffer is zeroed (no word holds an epoch >= 1) and complete before any kernel reads
+  // it; the fill runs on the null stream, which does not order work on a non-blocking caller
+  // stream.
+  if (slots_need > c->row_slots_bytes || flags_need > c->pair_flags_bytes) {
     PR_TRY(grow(&c->row_slots, &c->row_slots_bytes, slots_need));
-    // Zeroed (no slot holds an epoch >= 1) and complete before any kernel reads it: the fill
-    // runs on the null stream, which does not order work on a non-blocking caller stream.
+    if (flags_need > 0) PR_TRY(grow(&c->pair_flags, &c->pair_flags_bytes, flags_need));
     PR_HIP(hipMemset(c->row_slots, 0, c->row_slots_bytes));
+    if (c->pair_flags != nullptr) PR_HIP(hipMemset(c->pair_flags, 0, c->pair_flags_bytes));
     PR_HIP(hipDeviceSynchronize());
     c->epoch = 0;
   }
-  const size_t sync_need = (size_t)(2 + (rows_max + g.bm - 1) / g.bm) * sizeof(unsigned);
+  if (pairs) {
+    // Exchange regions: 128 KiB per workgroup of a round and round parity; a round holds at
+    // most one workgroup per CU.
+    const size_t xbuf_need = (size_t)2 * kNumCUs * 128 * 1024;
+    PR_TRY(grow(&c->xbuf, &c->xbuf_bytes, xbuf_need));
+  }
+  const int blocks = pairs ? 2 * ((rows_max + 255) / 256) : (rows_max + g.bm - 1) / g.bm;
+  const size_t sync_need = (size_t)(2 + blocks) * sizeof(unsigned);
   if (sync_need > c->sync_bytes) {
     void* p = c->sync;
     size_t have = c->sync_bytes;
@@ -401,6 +421,7 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
       // After 2^32 - 1 launches the slots are cleared once so that epochs stay unique.
       PR_HIP(hipDeviceSynchronize());
       PR_HIP(hipMemset(c->row_slots, 0, c->row_slots_bytes));
+      if (c->pair_flags != nullptr) PR_HIP(hipMemset(c->pair_flags, 0, c->pair_flags_bytes));
       PR_HIP(hipDeviceSynchronize());
       c->epoch = 1;
     }
@@ -409,7 +430,10 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
     PR_TRY(timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
       return launch_gemm_add_rmsnorm(x + r0 * K, W, r + r0 * H, w, out + r0 * H,
                                      static_cast<unsigned long long*>(c->row_slots), c->sync, rows,
-                                     H, K, g, eps, gemma, epoch, read_epoch, limit, s, t0, t1);
+                                     H, K, g, eps, gemma, epoch, read_epoch, limit, s, t0, t1,
+                                     static_cast<unsigned long long*>(c->pair_flags),
+                                     static_cast<unsigned long long*>(c->xbuf),
+                                     c->xbuf_bytes / sizeof(unsigned long long));
     }));
   }
   return PR_OK;

@@ -96,18 +96,25 @@ def test_random_parity_small(T, K, H, kind):
 
 
 # ------------------------------------------------------------- single-launch fused path
-# (tile, waves per workgroup, K groups) of every single-launch instantiation
-SINGLE_CFGS = [("256x256", 8, 1), ("256x128", 8, 1), ("256x128", 4, 1), ("256x128", 8, 2),
-               ("128x128", 8, 1)]
+# (tile, waves per workgroup, K groups, K split) of every single-launch instantiation; split 2
+# is the pair form (each 256x256 tile's K halves on two workgroups)
+SINGLE_CFGS = [("256x256", 8, 1, 1), ("256x128", 8, 1, 1), ("256x128", 4, 1, 1),
+               ("256x128", 8, 2, 1), ("128x128", 8, 1, 1), ("256x256", 8, 1, 2)]
 
 
-@pytest.mark.parametrize("tile,waves,kgroups", SINGLE_CFGS)
-def test_single_launch_integer_projection_is_exact(monkeypatch, tile, waves, kgroups):
-    """Small integers: the fp32 residual is exact, so it must match bitwise.  T=300 leaves a
-    ragged last tile row; H=768 is 3 or 6 tile columns."""
+def _force_single(monkeypatch, tile, waves, kgroups, split):
     monkeypatch.setenv("PR_FORCE_TILE", tile)
     monkeypatch.setenv("PR_FORCE_WAVES", str(waves))
     monkeypatch.setenv("PR_FORCE_KGROUPS", str(kgroups))
+    monkeypatch.setenv("PR_FORCE_SPLIT", str(split))
+    print(f"single launch {tile} {waves} waves {kgroups} K groups split {split}", flush=True)
+
+
+@pytest.mark.parametrize("tile,waves,kgroups,split", SINGLE_CFGS)
+def test_single_launch_integer_projection_is_exact(monkeypatch, tile, waves, kgroups, split):
+    """Small integers: the fp32 residual is exact, so it must match bitwise.  T=300 leaves a
+    ragged last tile row; H=768 is 3 or 6 tile columns."""
+    _force_single(monkeypatch, tile, waves, kgroups, split)
     d = synth.integer_inputs(300, 1024, 768, seed=3)
     dev = Device(d)
     r_dev, out_bits = dev.run("single")
@@ -118,35 +125,37 @@ def test_single_launch_integer_projection_is_exact(monkeypatch, tile, waves, kgr
     assert oracle.within_tolerance(err), err
 
 
-@pytest.mark.parametrize("tile,waves,kgroups", SINGLE_CFGS)
+@pytest.mark.parametrize("tile,waves,kgroups,split", SINGLE_CFGS)
 @pytest.mark.parametrize("kind", [0, 1])
 @pytest.mark.parametrize("T,K,H", [(300, 512, 768), (64, 512, 512), (1, 256, 512),
                                    (513, 1024, 256)])
-def test_single_launch_random_parity_small(monkeypatch, tile, waves, kgroups, kind, T, K, H):
+def test_single_launch_random_parity_small(monkeypatch, tile, waves, kgroups, split, kind, T, K,
+                                           H):
     if H % int(tile.split("x")[1]):
         pytest.skip("tile columns do not divide H")
-    monkeypatch.setenv("PR_FORCE_TILE", tile)
-    monkeypatch.setenv("PR_FORCE_WAVES", str(waves))
-    monkeypatch.setenv("PR_FORCE_KGROUPS", str(kgroups))
+    _force_single(monkeypatch, tile, waves, kgroups, split)
     d = synth.make_custom(T, K, H, seed=T + K, norm_kind=kind, eps=1e-5)
     dev = Device(d)
     r_dev, out_bits = dev.run("single")
     _check(d, r_dev, out_bits, "fused")
 
 
-@pytest.mark.parametrize("tile,waves,kgroups,T,H", [("256x128", 8, 1, 4096, 4096),
-                                                    ("256x128", 4, 1, 4096, 4096),
-                                                    ("256x128", 8, 2, 4096, 4096),
-                                                    ("128x128", 8, 1, 8192, 2048),
-                                                    ("256x256", 8, 1, 4100, 8192)])
-def test_single_launch_several_rounds(monkeypatch, tile, waves, kgroups, T, H):
+@pytest.mark.parametrize("tile,waves,kgroups,split,T,H", [("256x128", 8, 1, 1, 4096, 4096),
+                                                          ("256x128", 4, 1, 1, 4096, 4096),
+                                                          ("256x128", 8, 2, 1, 4096, 4096),
+                                                          ("128x128", 8, 1, 1, 8192, 2048),
+                                                          ("256x256", 8, 1, 1, 4100, 8192),
+                                                          ("256x256", 8, 1, 2, 4100, 8192),
+                                                          ("256x256", 8, 1, 2, 1000, 1280),
+                                                          ("256x256", 8, 1, 2, 2048, 4096)])
+def test_single_launch_several_rounds(monkeypatch, tile, waves, kgroups, split, T, H):
     """More tiles than resident workgroups: the launch runs several rounds of whole tile rows
     (256x128: 512 tiles in 2 rounds; 128x128: 1024 tiles in 2; 256x256: 17 x 32 tiles, the
-    last round one ragged tile row)."""
-    monkeypatch.setenv("PR_FORCE_TILE", tile)
-    monkeypatch.setenv("PR_FORCE_WAVES", str(waves))
-    monkeypatch.setenv("PR_FORCE_KGROUPS", str(kgroups))
-    print(f"single launch {tile} {waves} waves {kgroups} K groups T={T} H={H}", flush=True)
+    last round one ragged tile row).  Pairs: 17 x 32 tiles in 5 rounds of 4 tile rows (both
+    exchange-region parities); 4 x 5 tiles in one round with 32 workgroups in same-XCD pairs and
+    8 in neighbour pairs; the o_proj shape in one full round."""
+    _force_single(monkeypatch, tile, waves, kgroups, split)
+    print(f"T={T} H={H}", flush=True)
     d = synth.make_custom(T, 256, H, seed=11)
     dev = Device(d)
     r_dev, out_bits = dev.run("single")
@@ -181,9 +190,13 @@ def test_single_launch_padded_rows_untouched():
     assert np.all(bits(dev.out)[T:] == 0x7BAD)
 
 
-def test_single_launch_back_to_back_calls():
+@pytest.mark.parametrize("split", [1, 2])
+def test_single_launch_back_to_back_calls(monkeypatch, split):
     """The completion counters return to zero at the end of every launch: calls of different
-    sizes in a row (on one stream, no host synchronisation between them) are all correct."""
+    sizes in a row (on one stream, no host synchronisation between them) are all correct.
+    Split 2: the pair form, whose flags are epoch-tagged per launch."""
+    if split == 2:
+        _force_single(monkeypatch, "256x256", 8, 1, 2)
     cases = [synth.make_custom(T, 512, 1024, seed=T) for T in (1000, 300, 1000, 17)]
     devs = [Device(d) for d in cases]
     for dev in devs:
@@ -212,10 +225,14 @@ def test_single_launch_agrees_with_pipeline():
     assert np.max(diff) <= 2 ** -7 * np.max(np.abs(b.view(np.float32)))
 
 
-def test_single_launch_wait_limit_reports(monkeypatch):
+@pytest.mark.parametrize("split", [1, 2])
+def test_single_launch_wait_limit_reports(monkeypatch, split):
     """Row reads that look for an epoch no slot carries (set from the host) give up after 64
     polls each; the kernel ends, the status bit reports it and reading clears it.  A later
-    call without the fault is correct."""
+    call without the fault is correct.  Split 2: the pair form's partner wait gives up first,
+    and neither half writes anything."""
+    if split == 2:
+        _force_single(monkeypatch, "256x256", 8, 1, 2)
     monkeypatch.setenv("PR_FAULT_INJECT", "wait")
     monkeypatch.setenv("PR_SPIN_LIMIT", "64")
     d = synth.make_custom(600, 256, 1024, seed=4)
