@@ -114,6 +114,7 @@ def counter_table(path: str, kernels: List[str], grid: int = 0) -> Dict[str, dic
 
 NAMEPLATE_GHZ = 2.4
 XCDS = 8
+SHADER_ENGINES = 32  # 4 per XCD
 
 
 def derived(mean: Dict[str, float]) -> Dict[str, float]:
@@ -128,7 +129,10 @@ def derived(mean: Dict[str, float]) -> Dict[str, float]:
       mfma_util_active: busy cycles / (SIMDs x GRBM_GUI_ACTIVE / 8), against the cycles the
         GPU clock actually ran;
       lds_bank_conflict_frac: conflict cycles / LDS-active cycles;
-      lds_active_frac: LDS-active cycles per CU / (GRBM_GUI_ACTIVE / 8)."""
+      lds_active_frac: LDS-active cycles per CU / (GRBM_GUI_ACTIVE / 8);
+      shader_clock_GHz: SQ_BUSY_CYCLES (shader-clock cycles with waves present, summed over the
+        32 shader engines) / (32 x duration), the clock the kernel actually ran at;
+      mfma_util_at_shader_clock: MFMA busy cycles / (SIMDs x duration x that clock)."""
     out = {}
     simds = CU_COUNT * SIMDS_PER_CU
     busy, active = mean.get("SQ_VALU_MFMA_BUSY_CYCLES"), mean.get("GRBM_GUI_ACTIVE")
@@ -141,6 +145,11 @@ def derived(mean: Dict[str, float]) -> Dict[str, float]:
         out["mfma_util_nameplate"] = busy / (simds * dur * NAMEPLATE_GHZ)
     if busy is not None and active:
         out["mfma_util_active"] = busy / (simds * active / XCDS)
+    if mean.get("SQ_BUSY_CYCLES") and dur:
+        clk = mean["SQ_BUSY_CYCLES"] / SHADER_ENGINES / dur
+        out["shader_clock_GHz"] = clk
+        if busy is not None:
+            out["mfma_util_at_shader_clock"] = busy / (simds * dur * clk)
     if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:
         out["mfma_bf16_flops"] = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * MOP_FLOPS
         if dur:

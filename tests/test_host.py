@@ -429,3 +429,7 @@ def test_counter_summary_derivations(tmp_path):
     assert abs(dv["lds_bank_conflict_frac"] - 0.25) < 1e-12
     assert abs(dv["lds_active_frac"] - 1000.0 / 200e3) < 1e-12
     assert counter_table(str(path), ["gemm_add_rmsnorm_kernel"], grid=256) == {}
+    # shader clock from SQ_BUSY_CYCLES over the 32 shader engines: 1.5 GHz for 100 us
+    dv = derived({**t["mean"], "SQ_BUSY_CYCLES": 32 * 100e3 * 1.5})
+    assert abs(dv["shader_clock_GHz"] - 1.5) < 1e-9
+    assert abs(dv["mfma_util_at_shader_clock"] - 0.8) < 1e-9  # 0.5 of 2.4 GHz = 0.8 of 1.5
