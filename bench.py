@@ -52,6 +52,10 @@ def parse():
                     help="run the token-threshold search on the K=H=8192 sweep and print it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--tp-share", default="",
+                    help="comma-separated tensor-parallel degrees P: time one rank's share of "
+                         "the workload (projection over K/P, add/norm of T/P rows with P fp32 "
+                         "partials) and print the table")
     return ap.parse_args()
 
 
@@ -124,6 +128,100 @@ def tune_sweep(pr, torch, args) -> int:
     return 0
 
 
+XGMI_LINK_GBS = 153.0   # one xGMI link, per direction
+
+
+def tp_share(pr, torch, args) -> int:
+    """One rank's share of the row-parallel projection region under tensor parallelism of
+    degree P, measured on this GPU: the projection of all T (or one chunk of mc) tokens over the
+    rank's K/P input columns into an fp32 partial, and the add/norm of the rank's T/P (mc/P)
+    token shard summing P fp32 partials in rank order.  The reduce-scatter of the partials and
+    the all-gather of the bf16 output between them are modelled, not run: a one-shot exchange
+    in which every rank sends each peer its shard over that peer's own xGMI link."""
+    import synth
+    wl = synth.WORKLOADS[args.workload]
+    T, K, H = wl.T, wl.K, wl.H
+    dev = "cuda:0"
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    steps = max(args.steps, 5)
+
+    def per_launch(call, kind):
+        for _ in range(max(args.warmup, 2)):
+            call()
+        torch.cuda.synchronize()
+        pr.pr_profile_enable(True)
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        prof = pr.pr_profile_read()
+        pr.pr_profile_enable(False)
+        ms, n = prof[kind + "_ms"], prof[kind + "_launches"]
+        return ms / max(n, 1) * 1e3  # us
+
+    def device_inputs(rows, k):
+        d = synth.make_custom(rows, k, H, seed=rows + k, norm_kind=wl.norm_kind, eps=wl.eps,
+                              x_dist=wl.x_dist)
+        x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+        W_src = torch.from_numpy(d["W"].view(np.int16)).to(dev)
+        Wp = torch.empty(k * H, dtype=torch.int16, device=dev)
+        pr.pr_prepare_weight(W_src, pr.PR_WEIGHT_OUT_IN, Wp, k, H)
+        r = torch.from_numpy(d["residual"]).to(dev)
+        w = torch.from_numpy(d["norm_w"]).to(dev)
+        out = torch.empty((rows, H), dtype=torch.int16, device=dev)
+        return d, x, Wp, r, w, out
+
+    rows_out = []
+    for P in [int(v) for v in args.tp_share.split(",") if v]:
+        if K % (64 * P) != 0 or T % P != 0:
+            log(f"P={P}: K/P or T/P is not a whole number of 64-column groups / rows; skipped")
+            continue
+        kp = K // P
+        for mc in (T, 512):
+            n_chunks = T // mc
+            # projection share: one chunk of mc tokens over K/P columns into one fp32 partial
+            # (K split 1), and as the library would run it (its own tile and K split; the
+            # split partials would be summed before the exchange)
+            d, x, Wp, r, w, out = device_inputs(mc, kp)
+            call = lambda: pr.proj_add_rmsnorm(x, Wp, r, w, d["eps"], mc, kp, H, mc, wl.norm_kind,
+                                               out)
+            auto_split = pr.pr_select(mc, kp, H, mc)["split_k"]
+            t_auto = per_launch(call, "gemm")
+            os.environ["PR_FORCE_SPLIT"] = "1"
+            t_proj = per_launch(call, "gemm")
+            # add/norm share: mc/P rows, P fp32 partials (a minimal projection produces them)
+            rows = mc // P
+            os.environ["PR_FORCE_SPLIT"] = str(P)
+            d, x, Wp, r, w, out = device_inputs(rows, 64 * P)
+            t_an = per_launch(lambda: pr.proj_add_rmsnorm(x, Wp, r, w, d["eps"], rows, 64 * P, H,
+                                                          rows, wl.norm_kind, out), "addnorm")
+            os.environ.pop("PR_FORCE_SPLIT", None)
+            rs_fp32 = (P - 1) and rows * H * 4 / (XGMI_LINK_GBS * 1e3)  # us per link
+            rs_bf16 = (P - 1) and rows * H * 2 / (XGMI_LINK_GBS * 1e3)
+            ag_bf16 = (P - 1) and rows * H * 2 / (XGMI_LINK_GBS * 1e3)
+            serial = t_proj + rs_fp32 + t_an + ag_bf16
+            overlapped = max(t_proj, rs_fp32, t_an, ag_bf16)
+            row = {"P": P, "mc": mc, "chunks": n_chunks, "K_share": kp, "rows_share": rows,
+                   "proj_share_us": t_proj, "addnorm_share_us": t_an,
+                   "proj_share_tflops": 2.0 * mc * kp * H / t_proj / 1e6,
+                   "proj_share_auto_us": t_auto, "proj_share_auto_split": auto_split,
+                   "addnorm_share_gbs": rows * H * (4 * P + 10) / t_an / 1e3,
+                   "rs_fp32_model_us": rs_fp32, "rs_bf16_model_us": rs_bf16,
+                   "ag_bf16_model_us": ag_bf16,
+                   "per_chunk_serial_us": serial, "per_chunk_overlapped_bound_us": overlapped,
+                   "call_serial_us": serial * n_chunks,
+                   "call_pipelined_bound_us": (overlapped * n_chunks + serial - overlapped
+                                               if n_chunks > 1 else serial)}
+            rows_out.append(row)
+            log(f"P={P} mc={mc}: proj share {t_proj:.1f} us (library's choice, split "
+                f"{auto_split}: {t_auto:.1f} us), add/norm share {t_an:.1f} us, "
+                f"RS fp32 {rs_fp32:.1f} / AG bf16 {ag_bf16:.1f} us (model)")
+    print(json.dumps({"tp_share": {"workload": wl.name, "T": T, "K": K, "H": H,
+                                   "xgmi_link_GBs": XGMI_LINK_GBS, "rows": rows_out}}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -138,6 +236,8 @@ def main() -> int:
         return 1
     if args.tune_sweep:
         return tune_sweep(pr, torch, args)
+    if args.tp_share:
+        return tp_share(pr, torch, args)
     wl = synth.WORKLOADS[args.workload]
     T, K, H = wl.T, wl.K, wl.H
     log(f"workload {wl.name}: T={T} K={K} H={H} chunk sizes {wl.microchunks}")
