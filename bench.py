@@ -70,6 +70,28 @@ def time_steps(call, steps: int, warmup: int, torch):
     return time.perf_counter() - t0
 
 
+def per_call_stats(call, r, r0, steps: int, torch, stream, flush=None) -> dict:
+    """Single calls timed with events on the calling stream.  Before each call (untimed) the
+    residual is restored from a pristine copy and, with `flush`, a buffer twice the size of the
+    256 MB Infinity Cache is written, so that none of the call's operands is cached."""
+    times = []
+    for i in range(steps + 3):
+        r.copy_(r0)
+        if flush is not None:
+            flush.fill_(float(i))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        e1.synchronize()
+        if i >= 3:
+            times.append(e0.elapsed_time(e1))
+    t = np.array(times)
+    return {"median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
+            "p90_ms": float(np.percentile(t, 90)), "calls": len(times)}
+
+
 def traffic_label(workload: str, mc, chunk_cfgs: dict) -> str:
     """Label of a traffic measurement: workload, fused form (chunk size or "single") and the
     projection configuration it ran with (counters taken under another configuration do not
@@ -375,6 +397,23 @@ def main() -> int:
         "chunk_configs": chunk_cfgs,
         "conventional": conv,
     }
+    # Per-call statistics of the headline form and the conventional path: residual restored
+    # before every call; warm (operands may sit in the Infinity Cache) and flushed.
+    r0 = r.clone()
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MB
+    result["per_call"] = {
+        "form": "single launch" if single else f"mc={mc}",
+        "fused_warm": per_call_stats(fused(mc), r, r0, args.steps, torch, stream),
+        "fused_flushed": per_call_stats(fused(mc), r, r0, args.steps, torch, stream, flush),
+        "conventional_warm": per_call_stats(conventional, r, r0, args.steps, torch, stream),
+        "conventional_flushed": per_call_stats(conventional, r, r0, args.steps, torch, stream,
+                                               flush)}
+    del flush, r0
+    log("per call (median ms, warm / flushed): fused "
+        f"{result['per_call']['fused_warm']['median_ms']:.4f} / "
+        f"{result['per_call']['fused_flushed']['median_ms']:.4f}, conventional "
+        f"{result['per_call']['conventional_warm']['median_ms']:.4f} / "
+        f"{result['per_call']['conventional_flushed']['median_ms']:.4f}")
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
