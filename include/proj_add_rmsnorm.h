@@ -287,6 +287,21 @@ int pr_set_chunk_config(int K, int H, int microchunk, int tile_m, int tile_n, in
 /* Remove every installed tuning result and chunk configuration. */
 void pr_clear_tuning(void);
 
+/*
+ * Tuning results across processes: the page tunes once per shape group and keeps the result
+ * ("TPSP Design" section 3, Profiling and fallback); these keep it past the process.
+ * pr_tuning_save writes every installed tuning result and chunk configuration to the text file
+ * `path` (replacing it), under a header naming the library version and a device key.
+ * pr_tuning_load reads such a file and installs its records (replacing installed ones of the
+ * same shape group and chunk size, keeping the others); a file of another library version or
+ * device key is refused (PR_ERR_UNSUPPORTED) and a malformed or invalid record fails the whole
+ * load (PR_ERR_INVALID_ARG, or the setter's code), leaving the installed tables as they were.
+ * device_key NULL means the current device ("<gcnArchName>:<CU count>", which needs a device);
+ * a caller may pass its own key (no white space).  Host-only apart from that device query.
+ */
+int pr_tuning_save(const char* path, const char* device_key);
+int pr_tuning_load(const char* path, const char* device_key);
+
 typedef struct {
   int threshold_tokens; /* INT32_MAX when inconclusive                         */
   int max_tokens;

@@ -83,6 +83,8 @@ SIGNATURES = {
     "pr_set_tuning": (_i, [_i, _i, _i, _i, _c.POINTER(_i), _c.POINTER(_i), _i]),
     "pr_set_chunk_config": (_i, [_i, _i, _i, _i, _i, _i, _i]),
     "pr_clear_tuning": (None, []),
+    "pr_tuning_save": (_i, [_c.c_char_p, _c.c_char_p]),
+    "pr_tuning_load": (_i, [_c.c_char_p, _c.c_char_p]),
     "pr_tune": (_i, [_c.POINTER(_i), _c.POINTER(_i), _i, _i, _c.POINTER(_i), _i, _c.POINTER(_i),
                      _i, _i, _c.POINTER(pr_tune_report), _c.POINTER(_d), _vp]),
     "pr_strerror": (_c.c_char_p, [_i]),
@@ -253,6 +255,16 @@ def pr_set_chunk_config(K: int, H: int, microchunk: int, tile_m: int, tile_n: in
 
 def pr_clear_tuning() -> None:
     _lib().pr_clear_tuning()
+
+
+def pr_tuning_save(path: str, device_key: Optional[str] = None) -> None:
+    _check(_lib().pr_tuning_save(os.fsencode(path),
+                                 None if device_key is None else device_key.encode()))
+
+
+def pr_tuning_load(path: str, device_key: Optional[str] = None) -> None:
+    _check(_lib().pr_tuning_load(os.fsencode(path),
+                                 None if device_key is None else device_key.encode()))
 
 
 def pr_tune(Ks: Sequence[int], Hs: Sequence[int], norm_kind: int, T_grid: Sequence[int],

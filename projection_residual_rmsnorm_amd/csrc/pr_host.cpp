@@ -537,4 +537,143 @@ void pr_clear_tuning(void) {
   g_chunk_cfg.clear();
 }
 
+// Tuning file, one record per line (tokens separated by single spaces):
+//   pr_tuning 1 <library version> <device key>
+//   tuning <K> <H> <threshold> <max tokens> <nT> then nT pairs <T> <chunk>
+//   chunk <K> <H> <microchunk> <tile rows> <tile columns> <K split> <waves>
+int pr_tuning_save(const char* path, const char* device_key) {
+  if (path == nullptr) return fail(PR_ERR_INVALID_ARG, "path is NULL");
+  std::string key;
+  if (device_key != nullptr) {
+    key = device_key;
+  } else {
+    const int rc = current_device_key(&key);
+    if (rc != PR_OK) return rc;
+  }
+  if (key.empty() || key.find_first_of(" \t\n") != std::string::npos)
+    return fail(PR_ERR_INVALID_ARG, "device key \"%s\" is empty or has white space", key.c_str());
+  std::string text = "pr_tuning 1 " + std::to_string(PR_VERSION) + " " + key + "\n";
+  {
+    std::lock_guard<std::mutex> lk(g_tuning_mu);
+    for (const auto& kv : g_tuning) {
+      const Tuning& tu = kv.second;
+      text += "tuning " + std::to_string(kv.first.first) + " " + std::to_string(kv.first.second) +
+              " " + std::to_string(tu.threshold) + " " + std::to_string(tu.max_tokens) + " " +
+              std::to_string(tu.T_grid.size());
+      for (size_t i = 0; i < tu.T_grid.size(); ++i)
+        text += " " + std::to_string(tu.T_grid[i]) + " " + std::to_string(tu.mc_for_T[i]);
+      text += "\n";
+    }
+    for (const auto& kv : g_chunk_cfg) {
+      const GemmCfg& g = kv.second;
+      text += "chunk " + std::to_string(std::get<0>(kv.first)) + " " +
+              std::to_string(std::get<1>(kv.first)) + " " + std::to_string(std::get<2>(kv.first)) +
+              " " + std::to_string(g.bm) + " " + std::to_string(g.bn) + " " +
+              std::to_string(g.split) + " " + std::to_string(g.waves) + "\n";
+    }
+  }
+  FILE* f = std::fopen(path, "w");
+  if (f == nullptr) return fail(PR_ERR_INVALID_ARG, "cannot write %s", path);
+  const bool ok = std::fwrite(text.data(), 1, text.size(), f) == text.size();
+  if (std::fclose(f) != 0 || !ok) return fail(PR_ERR_INVALID_ARG, "cannot write %s", path);
+  return PR_OK;
+}
+
+namespace {
+// Whole-line integer parsing: every token must be a decimal integer in int range.
+bool parse_ints(const std::vector<std::string>& tok, size_t from, std::vector<long long>* out) {
+  for (size_t i = from; i < tok.size(); ++i) {
+    const char* b = tok[i].c_str();
+    char* e = nullptr;
+    const long long v = std::strtoll(b, &e, 10);
+    if (e == b || *e != '\0' || v < INT32_MIN || v > INT32_MAX) return false;
+    out->push_back(v);
+  }
+  return true;
+}
+}  // namespace
+
+int pr_tuning_load(const char* path, const char* device_key) {
+  if (path == nullptr) return fail(PR_ERR_INVALID_ARG, "path is NULL");
+  std::string key;
+  if (device_key != nullptr) {
+    key = device_key;
+  } else {
+    const int rc = current_device_key(&key);
+    if (rc != PR_OK) return rc;
+  }
+  FILE* f = std::fopen(path, "r");
+  if (f == nullptr) return fail(PR_ERR_INVALID_ARG, "cannot read %s", path);
+  std::vector<std::vector<std::string>> lines;
+  {
+    std::string cur;
+    std::vector<std::string> tok;
+    int c;
+    while ((c = std::fgetc(f)) != EOF) {
+      if (c == ' ' || c == '\n') {
+        if (!cur.empty()) tok.push_back(cur);
+        cur.clear();
+        if (c == '\n') {
+          if (!tok.empty()) lines.push_back(tok);
+          tok.clear();
+        }
+      } else {
+        cur.push_back((char)c);
+      }
+    }
+    if (!cur.empty()) tok.push_back(cur);
+    if (!tok.empty()) lines.push_back(tok);
+  }
+  std::fclose(f);
+  if (lines.empty() || lines[0].size() != 4 || lines[0][0] != "pr_tuning" || lines[0][1] != "1")
+    return fail(PR_ERR_INVALID_ARG, "%s is not a tuning file of format 1", path);
+  if (lines[0][2] != std::to_string(PR_VERSION))
+    return fail(PR_ERR_UNSUPPORTED, "%s was written by library version %s (this is %d)", path,
+                lines[0][2].c_str(), PR_VERSION);
+  if (lines[0][3] != key)
+    return fail(PR_ERR_UNSUPPORTED, "%s was tuned on device %s, not %s", path,
+                lines[0][3].c_str(), key.c_str());
+  // Install every record through the setters (which validate it); on any failure restore the
+  // tables as they were, so a bad file installs nothing.
+  std::map<std::pair<int, int>, Tuning> saved_tuning;
+  std::map<std::tuple<int, int, int>, GemmCfg> saved_chunk;
+  {
+    std::lock_guard<std::mutex> lk(g_tuning_mu);
+    saved_tuning = g_tuning;
+    saved_chunk = g_chunk_cfg;
+  }
+  int rc = PR_OK;
+  for (size_t ln = 1; ln < lines.size() && rc == PR_OK; ++ln) {
+    const auto& tok = lines[ln];
+    std::vector<long long> v;
+    if (!parse_ints(tok, 1, &v)) {
+      rc = fail(PR_ERR_INVALID_ARG, "%s line %zu: not a list of integers", path, ln + 1);
+    } else if (tok[0] == "tuning" && v.size() >= 5 && v[4] >= 0 &&
+               v.size() == 5 + 2 * (size_t)v[4]) {
+      std::vector<int> Tg, mc;
+      for (long long i = 0; i < v[4]; ++i) {
+        Tg.push_back((int)v[5 + 2 * i]);
+        mc.push_back((int)v[6 + 2 * i]);
+      }
+      rc = pr_set_tuning((int)v[0], (int)v[1], (int)v[2], (int)v[3], Tg.data(), mc.data(),
+                         (int)v[4]);
+    } else if (tok[0] == "chunk" && v.size() == 7) {
+      rc = pr_set_chunk_config((int)v[0], (int)v[1], (int)v[2], (int)v[3], (int)v[4], (int)v[5],
+                               (int)v[6]);
+    } else {
+      rc = fail(PR_ERR_INVALID_ARG, "%s line %zu: unknown or malformed record", path, ln + 1);
+    }
+  }
+  if (rc != PR_OK) {
+    const std::string msg = pr_last_error();
+    {
+      std::lock_guard<std::mutex> lk(g_tuning_mu);
+      g_tuning = saved_tuning;
+      g_chunk_cfg = saved_chunk;
+    }
+    return fail(rc, "%s", msg.c_str());
+  }
+  return PR_OK;
+}
+
 }  // extern "C"

@@ -44,6 +44,9 @@ bool log_enabled();
 // Auto-mode / explicit decision (host only); `microchunk` = -1 marks the unfused entry point.
 int decide(int T, int K, int H, int microchunk, pr_decision* d);
 
+// Identity of the current device for tuning files: "<gcnArchName>:<CU count>" (runtime).
+int current_device_key(std::string* key);
+
 // Environment overrides: returns PR_OK and sets the values (0 when unset) or an error for a
 // malformed value.
 int read_overrides(int* mc_override, int* threshold_override);

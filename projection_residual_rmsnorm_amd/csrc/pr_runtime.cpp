@@ -134,6 +134,19 @@ bool wait_fault_injected() {
   return v != nullptr && std::strcmp(v, "wait") == 0;
 }
 
+}  // namespace
+
+int current_device_key(std::string* key) {
+  int dev = -1;
+  PR_HIP(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  PR_HIP(hipGetDeviceProperties(&prop, dev));
+  *key = std::string(prop.gcnArchName) + ":" + std::to_string(prop.multiProcessorCount);
+  return PR_OK;
+}
+
+namespace {
+
 int get_ctx(DevCtx** out) {
   int dev = -1;
   PR_HIP(hipGetDevice(&dev));

@@ -526,3 +526,27 @@ def test_workload_parity_full_size(name):
         err = _check(d, r_dev, out_bits, "conventional" if mc is None else "fused", rows)
         print(name, mc, err, flush=True)
         assert np.all(np.isfinite(r_dev))
+
+
+def test_tuning_file_on_the_device(tmp_path):
+    """A tuning file saved on this device carries its key (architecture and CU count);
+    reloaded after a clear it restores every decision, and an auto-mode call then runs the
+    restored choice (the single launch at T=2048) with oracle parity."""
+    pr.pr_clear_tuning()
+    pr.pr_set_tuning(1024, 2048, 1024, 8192, [128, 1024], [128, pr.PR_SINGLE_LAUNCH])
+    pr.pr_set_chunk_config(1024, 2048, 128, 128, 128, 2, 8)
+    before = [pr.pr_select(T, 1024, 2048, 0) for T in (64, 512, 2048)]
+    path = tmp_path / "tune.txt"
+    pr.pr_tuning_save(str(path))
+    key = path.read_text().split("\n")[0].split()[3]
+    print("device key", key, flush=True)
+    assert key.startswith("gfx950") and key.rsplit(":", 1)[1].isdigit()
+    pr.pr_clear_tuning()
+    pr.pr_tuning_load(str(path))
+    assert [pr.pr_select(T, 1024, 2048, 0) for T in (64, 512, 2048)] == before
+    assert before[2]["path"] == pr.PR_PATH_SINGLE
+    d = synth.make_custom(2048, 1024, 2048, seed=21)
+    dev = Device(d)
+    r_dev, out_bits = dev.run(0)
+    _check(d, r_dev, out_bits, "fused")
+    pr.pr_clear_tuning()

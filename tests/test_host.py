@@ -433,3 +433,87 @@ def test_counter_summary_derivations(tmp_path):
     dv = derived({**t["mean"], "SQ_BUSY_CYCLES": 32 * 100e3 * 1.5})
     assert abs(dv["shader_clock_GHz"] - 1.5) < 1e-9
     assert abs(dv["mfma_util_at_shader_clock"] - 0.8) < 1e-9  # 0.5 of 2.4 GHz = 0.8 of 1.5
+
+
+# ------------------------------------------------------------------ tuning files
+TUNE_KEY = "gfx950-test:256"
+
+
+def _install_example_tuning():
+    pr.pr_set_tuning(4096, 4096, 1024, 8192, [128, 1024, 4096], [128, 512, pr.PR_SINGLE_LAUNCH])
+    pr.pr_set_tuning(8192, 8192, pr.INT32_MAX, 32768, [128, 32768], [512, 2048])  # inconclusive
+    pr.pr_set_chunk_config(4096, 4096, 512, 128, 128, 2, 8)
+    pr.pr_set_chunk_config(8192, 8192, 2048, 256, 256, 1, 4)
+
+
+def _decisions():
+    out = []
+    for K, H in ((4096, 4096), (8192, 8192)):
+        for T in (64, 128, 1000, 1024, 4000, 8192):
+            for mc in (0, 512, 2048):
+                out.append(pr.pr_select(T, K, H, mc))
+    return out
+
+
+def test_tuning_file_round_trip(tmp_path):
+    """Saved tuning results and chunk configurations, reloaded after a clear, give the same
+    decision for every call; a second save writes the same bytes."""
+    pr.pr_clear_tuning()
+    _install_example_tuning()
+    before = _decisions()
+    path = tmp_path / "tune.txt"
+    pr.pr_tuning_save(str(path), TUNE_KEY)
+    pr.pr_clear_tuning()
+    assert pr.pr_select(2048, 4096, 4096, 0)["reason"] == pr.REASON_NAMES.index("untuned")
+    pr.pr_tuning_load(str(path), TUNE_KEY)
+    assert _decisions() == before
+    again = tmp_path / "again.txt"
+    pr.pr_tuning_save(str(again), TUNE_KEY)
+    assert again.read_bytes() == path.read_bytes()
+    pr.pr_clear_tuning()
+
+
+@pytest.mark.parametrize("edit,code", [
+    (lambda t: t.replace(f" {TUNE_KEY}", " gfx942:304"), pr.PR_ERR_UNSUPPORTED),   # device
+    (lambda t: t.replace("pr_tuning 1 1 ", "pr_tuning 1 99 "), pr.PR_ERR_UNSUPPORTED),  # version
+    (lambda t: t.replace("pr_tuning 1", "pr_tuning 2"), pr.PR_ERR_INVALID_ARG),      # format
+    (lambda t: t + "chunk 4096 4096 256 100 128 1 8\n", pr.PR_ERR_INVALID_ARG),     # no such tile
+    (lambda t: t + "chunk 4096 4096 256 128 128 3 8\n", pr.PR_ERR_INVALID_ARG),     # split
+    (lambda t: t + "tuning 1024 1024 64 4096 1 64 5000\n", pr.PR_ERR_MICROCHUNK),   # chunk size
+    (lambda t: t + "tuning 1024 1024 64 4096 2 64 64\n", pr.PR_ERR_INVALID_ARG),    # pair count
+    (lambda t: t + "tuning 1024 1024 64 4096 2 512 64 64 64\n", pr.PR_ERR_INVALID_ARG),  # order
+    (lambda t: t + "chunk 4096 4096 x 128 128 1 8\n", pr.PR_ERR_INVALID_ARG),       # not a number
+    (lambda t: t + "grid 1 2 3\n", pr.PR_ERR_INVALID_ARG),                          # record kind
+])
+def test_tuning_file_refusals(tmp_path, edit, code):
+    """A file of another device or library version is refused; a malformed or invalid record
+    fails the whole load and leaves the installed tables as they were (its valid records,
+    read before the bad one, are rolled back)."""
+    pr.pr_clear_tuning()
+    _install_example_tuning()
+    path = tmp_path / "tune.txt"
+    pr.pr_tuning_save(str(path), TUNE_KEY)
+    pr.pr_clear_tuning()
+    pr.pr_set_tuning(2048, 2048, 256, 4096, [256], [256])  # installed before the load
+    kept = pr.pr_select(1000, 2048, 2048, 0)
+    path.write_text(edit(path.read_text()))
+    with pytest.raises(pr.PRError) as e:
+        pr.pr_tuning_load(str(path), TUNE_KEY)
+    assert e.value.code == code, pr.pr_last_error()
+    assert pr.pr_select(2048, 4096, 4096, 0)["reason"] == pr.REASON_NAMES.index("untuned")
+    assert pr.pr_select(1000, 2048, 2048, 0) == kept
+    pr.pr_clear_tuning()
+
+
+def test_tuning_file_needs_a_key_without_a_device(tmp_path):
+    """Without a device the current-device key cannot be formed: the call fails cleanly (a
+    caller-supplied key works, as above)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(pr.PRError):
+        pr.pr_tuning_save(str(tmp_path / "t.txt"))
+    with pytest.raises(pr.PRError):
+        pr.pr_tuning_save(str(tmp_path / "t.txt"), "has space")
+    with pytest.raises(pr.PRError):
+        pr.pr_tuning_load(str(tmp_path / "missing.txt"), TUNE_KEY)
