@@ -132,7 +132,10 @@ def derived(mean: Dict[str, float]) -> Dict[str, float]:
       lds_active_frac: LDS-active cycles per CU / (GRBM_GUI_ACTIVE / 8);
       shader_clock_GHz: SQ_BUSY_CYCLES (shader-clock cycles with waves present, summed over the
         32 shader engines) / (32 x duration), the clock the kernel actually ran at;
-      mfma_util_at_shader_clock: MFMA busy cycles / (SIMDs x duration x that clock)."""
+      mfma_util_at_shader_clock: MFMA busy cycles / (SIMDs x duration x that clock);
+      l1_l2_read_MB_at_64B: L1 -> L2 read requests x 64 bytes;
+      l1_l2_read_latency_cycles: summed request latency / requests;
+      l1_pending_stall_cycles_per_cu: cycles an L1 waited on data pending from L2, per CU."""
     out = {}
     simds = CU_COUNT * SIMDS_PER_CU
     busy, active = mean.get("SQ_VALU_MFMA_BUSY_CYCLES"), mean.get("GRBM_GUI_ACTIVE")
@@ -150,6 +153,13 @@ def derived(mean: Dict[str, float]) -> Dict[str, float]:
         out["shader_clock_GHz"] = clk
         if busy is not None:
             out["mfma_util_at_shader_clock"] = busy / (simds * dur * clk)
+    req = mean.get("TCP_TCC_READ_REQ_sum")
+    if req:
+        out["l1_l2_read_MB_at_64B"] = req * 64 / 1e6
+        if "TCP_TCC_READ_REQ_LATENCY_sum" in mean:
+            out["l1_l2_read_latency_cycles"] = mean["TCP_TCC_READ_REQ_LATENCY_sum"] / req
+    if "TCP_PENDING_STALL_CYCLES_sum" in mean:
+        out["l1_pending_stall_cycles_per_cu"] = mean["TCP_PENDING_STALL_CYCLES_sum"] / CU_COUNT
     if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:
         out["mfma_bf16_flops"] = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * MOP_FLOPS
         if dur:

@@ -433,6 +433,12 @@ def test_counter_summary_derivations(tmp_path):
     dv = derived({**t["mean"], "SQ_BUSY_CYCLES": 32 * 100e3 * 1.5})
     assert abs(dv["shader_clock_GHz"] - 1.5) < 1e-9
     assert abs(dv["mfma_util_at_shader_clock"] - 0.8) < 1e-9  # 0.5 of 2.4 GHz = 0.8 of 1.5
+    # L1 -> L2 reads: 64-byte requests, mean latency, pending-stall cycles per CU
+    dv = derived({**t["mean"], "TCP_TCC_READ_REQ_sum": 1e6, "TCP_TCC_READ_REQ_LATENCY_sum": 5e8,
+                  "TCP_PENDING_STALL_CYCLES_sum": 256 * 7e4})
+    assert dv["l1_l2_read_MB_at_64B"] == 64.0
+    assert dv["l1_l2_read_latency_cycles"] == 500.0
+    assert dv["l1_pending_stall_cycles_per_cu"] == 7e4
 
 
 # ------------------------------------------------------------------ tuning files
