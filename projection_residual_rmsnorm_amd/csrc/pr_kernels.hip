@@ -125,6 +125,15 @@ struct TileAcc {
   f32x16_t v[TM][TN];
 };
 
+// Main-loop tail hook: what the ring's last refills load.  With NoTail they re-read the last
+// stage (the buffers are never read again); a hook with kLoads >= 0 is called instead as
+// tail(j, buffer) for the j-th refill past the last stage (j = 0 .. NB-2) and must issue exactly
+// kLoads direct-to-LDS loads per wave, the count of a stage, so the loop's waits stay exact.
+struct NoTail {
+  static constexpr int kLoads = -1;
+  __device__ void operator()(int, char*) const {}
+};
+
 // Main loop of one output tile: the product of A[m0 .. m0+BM)[k_begin .. k_begin + 32 KG nk)
 // and the weight columns [n0 .. n0+BN) over the same K range, in the 32x32 MFMA accumulator
 // layout.  Returns with each wave past its own last fragment read: callers that reuse the
@@ -135,10 +144,10 @@ struct TileAcc {
 // half g of every stage.  Each wave then holds a partial sum over 1/KG of K (the caller adds
 // the groups' partials); with KG = 2 and 4-wave groups every SIMD runs two waves while each
 // wave keeps the large wave tile.
-template <int BM, int BN, int NB, int WM, int WN, int KG = 1>
+template <int BM, int BN, int NB, int WM, int WN, int KG = 1, typename Tail = NoTail>
 __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp, int M, int N, int K, int m0,
-    int n0, int k_begin, int nk) {
+    int n0, int k_begin, int nk, const Tail& tail = Tail()) {
   constexpr int GW = WM * WN;  // waves per group
   constexpr int NW = GW * KG;  // waves per workgroup (4: one per SIMD, 8: two per SIMD)
   constexpr int WTM = BM / WM;  // wave tile rows
@@ -158,6 +167,7 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   static_assert(NB >= 2 && NB <= 8 && NB * KG * (A_BYTES + B_BYTES) <= 160 * 1024, "LDS budget");
   static_assert(LPW * (P - 1) < 64, "vmcnt range");
   static_assert(KG == 1 || KG == 2, "one or two K groups");
+  static_assert(Tail::kLoads < 0 || Tail::kLoads == LPW, "a tail refill issues a stage's loads");
 
   constexpr int HALF = A_BYTES + B_BYTES;  // one 32-deep half of a stage
   constexpr int STAGE = KG * HALF;
@@ -275,9 +285,16 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
 
   // The refill is issued in every step so that the count of loads in flight is the same in
   // every step; past the last stage it re-reads the last stage (an L2 hit) into the buffer
-  // being refilled, which is never read again.
+  // being refilled, which is never read again, or runs the tail hook.
   auto step = [&](int kt, char* cur, char* next, char* refill) {
-    issue_stage(min(kt + P, nk - 1), refill);
+    if constexpr (Tail::kLoads >= 0) {
+      if (kt + P >= nk)
+        tail(kt + P - nk, refill);
+      else
+        issue_stage(kt + P, refill);
+    } else {
+      issue_stage(min(kt + P, nk - 1), refill);
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_frags(cur, 1, fa1, fb1);
     mfmas(fa0, fb0);
@@ -791,10 +808,11 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
 // row has tiles_n column tiles, one slot per row and column tile, and one counter per
 // 128-row block.
 //
-// The four waves that hand their rows over load the residual of the kept rows into LDS (ring
-// buffers 0..3, 32 rows of 1 KiB each) while the exchange completes; the four waves that keep
-// their rows add the partner's partial, form r + y in place in LDS and the row sums; all eight
-// waves then write the residual, wait for the row block and write the output from LDS.
+// The main loop's last four ring refills load the kept rows' residual into LDS (one 1 KiB row
+// per load, the loads a stage would take), so it lands while the last stages compute.  After
+// the loop the four waves that hand their rows over write the hand-over; the four waves that
+// keep their rows add the partner's partial, form r + y in place in LDS and the row sums; all
+// eight waves then write the residual, wait for the row block and write the output from LDS.
 //
 // Exchange regions: `xbuf` holds 128 KiB per workgroup and round parity (the region a
 // workgroup writes in round q is rewritten in round q + 2 only after the partner's round q + 1
@@ -802,6 +820,25 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
 // of the launch, per half h the XCD-id word [4 t + 2 h] and the ready word [4 t + 2 h + 1],
 // each {epoch of the launch that wrote it, value}.
 // --------------------------------------------------------------------------------------------
+// Tail hook of the pair form: the main loop's last NB - 1 refills load the kept rows'
+// residual instead of re-reading the last stage.  Refill j brings kept rows [32 j, 32 j + 32)
+// (1 KiB rows of 256 fp32 columns), four rows per wave, into the buffer it refills.
+struct ResidualTail {
+  static constexpr int kLoads = 4;
+  const float* R;
+  int N, n0, row0, M, wave;
+  uint32_t lane_off;
+  __device__ void operator()(int j, char* buf) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int row = row0 + 32 * j + 4 * wave + i;
+      row = row < M ? row : M - 1;  // rows past M are computed, never stored
+      load_to_lds16(reinterpret_cast<const char*>(R + (long long)row * N + n0), lane_off,
+                    buf + (4 * wave + i) * 1024);
+    }
+  }
+};
+
 template <int NB>
 __global__ void __launch_bounds__(512, 1)
     gemm_add_rmsnorm_pair_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp,
@@ -818,19 +855,24 @@ __global__ void __launch_bounds__(512, 1)
   constexpr int HB = 128;             // rows kept per workgroup
   constexpr int STAGE = (BM + BN) * kBK * 2;  // 32 KiB
   constexpr int XW = TM * TN * 8 * 64;        // 64-bit exchange words per wave (32 KiB)
-  static_assert(NB == 5 && STAGE == 32 * 1024, "residual in buffers 0..3, staging in 4");
+  static_assert(NB == 5 && STAGE == 32 * 1024, "four residual buffers and a staging buffer");
   constexpr int EP_LD = 64 + 4;
   constexpr int EP_BYTES = 16 * EP_LD * 4;
   static_assert(4 * EP_BYTES + (HB * WN + HB + 3) * 4 <= STAGE, "staging fits in buffer 4");
-  // Residual buffers 0..3 (separate LDS objects), chosen by a wave-uniform index.
-  auto rbuf = [](int u) -> char* {
+  // The main loop's last refills bring the kept rows' residual: block j (32 rows) lands in
+  // ring buffer (nk + j) % NB, and the buffer of the last stage, (nk - 1) % NB, is the staging
+  // buffer of the epilogue.  Buffers are separate LDS objects, chosen by a uniform index.
+  const int nk = K / 2 / kBK;  // >= NB - 1 (K >= 256), so the last NB - 1 steps are tail refills
+  auto ringbuf = [](int u) -> char* {
     char* const b0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
     char* const b1 = ring_buffer<1, STAGE, BM, BN, NB, WM, WN>();
     char* const b2 = ring_buffer<2, STAGE, BM, BN, NB, WM, WN>();
     char* const b3 = ring_buffer<3, STAGE, BM, BN, NB, WM, WN>();
-    return u == 0 ? b0 : (u == 1 ? b1 : (u == 2 ? b2 : b3));
+    char* const b4 = ring_buffer<4, STAGE, BM, BN, NB, WM, WN>();
+    return u == 0 ? b0 : (u == 1 ? b1 : (u == 2 ? b2 : (u == 3 ? b3 : b4)));
   };
-  char* const sb4 = ring_buffer<4, STAGE, BM, BN, NB, WM, WN>();
+  auto rbuf = [&](int j) -> char* { return ringbuf((nk + j) % NB); };
+  char* const sb4 = ringbuf((nk + NB - 1) % NB);
   float* const sred = reinterpret_cast<float*>(sb4 + 4 * EP_BYTES);
   float* const sinv = sred + HB * WN;
   int* const sflag = reinterpret_cast<int*>(sinv + HB);
@@ -887,8 +929,9 @@ __global__ void __launch_bounds__(512, 1)
     if (threadIdx.x == 0)
       __hip_atomic_store(my_words, tag | xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    TileAcc<TM, TN> acc = tile_mainloop<BM, BN, NB, WM, WN>(A, Bp, M, N, K, m0, n0, h * (K / 2),
-                                                            K / 2 / kBK);
+    const ResidualTail rtail{R, N, n0, own0, M, wave, (uint32_t)lane * 16u};
+    TileAcc<TM, TN> acc = tile_mainloop<BM, BN, NB, WM, WN, 1, ResidualTail>(
+        A, Bp, M, N, K, m0, n0, h * (K / 2), nk, rtail);
     // Plain hand-over only if the partner's id word is this launch's and names this XCD.
     unsigned long long pid = 0;
     if (threadIdx.x == 0)
@@ -909,16 +952,8 @@ __global__ void __launch_bounds__(512, 1)
     const unsigned long long* const xpart =
         xbuf + (size_t)((round & 1) * gridDim.x + partner) * (4 * XW);
     if (wm != h) {
-      // Fetch 32 rows of the kept rows' residual into ring buffer wn, then hand over this
-      // wave's rows (the partner keeps them): 16-byte plain stores (same XCD) or 8-byte
-      // device-scope stores, each in its own layout.
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        int row = own0 + wn * 32 + k;
-        row = row < M ? row : M - 1;  // rows past M are computed, never stored
-        load_to_lds16(reinterpret_cast<const char*>(R + (long long)row * N + n0),
-                      (uint32_t)el * 16u, rbuf(wn) + k * 1024);
-      }
+      // Hand over this wave's rows (the partner keeps them): 16-byte plain stores (same XCD)
+      // or 8-byte device-scope stores, each in its own layout.
       if (plain) {
         float4* xw = reinterpret_cast<float4*>(xmine + wn * XW);
 #pragma unroll
@@ -945,7 +980,7 @@ __global__ void __launch_bounds__(512, 1)
                                  __HIP_MEMORY_SCOPE_AGENT);
             }
       }
-      __builtin_amdgcn_s_waitcnt(PR_VMCNT(0));  // hand-over written, residual landed
+      __builtin_amdgcn_s_waitcnt(PR_VMCNT(0));  // hand-over written
     }
     __syncthreads();
     if (et == 0) {
@@ -1657,10 +1692,10 @@ int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, con
   if (M <= 0) return PR_OK;
   if (cfg.split == 2) {
     if (cfg.bm != 256 || cfg.bn != 256 || cfg.waves != 8 || cfg.kgroups != 1 ||
-        K % (2 * kBK) != 0 || N % 256 != 0 || N / 256 > 64)
+        K % (2 * kBK) != 0 || K < 256 || N % 256 != 0 || N / 256 > 64)
       return fail(PR_ERR_SHAPE, "single launch (pairs): N=%d K=%d with tile %dx%d, %d waves, %d "
-                  "K groups not supported (256x256, 8 waves, N a multiple of 256)", N, K, cfg.bm,
-                  cfg.bn, cfg.waves, cfg.kgroups);
+                  "K groups not supported (256x256, 8 waves, N a multiple of 256, K >= 256)", N,
+                  K, cfg.bm, cfg.bn, cfg.waves, cfg.kgroups);
     return launch_pair(x, Wp, r, w, out, slots, sync, pair_words, xbuf, xbuf_words, M, N, K, eps,
                        gemma, epoch, read_epoch, spin_limit, s, t0, t1);
   }
