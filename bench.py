@@ -123,6 +123,33 @@ def cpu_baseline(d, seconds: float) -> dict:
                       f"full batch"}
 
 
+def clock_settings() -> dict:
+    """The GPU's clock settings as amd-smi reports them (run as a child process before this
+    process initialises the GPU): per-XCD shader-clock range, whether it is locked, and the
+    memory clock.  Clocks are left at their defaults; None when amd-smi is unavailable."""
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    try:
+        proc = subprocess.run([exe, "metric", "--clock", "--json"], capture_output=True,
+                              text=True, timeout=60)
+        gpu = json.loads(proc.stdout)["gpu_data"][0]["clock"]
+    except Exception:  # pragma: no cover - depends on the box
+        return None
+
+    def mhz(v):
+        return v["value"] if isinstance(v, dict) else None
+    gfx = [v for k, v in gpu.items() if k.startswith("gfx_")]
+    mem = gpu.get("mem_0", {})
+    return {"source": "amd-smi metric --clock",
+            "sclk_max_MHz": sorted({mhz(v.get("max_clk")) for v in gfx} - {None}),
+            "sclk_min_MHz": sorted({mhz(v.get("min_clk")) for v in gfx} - {None}),
+            "sclk_locked": sorted({v.get("clk_locked") for v in gfx}),
+            "xcds": len(gfx), "mclk_MHz": mhz(mem.get("clk"))}
+
+
 def tune_sweep(pr, torch, args) -> int:
     """Token-threshold search over the long-prefill sweep (K = H = 8192): every chunk size is
     checked against the conventional path, then timed; prints the table and the crossover."""
@@ -250,6 +277,7 @@ def main() -> int:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
               "inter-GPU step in this build", file=sys.stderr)
         return 2
+    clocks = clock_settings()  # before this process touches the GPU
     import torch
     import projection_residual_rmsnorm_amd as pr
     import synth
@@ -396,6 +424,7 @@ def main() -> int:
         "per_microchunk": {str(k): v for k, v in per_mc.items()},
         "chunk_configs": chunk_cfgs,
         "conventional": conv,
+        "clocks": clocks,
     }
     # Per-call statistics of the headline form and the conventional path: residual restored
     # before every call; warm (operands may sit in the Infinity Cache) and flushed.
