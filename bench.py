@@ -92,6 +92,24 @@ def per_call_stats(call, r, r0, steps: int, torch, stream, flush=None) -> dict:
             "p90_ms": float(np.percentile(t, 90)), "calls": len(times)}
 
 
+def add_per_call_stats(result, fused_call, conventional, r, steps, torch, stream, dev,
+                       form: str) -> None:
+    r0 = r.clone()
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MB
+    result["per_call"] = {
+        "form": form,
+        "fused_warm": per_call_stats(fused_call, r, r0, steps, torch, stream),
+        "fused_flushed": per_call_stats(fused_call, r, r0, steps, torch, stream, flush),
+        "conventional_warm": per_call_stats(conventional, r, r0, steps, torch, stream),
+        "conventional_flushed": per_call_stats(conventional, r, r0, steps, torch, stream, flush)}
+    del flush, r0
+    pc = result["per_call"]
+    log(f"per call (median ms, warm / flushed): fused {pc['fused_warm']['median_ms']:.4f} / "
+        f"{pc['fused_flushed']['median_ms']:.4f}, conventional "
+        f"{pc['conventional_warm']['median_ms']:.4f} / "
+        f"{pc['conventional_flushed']['median_ms']:.4f}")
+
+
 def traffic_label(workload: str, mc, chunk_cfgs: dict) -> str:
     """Label of a traffic measurement: workload, fused form (chunk size or "single") and the
     projection configuration it ran with (counters taken under another configuration do not
@@ -427,22 +445,13 @@ def main() -> int:
         "clocks": clocks,
     }
     # Per-call statistics of the headline form and the conventional path: residual restored
-    # before every call; warm (operands may sit in the Infinity Cache) and flushed.
-    r0 = r.clone()
-    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MB
-    result["per_call"] = {
-        "form": "single launch" if single else f"mc={mc}",
-        "fused_warm": per_call_stats(fused(mc), r, r0, args.steps, torch, stream),
-        "fused_flushed": per_call_stats(fused(mc), r, r0, args.steps, torch, stream, flush),
-        "conventional_warm": per_call_stats(conventional, r, r0, args.steps, torch, stream),
-        "conventional_flushed": per_call_stats(conventional, r, r0, args.steps, torch, stream,
-                                               flush)}
-    del flush, r0
-    log("per call (median ms, warm / flushed): fused "
-        f"{result['per_call']['fused_warm']['median_ms']:.4f} / "
-        f"{result['per_call']['fused_flushed']['median_ms']:.4f}, conventional "
-        f"{result['per_call']['conventional_warm']['median_ms']:.4f} / "
-        f"{result['per_call']['conventional_flushed']['median_ms']:.4f}")
+    # before every call; warm (operands may sit in the Infinity Cache) and flushed.  Not in
+    # profiler runs (--only-single), whose kernel averages must match the timed region.
+    if args.only_single:
+        result["per_call"] = None
+    else:
+        add_per_call_stats(result, fused(mc), conventional, r, args.steps, torch, stream, dev,
+                           "single launch" if single else f"mc={mc}")
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
