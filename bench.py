@@ -52,6 +52,9 @@ def parse():
                     help="run the token-threshold search on the K=H=8192 sweep and print it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--addnorm-roofline", action="store_true",
+                    help="HBM rate of the conventional path's add/norm kernel on every workload, "
+                         "Infinity Cache warm and flushed, beside a plain device copy")
     ap.add_argument("--tp-share", default="",
                     help="comma-separated tensor-parallel degrees P: time one rank's share of "
                          "the workload (projection over K/P, add/norm of T/P rows with P fp32 "
@@ -195,6 +198,78 @@ def tune_sweep(pr, torch, args) -> int:
     return 0
 
 
+def addnorm_roofline(pr, torch, args) -> int:
+    """The add/norm kernel alone, as the conventional path launches it after the projection:
+    algorithmic bytes per element (y read: 2 for bf16, 4 per fp32 plane; r read 4, r write 4,
+    out write 2) over its event-timed duration, with the Infinity Cache warm and flushed (a
+    512 MB write before each call), against 8 TB/s and against a device copy of the same bytes
+    (half read, half written) timed the same way."""
+    import synth
+    dev = "cuda:0"
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    names = ["o_proj", "down_proj", "gemma", "sweep_T8192"]
+    rows = []
+    for name in names:
+        wl = synth.WORKLOADS[name]
+        T, K, H = wl.T, wl.K, wl.H
+        d = synth.make_inputs(wl, seed=0)
+        x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+        W_src = torch.from_numpy(d["W"].view(np.int16)).to(dev)
+        Wp = torch.empty(K * H, dtype=torch.int16, device=dev)
+        pr.pr_prepare_weight(W_src, pr.PR_WEIGHT_OUT_IN, Wp, K, H)
+        del W_src
+        r = torch.from_numpy(d["residual"]).to(dev)
+        r0 = r.clone()
+        w = torch.from_numpy(d["norm_w"]).to(dev)
+        out = torch.empty((T, H), dtype=torch.int16, device=dev)
+        split = pr.pr_select(T, K, H, pr.PR_SELECT_UNFUSED)["split_k"]
+        per_elem = (2 if split == 1 else 4 * split) + 10
+        nbytes = per_elem * T * H
+        res = {"workload": name, "T": T, "H": H, "y": "bf16" if split == 1 else f"{split} fp32 planes",
+               "bytes_per_elem": per_elem, "bytes": nbytes}
+        for mode in ("warm", "flushed"):
+            ts = []
+            for i in range(max(args.steps // 5, 5) + 2):
+                r.copy_(r0)
+                if mode == "flushed":
+                    flush.fill_(float(i))
+                pr.pr_profile_enable(True)
+                pr.proj_add_rmsnorm_unfused(x, Wp, r, w, d["eps"], T, K, H, wl.norm_kind, out)
+                prof = pr.pr_profile_read()
+                pr.pr_profile_enable(False)
+                if i >= 2:
+                    ts.append(prof["addnorm_ms"] / max(prof["addnorm_launches"], 1))
+            t = float(np.median(ts)) / 1e3
+            res[f"{mode}_us"] = t * 1e6
+            res[f"{mode}_GBs"] = nbytes / t / 1e9
+        # a device copy of the same bytes: half read, half written
+        src = torch.empty(nbytes // 2 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        cts = []
+        for i in range(7):
+            flush.fill_(float(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            e1.synchronize()
+            if i >= 2:
+                cts.append(e0.elapsed_time(e1) / 1e3)
+        res["copy_flushed_GBs"] = nbytes / float(np.median(cts)) / 1e9
+        res["frac_hbm_peak_flushed"] = res["flushed_GBs"] / PEAK_HBM_GBS
+        rows.append(res)
+        log(f"{name}: add/norm {res['warm_us']:.1f} us warm ({res['warm_GBs']:.0f} GB/s), "
+            f"{res['flushed_us']:.1f} us flushed ({res['flushed_GBs']:.0f} GB/s); copy of the same "
+            f"bytes {res['copy_flushed_GBs']:.0f} GB/s")
+        del x, Wp, r, r0, w, out, src, dst
+        torch.cuda.empty_cache()
+    print(json.dumps({"addnorm_roofline": rows, "peak_GBs": PEAK_HBM_GBS}), flush=True)
+    return 0
+
+
 XGMI_LINK_GBS = 153.0   # one xGMI link, per direction
 
 
@@ -306,6 +381,8 @@ def main() -> int:
         return tune_sweep(pr, torch, args)
     if args.tp_share:
         return tp_share(pr, torch, args)
+    if args.addnorm_roofline:
+        return addnorm_roofline(pr, torch, args)
     wl = synth.WORKLOADS[args.workload]
     T, K, H = wl.T, wl.K, wl.H
     log(f"workload {wl.name}: T={T} K={K} H={H} chunk sizes {wl.microchunks}")
