@@ -137,8 +137,15 @@ def cpu_baseline(d, seconds: float) -> dict:
         oracle.proj_add_rmsnorm(x, d["W"], r, d["norm_w"], d["eps"], d["norm_kind"], "fused")
         t_total += time.perf_counter() - t0
         reps += 1
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                       None)
+    except OSError:  # pragma: no cover
+        pass
     return {"value": rows * reps / t_total, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "cpu": cpu, "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"first {rows} of {d['T']} tokens, {reps} calls of the float64 oracle "
                       f"({t_total:.1f} s); rows are independent, so tokens/s scales to the "
                       f"full batch"}
