@@ -151,8 +151,12 @@ int proj_add_rmsnorm_unfused(const uint16_t* x, const uint16_t* W, float* residu
  * with n <= 64 for one of the tiles the library instantiates (256 or 128 columns), else
  * PR_ERR_SHAPE.  The result agrees with the fused pipeline within rounding (the sum of squares
  * is taken in another order).  Uses a device workspace of T * H / 128 64-bit slots and
- * 2 + T / 128 counters, shared by all calls on the device (calls on one device are
- * sequential, as for every entry point).
+ * 3 + T / 128 words (status, completion counters, and the launch epoch, which the kernel
+ * itself advances), shared by all calls on the device (calls on one device are sequential,
+ * as for every entry point).  A call allocates or clears workspace only when it needs more
+ * than earlier calls did; once a call of the same or a larger shape has run on the device,
+ * a call makes no allocation, fill or host synchronisation and can be captured in a HIP
+ * graph on a non-null stream and replayed (each replay takes a fresh epoch on the device).
  *
  * A second form splits the K range of each 256 x 256 tile over a pair of workgroups, which
  * swap partial sums before the residual add (reached with the debug overrides

@@ -76,26 +76,39 @@ int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_s
                        void* done_event = nullptr, void* start_timing = nullptr,
                        void* stop_timing = nullptr);
 
+// Device workspace of the single launch (owned by the runtime, zeroed when allocated).
+//   slots: slot_words 64-bit row-partial slots, {epoch, fp32 partial}; a launch needs
+//          (N / tile columns) * M of them.
+//   sync:  [0] status bits (bit 0: a wait gave up after spin_limit polls), [1] finished
+//          workgroups, [2] epoch of the last launch, [3 ..] one completion counter per tile
+//          row (per 128-row block for the pair form); all but [0] and [2] are zero between
+//          launches, and [2] advances by one per launch (on the device).
+//   pwords, xbuf: the pair form's XCD-id and ready words (pword_words 64-bit words, epoch
+//          tagged like the slots; 4 per 256x256 tile) and exchange regions (xbuf_words 64-bit
+//          words: 16384 per workgroup of a round, twice that for launches of several rounds).
+//   fault_mask: 0, or a nonzero mask that makes every wait look for an epoch no word carries
+//          (tests of the give-up path); spin_limit: polls before a wait gives up.
+// An epoch-tagged word holding the launch's epoch was written by that launch; a cleared word
+// holds epoch 0, which no launch uses.
+struct SingleWs {
+  unsigned long long* slots = nullptr;
+  unsigned long long slot_words = 0;
+  unsigned* sync = nullptr;
+  unsigned long long* pwords = nullptr;
+  unsigned long long pword_words = 0;
+  unsigned long long* xbuf = nullptr;
+  size_t xbuf_words = 0;
+  unsigned fault_mask = 0;
+  unsigned spin_limit = 0;
+};
+
 // Projection, residual add and RMSNorm of M rows in one launch (tile cfg.bm x cfg.bn, 8 waves
-// or the 4-wave 256x128 form; N % cfg.bn == 0, N / cfg.bn <= 64).  slots: (N / cfg.bn) * M
-// 64-bit row-partial slots; a slot holding `epoch` in its high word is taken as written by
-// this launch, so epoch must differ from every value the slots held before (start from a
-// zeroed buffer, epoch >= 1).  The row reads look for read_epoch (= epoch; any other value
-// makes every wait give up).  sync: 2 + ceil(M / cfg.bm) words (split 2: 2 + 2 ceil(M / 256)),
-// zero before the launch and zero again after it, except word 0, which collects status bits
-// (bit 0: a wait gave up after spin_limit polls).
-// cfg.split == 2 selects the pair form (256x256, 8 waves, K halves on two workgroups):
-// pair_words holds 4 * ceil(M / 256) * (N / 256) 64-bit words with the same epoch rule as the
-// slots, and xbuf xbuf_words 64-bit words of exchange regions (16384 per workgroup of a round,
-// twice that when the launch takes several rounds).
+// or the 4-wave 256x128 form; N % cfg.bn == 0, N / cfg.bn <= 64); cfg.split == 2 selects the
+// pair form (256x256, 8 waves, K halves on two workgroups; N a multiple of 256, K >= 256).
 int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
-                            uint16_t* out, unsigned long long* slots, unsigned* sync, int M,
-                            int N, int K, const GemmCfg& cfg, float eps, int gemma,
-                            unsigned epoch, unsigned read_epoch, unsigned spin_limit,
-                            void* stream, void* start_timing = nullptr,
-                            void* stop_timing = nullptr,
-                            unsigned long long* pair_words = nullptr,
-                            unsigned long long* xbuf = nullptr, size_t xbuf_words = 0);
+                            uint16_t* out, const SingleWs& ws, int M, int N, int K,
+                            const GemmCfg& cfg, float eps, int gemma, void* stream,
+                            void* start_timing = nullptr, void* stop_timing = nullptr);
 
 int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,
                           void* stream);

@@ -444,6 +444,39 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
 // slots: tiles_n columns of M 64-bit slots (slot of row t and tile column q at q * M + t, so
 // the slot accesses of a wave are contiguous).
 // --------------------------------------------------------------------------------------------
+// Launch epochs.  sync[2] holds the epoch of the last launch; a launch uses one more.  Every
+// workgroup reads it at its start, and only the launch's last workgroup to finish (when every
+// other workgroup has finished) advances it, so all workgroups of a launch agree without any
+// host involvement and a captured launch replays with a fresh epoch each time.  A cleared word
+// carries epoch 0, which no launch uses.  Wave-uniform.
+__device__ __forceinline__ unsigned launch_epoch(const unsigned* sync) {
+  return __builtin_amdgcn_readfirstlane(
+             __hip_atomic_load(sync + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u;
+}
+
+// End of a launch, run by all threads of its last workgroup: the `ncounters` completion
+// counters (sync[3 ..]) and the finished count back to zero, and the epoch advanced.  The
+// launch that used the last 32-bit epoch first clears every epoch-tagged word (both buffers,
+// n0 and n1 words) so that the restarted epochs cannot meet a stale tag.
+__device__ void finish_launch(unsigned* sync, int ncounters, unsigned epoch,
+                              unsigned long long* tagged0, unsigned long long n0,
+                              unsigned long long* tagged1, unsigned long long n1) {
+  for (int i = threadIdx.x; i < ncounters; i += blockDim.x)
+    __hip_atomic_store(sync + 3 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool wrap = epoch == 0xFFFFFFFFu;
+  if (wrap) {
+    for (unsigned long long i = threadIdx.x; i < n0; i += blockDim.x)
+      __hip_atomic_store(tagged0 + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (unsigned long long i = threadIdx.x; i < n1; i += blockDim.x)
+      __hip_atomic_store(tagged1 + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(sync + 2, wrap ? 0u : epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Sum over each group of LANES consecutive lanes (8 or 16, within one 16-lane DPP row); every
 // lane of the group gets the same value (each step adds a lane and its partner, which is
 // commutative, so the partners' results are bitwise equal).
@@ -469,7 +502,9 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
                             uint16_t* __restrict__ out, unsigned long long* __restrict__ slots,
                             unsigned* __restrict__ sync, int M, int N, int K, int tiles_m,
                             int tiles_n, int rows_per_round, float eps, int gemma,
-                            unsigned epoch, unsigned read_epoch, unsigned spin_limit) {
+                            unsigned fault_mask, unsigned spin_limit,
+                            unsigned long long* __restrict__ pwords,
+                            unsigned long long slot_words, unsigned long long pword_words) {
   // Main loop: KG groups of WM x WN waves (wave tiles BM/WM x BN/WN, TM x TN MFMA blocks).
   // Epilogue: after the groups' partials are combined, EWM x WN waves, each owning a
   // BM/EWM x BN/WN tile (ETM x TN blocks).
@@ -495,6 +530,8 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
   const int wm = ((KG == 1 ? wave : wave % GW) / WN) * KG + kgrp;  // epilogue row block
   const int wn = wave % WN;
   const float g0 = gemma ? 1.0f : 0.0f;
+  const unsigned epoch = launch_epoch(sync);
+  const unsigned read_epoch = epoch ^ fault_mask;  // fault_mask != 0: every wait gives up
 
   constexpr int EP_LD = WTN + 4;
   constexpr int EP_BYTES = 16 * EP_LD * 4;
@@ -682,7 +719,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-      unsigned* cnt = sync + 2 + tm;
+      unsigned* cnt = sync + 3 + tm;
       __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       unsigned polls = 0;
       while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
@@ -779,12 +816,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     *sflag = prev == gridDim.x - 1;
   }
   __syncthreads();
-  if (*sflag) {
-    for (int i = threadIdx.x; i < tiles_m; i += blockDim.x)
-      __hip_atomic_store(sync + 2 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0)
-      __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (*sflag) finish_launch(sync, tiles_m, epoch, slots, slot_words, pwords, pword_words);
 }
 
 // --------------------------------------------------------------------------------------------
@@ -848,8 +880,9 @@ __global__ void __launch_bounds__(512, 1)
                                  unsigned long long* __restrict__ pwords,
                                  unsigned long long* __restrict__ xbuf, int M, int N, int K,
                                  int tiles_m, int tiles_n, int rows_per_round, float eps,
-                                 int gemma, unsigned epoch, unsigned read_epoch,
-                                 unsigned spin_limit) {
+                                 int gemma, unsigned fault_mask, unsigned spin_limit,
+                                 unsigned long long slot_words,
+                                 unsigned long long pword_words) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
   constexpr int TM = 4, TN = 2;       // 128 x 64 wave tiles
   constexpr int HB = 128;             // rows kept per workgroup
@@ -883,6 +916,8 @@ __global__ void __launch_bounds__(512, 1)
   const int wm = wave / WN;
   const int wn = wave % WN;
   const float g0 = gemma ? 1.0f : 0.0f;
+  const unsigned epoch = launch_epoch(sync);
+  const unsigned read_epoch = epoch ^ fault_mask;  // fault_mask != 0: every wait gives up
 
   for (int round = 0; round * rows_per_round < tiles_m; ++round) {
     const int rows_here = min(rows_per_round, tiles_m - round * rows_per_round);
@@ -1093,7 +1128,7 @@ __global__ void __launch_bounds__(512, 1)
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    unsigned* const cnt = sync + 2 + tm * 2 + h;
+    unsigned* const cnt = sync + 3 + tm * 2 + h;
     if (et == 0)
       __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // The updated residual: 16 rows of 1 KiB per wave, from LDS.
@@ -1201,12 +1236,7 @@ __global__ void __launch_bounds__(512, 1)
     *sflag = prev == gridDim.x - 1;
   }
   __syncthreads();
-  if (*sflag) {
-    for (int i = threadIdx.x; i < 2 * tiles_m; i += blockDim.x)
-      __hip_atomic_store(sync + 2 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0)
-      __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (*sflag) finish_launch(sync, 2 * tiles_m, epoch, slots, slot_words, pwords, pword_words);
 }
 
 // --------------------------------------------------------------------------------------------
@@ -1566,9 +1596,8 @@ int resident_workgroups(Kern kern, int threads, int* out) {
 
 template <int BM, int BN, int NB, int WM, int WN, int KG>
 int launch_single_t(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
-                    uint16_t* out, unsigned long long* slots, unsigned* sync, int M, int N,
-                    int K, float eps, int gemma, unsigned epoch, unsigned read_epoch,
-                    unsigned spin_limit, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+                    uint16_t* out, const SingleWs& ws, int M, int N, int K, float eps, int gemma,
+                    hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   auto kern = gemm_add_rmsnorm_kernel<BM, BN, NB, WM, WN, KG>;
   constexpr int threads = WM * WN * KG * 64;
   static int resident = 0;  // per instantiation; the library runs on one kind of device
@@ -1582,12 +1611,13 @@ int launch_single_t(const uint16_t* x, const uint16_t* Wp, float* r, const float
   const unsigned grid = (unsigned)(rows_per_round * tiles_n);
   if (t0 != nullptr) {
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, t0, t1, 0, x, Wp, r, w, out,
-                          slots, sync, M, N, K, tiles_m, tiles_n, rows_per_round, eps, gemma,
-                          epoch, read_epoch, spin_limit);
+                          ws.slots, ws.sync, M, N, K, tiles_m, tiles_n, rows_per_round, eps,
+                          gemma, ws.fault_mask, ws.spin_limit, ws.pwords, ws.slot_words,
+                          ws.pword_words);
   } else {
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, Wp, r, w, out, slots, sync, M,
-                       N, K, tiles_m, tiles_n, rows_per_round, eps, gemma, epoch, read_epoch,
-                       spin_limit);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, Wp, r, w, out, ws.slots,
+                       ws.sync, M, N, K, tiles_m, tiles_n, rows_per_round, eps, gemma,
+                       ws.fault_mask, ws.spin_limit, ws.pwords, ws.slot_words, ws.pword_words);
   }
   return check_launch("gemm_add_rmsnorm_kernel");
 }
@@ -1595,10 +1625,8 @@ int launch_single_t(const uint16_t* x, const uint16_t* Wp, float* r, const float
 // Pair form (256 x 256 tiles, 8 waves, K split over two workgroups).  Rounds cover whole tile
 // rows; every pair and row block of a round is resident at once.
 int launch_pair(const uint16_t* x, const uint16_t* Wp, float* r, const float* w, uint16_t* out,
-                unsigned long long* slots, unsigned* sync, unsigned long long* pwords,
-                unsigned long long* xbuf, size_t xbuf_words, int M, int N, int K, float eps,
-                int gemma, unsigned epoch, unsigned read_epoch, unsigned spin_limit,
-                hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+                const SingleWs& ws, int M, int N, int K, float eps, int gemma, hipStream_t s,
+                hipEvent_t t0, hipEvent_t t1) {
   auto kern = gemm_add_rmsnorm_pair_kernel<5>;
   constexpr int threads = 512;
   static int resident = 0;
@@ -1612,17 +1640,18 @@ int launch_pair(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
                 "the %d resident workgroups", 2 * tiles_n, resident);
   const unsigned grid = (unsigned)(2 * rows_per_round * tiles_n);
   const size_t parities = rows_per_round < tiles_m ? 2 : 1;
-  if (xbuf == nullptr || pwords == nullptr || parities * grid * 16384u > xbuf_words)
+  if (ws.xbuf == nullptr || ws.pwords == nullptr || parities * grid * 16384u > ws.xbuf_words)
     return fail(PR_ERR_INVALID_ARG, "single launch (pairs): exchange buffer of %zu words is "
-                "smaller than %zu", xbuf_words, parities * grid * 16384u);
+                "smaller than %zu", ws.xbuf_words, parities * grid * 16384u);
   if (t0 != nullptr) {
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, t0, t1, 0, x, Wp, r, w, out,
-                          slots, sync, pwords, xbuf, M, N, K, tiles_m, tiles_n, rows_per_round,
-                          eps, gemma, epoch, read_epoch, spin_limit);
+                          ws.slots, ws.sync, ws.pwords, ws.xbuf, M, N, K, tiles_m, tiles_n,
+                          rows_per_round, eps, gemma, ws.fault_mask, ws.spin_limit,
+                          ws.slot_words, ws.pword_words);
   } else {
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, Wp, r, w, out, slots, sync,
-                       pwords, xbuf, M, N, K, tiles_m, tiles_n, rows_per_round, eps, gemma, epoch,
-                       read_epoch, spin_limit);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, Wp, r, w, out, ws.slots,
+                       ws.sync, ws.pwords, ws.xbuf, M, N, K, tiles_m, tiles_n, rows_per_round,
+                       eps, gemma, ws.fault_mask, ws.spin_limit, ws.slot_words, ws.pword_words);
   }
   return check_launch("gemm_add_rmsnorm_pair_kernel");
 }
@@ -1680,12 +1709,9 @@ int launch_gemm(const uint16_t* x, const uint16_t* Wp, void* C, bool bf16_out, i
 }
 
 int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
-                            uint16_t* out, unsigned long long* slots, unsigned* sync, int M,
-                            int N, int K, const GemmCfg& cfg, float eps, int gemma,
-                            unsigned epoch, unsigned read_epoch, unsigned spin_limit,
-                            void* stream, void* start_timing, void* stop_timing,
-                            unsigned long long* pair_words, unsigned long long* xbuf,
-                            size_t xbuf_words) {
+                            uint16_t* out, const SingleWs& ws, int M, int N, int K,
+                            const GemmCfg& cfg, float eps, int gemma, void* stream,
+                            void* start_timing, void* stop_timing) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t t0 = static_cast<hipEvent_t>(start_timing);
   hipEvent_t t1 = static_cast<hipEvent_t>(stop_timing);
@@ -1696,8 +1722,7 @@ int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, con
       return fail(PR_ERR_SHAPE, "single launch (pairs): N=%d K=%d with tile %dx%d, %d waves, %d "
                   "K groups not supported (256x256, 8 waves, N a multiple of 256, K >= 256)", N,
                   K, cfg.bm, cfg.bn, cfg.waves, cfg.kgroups);
-    return launch_pair(x, Wp, r, w, out, slots, sync, pair_words, xbuf, xbuf_words, M, N, K, eps,
-                       gemma, epoch, read_epoch, spin_limit, s, t0, t1);
+    return launch_pair(x, Wp, r, w, out, ws, M, N, K, eps, gemma, s, t0, t1);
   }
   const bool r256x128 = cfg.bm == 256 && cfg.bn == 128;
   if (K % (2 * kBK) != 0 || N % cfg.bn != 0 || N / cfg.bn > 64 || cfg.split != 1 ||
@@ -1706,20 +1731,20 @@ int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, con
     return fail(PR_ERR_SHAPE, "single launch: N=%d K=%d with tile %dx%d split %d, %d waves, %d K "
                 "groups not supported", N, K, cfg.bm, cfg.bn, cfg.split, cfg.waves, cfg.kgroups);
   if (cfg.bm == 256 && cfg.bn == 256)
-    return launch_single_t<256, 256, 5, 2, 4, 1>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
-                                              epoch, read_epoch, spin_limit, s, t0, t1);
+    return launch_single_t<256, 256, 5, 2, 4, 1>(x, Wp, r, w, out, ws, M, N, K, eps, gemma, s,
+                                                 t0, t1);
   if (r256x128 && cfg.kgroups == 2)
-    return launch_single_t<256, 128, 3, 2, 2, 2>(x, Wp, r, w, out, slots, sync, M, N, K, eps,
-                                                 gemma, epoch, read_epoch, spin_limit, s, t0, t1);
+    return launch_single_t<256, 128, 3, 2, 2, 2>(x, Wp, r, w, out, ws, M, N, K, eps, gemma, s,
+                                                 t0, t1);
   if (cfg.bm == 256 && cfg.bn == 128 && cfg.waves == 4)
-    return launch_single_t<256, 128, 4, 2, 2, 1>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
-                                              epoch, read_epoch, spin_limit, s, t0, t1);
+    return launch_single_t<256, 128, 4, 2, 2, 1>(x, Wp, r, w, out, ws, M, N, K, eps, gemma, s,
+                                                 t0, t1);
   if (cfg.bm == 256 && cfg.bn == 128)
-    return launch_single_t<256, 128, 4, 4, 2, 1>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
-                                              epoch, read_epoch, spin_limit, s, t0, t1);
+    return launch_single_t<256, 128, 4, 4, 2, 1>(x, Wp, r, w, out, ws, M, N, K, eps, gemma, s,
+                                                 t0, t1);
   if (cfg.bm == 128 && cfg.bn == 128)
-    return launch_single_t<128, 128, 4, 2, 4, 1>(x, Wp, r, w, out, slots, sync, M, N, K, eps, gemma,
-                                              epoch, read_epoch, spin_limit, s, t0, t1);
+    return launch_single_t<128, 128, 4, 2, 4, 1>(x, Wp, r, w, out, ws, M, N, K, eps, gemma, s,
+                                                 t0, t1);
   return fail(PR_ERR_INVALID_ARG, "single launch: no tile %dx%d", cfg.bm, cfg.bn);
 }
 

@@ -40,8 +40,8 @@ struct DevCtx {
   size_t conv_bytes = 0;
   uint16_t* out_ws = nullptr;  // borrowed output
   size_t out_ws_bytes = 0;
-  // single-launch path: row-partial slots (epoch-tagged), the status / completion words (zero
-  // between calls) and the epoch of the last launch
+  // single-launch path: row-partial slots (epoch-tagged) and the status / completion / epoch
+  // words (the epoch lives on the device and advances per launch)
   void* row_slots = nullptr;
   size_t row_slots_bytes = 0;
   unsigned* sync = nullptr;
@@ -52,7 +52,6 @@ struct DevCtx {
   size_t pair_flags_bytes = 0;
   void* xbuf = nullptr;
   size_t xbuf_bytes = 0;
-  unsigned epoch = 0;
   const uint16_t* last_borrowed = nullptr;
   // the previous pipeline call: its caller stream and the done slots of its last chunk on
   // each stream (-1 if none)
@@ -397,17 +396,28 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
   const size_t slots_need = (size_t)rows_max * (H / g.bn) * sizeof(unsigned long long);
   const size_t flags_need =
       pairs ? (size_t)4 * ((rows_max + 255) / 256) * (H / 256) * sizeof(unsigned long long) : 0;
-  // Epoch-tagged buffers (row slots, pair flags): a grown buffer restarts the epochs, so every
-  // such buffer is zeroed (no word holds an epoch >= 1) and complete before any kernel reads
-  // it; the fill runs on the null stream, which does not order work on a non-blocking caller
-  // stream.
-  if (slots_need > c->row_slots_bytes || flags_need > c->pair_flags_bytes) {
+  const int blocks = pairs ? 2 * ((rows_max + 255) / 256) : (rows_max + g.bm - 1) / g.bm;
+  const size_t sync_need = (size_t)(3 + blocks) * sizeof(unsigned);
+  // Growing any of the epoch-tagged buffers (row slots, pair words) or the sync words: the new
+  // buffers are zeroed, and so are the others, since a new sync buffer restarts the device
+  // epoch at 0 and a zeroed tag (epoch 0) matches no launch.  The fills run on the null stream,
+  // which does not order work on a non-blocking caller stream, hence the synchronisation.
+  // Steady-state calls allocate and fill nothing, so they can be captured in a graph.
+  const bool grow_sync = sync_need > c->sync_bytes;
+  if (slots_need > c->row_slots_bytes || flags_need > c->pair_flags_bytes || grow_sync) {
     PR_TRY(grow(&c->row_slots, &c->row_slots_bytes, slots_need));
     if (flags_need > 0) PR_TRY(grow(&c->pair_flags, &c->pair_flags_bytes, flags_need));
+    if (grow_sync) {
+      void* p = c->sync;
+      size_t have = c->sync_bytes;
+      PR_TRY(grow(&p, &have, sync_need));
+      c->sync = static_cast<unsigned*>(p);
+      c->sync_bytes = have;
+      PR_HIP(hipMemset(c->sync, 0, c->sync_bytes));
+    }
     PR_HIP(hipMemset(c->row_slots, 0, c->row_slots_bytes));
     if (c->pair_flags != nullptr) PR_HIP(hipMemset(c->pair_flags, 0, c->pair_flags_bytes));
     PR_HIP(hipDeviceSynchronize());
-    c->epoch = 0;
   }
   if (pairs) {
     // Exchange regions: 128 KiB per workgroup of a round and round parity; a round holds at
@@ -415,38 +425,30 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
     const size_t xbuf_need = (size_t)2 * kNumCUs * 128 * 1024;
     PR_TRY(grow(&c->xbuf, &c->xbuf_bytes, xbuf_need));
   }
-  const int blocks = pairs ? 2 * ((rows_max + 255) / 256) : (rows_max + g.bm - 1) / g.bm;
-  const size_t sync_need = (size_t)(2 + blocks) * sizeof(unsigned);
-  if (sync_need > c->sync_bytes) {
-    void* p = c->sync;
-    size_t have = c->sync_bytes;
-    PR_TRY(grow(&p, &have, sync_need));
-    c->sync = static_cast<unsigned*>(p);
-    c->sync_bytes = have;
-    PR_HIP(hipMemset(c->sync, 0, have));  // the kernels keep it zero from here on
+  // Debug: PR_DEBUG_EPOCH=<n> stores n as the last launch's epoch before the call (tests of
+  // the wrap at 2^32 - 1 launches).
+  const char* dbg_epoch = std::getenv("PR_DEBUG_EPOCH");
+  if (dbg_epoch != nullptr && dbg_epoch[0] != '\0') {
+    const unsigned v = (unsigned)std::strtoul(dbg_epoch, nullptr, 10);
     PR_HIP(hipDeviceSynchronize());
+    PR_HIP(hipMemcpy(c->sync + 2, &v, sizeof(v), hipMemcpyHostToDevice));
   }
-  const unsigned limit = spin_limit();
+  SingleWs ws;
+  ws.slots = static_cast<unsigned long long*>(c->row_slots);
+  ws.slot_words = c->row_slots_bytes / sizeof(unsigned long long);
+  ws.sync = c->sync;
+  ws.pwords = static_cast<unsigned long long*>(c->pair_flags);
+  ws.pword_words = c->pair_flags_bytes / sizeof(unsigned long long);
+  ws.xbuf = static_cast<unsigned long long*>(c->xbuf);
+  ws.xbuf_words = c->xbuf_bytes / sizeof(unsigned long long);
+  ws.fault_mask = wait_fault_injected() ? 0x80000000u : 0u;
+  ws.spin_limit = spin_limit();
   const int gemma = norm_kind == PR_NORM_GEMMA;
   for (long long r0 = 0; r0 < T; r0 += rows_per) {
     const int rows = (int)std::min<long long>(rows_per, T - r0);
-    if (++c->epoch == 0) {
-      // After 2^32 - 1 launches the slots are cleared once so that epochs stay unique.
-      PR_HIP(hipDeviceSynchronize());
-      PR_HIP(hipMemset(c->row_slots, 0, c->row_slots_bytes));
-      if (c->pair_flags != nullptr) PR_HIP(hipMemset(c->pair_flags, 0, c->pair_flags_bytes));
-      PR_HIP(hipDeviceSynchronize());
-      c->epoch = 1;
-    }
-    const unsigned epoch = c->epoch;
-    const unsigned read_epoch = wait_fault_injected() ? epoch ^ 0x80000000u : epoch;
     PR_TRY(timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
-      return launch_gemm_add_rmsnorm(x + r0 * K, W, r + r0 * H, w, out + r0 * H,
-                                     static_cast<unsigned long long*>(c->row_slots), c->sync, rows,
-                                     H, K, g, eps, gemma, epoch, read_epoch, limit, s, t0, t1,
-                                     static_cast<unsigned long long*>(c->pair_flags),
-                                     static_cast<unsigned long long*>(c->xbuf),
-                                     c->xbuf_bytes / sizeof(unsigned long long));
+      return launch_gemm_add_rmsnorm(x + r0 * K, W, r + r0 * H, w, out + r0 * H, ws, rows, H, K,
+                                     g, eps, gemma, s, t0, t1);
     }));
   }
   return PR_OK;

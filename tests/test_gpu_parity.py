@@ -28,7 +28,7 @@ def _env(monkeypatch):
     for k in ("PR_MICROCHUNK_TOKENS", "PR_THRESHOLD_TOKENS", "PR_FORCE_TILE", "PR_FORCE_SPLIT",
               "PR_FORCE_WAVES", "PR_FORCE_STAGES", "PR_FORCE_KGROUPS", "PR_FORCE_ADDNORM_WGS",
               "PR_DEBUG_POISON",
-              "PR_DEBUG_DELAY", "PR_SPIN_LIMIT",
+              "PR_DEBUG_DELAY", "PR_SPIN_LIMIT", "PR_DEBUG_EPOCH",
               "PR_FAULT_INJECT"):
         monkeypatch.delenv(k, raising=False)
     pr.pr_clear_tuning()
@@ -550,3 +550,57 @@ def test_tuning_file_on_the_device(tmp_path):
     r_dev, out_bits = dev.run(0)
     _check(d, r_dev, out_bits, "fused")
     pr.pr_clear_tuning()
+
+
+@pytest.mark.parametrize("split", [1, 2])
+def test_single_launch_graph_replay(monkeypatch, split):
+    """The single launch keeps its epoch on the device, so a captured call replays correctly:
+    replays with the program's own work between them (residual restore, output reset,
+    synchronisation) all equal the eager call bitwise.  Split 2: the pair form."""
+    if split == 2:
+        _force_single(monkeypatch, "256x256", 8, 1, 2)
+    d = synth.make_custom(1000, 512, 1024, seed=31)
+    dev = Device(d)
+    r_eager, o_eager = dev.run("single")  # also sizes the workspace (not capturable)
+    r0 = torch.from_numpy(d["residual"]).to(DEV)
+    T = dev.T
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    dev.r.copy_(r0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        pr.proj_add_rmsnorm_single_launch(dev.x, dev.Wp, dev.r, dev.w, d["eps"], T, dev.K, dev.H,
+                                          d["norm_kind"], dev.out)
+    for rep in range(5):
+        dev.r.copy_(r0)
+        dev.out.fill_(0x7BAD)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print("replay", rep, flush=True)
+        assert pr.pr_device_status(torch.cuda.current_stream()) == 0
+        np.testing.assert_array_equal(dev.r[:T].cpu().numpy(), r_eager)
+        np.testing.assert_array_equal(bits(dev.out[:T]), o_eager)
+    dev.reset()
+    r_dev, out_bits = dev.run("single")  # eager again after the replays
+    np.testing.assert_array_equal(r_dev, r_eager)
+    np.testing.assert_array_equal(out_bits, o_eager)
+
+
+@pytest.mark.parametrize("split", [1, 2])
+def test_single_launch_epoch_wrap(monkeypatch, split):
+    """The launch that takes the last 32-bit epoch clears every epoch-tagged word and restarts
+    the count: that call and the two after it (epochs 1 and 2, whose tags stale words from
+    before the wrap could otherwise carry) are correct."""
+    if split == 2:
+        _force_single(monkeypatch, "256x256", 8, 1, 2)
+    d = synth.make_custom(600, 512, 1024, seed=41)
+    dev = Device(d)
+    dev.run("single")
+    for k in range(3):
+        if k == 0:
+            monkeypatch.setenv("PR_DEBUG_EPOCH", str(2 ** 32 - 2))
+        dev.reset()
+        r_dev, out_bits = dev.run("single")
+        _check(d, r_dev, out_bits, "fused")
+        monkeypatch.delenv("PR_DEBUG_EPOCH", raising=False)
