@@ -151,12 +151,22 @@ def cpu_baseline(d, seconds: float) -> dict:
                       f"full batch"}
 
 
+def under_profiler() -> bool:
+    """True when this process runs under rocprofv3 (its tool library is preloaded)."""
+    return ("rocprof" in os.environ.get("LD_PRELOAD", "")
+            or any(k.startswith(("ROCPROF_", "ROCPROFILER_")) for k in os.environ))
+
+
 def clock_settings() -> dict:
     """The GPU's clock settings as amd-smi reports them (run as a child process before this
     process initialises the GPU): per-XCD shader-clock range, whether it is locked, and the
     memory clock.  Clocks are left at their defaults; None when amd-smi is unavailable."""
     import shutil
     import subprocess
+    if under_profiler():
+        # A profiler's preloaded library reaches the child too and opens the GPU there before
+        # amd-smi's interpreter line replaces the process, which must not happen.
+        return None
     exe = shutil.which("amd-smi")
     if exe is None:
         return None
@@ -375,7 +385,7 @@ def main() -> int:
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
-              "inter-GPU step in this build", file=sys.stderr)
+              "inter-GPU step", file=sys.stderr)
         return 2
     clocks = clock_settings()  # before this process touches the GPU
     import torch

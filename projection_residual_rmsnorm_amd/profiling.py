@@ -1,7 +1,9 @@
 """Summaries of rocprofv3 CSV output for the kernels of this library.
 
     python -m projection_residual_rmsnorm_amd.profiling stats <kernel_stats.csv> <out.md> \
-        --command "<the rocprofv3 command that produced it>"
+        --command "<the rocprofv3 command that produced it>" \
+        [--trace <kernel_trace.csv> --kernel "<kernel name prefix>" --last N]
+        [--bench-log <stdout of the profiled bench.py>]
     python -m projection_residual_rmsnorm_amd.profiling traffic <fetch counter_collection.csv> \
         <write counter_collection.csv> --kernel "<kernel name prefix>" --out <traffic.json> \
         --command "<commands>"
@@ -43,6 +45,36 @@ def stats_summary(path: str, command: str) -> str:
                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
     return "\n".join(lines) + "\n"
+
+
+def last_dispatches(trace_csv: str, kernel: str, n: int) -> dict:
+    """Durations of the last n dispatches of a kernel (name prefix) in a kernel-trace CSV, in
+    dispatch order: the pass a bench run times with events when that pass ends the program."""
+    durs = []
+    for r in csv.DictReader(open(trace_csv)):
+        if short_name(r["Kernel_Name"]).startswith(kernel):
+            durs.append((int(r["Dispatch_Id"]),
+                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    if len(durs) < n:
+        raise SystemExit(f"kernel {kernel!r}: {len(durs)} dispatches in the trace, asked for {n}")
+    last = [d for _, d in sorted(durs)[-n:]]
+    return {"kernel": kernel, "n": n, "mean_us": statistics.mean(last),
+            "median_us": statistics.median(last), "min_us": min(last), "max_us": max(last)}
+
+
+def last_pass_lines(res: dict) -> List[str]:
+    return ["", f"Last {res['n']} dispatches of `{res['kernel']}` (the bench's event-timed pass): "
+                f"mean {res['mean_us']:.2f} us, median {res['median_us']:.2f}, "
+                f"min {res['min_us']:.2f}, max {res['max_us']:.2f}."]
+
+
+def bench_line_lines(log_path: str) -> List[str]:
+    """The roofline figures of the bench line printed by the profiled program itself."""
+    line = [l for l in open(log_path) if l.startswith("{")][-1]
+    roof = json.loads(line)["roofline"]
+    return ["", f"The bench line of the same run: `{roof['kernel']}` averaged "
+                f"{roof['avg_launch_us']:.2f} us over {roof['launches']} event-timed launches "
+                f"({roof['achieved']:.1f} {roof['unit']})."]
 
 
 def _counter(path: str, counter: str, grid: int = 0) -> Dict[str, List[float]]:
@@ -228,6 +260,10 @@ def main() -> None:
     s.add_argument("csv")
     s.add_argument("out")
     s.add_argument("--command", required=True)
+    s.add_argument("--trace", help="kernel_trace.csv of the same run")
+    s.add_argument("--kernel", help="kernel name prefix for the last-pass figure")
+    s.add_argument("--last", type=int, default=0, help="dispatches in the last timed pass")
+    s.add_argument("--bench-log", help="stdout of the profiled bench.py (its JSON line)")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_csv")
     t.add_argument("write_csv")
@@ -251,6 +287,11 @@ def main() -> None:
     elif a.cmd == "stats":
         with open(a.out, "w") as f:
             f.write(stats_summary(a.csv, a.command))
+            if a.trace and a.kernel and a.last:
+                f.write("\n".join(last_pass_lines(last_dispatches(a.trace, a.kernel, a.last)))
+                        + "\n")
+            if a.bench_log:
+                f.write("\n".join(bench_line_lines(a.bench_log)) + "\n")
     else:
         res = traffic(a.fetch_csv, a.write_csv, a.kernel, a.grid)
         res["commands"] = a.command

@@ -2,6 +2,7 @@
 validates arguments, decides the path per call, plans a race-free pipeline schedule, and
 computes the token threshold.  No GPU is touched (only host-only entry points are called)."""
 import ctypes
+import json
 import os
 import re
 
@@ -439,6 +440,29 @@ def test_counter_summary_derivations(tmp_path):
     assert dv["l1_l2_read_MB_at_64B"] == 64.0
     assert dv["l1_l2_read_latency_cycles"] == 500.0
     assert dv["l1_pending_stall_cycles_per_cu"] == 7e4
+
+
+def test_last_pass_and_bench_line(tmp_path):
+    """The last-pass figure takes the last n dispatches of the kernel in dispatch order (not
+    file order), and the bench figure comes from the JSON line of the profiled program."""
+    from projection_residual_rmsnorm_amd.profiling import bench_line_lines, last_dispatches
+    trace = tmp_path / "t.csv"
+    lines = ["Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp"]
+    durs = {1: 50, 2: 90, 5: 80, 3: 70, 4: 60, 6: 10}   # microseconds; 6 is another kernel
+    for d, us in durs.items():
+        k = "fill_nan_kernel" if d == 6 else "gemm_add_rmsnorm_kernel<256, 128, 4, 2, 2, 1>"
+        lines.append(f'{d},"void pr::{k}(x)",1000,{1000 + us * 1000}')
+    trace.write_text("\n".join(lines) + "\n")
+    res = last_dispatches(str(trace), "gemm_add_rmsnorm_kernel<256, 128", 3)
+    assert (res["mean_us"], res["min_us"], res["max_us"]) == (70.0, 60.0, 80.0)
+    with pytest.raises(SystemExit):
+        last_dispatches(str(trace), "gemm_add_rmsnorm_kernel", 6)
+    log = tmp_path / "b.log"
+    roof = {"kernel": "gemm_add_rmsnorm_kernel", "avg_launch_us": 81.25, "launches": 20,
+            "achieved": 845.0, "unit": "TFLOP/s"}
+    log.write_text("[bench] x\n" + json.dumps({"roofline": roof}) + "\n")
+    text = "\n".join(bench_line_lines(str(log)))
+    assert "81.25 us over 20" in text and "845.0 TFLOP/s" in text
 
 
 # ------------------------------------------------------------------ tuning files
