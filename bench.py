@@ -73,15 +73,23 @@ def time_steps(call, steps: int, warmup: int, torch):
     return time.perf_counter() - t0
 
 
+def evict(flush) -> None:
+    """Evicts the call's operands from the caches by READING a buffer twice the size of the
+    256 MB Infinity Cache.  A write of that buffer would evict them too, but would leave the
+    cache full of dirty lines whose write-back the next kernel's misses then pay for (a plain
+    50 MiB copy measured 33 us after such a write and 18 us after this read)."""
+    flush.sum()
+
+
 def per_call_stats(call, r, r0, steps: int, torch, stream, flush=None) -> dict:
     """Single calls timed with events on the calling stream.  Before each call (untimed) the
-    residual is restored from a pristine copy and, with `flush`, a buffer twice the size of the
-    256 MB Infinity Cache is written, so that none of the call's operands is cached."""
+    residual is restored from a pristine copy and, with `flush`, the caches are evicted, so that
+    none of the call's operands is cached."""
     times = []
     for i in range(steps + 3):
         r.copy_(r0)
         if flush is not None:
-            flush.fill_(float(i))
+            evict(flush)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -98,7 +106,7 @@ def per_call_stats(call, r, r0, steps: int, torch, stream, flush=None) -> dict:
 def add_per_call_stats(result, fused_call, conventional, r, steps, torch, stream, dev,
                        form: str) -> None:
     r0 = r.clone()
-    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)  # 512 MB
+    flush = torch.zeros(1 << 27, dtype=torch.float32, device=dev)  # 512 MB
     result["per_call"] = {
         "form": form,
         "fused_warm": per_call_stats(fused_call, r, r0, steps, torch, stream),
@@ -218,14 +226,15 @@ def tune_sweep(pr, torch, args) -> int:
 def addnorm_roofline(pr, torch, args) -> int:
     """The add/norm kernel alone, as the conventional path launches it after the projection:
     algorithmic bytes per element (y read: 2 for bf16, 4 per fp32 plane; r read 4, r write 4,
-    out write 2) over its event-timed duration, with the Infinity Cache warm and flushed (a
-    512 MB write before each call), against 8 TB/s and against a device copy of the same bytes
-    (half read, half written) timed the same way."""
+    out write 2) over its event-timed duration, with the Infinity Cache warm, flushed (a 512 MB
+    read before each call) and dirty (a 512 MB write before each call, whose write-backs the call
+    then shares the memory with), against 8 TB/s and against a device copy of the same bytes
+    (half read, half written) after the same read flush."""
     import synth
     dev = "cuda:0"
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
-    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    flush = torch.zeros(1 << 27, dtype=torch.float32, device=dev)
     names = ["o_proj", "down_proj", "gemma", "sweep_T8192"]
     rows = []
     for name in names:
@@ -246,11 +255,13 @@ def addnorm_roofline(pr, torch, args) -> int:
         nbytes = per_elem * T * H
         res = {"workload": name, "T": T, "H": H, "y": "bf16" if split == 1 else f"{split} fp32 planes",
                "bytes_per_elem": per_elem, "bytes": nbytes}
-        for mode in ("warm", "flushed"):
+        for mode in ("warm", "flushed", "dirty"):
             ts = []
             for i in range(max(args.steps // 5, 5) + 2):
                 r.copy_(r0)
                 if mode == "flushed":
+                    evict(flush)
+                elif mode == "dirty":
                     flush.fill_(float(i))
                 pr.pr_profile_enable(True)
                 pr.proj_add_rmsnorm_unfused(x, Wp, r, w, d["eps"], T, K, H, wl.norm_kind, out)
@@ -266,7 +277,7 @@ def addnorm_roofline(pr, torch, args) -> int:
         dst = torch.empty_like(src)
         cts = []
         for i in range(7):
-            flush.fill_(float(i))
+            evict(flush)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -279,8 +290,9 @@ def addnorm_roofline(pr, torch, args) -> int:
         res["frac_hbm_peak_flushed"] = res["flushed_GBs"] / PEAK_HBM_GBS
         rows.append(res)
         log(f"{name}: add/norm {res['warm_us']:.1f} us warm ({res['warm_GBs']:.0f} GB/s), "
-            f"{res['flushed_us']:.1f} us flushed ({res['flushed_GBs']:.0f} GB/s); copy of the same "
-            f"bytes {res['copy_flushed_GBs']:.0f} GB/s")
+            f"{res['flushed_us']:.1f} us flushed ({res['flushed_GBs']:.0f} GB/s), "
+            f"{res['dirty_us']:.1f} us dirty ({res['dirty_GBs']:.0f} GB/s); copy of the same "
+            f"bytes {res['copy_flushed_GBs']:.0f} GB/s flushed")
         del x, Wp, r, r0, w, out, src, dst
         torch.cuda.empty_cache()
     print(json.dumps({"addnorm_roofline": rows, "peak_GBs": PEAK_HBM_GBS}), flush=True)
