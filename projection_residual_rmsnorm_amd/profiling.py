@@ -11,6 +11,9 @@
     python -m projection_residual_rmsnorm_amd.profiling counters <counter_collection.csv> <out.md> \
         --kernel "<kernel name prefix>" [--kernel ...] [--grid N] --command "<command>"
 
+    python -m projection_residual_rmsnorm_amd.profiling runs <kernel_trace.csv> <out.md> \
+        --kernel "<kernel name prefix>" --per-run N --labels "a,b,..." --command "<command>"
+
 `traffic` calibrates FETCH_SIZE and WRITE_SIZE (KiB per dispatch) against the plain 1 GiB
 device copies that `bench.py --copy-calibration` runs in the same process: the factor that
 turns each counter into bytes is (1 GiB) / (the counter's reading for one such copy).
@@ -75,6 +78,36 @@ def bench_line_lines(log_path: str) -> List[str]:
     return ["", f"The bench line of the same run: `{roof['kernel']}` averaged "
                 f"{roof['avg_launch_us']:.2f} us over {roof['launches']} event-timed launches "
                 f"({roof['achieved']:.1f} {roof['unit']})."]
+
+
+def dispatch_runs(trace_csv: str, kernel: str, n: int, labels: List[str]) -> List[dict]:
+    """Consecutive runs of n dispatches of a kernel (name prefix) in dispatch order, one per
+    label, with their median, min and max durations in us."""
+    durs = []
+    for r in csv.DictReader(open(trace_csv)):
+        if short_name(r["Kernel_Name"]).startswith(kernel):
+            durs.append((int(r["Dispatch_Id"]),
+                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    durs = [d for _, d in sorted(durs)]
+    if len(durs) != n * len(labels):
+        raise SystemExit(f"kernel {kernel!r}: {len(durs)} dispatches, expected "
+                         f"{n} x {len(labels)} labels")
+    out = []
+    for i, label in enumerate(labels):
+        run = durs[i * n:(i + 1) * n]
+        out.append({"label": label, "n": n, "median_us": statistics.median(run),
+                    "min_us": min(run), "max_us": max(run)})
+    return out
+
+
+def runs_summary(trace_csv: str, kernel: str, n: int, labels: List[str], command: str) -> str:
+    lines = ["# rocprofv3 kernel trace: runs of dispatches", "", "Command:", "", "```", command,
+             "```", "", f"Kernel `{kernel}`, {n} dispatches per run, in dispatch order.", "",
+             "| run | dispatches | median us | min us | max us |", "|---|---|---|---|---|"]
+    for r in dispatch_runs(trace_csv, kernel, n, labels):
+        lines.append(f"| {r['label']} | {r['n']} | {r['median_us']:.2f} | {r['min_us']:.2f} | "
+                     f"{r['max_us']:.2f} |")
+    return "\n".join(lines) + "\n"
 
 
 def _counter(path: str, counter: str, grid: int = 0) -> Dict[str, List[float]]:
@@ -280,8 +313,18 @@ def main() -> None:
     c.add_argument("--kernel", action="append", required=True)
     c.add_argument("--grid", type=int, default=0)
     c.add_argument("--command", required=True)
+    u = sub.add_parser("runs")
+    u.add_argument("trace")
+    u.add_argument("out")
+    u.add_argument("--kernel", required=True)
+    u.add_argument("--per-run", type=int, required=True)
+    u.add_argument("--labels", required=True, help="comma-separated, one per run")
+    u.add_argument("--command", required=True)
     a = ap.parse_args()
-    if a.cmd == "counters":
+    if a.cmd == "runs":
+        with open(a.out, "w") as f:
+            f.write(runs_summary(a.trace, a.kernel, a.per_run, a.labels.split(","), a.command))
+    elif a.cmd == "counters":
         with open(a.out, "w") as f:
             f.write(counters_summary(a.csv, a.kernel, a.grid, a.command))
     elif a.cmd == "stats":

@@ -465,6 +465,24 @@ def test_last_pass_and_bench_line(tmp_path):
     assert "81.25 us over 20" in text and "845.0 TFLOP/s" in text
 
 
+def test_dispatch_runs(tmp_path):
+    """Runs are consecutive dispatches in dispatch order; a count that does not match the
+    labels is refused rather than silently regrouped."""
+    from projection_residual_rmsnorm_amd.profiling import dispatch_runs
+    trace = tmp_path / "t.csv"
+    lines = ["Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp"]
+    us = [10, 12, 11, 30, 31, 29]
+    for d in (6, 5, 4, 3, 2, 1):   # file order reversed
+        lines.append(f'{d},"void pr::add_rmsnorm_kernel<8, 2, true>(x)",0,{us[d - 1] * 1000}')
+    lines.append('7,"void pr::fill_nan_kernel(x)",0,5000')
+    trace.write_text("\n".join(lines) + "\n")
+    runs = dispatch_runs(str(trace), "add_rmsnorm_kernel", 3, ["warm", "flushed"])
+    assert [(r["label"], r["median_us"], r["min_us"], r["max_us"]) for r in runs] == [
+        ("warm", 11.0, 10.0, 12.0), ("flushed", 30.0, 29.0, 31.0)]
+    with pytest.raises(SystemExit):
+        dispatch_runs(str(trace), "add_rmsnorm_kernel", 2, ["a", "b"])
+
+
 # ------------------------------------------------------------------ tuning files
 TUNE_KEY = "gfx950-test:256"
 
