@@ -125,6 +125,35 @@ def test_single_launch_integer_projection_is_exact(monkeypatch, tile, waves, kgr
     assert oracle.within_tolerance(err), err
 
 
+def _identity_inputs(T, H, kind):
+    rng = np.random.default_rng(11)
+    w = (0.1 * rng.standard_normal(H)).astype(np.float32)
+    return {"x": synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)),
+            "W": synth.f32_to_bf16_bits(np.eye(H, dtype=np.float32)),
+            "residual": np.zeros((T, H), dtype=np.float32),
+            "norm_w": w + np.float32(1.0) if kind == 0 else w, "eps": float(np.float32(1e-5)),
+            "norm_kind": kind, "T": T, "K": H, "H": H, "K_real": H}
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("path", ["conventional", "pipeline", "single"] +
+                         [f"single {c[0]} {c[1]}w kg{c[2]} split{c[3]}" for c in SINGLE_CFGS])
+def test_identity_weight_residual_is_x_bitwise(monkeypatch, path, kind):
+    """W = I and r = 0: each output's projection has one nonzero product, so every path (any
+    tile, K split or chunking) returns x exactly and the updated residual equals x bitwise;
+    the output is RMSNorm(x).  T = 300 leaves ragged tile rows and chunks."""
+    T, H = 300, 512
+    if path.startswith("single "):
+        _force_single(monkeypatch, *SINGLE_CFGS[[f"single {c[0]} {c[1]}w kg{c[2]} split{c[3]}"
+                                                 for c in SINGLE_CFGS].index(path)])
+    d = _identity_inputs(T, H, kind)
+    dev = Device(d)
+    mc = {"conventional": None, "pipeline": 128}.get(path, "single")
+    r_dev, out_bits = dev.run(mc)
+    np.testing.assert_array_equal(r_dev, synth.bf16_bits_to_f32(d["x"]))
+    _check(d, r_dev, out_bits, "conventional" if mc is None else "fused")
+
+
 @pytest.mark.parametrize("tile,waves,kgroups,split", SINGLE_CFGS)
 @pytest.mark.parametrize("kind", [0, 1])
 @pytest.mark.parametrize("T,K,H", [(300, 512, 768), (64, 512, 512), (1, 256, 512),

@@ -200,6 +200,28 @@ def test_matches_torch_rms_norm_float64():
         np.testing.assert_allclose(oracle.rms_norm(rp, w, eps), want, rtol=1e-13, atol=1e-15)
 
 
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("mode", ["fused", "conventional"])
+def test_identity_weight_gives_rms_norm_of_x(kind, mode):
+    """W = I (K = H) and r = 0: the projection returns x itself, exactly in both modes since x
+    is bf16, so the updated residual is x and the output is RMSNorm(x) with gain w or 1 + w
+    (torch rms_norm in float64 as the reference)."""
+    rng = np.random.default_rng(9)
+    T, H = 5, 24
+    x = _bits(rng.standard_normal((T, H)) * 2)
+    W = _bits(np.eye(H))
+    r = np.zeros((T, H), dtype=np.float32)
+    w = (0.1 * rng.standard_normal(H)).astype(np.float32)
+    eps = float(np.float32(1e-5))
+    r_new, out = oracle.proj_add_rmsnorm(x, W, r, w, eps, kind, mode)
+    x64 = oracle.widen_bf16(x)
+    np.testing.assert_array_equal(r_new, x64)
+    g = w.astype(np.float64) + (1.0 if kind == 1 else 0.0)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(x64), (H,), torch.from_numpy(g),
+                                        eps=eps).numpy()
+    np.testing.assert_allclose(out, want, rtol=1e-13, atol=1e-15)
+
+
 def test_gemma_is_standard_with_one_plus_w():
     rng = np.random.default_rng(7)
     T, K, H = 3, 16, 10
