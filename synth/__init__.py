@@ -114,6 +114,22 @@ def make_custom(T: int, K: int, H: int, seed: int = 0, norm_kind: int = NORM_STA
     return make_inputs(wl, seed)
 
 
+def tiled_inputs(T: int, K: int, H: int, period: int, seed: int = 0) -> dict:
+    """Inputs for shapes whose x is too large to draw in full on the host: x is a block of
+    `period` drawn rows (N(0,1), bf16), repeated down the T rows, so token t's row is block row
+    t % period.  W ~ N(0, 1/K), the residual ~ N(0,1) and the norm weight 1 + N(0, 0.1) are
+    drawn in full, in that order after the block, with PCG64 ``default_rng(seed)``."""
+    rng = np.random.default_rng(seed)
+    xb = f32_to_bf16_bits(rng.standard_normal((period, K), dtype=np.float32))
+    W = f32_to_bf16_bits(rng.standard_normal((H, K), dtype=np.float32) *
+                         np.float32(1.0 / np.sqrt(K)))
+    residual = rng.standard_normal((T, H), dtype=np.float32)
+    nw = rng.standard_normal(H, dtype=np.float32) * np.float32(0.1) + np.float32(1.0)
+    return {"x_block": xb, "x_period": period, "W": W, "residual": residual,
+            "norm_w": nw.astype(np.float32), "eps": float(np.float32(1e-5)),
+            "norm_kind": NORM_STANDARD, "T": T, "K": K, "H": H, "K_real": K}
+
+
 def integer_inputs(T: int, K: int, H: int, seed: int = 0, lo: int = -4, hi: int = 4) -> dict:
     """Small-integer x and W (exact in bf16), integer residual, unit norm weight.
 

@@ -557,6 +557,44 @@ def test_workload_parity_full_size(name):
         assert np.all(np.isfinite(r_dev))
 
 
+def test_launch_split_past_2_30_elements_of_x():
+    """x with more than 2^30 elements (T = 65600, K = 16384) is projected in two launches,
+    since offsets inside a launch are 32-bit: rows on both sides of the boundary at row 65536
+    and the last rows match the oracle on the conventional path and the single launch.  x is a
+    4099-row block tiled down the rows (4099 does not divide 65536, so a row offset error across
+    the boundary reads other data)."""
+    T, K, H, P = 65600, 16384, 256, 4099
+    print(f"launch split: T={T} K={K} H={H}", flush=True)
+    d = synth.tiled_inputs(T, K, H, period=P, seed=13)
+    x = i16(d["x_block"]).repeat((T + P - 1) // P, 1)[:T].contiguous()
+    assert x.numel() > 2 ** 30
+    W_src = i16(d["W"])
+    Wp = torch.empty(K * H, dtype=torch.int16, device=DEV)
+    pr.pr_prepare_weight(W_src, pr.PR_WEIGHT_OUT_IN, Wp, K, H)
+    w = f32(d["norm_w"])
+    rng = np.random.default_rng(5)
+    rows = np.array(sorted(set(rng.choice(T, 40, replace=False).tolist()) |
+                           {0, 1, 65535, 65536, 65537, T - 2, T - 1}))
+    for path in ("conventional", "single"):
+        r = f32(d["residual"])
+        out = torch.full((T, H), 0x7BAD, dtype=torch.int16, device=DEV)
+        if path == "conventional":
+            pr.proj_add_rmsnorm_unfused(x, Wp, r, w, d["eps"], T, K, H, 0, out)
+        else:
+            pr.proj_add_rmsnorm_single_launch(x, Wp, r, w, d["eps"], T, K, H, 0, out)
+            assert pr.pr_device_status(torch.cuda.current_stream()) == 0
+        torch.cuda.synchronize()
+        r_dev, out_bits = r[rows].cpu().numpy(), bits(out[rows])
+        r_ref, out_ref = oracle.proj_add_rmsnorm(d["x_block"][rows % P], d["W"],
+                                                 d["residual"][rows], d["norm_w"], d["eps"], 0,
+                                                 "conventional" if path == "conventional" else
+                                                 "fused")
+        err = oracle.compare(r_dev, out_bits, r_ref, out_ref)
+        print(path, err, flush=True)
+        assert oracle.within_tolerance(err), (path, err)
+    del x
+
+
 def test_tuning_file_on_the_device(tmp_path):
     """A tuning file saved on this device carries its key (architecture and CU count);
     reloaded after a clear it restores every decision, and an auto-mode call then runs the

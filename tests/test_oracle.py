@@ -299,6 +299,16 @@ def test_compare_accepts_own_rounding_and_rejects_planted_errors():
     assert not oracle.within_tolerance(oracle.compare(r_noy, out_bits, r_ref, out_ref))
 
 
+def test_tiled_inputs_repeat_the_block():
+    d = synth.tiled_inputs(10, 64, 128, period=3, seed=1)
+    assert d["x_block"].shape == (3, 64) and d["x_block"].dtype == np.uint16
+    assert d["W"].shape == (128, 64) and d["residual"].shape == (10, 128)
+    x = oracle.widen_bf16(d["x_block"])
+    assert abs(float(np.mean(x))) < 0.2 and 0.8 < float(np.std(x)) < 1.2
+    again = synth.tiled_inputs(10, 64, 128, period=3, seed=1)
+    np.testing.assert_array_equal(again["x_block"], d["x_block"])
+
+
 def test_workload_inputs_statistics():
     """The recipes produce the stated distributions (W variance 1/K, silu*mul second moment)."""
     d = synth.make_inputs(synth.WORKLOADS["tiny"], seed=0)
