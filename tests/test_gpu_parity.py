@@ -451,7 +451,14 @@ def test_invalid_arguments_raise():
     with pytest.raises(pr.PRError) as e:
         pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 64, 512, 512, -1)
     assert e.value.code == pr.PR_ERR_MICROCHUNK
-    pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 0, 512, 512, 16)  # T == 0: no-op
+    # T == 0 is a successful no-op on every entry point: nothing is written
+    r_before, out_before = dev.r.clone(), dev.out.clone()
+    pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 0, 512, 512, 16)
+    pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 0, 512, 512, 0, 0, dev.out)
+    pr.proj_add_rmsnorm_unfused(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 0, 512, 512, 0, dev.out)
+    pr.proj_add_rmsnorm_single_launch(dev.x, dev.Wp, dev.r, dev.w, 1e-5, 0, 512, 512, 0, dev.out)
+    torch.cuda.synchronize()
+    assert torch.equal(dev.r, r_before) and torch.equal(dev.out, out_before)
 
 
 # --------------------------------------------------------------------- weight preparation
