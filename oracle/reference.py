@@ -103,6 +103,21 @@ def rms_norm(rp: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     return rp / np.sqrt(ms + eps) * g
 
 
+def silu_mul(gate_up_bits: np.ndarray, K: int) -> np.ndarray:
+    """SiluAndMul on the merged gate/up projection output ("Plugin Architecture" page, model
+    table, SiluAndMul row, and section "Fused projections stay fused": the merged projection
+    returns [..., 2d] and SiluAndMul slices gate and up out of it).  Each token's row holds gate
+    in columns [0, K) and up in [K, 2K); x = silu(gate) * up with silu(g) = g / (1 + e^-g),
+    evaluated in float64 and rounded once to bf16 (the model dtype), returned as bf16 bits
+    [T, K].  Zero-padded columns (gate = up = 0) give x = 0, which is why the page's load-time
+    padding of the intermediate size is inert."""
+    gu = widen_bf16(gate_up_bits)
+    g, u = gu[:, :K], gu[:, K:2 * K]
+    with np.errstate(over="ignore"):
+        x = g / (1.0 + np.exp(-g)) * u
+    return bf16_bits_of(round_bf16(x))
+
+
 # --------------------------------------------------------------------------------------------
 # whole region
 # --------------------------------------------------------------------------------------------

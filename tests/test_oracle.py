@@ -299,6 +299,40 @@ def test_compare_accepts_own_rounding_and_rejects_planted_errors():
     assert not oracle.within_tolerance(oracle.compare(r_noy, out_bits, r_ref, out_ref))
 
 
+# -------------------------------------------------------------------------------- SiluAndMul
+def test_silu_mul_hand_worked():
+    """Hand-derived values.  silu(1) * 2 = 2 / (1 + e^-1) = 1.46211715...; bf16 spacing in [1, 2)
+    is 2^-7, 1.46211715 / 2^-7 = 187.15 -> 187 -> 1 + 59/128 -> 0x3FBB.  silu(-1) * 1 =
+    -1 / (1 + e) = -0.26894142...; spacing in [1/4, 1/2) is 2^-9, 0.26894142 / 2^-9 = 137.70
+    -> 138 -> 2^-2 * (1 + 10/128) -> 0xBE8A.  silu(2) * 1 = 1.76159416 -> 225.48 -> 225 -> 0x3FE1.
+    Gate comes first in the row: swapping the halves would give silu(2) * 1 in the first
+    column instead."""
+    gu = synth.f32_to_bf16_bits(np.array([[1.0, -1.0, 2.0, 2.0, 1.0, 1.0]], dtype=np.float32))
+    assert oracle.silu_mul(gu, 3)[0].tolist() == [0x3FBB, 0xBE8A, 0x3FE1]
+
+
+def test_silu_mul_matches_torch_silu_and_padding_is_inert():
+    """torch's silu in float64 times up, rounded by round_bf16 (itself pinned against torch's
+    cast); zero gate and up columns (the load-time padding) give exact zeros; large positive
+    gates pass through (silu(g) = g to double precision), large negative ones vanish."""
+    rng = np.random.default_rng(21)
+    T, K, pad = 7, 40, 8
+    g = rng.standard_normal((T, K)) * 3
+    u = rng.standard_normal((T, K))
+    g[:, K - pad:] = 0.0
+    u[:, K - pad:] = 0.0
+    g[0, 0], u[0, 0] = 80.0, 1.5
+    g[0, 1], u[0, 1] = -80.0, 1.5
+    gu = synth.f32_to_bf16_bits(np.concatenate([g, u], axis=1).astype(np.float32))
+    got = oracle.silu_mul(gu, K)
+    gw, uw = oracle.widen_bf16(gu[:, :K]), oracle.widen_bf16(gu[:, K:])
+    want = torch.nn.functional.silu(torch.from_numpy(gw)).numpy() * uw
+    np.testing.assert_array_equal(got, oracle.bf16_bits_of(oracle.round_bf16(want)))
+    assert np.all(got[:, K - pad:] == 0)
+    assert oracle.widen_bf16(got[0, 0]) == oracle.round_bf16(np.array(80.0 * 1.5))
+    assert abs(oracle.widen_bf16(got[0, 1])) < 1e-30
+
+
 def test_tiled_inputs_repeat_the_block():
     d = synth.tiled_inputs(10, 64, 128, period=3, seed=1)
     assert d["x_block"].shape == (3, 64) and d["x_block"].dtype == np.uint16
