@@ -87,6 +87,23 @@ int pr_prepare_weight(const uint16_t* W_src, int src_layout, uint16_t* W_prep, i
                       void* stream);
 
 /*
+ * SiluAndMul, the step before down_proj ("Plugin Architecture" page, SiluAndMul row and section
+ * Fused projections stay fused: the merged gate/up projection returns [..., 2d] and SiluAndMul
+ * slices gate and up out of it; the intermediate size is zero-padded to a multiple of 64 at
+ * load, which is inert because silu(0) = 0).
+ *
+ * gate_up [T][2K] bf16, device, caller-owned: row t holds gate in columns [0, K) and up in
+ *         [K, 2K) (the merged projection's output as it is laid out).
+ * x       [T][K] bf16, device, caller-owned, written here: x = silu(gate) * up, computed in
+ *         fp32 with silu(g) = g / (1 + e^-g) and rounded once to bf16 (round to nearest even).
+ *         It is the x input of proj_add_rmsnorm and its siblings with the same K.
+ * K is the padded intermediate size, a positive multiple of 64.  Both pointers 16-byte aligned;
+ * x must not overlap gate_up.  Asynchronous on `stream`; T = 0 is a no-op.
+ * Errors: PR_ERR_SHAPE, PR_ERR_INVALID_ARG, PR_ERR_UNSUPPORTED (not a gfx950 device), PR_ERR_HIP.
+ */
+int pr_silu_mul(const uint16_t* gate_up, uint16_t* x, int T, int K, void* stream);
+
+/*
  * The fused region, one device's share ("TPSP Design" sections 1 and 3).
  *
  * x              [T][K] bf16, read only.

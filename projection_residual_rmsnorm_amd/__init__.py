@@ -70,6 +70,7 @@ SIGNATURES = {
     "pr_profile_enable": (_i, [_i]),
     "pr_profile_read": (_i, [_c.POINTER(pr_profile)]),
     "pr_prepare_weight": (_i, [_vp, _i, _vp, _i, _i, _vp]),
+    "pr_silu_mul": (_i, [_vp, _vp, _i, _i, _vp]),
     "proj_add_rmsnorm": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _i, _vp, _vp]),
     "proj_add_rmsnorm_unfused": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp, _vp]),
     "proj_add_rmsnorm_single_launch": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp, _vp]),
@@ -166,6 +167,13 @@ def pr_prepare_weight(W_src, src_layout: int, W_prep, K: int, H: int, stream=Non
     n = 2 * max(K, 0) * max(H, 0)
     _check(_lib().pr_prepare_weight(_ptr(W_src, n, "W_src"), src_layout,
                                     _ptr(W_prep, n, "W_prep"), K, H, _stream(stream, W_src)))
+
+
+def pr_silu_mul(gate_up, x, T: int, K: int, stream=None) -> None:
+    """x[T][K] = bf16(silu(gate) * up) from the merged gate_up[T][2K] (gate first)."""
+    n = 2 * max(T, 0) * max(K, 0)
+    _check(_lib().pr_silu_mul(_ptr(gate_up, 2 * n, "gate_up"), _ptr(x, n, "x"), T, K,
+                              _stream(stream, gate_up)))
 
 
 def _call_ptrs(x, W, residual_inout, norm_w, out, T: int, K: int, H: int):

@@ -113,6 +113,10 @@ int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, con
 int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,
                           void* stream);
 
+// x[T][K] = bf16(silu(gate) * up) from the merged gate_up[T][2K] (gate first); K % 8 == 0,
+// both 16-byte aligned.
+int launch_silu_mul(const uint16_t* gate_up, uint16_t* x, int T, int K, void* stream);
+
 // Debug helpers: a bounded sleep (iters x s_sleep 127) and a NaN fill.
 int launch_delay(int iters, void* stream);
 int launch_fill_nan(float* p, size_t n, void* stream);

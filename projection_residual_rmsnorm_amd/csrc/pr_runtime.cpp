@@ -506,6 +506,24 @@ int pr_prepare_weight(const uint16_t* W_src, int src_layout, uint16_t* W_prep, i
   return launch_prepare_weight(W_src, src_layout, W_prep, K, H, stream);
 }
 
+int pr_silu_mul(const uint16_t* gate_up, uint16_t* x, int T, int K, void* stream) {
+  clear_error();
+  if (T < 0 || K <= 0 || K % 64 != 0)
+    return fail(PR_ERR_SHAPE, "T=%d must be >= 0 and K=%d a positive multiple of 64", T, K);
+  if ((long long)T * K > (1LL << 40)) return fail(PR_ERR_SHAPE, "T=%d too large", T);
+  if (T == 0) return PR_OK;
+  if (gate_up == nullptr || x == nullptr) return fail(PR_ERR_INVALID_ARG, "null tensor pointer");
+  if ((uintptr_t)gate_up % 16 != 0 || (uintptr_t)x % 16 != 0)
+    return fail(PR_ERR_INVALID_ARG, "gate_up and x must be 16-byte aligned");
+  const uintptr_t g0 = (uintptr_t)gate_up, g1 = g0 + 4ULL * T * K;
+  const uintptr_t x0 = (uintptr_t)x, x1 = x0 + 2ULL * T * K;
+  if (x0 < g1 && g0 < x1) return fail(PR_ERR_INVALID_ARG, "x overlaps gate_up");
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  (void)c;
+  return launch_silu_mul(gate_up, x, T, K, stream);
+}
+
 int proj_add_rmsnorm(const uint16_t* x, const uint16_t* W, float* residual_inout,
                      const float* norm_w, float eps, int T, int K, int H, int microchunk,
                      int norm_kind, uint16_t* out, void* stream) {

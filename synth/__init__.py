@@ -114,6 +114,28 @@ def make_custom(T: int, K: int, H: int, seed: int = 0, norm_kind: int = NORM_STA
     return make_inputs(wl, seed)
 
 
+def gate_up_inputs(T: int, K: int, H: int, seed: int = 0, K_real: Optional[int] = None,
+                   eps: float = 1e-5) -> dict:
+    """Inputs of the down_proj block taken from the merged gate/up projection output:
+    gate_up [T, 2K] bf16 (gate in columns [0, K), up in [K, 2K); gate, up ~ N(0,1)), the
+    nn.Linear weight W [H, K] ~ N(0, 1/K_real), residual ~ N(0,1), norm weight 1 + N(0, 0.1).
+    Columns [K_real, K) of gate, up and W are zero: the load-time padding of the intermediate
+    size.  Drawn in that order with PCG64 ``default_rng(seed)``."""
+    Kr = K if K_real is None else K_real
+    rng = np.random.default_rng(seed)
+    gu = np.zeros((T, 2 * K), dtype=np.uint16)
+    gu[:, :Kr] = f32_to_bf16_bits(rng.standard_normal((T, Kr), dtype=np.float32))
+    gu[:, K:K + Kr] = f32_to_bf16_bits(rng.standard_normal((T, Kr), dtype=np.float32))
+    W = np.zeros((H, K), dtype=np.uint16)
+    W[:, :Kr] = f32_to_bf16_bits(rng.standard_normal((H, Kr), dtype=np.float32) *
+                                 np.float32(1.0 / np.sqrt(Kr)))
+    residual = rng.standard_normal((T, H), dtype=np.float32)
+    nw = rng.standard_normal(H, dtype=np.float32) * np.float32(0.1) + np.float32(1.0)
+    return {"gate_up": gu, "W": W, "residual": residual, "norm_w": nw.astype(np.float32),
+            "eps": float(np.float32(eps)), "norm_kind": NORM_STANDARD, "T": T, "K": K, "H": H,
+            "K_real": Kr}
+
+
 def tiled_inputs(T: int, K: int, H: int, period: int, seed: int = 0) -> dict:
     """Inputs for shapes whose x is too large to draw in full on the host: x is a block of
     `period` drawn rows (N(0,1), bf16), repeated down the T rows, so token t's row is block row

@@ -602,6 +602,101 @@ def test_launch_split_past_2_30_elements_of_x():
     del x
 
 
+# ---------------------------------------------------------------------------------- SiluAndMul
+def _bf16_ordered(b):
+    """bf16 bit patterns as integers in value order (one step per ulp; +0 and -0 both 0)."""
+    b = np.asarray(b, dtype=np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def _silu_mul_check(gu_bits, x_bits, K, K_real):
+    """x against the oracle: the kernel computes in fp32, the oracle in float64, and each
+    rounds once to bf16, so an element may land one bf16 ulp apart when the exact value sits
+    next to a rounding boundary.  Distances are counted in ulps on the value line, where the
+    two zeros coincide (a zero gate or up drawn with a sign gives -0 on the device, +0 in the
+    oracle).  Padded columns must be exactly zero."""
+    want = _bf16_ordered(oracle.silu_mul(gu_bits, K))
+    got = _bf16_ordered(x_bits)
+    assert np.all(np.abs(got - want) <= 1), np.abs(got - want).max()
+    assert np.mean(got != want) < 1e-3, np.mean(got != want)
+    assert np.all(x_bits[:, K_real:] == 0)
+
+
+@pytest.mark.parametrize("T,K,K_real", [(300, 512, 512), (1, 64, 64), (777, 2048, 2000),
+                                        (3000, 16384, 16360)])
+def test_silu_mul_matches_oracle(T, K, K_real):
+    """Ragged token counts, padded intermediate sizes (Gemma's 16360 padded to 16384), and a
+    sentinel row past T that must stay untouched."""
+    d = synth.gate_up_inputs(T, K, 64, seed=T + K, K_real=K_real)
+    gu = i16(d["gate_up"])
+    x = torch.full((T + 1, K), 0x7BAD, dtype=torch.int16, device=DEV)
+    pr.pr_silu_mul(gu, x, T, K)
+    torch.cuda.synchronize()
+    xb = bits(x)
+    _silu_mul_check(d["gate_up"], xb[:T], K, K_real)
+    assert np.all(xb[T] == 0x7BAD)
+
+
+@pytest.mark.parametrize("path", ["single", 128, None])
+def test_silu_mul_then_down_proj_parity(path):
+    """The down_proj block from the merged gate/up output: SiluAndMul, then the projection,
+    residual add and RMSNorm, against the oracle's SiluAndMul followed by its fused (or
+    conventional) region."""
+    T, K, H = 300, 1024, 512
+    d = synth.gate_up_inputs(T, K, H, seed=31, K_real=1000)
+    x = torch.empty((T, K), dtype=torch.int16, device=DEV)
+    pr.pr_silu_mul(i16(d["gate_up"]), x, T, K)
+    torch.cuda.synchronize()
+    dd = dict(d, x=oracle.silu_mul(d["gate_up"], K))
+    dev = Device(dd)
+    dev.x = x  # the device's own SiluAndMul output feeds the projection
+    r_dev, out_bits = dev.run(path)
+    _check(dd, r_dev, out_bits, "conventional" if path is None else "fused")
+
+
+def test_silu_mul_down_proj_full_size():
+    """down_proj at full size (T = 4096, intermediate 14336, H = 4096) from gate_up: x on
+    sampled rows, then the single launch on those rows."""
+    T, K, H = 4096, 14336, 4096
+    print(f"silu_mul down_proj: T={T} K={K} H={H}", flush=True)
+    d = synth.gate_up_inputs(T, K, H, seed=0)
+    gu = i16(d["gate_up"])
+    x = torch.empty((T, K), dtype=torch.int16, device=DEV)
+    pr.pr_silu_mul(gu, x, T, K)
+    torch.cuda.synchronize()
+    rows = _sample_rows(T, T, seed=3)
+    _silu_mul_check(d["gate_up"][rows], bits(x[rows]), K, K)
+    W_src = i16(d["W"])
+    Wp = torch.empty(K * H, dtype=torch.int16, device=DEV)
+    pr.pr_prepare_weight(W_src, pr.PR_WEIGHT_OUT_IN, Wp, K, H)
+    r = f32(d["residual"])
+    out = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    pr.proj_add_rmsnorm_single_launch(x, Wp, r, f32(d["norm_w"]), d["eps"], T, K, H, 0, out)
+    assert pr.pr_device_status(torch.cuda.current_stream()) == 0
+    torch.cuda.synchronize()
+    x_ref = oracle.silu_mul(d["gate_up"][rows], K)
+    r_ref, out_ref = oracle.proj_add_rmsnorm(x_ref, d["W"], d["residual"][rows], d["norm_w"],
+                                             d["eps"], 0, "fused")
+    err = oracle.compare(r[rows].cpu().numpy(), bits(out[rows]), r_ref, out_ref)
+    print(err, flush=True)
+    assert oracle.within_tolerance(err), err
+
+
+def test_silu_mul_invalid_arguments():
+    gu = torch.zeros((4, 256), dtype=torch.int16, device=DEV)
+    x = torch.zeros((4, 128), dtype=torch.int16, device=DEV)
+    with pytest.raises(pr.PRError) as e:
+        pr.pr_silu_mul(gu, x, 4, 96)
+    assert e.value.code == pr.PR_ERR_SHAPE
+    with pytest.raises(pr.PRError) as e:
+        pr.pr_silu_mul(gu, gu, 4, 64)   # x inside gate_up
+    assert e.value.code == pr.PR_ERR_INVALID_ARG
+    pr.pr_silu_mul(gu, x, 0, 128)        # T = 0: no-op
+    torch.cuda.synchronize()
+    assert int(x.abs().sum()) == 0
+
+
 def test_tuning_file_on_the_device(tmp_path):
     """A tuning file saved on this device carries its key (architecture and CU count);
     reloaded after a clear it restores every decision, and an auto-mode call then runs the
