@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--addnorm-roofline", action="store_true",
                     help="HBM rate of the conventional path's add/norm kernel on every workload, "
                          "Infinity Cache warm and flushed, beside a plain device copy")
+    ap.add_argument("--silu-mul", action="store_true",
+                    help="HBM rate of the SiluAndMul kernel (down_proj and Gemma intermediate "
+                         "sizes, warm and flushed) and the down_proj block it opens")
     ap.add_argument("--tp-share", default="",
                     help="comma-separated tensor-parallel degrees P: time one rank's share of "
                          "the workload (projection over K/P, add/norm of T/P rows with P fp32 "
@@ -299,6 +302,79 @@ def addnorm_roofline(pr, torch, args) -> int:
     return 0
 
 
+def silu_mul_roofline(pr, torch, args) -> int:
+    """SiluAndMul from the merged gate/up output: algorithmic bytes per element of x (gate 2 +
+    up 2 read, x 2 written) over the event-timed kernel, warm and flushed (a 512 MB read before
+    each call), against 8 TB/s; then the down_proj block (SiluAndMul followed by the single
+    launch) against the single launch alone, back to back, the two series alternated five
+    times (medians)."""
+    import synth
+    dev = "cuda:0"
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    flush = torch.zeros(1 << 27, dtype=torch.float32, device=dev)
+    rows = []
+    for name in ("down_proj", "gemma"):
+        wl = synth.WORKLOADS[name]
+        T, K, H = wl.T, wl.K, wl.H
+        d = synth.gate_up_inputs(T, K, H, seed=0, K_real=wl.K_real, eps=wl.eps)
+        gu = torch.from_numpy(d["gate_up"].view(np.int16)).to(dev)
+        x = torch.empty((T, K), dtype=torch.int16, device=dev)
+        nbytes = 6 * T * K
+        res = {"workload": name, "T": T, "K": K, "bytes": nbytes}
+        for mode in ("warm", "flushed"):
+            ts = []
+            for i in range(max(args.steps // 2, 10) + 2):
+                if mode == "flushed":
+                    evict(flush)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                pr.pr_silu_mul(gu, x, T, K, stream)
+                e1.record(stream)
+                e1.synchronize()
+                if i >= 2:
+                    ts.append(e0.elapsed_time(e1) / 1e3)
+            t = float(np.median(ts))
+            res[f"{mode}_us"] = t * 1e6
+            res[f"{mode}_GBs"] = nbytes / t / 1e9
+        res["frac_hbm_peak_flushed"] = res["flushed_GBs"] / PEAK_HBM_GBS
+        # the block: SiluAndMul then the single launch, against the single launch alone
+        W_src = torch.from_numpy(d["W"].view(np.int16)).to(dev)
+        Wp = torch.empty(K * H, dtype=torch.int16, device=dev)
+        pr.pr_prepare_weight(W_src, pr.PR_WEIGHT_OUT_IN, Wp, K, H)
+        del W_src
+        r = torch.from_numpy(d["residual"]).to(dev)
+        w = torch.from_numpy(d["norm_w"]).to(dev)
+        out = torch.empty((T, H), dtype=torch.int16, device=dev)
+
+        def single():
+            pr.proj_add_rmsnorm_single_launch(x, Wp, r, w, d["eps"], T, K, H, wl.norm_kind, out,
+                                              stream)
+
+        def block():
+            pr.pr_silu_mul(gu, x, T, K, stream)
+            single()
+        # alternated, so that clock drift between the two series cancels
+        series = {"single_launch": [], "block": []}
+        for _ in range(5):
+            for label, fn in (("single_launch", single), ("block", block)):
+                el = time_steps(fn, args.steps, args.warmup, torch)
+                series[label].append(el * 1e3 / args.steps)
+        for label, v in series.items():
+            res[f"{label}_ms"] = float(np.median(v))
+        if pr.pr_device_status(stream) != 0:
+            raise SystemExit("single-launch status bits set: a row wait gave up")
+        rows.append(res)
+        log(f"{name}: silu_mul {res['warm_us']:.1f} us warm ({res['warm_GBs']:.0f} GB/s), "
+            f"{res['flushed_us']:.1f} us flushed ({res['flushed_GBs']:.0f} GB/s); block "
+            f"{res['block_ms']:.4f} ms vs single launch {res['single_launch_ms']:.4f} ms")
+        del gu, x, Wp, r, w, out
+        torch.cuda.empty_cache()
+    print(json.dumps({"silu_mul": rows, "peak_GBs": PEAK_HBM_GBS}), flush=True)
+    return 0
+
+
 XGMI_LINK_GBS = 153.0   # one xGMI link, per direction
 
 
@@ -412,6 +488,8 @@ def main() -> int:
         return tp_share(pr, torch, args)
     if args.addnorm_roofline:
         return addnorm_roofline(pr, torch, args)
+    if args.silu_mul:
+        return silu_mul_roofline(pr, torch, args)
     wl = synth.WORKLOADS[args.workload]
     T, K, H = wl.T, wl.K, wl.H
     log(f"workload {wl.name}: T={T} K={K} H={H} chunk sizes {wl.microchunks}")

@@ -34,7 +34,8 @@ COPY_BYTES = 1 << 30
 def short_name(name: str) -> str:
     m = re.search(r"(gemm_add_rmsnorm_kernel<[^>]*>|gemm_bf16_kernel<[^>]*>|"
                   r"(?<!gemm_)add_rmsnorm\w*<[^>]*>|add_rmsnorm_generic_kernel|"
-                  r"prepare_weight\w*|__amd_rocclr_\w+|fill_\w+|delay_kernel)", name)
+                  r"prepare_weight\w*|silu_mul_kernel<[^>]*>|__amd_rocclr_\w+|fill_\w+|"
+                  r"delay_kernel)", name)
     return m.group(1) if m else name[:60]
 
 
@@ -80,29 +81,34 @@ def bench_line_lines(log_path: str) -> List[str]:
                 f"({roof['achieved']:.1f} {roof['unit']})."]
 
 
-def dispatch_runs(trace_csv: str, kernel: str, n: int, labels: List[str]) -> List[dict]:
-    """Consecutive runs of n dispatches of a kernel (name prefix) in dispatch order, one per
-    label, with their median, min and max durations in us."""
+def dispatch_runs(trace_csv: str, kernel: str, n, labels: List[str]) -> List[dict]:
+    """Consecutive runs of dispatches of a kernel (name prefix) in dispatch order, one per
+    label, with their median, min and max durations in us; n is the dispatch count of every
+    run, or a list with one count per run."""
+    counts = list(n) if isinstance(n, (list, tuple)) else [n] * len(labels)
+    if len(counts) != len(labels):
+        raise SystemExit(f"{len(counts)} run lengths for {len(labels)} labels")
     durs = []
     for r in csv.DictReader(open(trace_csv)):
         if short_name(r["Kernel_Name"]).startswith(kernel):
             durs.append((int(r["Dispatch_Id"]),
                          (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
     durs = [d for _, d in sorted(durs)]
-    if len(durs) != n * len(labels):
-        raise SystemExit(f"kernel {kernel!r}: {len(durs)} dispatches, expected "
-                         f"{n} x {len(labels)} labels")
-    out = []
-    for i, label in enumerate(labels):
-        run = durs[i * n:(i + 1) * n]
-        out.append({"label": label, "n": n, "median_us": statistics.median(run),
+    if len(durs) != sum(counts):
+        raise SystemExit(f"kernel {kernel!r}: {len(durs)} dispatches, expected {sum(counts)}")
+    out, at = [], 0
+    for label, c in zip(labels, counts):
+        run = durs[at:at + c]
+        at += c
+        out.append({"label": label, "n": c, "median_us": statistics.median(run),
                     "min_us": min(run), "max_us": max(run)})
     return out
 
 
-def runs_summary(trace_csv: str, kernel: str, n: int, labels: List[str], command: str) -> str:
+def runs_summary(trace_csv: str, kernel: str, n, labels: List[str], command: str) -> str:
     lines = ["# rocprofv3 kernel trace: runs of dispatches", "", "Command:", "", "```", command,
-             "```", "", f"Kernel `{kernel}`, {n} dispatches per run, in dispatch order.", "",
+             "```", "", f"Kernel `{kernel}`, consecutive runs of dispatches in dispatch order.",
+             "",
              "| run | dispatches | median us | min us | max us |", "|---|---|---|---|---|"]
     for r in dispatch_runs(trace_csv, kernel, n, labels):
         lines.append(f"| {r['label']} | {r['n']} | {r['median_us']:.2f} | {r['min_us']:.2f} | "
@@ -317,13 +323,16 @@ def main() -> None:
     u.add_argument("trace")
     u.add_argument("out")
     u.add_argument("--kernel", required=True)
-    u.add_argument("--per-run", type=int, required=True)
+    u.add_argument("--per-run", required=True,
+                   help="dispatches per run: one count, or one per label (comma-separated)")
     u.add_argument("--labels", required=True, help="comma-separated, one per run")
     u.add_argument("--command", required=True)
     a = ap.parse_args()
     if a.cmd == "runs":
         with open(a.out, "w") as f:
-            f.write(runs_summary(a.trace, a.kernel, a.per_run, a.labels.split(","), a.command))
+            counts = [int(c) for c in a.per_run.split(",")]
+            f.write(runs_summary(a.trace, a.kernel, counts if len(counts) > 1 else counts[0],
+                                 a.labels.split(","), a.command))
     elif a.cmd == "counters":
         with open(a.out, "w") as f:
             f.write(counters_summary(a.csv, a.kernel, a.grid, a.command))

@@ -481,6 +481,8 @@ def test_dispatch_runs(tmp_path):
         ("warm", 11.0, 10.0, 12.0), ("flushed", 30.0, 29.0, 31.0)]
     with pytest.raises(SystemExit):
         dispatch_runs(str(trace), "add_rmsnorm_kernel", 2, ["a", "b"])
+    runs = dispatch_runs(str(trace), "add_rmsnorm_kernel", [2, 4], ["a", "b"])
+    assert [(r["n"], r["median_us"]) for r in runs] == [(2, 11.0), (4, 29.5)]
 
 
 # ------------------------------------------------------------------ tuning files
