@@ -369,6 +369,26 @@ def test_calls_without_gpu_fail_cleanly():
     assert rc in (0, pr.PR_ERR_HIP, pr.PR_ERR_UNSUPPORTED)
 
 
+def test_silu_mul_validates_before_touching_a_device():
+    """pr_silu_mul checks shape, alignment and overlap on the host, before any device call;
+    valid arguments without a GPU report an error rather than crash."""
+    lib = pr.library()
+    g, x = A, A + (1 << 24)
+    assert lib.pr_silu_mul(g, x, 4, 96, None) == pr.PR_ERR_SHAPE       # K % 64 != 0
+    assert lib.pr_silu_mul(g, x, -1, 64, None) == pr.PR_ERR_SHAPE      # T < 0
+    assert lib.pr_silu_mul(g, x, 4, 0, None) == pr.PR_ERR_SHAPE        # K == 0
+    assert lib.pr_silu_mul(None, x, 4, 64, None) == pr.PR_ERR_INVALID_ARG
+    assert lib.pr_silu_mul(g + 8, x, 4, 64, None) == pr.PR_ERR_INVALID_ARG  # misaligned
+    assert lib.pr_silu_mul(g, g + 256, 4, 64, None) == pr.PR_ERR_INVALID_ARG  # x in gate_up
+    assert lib.pr_silu_mul(None, None, 0, 64, None) == 0                # T == 0: no-op
+    import torch
+    if torch.cuda.is_available():
+        return  # the calls below pass validation and would launch on the fake addresses
+    # adjacent buffers pass the overlap check; with no device the call then fails cleanly
+    assert lib.pr_silu_mul(g, g + 1024, 4, 64, None) in (pr.PR_ERR_HIP, pr.PR_ERR_UNSUPPORTED)
+    assert lib.pr_silu_mul(g, x, 4, 64, None) in (pr.PR_ERR_HIP, pr.PR_ERR_UNSUPPORTED)
+
+
 def test_binding_rejects_strided_or_short_tensors():
     """The binding hands the library raw addresses: tensors must be contiguous and hold the
     extent the shape arguments describe (checked before the library is reached)."""
