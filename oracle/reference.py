@@ -14,7 +14,9 @@ path.  It is the plain definition of what the path computes, written to be check
   "TPSP Design" section 4 Constraints) or g = 1 + w (the Gemma form, "Plugin Architecture"
   custom-op table, GemmaRMSNorm row), the weight multiply done in fp32 or wider;
 * the microchunk partition ("TPSP Design" section 3 "Microchunk pipeline"): chunks of mc
-  rows, the last padded, and only valid rows update residual and output.
+  rows, the last padded, and only valid rows update residual and output;
+* SiluAndMul, the step before down_proj ("Plugin Architecture" page, SiluAndMul row):
+  x = silu(gate) * up from the merged gate/up projection output.
 
 Two modes fix where the projection output may be rounded:
 * ``fused``: the projection result enters the add unrounded;
