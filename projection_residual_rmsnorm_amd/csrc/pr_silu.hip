@@ -27,19 +27,22 @@ __device__ __forceinline__ float bf16_f32(uint32_t b) { return __uint_as_float(b
 // instructions (relative error near 1e-6, far below the half ulp of the bf16 result).  Zero
 // columns of the load-time padding give zeros.
 // --------------------------------------------------------------------------------------------
+constexpr int kSiluThreads = 256;  // threads per workgroup; the column loop strides by it
+
 template <int U>
-__global__ void __launch_bounds__(256) silu_mul_kernel(const uint16_t* __restrict__ gu,
-                                                      uint16_t* __restrict__ x, int T, int K) {
+__global__ void __launch_bounds__(kSiluThreads) silu_mul_kernel(const uint16_t* __restrict__ gu,
+                                                                uint16_t* __restrict__ x, int T,
+                                                                int K) {
   const int kvec = K / 8;
   for (int t = blockIdx.x; t < T; t += gridDim.x) {
     const uint4* grow = reinterpret_cast<const uint4*>(gu + (long long)t * 2 * K);
     const uint4* urow = grow + kvec;
     uint4* xrow = reinterpret_cast<uint4*>(x + (long long)t * K);
-    for (int c0 = threadIdx.x; c0 < kvec; c0 += 256 * U) {
+    for (int c0 = threadIdx.x; c0 < kvec; c0 += kSiluThreads * U) {
       uint4 g[U], u[U];
 #pragma unroll
       for (int i = 0; i < U; ++i) {
-        const int c = c0 + 256 * i;
+        const int c = c0 + kSiluThreads * i;
         if (c < kvec) {
           g[i] = grow[c];
           u[i] = urow[c];
@@ -47,7 +50,7 @@ __global__ void __launch_bounds__(256) silu_mul_kernel(const uint16_t* __restric
       }
 #pragma unroll
       for (int i = 0; i < U; ++i) {
-        const int c = c0 + 256 * i;
+        const int c = c0 + kSiluThreads * i;
         if (c < kvec) {
           const uint32_t gw[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
           const uint32_t uw[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
@@ -74,7 +77,7 @@ int launch_silu_mul(const uint16_t* gate_up, uint16_t* x, int T, int K, void* st
   constexpr int kU = 4;
   // One row per workgroup up to 16 workgroups per CU; longer inputs stride over rows.
   const int grid = std::min(T, 16 * kNumCUs);
-  hipLaunchKernelGGL(silu_mul_kernel<kU>, dim3(grid), dim3(256), 0,
+  hipLaunchKernelGGL(silu_mul_kernel<kU>, dim3(grid), dim3(kSiluThreads), 0,
                      static_cast<hipStream_t>(stream), gate_up, x, T, K);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PR_ERR_HIP, "silu_mul_kernel: %s", hipGetErrorString(e));
