@@ -375,6 +375,93 @@ def silu_mul_roofline(pr, torch, args) -> int:
     return 0
 
 
+def conventional_addnorm_flushed(pr, torch, x, Wp, r, w, out, d, wl, steps, stream) -> dict:
+    """The conventional path's add/norm kernel (the pass after the projection) with no operand
+    in the caches: before each call the residual is restored and a 512 MB buffer is read.  Its
+    algorithmic bytes per element are y read (2 for bf16 y, 4 per fp32 plane), r read 4, r write
+    4, out write 2; the rate is those bytes over the kernel's event-timed duration."""
+    T, K, H = d["T"], d["K"], d["H"]
+    flush = torch.zeros(1 << 27, dtype=torch.float32, device=r.device)
+    r0 = r.clone()
+    split = pr.pr_select(T, K, H, pr.PR_SELECT_UNFUSED)["split_k"]
+    per_elem = (2 if split == 1 else 4 * split) + 10
+    ts = []
+    for i in range(max(steps // 2, 8) + 2):
+        r.copy_(r0)
+        evict(flush)
+        pr.pr_profile_enable(True)
+        pr.proj_add_rmsnorm_unfused(x, Wp, r, w, d["eps"], T, K, H, wl.norm_kind, out, stream)
+        prof = pr.pr_profile_read()
+        pr.pr_profile_enable(False)
+        if i >= 2:
+            ts.append(prof["addnorm_ms"] / max(prof["addnorm_launches"], 1) / 1e3)
+    r.copy_(r0)
+    del flush, r0
+    t = float(np.median(ts))
+    gbs = per_elem * T * H / t / 1e9
+    log(f"conventional add/norm, flushed: {t * 1e6:.1f} us, {gbs:.0f} GB/s "
+        f"({gbs / PEAK_HBM_GBS:.3f} of 8 TB/s)")
+    return {"kernel": "add_rmsnorm_kernel", "cache": "flushed (512 MB read before each call)",
+            "y": "bf16" if split == 1 else f"{split} fp32 planes", "bytes_per_elem": per_elem,
+            "median_us": t * 1e6, "GBs": gbs, "peak_GBs": PEAK_HBM_GBS,
+            "frac": gbs / PEAK_HBM_GBS, "calls": len(ts)}
+
+
+def down_proj_entry(pr, torch, args, stream) -> dict:
+    """The second 4096-class prefill shape, down_proj (T=4096, K=14336, H=4096, x = silu(a)*b):
+    the single launch and the conventional path, timed back to back (the two series
+    alternated three times, medians), and the single launch's kernel duration from the
+    library's events."""
+    import synth
+    wl = synth.WORKLOADS["down_proj"]
+    T, K, H = wl.T, wl.K, wl.H
+    dev = "cuda:0"
+    d = synth.make_inputs(wl, seed=0)
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+    W_src = torch.from_numpy(d["W"].view(np.int16)).to(dev)
+    Wp = torch.empty(K * H, dtype=torch.int16, device=dev)
+    pr.pr_prepare_weight(W_src, pr.PR_WEIGHT_OUT_IN, Wp, K, H)
+    del W_src
+    r = torch.from_numpy(d["residual"]).to(dev)
+    w = torch.from_numpy(d["norm_w"]).to(dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    flops = 2.0 * T * K * H
+    steps = max(args.steps // 2, 5)
+    calls = {
+        "single": lambda: pr.proj_add_rmsnorm_single_launch(x, Wp, r, w, d["eps"], T, K, H,
+                                                            wl.norm_kind, out, stream),
+        "conventional": lambda: pr.proj_add_rmsnorm_unfused(x, Wp, r, w, d["eps"], T, K, H,
+                                                            wl.norm_kind, out, stream)}
+    series = {k: [] for k in calls}
+    for _ in range(3):
+        for k, fn in calls.items():
+            series[k].append(time_steps(fn, steps, max(args.warmup // 2, 2), torch) / steps)
+    pr.pr_profile_enable(True)
+    for _ in range(steps):
+        calls["single"]()
+    torch.cuda.synchronize()
+    prof = pr.pr_profile_read()
+    pr.pr_profile_enable(False)
+    if pr.pr_device_status(stream) != 0:
+        raise SystemExit("single-launch status bits set: a row wait gave up")
+    t_s, t_c = float(np.median(series["single"])), float(np.median(series["conventional"]))
+    k_s = prof["gemm_ms"] / max(prof["gemm_launches"], 1) / 1e3
+    c = pr.pr_select(T, K, H, pr.PR_SINGLE_LAUNCH)
+    res = {"workload": "down_proj prefill", "T": T, "K": K, "H": H,
+           "single_launch_ms": t_s * 1e3, "tokens_per_s": T / t_s,
+           "tflops": flops / t_s / 1e12, "frac_bf16_peak": flops / t_s / 1e12 / PEAK_BF16_TFLOPS,
+           "kernel_avg_us": k_s * 1e6, "kernel_tflops": flops / k_s / 1e12,
+           "kernel_frac": flops / k_s / 1e12 / PEAK_BF16_TFLOPS,
+           "tile": f"{c['gemm_bm']}x{c['gemm_bn']} {c['gemm_waves']} waves",
+           "conventional_ms": t_c * 1e3, "conventional_tflops": flops / t_c / 1e12}
+    log(f"down_proj: single launch {res['single_launch_ms']:.4f} ms ({res['tflops']:.0f} "
+        f"TFLOP/s, kernel {res['kernel_avg_us']:.1f} us = {res['kernel_frac']:.3f} of peak), "
+        f"conventional {res['conventional_ms']:.4f} ms")
+    del x, Wp, r, w, out
+    torch.cuda.empty_cache()
+    return res
+
+
 XGMI_LINK_GBS = 153.0   # one xGMI link, per direction
 
 
@@ -636,6 +723,13 @@ def main() -> int:
     else:
         add_per_call_stats(result, fused(mc), conventional, r, args.steps, torch, stream, dev,
                            "single launch" if single else f"mc={mc}")
+    # The conventional add/norm with cold caches (the HBM-bound stage) and the second
+    # 4096-class shape; not in profiler runs (--only-single).
+    if not args.only_single:
+        result["addnorm_conventional"] = conventional_addnorm_flushed(
+            pr, torch, x, Wp, r, w, out, d, wl, args.steps, stream)
+        if wl.name == "o_proj":
+            result["down_proj"] = down_proj_entry(pr, torch, args, stream)
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)

@@ -25,7 +25,15 @@
  *    SiluAndMul row).  T >= 0; T == 0 is a successful no-op.
  *  - Return 0 (PR_OK) or a negative PR_ERR_* code; pr_last_error() gives a message.  Invalid
  *    arguments and HIP execution errors are returned to the caller; the library never retries
- *    or silently re-routes them ("TPSP Design" section 3, Profiling and fallback).
+ *    or silently re-routes them ("TPSP Design" section 3, Profiling and fallback).  An
+ *    execution failure found on the device after a call has returned (a single-launch wait
+ *    that gave up, see proj_add_rmsnorm_single_launch) is returned as PR_ERR_HIP by the next
+ *    call of any device entry point on that device, without any synchronisation.
+ *  - HIP graph capture: the single launch can be captured (see there), and so can the
+ *    conventional path once a call of the same or a larger shape has run on the device.  A
+ *    call that would have to grow a library workspace while its stream is capturing returns
+ *    PR_ERR_UNSUPPORTED before enqueuing anything, and so does every call that would run the
+ *    microchunk pipeline (it records events and waits across a library stream).
  *  - Calls on one device are sequential: the library-owned workspace (pipeline slots, the
  *    borrowed output) is shared by all calls on that device, so concurrent calls from several
  *    host threads or streams on one device race ("TPSP Design" section 4: shared workspace
@@ -125,6 +133,8 @@ int pr_silu_mul(const uint16_t* gate_up, uint16_t* x, int T, int K, void* stream
  *                  PR_MICROCHUNK_TOKENS and PR_THRESHOLD_TOKENS override the tuned values; with
  *                  both set no tuning is needed.
  *                < 0: PR_ERR_MICROCHUNK.
+ *                The pipeline cannot be captured in a HIP graph: on a capturing stream a call
+ *                that selects it returns PR_ERR_UNSUPPORTED and enqueues nothing.
  * norm_kind      PR_NORM_STANDARD or PR_NORM_GEMMA.
  * out            [T][H] bf16, caller-owned, written.  NULL: the result goes to a library
  *                workspace returned by pr_workspace_output(), borrowed until the next call on
@@ -160,9 +170,12 @@ int proj_add_rmsnorm_unfused(const uint16_t* x, const uint16_t* W, float* residu
  * every tile of its row has published and then writes its part of the output.  The grid never
  * exceeds the workgroups the device holds at once and a wait only involves tiles of the same
  * round, so every wait ends once the launch's workgroups are placed.  A wait that nevertheless
- * exceeds its poll limit (about two seconds) gives up: that tile's rows of the call are then
- * invalid (output not written, residual update possibly missing) and a status bit read by
- * pr_device_status is set.
+ * exceeds its poll limit (about two seconds; another process holding CUs can cause it) gives
+ * up: that tile writes neither its output rows nor its residual rows (the residual keeps its
+ * value before the call, since every tile stores it only after its wait), a status bit read
+ * by pr_device_status is set, and the next call of any device entry point on this device
+ * returns PR_ERR_HIP (it reads a flag in host-mapped memory that the kernel sets; no
+ * synchronisation is involved).
  *
  * Same arguments and ownership as proj_add_rmsnorm_unfused.  Requires H = tile columns * n
  * with n <= 64 for one of the tiles the library instantiates (256 or 128 columns), else
@@ -188,15 +201,27 @@ int proj_add_rmsnorm_single_launch(const uint16_t* x, const uint16_t* W, float* 
 
 /*
  * Status bits that single-launch calls on the current device collected since the last read:
- * bit 0 = a tile's wait for its row gave up (its output rows are not written).  Waits for the
- * calls enqueued on `stream` to finish, stores the bits in *status (0 when none) and clears
- * them.  Errors: PR_ERR_INVALID_ARG (status NULL), PR_ERR_HIP.
+ * bit 0 = a tile's wait for its row gave up (its output and residual rows are not written).
+ * Waits for the calls enqueued on `stream` to finish, stores the bits in *status (0 when
+ * none) and clears them, together with the host-side flag the next call would report.
+ * Errors: PR_ERR_INVALID_ARG (status NULL), PR_ERR_HIP.
  */
 int pr_device_status(void* stream, unsigned* status);
 
 /* Device pointer of the borrowed output of the last call made with out == NULL on the current
  * device, or NULL if there was none.  Valid until the next call on that device. */
 const uint16_t* pr_workspace_output(void);
+
+/*
+ * Frees every workspace the library has grown on the current device (pipeline slots, the
+ * conventional path's projection output, the borrowed output, the single launch's slots and
+ * words, the pair form's exchange regions) after waiting for all work on the device; the
+ * library stream and events stay.  The next call grows what it needs again ("TPSP Design"
+ * section 4, Resources: the workspace is sized by the largest microchunk and token count
+ * used).  The borrowed output pointer becomes invalid.  Not to be called while another call on
+ * the device is in flight.  Errors: PR_ERR_UNSUPPORTED (no usable device), PR_ERR_HIP.
+ */
+int pr_release_workspace(void);
 
 /* ---------------------------------------------------------------------------------------- *
  * Host-only helpers (no device work; usable without a GPU)

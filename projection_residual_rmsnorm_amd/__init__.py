@@ -76,6 +76,7 @@ SIGNATURES = {
     "proj_add_rmsnorm_single_launch": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp, _vp]),
     "pr_device_status": (_i, [_vp, _c.POINTER(_c.c_uint)]),
     "pr_workspace_output": (_vp, []),
+    "pr_release_workspace": (_i, []),
     "pr_validate": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _i, _vp]),
     "pr_select": (_i, [_i, _i, _i, _i, _c.POINTER(pr_decision)]),
     "pr_plan": (_i, [_i, _i, _c.POINTER(pr_plan_op), _i]),
@@ -215,6 +216,11 @@ def pr_device_status(stream=None) -> int:
 
 def pr_workspace_output() -> Optional[int]:
     return _lib().pr_workspace_output()
+
+
+def pr_release_workspace() -> None:
+    """Frees the library's grown workspaces on the current device (waits for the device)."""
+    _check(_lib().pr_release_workspace())
 
 
 def pr_validate(x, W, residual_inout, norm_w, eps, T, K, H, microchunk, norm_kind, out) -> int:

@@ -88,6 +88,8 @@ int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_s
 //          words: 16384 per workgroup of a round, twice that for launches of several rounds).
 //   fault_mask: 0, or a nonzero mask that makes every wait look for an epoch no word carries
 //          (tests of the give-up path); spin_limit: polls before a wait gives up.
+//   host_flag: NULL, or a word of host-mapped memory that a tile whose wait gives up sets to 1
+//          (the next library call on the device reads it without synchronising).
 // An epoch-tagged word holding the launch's epoch was written by that launch; a cleared word
 // holds epoch 0, which no launch uses.
 struct SingleWs {
@@ -100,6 +102,7 @@ struct SingleWs {
   size_t xbuf_words = 0;
   unsigned fault_mask = 0;
   unsigned spin_limit = 0;
+  unsigned* host_flag = nullptr;
 };
 
 // Projection, residual add and RMSNorm of M rows in one launch (tile cfg.bm x cfg.bn, 8 waves

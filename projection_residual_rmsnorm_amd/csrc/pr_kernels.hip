@@ -417,16 +417,16 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
 //   1. loads its tile's residual into registers (tiles where it fits: 64 registers per lane
 //      with two waves per SIMD, 128 with one) and runs the projection main loop of its BM x BN
 //      tile,
-//   2. forms r + y in fp32 (the fused mode's unrounded y), writes it as the updated residual
-//      (here or, for tiles whose residual was not prefetched, in step 5) and takes, per token,
-//      the sum of squares over its BN columns (lane partials in column order, reduced over the
-//      lanes of a row, then over the waves of the tile in wave order),
+//   2. forms r + y in fp32 (the fused mode's unrounded y), keeps it in registers and takes,
+//      per token, the sum of squares over its BN columns (lane partials in column order,
+//      reduced over the lanes of a row, then over the waves of the tile in wave order),
 //   3. publishes each token's partial in a 64-bit slot {call epoch, value} and adds one to its
 //      tile row's counter,
 //   4. waits (one lane, bounded) until the counter shows every tile of the row, reads the
 //      row's slots in tile-column order (re-reading any slot that does not yet carry this
 //      call's epoch, read_epoch, bounded) and forms 1/sqrt(sum/H + eps),
-//   5. writes the bf16 output of its tile.
+//   5. writes the updated residual and the bf16 output of its tile (both after the wait, so a
+//      tile whose wait gives up writes neither).
 // Slots and counters are written and read with device-scope atomic stores, loads and adds, so
 // no cache-wide fence is needed: a slot's epoch says whether its value is this call's.  r + y
 // stays in registers from step 2 to step 5, so HBM traffic beyond the projection is the
@@ -436,8 +436,9 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
 // never larger than the workgroups the GPU holds at once.  A wait only involves tiles of the
 // same round, and a tile reaches step 3 without waiting on anything, so the waits end once
 // the launch's workgroups have been placed (which needs only CU slots that other kernels
-// free by finishing).  A wait that exceeds spin_limit polls gives up (status bit 0 is set and
-// the tile writes no output), so every workgroup exits in any case.  read_epoch equals epoch;
+// free by finishing).  A wait that exceeds spin_limit polls gives up (status bit 0 is set, the
+// host flag too, and the tile writes neither residual nor output), so every workgroup exits in
+// any case.  read_epoch equals epoch;
 // a test of the give-up path passes one that no slot carries.
 // sync: [0] status bits, [1] workgroups finished, [2 ..] per tile row counters.  All are zero
 // before the launch; the last workgroup to finish sets [1 ..] back to zero.
@@ -477,6 +478,16 @@ __device__ void finish_launch(unsigned* sync, int ncounters, unsigned epoch,
   }
 }
 
+// A tile's wait gave up: status bit 0 in the device word sync[0] (read by pr_device_status)
+// and, when the runtime provides one, a flag in host-mapped memory that the next library call
+// on the device reads without synchronising (a system-scope vector store; many tiles may
+// store the same 1).
+__device__ __forceinline__ void report_give_up(unsigned* sync, unsigned* host_flag) {
+  __hip_atomic_fetch_or(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (host_flag != nullptr)
+    __hip_atomic_store(host_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Sum over each group of LANES consecutive lanes (8 or 16, within one 16-lane DPP row); every
 // lane of the group gets the same value (each step adds a lane and its partner, which is
 // commutative, so the partners' results are bitwise equal).
@@ -504,7 +515,8 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
                             int tiles_n, int rows_per_round, float eps, int gemma,
                             unsigned fault_mask, unsigned spin_limit,
                             unsigned long long* __restrict__ pwords,
-                            unsigned long long slot_words, unsigned long long pword_words) {
+                            unsigned long long slot_words, unsigned long long pword_words,
+                            unsigned* __restrict__ host_flag) {
   // Main loop: KG groups of WM x WN waves (wave tiles BM/WM x BN/WN, TM x TN MFMA blocks).
   // Epilogue: after the groups' partials are combined, EWM x WN waves, each owning a
   // BM/EWM x BN/WN tile (ETM x TN blocks).
@@ -691,14 +703,8 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
           const float4 y = *reinterpret_cast<const float4*>(ep + r_in * EP_LD + rcol);
           const float4 rv = keep[(i * 2 + h) * NR + rr];
           const float4 v = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
-          // Streaming stores: the updated residual and the output are not read again here.
-          // Without the prefetch the residual loads of the next slice would queue behind these
-          // stores (one counter covers loads and stores), so those tiles store it with the
-          // output instead.
-          if constexpr (PREFETCH)
-            if (m0 + trow < M)
-              __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
-                                          reinterpret_cast<f32x4_t*>(R + (long long)row * N + col));
+          // r + y stays in registers; the residual is stored with the output, after the row
+          // wait, so a tile whose wait gives up leaves its residual rows as they were.
           keep[(i * 2 + h) * NR + rr] = v;
           const float q = lane_group_sum<LPR>(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
           if (el % LPR == 0) sred[trow * WN + wn] = q;
@@ -775,8 +781,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     }
     __syncthreads();
     if (*sflag == 0) {
-      if (threadIdx.x == 0)
-        __hip_atomic_fetch_or(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) report_give_up(sync, host_flag);
     } else {
       const float4 g = *reinterpret_cast<const float4*>(w + col);
       const float gx = g.x + g0, gy = g.y + g0, gz = g.z + g0, gw = g.w + g0;
@@ -790,9 +795,9 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
             const int row = m0 + trow;
             if (row < M) {
               const float4 v = keep[(i * 2 + h) * NR + rr];
-              if constexpr (!PREFETCH)
-                __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
-                                            reinterpret_cast<f32x4_t*>(R + (long long)row * N + col));
+              // Streaming stores: the updated residual and the output are not read again here.
+              __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
+                                          reinterpret_cast<f32x4_t*>(R + (long long)row * N + col));
               const float inv = sinv[trow];
               const uint32_t o0 = f32_to_bf16_rne(v.x * inv * gx);
               const uint32_t o1 = f32_to_bf16_rne(v.y * inv * gy);
@@ -844,7 +849,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
 // per load, the loads a stage would take), so it lands while the last stages compute.  After
 // the loop the four waves that hand their rows over write the hand-over; the four waves that
 // keep their rows add the partner's partial, form r + y in place in LDS and the row sums; all
-// eight waves then write the residual, wait for the row block and write the output from LDS.
+// eight waves then wait for the row block and write the residual and the output from LDS.
 //
 // Exchange regions: `xbuf` holds 128 KiB per workgroup and round parity (the region a
 // workgroup writes in round q is rewritten in round q + 2 only after the partner's round q + 1
@@ -882,7 +887,8 @@ __global__ void __launch_bounds__(512, 1)
                                  int tiles_m, int tiles_n, int rows_per_round, float eps,
                                  int gemma, unsigned fault_mask, unsigned spin_limit,
                                  unsigned long long slot_words,
-                                 unsigned long long pword_words) {
+                                 unsigned long long pword_words,
+                                 unsigned* __restrict__ host_flag) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4;
   constexpr int TM = 4, TN = 2;       // 128 x 64 wave tiles
   constexpr int HB = 128;             // rows kept per workgroup
@@ -1039,8 +1045,7 @@ __global__ void __launch_bounds__(512, 1)
     if (*sflag == 0) {
       // The partner never announced its half: this block writes nothing (its row block's
       // waits give up in turn).
-      if (et == 0)
-        __hip_atomic_fetch_or(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (et == 0) report_give_up(sync, host_flag);
       __syncthreads();
       continue;
     }
@@ -1129,21 +1134,8 @@ __global__ void __launch_bounds__(512, 1)
     }
     __syncthreads();
     unsigned* const cnt = sync + 3 + tm * 2 + h;
-    if (et == 0)
-      __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // The updated residual: 16 rows of 1 KiB per wave, from LDS.
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int trow = wave * 16 + k;
-      const int row = own0 + trow;
-      const float4 v = *reinterpret_cast<const float4*>(rbuf(trow / 32) + (trow % 32) * 1024 +
-                                                        el * 16);
-      if (row < M)
-        __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
-                                    reinterpret_cast<f32x4_t*>(R + (long long)row * N + n0 +
-                                                               el * 4));
-    }
     if (et == 0) {
+      __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       unsigned polls = 0;
       while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                  (unsigned)tiles_n &&
@@ -1195,9 +1187,21 @@ __global__ void __launch_bounds__(512, 1)
     }
     __syncthreads();
     if (*sflag == 0) {
-      if (et == 0)
-        __hip_atomic_fetch_or(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (et == 0) report_give_up(sync, host_flag);
     } else {
+      // The updated residual (16 rows of 1 KiB per wave, from LDS), stored only now so that a
+      // block whose wait gave up leaves its residual rows as they were.
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int trow = wave * 16 + k;
+        const int row = own0 + trow;
+        const float4 v = *reinterpret_cast<const float4*>(rbuf(trow / 32) + (trow % 32) * 1024 +
+                                                          el * 16);
+        if (row < M)
+          __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
+                                      reinterpret_cast<f32x4_t*>(R + (long long)row * N + n0 +
+                                                                 el * 4));
+      }
       // Output: 16 rows per wave, two rows per instruction, 8 columns (16 bytes) per lane.
       const int c8 = (el & 31) * 8;
       const float4 ga = *reinterpret_cast<const float4*>(w + n0 + c8);
@@ -1613,11 +1617,12 @@ int launch_single_t(const uint16_t* x, const uint16_t* Wp, float* r, const float
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, t0, t1, 0, x, Wp, r, w, out,
                           ws.slots, ws.sync, M, N, K, tiles_m, tiles_n, rows_per_round, eps,
                           gemma, ws.fault_mask, ws.spin_limit, ws.pwords, ws.slot_words,
-                          ws.pword_words);
+                          ws.pword_words, ws.host_flag);
   } else {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, Wp, r, w, out, ws.slots,
                        ws.sync, M, N, K, tiles_m, tiles_n, rows_per_round, eps, gemma,
-                       ws.fault_mask, ws.spin_limit, ws.pwords, ws.slot_words, ws.pword_words);
+                       ws.fault_mask, ws.spin_limit, ws.pwords, ws.slot_words, ws.pword_words,
+                       ws.host_flag);
   }
   return check_launch("gemm_add_rmsnorm_kernel");
 }
@@ -1647,11 +1652,12 @@ int launch_pair(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, t0, t1, 0, x, Wp, r, w, out,
                           ws.slots, ws.sync, ws.pwords, ws.xbuf, M, N, K, tiles_m, tiles_n,
                           rows_per_round, eps, gemma, ws.fault_mask, ws.spin_limit,
-                          ws.slot_words, ws.pword_words);
+                          ws.slot_words, ws.pword_words, ws.host_flag);
   } else {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, Wp, r, w, out, ws.slots,
                        ws.sync, ws.pwords, ws.xbuf, M, N, K, tiles_m, tiles_n, rows_per_round,
-                       eps, gemma, ws.fault_mask, ws.spin_limit, ws.slot_words, ws.pword_words);
+                       eps, gemma, ws.fault_mask, ws.spin_limit, ws.slot_words, ws.pword_words,
+                       ws.host_flag);
   }
   return check_launch("gemm_add_rmsnorm_pair_kernel");
 }

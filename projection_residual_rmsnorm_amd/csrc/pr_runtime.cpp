@@ -53,6 +53,14 @@ struct DevCtx {
   void* xbuf = nullptr;
   size_t xbuf_bytes = 0;
   const uint16_t* last_borrowed = nullptr;
+  // Give-up flag of the single launch in host-mapped memory (host address and the address the
+  // kernels store to): set by a tile whose bounded wait gave up, read and cleared by the next
+  // library call on this device without any synchronisation.
+  unsigned* host_flag = nullptr;
+  unsigned* host_flag_dev = nullptr;
+  // The current call is being captured into a HIP graph on its stream: workspaces must not
+  // grow and no timing events are recorded.
+  bool capturing = false;
   // the previous pipeline call: its caller stream and the done slots of its last chunk on
   // each stream (-1 if none)
   hipStream_t prev_caller = nullptr;
@@ -99,7 +107,7 @@ int take_event(DevCtx* c, hipEvent_t* e) {
 // into two timing events (extended launch), else both are NULL.
 template <typename F>
 int timed(DevCtx* c, int kind, F&& launch) {
-  if (!g_profile.load(std::memory_order_relaxed)) return launch(nullptr, nullptr);
+  if (!g_profile.load(std::memory_order_relaxed) || c->capturing) return launch(nullptr, nullptr);
   DevCtx::Timed t{nullptr, nullptr, kind};
   PR_TRY(take_event(c, &t.start));
   if (const int rc = take_event(c, &t.stop); rc != PR_OK) {
@@ -168,8 +176,18 @@ int get_ctx(DevCtx** out) {
   hipError_t e = hipStreamCreateWithFlags(&c->sL, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreate(&c->entry);
   for (int s = 0; s < PR_NUM_SLOTS && e == hipSuccess; ++s) e = hipEventCreate(&c->done[s]);
+  if (e == hipSuccess) {
+    void* hp = nullptr;
+    e = hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e == hipSuccess) {
+      c->host_flag = static_cast<unsigned*>(hp);
+      __atomic_store_n(c->host_flag, 0u, __ATOMIC_RELEASE);
+      e = hipHostGetDevicePointer(reinterpret_cast<void**>(&c->host_flag_dev), hp, 0);
+    }
+  }
   if (e != hipSuccess) {
     // release what was created; the context is not kept
+    if (c->host_flag != nullptr) (void)hipHostFree(c->host_flag);
     for (int s = 0; s < PR_NUM_SLOTS; ++s)
       if (c->done[s] != nullptr) (void)hipEventDestroy(c->done[s]);
     if (c->entry != nullptr) (void)hipEventDestroy(c->entry);
@@ -182,10 +200,41 @@ int get_ctx(DevCtx** out) {
   return PR_OK;
 }
 
+// A give-up of an earlier single launch on this device (host flag set by the kernel): reported
+// once, as this call's error, and cleared.  The check reads host memory only.
+int check_give_up(DevCtx* c) {
+  if (c->host_flag == nullptr || __atomic_load_n(c->host_flag, __ATOMIC_ACQUIRE) == 0)
+    return PR_OK;
+  __atomic_store_n(c->host_flag, 0u, __ATOMIC_RELEASE);
+  return fail(PR_ERR_HIP,
+              "an earlier single-launch call on device %d did not complete: a tile's bounded "
+              "wait for its row gave up, so that tile's output and residual rows were not "
+              "written (pr_device_status reads and clears the device status bits)",
+              c->device);
+}
+
+// Whether `s` is capturing into a HIP graph.  The null stream is never the capturing stream
+// itself, so it is not queried.
+int stream_capturing(hipStream_t s, bool* capturing) {
+  *capturing = false;
+  if (s == nullptr) return PR_OK;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  PR_HIP(hipStreamIsCapturing(s, &st));
+  *capturing = st != hipStreamCaptureStatusNone;
+  return PR_OK;
+}
+
 // Grow a device buffer.  Growing waits for all outstanding work on the device first, since
-// earlier calls may still be reading the old buffer.
-int grow(void** p, size_t* have, size_t need) {
+// earlier calls may still be reading the old buffer; under graph capture a buffer cannot grow
+// (the call is refused before anything is enqueued).
+int grow(DevCtx* c, void** p, size_t* have, size_t need) {
   if (need <= *have) return PR_OK;
+  if (c->capturing)
+    return fail(PR_ERR_UNSUPPORTED,
+                "a workspace must grow from %zu to %zu bytes, which is not possible while the "
+                "stream is capturing a graph: make one call of this shape (or a larger one) "
+                "before the capture",
+                *have, need);
   if (*p != nullptr) {
     PR_HIP(hipDeviceSynchronize());
     PR_HIP(hipFree(*p));
@@ -232,7 +281,7 @@ int check_common(const uint16_t* x, const uint16_t* W, float* r, const float* w,
 uint16_t* resolve_out(DevCtx* c, uint16_t* out, int T, int H, int* rc) {
   *rc = PR_OK;
   if (out != nullptr) return out;
-  *rc = grow(reinterpret_cast<void**>(&c->out_ws), &c->out_ws_bytes, (size_t)T * H * 2);
+  *rc = grow(c, reinterpret_cast<void**>(&c->out_ws), &c->out_ws_bytes, (size_t)T * H * 2);
   if (*rc != PR_OK) return nullptr;
   c->last_borrowed = c->out_ws;
   return c->out_ws;
@@ -250,7 +299,7 @@ int run_conventional(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, 
   g.kgroups = d.gemm_kgroups;
   const long long plane = (long long)T * H;
   if (g.split == 1) {
-    PR_TRY(grow(&c->conv, &c->conv_bytes, (size_t)plane * 2));
+    PR_TRY(grow(c, &c->conv, &c->conv_bytes, (size_t)plane * 2));
     PR_TRY(timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
       return gemm_rows(x, W, c->conv, true, T, H, K, g, plane, s, nullptr, t0, t1);
     }));
@@ -260,7 +309,7 @@ int run_conventional(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, 
     }));
   } else {
     // K split: fp32 partial planes, summed and rounded to bf16 before the add.
-    PR_TRY(grow(&c->conv, &c->conv_bytes, (size_t)plane * 4 * g.split));
+    PR_TRY(grow(c, &c->conv, &c->conv_bytes, (size_t)plane * 4 * g.split));
     PR_TRY(timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
       return gemm_rows(x, W, c->conv, false, T, H, K, g, plane, s, nullptr, t0, t1);
     }));
@@ -289,7 +338,7 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
   if (slot_elems > c->slot_elems) {
     size_t have = c->slot_elems * PR_NUM_SLOTS * sizeof(float);
     void* p = c->slots;
-    PR_TRY(grow(&p, &have, slot_elems * PR_NUM_SLOTS * sizeof(float)));
+    PR_TRY(grow(c, &p, &have, slot_elems * PR_NUM_SLOTS * sizeof(float)));
     c->slots = static_cast<float*>(p);
     c->slot_elems = slot_elems;
   }
@@ -405,12 +454,12 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
   // Steady-state calls allocate and fill nothing, so they can be captured in a graph.
   const bool grow_sync = sync_need > c->sync_bytes;
   if (slots_need > c->row_slots_bytes || flags_need > c->pair_flags_bytes || grow_sync) {
-    PR_TRY(grow(&c->row_slots, &c->row_slots_bytes, slots_need));
-    if (flags_need > 0) PR_TRY(grow(&c->pair_flags, &c->pair_flags_bytes, flags_need));
+    PR_TRY(grow(c, &c->row_slots, &c->row_slots_bytes, slots_need));
+    if (flags_need > 0) PR_TRY(grow(c, &c->pair_flags, &c->pair_flags_bytes, flags_need));
     if (grow_sync) {
       void* p = c->sync;
       size_t have = c->sync_bytes;
-      PR_TRY(grow(&p, &have, sync_need));
+      PR_TRY(grow(c, &p, &have, sync_need));
       c->sync = static_cast<unsigned*>(p);
       c->sync_bytes = have;
       PR_HIP(hipMemset(c->sync, 0, c->sync_bytes));
@@ -423,12 +472,14 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
     // Exchange regions: 128 KiB per workgroup of a round and round parity; a round holds at
     // most one workgroup per CU.
     const size_t xbuf_need = (size_t)2 * kNumCUs * 128 * 1024;
-    PR_TRY(grow(&c->xbuf, &c->xbuf_bytes, xbuf_need));
+    PR_TRY(grow(c, &c->xbuf, &c->xbuf_bytes, xbuf_need));
   }
   // Debug: PR_DEBUG_EPOCH=<n> stores n as the last launch's epoch before the call (tests of
   // the wrap at 2^32 - 1 launches).
   const char* dbg_epoch = std::getenv("PR_DEBUG_EPOCH");
   if (dbg_epoch != nullptr && dbg_epoch[0] != '\0') {
+    if (c->capturing)
+      return fail(PR_ERR_UNSUPPORTED, "PR_DEBUG_EPOCH is not supported under graph capture");
     const unsigned v = (unsigned)std::strtoul(dbg_epoch, nullptr, 10);
     PR_HIP(hipDeviceSynchronize());
     PR_HIP(hipMemcpy(c->sync + 2, &v, sizeof(v), hipMemcpyHostToDevice));
@@ -443,6 +494,7 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
   ws.xbuf_words = c->xbuf_bytes / sizeof(unsigned long long);
   ws.fault_mask = wait_fault_injected() ? 0x80000000u : 0u;
   ws.spin_limit = spin_limit();
+  ws.host_flag = c->host_flag_dev;
   const int gemma = norm_kind == PR_NORM_GEMMA;
   for (long long r0 = 0; r0 < T; r0 += rows_per) {
     const int rows = (int)std::min<long long>(rows_per, T - r0);
@@ -471,14 +523,29 @@ int run_call(const uint16_t* x, const uint16_t* W, float* r, const float* w, flo
                  d.n_chunks, d.gemm_bm, d.gemm_bn, d.split_k, d.reason);
   DevCtx* c = nullptr;
   PR_TRY(get_ctx(&c));
+  PR_TRY(check_give_up(c));
   if (T == 0) return PR_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool capturing = false;
+  PR_TRY(stream_capturing(s, &capturing));
+  if (capturing && d.path == PR_PATH_FUSED)
+    return fail(PR_ERR_UNSUPPORTED,
+                "the microchunk pipeline cannot be captured in a HIP graph (it records events "
+                "and waits across a library stream); under capture use the single launch or "
+                "the conventional path");
+  c->capturing = capturing;
   int rc = PR_OK;
   out = resolve_out(c, out, T, H, &rc);
-  if (rc != PR_OK) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d.path == PR_PATH_FUSED) return run_pipeline(c, x, W, r, w, eps, T, K, H, norm_kind, out, d, s);
-  if (d.path == PR_PATH_SINGLE) return run_single(c, x, W, r, w, eps, T, K, H, norm_kind, out, d, s);
-  return run_conventional(c, x, W, r, w, eps, T, K, H, norm_kind, out, d, s);
+  if (rc == PR_OK) {
+    if (d.path == PR_PATH_FUSED)
+      rc = run_pipeline(c, x, W, r, w, eps, T, K, H, norm_kind, out, d, s);
+    else if (d.path == PR_PATH_SINGLE)
+      rc = run_single(c, x, W, r, w, eps, T, K, H, norm_kind, out, d, s);
+    else
+      rc = run_conventional(c, x, W, r, w, eps, T, K, H, norm_kind, out, d, s);
+  }
+  c->capturing = false;
+  return rc;
 }
 
 }  // namespace
@@ -502,7 +569,7 @@ int pr_prepare_weight(const uint16_t* W_src, int src_layout, uint16_t* W_prep, i
     return fail(PR_ERR_INVALID_ARG, "weights must be 16-byte aligned");
   DevCtx* c = nullptr;
   PR_TRY(get_ctx(&c));
-  (void)c;
+  PR_TRY(check_give_up(c));
   return launch_prepare_weight(W_src, src_layout, W_prep, K, H, stream);
 }
 
@@ -520,7 +587,7 @@ int pr_silu_mul(const uint16_t* gate_up, uint16_t* x, int T, int K, void* stream
   if (x0 < g1 && g0 < x1) return fail(PR_ERR_INVALID_ARG, "x overlaps gate_up");
   DevCtx* c = nullptr;
   PR_TRY(get_ctx(&c));
-  (void)c;
+  PR_TRY(check_give_up(c));
   return launch_silu_mul(gate_up, x, T, K, stream);
 }
 
@@ -554,6 +621,7 @@ int pr_device_status(void* stream, unsigned* status) {
   DevCtx* c = nullptr;
   PR_TRY(get_ctx(&c));
   PR_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  if (c->host_flag != nullptr) __atomic_store_n(c->host_flag, 0u, __ATOMIC_RELEASE);
   if (c->sync == nullptr) return PR_OK;
   unsigned v = 0;
   PR_HIP(hipMemcpy(&v, c->sync, sizeof(v), hipMemcpyDeviceToHost));
@@ -562,6 +630,28 @@ int pr_device_status(void* stream, unsigned* status) {
     PR_HIP(hipDeviceSynchronize());
   }
   *status = v;
+  return PR_OK;
+}
+
+int pr_release_workspace(void) {
+  clear_error();
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  // Outstanding work may still read the buffers.
+  PR_HIP(hipDeviceSynchronize());
+  void** bufs[] = {reinterpret_cast<void**>(&c->slots), &c->conv,
+                   reinterpret_cast<void**>(&c->out_ws), &c->row_slots,
+                   reinterpret_cast<void**>(&c->sync), &c->pair_flags, &c->xbuf};
+  for (void** b : bufs) {
+    if (*b != nullptr) PR_HIP(hipFree(*b));
+    *b = nullptr;
+  }
+  c->slot_elems = 0;
+  c->conv_bytes = c->out_ws_bytes = c->row_slots_bytes = c->sync_bytes = 0;
+  c->pair_flags_bytes = c->xbuf_bytes = 0;
+  c->last_borrowed = nullptr;
+  c->prev_caller = nullptr;
+  c->prev_done_slots[0] = c->prev_done_slots[1] = -1;
   return PR_OK;
 }
 

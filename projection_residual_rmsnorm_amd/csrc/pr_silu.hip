@@ -25,9 +25,9 @@ __device__ __forceinline__ float bf16_f32(uint32_t b) { return __uint_as_float(b
 // 16-byte vectors of 8 columns, U vectors per step with all their loads issued before any use,
 // so no index needs a division.  gate and up are read once, with streaming loads, so that
 // they do not evict the projection's weight from the Infinity Cache (x, which the projection
-// reads next, is stored normally).  The exponential and the quotient use the device's native
-// instructions (relative error near 1e-6, far below the half ulp of the bf16 result).  Zero
-// columns of the load-time padding give zeros.
+// reads next, is stored normally).  The exponential is the device's native one (__expf, a
+// scaled v_exp_f32: relative error near 1e-6, far below the half ulp of the bf16 result) and
+// the quotient an ordinary IEEE division.  Zero columns of the load-time padding give zeros.
 // --------------------------------------------------------------------------------------------
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 constexpr int kSiluThreads = 256;  // threads per workgroup; the column loop strides by it
@@ -64,8 +64,8 @@ __global__ void __launch_bounds__(kSiluThreads) silu_mul_kernel(const uint16_t* 
           for (int j = 0; j < 4; ++j) {
             const float g0 = bf16_f32(gw[j] & 0xffffu), g1 = bf16_f32(gw[j] >> 16);
             const float u0 = bf16_f32(uw[j] & 0xffffu), u1 = bf16_f32(uw[j] >> 16);
-            const float x0 = __fdividef(g0, 1.0f + __expf(-g0)) * u0;
-            const float x1 = __fdividef(g1, 1.0f + __expf(-g1)) * u1;
+            const float x0 = g0 / (1.0f + __expf(-g0)) * u0;
+            const float x1 = g1 / (1.0f + __expf(-g1)) * u1;
             o[j] = bf16_rne(x0) | (bf16_rne(x1) << 16);
           }
           xrow[c] = make_uint4(o[0], o[1], o[2], o[3]);

@@ -191,39 +191,35 @@ SHADER_ENGINES = 32  # 4 per XCD
 def derived(mean: Dict[str, float]) -> Dict[str, float]:
     """Ratios the counters support.
 
-    SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs (one 32x32x16 bf16 MFMA keeps a SIMD
-    busy 32 cycles, so the sum equals flops / 1024).  GRBM_GUI_ACTIVE is summed over the 8
-    XCDs (it reads about 8 x the shader clock x the dispatch time) and spans the counter
-    window, which is a few microseconds longer than the dispatch.
-      mfma_util_nameplate: busy cycles / (SIMDs x duration x 2.4 GHz), the fraction of the
-        dense bf16 peak;
-      mfma_util_active: busy cycles / (SIMDs x GRBM_GUI_ACTIVE / 8), against the cycles the
-        GPU clock actually ran;
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs; one 32x32x16 bf16 MFMA keeps a SIMD
+    busy 32 cycles, so for a bf16 kernel the sum is the instruction count x 32, i.e. flops /
+    1024: it restates the flop count and is not reported as a separate utilisation.
+    GRBM_GUI_ACTIVE spans the counter window, which is longer than the dispatch (several times
+    longer for a kernel of a few microseconds), so it gives no clock and is not used.
+      shader_clock_GHz_busy: SQ_BUSY_CYCLES (shader-clock cycles with waves present, summed
+        over the 32 shader engines) / (32 x duration).  An engine without waves for part of
+        the dispatch (the last workgroups' tail) lowers it, so it is a lower bound of the clock;
+      shader_clock_GHz_cycles: SQ_CYCLES / (32 x duration), over the counter window, which is
+        longer than the dispatch: an upper bound;
+      mfma_util_at_busy_clock: MFMA busy cycles / (SIMDs x duration x the lower-bound clock),
+        so an upper bound of the matrix cores' busy fraction at the clock the kernel ran at;
       lds_bank_conflict_frac: conflict cycles / LDS-active cycles;
-      lds_active_frac: LDS-active cycles per CU / (GRBM_GUI_ACTIVE / 8);
-      shader_clock_GHz: SQ_BUSY_CYCLES (shader-clock cycles with waves present, summed over the
-        32 shader engines) / (32 x duration), the clock the kernel actually ran at;
-      mfma_util_at_shader_clock: MFMA busy cycles / (SIMDs x duration x that clock);
       l1_l2_read_MB_at_64B: L1 -> L2 read requests x 64 bytes;
       l1_l2_read_latency_cycles: summed request latency / requests;
       l1_pending_stall_cycles_per_cu: cycles an L1 waited on data pending from L2, per CU."""
     out = {}
     simds = CU_COUNT * SIMDS_PER_CU
-    busy, active = mean.get("SQ_VALU_MFMA_BUSY_CYCLES"), mean.get("GRBM_GUI_ACTIVE")
+    busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES")
     dur = mean.get("duration_ns")
     if dur:
         out["duration_us"] = dur / 1e3
-    if active and dur:
-        out["gui_active_per_xcd_GHz"] = active / XCDS / dur
-    if busy is not None and dur:
-        out["mfma_util_nameplate"] = busy / (simds * dur * NAMEPLATE_GHZ)
-    if busy is not None and active:
-        out["mfma_util_active"] = busy / (simds * active / XCDS)
     if mean.get("SQ_BUSY_CYCLES") and dur:
         clk = mean["SQ_BUSY_CYCLES"] / SHADER_ENGINES / dur
-        out["shader_clock_GHz"] = clk
+        out["shader_clock_GHz_busy"] = clk
         if busy is not None:
-            out["mfma_util_at_shader_clock"] = busy / (simds * dur * clk)
+            out["mfma_util_at_busy_clock"] = busy / (simds * dur * clk)
+    if mean.get("SQ_CYCLES") and dur:
+        out["shader_clock_GHz_cycles"] = mean["SQ_CYCLES"] / SHADER_ENGINES / dur
     req = mean.get("TCP_TCC_READ_REQ_sum")
     if req:
         out["l1_l2_read_MB_at_64B"] = req * 64 / 1e6
@@ -237,8 +233,6 @@ def derived(mean: Dict[str, float]) -> Dict[str, float]:
             out["mfma_bf16_TFLOPs"] = out["mfma_bf16_flops"] / dur / 1e3
     if "SQ_LDS_BANK_CONFLICT" in mean and mean.get("SQ_LDS_IDX_ACTIVE"):
         out["lds_bank_conflict_frac"] = mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_LDS_IDX_ACTIVE"]
-        if active:
-            out["lds_active_frac"] = mean["SQ_LDS_IDX_ACTIVE"] / CU_COUNT / (active / XCDS)
     return out
 
 

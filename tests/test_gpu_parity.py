@@ -8,6 +8,7 @@ checked on sampled rows (rows are independent, so a row subset is an exact check
 rows), always including the last chunk's rows.
 """
 import os
+import zlib
 
 import numpy as np
 import pytest
@@ -192,16 +193,20 @@ def test_single_launch_several_rounds(monkeypatch, tile, waves, kgroups, split, 
     _check(d, r_dev, out_bits, "fused", rows)
 
 
-def test_single_launch_largest_workload():
-    """The largest configuration (K=H=8192, T=32768): 128 tile rows in 16 rounds of whole tile
-    rows per XCD; sampled rows against the oracle, conventional path beside it."""
+def test_largest_workload_every_path():
+    """The largest configuration (K=H=8192, T=32768) on every path: the single launch (128 tile
+    rows in rounds of whole tile rows per XCD pair), the microchunk pipeline at each chunk size
+    of the threshold sweep (512, 1024, 2048: 64, 32 and 16 chunks over two streams and three
+    slots) and the conventional path; sampled rows (each chunk size's last-chunk rows among
+    them) against the oracle."""
     wl = synth.WORKLOADS["sweep_T32768"]
-    print(f"single launch T={wl.T} K={wl.K} H={wl.H}", flush=True)
+    print(f"largest workload T={wl.T} K={wl.K} H={wl.H}", flush=True)
     d = synth.make_inputs(wl, seed=0)
     dev = Device(d)
-    rows = _sample_rows(wl.T, 256, n=64, seed=5)
-    for mc in ("single", None):
+    for mc in ("single",) + wl.microchunks + (None,):
+        rows = _sample_rows(wl.T, mc if isinstance(mc, int) else 256, n=64, seed=5)
         dev.reset()
+        print("path", mc, flush=True)
         r_dev, out_bits = dev.run(mc)
         err = _check(d, r_dev, out_bits, "conventional" if mc is None else "fused", rows)
         print(mc, err, flush=True)
@@ -254,23 +259,57 @@ def test_single_launch_agrees_with_pipeline():
     assert np.max(diff) <= 2 ** -7 * np.max(np.abs(b.view(np.float32)))
 
 
-@pytest.mark.parametrize("split", [1, 2])
-def test_single_launch_wait_limit_reports(monkeypatch, split):
+@pytest.mark.parametrize("tile,waves,split", [("256x128", 4, 1), ("256x256", 8, 1),
+                                              ("256x256", 8, 2)])
+def test_single_launch_wait_limit_reports(monkeypatch, tile, waves, split):
     """Row reads that look for an epoch no slot carries (set from the host) give up after 64
-    polls each; the kernel ends, the status bit reports it and reading clears it.  A later
-    call without the fault is correct.  Split 2: the pair form's partner wait gives up first,
-    and neither half writes anything."""
-    if split == 2:
-        _force_single(monkeypatch, "256x256", 8, 1, 2)
+    polls each; every kernel still ends.  The call leaves no state behind: no output row is
+    written and the residual keeps its value before the call (every tile stores it only after
+    its wait; the 256x128 tile with 4 waves is the one that prefetches the residual).  The next
+    call on the device, of any entry point, returns PR_ERR_HIP without the caller polling
+    anything and enqueues nothing; the status bit still reads set, and reading clears it.  A
+    later call without the fault is correct.  Split 2: the pair form's partner wait gives up
+    first, and neither half writes anything."""
+    _force_single(monkeypatch, tile, waves, 1, split)
     monkeypatch.setenv("PR_FAULT_INJECT", "wait")
     monkeypatch.setenv("PR_SPIN_LIMIT", "64")
     d = synth.make_custom(600, 256, 1024, seed=4)
     dev = Device(d)
+    print(f"forced give-up: tile {tile}, {waves} waves, split {split}", flush=True)
+    pr.proj_add_rmsnorm_single_launch(dev.x, dev.Wp, dev.r, dev.w, d["eps"], dev.T, dev.K, dev.H,
+                                      d["norm_kind"], dev.out)
+    torch.cuda.synchronize()
+    assert np.all(bits(dev.out) == 0x7BAD)  # no tile wrote output
+    np.testing.assert_array_equal(dev.r.cpu().numpy(), d["residual"])  # nor the residual
+    monkeypatch.delenv("PR_FAULT_INJECT")
+    monkeypatch.delenv("PR_SPIN_LIMIT")
+    for k in ("PR_FORCE_TILE", "PR_FORCE_WAVES", "PR_FORCE_KGROUPS", "PR_FORCE_SPLIT"):
+        monkeypatch.delenv(k, raising=False)
+    with pytest.raises(pr.PRError) as e:
+        dev.run(None)  # the next call on the device: the conventional entry point
+    assert e.value.code == pr.PR_ERR_HIP and "gave up" in str(e.value), str(e.value)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dev.r.cpu().numpy(), d["residual"])  # it enqueued nothing
+    assert pr.pr_device_status(torch.cuda.current_stream()) & 1
+    assert pr.pr_device_status(torch.cuda.current_stream()) == 0
+    dev.reset()
+    r_dev, out_bits = dev.run(None)  # reported once: calls work again
+    _check(d, r_dev, out_bits, "conventional")
+    _force_single(monkeypatch, tile, waves, 1, split)
+    dev.reset()
+    r_dev, out_bits = dev.run("single")
+    _check(d, r_dev, out_bits, "fused")
+
+
+def test_give_up_status_read_clears_host_flag(monkeypatch):
+    """pr_device_status consumes the report: after it, the next call is not failed."""
+    monkeypatch.setenv("PR_FAULT_INJECT", "wait")
+    monkeypatch.setenv("PR_SPIN_LIMIT", "64")
+    d = synth.make_custom(300, 256, 512, seed=6)
+    dev = Device(d)
     pr.proj_add_rmsnorm_single_launch(dev.x, dev.Wp, dev.r, dev.w, d["eps"], dev.T, dev.K, dev.H,
                                       d["norm_kind"], dev.out)
     assert pr.pr_device_status(torch.cuda.current_stream()) & 1
-    assert pr.pr_device_status(torch.cuda.current_stream()) == 0
-    assert np.all(bits(dev.out) == 0x7BAD)  # no tile wrote output
     monkeypatch.delenv("PR_FAULT_INJECT")
     monkeypatch.delenv("PR_SPIN_LIMIT")
     dev.reset()
@@ -391,6 +430,83 @@ def test_microchunked_equals_unchunked_bitwise(monkeypatch, tile, split, T, K, H
         r2, o2 = dev.run(mc)
         np.testing.assert_array_equal(r1, r2)
         np.testing.assert_array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("mc", [128, 200, 256, "single", None])
+def test_caller_stream_join_before_any_sync(monkeypatch, mc):
+    """The join (the caller's stream waits for the library stream's last chunk) checked on the
+    GPU: on a side stream, the call is followed at once by torch copies of the residual and the
+    output on that same stream, with no synchronisation in between, and every library launch
+    is delayed (PR_DEBUG_DELAY) so that the library stream runs late.  The copies must hold the
+    finished result.  T = 1000: mc = 128 and 256 end on a library-stream chunk, mc = 200 on a
+    caller-stream chunk after a library-stream one; the single launch and the conventional
+    path run on the caller's stream."""
+    d = synth.make_custom(1000, 512, 1024, seed=23)
+    dev = Device(d)
+    monkeypatch.setenv("PR_DEBUG_DELAY", "150")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        if mc is None:
+            pr.proj_add_rmsnorm_unfused(dev.x, dev.Wp, dev.r, dev.w, d["eps"], dev.T, dev.K,
+                                        dev.H, d["norm_kind"], dev.out, s)
+        elif mc == "single":
+            pr.proj_add_rmsnorm_single_launch(dev.x, dev.Wp, dev.r, dev.w, d["eps"], dev.T, dev.K,
+                                              dev.H, d["norm_kind"], dev.out, s)
+        else:
+            pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, d["eps"], dev.T, dev.K, dev.H, mc,
+                                d["norm_kind"], dev.out, s)
+        r_copy = dev.r.clone()
+        o_copy = dev.out.clone()
+    torch.cuda.synchronize()
+    _check(d, r_copy[:dev.T].cpu().numpy(), bits(o_copy[:dev.T]),
+           "conventional" if mc is None else "fused")
+
+
+def test_pipeline_refuses_graph_capture():
+    """Capture of the microchunk pipeline is refused before anything is enqueued (it records
+    events and waits across a library stream); the conventional path is captured once its
+    workspace exists, and a call whose workspace would have to grow under capture is refused.
+    Every refusal leaves the capture valid: the graph replays the calls that were accepted."""
+    d = synth.make_custom(300, 512, 512, seed=3)
+    dev = Device(d)
+    pr.pr_release_workspace()  # earlier calls may have grown it past the larger call below
+    r_eager, o_eager = dev.run(None)  # sizes the conventional workspace
+    big = synth.make_custom(600, 512, 512, seed=4)
+    dbig = Device(big)
+    r0 = torch.from_numpy(d["residual"]).to(DEV)
+    T = dev.T
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    dev.r.copy_(r0)
+    torch.cuda.synchronize()
+    codes = []
+    with torch.cuda.graph(graph, stream=side):
+        for call in (lambda: pr.proj_add_rmsnorm(dev.x, dev.Wp, dev.r, dev.w, d["eps"], T,
+                                                 dev.K, dev.H, 64, d["norm_kind"], dev.out),
+                     lambda: pr.proj_add_rmsnorm_unfused(dbig.x, dbig.Wp, dbig.r, dbig.w,
+                                                         big["eps"], dbig.T, dbig.K, dbig.H,
+                                                         big["norm_kind"], dbig.out)):
+            try:
+                call()
+                codes.append(0)
+            except pr.PRError as e:
+                codes.append(e.code)
+        pr.proj_add_rmsnorm_unfused(dev.x, dev.Wp, dev.r, dev.w, d["eps"], T, dev.K, dev.H,
+                                    d["norm_kind"], dev.out)
+    assert codes == [pr.PR_ERR_UNSUPPORTED, pr.PR_ERR_UNSUPPORTED], codes
+    for rep in range(3):
+        dev.r.copy_(r0)
+        dev.out.fill_(0x7BAD)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print("replay", rep, flush=True)
+        np.testing.assert_array_equal(dev.r[:T].cpu().numpy(), r_eager)
+        np.testing.assert_array_equal(bits(dev.out[:T]), o_eager)
+    dev.reset()
+    r_dev, out_bits = dev.run(64)  # the pipeline still works outside a capture
+    _check(d, r_dev, out_bits, "fused")
 
 
 def test_deterministic_and_stream_ordered():
@@ -549,16 +665,22 @@ def _sample_rows(T, mc, n=48, seed=0):
 
 
 @pytest.mark.parametrize("name", ["tiny", "o_proj", "down_proj", "gemma", "sweep_T128",
-                                  "sweep_T2048"])
+                                  "sweep_T512", "sweep_T2048", "sweep_T8192"])
 def test_workload_parity_full_size(name):
+    """Every workload at its full size on every path: the conventional path, the pipeline at
+    each of the workload's chunk sizes (for the threshold sweep, 512, 1024 and 2048 where they
+    do not exceed T) and the single launch, on sampled rows (a fixed per-workload seed, so a
+    failure replays) that always include each chunk size's last-chunk rows."""
     wl = synth.WORKLOADS[name]
     print(f"workload {name}: T={wl.T} K={wl.K} H={wl.H}", flush=True)
     d = synth.make_inputs(wl, seed=0)
     dev = Device(d)
+    seed = zlib.crc32(name.encode()) % 1000
     for mc in (None,) + wl.microchunks + ("single",):
         dev.reset()
+        print("path", mc, flush=True)
         r_dev, out_bits = dev.run(mc)
-        rows = _sample_rows(wl.T, mc if isinstance(mc, int) else wl.T, seed=hash(name) % 1000)
+        rows = _sample_rows(wl.T, mc if isinstance(mc, int) else wl.T, seed=seed)
         err = _check(d, r_dev, out_bits, "conventional" if mc is None else "fused", rows)
         print(name, mc, err, flush=True)
         assert np.all(np.isfinite(r_dev))
@@ -636,6 +758,34 @@ def test_silu_mul_matches_oracle(T, K, K_real):
     xb = bits(x)
     _silu_mul_check(d["gate_up"], xb[:T], K, K_real)
     assert np.all(xb[T] == 0x7BAD)
+
+
+def test_silu_mul_large_and_special_gates():
+    """Gates far out in both tails and at infinity: silu(g) tends to g for large g and to 0
+    for large -g.  The device's native exponential overflows to infinity for -g above about
+    88.7, where the quotient becomes a signed zero; the float64 oracle's value there is below
+    half the smallest bf16 subnormal, so both round to zero.  An infinite gate gives a NaN
+    where the oracle gives one (-inf / inf, or inf * 0), and +-inf otherwise."""
+    gates = [0.0, -0.0, 1.0, -1.0, 20.0, -20.0, 60.0, -60.0, 88.0, -88.0, 100.0, -100.0,
+             np.inf, -np.inf]
+    K = 64
+    rng = np.random.default_rng(77)
+    T = len(gates) * 3
+    g = np.repeat(np.array(gates, dtype=np.float32), 3)[:, None] * np.ones((1, K), np.float32)
+    u = rng.standard_normal((T, K), dtype=np.float32)
+    u[::7, ::5] = 0.0
+    gu = np.concatenate([synth.f32_to_bf16_bits(g), synth.f32_to_bf16_bits(u)], axis=1)
+    x = torch.empty((T, K), dtype=torch.int16, device=DEV)
+    pr.pr_silu_mul(i16(gu), x, T, K)
+    torch.cuda.synchronize()
+    got = bits(x)
+    want = oracle.silu_mul(gu, K)
+    is_nan = lambda b: ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
+    assert np.array_equal(is_nan(got), is_nan(want))
+    keep = ~is_nan(want)
+    d_ulp = np.abs(_bf16_ordered(got[keep]) - _bf16_ordered(want[keep]))
+    assert d_ulp.max() <= 1, d_ulp.max()
+    assert np.all(np.isinf(oracle.widen_bf16(got[keep])) == np.isinf(oracle.widen_bf16(want[keep])))
 
 
 @pytest.mark.parametrize("path", ["single", 128, None])

@@ -443,17 +443,19 @@ def test_counter_summary_derivations(tmp_path):
     assert t["dispatches"] == 2
     dv = derived(t["mean"])
     assert abs(dv["duration_us"] - 100.0) < 1e-9
-    assert abs(dv["mfma_util_nameplate"] - 0.5) < 1e-9
-    assert abs(dv["mfma_util_active"] - 0.6) < 1e-9      # the clock ran at 2.0 of 2.4 GHz
-    assert abs(dv["gui_active_per_xcd_GHz"] - 2.0) < 1e-9
+    # GRBM_GUI_ACTIVE spans the counter window, not the dispatch: no clock is derived from it,
+    # and the MFMA busy sum (flops / 1024 for bf16) is not restated as a utilisation
+    assert not any("gui" in k or "nameplate" in k for k in dv), dv
     assert dv["mfma_bf16_flops"] == 512e6
     assert abs(dv["lds_bank_conflict_frac"] - 0.25) < 1e-12
-    assert abs(dv["lds_active_frac"] - 1000.0 / 200e3) < 1e-12
     assert counter_table(str(path), ["gemm_add_rmsnorm_kernel"], grid=256) == {}
-    # shader clock from SQ_BUSY_CYCLES over the 32 shader engines: 1.5 GHz for 100 us
-    dv = derived({**t["mean"], "SQ_BUSY_CYCLES": 32 * 100e3 * 1.5})
-    assert abs(dv["shader_clock_GHz"] - 1.5) < 1e-9
-    assert abs(dv["mfma_util_at_shader_clock"] - 0.8) < 1e-9  # 0.5 of 2.4 GHz = 0.8 of 1.5
+    # shader clock bounds over the 32 shader engines: SQ_BUSY_CYCLES (cycles with waves
+    # present) 1.5 GHz for 100 us, SQ_CYCLES (the counter window) 2.0 GHz
+    dv = derived({**t["mean"], "SQ_BUSY_CYCLES": 32 * 100e3 * 1.5,
+                  "SQ_CYCLES": 32 * 100e3 * 2.0})
+    assert abs(dv["shader_clock_GHz_busy"] - 1.5) < 1e-9
+    assert abs(dv["shader_clock_GHz_cycles"] - 2.0) < 1e-9
+    assert abs(dv["mfma_util_at_busy_clock"] - 0.8) < 1e-9  # 0.5 of 2.4 GHz = 0.8 of 1.5
     # L1 -> L2 reads: 64-byte requests, mean latency, pending-stall cycles per CU
     dv = derived({**t["mean"], "TCP_TCC_READ_REQ_sum": 1e6, "TCP_TCC_READ_REQ_LATENCY_sum": 5e8,
                   "TCP_PENDING_STALL_CYCLES_sum": 256 * 7e4})
