@@ -200,6 +200,43 @@ int proj_add_rmsnorm_single_launch(const uint16_t* x, const uint16_t* W, float* 
                                    int norm_kind, uint16_t* out, void* stream);
 
 /*
+ * Library set-up on the current device: creates the device's library stream, events and the
+ * host-mapped status flag, and looks up and clears the fixed workspace of
+ * proj_add_rmsnorm_single_launch_noalloc (synchronises the device).  Every other entry point
+ * sets itself up on first use; the no-allocation entry point requires this call once per
+ * device beforehand.  Calling it again is a no-op.  Errors: PR_ERR_UNSUPPORTED (not a gfx950
+ * device), PR_ERR_HIP.
+ */
+int pr_init(void);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): proj_add_rmsnorm_single_launch with its workspace
+ * in a fixed device array of the library instead of a grown one.  The call allocates nothing
+ * and fills nothing; it only enqueues the single-launch kernels on `stream`.
+ *
+ * Same arguments, semantics and result as proj_add_rmsnorm_single_launch (the same kernels and
+ * configuration; the result is bitwise equal), except:
+ *  - pr_init() must have been called on the current device (else PR_ERR_UNSUPPORTED);
+ *  - out must not be NULL (a borrowed output would be allocated): PR_ERR_INVALID_ARG;
+ *  - the fixed array holds 2^20 64-bit row slots (8 MiB) and 4096 32-bit words per device:
+ *    a launch needs min(T, rows per launch) * H / (tile columns) slots and 3 + tile rows words,
+ *    so with 128-column tiles T * H <= 2^27 (T = 32768 at H = 4096) and with 256-column tiles
+ *    T * H <= 2^28 (T = 32768 at H = 8192); a larger call returns PR_ERR_SHAPE before
+ *    enqueuing anything.  The K-split pair form (a debug override) is not available:
+ *    PR_ERR_UNSUPPORTED.
+ *  - every call on a device shares that device's array, which keeps the last call's contents
+ *    (epoch-tagged slots; each launch returns its completion counters to zero), so calls that
+ *    overlap on one device race: enqueue them on one stream or order them.
+ * No timing events are recorded for it (pr_profile_enable does not see it).  A wait that gives
+ * up is reported as for the single launch (pr_device_status covers the fixed array too).
+ */
+int proj_add_rmsnorm_single_launch_noalloc(const uint16_t* x, const uint16_t* W,
+                                           float* residual_inout, const float* norm_w, float eps,
+                                           int T, int K, int H, int norm_kind, uint16_t* out,
+                                           void* stream);
+
+/*
  * Status bits that single-launch calls on the current device collected since the last read:
  * bit 0 = a tile's wait for its row gave up (its output and residual rows are not written).
  * Waits for the calls enqueued on `stream` to finish, stores the bits in *status (0 when

@@ -74,6 +74,9 @@ SIGNATURES = {
     "proj_add_rmsnorm": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _i, _vp, _vp]),
     "proj_add_rmsnorm_unfused": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp, _vp]),
     "proj_add_rmsnorm_single_launch": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp, _vp]),
+    "proj_add_rmsnorm_single_launch_noalloc": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp,
+                                                   _vp]),
+    "pr_init": (_i, []),
     "pr_device_status": (_i, [_vp, _c.POINTER(_c.c_uint)]),
     "pr_workspace_output": (_vp, []),
     "pr_release_workspace": (_i, []),
@@ -205,6 +208,20 @@ def proj_add_rmsnorm_single_launch(x, W, residual_inout, norm_w, eps: float, T: 
     px, pw, pr_, pn, po = _call_ptrs(x, W, residual_inout, norm_w, out, T, K, H)
     _check(_lib().proj_add_rmsnorm_single_launch(px, pw, pr_, pn, eps, T, K, H, norm_kind, po,
                                                  _stream(stream, x, residual_inout)))
+
+
+def pr_init() -> None:
+    """Sets the library up on the current device (needed before the no-allocation call)."""
+    _check(_lib().pr_init())
+
+
+def proj_add_rmsnorm_single_launch_noalloc(x, W, residual_inout, norm_w, eps: float, T: int,
+                                           K: int, H: int, norm_kind: int = PR_NORM_STANDARD,
+                                           out=None, stream=None) -> None:
+    px, pw, pr_, pn, po = _call_ptrs(x, W, residual_inout, norm_w, out, T, K, H)
+    _check(_lib().proj_add_rmsnorm_single_launch_noalloc(px, pw, pr_, pn, eps, T, K, H,
+                                                         norm_kind, po,
+                                                         _stream(stream, x, residual_inout)))
 
 
 def pr_device_status(stream=None) -> int:

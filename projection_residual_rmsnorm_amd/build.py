@@ -18,7 +18,8 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libprojaddnorm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["pr_kernels.hip", "pr_silu.hip", "pr_host.cpp", "pr_runtime.cpp", "pr_tune.cpp"]
+SOURCES = ["pr_kernels.hip", "pr_silu.hip", "pr_noalloc.hip", "pr_host.cpp", "pr_runtime.cpp",
+           "pr_tune.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -116,6 +116,17 @@ int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, con
 int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,
                           void* stream);
 
+// Fixed single-launch workspace of the entry point that allocates nothing (pr_noalloc.hip):
+// kNoallocSlotWords 64-bit row-partial slots (8 MiB) and kNoallocSyncWords 32-bit words.
+constexpr unsigned long long kNoallocSlotWords = 1ull << 20;
+constexpr unsigned long long kNoallocSyncWords = 4096;
+// Once per device, with the device current: looks up the array's device address and clears it
+// (synchronises the device).
+int noalloc_setup();
+// The current device's fixed workspace as slots and sync words of `ws` (the other fields are
+// left to the caller); PR_ERR_UNSUPPORTED when noalloc_setup has not run on the device.
+int noalloc_workspace(SingleWs* ws);
+
 // x[T][K] = bf16(silu(gate) * up) from the merged gate_up[T][2K] (gate first); K % 8 == 0,
 // both 16-byte aligned.
 int launch_silu_mul(const uint16_t* gate_up, uint16_t* x, int T, int K, void* stream);

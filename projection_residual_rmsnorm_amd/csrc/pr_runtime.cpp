@@ -200,6 +200,17 @@ int get_ctx(DevCtx** out) {
   return PR_OK;
 }
 
+// The current device's context if one exists (never creates one).
+int find_ctx(DevCtx** out) {
+  int dev = -1;
+  PR_HIP(hipGetDevice(&dev));
+  *out = nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return fail(PR_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lk(g_ctx_mu);
+  *out = g_ctx[dev];
+  return PR_OK;
+}
+
 // A give-up of an earlier single launch on this device (host flag set by the kernel): reported
 // once, as this call's error, and cleared.  The check reads host memory only.
 int check_give_up(DevCtx* c) {
@@ -425,9 +436,31 @@ unsigned spin_limit() {
   return 1u << 21;
 }
 
-int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const float* w,
-               float eps, int T, int K, int H, int norm_kind, uint16_t* out,
-               const pr_decision& d, hipStream_t s) {
+// The single-launch kernels over all T rows with workspace `ws` (slots and sync words set by
+// the caller): one launch per block of rows whose x slice stays below 2^30 elements (32-bit
+// offsets in the kernel); the launches are independent (rows do not interact) and run in
+// order on `s`.  `timing`: record the library's timing events when profiling is on.
+int launch_single_rows(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const float* w,
+                       float eps, int T, int K, int H, int norm_kind, uint16_t* out,
+                       const GemmCfg& g, SingleWs ws, hipStream_t s, bool timing) {
+  const long long rows_per = ((1LL << 30) / K) / g.bm * g.bm;
+  if (rows_per <= 0) return fail(PR_ERR_SHAPE, "K=%d too large", K);
+  ws.fault_mask = wait_fault_injected() ? 0x80000000u : 0u;
+  ws.spin_limit = spin_limit();
+  ws.host_flag = c->host_flag_dev;
+  const int gemma = norm_kind == PR_NORM_GEMMA;
+  for (long long r0 = 0; r0 < T; r0 += rows_per) {
+    const int rows = (int)std::min<long long>(rows_per, T - r0);
+    auto launch = [&](hipEvent_t t0, hipEvent_t t1) {
+      return launch_gemm_add_rmsnorm(x + r0 * K, W, r + r0 * H, w, out + r0 * H, ws, rows, H, K,
+                                     g, eps, gemma, s, t0, t1);
+    };
+    PR_TRY(timing ? timed(c, 0, launch) : launch(nullptr, nullptr));
+  }
+  return PR_OK;
+}
+
+GemmCfg cfg_of(const pr_decision& d) {
   GemmCfg g;
   g.bm = d.gemm_bm;
   g.bn = d.gemm_bn;
@@ -435,6 +468,13 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
   g.waves = d.gemm_waves;
   g.stages = d.gemm_stages;
   g.kgroups = d.gemm_kgroups;
+  return g;
+}
+
+int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const float* w,
+               float eps, int T, int K, int H, int norm_kind, uint16_t* out,
+               const pr_decision& d, hipStream_t s) {
+  const GemmCfg g = cfg_of(d);
   if (fault_injected()) return fail(PR_ERR_HIP, "injected launch failure (PR_FAULT_INJECT)");
   // Launches cover at most 2^30 elements of x each (32-bit offsets in the kernel), in whole
   // tile rows; each launch is independent (rows do not interact).
@@ -492,18 +532,7 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
   ws.pword_words = c->pair_flags_bytes / sizeof(unsigned long long);
   ws.xbuf = static_cast<unsigned long long*>(c->xbuf);
   ws.xbuf_words = c->xbuf_bytes / sizeof(unsigned long long);
-  ws.fault_mask = wait_fault_injected() ? 0x80000000u : 0u;
-  ws.spin_limit = spin_limit();
-  ws.host_flag = c->host_flag_dev;
-  const int gemma = norm_kind == PR_NORM_GEMMA;
-  for (long long r0 = 0; r0 < T; r0 += rows_per) {
-    const int rows = (int)std::min<long long>(rows_per, T - r0);
-    PR_TRY(timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
-      return launch_gemm_add_rmsnorm(x + r0 * K, W, r + r0 * H, w, out + r0 * H, ws, rows, H, K,
-                                     g, eps, gemma, s, t0, t1);
-    }));
-  }
-  return PR_OK;
+  return launch_single_rows(c, x, W, r, w, eps, T, K, H, norm_kind, out, g, ws, s, true);
 }
 
 int run_call(const uint16_t* x, const uint16_t* W, float* r, const float* w, float eps, int T,
@@ -614,6 +643,53 @@ int proj_add_rmsnorm_single_launch(const uint16_t* x, const uint16_t* W, float* 
                   stream);
 }
 
+int pr_init(void) {
+  clear_error();
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  return noalloc_setup();
+}
+
+int proj_add_rmsnorm_single_launch_noalloc(const uint16_t* x, const uint16_t* W,
+                                           float* residual_inout, const float* norm_w, float eps,
+                                           int T, int K, int H, int norm_kind, uint16_t* out,
+                                           void* stream) {
+  clear_error();
+  PR_TRY(check_common(x, W, residual_inout, norm_w, eps, T, K, H, 0, norm_kind, out));
+  if (T > 0 && out == nullptr)
+    return fail(PR_ERR_INVALID_ARG, "out must be given: a borrowed output would be allocated");
+  pr_decision d;
+  PR_TRY(decide(T, K, H, PR_SINGLE_LAUNCH, &d));
+  DevCtx* c = nullptr;
+  PR_TRY(find_ctx(&c));
+  if (c == nullptr)
+    return fail(PR_ERR_UNSUPPORTED, "pr_init() has not been called on the current device");
+  PR_TRY(check_give_up(c));
+  if (T == 0) return PR_OK;
+  if (fault_injected()) return fail(PR_ERR_HIP, "injected launch failure (PR_FAULT_INJECT)");
+  const GemmCfg g = cfg_of(d);
+  if (g.split != 1)
+    return fail(PR_ERR_UNSUPPORTED, "the K-split pair form needs exchange regions beyond the "
+                "fixed workspace");
+  const char* dbg_epoch = std::getenv("PR_DEBUG_EPOCH");
+  if (dbg_epoch != nullptr && dbg_epoch[0] != '\0')
+    return fail(PR_ERR_UNSUPPORTED, "PR_DEBUG_EPOCH is not supported without allocation");
+  SingleWs ws;
+  PR_TRY(noalloc_workspace(&ws));
+  // One launch covers at most rows_per rows; its slots and counters must fit the fixed array.
+  const long long rows_per = std::max<long long>(((1LL << 30) / K) / g.bm * g.bm, 1);
+  const long long rows_max = std::min<long long>(rows_per, T);
+  const unsigned long long slots_need = (unsigned long long)rows_max * (H / g.bn);
+  const unsigned long long sync_need = 3 + (rows_max + g.bm - 1) / g.bm;
+  if (slots_need > kNoallocSlotWords || sync_need > kNoallocSyncWords)
+    return fail(PR_ERR_SHAPE,
+                "T=%d, H=%d needs %llu row slots and %llu words per launch with %dx%d tiles; "
+                "the fixed workspace holds %llu and %llu",
+                T, H, slots_need, sync_need, g.bm, g.bn, kNoallocSlotWords, kNoallocSyncWords);
+  return launch_single_rows(c, x, W, residual_inout, norm_w, eps, T, K, H, norm_kind, out, g,
+                            ws, static_cast<hipStream_t>(stream), false);
+}
+
 int pr_device_status(void* stream, unsigned* status) {
   clear_error();
   if (status == nullptr) return fail(PR_ERR_INVALID_ARG, "null status");
@@ -622,14 +698,23 @@ int pr_device_status(void* stream, unsigned* status) {
   PR_TRY(get_ctx(&c));
   PR_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
   if (c->host_flag != nullptr) __atomic_store_n(c->host_flag, 0u, __ATOMIC_RELEASE);
-  if (c->sync == nullptr) return PR_OK;
-  unsigned v = 0;
-  PR_HIP(hipMemcpy(&v, c->sync, sizeof(v), hipMemcpyDeviceToHost));
-  if (v != 0) {
-    PR_HIP(hipMemset(c->sync, 0, sizeof(unsigned)));
-    PR_HIP(hipDeviceSynchronize());
+  // The status words of the grown workspace and of the fixed one (when set up).
+  unsigned* words[2] = {c->sync, nullptr};
+  SingleWs fixed;
+  if (noalloc_workspace(&fixed) == PR_OK) words[1] = fixed.sync;
+  clear_error();  // a fixed workspace that is not set up is not an error here
+  unsigned all = 0;
+  for (unsigned* wd : words) {
+    if (wd == nullptr) continue;
+    unsigned v = 0;
+    PR_HIP(hipMemcpy(&v, wd, sizeof(v), hipMemcpyDeviceToHost));
+    if (v != 0) {
+      PR_HIP(hipMemset(wd, 0, sizeof(unsigned)));
+      PR_HIP(hipDeviceSynchronize());
+    }
+    all |= v;
   }
-  *status = v;
+  *status = all;
   return PR_OK;
 }
 
