@@ -16,7 +16,15 @@ path.  It is the plain definition of what the path computes, written to be check
 * the microchunk partition ("TPSP Design" section 3 "Microchunk pipeline"): chunks of mc
   rows, the last padded, and only valid rows update residual and output;
 * SiluAndMul, the step before down_proj ("Plugin Architecture" page, SiluAndMul row):
-  x = silu(gate) * up from the merged gate/up projection output.
+  x = silu(gate) * up from the merged gate/up projection output;
+* FP8 dense projections ("TPSP Design" page, section 5 To-do: quantized projections with
+  their scales handled across microchunks).  The page names no format, so these functions
+  take the plainest one the MI355X matrix cores run: OCP E4M3 (4 exponent bits, bias 7, 3
+  mantissa bits, no infinities, S.1111.111 the only NaN, largest finite 448); the weight has one
+  scale per tensor, the activations one per group of consecutive rows (a microchunk), each
+  scale = the group's largest magnitude / 448 (1 for an all-zero group), and a code is the
+  value divided by its scale in fp32, rounded to the nearest E4M3 value (ties to even) and
+  clamped to +-448.  The quantised projection is y = s_x * s_w * sum_k dec(q_x) dec(q_w).
 
 Two modes fix where the projection output may be rounded:
 * ``fused``: the projection result enters the add unrounded;
@@ -118,6 +126,95 @@ def silu_mul(gate_up_bits: np.ndarray, K: int) -> np.ndarray:
     with np.errstate(over="ignore"):
         x = g / (1.0 + np.exp(-g)) * u
     return bf16_bits_of(round_bf16(x))
+
+
+# --------------------------------------------------------------------------------------------
+# FP8 (OCP E4M3) projection inputs
+# --------------------------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """OCP E4M3 codes (uint8) -> float64, exactly.  Bit 7 is the sign, bits 6..3 the biased
+    exponent e (bias 7), bits 2..0 the mantissa m.  e = 0: subnormal m * 2^-9; e > 0:
+    (8 + m) * 2^(e - 10), i.e. 1.m * 2^(e-7); e = 15 with m = 7 is NaN (no infinities)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, np.ldexp(m.astype(np.float64), -9),
+                   np.ldexp((8 + m).astype(np.float64), (e - 10).astype(np.int64)))
+    out = sign * mag
+    out[(e == 15) & (m == 7)] = np.nan
+    return out
+
+
+def _e4m3_grid():
+    """All non-negative finite E4M3 values in code order (codes 0x00 .. 0x7E); the values
+    increase with the code."""
+    return decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+
+
+def encode_e4m3(v: np.ndarray) -> np.ndarray:
+    """float values -> OCP E4M3 codes: the nearest representable magnitude, a tie going to
+    the even code (the even mantissa), magnitudes above 448 clamped to 448; the sign bit is
+    kept (-0 -> 0x80); NaN -> 0x7F."""
+    v = np.asarray(v, dtype=np.float64)
+    grid = _e4m3_grid()
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.searchsorted(grid, a, side="left")         # first grid value >= a
+    hi = np.minimum(hi, len(grid) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - grid[lo], grid[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(grid[hi] == a, hi, pick)           # exact hits (also a == 0)
+    code = pick.astype(np.uint8) | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+    code[np.isnan(v)] = 0x7F
+    return code
+
+
+def quantize_fp8(src_bits: np.ndarray, group_rows: int):
+    """Scaled E4M3 quantisation of a bf16 matrix [R, C] (bit patterns) by groups of
+    `group_rows` consecutive rows (the last group may be shorter).  For group g: amax = the
+    largest |value| in its rows; scale = amax / 448 computed in fp32 (1 when amax = 0); each
+    code = encode_e4m3(value / scale), the quotient taken in fp32 (the precision the device
+    takes this integer decision in).  Returns (codes uint8 [R, C], scales float32 [groups])."""
+    x32 = widen_bf16(src_bits).astype(np.float32)     # bf16 values are exact in fp32
+    R = x32.shape[0]
+    G = int(group_rows)
+    n_groups = -(-R // G) if R else 0
+    codes = np.zeros(x32.shape, dtype=np.uint8)
+    scales = np.ones(n_groups, dtype=np.float32)
+    for g in range(n_groups):
+        rows = slice(g * G, min(R, (g + 1) * G))
+        amax = np.float32(np.max(np.abs(x32[rows]))) if x32[rows].size else np.float32(0)
+        scale = np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(E4M3_MAX))
+        scales[g] = scale
+        codes[rows] = encode_e4m3((x32[rows] / scale).astype(np.float32))
+    return codes, scales
+
+
+def projection_fp8(xq: np.ndarray, x_scales: np.ndarray, group_rows: int, wq: np.ndarray,
+                   w_scale: float) -> np.ndarray:
+    """y[t,h] = s_x[t // group_rows] * s_w * sum_k dec(xq[t,k]) * dec(wq[h,k]) in float64
+    (wq in nn.Linear [out, in] layout)."""
+    x = decode_e4m3(xq)
+    W = decode_e4m3(wq)
+    sx = np.repeat(np.asarray(x_scales, np.float64), int(group_rows))[:x.shape[0]]
+    return (x @ W.T) * sx[:, None] * float(np.float32(w_scale))
+
+
+def proj_add_rmsnorm_fp8(xq, x_scales, group_rows, wq, w_scale, residual, norm_w, eps,
+                         norm_kind=NORM_STANDARD):
+    """The fused region with the FP8 projection: y enters the residual add unrounded, as
+    in the bf16 fused mode; residual add and RMSNorm as there.  Returns (r_new, out) in
+    float64, out unrounded."""
+    r = widen_f32(residual)
+    g = norm_gain(widen_f32(norm_w), norm_kind)
+    e = float(np.float32(eps))
+    y = projection_fp8(xq, x_scales, group_rows, wq, w_scale)
+    rp = residual_add(r, y)
+    return rp, rms_norm(rp, g, e)
 
 
 # --------------------------------------------------------------------------------------------

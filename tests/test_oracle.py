@@ -356,3 +356,151 @@ def test_workload_inputs_statistics():
     x = oracle.widen_bf16(dp["x"])
     assert 0.3 < float(np.mean(x * x)) < 0.42          # E[(silu(a) b)^2] ~ 0.356
 
+
+
+# ------------------------------------------------------------------------------- FP8 (E4M3)
+GOLDEN_E4M3 = os.path.join(os.path.dirname(__file__), "golden", "e4m3_hand.json")
+
+
+def _golden_value(v):
+    if v == "nan":
+        return np.nan
+    if v == "-0":
+        return -0.0
+    return float(v)
+
+
+def test_e4m3_decode_hand_table():
+    """Hand-derived bit-field values: subnormals, the smallest normal, ones, the largest finite,
+    both NaN codes and the signed zero."""
+    g = json.load(open(GOLDEN_E4M3))
+    for e in g["decode"]:
+        got = oracle.decode_e4m3(np.array([int(e["code"], 16)], np.uint8))[0]
+        want = _golden_value(e["value"])
+        if np.isnan(want):
+            assert np.isnan(got), e
+        else:
+            assert got == want and np.signbit(got) == np.signbit(want), (e, got)
+
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    """All 256 codes against torch's float8_e4m3fn (a library routine of the same format)."""
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.decode_e4m3(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    np.testing.assert_array_equal(got[ok], want[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+def test_e4m3_encode_hand_table():
+    """Ties to the even mantissa (normal and subnormal), clamping above 448, the kept sign."""
+    g = json.load(open(GOLDEN_E4M3))
+    for e in g["encode"]:
+        got = oracle.encode_e4m3(np.array([_golden_value(e["value"])]))[0]
+        assert got == int(e["code"], 16), (e, hex(got))
+
+
+def test_e4m3_encode_matches_torch_within_range():
+    """Random fp32 values over the whole finite range (subnormals to 448, both signs), every
+    midpoint between neighbouring codes and values just beside them, against torch's
+    round-to-nearest-even cast to float8_e4m3fn.  (torch does not clamp above 448: that part
+    is pinned by the hand table.)"""
+    rng = np.random.default_rng(3)
+    mags = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), 20000)).astype(np.float32)
+    vals = mags * rng.choice([-1.0, 1.0], mags.size).astype(np.float32)
+    grid = oracle.decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)
+    beside = np.concatenate([np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    vals = np.concatenate([vals, mids, -mids, beside, grid.astype(np.float32)])
+    want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.encode_e4m3(vals)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_e4m3_encode_decode_round_trip():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    np.testing.assert_array_equal(oracle.encode_e4m3(oracle.decode_e4m3(codes)), codes)
+    assert oracle.encode_e4m3(np.array([np.nan]))[0] == 0x7F
+
+
+def test_quantize_fp8_hand_worked():
+    g = json.load(open(GOLDEN_E4M3))["quantize"]
+    row = synth.f32_to_bf16_bits(np.array([g["row"]], np.float32))
+    codes, scales = oracle.quantize_fp8(row, 1)
+    assert [int(c) for c in codes[0]] == [int(c, 16) for c in g["codes"]]
+    assert scales[0] == np.float32(g["scale_numerator"]) / np.float32(g["scale_denominator"])
+
+
+def test_quantize_fp8_group_properties():
+    """Ragged groups of rows: each group's largest magnitude lands on +-448 (its scale is
+    amax / 448); an all-zero group has scale 1 and zero codes; every dequantised value is
+    within half a code step of the input (relative 2^-4 in the normal range, 2^-10 * scale
+    absolute below it)."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((23, 64)).astype(np.float32) * np.float32(3.0)
+    x[10:15] = 0.0                      # group 2 (rows 10..14) all zero
+    bits = synth.f32_to_bf16_bits(x)
+    codes, scales = oracle.quantize_fp8(bits, 5)
+    assert scales.shape == (5,) and scales.dtype == np.float32
+    xv = oracle.widen_bf16(bits)
+    for gi in range(5):
+        rows = slice(5 * gi, min(23, 5 * gi + 5))
+        dq = oracle.decode_e4m3(codes[rows])
+        if gi == 2:
+            assert scales[gi] == 1.0 and np.all(dq == 0)
+            continue
+        amax = np.max(np.abs(xv[rows]))
+        assert scales[gi] == np.float32(np.float32(amax) / np.float32(448.0))
+        assert np.max(np.abs(dq)) == 448.0
+        err = np.abs(dq * float(scales[gi]) - xv[rows])
+        bound = np.maximum(np.abs(xv[rows]) * 2.0 ** -4, 2.0 ** -10 * float(scales[gi]))
+        assert np.all(err <= bound * (1 + 1e-6))
+
+
+def test_projection_fp8_brute_force():
+    """Pure-Python sums (math.fsum) on a non-square tiny shape with ragged scale groups: a
+    dropped scale, a wrong group index or a transposed weight fails it."""
+    rng = np.random.default_rng(9)
+    T, K, H, G = 7, 5, 3, 3
+    xq = rng.integers(0, 256, (T, K)).astype(np.uint8)
+    wq = rng.integers(0, 256, (H, K)).astype(np.uint8)
+    xq[(xq & 0x7F) == 0x7F] = 0x38   # no NaN codes
+    wq[(wq & 0x7F) == 0x7F] = 0x40
+    sx = np.array([0.5, 3.0, 0.25], np.float32)
+    sw = np.float32(0.125)
+    got = oracle.projection_fp8(xq, sx, G, wq, sw)
+    xd, wd = oracle.decode_e4m3(xq), oracle.decode_e4m3(wq)
+    for t in range(T):
+        for h in range(H):
+            s = math.fsum(float(xd[t, k]) * float(wd[h, k]) for k in range(K))
+            want = s * float(sx[t // G]) * float(sw)
+            assert got[t, h] == pytest.approx(want, rel=1e-12, abs=1e-300)
+
+
+def test_fp8_region_exact_on_representable_integers():
+    """Inputs whose every value is an E4M3 value and whose largest magnitude is 448 in every
+    group quantise with scale exactly 1 and codes that decode to the inputs, so the FP8 region
+    equals the bf16 region on the same values and the projection is an exact integer
+    (checked against int64 arithmetic)."""
+    rng = np.random.default_rng(12)
+    T, K, H = 12, 64, 24
+    vals = np.array([0, 1, 2, 3, 4, 6, 8, 12, 16], np.float32)
+    x = rng.choice(vals, (T, K)) * rng.choice([-1.0, 1.0], (T, K)).astype(np.float32)
+    W = rng.choice(vals, (H, K)) * rng.choice([-1.0, 1.0], (H, K)).astype(np.float32)
+    x[:, 0] = 448.0
+    W[:, 0] = -448.0
+    xb, Wb = synth.f32_to_bf16_bits(x), synth.f32_to_bf16_bits(W)
+    xq, sx = oracle.quantize_fp8(xb, 4)
+    wq, sw = oracle.quantize_fp8(Wb, H)
+    assert np.all(sx == 1.0) and np.all(sw == 1.0)
+    np.testing.assert_array_equal(oracle.decode_e4m3(xq), x)
+    y = oracle.projection_fp8(xq, sx, 4, wq, sw[0])
+    np.testing.assert_array_equal(y, x.astype(np.int64) @ W.astype(np.int64).T)
+    r = rng.standard_normal((T, H)).astype(np.float32)
+    w = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    a = oracle.proj_add_rmsnorm_fp8(xq, sx, 4, wq, sw[0], r, w, 1e-5)
+    b = oracle.proj_add_rmsnorm(xb, Wb, r, w, 1e-5, oracle.NORM_STANDARD, "fused")
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
