@@ -199,6 +199,64 @@ int proj_add_rmsnorm_single_launch(const uint16_t* x, const uint16_t* W, float* 
                                    const float* norm_w, float eps, int T, int K, int H,
                                    int norm_kind, uint16_t* out, void* stream);
 
+/* ---------------------------------------------------------------------------------------- *
+ * FP8 projections ("TPSP Design" section 5 To-do: quantized projections, with their scales
+ * handled across microchunks).  The format is OCP E4M3 (sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, no infinities, S.1111.111 the only NaN, largest finite 448), the format the
+ * gfx950 matrix cores take for FP8.  Codes are passed as uint8_t.
+ * ---------------------------------------------------------------------------------------- */
+
+/*
+ * Scaled E4M3 quantisation of a bf16 matrix by groups of rows.
+ *
+ * src     [rows][cols] bf16, device, read.  Finite values.
+ * dst     [rows][cols] E4M3 codes, device, written.
+ * scales  [ceil(rows / group_rows)] fp32, device, written: for the group of rows
+ *         [g * group_rows, min(rows, (g + 1) * group_rows)), scale = largest |value| / 448 in
+ *         fp32 (1 when the group is all zero).  Each code is value / scale (an fp32 division),
+ *         rounded to the nearest E4M3 value with ties to even, magnitudes clamped to 448.
+ * Activations: group_rows = the microchunk (1 gives per-token scales).  A weight [H][K] with
+ * one per-tensor scale: rows = H, cols = K, group_rows = H.
+ * cols a positive multiple of 16; src, dst 16-byte aligned, scales 4-byte aligned; the three
+ * must not overlap.  Uses a library workspace of `rows` floats (grown; under graph capture it
+ * must already be large enough).  Asynchronous on `stream`; rows = 0 is a no-op.
+ * Errors: PR_ERR_SHAPE, PR_ERR_INVALID_ARG, PR_ERR_UNSUPPORTED, PR_ERR_NOMEM, PR_ERR_HIP.
+ */
+int pr_quantize_fp8(const uint16_t* src, uint8_t* dst, float* scales, int rows, int cols,
+                    int group_rows, void* stream);
+
+/*
+ * FP8 weight preparation, once after load: W_src E4M3 codes [H][K] (PR_WEIGHT_OUT_IN) or
+ * [K][H] (PR_WEIGHT_IN_OUT) to W_prep[((k/16)*H + h)*16 + k%16] = W[h][k] (each output
+ * column's 16 consecutive k-values form one 16-byte matrix-core operand).  K and H positive
+ * multiples of 64; 16-byte aligned; no overlap.  Errors: PR_ERR_INVALID_ARG, PR_ERR_SHAPE,
+ * PR_ERR_HIP.
+ */
+int pr_prepare_weight_fp8(const uint8_t* W_src, int src_layout, uint8_t* W_prep, int K, int H,
+                          void* stream);
+
+/*
+ * The fused region with the FP8 projection, in the single-launch form (the pipeline's chunk
+ * hand-offs inside one kernel, as proj_add_rmsnorm_single_launch):
+ *
+ *     y[t,h]  = x_scales[t / scale_rows] * w_scale[0] * sum_k dec(x_q[t,k]) * dec(W[h,k])
+ *               (products exact, fp32 accumulation, the scale applied in fp32)
+ *     r[t,h] <- r[t,h] + y[t,h];   out = RMSNorm(r) as for proj_add_rmsnorm.
+ *
+ * x_q       [T][K] E4M3 codes (pr_quantize_fp8 with group_rows = scale_rows).
+ * x_scales  [ceil(T / scale_rows)] fp32 activation scales; scale_rows >= 1.
+ * W_q       the weight prepared by pr_prepare_weight_fp8; w_scale: one fp32 on the device.
+ * residual_inout, norm_w, eps, norm_kind, out, stream: as proj_add_rmsnorm_single_launch
+ * (out NULL borrows the output workspace), with the same workspace, graph-capture and
+ * give-up behaviour.  Same shape rules (K, H multiples of 64; H a multiple of the tile
+ * columns).  Errors: as proj_add_rmsnorm_single_launch, plus PR_ERR_INVALID_ARG for
+ * scale_rows < 1 or null or misaligned scale pointers.
+ */
+int proj_add_rmsnorm_fp8(const uint8_t* x_q, const float* x_scales, int scale_rows,
+                         const uint8_t* W_q, const float* w_scale, float* residual_inout,
+                         const float* norm_w, float eps, int T, int K, int H, int norm_kind,
+                         uint16_t* out, void* stream);
+
 /*
  * Library set-up on the current device: creates the device's library stream, events and the
  * host-mapped status flag, and looks up and clears the fixed workspace of
@@ -268,6 +326,12 @@ int pr_release_workspace(void);
  * the written buffers with the others; nothing is dereferenced). */
 int pr_validate(const void* x, const void* W, const void* residual_inout, const void* norm_w,
                 float eps, int T, int K, int H, int microchunk, int norm_kind, const void* out);
+
+/* Argument checks of proj_add_rmsnorm_fp8 (x_q and W_q hold one byte per element; the scale
+ * pointers must be non-null and 4-byte aligned and must not overlap the written buffers). */
+int pr_validate_fp8(const void* x_q, const void* x_scales, int scale_rows, const void* W_q,
+                    const void* w_scale, const void* residual_inout, const void* norm_w,
+                    float eps, int T, int K, int H, int norm_kind, const void* out);
 
 /* Execution decision for one call. */
 typedef struct {

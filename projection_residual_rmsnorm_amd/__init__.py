@@ -77,6 +77,11 @@ SIGNATURES = {
     "proj_add_rmsnorm_single_launch_noalloc": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp,
                                                    _vp]),
     "pr_init": (_i, []),
+    "pr_quantize_fp8": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
+    "pr_prepare_weight_fp8": (_i, [_vp, _i, _vp, _i, _i, _vp]),
+    "proj_add_rmsnorm_fp8": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp,
+                                  _vp]),
+    "pr_validate_fp8": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp]),
     "pr_device_status": (_i, [_vp, _c.POINTER(_c.c_uint)]),
     "pr_workspace_output": (_vp, []),
     "pr_release_workspace": (_i, []),
@@ -222,6 +227,43 @@ def proj_add_rmsnorm_single_launch_noalloc(x, W, residual_inout, norm_w, eps: fl
     _check(_lib().proj_add_rmsnorm_single_launch_noalloc(px, pw, pr_, pn, eps, T, K, H,
                                                          norm_kind, po,
                                                          _stream(stream, x, residual_inout)))
+
+
+def pr_quantize_fp8(src, dst, scales, rows: int, cols: int, group_rows: int,
+                    stream=None) -> None:
+    """E4M3 codes of the bf16 src [rows][cols] by groups of group_rows rows; scales per group."""
+    rows_, cols_ = max(rows, 0), max(cols, 0)
+    groups = (rows_ - 1) // group_rows + 1 if rows_ > 0 and group_rows > 0 else 0
+    _check(_lib().pr_quantize_fp8(_ptr(src, 2 * rows_ * cols_, "src"),
+                                  _ptr(dst, rows_ * cols_, "dst"),
+                                  _ptr(scales, 4 * groups, "scales"), rows, cols, group_rows,
+                                  _stream(stream, src)))
+
+
+def pr_prepare_weight_fp8(W_src, src_layout: int, W_prep, K: int, H: int, stream=None) -> None:
+    n = max(K, 0) * max(H, 0)
+    _check(_lib().pr_prepare_weight_fp8(_ptr(W_src, n, "W_src"), src_layout,
+                                        _ptr(W_prep, n, "W_prep"), K, H, _stream(stream, W_src)))
+
+
+def proj_add_rmsnorm_fp8(x_q, x_scales, scale_rows: int, W_q, w_scale, residual_inout, norm_w,
+                         eps: float, T: int, K: int, H: int, norm_kind: int = PR_NORM_STANDARD,
+                         out=None, stream=None) -> None:
+    T_, K_, H_ = max(T, 0), max(K, 0), max(H, 0)
+    groups = (T_ - 1) // scale_rows + 1 if T_ > 0 and scale_rows > 0 else 0
+    _check(_lib().proj_add_rmsnorm_fp8(
+        _ptr(x_q, T_ * K_, "x_q"), _ptr(x_scales, 4 * groups, "x_scales"), scale_rows,
+        _ptr(W_q, K_ * H_, "W_q"), _ptr(w_scale, 4, "w_scale"),
+        _ptr(residual_inout, 4 * T_ * H_, "residual_inout"), _ptr(norm_w, 4 * H_, "norm_w"), eps,
+        T, K, H, norm_kind, _ptr(out, 2 * T_ * H_, "out"), _stream(stream, x_q, residual_inout)))
+
+
+def pr_validate_fp8(x_q, x_scales, scale_rows, W_q, w_scale, residual_inout, norm_w, eps, T, K,
+                    H, norm_kind, out) -> int:
+    """Returns the code (does not raise)."""
+    return _lib().pr_validate_fp8(_ptr(x_q), _ptr(x_scales), scale_rows, _ptr(W_q),
+                                  _ptr(w_scale), _ptr(residual_inout), _ptr(norm_w), eps, T, K,
+                                  H, norm_kind, _ptr(out))
 
 
 def pr_device_status(stream=None) -> int:

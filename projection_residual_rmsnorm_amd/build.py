@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libprojaddnorm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["pr_kernels.hip", "pr_silu.hip", "pr_noalloc.hip", "pr_host.cpp", "pr_runtime.cpp",
+SOURCES = ["pr_kernels.hip", "pr_silu.hip", "pr_fp8.hip", "pr_noalloc.hip", "pr_host.cpp", "pr_runtime.cpp",
            "pr_tune.cpp"]
 
 HIPCC_FLAGS = [

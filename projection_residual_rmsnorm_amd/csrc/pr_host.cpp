@@ -319,37 +319,20 @@ int decide(int T, int K, int H, int microchunk, pr_decision* d) {
 
 }  // namespace pr
 
-using namespace pr;
+namespace pr {
+namespace {
 
-extern "C" {
-
-int pr_version(void) { return PR_VERSION; }
-
-const char* pr_strerror(int code) {
-  switch (code) {
-    case PR_OK:
-      return "success";
-    case PR_ERR_INVALID_ARG:
-      return "invalid argument";
-    case PR_ERR_SHAPE:
-      return "unsupported shape";
-    case PR_ERR_MICROCHUNK:
-      return "invalid microchunk";
-    case PR_ERR_UNSUPPORTED:
-      return "unsupported call";
-    case PR_ERR_NOMEM:
-      return "out of device memory";
-    case PR_ERR_HIP:
-      return "HIP error";
-    default:
-      return "unknown error";
-  }
-}
-
-const char* pr_last_error(void) { return pr::g_last_error.c_str(); }
-
-int pr_validate(const void* x, const void* W, const void* residual_inout, const void* norm_w,
-                float eps, int T, int K, int H, int microchunk, int norm_kind, const void* out) {
+// Checks shared by the bf16 and the FP8 region: sizes, microchunk, norm kind, eps, null
+// pointers, alignment, and that the written buffers (residual, out) overlap nothing else the
+// call touches.  x and W hold `eb` bytes per element; `extra` lists further read-only inputs.
+struct Extra {
+  const void* p;
+  unsigned long long bytes;
+  const char* name;
+};
+int validate_region(const void* x, const void* W, const void* residual_inout, const void* norm_w,
+                    float eps, int T, int K, int H, int microchunk, int norm_kind,
+                    const void* out, unsigned eb, const Extra* extra, int n_extra) {
   if (T < 0 || K <= 0 || H <= 0)
     return fail(PR_ERR_INVALID_ARG, "sizes must satisfy T >= 0, K > 0, H > 0 (T=%d K=%d H=%d)",
                 T, K, H);
@@ -382,22 +365,81 @@ int pr_validate(const void* x, const void* W, const void* residual_inout, const 
   auto range = [](const void* p, unsigned long long bytes, const char* name) {
     return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes, name};
   };
-  const Range rx = range(x, 2ULL * T * K, "x"), rw = range(W, 2ULL * K * H, "W"),
+  const Range rx = range(x, (unsigned long long)eb * T * K, "x"),
+              rw = range(W, (unsigned long long)eb * K * H, "W"),
               rr = range(residual_inout, 4ULL * T * H, "residual"),
               rn = range(norm_w, 4ULL * H, "norm_w");
   auto overlap = [](const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; };
   for (const Range& o : {rx, rw, rn})
     if (overlap(rr, o)) return fail(PR_ERR_INVALID_ARG, "residual overlaps %s", o.name);
+  for (int i = 0; i < n_extra; ++i) {
+    if (extra[i].p == nullptr) return fail(PR_ERR_INVALID_ARG, "null %s", extra[i].name);
+    if ((uintptr_t)extra[i].p % 4 != 0)
+      return fail(PR_ERR_INVALID_ARG, "%s must be 4-byte aligned", extra[i].name);
+    if (overlap(rr, range(extra[i].p, extra[i].bytes, extra[i].name)))
+      return fail(PR_ERR_INVALID_ARG, "residual overlaps %s", extra[i].name);
+  }
   if (out != nullptr) {
     const Range ro = range(out, 2ULL * T * H, "out");
     for (const Range& o : {rx, rw, rr, rn})
       if (overlap(ro, o)) return fail(PR_ERR_INVALID_ARG, "out overlaps %s", o.name);
+    for (int i = 0; i < n_extra; ++i)
+      if (overlap(ro, range(extra[i].p, extra[i].bytes, extra[i].name)))
+        return fail(PR_ERR_INVALID_ARG, "out overlaps %s", extra[i].name);
   }
   const uintptr_t a[5] = {(uintptr_t)x, (uintptr_t)W, (uintptr_t)residual_inout,
                           (uintptr_t)norm_w, (uintptr_t)out};
   for (uintptr_t p : a)
     if (p % 16 != 0) return fail(PR_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   return PR_OK;
+}
+
+}  // namespace
+}  // namespace pr
+
+using namespace pr;
+
+extern "C" {
+
+int pr_version(void) { return PR_VERSION; }
+
+const char* pr_strerror(int code) {
+  switch (code) {
+    case PR_OK:
+      return "success";
+    case PR_ERR_INVALID_ARG:
+      return "invalid argument";
+    case PR_ERR_SHAPE:
+      return "unsupported shape";
+    case PR_ERR_MICROCHUNK:
+      return "invalid microchunk";
+    case PR_ERR_UNSUPPORTED:
+      return "unsupported call";
+    case PR_ERR_NOMEM:
+      return "out of device memory";
+    case PR_ERR_HIP:
+      return "HIP error";
+    default:
+      return "unknown error";
+  }
+}
+
+const char* pr_last_error(void) { return pr::g_last_error.c_str(); }
+
+int pr_validate(const void* x, const void* W, const void* residual_inout, const void* norm_w,
+                float eps, int T, int K, int H, int microchunk, int norm_kind, const void* out) {
+  return pr::validate_region(x, W, residual_inout, norm_w, eps, T, K, H, microchunk, norm_kind,
+                             out, 2, nullptr, 0);
+}
+
+int pr_validate_fp8(const void* x_q, const void* x_scales, int scale_rows, const void* W_q,
+                    const void* w_scale, const void* residual_inout, const void* norm_w,
+                    float eps, int T, int K, int H, int norm_kind, const void* out) {
+  if (scale_rows < 1) return pr::fail(PR_ERR_INVALID_ARG, "scale_rows=%d must be >= 1", scale_rows);
+  const unsigned long long groups = T > 0 ? (unsigned long long)(T - 1) / scale_rows + 1 : 0;
+  const pr::Extra extra[2] = {{x_scales, 4ULL * groups, "x_scales"}, {w_scale, 4, "w_scale"}};
+  return pr::validate_region(x_q, W_q, residual_inout, norm_w, eps, T, K, H, 0, norm_kind, out,
+                             1, extra, T > 0 ? 2 : 0);
 }
 
 int pr_select(int T, int K, int H, int microchunk, pr_decision* d) {

@@ -113,6 +113,17 @@ int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, con
                             const GemmCfg& cfg, float eps, int gemma, void* stream,
                             void* start_timing = nullptr, void* stop_timing = nullptr);
 
+// The single launch with the FP8 projection: xq [M][K] and the prepared Wq (E4M3 bytes,
+// Wq[((k/16)*N + n)*16 + k%16] = W[n][k]); y = acc * x_scales[(scale_row0 + row) / scale_rows]
+// * w_scale[0] before the residual add.  Tiles 256x256, 256x128, 128x128 with 8 waves; K a
+// multiple of 64.
+int launch_gemm_add_rmsnorm_fp8(const uint8_t* xq, const uint8_t* Wq, float* r, const float* w,
+                                uint16_t* out, const SingleWs& ws, int M, int N, int K,
+                                const GemmCfg& cfg, const float* x_scales, int scale_rows,
+                                int scale_row0, const float* w_scale, float eps, int gemma,
+                                void* stream, void* start_timing = nullptr,
+                                void* stop_timing = nullptr);
+
 int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,
                           void* stream);
 
@@ -129,6 +140,14 @@ int noalloc_workspace(SingleWs* ws);
 
 // x[T][K] = bf16(silu(gate) * up) from the merged gate_up[T][2K] (gate first); K % 8 == 0,
 // both 16-byte aligned.
+// FP8 quantisation (pr_fp8.hip): codes [rows][cols] E4M3 of the bf16 src by groups of
+// group_rows rows, scales[g] = amax / 448 (1 for an all-zero group); row_amax is a workspace of
+// `rows` floats.  cols % 16 == 0.
+int launch_quantize_fp8(const uint16_t* src, uint8_t* dst, float* scales, float* row_amax,
+                        int rows, int cols, int group_rows, void* stream);
+// FP8 weight layout: dst[((k/16)*H + h)*16 + k%16] = W[h][k] from [H][K] or [K][H] bytes.
+int launch_prepare_weight_fp8(const uint8_t* src, int src_layout, uint8_t* dst, int K, int H,
+                              void* stream);
 int launch_silu_mul(const uint16_t* gate_up, uint16_t* x, int T, int K, void* stream);
 
 // Debug helpers: a bounded sleep (iters x s_sleep 127) and a NaN fill.

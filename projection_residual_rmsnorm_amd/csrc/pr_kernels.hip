@@ -21,6 +21,8 @@ namespace pr {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -144,7 +146,16 @@ struct NoTail {
 // half g of every stage.  Each wave then holds a partial sum over 1/KG of K (the caller adds
 // the groups' partials); with KG = 2 and 4-wave groups every SIMD runs two waves while each
 // wave keeps the large wave tile.
-template <int BM, int BN, int NB, int WM, int WN, int KG = 1, typename Tail = NoTail>
+//
+// FP8: A and Bp hold OCP E4M3 bytes (A [M][K] bytes, Bp[((k/16)*N + n)*16 + k%16] = W[n][k]),
+// and a stage's 64 bytes per row are 64 k-values.  The stage layouts and loads are byte for
+// byte those of bf16, with 16-byte k-groups of 16 values instead of 8.  One
+// v_mfma_scale_f32_32x32x64_f8f6f4 (format 0 = E4M3, unit scales) per 32x32 block covers the
+// stage; lane l supplies the 16-byte k-groups l/32 and 2 + l/32 of its row (A) or column (B),
+// which are the two fragments the bf16 loop reads for its two 16-deep substeps.  The matrix
+// core only needs A and B to take the same k order, which this gives.
+template <int BM, int BN, int NB, int WM, int WN, int KG = 1, typename Tail = NoTail,
+          bool FP8 = false>
 __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp, int M, int N, int K, int m0,
     int n0, int k_begin, int nk, const Tail& tail = Tail()) {
@@ -168,6 +179,7 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   static_assert(LPW * (P - 1) < 64, "vmcnt range");
   static_assert(KG == 1 || KG == 2, "one or two K groups");
   static_assert(Tail::kLoads < 0 || Tail::kLoads == LPW, "a tail refill issues a stage's loads");
+  static_assert(!FP8 || (KG == 1 && Tail::kLoads < 0), "FP8: one K group, no tail hook");
 
   constexpr int HALF = A_BYTES + B_BYTES;  // one 32-deep half of a stage
   constexpr int STAGE = KG * HALF;
@@ -204,7 +216,10 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
     const int kg = (lane & 3) ^ (((trow >> 1) ^ (trow >> 3)) & 3);
     int row = m0 + trow;
     row = row < M ? row : M - 1;
-    a_off[i] = (uint32_t)(row * K + kg * 8) * 2u;
+    if constexpr (FP8)
+      a_off[i] = (uint32_t)(row * K + kg * 16);  // bytes: rows of K one-byte values
+    else
+      a_off[i] = (uint32_t)(row * K + kg * 8) * 2u;
   }
   int b_col = n0 + (wave % CG) * 64 + lane;
   b_col = b_col < N ? b_col : N - 1;
@@ -212,8 +227,11 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   const uint32_t b_step = (uint32_t)((NW / CG) * N * 8) * 2u;
 
   // Stage bases advance by a fixed number of bytes per half (scalar arithmetic only).
-  const char* a_base0 = reinterpret_cast<const char*>(A + k_begin);
-  const char* b_base0 = reinterpret_cast<const char*>(Bp + (long long)(k_begin / 8) * N * 8);
+  const char* a_base0 = FP8 ? reinterpret_cast<const char*>(A) + k_begin
+                            : reinterpret_cast<const char*>(A + k_begin);
+  const char* b_base0 =
+      FP8 ? reinterpret_cast<const char*>(Bp) + (long long)(k_begin / 16) * N * 16
+          : reinterpret_cast<const char*>(Bp + (long long)(k_begin / 8) * N * 8);
   const long long b_half_bytes = (long long)(kBK / 8) * N * 16;
   auto issue_stage = [&](int kt, char* buf) {
 #pragma unroll
@@ -275,6 +293,70 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   };
 
   bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+
+  if constexpr (FP8) {
+    // A stage's fragments: per B column block and A row block, k-groups l/32 and 2 + l/32 of
+    // the lane's row or column, joined into the 32-byte operand (B first: every MFMA needs
+    // all of B's blocks of its wave tile).
+    i32x8_t f8a[TM], f8b[TN];
+    auto load_frags8 = [&](const char* buf) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = wn * WTN + j * 32 + (lane & 31);
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(buf + A_BYTES +
+                                                             ((lane >> 5) * BN + col) * 16);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(buf + A_BYTES +
+                                                             ((2 + (lane >> 5)) * BN + col) * 16);
+        f8b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const char* rowp = buf + (wm * TM + i) * 2048;
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(rowp + a_lane0);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(rowp + a_lane1);
+        f8a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
+    // Prologue: stages 0 .. P-1 in flight, wait for stage 0, read its fragments.
+#pragma unroll
+    for (int p = 0; p < P; ++p) issue_stage(min(p, nk - 1), smem(p));
+    __builtin_amdgcn_s_waitcnt(PR_VMCNT(LPW * (P - 1)));
+    barrier_no_fence();
+    load_frags8(smem(0));
+    // A step: the refill, the stage's MFMAs, then (stage kt+1 landed, every wave past the
+    // barrier) the next stage's fragments.
+    auto step8 = [&](int kt, char* next, char* refill) {
+      issue_stage(min(kt + P, nk - 1), refill);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f8a[i], f8b[j], acc[i][j],
+                                                                      0, 0, 0, 127, 0, 127);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(PR_VMCNT(LPW * (P - 1)));  // stage kt+1 landed
+      __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);
+      barrier_no_fence();
+      load_frags8(next);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + NB <= nk; kt += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) step8(kt + u, smem((u + 1) % NB), smem((u + P) % NB));
+    }
+    const int rem = nk - kt;
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u)
+      if (u < rem) step8(kt + u, smem((u + 1) % NB), smem((u + P) % NB));
+    TileAcc<TM, TN> res;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) res.v[i][j] = acc[i][j];
+    return res;
+  }
 
   // Prologue: stages 0 .. P-1 in flight, wait for stage 0, read its first fragments.
 #pragma unroll
@@ -506,7 +588,10 @@ __device__ __forceinline__ float lane_group_sum(float q) {
   return q;
 }
 
-template <int BM, int BN, int NB, int WM, int WN, int KG>
+// FP8: A and Bp point at E4M3 bytes (see tile_mainloop) and y = acc * x_scales[(scale_row0 +
+// row) / scale_rows] * w_scale[0] in fp32 before the residual add; otherwise those arguments
+// are unused.
+template <int BM, int BN, int NB, int WM, int WN, int KG, bool FP8 = false>
 __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     gemm_add_rmsnorm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp,
                             float* __restrict__ R, const float* __restrict__ w,
@@ -516,7 +601,8 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
                             unsigned fault_mask, unsigned spin_limit,
                             unsigned long long* __restrict__ pwords,
                             unsigned long long slot_words, unsigned long long pword_words,
-                            unsigned* __restrict__ host_flag) {
+                            unsigned* __restrict__ host_flag, const float* __restrict__ x_scales,
+                            int scale_rows, int scale_row0, const float* __restrict__ w_scale) {
   // Main loop: KG groups of WM x WN waves (wave tiles BM/WM x BN/WN, TM x TN MFMA blocks).
   // Epilogue: after the groups' partials are combined, EWM x WN waves, each owning a
   // BM/EWM x BN/WN tile (ETM x TN blocks).
@@ -530,12 +616,14 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
   constexpr int TN = WTN / 32;
   constexpr int STAGE = KG * (BM + BN) * kBK * 2;
   static_assert(NB >= 3, "the norm epilogue uses the third ring buffer");
-  static_assert((BM * WN + BM + 1) * 4 <= STAGE, "row partials fit in one stage buffer");
+  static_assert((BM * WN + 2 * BM + 4) * 4 <= STAGE, "row partials fit in one stage buffer");
+  static_assert(!FP8 || KG == 1, "FP8: one K group");
   char* const sb0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
   char* const sb1 = ring_buffer<1, STAGE, BM, BN, NB, WM, WN>();
   float* const sred = reinterpret_cast<float*>(ring_buffer<2, STAGE, BM, BN, NB, WM, WN>());
   float* const sinv = sred + BM * WN;
   int* const sflag = reinterpret_cast<int*>(sinv + BM);
+  float* const sscl = sinv + BM + 4;  // FP8: the tile's per-row dequantisation scales
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kgrp = KG == 1 ? 0 : wave / GW;  // K group of the main loop
@@ -607,12 +695,20 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
           }
     }
 
-    const TileAcc<TM, TN> part_acc =
-        tile_mainloop<BM, BN, NB, WM, WN, KG>(A, Bp, M, N, K, m0, n0, 0, K / (kBK * KG));
+    const TileAcc<TM, TN> part_acc = tile_mainloop<BM, BN, NB, WM, WN, KG, NoTail, FP8>(
+        A, Bp, M, N, K, m0, n0, 0, FP8 ? K / (2 * kBK) : K / (kBK * KG));
     // The ring's trailing refills (direct-to-LDS loads) have landed and every wave is past its
     // last fragment read before the stage buffers are reused below.
     __builtin_amdgcn_s_waitcnt(PR_VMCNT(0));
     __syncthreads();
+    if constexpr (FP8) {
+      // One scale per tile row: the row's activation-group scale times the weight scale.
+      if (threadIdx.x < BM) {
+        const int row = min(m0 + (int)threadIdx.x, M - 1);
+        sscl[threadIdx.x] = x_scales[(scale_row0 + row) / scale_rows] * w_scale[0];
+      }
+      __syncthreads();
+    }
     TileAcc<ETM, TN> tacc;
     if constexpr (KG == 1) {
       tacc = part_acc;
@@ -700,7 +796,11 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
           const int trow = row_of(el, i, h, rr);
           const int r_in = rr * RPI + lrow;
           const int row = min(m0 + trow, M - 1);  // rows past M are computed, never stored
-          const float4 y = *reinterpret_cast<const float4*>(ep + r_in * EP_LD + rcol);
+          float4 y = *reinterpret_cast<const float4*>(ep + r_in * EP_LD + rcol);
+          if constexpr (FP8) {
+            const float sc = sscl[trow];
+            y = make_float4(y.x * sc, y.y * sc, y.z * sc, y.w * sc);
+          }
           const float4 rv = keep[(i * 2 + h) * NR + rr];
           const float4 v = make_float4(rv.x + y.x, rv.y + y.y, rv.z + y.z, rv.w + y.w);
           // r + y stays in registers; the residual is stored with the output, after the row
@@ -1598,11 +1698,21 @@ int resident_workgroups(Kern kern, int threads, int* out) {
   return PR_OK;
 }
 
-template <int BM, int BN, int NB, int WM, int WN, int KG>
+// Scales of the FP8 form (unused otherwise): per-group activation scales read at
+// (scale_row0 + row) / scale_rows, and the weight's scale.
+struct Fp8Scales {
+  const float* x_scales = nullptr;
+  int scale_rows = 1;
+  int scale_row0 = 0;
+  const float* w_scale = nullptr;
+};
+
+template <int BM, int BN, int NB, int WM, int WN, int KG, bool FP8 = false>
 int launch_single_t(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
                     uint16_t* out, const SingleWs& ws, int M, int N, int K, float eps, int gemma,
-                    hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  auto kern = gemm_add_rmsnorm_kernel<BM, BN, NB, WM, WN, KG>;
+                    hipStream_t s, hipEvent_t t0, hipEvent_t t1,
+                    const Fp8Scales& sc = Fp8Scales()) {
+  auto kern = gemm_add_rmsnorm_kernel<BM, BN, NB, WM, WN, KG, FP8>;
   constexpr int threads = WM * WN * KG * 64;
   static int resident = 0;  // per instantiation; the library runs on one kind of device
   if (resident == 0) PR_TRY_K(resident_workgroups(kern, threads, &resident));
@@ -1617,12 +1727,13 @@ int launch_single_t(const uint16_t* x, const uint16_t* Wp, float* r, const float
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, t0, t1, 0, x, Wp, r, w, out,
                           ws.slots, ws.sync, M, N, K, tiles_m, tiles_n, rows_per_round, eps,
                           gemma, ws.fault_mask, ws.spin_limit, ws.pwords, ws.slot_words,
-                          ws.pword_words, ws.host_flag);
+                          ws.pword_words, ws.host_flag, sc.x_scales, sc.scale_rows,
+                          sc.scale_row0, sc.w_scale);
   } else {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, x, Wp, r, w, out, ws.slots,
                        ws.sync, M, N, K, tiles_m, tiles_n, rows_per_round, eps, gemma,
                        ws.fault_mask, ws.spin_limit, ws.pwords, ws.slot_words, ws.pword_words,
-                       ws.host_flag);
+                       ws.host_flag, sc.x_scales, sc.scale_rows, sc.scale_row0, sc.w_scale);
   }
   return check_launch("gemm_add_rmsnorm_kernel");
 }
@@ -1752,6 +1863,39 @@ int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, con
     return launch_single_t<128, 128, 4, 2, 4, 1>(x, Wp, r, w, out, ws, M, N, K, eps, gemma, s,
                                                  t0, t1);
   return fail(PR_ERR_INVALID_ARG, "single launch: no tile %dx%d", cfg.bm, cfg.bn);
+}
+
+int launch_gemm_add_rmsnorm_fp8(const uint8_t* xq, const uint8_t* Wq, float* r, const float* w,
+                                uint16_t* out, const SingleWs& ws, int M, int N, int K,
+                                const GemmCfg& cfg, const float* x_scales, int scale_rows,
+                                int scale_row0, const float* w_scale, float eps, int gemma,
+                                void* stream, void* start_timing, void* stop_timing) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t t0 = static_cast<hipEvent_t>(start_timing);
+  hipEvent_t t1 = static_cast<hipEvent_t>(stop_timing);
+  if (M <= 0) return PR_OK;
+  if (K % (2 * kBK) != 0 || N % cfg.bn != 0 || N / cfg.bn > 64 || cfg.split != 1 ||
+      cfg.kgroups != 1 || cfg.waves != 8)
+    return fail(PR_ERR_SHAPE, "FP8 single launch: N=%d K=%d with tile %dx%d split %d, %d waves "
+                "not supported (K a multiple of 64, 8 waves, one K group)", N, K, cfg.bm,
+                cfg.bn, cfg.split, cfg.waves);
+  Fp8Scales sc;
+  sc.x_scales = x_scales;
+  sc.scale_rows = scale_rows;
+  sc.scale_row0 = scale_row0;
+  sc.w_scale = w_scale;
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(xq);  // byte arrays (see the kernel)
+  const uint16_t* Wp = reinterpret_cast<const uint16_t*>(Wq);
+  if (cfg.bm == 256 && cfg.bn == 256)
+    return launch_single_t<256, 256, 5, 2, 4, 1, true>(x, Wp, r, w, out, ws, M, N, K, eps, gemma,
+                                                       s, t0, t1, sc);
+  if (cfg.bm == 256 && cfg.bn == 128)
+    return launch_single_t<256, 128, 4, 4, 2, 1, true>(x, Wp, r, w, out, ws, M, N, K, eps, gemma,
+                                                       s, t0, t1, sc);
+  if (cfg.bm == 128 && cfg.bn == 128)
+    return launch_single_t<128, 128, 4, 2, 4, 1, true>(x, Wp, r, w, out, ws, M, N, K, eps, gemma,
+                                                       s, t0, t1, sc);
+  return fail(PR_ERR_INVALID_ARG, "FP8 single launch: no tile %dx%d", cfg.bm, cfg.bn);
 }
 
 int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_stride,

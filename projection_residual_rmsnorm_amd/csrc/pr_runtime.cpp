@@ -52,6 +52,9 @@ struct DevCtx {
   size_t pair_flags_bytes = 0;
   void* xbuf = nullptr;
   size_t xbuf_bytes = 0;
+  // FP8 quantisation: per-row maxima
+  void* row_amax = nullptr;
+  size_t row_amax_bytes = 0;
   const uint16_t* last_borrowed = nullptr;
   // Give-up flag of the single launch in host-mapped memory (host address and the address the
   // kernels store to): set by a tile whose bounded wait gave up, read and cleared by the next
@@ -471,11 +474,9 @@ GemmCfg cfg_of(const pr_decision& d) {
   return g;
 }
 
-int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const float* w,
-               float eps, int T, int K, int H, int norm_kind, uint16_t* out,
-               const pr_decision& d, hipStream_t s) {
-  const GemmCfg g = cfg_of(d);
-  if (fault_injected()) return fail(PR_ERR_HIP, "injected launch failure (PR_FAULT_INJECT)");
+// The grown single-launch workspace for T rows with configuration g (row slots, sync words,
+// the pair form's words and exchange regions), as `ws` (slots, sync, pair fields).
+int single_workspace(DevCtx* c, const GemmCfg& g, int T, int K, int H, SingleWs* ws) {
   // Launches cover at most 2^30 elements of x each (32-bit offsets in the kernel), in whole
   // tile rows; each launch is independent (rows do not interact).
   const long long rows_per = ((1LL << 30) / K) / g.bm * g.bm;
@@ -524,14 +525,23 @@ int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const 
     PR_HIP(hipDeviceSynchronize());
     PR_HIP(hipMemcpy(c->sync + 2, &v, sizeof(v), hipMemcpyHostToDevice));
   }
+  ws->slots = static_cast<unsigned long long*>(c->row_slots);
+  ws->slot_words = c->row_slots_bytes / sizeof(unsigned long long);
+  ws->sync = c->sync;
+  ws->pwords = static_cast<unsigned long long*>(c->pair_flags);
+  ws->pword_words = c->pair_flags_bytes / sizeof(unsigned long long);
+  ws->xbuf = static_cast<unsigned long long*>(c->xbuf);
+  ws->xbuf_words = c->xbuf_bytes / sizeof(unsigned long long);
+  return PR_OK;
+}
+
+int run_single(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, const float* w,
+               float eps, int T, int K, int H, int norm_kind, uint16_t* out,
+               const pr_decision& d, hipStream_t s) {
+  const GemmCfg g = cfg_of(d);
+  if (fault_injected()) return fail(PR_ERR_HIP, "injected launch failure (PR_FAULT_INJECT)");
   SingleWs ws;
-  ws.slots = static_cast<unsigned long long*>(c->row_slots);
-  ws.slot_words = c->row_slots_bytes / sizeof(unsigned long long);
-  ws.sync = c->sync;
-  ws.pwords = static_cast<unsigned long long*>(c->pair_flags);
-  ws.pword_words = c->pair_flags_bytes / sizeof(unsigned long long);
-  ws.xbuf = static_cast<unsigned long long*>(c->xbuf);
-  ws.xbuf_words = c->xbuf_bytes / sizeof(unsigned long long);
+  PR_TRY(single_workspace(c, g, T, K, H, &ws));
   return launch_single_rows(c, x, W, r, w, eps, T, K, H, norm_kind, out, g, ws, s, true);
 }
 
@@ -643,6 +653,106 @@ int proj_add_rmsnorm_single_launch(const uint16_t* x, const uint16_t* W, float* 
                   stream);
 }
 
+int pr_quantize_fp8(const uint16_t* src, uint8_t* dst, float* scales, int rows, int cols,
+                    int group_rows, void* stream) {
+  clear_error();
+  if (rows < 0 || cols <= 0 || cols % 16 != 0)
+    return fail(PR_ERR_SHAPE, "rows=%d must be >= 0 and cols=%d a positive multiple of 16", rows,
+                cols);
+  if (group_rows < 1) return fail(PR_ERR_INVALID_ARG, "group_rows=%d must be >= 1", group_rows);
+  if ((long long)rows * cols > (1LL << 40)) return fail(PR_ERR_SHAPE, "rows=%d too large", rows);
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  PR_TRY(check_give_up(c));
+  if (rows == 0) return PR_OK;
+  if (src == nullptr || dst == nullptr || scales == nullptr)
+    return fail(PR_ERR_INVALID_ARG, "null tensor pointer");
+  if ((uintptr_t)src % 16 != 0 || (uintptr_t)dst % 16 != 0 || (uintptr_t)scales % 4 != 0)
+    return fail(PR_ERR_INVALID_ARG, "src and dst must be 16-byte aligned, scales 4-byte aligned");
+  const uintptr_t s0 = (uintptr_t)src, s1 = s0 + 2ULL * rows * cols;
+  const uintptr_t d0 = (uintptr_t)dst, d1 = d0 + 1ULL * rows * cols;
+  const uintptr_t c0 = (uintptr_t)scales, c1 = c0 + 4ULL * ((rows - 1) / group_rows + 1);
+  if ((d0 < s1 && s0 < d1) || (c0 < s1 && s0 < c1) || (c0 < d1 && d0 < c1))
+    return fail(PR_ERR_INVALID_ARG, "src, dst and scales must not overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool capturing = false;
+  PR_TRY(stream_capturing(s, &capturing));
+  c->capturing = capturing;
+  int rc = grow(c, &c->row_amax, &c->row_amax_bytes, (size_t)rows * sizeof(float));
+  c->capturing = false;
+  if (rc != PR_OK) return rc;
+  return launch_quantize_fp8(src, dst, scales, static_cast<float*>(c->row_amax), rows, cols,
+                             group_rows, s);
+}
+
+int pr_prepare_weight_fp8(const uint8_t* W_src, int src_layout, uint8_t* W_prep, int K, int H,
+                          void* stream) {
+  clear_error();
+  if (W_src == nullptr || W_prep == nullptr) return fail(PR_ERR_INVALID_ARG, "null weight");
+  if (src_layout != PR_WEIGHT_OUT_IN && src_layout != PR_WEIGHT_IN_OUT)
+    return fail(PR_ERR_INVALID_ARG, "unknown weight layout %d", src_layout);
+  if (K <= 0 || H <= 0 || K % 64 != 0 || H % 64 != 0)
+    return fail(PR_ERR_SHAPE, "K=%d and H=%d must be positive multiples of 64", K, H);
+  if ((long long)K * H > (1LL << 31)) return fail(PR_ERR_SHAPE, "weight too large");
+  if ((uintptr_t)W_src % 16 != 0 || (uintptr_t)W_prep % 16 != 0)
+    return fail(PR_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  const uintptr_t a0 = (uintptr_t)W_src, a1 = a0 + 1ULL * K * H;
+  const uintptr_t b0 = (uintptr_t)W_prep, b1 = b0 + 1ULL * K * H;
+  if (a0 < b1 && b0 < a1) return fail(PR_ERR_INVALID_ARG, "W_prep must not overlap W_src");
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  PR_TRY(check_give_up(c));
+  return launch_prepare_weight_fp8(W_src, src_layout, W_prep, K, H, stream);
+}
+
+int proj_add_rmsnorm_fp8(const uint8_t* x_q, const float* x_scales, int scale_rows,
+                         const uint8_t* W_q, const float* w_scale, float* residual_inout,
+                         const float* norm_w, float eps, int T, int K, int H, int norm_kind,
+                         uint16_t* out, void* stream) {
+  clear_error();
+  PR_TRY(pr_validate_fp8(x_q, x_scales, scale_rows, W_q, w_scale, residual_inout, norm_w, eps, T,
+                         K, H, norm_kind, out));
+  pr_decision d;
+  PR_TRY(decide(T, K, H, PR_SINGLE_LAUNCH, &d));
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  PR_TRY(check_give_up(c));
+  if (T == 0) return PR_OK;
+  if (fault_injected()) return fail(PR_ERR_HIP, "injected launch failure (PR_FAULT_INJECT)");
+  // The tile the time model picks, with two waves per SIMD and one K group (the FP8 loop's
+  // only forms); the K-split pair form has no FP8 variant.
+  GemmCfg g = cfg_of(d);
+  if (g.split != 1)
+    return fail(PR_ERR_UNSUPPORTED, "the K-split pair form has no FP8 variant");
+  g.waves = 8;
+  g.kgroups = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool capturing = false;
+  PR_TRY(stream_capturing(s, &capturing));
+  c->capturing = capturing;
+  int rc = PR_OK;
+  out = resolve_out(c, out, T, H, &rc);
+  SingleWs ws;
+  if (rc == PR_OK) rc = single_workspace(c, g, T, K, H, &ws);
+  c->capturing = false;
+  if (rc != PR_OK) return rc;
+  ws.fault_mask = wait_fault_injected() ? 0x80000000u : 0u;
+  ws.spin_limit = spin_limit();
+  ws.host_flag = c->host_flag_dev;
+  const int gemma = norm_kind == PR_NORM_GEMMA;
+  const long long rows_per = ((1LL << 30) / K) / g.bm * g.bm;
+  for (long long r0 = 0; r0 < T; r0 += rows_per) {
+    const int rows = (int)std::min<long long>(rows_per, T - r0);
+    auto launch = [&](hipEvent_t t0, hipEvent_t t1) {
+      return launch_gemm_add_rmsnorm_fp8(x_q + r0 * K, W_q, residual_inout + r0 * H, norm_w,
+                                         out + r0 * H, ws, rows, H, K, g, x_scales, scale_rows,
+                                         (int)r0, w_scale, eps, gemma, s, t0, t1);
+    };
+    PR_TRY(capturing ? launch(nullptr, nullptr) : timed(c, 0, launch));
+  }
+  return PR_OK;
+}
+
 int pr_init(void) {
   clear_error();
   DevCtx* c = nullptr;
@@ -726,14 +836,14 @@ int pr_release_workspace(void) {
   PR_HIP(hipDeviceSynchronize());
   void** bufs[] = {reinterpret_cast<void**>(&c->slots), &c->conv,
                    reinterpret_cast<void**>(&c->out_ws), &c->row_slots,
-                   reinterpret_cast<void**>(&c->sync), &c->pair_flags, &c->xbuf};
+                   reinterpret_cast<void**>(&c->sync), &c->pair_flags, &c->xbuf, &c->row_amax};
   for (void** b : bufs) {
     if (*b != nullptr) PR_HIP(hipFree(*b));
     *b = nullptr;
   }
   c->slot_elems = 0;
   c->conv_bytes = c->out_ws_bytes = c->row_slots_bytes = c->sync_bytes = 0;
-  c->pair_flags_bytes = c->xbuf_bytes = 0;
+  c->pair_flags_bytes = c->xbuf_bytes = c->row_amax_bytes = 0;
   c->last_borrowed = nullptr;
   c->prev_caller = nullptr;
   c->prev_done_slots[0] = c->prev_done_slots[1] = -1;
