@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -407,6 +408,53 @@ def conventional_addnorm_flushed(pr, torch, x, Wp, r, w, out, d, wl, steps, stre
             "frac": gbs / PEAK_HBM_GBS, "calls": len(ts)}
 
 
+def fp8_entry(pr, torch, x, W_src, r, w, out, d, norm_kind, scale_rows, args, stream) -> dict:
+    """The same region with the FP8 (OCP E4M3) projection.  Load time (untimed): the weight is
+    quantised with one per-tensor scale and laid out for the matrix cores.  A step: the
+    activations quantised with one scale per `scale_rows` tokens, then the FP8 single launch.
+    The kernel's own duration comes from the library's events; its rate is priced against the
+    dense fp8 peak."""
+    T, K, H = d["T"], d["K"], d["H"]
+    dev = r.device
+    wq = torch.empty((H, K), dtype=torch.uint8, device=dev)
+    sw = torch.empty(1, dtype=torch.float32, device=dev)
+    pr.pr_quantize_fp8(W_src, wq, sw, H, K, H, stream)
+    Wp8 = torch.empty(K * H, dtype=torch.uint8, device=dev)
+    pr.pr_prepare_weight_fp8(wq, pr.PR_WEIGHT_OUT_IN, Wp8, K, H, stream)
+    xq = torch.empty((T, K), dtype=torch.uint8, device=dev)
+    sx = torch.empty(((T - 1) // scale_rows + 1,), dtype=torch.float32, device=dev)
+
+    def step():
+        pr.pr_quantize_fp8(x, xq, sx, T, K, scale_rows, stream)
+        pr.proj_add_rmsnorm_fp8(xq, sx, scale_rows, Wp8, sw, r, w, d["eps"], T, K, H, norm_kind,
+                                out, stream)
+
+    steps = max(args.steps, 5)
+    el = time_steps(step, steps, max(args.warmup, 2), torch)
+    pr.pr_profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    prof = pr.pr_profile_read()
+    pr.pr_profile_enable(False)
+    if pr.pr_device_status(stream) != 0:
+        raise SystemExit("FP8 single-launch status bits set: a row wait gave up")
+    flops = 2.0 * T * K * H
+    k_s = prof["gemm_ms"] / max(prof["gemm_launches"], 1) / 1e3
+    res = {"format": "OCP E4M3 (x per-group and W per-tensor fp32 scales)",
+           "scale_rows": scale_rows, "ms_per_step": el * 1e3 / steps,
+           "tokens_per_s": T * steps / el, "step_tflops": flops * steps / el / 1e12,
+           "kernel": "gemm_add_rmsnorm_kernel (FP8)", "kernel_avg_us": k_s * 1e6,
+           "kernel_tflops": flops / k_s / 1e12, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+           "frac": flops / k_s / 1e12 / PEAK_FP8_TFLOPS,
+           "quantize_us_per_step": max(el / steps - k_s, 0.0) * 1e6}
+    log(f"fp8: {res['ms_per_step']:.4f} ms/step (quantise + single launch), kernel "
+        f"{res['kernel_avg_us']:.1f} us = {res['kernel_tflops']:.0f} TFLOP/s, "
+        f"{res['frac']:.3f} of the fp8 peak")
+    del wq, sw, Wp8, xq, sx
+    return res
+
+
 def down_proj_entry(pr, torch, args, stream) -> dict:
     """The second 4096-class prefill shape, down_proj (T=4096, K=14336, H=4096, x = silu(a)*b):
     the single launch and the conventional path, timed back to back (the two series
@@ -421,7 +469,6 @@ def down_proj_entry(pr, torch, args, stream) -> dict:
     W_src = torch.from_numpy(d["W"].view(np.int16)).to(dev)
     Wp = torch.empty(K * H, dtype=torch.int16, device=dev)
     pr.pr_prepare_weight(W_src, pr.PR_WEIGHT_OUT_IN, Wp, K, H)
-    del W_src
     r = torch.from_numpy(d["residual"]).to(dev)
     w = torch.from_numpy(d["norm_w"]).to(dev)
     out = torch.empty((T, H), dtype=torch.int16, device=dev)
@@ -454,6 +501,8 @@ def down_proj_entry(pr, torch, args, stream) -> dict:
            "kernel_frac": flops / k_s / 1e12 / PEAK_BF16_TFLOPS,
            "tile": f"{c['gemm_bm']}x{c['gemm_bn']} {c['gemm_waves']} waves",
            "conventional_ms": t_c * 1e3, "conventional_tflops": flops / t_c / 1e12}
+    res["fp8"] = fp8_entry(pr, torch, x, W_src, r, w, out, d, wl.norm_kind, 512, args, stream)
+    del W_src
     log(f"down_proj: single launch {res['single_launch_ms']:.4f} ms ({res['tflops']:.0f} "
         f"TFLOP/s, kernel {res['kernel_avg_us']:.1f} us = {res['kernel_frac']:.3f} of peak), "
         f"conventional {res['conventional_ms']:.4f} ms")
@@ -468,8 +517,9 @@ XGMI_LINK_GBS = 153.0   # one xGMI link, per direction
 def tp_share(pr, torch, args) -> int:
     """One rank's share of the row-parallel projection region under tensor parallelism of
     degree P, measured on this GPU: the projection of all T (or one chunk of mc) tokens over the
-    rank's K/P input columns into an fp32 partial, and the add/norm of the rank's T/P (mc/P)
-    token shard summing P fp32 partials in rank order.  The reduce-scatter of the partials and
+    rank's K/P input columns into an fp32 partial (pr_project_partial; beside it the library's
+    own tile and K split through the fused entry point), and the add/norm of the rank's T/P
+    (mc/P) token shard summing P fp32 partials in rank order (pr_add_rmsnorm_partials).  The reduce-scatter of the partials and
     the all-gather of the bf16 output between them are modelled, not run: a one-shot exchange
     in which every rank sends each peer its shard over that peer's own xGMI link."""
     import synth
@@ -521,15 +571,15 @@ def tp_share(pr, torch, args) -> int:
                                                out)
             auto_split = pr.pr_select(mc, kp, H, mc)["split_k"]
             t_auto = per_launch(call, "gemm")
-            os.environ["PR_FORCE_SPLIT"] = "1"
-            t_proj = per_launch(call, "gemm")
-            # add/norm share: mc/P rows, P fp32 partials (a minimal projection produces them)
+            y_part = torch.empty((P, mc, H), dtype=torch.float32, device=dev)
+            t_proj = per_launch(lambda: pr.pr_project_partial(x, Wp, y_part[0], mc, kp, H),
+                                "gemm")
+            # add/norm share: the owner's mc/P rows summing the P fp32 partials in rank order
             rows = mc // P
-            os.environ["PR_FORCE_SPLIT"] = str(P)
-            d, x, Wp, r, w, out = device_inputs(rows, 64 * P)
-            t_an = per_launch(lambda: pr.proj_add_rmsnorm(x, Wp, r, w, d["eps"], rows, 64 * P, H,
-                                                          rows, wl.norm_kind, out), "addnorm")
-            os.environ.pop("PR_FORCE_SPLIT", None)
+            t_an = per_launch(lambda: pr.pr_add_rmsnorm_partials(y_part, P, mc * H, r, w,
+                                                                 d["eps"], rows, H, wl.norm_kind,
+                                                                 out), "addnorm")
+            del y_part
             rs_fp32 = (P - 1) and rows * H * 4 / (XGMI_LINK_GBS * 1e3)  # us per link
             rs_bf16 = (P - 1) and rows * H * 2 / (XGMI_LINK_GBS * 1e3)
             ag_bf16 = (P - 1) and rows * H * 2 / (XGMI_LINK_GBS * 1e3)
@@ -589,7 +639,6 @@ def main() -> int:
     r = torch.from_numpy(d["residual"]).to(dev)
     w = torch.from_numpy(d["norm_w"]).to(dev)
     out = torch.empty((T, H), dtype=torch.int16, device=dev)
-    del W_src
     torch.cuda.synchronize()
     # All timed work runs on one dedicated stream (the legacy null stream adds host-side
     # synchronisation to every event record on it).
@@ -728,6 +777,8 @@ def main() -> int:
     if not args.only_single:
         result["addnorm_conventional"] = conventional_addnorm_flushed(
             pr, torch, x, Wp, r, w, out, d, wl, args.steps, stream)
+        result["fp8"] = fp8_entry(pr, torch, x, W_src, r, w, out, d, wl.norm_kind,
+                                  min(wl.microchunks), args, stream)
         if wl.name == "o_proj":
             result["down_proj"] = down_proj_entry(pr, torch, args, stream)
     if args.copy_calibration:
@@ -737,6 +788,7 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    del W_src
     if not args.no_cpu_baseline:
         log(f"timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
         result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)

@@ -200,6 +200,43 @@ int proj_add_rmsnorm_single_launch(const uint16_t* x, const uint16_t* W, float* 
                                    int norm_kind, uint16_t* out, void* stream);
 
 /* ---------------------------------------------------------------------------------------- *
+ * One rank's share under tensor parallelism, on one GPU ("TPSP Design" section 1 Motivation:
+ * with a row-parallel projection each rank holds a slice of the input columns and of the
+ * weight, its projection gives a partial sum of y, a reduce-scatter leaves each rank the
+ * summed rows of its token shard, and each rank normalises about T/P tokens; section 3
+ * Microchunk pipeline: the same per microchunk).  The collectives themselves are not part of
+ * this library; these are the two computations on either side of them.
+ * ---------------------------------------------------------------------------------------- */
+
+/*
+ * The rank's projection share: y_partial = x . W_slice^T with fp32 accumulation, unrounded.
+ * x          [T][K] bf16: the rank's K input columns of the T tokens (K = the full input size /
+ *            P), device, read.
+ * W          the matching [H][K] column slice of the weight, prepared by pr_prepare_weight.
+ * y_partial  [T][H] fp32, device, written (one plane: no K split inside the call).
+ * K, H positive multiples of 64; 16-byte aligned; y_partial must not overlap x or W.
+ * Asynchronous on `stream`; T = 0 is a no-op.  Errors: PR_ERR_SHAPE, PR_ERR_INVALID_ARG,
+ * PR_ERR_HIP.
+ */
+int pr_project_partial(const uint16_t* x, const uint16_t* W, float* y_partial, int T, int K,
+                       int H, void* stream);
+
+/*
+ * The owner's step after the reduce-scatter, for its `rows` tokens:
+ *     r[t,h] <- r[t,h] + (partial_0 + partial_1 + ... + partial_{P-1})[t,h]  (fp32, rank order)
+ *     out    =  RMSNorm(r) as for proj_add_rmsnorm.
+ * partials        P planes of [rows][H] fp32, plane p at partials + p * plane_stride (elements;
+ *                 plane_stride >= rows * H, a multiple of 4), device, read.
+ * residual_inout  [rows][H] fp32 (the rank's token shard), read and updated in place.
+ * norm_w, eps, norm_kind as proj_add_rmsnorm; out [rows][H] bf16 (not NULL).
+ * The written buffers must not overlap the others.  Asynchronous on `stream`; rows = 0 is a
+ * no-op.  Errors: PR_ERR_SHAPE, PR_ERR_INVALID_ARG, PR_ERR_HIP.
+ */
+int pr_add_rmsnorm_partials(const float* partials, int P, long long plane_stride,
+                            float* residual_inout, const float* norm_w, float eps, int rows,
+                            int H, int norm_kind, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------------------- *
  * FP8 projections ("TPSP Design" section 5 To-do: quantized projections, with their scales
  * handled across microchunks).  The format is OCP E4M3 (sign, 4 exponent bits with bias 7, 3
  * mantissa bits, no infinities, S.1111.111 the only NaN, largest finite 448), the format the

@@ -77,6 +77,9 @@ SIGNATURES = {
     "proj_add_rmsnorm_single_launch_noalloc": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp,
                                                    _vp]),
     "pr_init": (_i, []),
+    "pr_project_partial": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
+    "pr_add_rmsnorm_partials": (_i, [_vp, _i, _c.c_longlong, _vp, _vp, _f, _i, _i, _i, _vp,
+                                     _vp]),
     "pr_quantize_fp8": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "pr_prepare_weight_fp8": (_i, [_vp, _i, _vp, _i, _i, _vp]),
     "proj_add_rmsnorm_fp8": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp,
@@ -227,6 +230,27 @@ def proj_add_rmsnorm_single_launch_noalloc(x, W, residual_inout, norm_w, eps: fl
     _check(_lib().proj_add_rmsnorm_single_launch_noalloc(px, pw, pr_, pn, eps, T, K, H,
                                                          norm_kind, po,
                                                          _stream(stream, x, residual_inout)))
+
+
+def pr_project_partial(x, W, y_partial, T: int, K: int, H: int, stream=None) -> None:
+    """One rank's projection share: y_partial [T][H] fp32 = x [T][K] . W_slice^T."""
+    T_, K_, H_ = max(T, 0), max(K, 0), max(H, 0)
+    _check(_lib().pr_project_partial(_ptr(x, 2 * T_ * K_, "x"), _ptr(W, 2 * K_ * H_, "W"),
+                                     _ptr(y_partial, 4 * T_ * H_, "y_partial"), T, K, H,
+                                     _stream(stream, x)))
+
+
+def pr_add_rmsnorm_partials(partials, P: int, plane_stride: int, residual_inout, norm_w,
+                            eps: float, rows: int, H: int, norm_kind: int = PR_NORM_STANDARD,
+                            out=None, stream=None) -> None:
+    """The owner's add/norm after a reduce-scatter: r += sum of P fp32 partials (rank order)."""
+    rows_, H_ = max(rows, 0), max(H, 0)
+    need = 4 * ((max(P, 1) - 1) * plane_stride + rows_ * H_) if rows_ else 0
+    _check(_lib().pr_add_rmsnorm_partials(
+        _ptr(partials, need, "partials"), P, plane_stride,
+        _ptr(residual_inout, 4 * rows_ * H_, "residual_inout"), _ptr(norm_w, 4 * H_, "norm_w"),
+        eps, rows, H, norm_kind, _ptr(out, 2 * rows_ * H_, "out"),
+        _stream(stream, partials, residual_inout)))
 
 
 def pr_quantize_fp8(src, dst, scales, rows: int, cols: int, group_rows: int,

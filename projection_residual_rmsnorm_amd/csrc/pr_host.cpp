@@ -179,6 +179,22 @@ GemmCfg choose_gemm(int M, int N, int K, bool fp32_out) {
   return best;
 }
 
+// One fp32 output plane (no K split): the modelled fastest tile with split 1.
+GemmCfg choose_gemm_unsplit(int M, int N, int K) {
+  GemmCfg best;
+  best.waves = 8;
+  double best_t = std::numeric_limits<double>::infinity();
+  for (int c = 0; c < kNumTileCfgs; ++c) {
+    const double t = model_gemm_time(M, N, K, c, 1, true, kNumCUs);
+    if (t < best_t * 0.999) {
+      best_t = t;
+      best.bm = kTileBM[c];
+      best.bn = kTileBN[c];
+    }
+  }
+  return best;
+}
+
 // Tile of the single-launch path: the modelled fastest tile whose columns divide H into at most
 // 64 tile columns (the kernel's row-partial limit); bm = 0 if there is none.  A 256 x 128 tile
 // grid that fits in one round runs with 4 waves per workgroup (measured on 2048 x 4096 x 4096:

@@ -31,6 +31,8 @@ constexpr int kTileBN[kNumTileCfgs] = {256, 128, 128};
 // Cost-model choice of tile and split for an M x N x K projection.  `fp32_out` is true when the
 // projection result is kept in fp32 (the pipeline's slot), false when it is emitted in bf16.
 GemmCfg choose_gemm(int M, int N, int K, bool fp32_out);
+// The same choice restricted to one K partition (a single fp32 output plane).
+GemmCfg choose_gemm_unsplit(int M, int N, int K);
 // Modelled time (seconds) of the projection of M x N x K with tile configuration c (index into
 // kTileBM/kTileBN) and K split, including the add/norm's read of its output, when it has `cus`
 // CUs and that share of the chip's power to itself (kNumCUs: alone on the GPU).

@@ -753,6 +753,73 @@ int proj_add_rmsnorm_fp8(const uint8_t* x_q, const float* x_scales, int scale_ro
   return PR_OK;
 }
 
+int pr_project_partial(const uint16_t* x, const uint16_t* W, float* y_partial, int T, int K,
+                       int H, void* stream) {
+  clear_error();
+  if (T < 0 || K <= 0 || H <= 0 || K % 64 != 0 || H % 64 != 0)
+    return fail(PR_ERR_SHAPE, "T=%d must be >= 0 and K=%d, H=%d positive multiples of 64", T, K,
+                H);
+  if ((long long)K * H > (1LL << 30) || (long long)T * H > (1LL << 40))
+    return fail(PR_ERR_SHAPE, "sizes too large");
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  PR_TRY(check_give_up(c));
+  if (T == 0) return PR_OK;
+  if (x == nullptr || W == nullptr || y_partial == nullptr)
+    return fail(PR_ERR_INVALID_ARG, "null tensor pointer");
+  if ((uintptr_t)x % 16 != 0 || (uintptr_t)W % 16 != 0 || (uintptr_t)y_partial % 16 != 0)
+    return fail(PR_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const uintptr_t y0 = (uintptr_t)y_partial, y1 = y0 + 4ULL * T * H;
+  const uintptr_t x0 = (uintptr_t)x, x1 = x0 + 2ULL * T * K;
+  const uintptr_t w0 = (uintptr_t)W, w1 = w0 + 2ULL * K * H;
+  if ((y0 < x1 && x0 < y1) || (y0 < w1 && w0 < y1))
+    return fail(PR_ERR_INVALID_ARG, "y_partial overlaps x or W");
+  const GemmCfg g = choose_gemm_unsplit(T, H, K);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
+    return gemm_rows(x, W, y_partial, false, T, H, K, g, (long long)T * H, s, nullptr, t0, t1);
+  });
+}
+
+int pr_add_rmsnorm_partials(const float* partials, int P, long long plane_stride,
+                            float* residual_inout, const float* norm_w, float eps, int rows,
+                            int H, int norm_kind, uint16_t* out, void* stream) {
+  clear_error();
+  if (rows < 0 || H <= 0 || H % 64 != 0)
+    return fail(PR_ERR_SHAPE, "rows=%d must be >= 0 and H=%d a positive multiple of 64", rows, H);
+  if (P < 1 || plane_stride < (long long)rows * H)
+    return fail(PR_ERR_INVALID_ARG, "P=%d must be >= 1 and plane_stride=%lld >= rows * H", P,
+                plane_stride);
+  if (norm_kind != PR_NORM_STANDARD && norm_kind != PR_NORM_GEMMA)
+    return fail(PR_ERR_INVALID_ARG, "unknown norm_kind %d", norm_kind);
+  if (!(eps >= 0.0f) || std::isinf(eps)) return fail(PR_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  PR_TRY(check_give_up(c));
+  if (rows == 0) return PR_OK;
+  if (partials == nullptr || residual_inout == nullptr || norm_w == nullptr || out == nullptr)
+    return fail(PR_ERR_INVALID_ARG, "null tensor pointer");
+  const uintptr_t a[4] = {(uintptr_t)partials, (uintptr_t)residual_inout, (uintptr_t)norm_w,
+                          (uintptr_t)out};
+  for (uintptr_t p : a)
+    if (p % 16 != 0 || (plane_stride * 4) % 16 != 0)
+      return fail(PR_ERR_INVALID_ARG, "pointers and the plane stride must be 16-byte aligned");
+  struct R { uintptr_t lo, hi; };
+  const R rp{(uintptr_t)partials, (uintptr_t)partials + 4ULL * ((P - 1) * plane_stride +
+                                                             (long long)rows * H)};
+  const R rr{(uintptr_t)residual_inout, (uintptr_t)residual_inout + 4ULL * rows * H};
+  const R rn{(uintptr_t)norm_w, (uintptr_t)norm_w + 4ULL * H};
+  const R ro{(uintptr_t)out, (uintptr_t)out + 2ULL * rows * H};
+  auto ov = [](const R& u, const R& v) { return u.lo < v.hi && v.lo < u.hi; };
+  if (ov(rr, rp) || ov(rr, rn) || ov(ro, rp) || ov(ro, rr) || ov(ro, rn))
+    return fail(PR_ERR_INVALID_ARG, "the residual or out overlaps another buffer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(c, 1, [&](hipEvent_t t0, hipEvent_t t1) {
+    return launch_add_rmsnorm(partials, 0, P, plane_stride, 0, residual_inout, norm_w, out, rows,
+                              H, eps, norm_kind == PR_NORM_GEMMA, 0, s, nullptr, t0, t1);
+  });
+}
+
 int pr_init(void) {
   clear_error();
   DevCtx* c = nullptr;
