@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--silu-mul", action="store_true",
                     help="HBM rate of the SiluAndMul kernel (down_proj and Gemma intermediate "
                          "sizes, warm and flushed) and the down_proj block it opens")
+    ap.add_argument("--cu-split", default="",
+                    help="comma-separated CU counts reserved for the add/norm stream (0 = the "
+                         "ping-pong schedule): time the pipeline of the workload at each chunk "
+                         "size and split, round-robin, and print the table")
     ap.add_argument("--tp-share", default="",
                     help="comma-separated tensor-parallel degrees P: time one rank's share of "
                          "the workload (projection over K/P, add/norm of T/P rows with P fp32 "
@@ -511,6 +515,55 @@ def down_proj_entry(pr, torch, args, stream) -> dict:
     return res
 
 
+def cu_split_table(pr, torch, args) -> int:
+    """The CU-partitioned pipeline against the ping-pong one: for each chunk size of the
+    workload and each split (CUs reserved for the add/norm stream; 0 = ping-pong), the call
+    time of back-to-back calls.  The splits of one chunk size are timed in rounds, one series
+    of `steps` calls each per round, five rounds, medians (clock drift cancels)."""
+    import synth
+    wl = synth.WORKLOADS[args.workload]
+    T, K, H = wl.T, wl.K, wl.H
+    dev = "cuda:0"
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    d = synth.make_inputs(wl, seed=0)
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+    W_src = torch.from_numpy(d["W"].view(np.int16)).to(dev)
+    Wp = torch.empty(K * H, dtype=torch.int16, device=dev)
+    pr.pr_prepare_weight(W_src, pr.PR_WEIGHT_OUT_IN, Wp, K, H)
+    r = torch.from_numpy(d["residual"]).to(dev)
+    w = torch.from_numpy(d["norm_w"]).to(dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    splits = [int(v) for v in args.cu_split.split(",") if v != ""]
+    if len(splits) > 2 or (len(splits) == 2 and 0 not in splits):
+        raise SystemExit("--cu-split takes one split, or 0 and one split: the library keeps one "
+                         "CU-masked stream pair per device (run one process per split)")
+    rows = []
+    conv = lambda: pr.proj_add_rmsnorm_unfused(x, Wp, r, w, d["eps"], T, K, H, wl.norm_kind, out)
+    t_conv = float(np.median([time_steps(conv, args.steps, args.warmup, torch) / args.steps
+                              for _ in range(3)]))
+    for mc in wl.microchunks:
+        series = {n: [] for n in splits}
+        for _ in range(5):
+            for n in splits:
+                os.environ["PR_FORCE_CU_SPLIT"] = str(n)
+                call = lambda: pr.proj_add_rmsnorm(x, Wp, r, w, d["eps"], T, K, H, mc,
+                                                   wl.norm_kind, out)
+                series[n].append(time_steps(call, args.steps, args.warmup, torch) / args.steps)
+        for n in splits:
+            os.environ["PR_FORCE_CU_SPLIT"] = str(n)
+            c = pr.pr_select(T, K, H, mc)
+            t = float(np.median(series[n]))
+            cfg = f"{c['gemm_bm']}x{c['gemm_bn']} split {c['split_k']}"
+            rows.append({"mc": mc, "addnorm_cus": n, "ms": t * 1e3, "chunk_projection": cfg})
+            log(f"mc={mc} split {n}: {t * 1e3:.4f} ms ({cfg})")
+        os.environ.pop("PR_FORCE_CU_SPLIT", None)
+    log(f"conventional: {t_conv * 1e3:.4f} ms")
+    print(json.dumps({"cu_split": {"workload": wl.name, "T": T, "K": K, "H": H,
+                                   "conventional_ms": t_conv * 1e3, "rows": rows}}), flush=True)
+    return 0
+
+
 XGMI_LINK_GBS = 153.0   # one xGMI link, per direction
 
 
@@ -623,6 +676,8 @@ def main() -> int:
         return tune_sweep(pr, torch, args)
     if args.tp_share:
         return tp_share(pr, torch, args)
+    if args.cu_split:
+        return cu_split_table(pr, torch, args)
     if args.addnorm_roofline:
         return addnorm_roofline(pr, torch, args)
     if args.silu_mul:

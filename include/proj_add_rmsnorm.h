@@ -385,6 +385,9 @@ typedef struct {
   int gemm_kgroups; /* K groups inside a projection workgroup (1, or 2 for the single
                        launch's 256x128 tile with 8 waves: two groups of 4 waves each
                        computing the tile over alternate 32-deep halves of K)          */
+  int addnorm_cus;  /* fused pipeline: CUs reserved for the add/norm stream (the
+                       CU-partitioned schedule of pr_plan_cu_split); 0 = the two-stream
+                       ping-pong schedule of pr_plan                                    */
 } pr_decision;
 
 #define PR_REASON_EXPLICIT 0          /* microchunk > 0 given by the caller            */
@@ -429,9 +432,25 @@ typedef struct {
 #define PR_OP_JOIN 6         /* caller stream: wait done[slot] of the library stream's last */
 #define PR_OP_WAIT_PREV 7    /* caller stream: wait for the previous call's last chunks when
                                 that call was made on a different caller stream            */
+#define PR_OP_RECORD_READY 8 /* record ready[slot] after the chunk's projection             */
+#define PR_OP_WAIT_READY 9   /* wait ready[slot] before the chunk's add/norm                */
 #define PR_NUM_SLOTS 3
 
 int pr_plan(int T, int microchunk, pr_plan_op* ops, int max_ops);
+
+/*
+ * Dry-run schedule of the CU-partitioned pipeline ("TPSP Design" section 3, Profiling and
+ * fallback: the microchunk size is tuned together with SM-count targets; on MI355X the target
+ * is a CU mask on each stream).  Stream 1 is a library stream restricted to the projection's
+ * CUs and runs every chunk's projection; stream 2 is a library stream restricted to the CUs
+ * reserved for the add/norm and runs every chunk's add/norm, so chunk c+1's projection and
+ * chunk c's add/norm run on disjoint CUs at the same time.  Slot s = c % 3: the projection
+ * records ready[s], the add/norm waits for it and records done[s], and chunk c+3's projection
+ * waits for done[s] before it overwrites the slot.  Both streams start after the caller's
+ * prior work (entry event) and the caller's stream waits for the last chunk's done (join).
+ * Same return convention as pr_plan; stream ids 0 (caller), 1 and 2.
+ */
+int pr_plan_cu_split(int T, int microchunk, pr_plan_op* ops, int max_ops);
 
 /* ---------------------------------------------------------------------------------------- *
  * Token-threshold tuning ("TPSP Design" section 3, Profiling and fallback)
@@ -467,6 +486,15 @@ int pr_set_tuning(int K, int H, int threshold_tokens, int max_tokens, const int*
  * PR_ERR_INVALID_ARG. */
 int pr_set_chunk_config(int K, int H, int microchunk, int tile_m, int tile_n, int split_k,
                         int waves);
+
+/* Install the CU split of the fused pipeline for the shape group (K, H) with this microchunk:
+ * addnorm_cus CUs (a multiple of 8 from 8 to 128, spread evenly over the 8 XCDs) run the
+ * add/norms and the other CUs the projections, on two CU-masked library streams
+ * (pr_plan_cu_split); 0 selects the two-stream ping-pong schedule of pr_plan.  The chunk's
+ * projection configuration is kept (the time model's when none was installed).  The result is
+ * bitwise the same for every split (same kernels, same configurations).  Errors:
+ * PR_ERR_SHAPE, PR_ERR_MICROCHUNK, PR_ERR_INVALID_ARG. */
+int pr_set_cu_split(int K, int H, int microchunk, int addnorm_cus);
 
 /* Remove every installed tuning result and chunk configuration. */
 void pr_clear_tuning(void);
@@ -509,8 +537,12 @@ typedef struct {
  * the GPU and its three best with half the GPU (the other stream's chunk runs alongside), each
  * with 8 and 4 waves, are checked and timed round-robin in the pipeline at
  * T = min(max T_grid, 4 x chunk size), and the fastest that passes is installed with
- * pr_set_chunk_config, the model's first choice standing unless beaten by more than 3%
- * (skipped when a PR_FORCE_* override is set).  Installs the result with pr_set_tuning for
+ * pr_set_chunk_config, the model's first choice standing unless beaten by more than 3%; then,
+ * with that configuration, the CU split of the chunk size (the page tunes SM-count targets
+ * jointly with the microchunk): the ping-pong schedule and the CU-partitioned one with 32 and
+ * 64 CUs reserved for the add/norms are checked and timed round-robin at the same T, and a
+ * split is installed with pr_set_cu_split only if it beats the ping-pong schedule by more than
+ * 3% (both steps skipped when a PR_FORCE_* override is set).  Installs the result with pr_set_tuning for
  * every group (chunk value PR_SINGLE_LAUNCH where the single launch is the fastest fused
  * candidate).  timings_out (optional): [ngroups][nT][3 + nmc] seconds: conventional, best
  * fused, each chunk size in mc_cand order, then the single launch; <= 0 for skipped or

@@ -37,7 +37,7 @@ PR_NUM_SLOTS = 3
 INT32_MAX = 2**31 - 1
 
 OP_NAMES = ["RECORD_ENTRY", "WAIT_ENTRY", "WAIT_DONE", "GEMM", "ADDNORM", "RECORD_DONE", "JOIN",
-            "WAIT_PREV"]
+            "WAIT_PREV", "RECORD_READY", "WAIT_READY"]
 REASON_NAMES = ["explicit", "above_threshold", "below_threshold", "untuned", "inconclusive",
                 "unfused_call", "single_call"]
 
@@ -49,7 +49,8 @@ _vp, _i, _f, _d = _c.c_void_p, _c.c_int, _c.c_float, _c.c_double
 class pr_decision(_c.Structure):
     _fields_ = [("path", _i), ("microchunk", _i), ("n_chunks", _i), ("last_valid", _i),
                 ("gemm_bm", _i), ("gemm_bn", _i), ("split_k", _i), ("gemm_waves", _i),
-                ("reason", _i), ("gemm_stages", _i), ("gemm_kgroups", _i)]
+                ("reason", _i), ("gemm_stages", _i), ("gemm_kgroups", _i),
+                ("addnorm_cus", _i)]
 
 
 class pr_plan_op(_c.Structure):
@@ -91,6 +92,8 @@ SIGNATURES = {
     "pr_validate": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _i, _vp]),
     "pr_select": (_i, [_i, _i, _i, _i, _c.POINTER(pr_decision)]),
     "pr_plan": (_i, [_i, _i, _c.POINTER(pr_plan_op), _i]),
+    "pr_plan_cu_split": (_i, [_i, _i, _c.POINTER(pr_plan_op), _i]),
+    "pr_set_cu_split": (_i, [_i, _i, _i, _i]),
     "pr_threshold_from_timings": (_i, [_i, _i, _c.POINTER(_i), _c.POINTER(_d), _c.POINTER(_d),
                                        _c.POINTER(_d), _c.POINTER(_i)]),
     "pr_set_tuning": (_i, [_i, _i, _i, _i, _c.POINTER(_i), _c.POINTER(_i), _i]),
@@ -318,13 +321,27 @@ def pr_select(T: int, K: int, H: int, microchunk: int) -> dict:
     return {f: getattr(d, f) for f, _ in pr_decision._fields_}
 
 
-def pr_plan(T: int, microchunk: int) -> List[Tuple[str, int, int, int, int]]:
-    n = _lib().pr_plan(T, microchunk, None, 0)
+def _plan(fn, T: int, microchunk: int) -> List[Tuple[str, int, int, int, int]]:
+    n = fn(T, microchunk, None, 0)
     if n < 0:
         _check(n)
     ops = (pr_plan_op * max(n, 1))()
-    _check(0 if _lib().pr_plan(T, microchunk, ops, n) == n else PR_ERR_INVALID_ARG)
+    _check(0 if fn(T, microchunk, ops, n) == n else PR_ERR_INVALID_ARG)
     return [(OP_NAMES[o.op], o.stream, o.chunk, o.slot, o.rows) for o in ops[:n]]
+
+
+def pr_plan(T: int, microchunk: int) -> List[Tuple[str, int, int, int, int]]:
+    """The ping-pong pipeline's schedule: (op, stream, chunk, slot, rows) in host order."""
+    return _plan(_lib().pr_plan, T, microchunk)
+
+
+def pr_plan_cu_split(T: int, microchunk: int) -> List[Tuple[str, int, int, int, int]]:
+    """The CU-partitioned pipeline's schedule (streams 0 caller, 1 projections, 2 add/norms)."""
+    return _plan(_lib().pr_plan_cu_split, T, microchunk)
+
+
+def pr_set_cu_split(K: int, H: int, microchunk: int, addnorm_cus: int) -> None:
+    _check(_lib().pr_set_cu_split(K, H, microchunk, addnorm_cus))
 
 
 def pr_threshold_from_timings(T_grid: Sequence[int], t_conv, t_fused, spread=None) -> int:

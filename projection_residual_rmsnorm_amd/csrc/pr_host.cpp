@@ -160,14 +160,14 @@ double model_gemm_time(int M, int N, int K, int c, int split, bool fp32_out, int
   return t + y_bytes / kWriteBW + y_bytes / kReadBW;
 }
 
-GemmCfg choose_gemm(int M, int N, int K, bool fp32_out) {
+GemmCfg choose_gemm(int M, int N, int K, bool fp32_out, int cus) {
   GemmCfg best;
   best.waves = 8;
   double best_t = std::numeric_limits<double>::infinity();
   for (int c = 0; c < kNumTileCfgs; ++c) {
     for (int split = 1; split <= 16; split *= 2) {
       if (K % (64 * split) != 0) break;
-      const double t = model_gemm_time(M, N, K, c, split, fp32_out, kNumCUs);
+      const double t = model_gemm_time(M, N, K, c, split, fp32_out, cus);
       if (t < best_t * 0.999) {
         best_t = t;
         best.bm = kTileBM[c];
@@ -218,6 +218,10 @@ GemmCfg choose_single(int M, int N, int K) {
     best.waves = 4;
   return best;
 }
+
+// A CU split of the pipeline: 0 (no partition) or a multiple of 8 CUs (whole CUs on every XCD)
+// up to half the GPU.
+bool valid_cu_split(int n) { return n == 0 || (n >= 8 && n <= 128 && n % 8 == 0); }
 
 // ---------------------------------------------------------------------------------------------
 // Per-call decision.
@@ -307,7 +311,22 @@ int decide(int T, int K, int H, int microchunk, pr_decision* d) {
         tuned = true;
       }
     }
-    if (!tuned) g = choose_gemm(eff, H, K, true);
+    // PR_FORCE_CU_SPLIT=<n>: the CU split of every pipeline call (tests, measurements).
+    const char* cs = std::getenv("PR_FORCE_CU_SPLIT");
+    if (cs != nullptr && cs[0] != '\0') {
+      const int n = std::atoi(cs);
+      if (!valid_cu_split(n))
+        return fail(PR_ERR_INVALID_ARG, "PR_FORCE_CU_SPLIT=%s must be 0 or a multiple of 8 in "
+                    "8..128", cs);
+      g.addnorm_cus = n;
+    }
+    // Untuned: the time model's configuration for the CUs the projections get.
+    if (!tuned) {
+      const int n = g.addnorm_cus;
+      g = choose_gemm(eff, H, K, true, kNumCUs - n);
+      g.addnorm_cus = n;
+    }
+    d->addnorm_cus = g.addnorm_cus;
   } else if (path == PR_PATH_SINGLE) {
     d->microchunk = T;
     d->n_chunks = T > 0 ? 1 : 0;
@@ -515,6 +534,46 @@ int pr_plan(int T, int microchunk, pr_plan_op* ops, int max_ops) {
   return n;
 }
 
+int pr_plan_cu_split(int T, int microchunk, pr_plan_op* ops, int max_ops) {
+  if (T < 0 || microchunk <= 0 || microchunk > PR_MAX_MICROCHUNK)
+    return fail(PR_ERR_INVALID_ARG, "pr_plan_cu_split needs T >= 0 and 0 < microchunk <= %d",
+                PR_MAX_MICROCHUNK);
+  if (max_ops < 0 || (max_ops > 0 && ops == nullptr))
+    return fail(PR_ERR_INVALID_ARG, "bad op buffer");
+  int n = 0;
+  auto emit = [&](int op, int stream, int chunk, int slot, int rows) {
+    if (n < max_ops) ops[n] = pr_plan_op{op, stream, chunk, slot, rows};
+    ++n;
+  };
+  if (T == 0) return 0;
+  const int nc = (T + microchunk - 1) / microchunk;
+  auto rows_of = [&](int c) { return std::min(microchunk, T - c * microchunk); };
+  emit(PR_OP_WAIT_PREV, 0, -1, -1, 0);
+  emit(PR_OP_RECORD_ENTRY, 0, -1, -1, 0);
+  emit(PR_OP_WAIT_ENTRY, 1, -1, -1, 0);
+  emit(PR_OP_WAIT_ENTRY, 2, -1, -1, 0);
+  auto addnorm = [&](int c) {
+    const int s = c % PR_NUM_SLOTS;
+    emit(PR_OP_WAIT_READY, 2, c, s, 0);
+    emit(PR_OP_ADDNORM, 2, c, s, rows_of(c));
+    // done[slot]: waited for by chunk c + 3's projection and, for the last chunk, by the join
+    // and by a next call made from another stream.
+    if (c + PR_NUM_SLOTS < nc || c == nc - 1) emit(PR_OP_RECORD_DONE, 2, c, s, 0);
+  };
+  // Host order: chunk c's projection (and its slot wait) before chunk c-1's add/norm, so the
+  // projection stream is fed ahead; a wait is enqueued after the record it waits for.
+  for (int c = 0; c < nc; ++c) {
+    const int s = c % PR_NUM_SLOTS;
+    if (c >= PR_NUM_SLOTS) emit(PR_OP_WAIT_DONE, 1, c, s, 0);
+    emit(PR_OP_GEMM, 1, c, s, rows_of(c));
+    emit(PR_OP_RECORD_READY, 1, c, s, 0);
+    if (c >= 1) addnorm(c - 1);
+  }
+  addnorm(nc - 1);
+  emit(PR_OP_JOIN, 0, nc - 1, (nc - 1) % PR_NUM_SLOTS, 0);
+  return n;
+}
+
 int pr_threshold_from_timings(int ngroups, int nT, const int* T_grid, const double* t_conv,
                               const double* t_fused, const double* spread, int* threshold) {
   if (ngroups <= 0 || nT <= 0 || T_grid == nullptr || t_conv == nullptr || t_fused == nullptr ||
@@ -585,7 +644,26 @@ int pr_set_chunk_config(int K, int H, int microchunk, int tile_m, int tile_n, in
   g.split = split_k;
   g.waves = waves;
   std::lock_guard<std::mutex> lk(g_tuning_mu);
+  auto it = g_chunk_cfg.find({K, H, microchunk});
+  if (it != g_chunk_cfg.end()) g.addnorm_cus = it->second.addnorm_cus;  // kept
   g_chunk_cfg[{K, H, microchunk}] = g;
+  return PR_OK;
+}
+
+int pr_set_cu_split(int K, int H, int microchunk, int addnorm_cus) {
+  if (K <= 0 || H <= 0 || K % 64 != 0 || H % 64 != 0)
+    return fail(PR_ERR_SHAPE, "K=%d and H=%d must be positive multiples of 64", K, H);
+  if (microchunk <= 0 || microchunk > PR_MAX_MICROCHUNK)
+    return fail(PR_ERR_MICROCHUNK, "microchunk=%d out of range", microchunk);
+  if (!valid_cu_split(addnorm_cus))
+    return fail(PR_ERR_INVALID_ARG, "addnorm_cus=%d must be 0 or a multiple of 8 in 8..128",
+                addnorm_cus);
+  std::lock_guard<std::mutex> lk(g_tuning_mu);
+  auto it = g_chunk_cfg.find({K, H, microchunk});
+  if (it == g_chunk_cfg.end())  // the model's configuration for the projections' CUs
+    it = g_chunk_cfg.emplace(std::make_tuple(K, H, microchunk),
+                             choose_gemm(microchunk, H, K, true, kNumCUs - addnorm_cus)).first;
+  it->second.addnorm_cus = addnorm_cus;
   return PR_OK;
 }
 
@@ -599,6 +677,7 @@ void pr_clear_tuning(void) {
 //   pr_tuning 1 <library version> <device key>
 //   tuning <K> <H> <threshold> <max tokens> <nT> then nT pairs <T> <chunk>
 //   chunk <K> <H> <microchunk> <tile rows> <tile columns> <K split> <waves>
+//   cusplit <K> <H> <microchunk> <add/norm CUs>         (after the chunk record it refines)
 int pr_tuning_save(const char* path, const char* device_key) {
   if (path == nullptr) return fail(PR_ERR_INVALID_ARG, "path is NULL");
   std::string key;
@@ -629,6 +708,12 @@ int pr_tuning_save(const char* path, const char* device_key) {
               " " + std::to_string(g.bm) + " " + std::to_string(g.bn) + " " +
               std::to_string(g.split) + " " + std::to_string(g.waves) + "\n";
     }
+    for (const auto& kv : g_chunk_cfg)
+      if (kv.second.addnorm_cus > 0)
+        text += "cusplit " + std::to_string(std::get<0>(kv.first)) + " " +
+                std::to_string(std::get<1>(kv.first)) + " " +
+                std::to_string(std::get<2>(kv.first)) + " " +
+                std::to_string(kv.second.addnorm_cus) + "\n";
   }
   FILE* f = std::fopen(path, "w");
   if (f == nullptr) return fail(PR_ERR_INVALID_ARG, "cannot write %s", path);
@@ -718,6 +803,8 @@ int pr_tuning_load(const char* path, const char* device_key) {
     } else if (tok[0] == "chunk" && v.size() == 7) {
       rc = pr_set_chunk_config((int)v[0], (int)v[1], (int)v[2], (int)v[3], (int)v[4], (int)v[5],
                                (int)v[6]);
+    } else if (tok[0] == "cusplit" && v.size() == 4) {
+      rc = pr_set_cu_split((int)v[0], (int)v[1], (int)v[2], (int)v[3]);
     } else {
       rc = fail(PR_ERR_INVALID_ARG, "%s line %zu: unknown or malformed record", path, ln + 1);
     }

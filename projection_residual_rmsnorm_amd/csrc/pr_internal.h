@@ -21,6 +21,7 @@ struct GemmCfg {
   int waves = 4;  // waves per workgroup: 4 (one per SIMD) or 8 (two per SIMD)
   int stages = 0; // LDS ring depth; 0 = the deepest the tile fits in LDS
   int kgroups = 1; // K groups inside the workgroup (single launch, 256x128 with 8 waves: 2)
+  int addnorm_cus = 0;  // pipeline: CUs reserved for the add/norm stream (0: ping-pong schedule)
 };
 
 // Tile configurations the library instantiates (rows x columns per workgroup).
@@ -28,9 +29,10 @@ constexpr int kNumTileCfgs = 3;
 constexpr int kTileBM[kNumTileCfgs] = {256, 256, 128};
 constexpr int kTileBN[kNumTileCfgs] = {256, 128, 128};
 
-// Cost-model choice of tile and split for an M x N x K projection.  `fp32_out` is true when the
-// projection result is kept in fp32 (the pipeline's slot), false when it is emitted in bf16.
-GemmCfg choose_gemm(int M, int N, int K, bool fp32_out);
+// Cost-model choice of tile and split for an M x N x K projection on `cus` CUs.  `fp32_out` is
+// true when the projection result is kept in fp32 (the pipeline's slot), false when it is
+// emitted in bf16.
+GemmCfg choose_gemm(int M, int N, int K, bool fp32_out, int cus = kNumCUs);
 // The same choice restricted to one K partition (a single fp32 output plane).
 GemmCfg choose_gemm_unsplit(int M, int N, int K);
 // Modelled time (seconds) of the projection of M x N x K with tile configuration c (index into

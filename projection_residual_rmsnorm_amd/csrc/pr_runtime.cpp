@@ -29,11 +29,22 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
+// A pair of CU-masked library streams for the CU-partitioned pipeline: `proj` may use every
+// CU but the `cus` reserved ones, `addnorm` only those (spread evenly over the XCDs).
+struct MaskedPair {
+  int cus = 0;
+  hipStream_t proj = nullptr;
+  hipStream_t addnorm = nullptr;
+};
+
 struct DevCtx {
   int device = -1;
   hipStream_t sL = nullptr;  // library stream (odd chunks)
   hipEvent_t entry = nullptr;
   hipEvent_t done[PR_NUM_SLOTS] = {};
+  hipEvent_t ready[PR_NUM_SLOTS] = {};  // CU-partitioned pipeline: projection -> add/norm
+  MaskedPair masked;  // at most one pair per device (a process has few hardware queues)
+  int cu_count = 0;
   float* slots = nullptr;  // PR_NUM_SLOTS slots of slot_elems fp32 each
   size_t slot_elems = 0;
   void* conv = nullptr;  // conventional path: bf16 y or fp32 partial planes
@@ -179,6 +190,8 @@ int get_ctx(DevCtx** out) {
   hipError_t e = hipStreamCreateWithFlags(&c->sL, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreate(&c->entry);
   for (int s = 0; s < PR_NUM_SLOTS && e == hipSuccess; ++s) e = hipEventCreate(&c->done[s]);
+  for (int s = 0; s < PR_NUM_SLOTS && e == hipSuccess; ++s) e = hipEventCreate(&c->ready[s]);
+  c->cu_count = prop.multiProcessorCount;
   if (e == hipSuccess) {
     void* hp = nullptr;
     e = hipHostMalloc(&hp, 64, hipHostMallocMapped | hipHostMallocCoherent);
@@ -191,8 +204,10 @@ int get_ctx(DevCtx** out) {
   if (e != hipSuccess) {
     // release what was created; the context is not kept
     if (c->host_flag != nullptr) (void)hipHostFree(c->host_flag);
-    for (int s = 0; s < PR_NUM_SLOTS; ++s)
+    for (int s = 0; s < PR_NUM_SLOTS; ++s) {
       if (c->done[s] != nullptr) (void)hipEventDestroy(c->done[s]);
+      if (c->ready[s] != nullptr) (void)hipEventDestroy(c->ready[s]);
+    }
     if (c->entry != nullptr) (void)hipEventDestroy(c->entry);
     if (c->sL != nullptr) (void)hipStreamDestroy(c->sL);
     return fail(PR_ERR_HIP, "creating the library stream and events on device %d: %s", dev,
@@ -262,6 +277,49 @@ int grow(DevCtx* c, void** p, size_t* have, size_t need) {
     return fail(PR_ERR_NOMEM, "workspace of %zu bytes: %s", need, hipGetErrorString(e));
   }
   *have = need;
+  return PR_OK;
+}
+
+// The CU-masked stream pair reserving `cus` CUs for the add/norm.  Mask bit i enables CU i of
+// the device's numbering, in which consecutive CUs lie on consecutive XCDs (checked on MI355X:
+// the top n bits give n / 8 CUs on every XCD), so the top `cus` bits reserve cus / 8 CUs per
+// XCD.  A CU mask belongs to a hardware queue and a process gets only a few of those, so a
+// device keeps one pair: a call with another split waits for the old pair's work, destroys it
+// and creates the new one (a tuning-time cost; steady-state calls reuse the pair).
+int masked_pair(DevCtx* c, int cus, MaskedPair** out) {
+  MaskedPair* slot = &c->masked;
+  if (slot->proj != nullptr && slot->cus == cus) {
+    *out = slot;
+    return PR_OK;
+  }
+  if (c->capturing)
+    return fail(PR_ERR_UNSUPPORTED, "a CU-masked stream pair cannot be created under capture");
+  if (slot->proj != nullptr) {
+    PR_HIP(hipStreamSynchronize(slot->proj));
+    PR_HIP(hipStreamSynchronize(slot->addnorm));
+    PR_HIP(hipStreamDestroy(slot->proj));
+    PR_HIP(hipStreamDestroy(slot->addnorm));
+    *slot = MaskedPair();
+  }
+  const int n = c->cu_count;
+  if (cus <= 0 || cus >= n || n > 32 * 16)
+    return fail(PR_ERR_UNSUPPORTED, "CU split %d on a device of %d CUs", cus, n);
+  const int words = (n + 31) / 32;
+  std::vector<uint32_t> mp(words, 0), ma(words, 0);
+  for (int i = 0; i < n; ++i) {
+    std::vector<uint32_t>& m = i < n - cus ? mp : ma;
+    m[i / 32] |= 1u << (i % 32);
+  }
+  MaskedPair p;
+  p.cus = cus;
+  PR_HIP(hipExtStreamCreateWithCUMask(&p.proj, (uint32_t)words, mp.data()));
+  const hipError_t e = hipExtStreamCreateWithCUMask(&p.addnorm, (uint32_t)words, ma.data());
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(p.proj);
+    return fail(PR_ERR_HIP, "hipExtStreamCreateWithCUMask: %s", hipGetErrorString(e));
+  }
+  *slot = p;
+  *out = slot;
   return PR_OK;
 }
 
@@ -361,20 +419,34 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
   const bool poison = env_int("PR_DEBUG_POISON") != 0;
   const int gemma = norm_kind == PR_NORM_GEMMA;
 
-  std::vector<pr_plan_op> ops(8 + 6 * (size_t)d.n_chunks);
-  const int n = pr_plan(T, mc, ops.data(), (int)ops.size());
+  // The ping-pong schedule (caller stream and the library stream) or, with a CU split, the
+  // partitioned one (projections and add/norms on two CU-masked library streams).
+  const bool partitioned = d.addnorm_cus > 0;
+  MaskedPair* mp = nullptr;
+  if (partitioned) PR_TRY(masked_pair(c, d.addnorm_cus, &mp));
+  std::vector<pr_plan_op> ops(8 + 8 * (size_t)d.n_chunks);
+  const int n = partitioned ? pr_plan_cu_split(T, mc, ops.data(), (int)ops.size())
+                            : pr_plan(T, mc, ops.data(), (int)ops.size());
   if (n < 0) return n;
-  auto stream_of = [&](int id) { return id == 0 ? caller : c->sL; };
-  int last_slot[2] = {-1, -1};
+  auto stream_of = [&](int id) {
+    if (id == 0) return caller;
+    if (partitioned) return id == 1 ? mp->proj : mp->addnorm;
+    return c->sL;
+  };
+  int last_slot[2] = {-1, -1};  // last done slot recorded on the caller / library streams
   for (int i = 0; i < n; ++i) {
     const pr_plan_op& op = ops[i];
     float* slot = op.slot >= 0 ? c->slots + (size_t)op.slot * c->slot_elems : nullptr;
     const long long row0 = (long long)op.chunk * mc;
     hipStream_t st = stream_of(op.stream);
-    // A done record that directly follows the add/norm it marks is signalled by the launch.
+    // A done (ready) record that directly follows the add/norm (projection) it marks is
+    // signalled by the launch.
     const bool fuse_next = op.op == PR_OP_ADDNORM && i + 1 < n &&
                            ops[i + 1].op == PR_OP_RECORD_DONE && ops[i + 1].stream == op.stream &&
                            !poison;
+    const bool fuse_ready = op.op == PR_OP_GEMM && i + 1 < n &&
+                            ops[i + 1].op == PR_OP_RECORD_READY &&
+                            ops[i + 1].stream == op.stream && delay == 0;
     switch (op.op) {
       case PR_OP_WAIT_PREV:
         // In order on one caller stream (and joined), the previous call needs no wait; a call
@@ -397,8 +469,16 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
         if (delay > 0) PR_TRY(launch_delay(delay, st));
         PR_TRY(timed(c, 0, [&](hipEvent_t t0, hipEvent_t t1) {
           return gemm_rows(x + row0 * K, W, slot, false, op.rows, H, K, g,
-                           (long long)op.rows * H, st, nullptr, t0, t1);
+                           (long long)op.rows * H, st, fuse_ready ? c->ready[op.slot] : nullptr,
+                           t0, t1);
         }));
+        if (fuse_ready) ++i;
+        break;
+      case PR_OP_RECORD_READY:
+        PR_HIP(hipEventRecord(c->ready[op.slot], st));
+        break;
+      case PR_OP_WAIT_READY:
+        PR_HIP(hipStreamWaitEvent(st, c->ready[op.slot], 0));
         break;
       case PR_OP_ADDNORM:
         if (delay > 0) PR_TRY(launch_delay(delay, st));
@@ -409,13 +489,13 @@ int run_pipeline(DevCtx* c, const uint16_t* x, const uint16_t* W, float* r, cons
         }));
         if (poison) PR_TRY(launch_fill_nan(slot, c->slot_elems, st));
         if (fuse_next) {
-          last_slot[op.stream] = op.slot;
+          last_slot[op.stream == 0 ? 0 : 1] = op.slot;
           ++i;
         }
         break;
       case PR_OP_RECORD_DONE:
         PR_HIP(hipEventRecord(c->done[op.slot], st));
-        last_slot[op.stream] = op.slot;
+        last_slot[op.stream == 0 ? 0 : 1] = op.slot;
         break;
       case PR_OP_JOIN:
         PR_HIP(hipStreamWaitEvent(caller, c->done[op.slot], 0));

@@ -171,7 +171,7 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
   };
   const bool forced_cfg = env_on("PR_FORCE_TILE") || env_on("PR_FORCE_SPLIT") ||
                           env_on("PR_FORCE_WAVES") || env_on("PR_FORCE_STAGES") ||
-                          env_on("PR_FORCE_KGROUPS");
+                          env_on("PR_FORCE_KGROUPS") || env_on("PR_FORCE_CU_SPLIT");
   const int ncols = 3 + nmc;
   std::vector<double> t_conv(ngroups * nT, -1), t_fused(ngroups * nT, -1),
       spread(ngroups * nT, 0);
@@ -329,6 +329,53 @@ extern "C" int pr_tune(const int* Ks, const int* Hs, int ngroups, int norm_kind,
         const Cand& pick = cs[best_k >= 0 ? best_k : 0];
         PR_TRY(pr_set_chunk_config(K, H, mc, kTileBM[pick.c], kTileBN[pick.c], pick.split,
                                    pick.waves));
+
+        // The CU split with this chunk size, tuned jointly with the chunk projection's
+        // configuration (the page tunes SM-count targets together with the microchunk): the
+        // ping-pong schedule with the configuration just chosen, against the partitioned
+        // schedule with 32 and 64 CUs reserved for the add/norms, each with the time model's
+        // two best configurations for the CUs the projections keep.  Each candidate is
+        // checked, then all are timed round-robin; a partition is installed only if it beats
+        // the ping-pong schedule by more than 3%.
+        struct SplitCand {
+          int cus, c, split, waves;
+        };
+        std::vector<SplitCand> sc = {{0, best_k >= 0 ? pick.c : cs[0].c, pick.split, pick.waves}};
+        for (const int n : {32, 64}) {
+          std::vector<Cand> rk = ranking(kNumCUs - n);
+          for (size_t k = 0; k < rk.size() && k < 2; ++k) sc.push_back({n, rk[k].c, rk[k].split, 8});
+        }
+        auto install = [&](const SplitCand& x) -> int {
+          PR_TRY(pr_set_chunk_config(K, H, mc, kTileBM[x.c], kTileBN[x.c], x.split, x.waves));
+          return pr_set_cu_split(K, H, mc, x.cus);
+        };
+        std::vector<size_t> sc_ok;
+        for (size_t k = 0; k < sc.size(); ++k) {
+          PR_TRY(install(sc[k]));
+          PR_TRY(reset_r(Tc));
+          PR_TRY(fused_call_at(Tc, mc));
+          PR_TRY(fetch(Tc, out_try, r_try));
+          if (candidate_ok(out_try, out_ref, r_try, r_ref, r_before)) sc_ok.push_back(k);
+        }
+        std::vector<std::function<int()>> split_calls;
+        for (size_t k : sc_ok)
+          split_calls.push_back([&, k, mc, Tc]() {
+            const int rc = install(sc[k]);
+            return rc != PR_OK ? rc : fused_call_at(Tc, mc);
+          });
+        std::vector<Stats> sst;
+        if (!split_calls.empty()) PR_TRY(time_round_robin(split_calls, std::max(reps, 7), s, &sst));
+        size_t best_sc = 0;
+        double t0 = -1, tb = -1;
+        for (size_t n = 0; n < sc_ok.size(); ++n) {
+          if (sc_ok[n] == 0) t0 = sst[n].median;
+          if (tb < 0 || sst[n].median < tb) {
+            tb = sst[n].median;
+            best_sc = sc_ok[n];
+          }
+        }
+        if (t0 > 0 && t0 <= 1.03 * tb) best_sc = 0;
+        PR_TRY(install(sc[best_sc]));
       }
     }
 

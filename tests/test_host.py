@@ -18,7 +18,8 @@ A = 1 << 20  # a fake, 16-byte aligned address for pointer arguments
 @pytest.fixture(autouse=True)
 def _clean_env(monkeypatch):
     for k in ("PR_MICROCHUNK_TOKENS", "PR_THRESHOLD_TOKENS", "PR_LOG", "PR_FORCE_TILE",
-              "PR_FORCE_SPLIT", "PR_FORCE_WAVES", "PR_FORCE_STAGES", "PR_FORCE_KGROUPS"):
+              "PR_FORCE_SPLIT", "PR_FORCE_WAVES", "PR_FORCE_STAGES", "PR_FORCE_KGROUPS",
+              "PR_FORCE_CU_SPLIT"):
         monkeypatch.delenv(k, raising=False)
     pr.pr_clear_tuning()
     yield
@@ -240,7 +241,7 @@ def _simulate(calls):
         return c
 
     for k, (ops, caller) in enumerate(calls):
-        names = {0: caller, 1: "library"}
+        names = {0: caller, 1: "library", 2: "library_addnorm"}
         tick(caller, ("caller_pre", k))
         stamps = {}
         last_done = {}
@@ -261,6 +262,10 @@ def _simulate(calls):
                 last_done[stream] = ("done", slot)
             elif name == "WAIT_DONE":
                 clocks[sn] = {**clocks.get(sn, {}), **events[("done", slot)]}
+            elif name == "RECORD_READY":
+                events[("ready", slot)] = dict(clocks.get(sn, {}))
+            elif name == "WAIT_READY":
+                clocks[sn] = {**clocks.get(sn, {}), **events[("ready", slot)]}
             elif name == "JOIN":
                 clocks[sn] = {**clocks.get(sn, {}), **events[("done", slot)]}
             else:
@@ -307,6 +312,95 @@ def test_consecutive_calls_are_ordered(T1, mc1, T2, mc2, same_stream):
     for c2 in range(nc2):
         for c1 in range(nc1):
             assert ("ADDNORM", c1, 0) in st2[("GEMM", c2)][0], (c1, c2)
+
+
+@pytest.mark.parametrize("T,mc", [(64, 16), (3000, 256), (2048, 512), (7, 7), (1, 4096),
+                                  (10, 3), (4096, 1024), (5000, 512)])
+def test_cu_split_plan_is_race_free(T, mc):
+    """The CU-partitioned schedule: every projection on stream 1, every add/norm on stream 2;
+    a chunk's add/norm reads its slot only after the projection wrote it, a slot is rewritten
+    only after the add/norm three chunks earlier read it, the caller waits for every chunk,
+    nothing starts before the call's entry, and the next chunk's projection does not wait for
+    the previous chunk's add/norm (they can co-run on their disjoint CUs)."""
+    ops = pr.pr_plan_cu_split(T, mc)
+    nc = -(-T // mc)
+    gemms = [o for o in ops if o[0] == "GEMM"]
+    norms = [o for o in ops if o[0] == "ADDNORM"]
+    assert len(gemms) == nc and len(norms) == nc
+    assert all(o[1] == 1 for o in gemms) and all(o[1] == 2 for o in norms)
+    assert sum(o[4] for o in norms) == T and norms[-1][4] == T - (nc - 1) * mc
+    (st, caller_end), = _simulate([(ops, "caller")])
+    for c in range(nc):
+        assert ("GEMM", c, 0) in st[("ADDNORM", c)][0]
+        if c + 3 < nc:
+            assert ("ADDNORM", c, 0) in st[("GEMM", c + 3)][0]
+        assert ("ADDNORM", c, 0) in caller_end
+        assert ("caller_pre", 0) in st[("GEMM", c)][0]
+        assert ("caller_pre", 0) in st[("ADDNORM", c)][0]
+    for c in range(nc - 1):
+        assert ("ADDNORM", c, 0) not in st[("GEMM", c + 1)][0]
+
+
+@pytest.mark.parametrize("first,second", [("split", "split"), ("split", "pingpong"),
+                                          ("pingpong", "split")])
+@pytest.mark.parametrize("same_stream", [True, False])
+def test_consecutive_calls_across_schedules_are_ordered(first, second, same_stream):
+    """Calls alternating between the two schedules share slots, rows and the residual: every
+    chunk of the second starts after every chunk of the first."""
+    plan = {"split": pr.pr_plan_cu_split, "pingpong": pr.pr_plan}
+    a, b = plan[first](3000, 256), plan[second](700, 128)
+    (st1, _), (st2, _) = _simulate([(a, "s1"), (b, "s1" if same_stream else "s2")])
+    for c2 in range(-(-700 // 128)):
+        for c1 in range(-(-3000 // 256)):
+            assert ("ADDNORM", c1, 0) in st2[("GEMM", c2)][0], (c1, c2)
+
+
+def test_cu_split_plan_detects_a_missing_ready_wait():
+    ops = [o for o in pr.pr_plan_cu_split(2048, 256) if o[0] != "WAIT_READY"]
+    (st, _), = _simulate([(ops, "caller")])
+    assert not all(("GEMM", c, 0) in st[("ADDNORM", c)][0] for c in range(8))
+
+
+def test_cu_split_setting_and_decision(monkeypatch):
+    monkeypatch.delenv("PR_FORCE_CU_SPLIT", raising=False)
+    assert pr.pr_select(2048, 4096, 4096, 512)["addnorm_cus"] == 0
+    pr.pr_set_cu_split(4096, 4096, 512, 32)
+    d = pr.pr_select(2048, 4096, 4096, 512)
+    assert d["addnorm_cus"] == 32 and d["path"] == pr.PR_PATH_FUSED
+    before = (d["gemm_bm"], d["gemm_bn"], d["split_k"])
+    pr.pr_set_chunk_config(4096, 4096, 512, 128, 128, 2, 8)   # keeps the split
+    d = pr.pr_select(2048, 4096, 4096, 512)
+    assert d["addnorm_cus"] == 32 and (d["gemm_bm"], d["split_k"]) == (128, 2)
+    assert pr.pr_select(2048, 4096, 4096, 256)["addnorm_cus"] == 0   # other chunk sizes
+    assert pr.pr_select(2048, 4096, 4096, pr.PR_SELECT_UNFUSED)["addnorm_cus"] == 0
+    for bad in (4, 7, 136, -8):
+        with pytest.raises(pr.PRError):
+            pr.pr_set_cu_split(4096, 4096, 512, bad)
+    monkeypatch.setenv("PR_FORCE_CU_SPLIT", "64")
+    assert pr.pr_select(2048, 4096, 4096, 256)["addnorm_cus"] == 64
+    monkeypatch.setenv("PR_FORCE_CU_SPLIT", "12")
+    with pytest.raises(pr.PRError):
+        pr.pr_select(2048, 4096, 4096, 256)
+    assert before[0] in (128, 256)
+
+
+def test_cu_split_in_tuning_file(tmp_path):
+    pr.pr_set_chunk_config(1024, 2048, 256, 128, 128, 2, 8)
+    pr.pr_set_cu_split(1024, 2048, 256, 64)
+    pr.pr_set_cu_split(1024, 2048, 512, 16)   # no chunk record: the model's tile
+    path = tmp_path / "t.txt"
+    pr.pr_tuning_save(str(path), "dev:1")
+    text = path.read_text()
+    assert "cusplit 1024 2048 256 64" in text and "cusplit 1024 2048 512 16" in text
+    pr.pr_clear_tuning()
+    pr.pr_tuning_load(str(path), "dev:1")
+    assert pr.pr_select(4096, 1024, 2048, 256)["addnorm_cus"] == 64
+    assert pr.pr_select(4096, 1024, 2048, 256)["split_k"] == 2
+    assert pr.pr_select(4096, 1024, 2048, 512)["addnorm_cus"] == 16
+    path.write_text(text + "cusplit 1024 2048 256 12\n")
+    with pytest.raises(pr.PRError):
+        pr.pr_tuning_load(str(path), "dev:1")
+    assert pr.pr_select(4096, 1024, 2048, 256)["addnorm_cus"] == 64   # load is all-or-nothing
 
 
 def test_plan_detects_a_missing_wait():
