@@ -311,8 +311,8 @@ def silu_mul_roofline(pr, torch, args) -> int:
     """SiluAndMul from the merged gate/up output: algorithmic bytes per element of x (gate 2 +
     up 2 read, x 2 written) over the event-timed kernel, warm and flushed (a 512 MB read before
     each call), against 8 TB/s; then the down_proj block (SiluAndMul followed by the single
-    launch) against the single launch alone, back to back, the two series alternated five
-    times (medians)."""
+    launch), the same block in one launch with SiluAndMul in the main loop, and the single
+    launch alone, back to back, the three series alternated five times (medians)."""
     import synth
     dev = "cuda:0"
     stream = torch.cuda.Stream()
@@ -360,10 +360,14 @@ def silu_mul_roofline(pr, torch, args) -> int:
         def block():
             pr.pr_silu_mul(gu, x, T, K, stream)
             single()
-        # alternated, so that clock drift between the two series cancels
-        series = {"single_launch": [], "block": []}
+
+        def fused_block():
+            pr.proj_add_rmsnorm_silu(gu, Wp, r, w, d["eps"], T, K, H, wl.norm_kind, out, stream)
+        # alternated, so that clock drift between the series cancels
+        series = {"single_launch": [], "block": [], "fused_block": []}
         for _ in range(5):
-            for label, fn in (("single_launch", single), ("block", block)):
+            for label, fn in (("single_launch", single), ("block", block),
+                              ("fused_block", fused_block)):
                 el = time_steps(fn, args.steps, args.warmup, torch)
                 series[label].append(el * 1e3 / args.steps)
         for label, v in series.items():
@@ -373,7 +377,8 @@ def silu_mul_roofline(pr, torch, args) -> int:
         rows.append(res)
         log(f"{name}: silu_mul {res['warm_us']:.1f} us warm ({res['warm_GBs']:.0f} GB/s), "
             f"{res['flushed_us']:.1f} us flushed ({res['flushed_GBs']:.0f} GB/s); block "
-            f"{res['block_ms']:.4f} ms vs single launch {res['single_launch_ms']:.4f} ms")
+            f"{res['block_ms']:.4f} ms (SiluAndMul in the main loop: "
+            f"{res['fused_block_ms']:.4f} ms) vs single launch {res['single_launch_ms']:.4f} ms")
         del gu, x, Wp, r, w, out
         torch.cuda.empty_cache()
     print(json.dumps({"silu_mul": rows, "peak_GBs": PEAK_HBM_GBS}), flush=True)

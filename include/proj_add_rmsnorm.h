@@ -199,6 +199,27 @@ int proj_add_rmsnorm_single_launch(const uint16_t* x, const uint16_t* W, float* 
                                    const float* norm_w, float eps, int T, int K, int H,
                                    int norm_kind, uint16_t* out, void* stream);
 
+/*
+ * The down_proj region from the merged gate/up projection output, in one launch: SiluAndMul
+ * ("Plugin Architecture" page, SiluAndMul row: x = silu(gate) * up from the [..., 2d] output
+ * of the merged projection) formed inside the projection's main loop, then the single launch's
+ * residual add and RMSNorm.
+ *
+ * gate_up   [T][2K] bf16 as for pr_silu_mul (gate in columns [0, K), up in [K, 2K); K the
+ *           padded intermediate size, zero-padded columns inert).
+ * x is never written: each LDS stage of gate and up is converted in place to
+ * x = bf16(silu(gate) * up) with the fp32 arithmetic of pr_silu_mul, so the result equals
+ * pr_silu_mul followed by proj_add_rmsnorm_single_launch on the same tile configuration.
+ * Every tile column of a row band converts the band's x again (H / tile columns times), which
+ * the separate SiluAndMul pass does once.
+ * W, residual_inout, norm_w, eps, norm_kind, out, stream: as proj_add_rmsnorm_single_launch,
+ * with the same workspace, graph-capture and give-up behaviour and shape rules.
+ * Errors: as proj_add_rmsnorm_single_launch.
+ */
+int proj_add_rmsnorm_silu(const uint16_t* gate_up, const uint16_t* W, float* residual_inout,
+                          const float* norm_w, float eps, int T, int K, int H, int norm_kind,
+                          uint16_t* out, void* stream);
+
 /* ---------------------------------------------------------------------------------------- *
  * One rank's share under tensor parallelism, on one GPU ("TPSP Design" section 1 Motivation:
  * with a row-parallel projection each rank holds a slice of the input columns and of the
@@ -363,6 +384,11 @@ int pr_release_workspace(void);
  * the written buffers with the others; nothing is dereferenced). */
 int pr_validate(const void* x, const void* W, const void* residual_inout, const void* norm_w,
                 float eps, int T, int K, int H, int microchunk, int norm_kind, const void* out);
+
+/* Argument checks of proj_add_rmsnorm_silu (gate_up holds 4 * T * K bytes). */
+int pr_validate_silu(const void* gate_up, const void* W, const void* residual_inout,
+                     const void* norm_w, float eps, int T, int K, int H, int norm_kind,
+                     const void* out);
 
 /* Argument checks of proj_add_rmsnorm_fp8 (x_q and W_q hold one byte per element; the scale
  * pointers must be non-null and 4-byte aligned and must not overlap the written buffers). */

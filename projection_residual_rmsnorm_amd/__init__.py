@@ -78,6 +78,8 @@ SIGNATURES = {
     "proj_add_rmsnorm_single_launch_noalloc": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp,
                                                    _vp]),
     "pr_init": (_i, []),
+    "proj_add_rmsnorm_silu": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp, _vp]),
+    "pr_validate_silu": (_i, [_vp, _vp, _vp, _vp, _f, _i, _i, _i, _i, _vp]),
     "pr_project_partial": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "pr_add_rmsnorm_partials": (_i, [_vp, _i, _c.c_longlong, _vp, _vp, _f, _i, _i, _i, _vp,
                                      _vp]),
@@ -233,6 +235,23 @@ def proj_add_rmsnorm_single_launch_noalloc(x, W, residual_inout, norm_w, eps: fl
     _check(_lib().proj_add_rmsnorm_single_launch_noalloc(px, pw, pr_, pn, eps, T, K, H,
                                                          norm_kind, po,
                                                          _stream(stream, x, residual_inout)))
+
+
+def proj_add_rmsnorm_silu(gate_up, W, residual_inout, norm_w, eps: float, T: int, K: int,
+                          H: int, norm_kind: int = PR_NORM_STANDARD, out=None,
+                          stream=None) -> None:
+    """The down_proj region from the merged gate/up output, SiluAndMul inside the launch."""
+    T_, K_, H_ = max(T, 0), max(K, 0), max(H, 0)
+    _check(_lib().proj_add_rmsnorm_silu(
+        _ptr(gate_up, 4 * T_ * K_, "gate_up"), _ptr(W, 2 * K_ * H_, "W"),
+        _ptr(residual_inout, 4 * T_ * H_, "residual_inout"), _ptr(norm_w, 4 * H_, "norm_w"), eps,
+        T, K, H, norm_kind, _ptr(out, 2 * T_ * H_, "out"), _stream(stream, gate_up, residual_inout)))
+
+
+def pr_validate_silu(gate_up, W, residual_inout, norm_w, eps, T, K, H, norm_kind, out) -> int:
+    """Returns the code (does not raise)."""
+    return _lib().pr_validate_silu(_ptr(gate_up), _ptr(W), _ptr(residual_inout), _ptr(norm_w), eps,
+                                   T, K, H, norm_kind, _ptr(out))
 
 
 def pr_project_partial(x, W, y_partial, T: int, K: int, H: int, stream=None) -> None:

@@ -359,7 +359,8 @@ namespace {
 
 // Checks shared by the bf16 and the FP8 region: sizes, microchunk, norm kind, eps, null
 // pointers, alignment, and that the written buffers (residual, out) overlap nothing else the
-// call touches.  x and W hold `eb` bytes per element; `extra` lists further read-only inputs.
+// call touches.  x holds `xb` bytes per element of the projection input (4 for the merged
+// gate/up output), W `eb`; `extra` lists further read-only inputs.
 struct Extra {
   const void* p;
   unsigned long long bytes;
@@ -367,7 +368,8 @@ struct Extra {
 };
 int validate_region(const void* x, const void* W, const void* residual_inout, const void* norm_w,
                     float eps, int T, int K, int H, int microchunk, int norm_kind,
-                    const void* out, unsigned eb, const Extra* extra, int n_extra) {
+                    const void* out, unsigned xb, unsigned eb, const Extra* extra,
+                    int n_extra) {
   if (T < 0 || K <= 0 || H <= 0)
     return fail(PR_ERR_INVALID_ARG, "sizes must satisfy T >= 0, K > 0, H > 0 (T=%d K=%d H=%d)",
                 T, K, H);
@@ -400,7 +402,7 @@ int validate_region(const void* x, const void* W, const void* residual_inout, co
   auto range = [](const void* p, unsigned long long bytes, const char* name) {
     return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes, name};
   };
-  const Range rx = range(x, (unsigned long long)eb * T * K, "x"),
+  const Range rx = range(x, (unsigned long long)xb * T * K, "x"),
               rw = range(W, (unsigned long long)eb * K * H, "W"),
               rr = range(residual_inout, 4ULL * T * H, "residual"),
               rn = range(norm_w, 4ULL * H, "norm_w");
@@ -464,7 +466,14 @@ const char* pr_last_error(void) { return pr::g_last_error.c_str(); }
 int pr_validate(const void* x, const void* W, const void* residual_inout, const void* norm_w,
                 float eps, int T, int K, int H, int microchunk, int norm_kind, const void* out) {
   return pr::validate_region(x, W, residual_inout, norm_w, eps, T, K, H, microchunk, norm_kind,
-                             out, 2, nullptr, 0);
+                             out, 2, 2, nullptr, 0);
+}
+
+int pr_validate_silu(const void* gate_up, const void* W, const void* residual_inout,
+                     const void* norm_w, float eps, int T, int K, int H, int norm_kind,
+                     const void* out) {
+  return pr::validate_region(gate_up, W, residual_inout, norm_w, eps, T, K, H, 0, norm_kind, out,
+                             4, 2, nullptr, 0);
 }
 
 int pr_validate_fp8(const void* x_q, const void* x_scales, int scale_rows, const void* W_q,
@@ -474,7 +483,7 @@ int pr_validate_fp8(const void* x_q, const void* x_scales, int scale_rows, const
   const unsigned long long groups = T > 0 ? (unsigned long long)(T - 1) / scale_rows + 1 : 0;
   const pr::Extra extra[2] = {{x_scales, 4ULL * groups, "x_scales"}, {w_scale, 4, "w_scale"}};
   return pr::validate_region(x_q, W_q, residual_inout, norm_w, eps, T, K, H, 0, norm_kind, out,
-                             1, extra, T > 0 ? 2 : 0);
+                             1, 1, extra, T > 0 ? 2 : 0);
 }
 
 int pr_select(int T, int K, int H, int microchunk, pr_decision* d) {

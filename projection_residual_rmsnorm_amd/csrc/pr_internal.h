@@ -128,6 +128,14 @@ int launch_gemm_add_rmsnorm_fp8(const uint8_t* xq, const uint8_t* Wq, float* r, 
                                 void* stream, void* start_timing = nullptr,
                                 void* stop_timing = nullptr);
 
+// The single launch with SiluAndMul in the main loop: gate_up [M][2K] bf16 (gate first); the
+// projection's x = bf16(silu(gate) * up) is formed per LDS stage.  Tiles 256x256, 256x128,
+// 128x128 with 8 waves.
+int launch_gemm_add_rmsnorm_silu(const uint16_t* gate_up, const uint16_t* Wp, float* r,
+                                 const float* w, uint16_t* out, const SingleWs& ws, int M, int N,
+                                 int K, const GemmCfg& cfg, float eps, int gemma, void* stream,
+                                 void* start_timing = nullptr, void* stop_timing = nullptr);
+
 int launch_prepare_weight(const uint16_t* src, int src_layout, uint16_t* dst, int K, int H,
                           void* stream);
 

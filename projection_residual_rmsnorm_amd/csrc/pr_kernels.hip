@@ -154,8 +154,15 @@ struct NoTail {
 // stage; lane l supplies the 16-byte k-groups l/32 and 2 + l/32 of its row (A) or column (B),
 // which are the two fragments the bf16 loop reads for its two 16-deep substeps.  The matrix
 // core only needs A and B to take the same k order, which this gives.
+//
+// SILU: A points at the merged gate/up projection output [M][2K] (gate in columns [0, K), up
+// in [K, 2K)) and the loop's A operand is x = bf16(silu(gate) * up) ("Plugin Architecture"
+// page, SiluAndMul row).  A stage holds the gate and the up tile, loaded like the bf16 A tile;
+// once a stage has landed, the workgroup converts it in place (each thread a few 16-byte
+// groups: x = gate / (1 + e^-gate) * up in fp32, rounded once to bf16, the arithmetic of the
+// stand-alone SiluAndMul kernel) and meets at a second barrier before any fragment read.
 template <int BM, int BN, int NB, int WM, int WN, int KG = 1, typename Tail = NoTail,
-          bool FP8 = false>
+          bool FP8 = false, bool SILU = false>
 __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp, int M, int N, int K, int m0,
     int n0, int k_begin, int nk, const Tail& tail = Tail()) {
@@ -166,22 +173,24 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   constexpr int TM = WTM / 32;
   constexpr int TN = WTN / 32;
   constexpr int A_BYTES = BM * kBK * 2;
+  constexpr int A_RAW = SILU ? 2 * A_BYTES : A_BYTES;  // gate and up tiles (SILU) or x
   constexpr int B_BYTES = BN * kBK * 2;
   constexpr int A_LPW = A_BYTES / 1024 / NW;  // 1 KiB loads per wave per 32-deep half
   constexpr int B_LPW = B_BYTES / 1024 / NW;
-  constexpr int LPW = KG * (A_LPW + B_LPW);   // per stage
+  constexpr int LPW = KG * ((SILU ? 2 : 1) * A_LPW + B_LPW);  // per stage
   constexpr int P = NB - 1;  // stages in flight ahead of the one being computed
   constexpr int CG = BN / 64;
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "load split");
   static_assert(NW % CG == 0, "B loads: waves must cover whole k-groups");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
-  static_assert(NB >= 2 && NB <= 8 && NB * KG * (A_BYTES + B_BYTES) <= 160 * 1024, "LDS budget");
+  static_assert(NB >= 2 && NB <= 8 && NB * KG * (A_RAW + B_BYTES) <= 160 * 1024, "LDS budget");
   static_assert(LPW * (P - 1) < 64, "vmcnt range");
   static_assert(KG == 1 || KG == 2, "one or two K groups");
   static_assert(Tail::kLoads < 0 || Tail::kLoads == LPW, "a tail refill issues a stage's loads");
   static_assert(!FP8 || (KG == 1 && Tail::kLoads < 0), "FP8: one K group, no tail hook");
+  static_assert(!SILU || (KG == 1 && Tail::kLoads < 0 && !FP8), "SILU: bf16, one K group");
 
-  constexpr int HALF = A_BYTES + B_BYTES;  // one 32-deep half of a stage
+  constexpr int HALF = A_RAW + B_BYTES;  // one 32-deep half of a stage
   constexpr int STAGE = KG * HALF;
   char* const sb0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
   char* const sb1 = ring_buffer<1, STAGE, BM, BN, NB, WM, WN>();
@@ -218,6 +227,8 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
     row = row < M ? row : M - 1;
     if constexpr (FP8)
       a_off[i] = (uint32_t)(row * K + kg * 16);  // bytes: rows of K one-byte values
+    else if constexpr (SILU)
+      a_off[i] = (uint32_t)(row * 2 * K + kg * 8) * 2u;  // rows of 2K (gate, then up)
     else
       a_off[i] = (uint32_t)(row * K + kg * 8) * 2u;
   }
@@ -241,9 +252,16 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
       char* hb = buf + h * HALF;
 #pragma unroll
       for (int i = 0; i < A_LPW; ++i) load_to_lds16(a_base, a_off[i], hb + (wave + NW * i) * 1024);
+      if constexpr (SILU) {
+        // the up tile: the same rows, K columns further
+#pragma unroll
+        for (int i = 0; i < A_LPW; ++i)
+          load_to_lds16(a_base + (long long)K * 2, a_off[i],
+                        hb + A_BYTES + (wave + NW * i) * 1024);
+      }
 #pragma unroll
       for (int i = 0; i < B_LPW; ++i)
-        load_to_lds16(b_base, b_lane_off + i * b_step, hb + A_BYTES + (wave + NW * i) * 1024);
+        load_to_lds16(b_base, b_lane_off + i * b_step, hb + A_RAW + (wave + NW * i) * 1024);
     }
   };
 
@@ -272,7 +290,7 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
     for (int j = 0; j < TN; ++j) {
       const int col = wn * WTN + j * 32;
       bfr[j] = *reinterpret_cast<const bf16x8_t*>(
-          buf + A_BYTES + ((2 * s + (lane >> 5)) * BN + col + (lane & 31)) * 16);
+          buf + A_RAW + ((2 * s + (lane >> 5)) * BN + col + (lane & 31)) * 16);
     }
   };
   auto mfmas = [&](const bf16x8_t* af, const bf16x8_t* bfr) {
@@ -303,9 +321,9 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int col = wn * WTN + j * 32 + (lane & 31);
-        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(buf + A_BYTES +
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(buf + A_RAW +
                                                              ((lane >> 5) * BN + col) * 16);
-        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(buf + A_BYTES +
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(buf + A_RAW +
                                                              ((2 + (lane >> 5)) * BN + col) * 16);
         f8b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
@@ -350,6 +368,78 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u)
       if (u < rem) step8(kt + u, smem((u + 1) % NB), smem((u + P) % NB));
+    TileAcc<TM, TN> res;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) res.v[i][j] = acc[i][j];
+    return res;
+  }
+
+  if constexpr (SILU) {
+    // In-place SiluAndMul of a landed stage: 16-byte group q of the gate tile and the same
+    // group of the up tile (same row and k-group, same swizzled position) give group q of x.
+    constexpr int NT = NW * 64;
+    constexpr int GROUPS = A_BYTES / 16;
+    static_assert(GROUPS % NT == 0, "whole groups per thread");
+    auto convert = [&](char* buf) {
+#pragma unroll
+      for (int q0 = 0; q0 < GROUPS; q0 += NT) {
+        const int q = q0 + (int)threadIdx.x;
+        const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(buf + q * 16);
+        const u32x4_t uv = *reinterpret_cast<const u32x4_t*>(buf + A_BYTES + q * 16);
+        u32x4_t xv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float g0 = bf16_to_f32(gv[j] & 0xffffu), g1 = bf16_to_f32(gv[j] >> 16);
+          const float u0 = bf16_to_f32(uv[j] & 0xffffu), u1 = bf16_to_f32(uv[j] >> 16);
+          const float x0 = g0 / (1.0f + __expf(-g0)) * u0;
+          const float x1 = g1 / (1.0f + __expf(-g1)) * u1;
+          xv[j] = f32_to_bf16_rne(x0) | (f32_to_bf16_rne(x1) << 16);
+        }
+        *reinterpret_cast<u32x4_t*>(buf + q * 16) = xv;
+      }
+    };
+    // Prologue: stages 0 .. P-1 in flight, wait for stage 0, convert it, read its first
+    // fragments.
+#pragma unroll
+    for (int p = 0; p < P; ++p) issue_stage(min(p, nk - 1), smem(p));
+    __builtin_amdgcn_s_waitcnt(PR_VMCNT(LPW * (P - 1)));
+    barrier_no_fence();
+    convert(smem(0));
+    __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);
+    barrier_no_fence();
+    load_frags(smem(0), 0, fa0, fb0);
+    // A step: the refill; the stage's first substep; (stage kt+1's gate and up landed for
+    // every wave) the second substep's MFMAs while stage kt+1 is converted; (every wave's
+    // conversion written) the next stage's first fragments.
+    auto step_silu = [&](int kt, char* cur, char* next, char* refill) {
+      issue_stage(min(kt + P, nk - 1), refill);
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(cur, 1, fa1, fb1);
+      mfmas(fa0, fb0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(PR_VMCNT(LPW * (P - 1)));  // stage kt+1 landed
+      __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);
+      barrier_no_fence();
+      mfmas(fa1, fb1);
+      convert(next);
+      __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);
+      barrier_no_fence();
+      load_frags(next, 0, fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + NB <= nk; kt += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        step_silu(kt + u, smem(u), smem((u + 1) % NB), smem((u + P) % NB));
+    }
+    const int rem = nk - kt;
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u)
+      if (u < rem) step_silu(kt + u, smem(u), smem((u + 1) % NB), smem((u + P) % NB));
     TileAcc<TM, TN> res;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -591,7 +681,9 @@ __device__ __forceinline__ float lane_group_sum(float q) {
 // FP8: A and Bp point at E4M3 bytes (see tile_mainloop) and y = acc * x_scales[(scale_row0 +
 // row) / scale_rows] * w_scale[0] in fp32 before the residual add; otherwise those arguments
 // are unused.
-template <int BM, int BN, int NB, int WM, int WN, int KG, bool FP8 = false>
+// SILU: A is the merged gate/up output [M][2K] and the projection's x is SiluAndMul of it,
+// formed in the main loop (see tile_mainloop).
+template <int BM, int BN, int NB, int WM, int WN, int KG, bool FP8 = false, bool SILU = false>
 __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     gemm_add_rmsnorm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bp,
                             float* __restrict__ R, const float* __restrict__ w,
@@ -614,7 +706,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
   constexpr int WTN = BN / WN;
   constexpr int ETM = WTM / 32;
   constexpr int TN = WTN / 32;
-  constexpr int STAGE = KG * (BM + BN) * kBK * 2;
+  constexpr int STAGE = KG * ((SILU ? 2 * BM : BM) + BN) * kBK * 2;
   static_assert(NB >= 3, "the norm epilogue uses the third ring buffer");
   static_assert((BM * WN + 2 * BM + 4) * 4 <= STAGE, "row partials fit in one stage buffer");
   static_assert(!FP8 || KG == 1, "FP8: one K group");
@@ -695,7 +787,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
           }
     }
 
-    const TileAcc<TM, TN> part_acc = tile_mainloop<BM, BN, NB, WM, WN, KG, NoTail, FP8>(
+    const TileAcc<TM, TN> part_acc = tile_mainloop<BM, BN, NB, WM, WN, KG, NoTail, FP8, SILU>(
         A, Bp, M, N, K, m0, n0, 0, FP8 ? K / (2 * kBK) : K / (kBK * KG));
     // The ring's trailing refills (direct-to-LDS loads) have landed and every wave is past its
     // last fragment read before the stage buffers are reused below.
@@ -1707,12 +1799,12 @@ struct Fp8Scales {
   const float* w_scale = nullptr;
 };
 
-template <int BM, int BN, int NB, int WM, int WN, int KG, bool FP8 = false>
+template <int BM, int BN, int NB, int WM, int WN, int KG, bool FP8 = false, bool SILU = false>
 int launch_single_t(const uint16_t* x, const uint16_t* Wp, float* r, const float* w,
                     uint16_t* out, const SingleWs& ws, int M, int N, int K, float eps, int gemma,
                     hipStream_t s, hipEvent_t t0, hipEvent_t t1,
                     const Fp8Scales& sc = Fp8Scales()) {
-  auto kern = gemm_add_rmsnorm_kernel<BM, BN, NB, WM, WN, KG, FP8>;
+  auto kern = gemm_add_rmsnorm_kernel<BM, BN, NB, WM, WN, KG, FP8, SILU>;
   constexpr int threads = WM * WN * KG * 64;
   static int resident = 0;  // per instantiation; the library runs on one kind of device
   if (resident == 0) PR_TRY_K(resident_workgroups(kern, threads, &resident));
@@ -1896,6 +1988,33 @@ int launch_gemm_add_rmsnorm_fp8(const uint8_t* xq, const uint8_t* Wq, float* r, 
     return launch_single_t<128, 128, 4, 2, 4, 1, true>(x, Wp, r, w, out, ws, M, N, K, eps, gemma,
                                                        s, t0, t1, sc);
   return fail(PR_ERR_INVALID_ARG, "FP8 single launch: no tile %dx%d", cfg.bm, cfg.bn);
+}
+
+int launch_gemm_add_rmsnorm_silu(const uint16_t* gate_up, const uint16_t* Wp, float* r,
+                                 const float* w, uint16_t* out, const SingleWs& ws, int M, int N,
+                                 int K, const GemmCfg& cfg, float eps, int gemma, void* stream,
+                                 void* start_timing, void* stop_timing) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t t0 = static_cast<hipEvent_t>(start_timing);
+  hipEvent_t t1 = static_cast<hipEvent_t>(stop_timing);
+  if (M <= 0) return PR_OK;
+  if (K % (2 * kBK) != 0 || N % cfg.bn != 0 || N / cfg.bn > 64 || cfg.split != 1 ||
+      cfg.kgroups != 1 || cfg.waves != 8)
+    return fail(PR_ERR_SHAPE, "SiluAndMul single launch: N=%d K=%d with tile %dx%d split %d, %d "
+                "waves not supported (8 waves, one K group)", N, K, cfg.bm, cfg.bn, cfg.split,
+                cfg.waves);
+  // Stages of gate, up and weight tiles: 48 KiB (256x256: 3 in the ring), 40 KiB (256x128:
+  // 4), 24 KiB (128x128: 4).
+  if (cfg.bm == 256 && cfg.bn == 256)
+    return launch_single_t<256, 256, 3, 2, 4, 1, false, true>(gate_up, Wp, r, w, out, ws, M, N, K,
+                                                              eps, gemma, s, t0, t1);
+  if (cfg.bm == 256 && cfg.bn == 128)
+    return launch_single_t<256, 128, 4, 4, 2, 1, false, true>(gate_up, Wp, r, w, out, ws, M, N, K,
+                                                              eps, gemma, s, t0, t1);
+  if (cfg.bm == 128 && cfg.bn == 128)
+    return launch_single_t<128, 128, 4, 2, 4, 1, false, true>(gate_up, Wp, r, w, out, ws, M, N, K,
+                                                              eps, gemma, s, t0, t1);
+  return fail(PR_ERR_INVALID_ARG, "SiluAndMul single launch: no tile %dx%d", cfg.bm, cfg.bn);
 }
 
 int launch_add_rmsnorm(const void* y, int y_bf16, int nplanes, long long plane_stride,

@@ -900,6 +900,53 @@ int pr_add_rmsnorm_partials(const float* partials, int P, long long plane_stride
   });
 }
 
+int proj_add_rmsnorm_silu(const uint16_t* gate_up, const uint16_t* W, float* residual_inout,
+                          const float* norm_w, float eps, int T, int K, int H, int norm_kind,
+                          uint16_t* out, void* stream) {
+  clear_error();
+  PR_TRY(pr_validate_silu(gate_up, W, residual_inout, norm_w, eps, T, K, H, norm_kind, out));
+  pr_decision d;
+  PR_TRY(decide(T, K, H, PR_SINGLE_LAUNCH, &d));
+  DevCtx* c = nullptr;
+  PR_TRY(get_ctx(&c));
+  PR_TRY(check_give_up(c));
+  if (T == 0) return PR_OK;
+  if (fault_injected()) return fail(PR_ERR_HIP, "injected launch failure (PR_FAULT_INJECT)");
+  // The single launch's tile, with two waves per SIMD and one K group (the forms with the
+  // SiluAndMul main loop); the K-split pair form has none.
+  GemmCfg g = cfg_of(d);
+  if (g.split != 1)
+    return fail(PR_ERR_UNSUPPORTED, "the K-split pair form has no SiluAndMul variant");
+  g.waves = 8;
+  g.kgroups = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool capturing = false;
+  PR_TRY(stream_capturing(s, &capturing));
+  c->capturing = capturing;
+  int rc = PR_OK;
+  out = resolve_out(c, out, T, H, &rc);
+  SingleWs ws;
+  if (rc == PR_OK) rc = single_workspace(c, g, T, K, H, &ws);
+  c->capturing = false;
+  if (rc != PR_OK) return rc;
+  ws.fault_mask = wait_fault_injected() ? 0x80000000u : 0u;
+  ws.spin_limit = spin_limit();
+  ws.host_flag = c->host_flag_dev;
+  const int gemma = norm_kind == PR_NORM_GEMMA;
+  // Offsets inside a launch are 32-bit: at most 2^30 elements of gate_up per launch.
+  const long long rows_per = std::max<long long>(((1LL << 30) / (2LL * K)) / g.bm * g.bm, g.bm);
+  for (long long r0 = 0; r0 < T; r0 += rows_per) {
+    const int rows = (int)std::min<long long>(rows_per, T - r0);
+    auto launch = [&](hipEvent_t t0, hipEvent_t t1) {
+      return launch_gemm_add_rmsnorm_silu(gate_up + r0 * 2 * K, W, residual_inout + r0 * H,
+                                          norm_w, out + r0 * H, ws, rows, H, K, g, eps, gemma, s,
+                                          t0, t1);
+    };
+    PR_TRY(capturing ? launch(nullptr, nullptr) : timed(c, 0, launch));
+  }
+  return PR_OK;
+}
+
 int pr_init(void) {
   clear_error();
   DevCtx* c = nullptr;
