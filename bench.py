@@ -723,12 +723,17 @@ def main() -> int:
     if not args.no_tune:
         t_tune = time.perf_counter()
         rep = pr.pr_tune([K], [H], wl.norm_kind, [T], mcs, reps=5, stream=stream)
-        for m in mcs + [pr.PR_SINGLE_LAUNCH]:
-            c = pr.pr_select(T, K, H, m)
-            chunk_cfgs["single" if m == pr.PR_SINGLE_LAUNCH else str(m)] = (
-                f"{c['gemm_bm']}x{c['gemm_bn']} split {c['split_k']} {c['gemm_waves']} waves")
-        log(f"tuned in {time.perf_counter() - t_tune:.1f} s: {chunk_cfgs} "
-            f"(checked {rep['n_checked']}, rejected {rep['n_rejected']})")
+        log(f"tuned in {time.perf_counter() - t_tune:.1f} s (checked {rep['n_checked']}, "
+            f"rejected {rep['n_rejected']})")
+    # The configuration each fused form runs with (tuned, or the time model's without tuning;
+    # the single launch's does not depend on tuning).
+    for m in mcs + [pr.PR_SINGLE_LAUNCH]:
+        c = pr.pr_select(T, K, H, m)
+        chunk_cfgs["single" if m == pr.PR_SINGLE_LAUNCH else str(m)] = (
+            f"{c['gemm_bm']}x{c['gemm_bn']} split {c['split_k']} {c['gemm_waves']} waves"
+            + (f" {c['gemm_kgroups']} K groups" if c["gemm_kgroups"] > 1 else "")
+            + (f" CU split {c['addnorm_cus']}" if c["addnorm_cus"] > 0 else ""))
+    log(f"configurations: {chunk_cfgs}")
     per_mc = {}
     if args.only_single:
         forms = ["single"]

@@ -110,6 +110,8 @@ static int apply_forced_tile(int K, GemmCfg* g) {
       return fail(PR_ERR_INVALID_ARG, "PR_FORCE_STAGES=%s must be in 2..8", st);
     g->stages = stages;
   }
+  // A forced tile or wave count means the one-group form unless K groups are forced as well.
+  if ((t != nullptr && t[0] != '\0') || (wv != nullptr && wv[0] != '\0')) g->kgroups = 1;
   const char* kgv = std::getenv("PR_FORCE_KGROUPS");
   if (kgv != nullptr && kgv[0] != '\0') {
     const int kg = std::atoi(kgv);
@@ -197,8 +199,10 @@ GemmCfg choose_gemm_unsplit(int M, int N, int K) {
 
 // Tile of the single-launch path: the modelled fastest tile whose columns divide H into at most
 // 64 tile columns (the kernel's row-partial limit); bm = 0 if there is none.  A 256 x 128 tile
-// grid that fits in one round runs with 4 waves per workgroup (measured on 2048 x 4096 x 4096:
-// 7% faster than 8 waves; with several rounds 8 waves were as fast or faster).
+// grid that fits in one round runs with 8 waves in two K groups (two waves per SIMD, each wave
+// keeping the 128 x 64 wave tile; on 2048 x 4096 x 4096, same box, three alternating rounds:
+// 0.0858-0.0861 ms against 0.0875-0.0886 ms for 4 waves and 0.0868-0.0887 ms for 8 waves in
+// one group, with every tile storing its residual after the row wait).
 GemmCfg choose_single(int M, int N, int K) {
   GemmCfg best;
   best.bm = best.bn = 0;
@@ -215,7 +219,7 @@ GemmCfg choose_single(int M, int N, int K) {
   }
   if (best.bm == 256 && best.bn == 128 &&
       (long long)((M + 255) / 256) * (N / 128) <= kNumCUs)
-    best.waves = 4;
+    best.kgroups = 2;
   return best;
 }
 

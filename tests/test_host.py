@@ -148,13 +148,21 @@ def test_select_single_launch():
     assert d["path"] == pr.PR_PATH_SINGLE and d["reason"] == 6
     assert (d["microchunk"], d["n_chunks"], d["last_valid"]) == (2048, 1, 2048)
     assert d["split_k"] == 1 and 4096 % d["gemm_bn"] == 0
-    # one round of 256 x 128 tiles (8 x 32 = 256 workgroups) runs with 4 waves
-    assert (d["gemm_bm"], d["gemm_bn"], d["gemm_waves"]) == (256, 128, 4)
+    # one round of 256 x 128 tiles (8 x 32 = 256 workgroups) runs with 8 waves in 2 K groups
+    assert (d["gemm_bm"], d["gemm_bn"], d["gemm_waves"], d["gemm_kgroups"]) == (256, 128, 8, 2)
+    # a forced tile or wave count takes the one-group form unless K groups are forced too
     for T, K, H in [(4096, 14336, 4096), (3000, 16384, 3072), (32768, 8192, 8192), (1, 512, 512)]:
         d = pr.pr_select(T, K, H, pr.PR_SINGLE_LAUNCH)
         assert d["path"] == pr.PR_PATH_SINGLE
         assert H % d["gemm_bn"] == 0 and H // d["gemm_bn"] <= 64
         assert d["gemm_waves"] in (4, 8)
+    with pytest.MonkeyPatch.context() as mp:
+        mp.setenv("PR_FORCE_WAVES", "4")
+        d = pr.pr_select(2048, 4096, 4096, pr.PR_SINGLE_LAUNCH)
+        assert (d["gemm_waves"], d["gemm_kgroups"]) == (4, 1)
+        mp.setenv("PR_FORCE_WAVES", "8")
+        mp.setenv("PR_FORCE_KGROUPS", "2")
+        assert pr.pr_select(2048, 4096, 4096, pr.PR_SINGLE_LAUNCH)["gemm_kgroups"] == 2
     with pytest.raises(pr.PRError) as e:  # no tile's columns divide H = 320
         pr.pr_select(64, 256, 320, pr.PR_SINGLE_LAUNCH)
     assert e.value.code == pr.PR_ERR_SHAPE
