@@ -267,12 +267,15 @@ int pr_add_rmsnorm_partials(const float* partials, int P, long long plane_stride
 /*
  * Scaled E4M3 quantisation of a bf16 matrix by groups of rows.
  *
- * src     [rows][cols] bf16, device, read.  Finite values.
+ * src     [rows][cols] bf16, device, read.
  * dst     [rows][cols] E4M3 codes, device, written.
  * scales  [ceil(rows / group_rows)] fp32, device, written: for the group of rows
  *         [g * group_rows, min(rows, (g + 1) * group_rows)), scale = largest |value| / 448 in
  *         fp32 (1 when the group is all zero).  Each code is value / scale (an fp32 division),
  *         rounded to the nearest E4M3 value with ties to even, magnitudes clamped to 448.
+ *         Non-finite values follow the same definition: a group holding a NaN has a NaN scale
+ *         and every code 0x7F; one holding an infinity (and no NaN) an infinite scale, codes
+ *         +-0 for its finite values and 0x7F for the infinities.
  * Activations: group_rows = the microchunk (1 gives per-token scales).  A weight [H][K] with
  * one per-tensor scale: rows = H, cols = K, group_rows = H.
  * cols a positive multiple of 16; src, dst 16-byte aligned, scales 4-byte aligned; the three

@@ -20,24 +20,41 @@ constexpr float kE4M3Max = 448.0f;
 
 __device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Nearest E4M3 code of v (ties to the even code), magnitudes at or above 448 clamped to 448,
-// the sign kept (-0 -> 0x80), NaN -> 0x7F.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (!(a == a)) return 0x7Fu;
-  if (a >= kE4M3Max) return sign | 0x7Eu;
-  // Below 2^-6 the codes are the subnormals m * 2^-9 (m = 8 is the smallest normal, code 8):
-  // a * 512 is exact and rintf rounds half to even.
-  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);
-  // Normal: keep 3 of fp32's 23 mantissa bits, rounding to nearest even (a carry moves into
-  // the exponent), and rebias the exponent from 127 to 7.
-  const uint32_t au = u & 0x7FFFFFFFu;
-  const uint32_t r = au + 0x7FFFFu + ((au >> 20) & 1u);
-  const uint32_t code = (r >> 20) - (120u << 3);
-  return sign | min(code, 0x7Eu);
+// E4M3 code conversion: v_cvt_pk_fp8_f32, gfx950's OCP E4M3 conversion, rounds to the
+// nearest value with ties to even and keeps the sign (-0 -> 0x80); inputs are clamped to +-448
+// first.  HI selects the word the two codes go to (first value in the lower byte).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b, uint32_t old) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
+  const float cb = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, (int)old, HI);
 }
+
+// Codes of 8 bf16 values (one 16-byte vector) divided by scale: the quotient is an IEEE fp32
+// division, and a NaN quotient gives 0x7F.
+__device__ __forceinline__ uint2 e4m3_codes8(const uint4& v, float scale) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float q[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    q[2 * j] = bf16_value(w[j] & 0xFFFFu) / scale;
+    q[2 * j + 1] = bf16_value(w[j] >> 16) / scale;
+  }
+  uint32_t p[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    p[h] = e4m3_pair<true>(q[4 * h + 2], q[4 * h + 3],
+                           e4m3_pair<false>(q[4 * h], q[4 * h + 1], 0u));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (q[4 * h + e] != q[4 * h + e]) p[h] = (p[h] & ~(0xFFu << (8 * e))) | (0x7Fu << (8 * e));
+  }
+  return make_uint2(p[0], p[1]);
+}
+
+// 16-byte vectors a lane loads before it uses any of them: a row of 4096 bf16 values is one
+// batch, so every load of a wave is in flight at once.
+constexpr int kQuantU = 8;
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
@@ -45,14 +62,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_max_f32(float v) {
+// Loads of one batch: kQuantU 16-byte vectors per lane, vector c0 + 64 i of the row.  Indexes
+// past the row load its last vector again (unconditional loads keep the batch free of
+// branches, so the loads stay in flight together): a repeated value does not change a maximum,
+// and codes past the row are not stored.
+__device__ __forceinline__ void load_batch(const uint4* __restrict__ p, int c0, int nvec,
+                                           uint4 (&v)[kQuantU]) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  for (int i = 0; i < kQuantU; ++i) v[i] = p[min(c0 + 64 * i, nvec - 1)];
 }
 
-// Largest |value| of each row: one wave per row, 16-byte loads of 8 bf16 values; bf16
-// magnitudes order like their bit patterns with the sign cleared, so an integer max is exact.
+// Largest |value| of each row: one wave per row, 16-byte loads of 8 bf16 values in batches of
+// kQuantU per lane; bf16 magnitudes order like their bit patterns with the sign cleared, so an
+// integer max is exact.
 __global__ void __launch_bounds__(256)
     fp8_row_amax_kernel(const uint16_t* __restrict__ src, float* __restrict__ row_amax, int rows,
                         int cols) {
@@ -61,20 +83,26 @@ __global__ void __launch_bounds__(256)
   for (int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
     const uint4* p = reinterpret_cast<const uint4*>(src + (long long)row * cols);
     uint32_t m = 0;
-    for (int c = lane; c < nvec; c += 64) {
-      const uint4 v = p[c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int c0 = lane; c0 < nvec; c0 += 64 * kQuantU) {
+      uint4 v[kQuantU];
+      load_batch(p, c0, nvec, v);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+      for (int i = 0; i < kQuantU; ++i) {
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+      }
     }
     m = wave_max_u32(m);
     if (lane == 0) row_amax[row] = bf16_value(m);
   }
 }
 
-// Codes of each row with its group's scale: one wave per row.  The wave takes the group's
-// largest magnitude from the row maxima, forms the scale and converts its row, 8 values per
-// lane and step; the first row of a group also stores the group's scale.
+// Codes of each row with its group's scale: one wave per row.  The wave issues the loads of
+// its group's row maxima (up to 256 rows at once) and of its first batch, forms the scale from
+// the maxima while the batch is in flight, then converts its row in batches of kQuantU 16-byte
+// vectors per lane (the waves sharing a SIMD overlap one another's loads and conversions);
+// the first row of a group also stores the group's scale.
 __global__ void __launch_bounds__(256)
     fp8_quantize_kernel(const uint16_t* __restrict__ src, const float* __restrict__ row_amax,
                         uint8_t* __restrict__ dst, float* __restrict__ scales, int rows,
@@ -82,26 +110,34 @@ __global__ void __launch_bounds__(256)
   const int lane = threadIdx.x & 63;
   const int nvec = cols / 8;
   for (int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
-    const int g = row / group_rows;
-    const int r0 = g * group_rows, r1 = min(rows, r0 + group_rows);
-    float amax = 0.0f;
-    for (int r = r0 + lane; r < r1; r += 64) amax = fmaxf(amax, row_amax[r]);
-    amax = wave_max_f32(amax);
-    const float scale = amax == 0.0f ? 1.0f : amax / kE4M3Max;
-    if (row == r0 && lane == 0) scales[g] = scale;
     const uint4* p = reinterpret_cast<const uint4*>(src + (long long)row * cols);
     uint2* q = reinterpret_cast<uint2*>(dst + (long long)row * cols);
-    for (int c = lane; c < nvec; c += 64) {
-      const uint4 v = p[c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t b[8];
+    const int g = row / group_rows;
+    const int r0 = g * group_rows, r1 = min(rows, r0 + group_rows);
+    // The row maxima are non-negative or NaN, so an integer max of their bits is their max
+    // with NaN (above infinity) propagated: a group holding a NaN gets a NaN scale.
+    // Indexes past the group read its last row again, which leaves the maximum unchanged.
+    uint32_t ra[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        b[2 * j] = e4m3_code(bf16_value(w[j] & 0xFFFFu) / scale);
-        b[2 * j + 1] = e4m3_code(bf16_value(w[j] >> 16) / scale);
+    for (int j = 0; j < 4; ++j) ra[j] = __float_as_uint(row_amax[min(r0 + lane + 64 * j, r1 - 1)]);
+    uint4 v[kQuantU];
+    load_batch(p, lane, nvec, v);
+    uint32_t abits = max(max(ra[0], ra[1]), max(ra[2], ra[3]));
+    if (r1 - r0 > 256) {  // uniform: groups of more than 256 rows (a per-tensor weight scale)
+      for (int r = r0 + 256 + lane; r < r1; r += 64)
+        abits = max(abits, __float_as_uint(row_amax[r]));
+    }
+    const float amax = __uint_as_float(wave_max_u32(abits));
+    const float scale = amax == 0.0f ? 1.0f : amax / kE4M3Max;
+    if (row == r0 && lane == 0) scales[g] = scale;
+    for (int c0 = lane; c0 < nvec; c0 += 64 * kQuantU) {
+      if (c0 != lane) load_batch(p, c0, nvec, v);  // the first batch is in flight already
+#pragma unroll
+      for (int i = 0; i < kQuantU; ++i) {
+        const int c = c0 + 64 * i;
+        const uint2 code = e4m3_codes8(v[i], scale);
+        if (c < nvec) q[c] = code;
       }
-      q[c] = make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-                        b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
     }
   }
 }

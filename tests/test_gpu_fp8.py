@@ -58,6 +58,115 @@ def test_quantize_codes_and_scales_bitwise(R, C, G):
     np.testing.assert_array_equal(dst.cpu().numpy(), want_q)
 
 
+def _bf16_bits_to_f32(b):
+    return (np.asarray(b, np.uint32) << 16).view(np.float32)
+
+
+def _midpoints():
+    """The values midway between neighbouring non-negative E4M3 codes (0 .. 448), and 464."""
+    v = oracle.decode_e4m3(np.arange(0, 0x7F, dtype=np.uint8))
+    return np.append((v[:-1] + v[1:]) / 2, 464.0).astype(np.float32)
+
+
+def _boundary_rows(cols=64):
+    """Rows (one scale group each) whose fp32 quotients value / scale fall on an E4M3 rounding
+    boundary or within 8 fp32 ulps of one: exact ties with scales that are powers of two, and,
+    for 6000 drawn bf16 row maxima, the bf16 values next to boundary * scale whose quotient
+    lands that close.  Column 0 holds the row maximum."""
+    mids = _midpoints()
+    rows = []
+
+    def emit(amax_bits, xs_bits):
+        xs_bits = np.concatenate([xs_bits, xs_bits | 0x8000]).astype(np.uint16)
+        for i in range(0, len(xs_bits), cols - 1):
+            r = np.zeros(cols, np.uint16)
+            r[0] = amax_bits
+            chunk = xs_bits[i:i + cols - 1]
+            r[1:1 + len(chunk)] = chunk
+            rows.append(r)
+
+    # scale = 2^k: value / scale is exact, so every midpoint is an exact tie
+    for k in range(-30, 9):
+        amax = np.float32(448.0 * 2.0 ** k)
+        xs = synth.f32_to_bf16_bits((mids[:-1].astype(np.float64) * 2.0 ** k).astype(np.float32))
+        emit(synth.f32_to_bf16_bits(np.array([amax], np.float32))[0], xs)
+    # drawn scales: bf16 candidates around boundary * scale
+    rng = np.random.default_rng(1234)
+    amax = synth.f32_to_bf16_bits(np.exp2(rng.uniform(-12, 13, 6000)).astype(np.float32))
+    a32 = _bf16_bits_to_f32(amax)
+    s = (a32 / np.float32(448.0)).astype(np.float32)
+    target = (mids[None, :].astype(np.float64) * s[:, None].astype(np.float64)).astype(np.float32)
+    base = (target.view(np.uint32) >> 16).astype(np.int64)
+    for d in (-1, 0, 1, 2):
+        cand = (base + d).astype(np.uint32)
+        x = (cand << 16).view(np.float32)
+        q = (x / s[:, None]).astype(np.float32)
+        ulps = np.abs(q.view(np.int32).astype(np.int64) - mids[None, :].view(np.int32))
+        ok = (ulps <= 8) & (x > 0) & (x <= a32[:, None])
+        for i in np.nonzero(ok.any(axis=1))[0]:
+            emit(amax[i], cand[i][ok[i]].astype(np.uint16))
+    return np.stack(rows)
+
+
+def test_quantize_rounding_boundaries_bitwise():
+    """Quotients on or next to a rounding boundary decide the code by the last fp32 ulp: the
+    device's codes equal the oracle's there too (ties to the even code, per-row scales)."""
+    xb = _boundary_rows()
+    q = (_bf16_bits_to_f32(xb[:, 1:]) / (_bf16_bits_to_f32(xb[:, :1]) / np.float32(448.0)))
+    near = np.abs(q.astype(np.float32).view(np.int32)[..., None].astype(np.int64)
+                  - np.abs(_midpoints()).view(np.int32)[None, None, :]).min(axis=-1)
+    assert (near == 0).sum() > 1000 and ((near > 0) & (near <= 8)).sum() > 300
+    dst, scales = _quantize_dev(xb, 1)
+    want_q, want_s = oracle.quantize_fp8(xb, 1)
+    np.testing.assert_array_equal(scales.cpu().numpy(), want_s)
+    np.testing.assert_array_equal(dst.cpu().numpy(), want_q)
+
+
+def test_quantize_every_bf16_value_unit_scale():
+    """Every bf16 pattern of magnitude <= 448 with scale 1 (448 in every row): the codes are
+    the nearest E4M3 values of the bf16 values themselves."""
+    allb = np.arange(0, 0x10000, dtype=np.uint32)
+    mag = _bf16_bits_to_f32(allb & 0x7FFF)
+    xs = allb[mag <= 448.0].astype(np.uint16)
+    cols = 512
+    n = -(-len(xs) // (cols - 1))
+    xb = np.zeros((n, cols), np.uint16)
+    xb[:, 0] = 0x43E0  # 448
+    flat = np.zeros(n * (cols - 1), np.uint16)
+    flat[:len(xs)] = xs
+    xb[:, 1:] = flat.reshape(n, cols - 1)
+    dst, scales = _quantize_dev(xb, 1)
+    want_q, want_s = oracle.quantize_fp8(xb, 1)
+    assert np.all(want_s == 1.0)
+    np.testing.assert_array_equal(scales.cpu().numpy(), want_s)
+    np.testing.assert_array_equal(dst.cpu().numpy(), want_q)
+
+
+def test_quantize_nonfinite_and_tiny_groups():
+    """Groups holding a NaN, an infinity, only bf16 subnormals (a scale far below 2^-100) or
+    only zeros get what the definition gives: the oracle's codes and scales."""
+    rng = np.random.default_rng(7)
+    G, C = 4, 256
+    x = rng.standard_normal((6 * G, C)).astype(np.float32)
+    x[1, 5] = np.nan
+    x[G + 2, 9] = np.inf
+    x[2 * G + 3, 0] = -np.inf
+    x[2 * G, 1] = np.nan
+    x[3 * G:4 * G] *= np.float32(1e-3)
+    xb = synth.f32_to_bf16_bits(x)
+    sub = rng.integers(1, 0x7F, (G, C)).astype(np.uint16) | (rng.integers(0, 2, (G, C)) << 15).astype(np.uint16)
+    xb[4 * G:5 * G] = sub  # bf16 subnormals only
+    xb[5 * G:6 * G] = 0
+    dst, scales = _quantize_dev(xb, G)
+    with np.errstate(invalid="ignore"):  # inf / inf in the definition
+        want_q, want_s = oracle.quantize_fp8(xb, G)
+    got_s = scales.cpu().numpy()
+    assert np.isnan(want_s[0]) and np.isinf(want_s[1]) and np.isnan(want_s[2])
+    assert 0 < want_s[4] < 2.0 ** -100 and want_s[5] == 1.0
+    np.testing.assert_array_equal(got_s, want_s)
+    np.testing.assert_array_equal(dst.cpu().numpy(), want_q)
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 def test_prepare_weight_fp8_layout(layout):
     K, H = 256, 192
