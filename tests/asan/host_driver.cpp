@@ -1,5 +1,6 @@
-// Exercises every host-only entry point of the library (argument checks, the path decision,
-// the pipeline schedule, the threshold search, tuning tables and files) on many inputs,
+// Exercises every host-only entry point of the library (argument checks of every region entry
+// point, the path decision, both pipeline schedules, the threshold search, tuning tables, CU
+// splits and files) on many inputs,
 // including invalid ones.  Built together with the host source under AddressSanitizer and
 // UndefinedBehaviorSanitizer by tests/test_host_asan.py; a sanitizer report fails the test.
 #include <cstdint>
@@ -44,6 +45,34 @@ int main(int argc, char** argv) {
           checks += pr_validate(a + 1, b, c, d, 1e-5f, T, K, H, mc, 0, e) == PR_OK;  // misaligned
           checks += pr_validate(a, b, a, d, 1e-5f, T, K, H, mc, 0, e) == PR_OK;      // aliasing
         }
+  // The fused-SiluAndMul and FP8 argument checks (gate_up: 4 bytes per element of x; FP8:
+  // byte operands and two scale pointers, including misaligned and overlapping ones).
+  char* f = a + 20480;
+  char* g = a + 24576;
+  for (int T : Ts)
+    for (int K : Ks)
+      for (int H : Hs) {
+        for (int kind = -1; kind <= 2; ++kind)
+          checks += pr_validate_silu(a, b, c, d, 1e-5f, T, K, H, kind, e) == PR_OK;
+        checks += pr_validate_silu(a, b, a + 16, d, 1e-5f, T, K, H, 0, e) == PR_OK;
+        for (int sr : {-1, 0, 1, 7, 256, 1 << 30}) {
+          checks += pr_validate_fp8(a, f, sr, b, g, c, d, 1e-5f, T, K, H, 0, e) == PR_OK;
+          checks += pr_validate_fp8(a, f + 2, sr, b, g, c, d, 1e-5f, T, K, H, 0, e) == PR_OK;
+          checks += pr_validate_fp8(a, nullptr, sr, b, g, c, d, 1e-5f, T, K, H, 1, e) == PR_OK;
+          checks += pr_validate_fp8(a, c, sr, b, c + 8, c, d, 1e-5f, T, K, H, 0, e) == PR_OK;
+        }
+      }
+  for (int T : Ts)
+    for (int mc : mcs) {
+      const int n = pr_plan_cu_split(T, mc, nullptr, 0);
+      if (n < 0) continue;
+      std::vector<pr_plan_op> ops(n > 0 ? n : 1);
+      checks += pr_plan_cu_split(T, mc, ops.data(), n) == n;
+      if (n > 2) checks += pr_plan_cu_split(T, mc, ops.data(), n / 2) >= 0;
+    }
+  for (int n : {-8, 0, 7, 8, 32, 64, 128, 136, 1 << 30})
+    for (int mc : mcs) checks += pr_set_cu_split(4096, 4096, mc, n) == PR_OK;
+  pr_clear_tuning();
   for (int T : Ts)
     for (int mc : mcs) {
       const int n = pr_plan(T, mc, nullptr, 0);

@@ -71,6 +71,55 @@ def test_validate():
     assert pr.pr_validate(**dict(ok, microchunk=4096, out=None)) == 0
 
 
+def test_validate_silu():
+    """The fused SiluAndMul region reads gate_up, twice the bytes of x (4 T K): a residual
+    placed in gate_up's upper half overlaps it, one placed beyond it does not."""
+    T, K, H = 64, 512, 512
+    ok = dict(gate_up=A, W=A * 2, residual_inout=A * 3, norm_w=A * 4, eps=1e-5, T=T, K=K, H=H,
+              norm_kind=0, out=A * 5)
+    assert pr.pr_validate_silu(**ok) == 0
+    bad = [
+        (dict(K=100), pr.PR_ERR_SHAPE), (dict(norm_kind=2), pr.PR_ERR_INVALID_ARG),
+        (dict(gate_up=None), pr.PR_ERR_INVALID_ARG), (dict(gate_up=A + 8), pr.PR_ERR_INVALID_ARG),
+        (dict(residual_inout=A + 2 * T * K), pr.PR_ERR_INVALID_ARG),   # inside the up half
+        (dict(out=A * 2 + 1024), pr.PR_ERR_INVALID_ARG),               # inside the weight
+        (dict(eps=float("inf")), pr.PR_ERR_INVALID_ARG),
+    ]
+    for change, code in bad:
+        assert pr.pr_validate_silu(**dict(ok, **change)) == code, change
+    assert pr.pr_validate_silu(**dict(ok, residual_inout=A + 4 * T * K)) == 0  # just past it
+    assert pr.pr_validate_silu(None, None, None, None, 1e-5, 0, K, H, 0, None) == 0
+
+
+def test_validate_fp8():
+    """One byte per element for x_q and W_q; the scale pointers are checked for NULL, 4-byte
+    alignment and overlap with the written buffers; scale_rows >= 1."""
+    T, K, H = 64, 512, 512
+    ok = dict(x_q=A, x_scales=A * 6, scale_rows=16, W_q=A * 2, w_scale=A * 7,
+              residual_inout=A * 3, norm_w=A * 4, eps=1e-5, T=T, K=K, H=H, norm_kind=0,
+              out=A * 5)
+    assert pr.pr_validate_fp8(**ok) == 0
+    bad = [
+        (dict(scale_rows=0), pr.PR_ERR_INVALID_ARG), (dict(x_scales=None), pr.PR_ERR_INVALID_ARG),
+        (dict(w_scale=None), pr.PR_ERR_INVALID_ARG), (dict(x_scales=A * 6 + 2), pr.PR_ERR_INVALID_ARG),
+        (dict(w_scale=A * 3 + 8), pr.PR_ERR_INVALID_ARG),      # scale inside the residual
+        (dict(x_scales=A * 5 + 16), pr.PR_ERR_INVALID_ARG),    # scales inside the output
+        (dict(residual_inout=A + T * K // 2), pr.PR_ERR_INVALID_ARG),  # inside x_q
+        (dict(out=A * 2 + K * H // 2), pr.PR_ERR_INVALID_ARG),          # inside W_q
+        (dict(K=96), pr.PR_ERR_SHAPE), (dict(T=-1), pr.PR_ERR_INVALID_ARG),
+    ]
+    for change, code in bad:
+        assert pr.pr_validate_fp8(**dict(ok, **change)) == code, change
+    # byte operands: a residual right after x_q's T*K bytes and an output right after W_q's
+    # K*H bytes do not overlap them
+    assert pr.pr_validate_fp8(**dict(ok, residual_inout=A + T * K)) == 0
+    assert pr.pr_validate_fp8(**dict(ok, out=A * 2 + K * H)) == 0
+    # the last of ceil(T / scale_rows) scales may not reach into the residual
+    assert pr.pr_validate_fp8(**dict(ok, x_scales=A * 3 - 4 * (T // 16))) == 0
+    assert pr.pr_validate_fp8(**dict(ok, x_scales=A * 3 - 4 * (T // 16) + 4)) == pr.PR_ERR_INVALID_ARG
+    assert pr.pr_validate_fp8(None, None, 16, None, None, None, None, 1e-5, 0, K, H, 0, None) == 0
+
+
 def test_select_explicit_and_unfused():
     d = pr.pr_select(3000, 16384, 3072, 256)
     assert d["path"] == pr.PR_PATH_FUSED and d["microchunk"] == 256
