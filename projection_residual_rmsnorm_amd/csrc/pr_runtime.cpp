@@ -799,13 +799,14 @@ int proj_add_rmsnorm_fp8(const uint8_t* x_q, const float* x_scales, int scale_ro
   PR_TRY(check_give_up(c));
   if (T == 0) return PR_OK;
   if (fault_injected()) return fail(PR_ERR_HIP, "injected launch failure (PR_FAULT_INJECT)");
-  // The tile the time model picks, with two waves per SIMD and one K group (the FP8 loop's
-  // only forms); the K-split pair form has no FP8 variant.
+  // The tile the time model picks, with two waves per SIMD (the FP8 loop's only forms), in two
+  // K groups where the bf16 single launch uses them (one-round 256 x 128 grids) and K holds
+  // whole 128-deep stages; the K-split pair form has no FP8 variant.
   GemmCfg g = cfg_of(d);
   if (g.split != 1)
     return fail(PR_ERR_UNSUPPORTED, "the K-split pair form has no FP8 variant");
   g.waves = 8;
-  g.kgroups = 1;
+  if (!(g.bm == 256 && g.bn == 128 && g.kgroups == 2 && K % 128 == 0)) g.kgroups = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   bool capturing = false;
   PR_TRY(stream_capturing(s, &capturing));

@@ -225,16 +225,30 @@ class Fp8Device:
         return err
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128"])
+def _force_fp8_tile(monkeypatch, tile):
+    """tile: "BMxBN", or "256x128kg2" for 8 waves in two K groups."""
+    kg2 = tile.endswith("kg2")
+    monkeypatch.setenv("PR_FORCE_TILE", tile[:-3] if kg2 else tile)
+    monkeypatch.setenv("PR_FORCE_WAVES", "8")
+    if kg2:
+        monkeypatch.setenv("PR_FORCE_KGROUPS", "2")
+    return (int(v) for v in (tile[:-3] if kg2 else tile).split("x"))
+
+
+FP8_TILES = ["256x256", "256x128", "256x128kg2", "128x128"]
+
+
+@pytest.mark.parametrize("tile", FP8_TILES)
 @pytest.mark.parametrize("kind", [0, 1])
-@pytest.mark.parametrize("T,K,H,G", [(300, 512, 768, 128), (64, 256, 512, 1), (513, 1024, 256, 77)])
+@pytest.mark.parametrize("T,K,H,G", [(300, 512, 768, 128), (64, 256, 512, 1), (513, 1024, 256, 77),
+                                     (100, 320, 256, 16)])
 def test_fp8_region_parity_small(monkeypatch, tile, kind, T, K, H, G):
-    """Every FP8 tile, both norm forms, ragged tile rows, per-token and ragged scale groups."""
-    bm, bn = (int(v) for v in tile.split("x"))
+    """Every FP8 tile and wave form, both norm forms, ragged tile rows, per-token and ragged
+    scale groups; K = 320 is not a whole number of the two K groups' 128-deep stages, so the
+    K-group request falls back to one group there."""
+    bm, bn = _force_fp8_tile(monkeypatch, tile)
     if H % bn:
         pytest.skip(f"H={H} is not a multiple of the tile's {bn} columns")
-    monkeypatch.setenv("PR_FORCE_TILE", tile)
-    monkeypatch.setenv("PR_FORCE_WAVES", "8")
     print(f"fp8 tile {tile} T={T} K={K} H={H} G={G} kind={kind}", flush=True)
     d = synth.make_custom(T, K, H, seed=T + K + kind, norm_kind=kind)
     dev = Fp8Device(d, G)
@@ -243,12 +257,11 @@ def test_fp8_region_parity_small(monkeypatch, tile, kind, T, K, H, G):
     print(err, flush=True)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x128", "128x128"])
+@pytest.mark.parametrize("tile", FP8_TILES)
 def test_fp8_integer_projection_is_exact(monkeypatch, tile):
     """E4M3-representable integer inputs with 448 in every scale group quantise with unit
     scales; with a zero residual the updated residual is the integer projection, bitwise."""
-    monkeypatch.setenv("PR_FORCE_TILE", tile)
-    monkeypatch.setenv("PR_FORCE_WAVES", "8")
+    _force_fp8_tile(monkeypatch, tile)
     T, K, H, G = 300, 1024, 512, 64
     rng = np.random.default_rng(17)
     vals = np.array([0, 1, 2, 3, 4, 6, 8, 12], np.float32)
