@@ -241,7 +241,7 @@ FP8_TILES = ["256x256", "256x128", "256x128kg2", "128x128"]
 @pytest.mark.parametrize("tile", FP8_TILES)
 @pytest.mark.parametrize("kind", [0, 1])
 @pytest.mark.parametrize("T,K,H,G", [(300, 512, 768, 128), (64, 256, 512, 1), (513, 1024, 256, 77),
-                                     (100, 320, 256, 16)])
+                                     (100, 320, 256, 16), (70, 128, 256, 70)])
 def test_fp8_region_parity_small(monkeypatch, tile, kind, T, K, H, G):
     """Every FP8 tile and wave form, both norm forms, ragged tile rows, per-token and ragged
     scale groups; K = 320 is not a whole number of the two K groups' 128-deep stages, so the

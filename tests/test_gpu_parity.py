@@ -126,6 +126,23 @@ def test_single_launch_integer_projection_is_exact(monkeypatch, tile, waves, kgr
     assert oracle.within_tolerance(err), err
 
 
+@pytest.mark.parametrize("tile,waves,kgroups,split", [c for c in SINGLE_CFGS if c[3] == 1])
+@pytest.mark.parametrize("K", [64, 128, 192])
+def test_single_launch_short_k_is_exact(monkeypatch, tile, waves, kgroups, split, K):
+    """K of one to three 64-deep stages: the main loop is all prologue and tail refills (two K
+    groups: one stage at K = 64, the whole loop in the thin tail), and the residual must still
+    be exact on small integers."""
+    _force_single(monkeypatch, tile, waves, kgroups, split)
+    d = synth.integer_inputs(300, K, 768, seed=K)
+    dev = Device(d)
+    r_dev, out_bits = dev.run("single")
+    r_ref, out_ref = oracle.proj_add_rmsnorm(d["x"], d["W"], d["residual"], d["norm_w"],
+                                             d["eps"], 0, "fused")
+    np.testing.assert_array_equal(r_dev.astype(np.float64), r_ref)
+    err = oracle.compare(r_dev, out_bits, r_ref, out_ref)
+    assert oracle.within_tolerance(err), err
+
+
 def _identity_inputs(T, H, kind):
     rng = np.random.default_rng(11)
     w = (0.1 * rng.standard_normal(H)).astype(np.float32)
