@@ -460,6 +460,24 @@ def fp8_entry(pr, torch, x, W_src, r, w, out, d, norm_kind, scale_rows, args, st
     log(f"fp8: {res['ms_per_step']:.4f} ms/step (quantise + single launch), kernel "
         f"{res['kernel_avg_us']:.1f} us = {res['kernel_tflops']:.0f} TFLOP/s, "
         f"{res['frac']:.3f} of the fp8 peak")
+    if scale_rows != 1:
+        # The same step with per-token activation scales (rows of up to 8192 columns are
+        # quantised in one pass).
+        sx1 = torch.empty((T,), dtype=torch.float32, device=dev)
+
+        def step1():
+            pr.pr_quantize_fp8(x, xq, sx1, T, K, 1, stream)
+            pr.proj_add_rmsnorm_fp8(xq, sx1, 1, Wp8, sw, r, w, d["eps"], T, K, H, norm_kind, out,
+                                    stream)
+
+        el1 = time_steps(step1, steps, max(args.warmup, 2), torch)
+        if pr.pr_device_status(stream) != 0:
+            raise SystemExit("FP8 single-launch status bits set: a row wait gave up")
+        res["per_token"] = {"scale_rows": 1, "ms_per_step": el1 * 1e3 / steps,
+                            "tokens_per_s": T * steps / el1,
+                            "step_tflops": flops * steps / el1 / 1e12}
+        log(f"fp8, per-token scales: {res['per_token']['ms_per_step']:.4f} ms/step")
+        del sx1
     del wq, sw, Wp8, xq, sx
     return res
 

@@ -279,8 +279,10 @@ int pr_add_rmsnorm_partials(const float* partials, int P, long long plane_stride
  * Activations: group_rows = the microchunk (1 gives per-token scales).  A weight [H][K] with
  * one per-tensor scale: rows = H, cols = K, group_rows = H.
  * cols a positive multiple of 16; src, dst 16-byte aligned, scales 4-byte aligned; the three
- * must not overlap.  Uses a library workspace of `rows` floats (grown; under graph capture it
- * must already be large enough).  Asynchronous on `stream`; rows = 0 is a no-op.
+ * must not overlap.  Groups of 1, 2 or 4 rows with cols <= 8192 are quantised in one pass over
+ * the data; other calls take two passes and a library workspace of `rows` floats (grown; under
+ * graph capture it must already be large enough).  Asynchronous on `stream`; rows = 0 is a
+ * no-op.
  * Errors: PR_ERR_SHAPE, PR_ERR_INVALID_ARG, PR_ERR_UNSUPPORTED, PR_ERR_NOMEM, PR_ERR_HIP.
  */
 int pr_quantize_fp8(const uint16_t* src, uint8_t* dst, float* scales, int rows, int cols,

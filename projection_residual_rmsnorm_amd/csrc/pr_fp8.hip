@@ -142,6 +142,59 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// One pass for groups of 1, 2 or 4 rows whose rows fit in registers (NV 16-byte vectors per
+// lane): a workgroup's four waves take four consecutive rows, so a group never straddles two
+// workgroups.  Each wave loads its whole row, takes its largest magnitude (the integer max of
+// the magnitude bits, as fp8_row_amax_kernel), the waves of a group combine theirs through LDS,
+// and the codes are formed from the registers with the group's scale: the same values and
+// arithmetic as the two kernels above, with one read of the row and no workspace.
+template <int NV>
+__global__ void __launch_bounds__(256)
+    fp8_quantize_rows_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst,
+                             float* __restrict__ scales, int rows, int cols, int group_rows) {
+  __shared__ uint32_t s_max[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nvec = cols / 8;
+  for (int row0 = blockIdx.x * 4; row0 < rows; row0 += gridDim.x * 4) {  // uniform per workgroup
+    const int row = row0 + wave;
+    // A wave past the last row reads that row again and stores nothing.
+    const uint4* p = reinterpret_cast<const uint4*>(src + (long long)min(row, rows - 1) * cols);
+    uint4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = p[min(lane + 64 * i, nvec - 1)];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    }
+    m = wave_max_u32(m);
+    if (group_rows > 1) {  // uniform
+      if (lane == 0) s_max[wave] = row < rows ? m : 0u;
+      __syncthreads();
+      const int first = wave / group_rows * group_rows;
+      uint32_t gm = 0;
+      for (int q = 0; q < group_rows; ++q) gm = max(gm, s_max[first + q]);
+      m = gm;
+      __syncthreads();  // s_max is rewritten by the next rows
+    }
+    const float amax = bf16_value(m);
+    const float scale = amax == 0.0f ? 1.0f : amax / kE4M3Max;
+    if (row < rows) {
+      if (lane == 0 && row % group_rows == 0) scales[row / group_rows] = scale;
+      uint2* q = reinterpret_cast<uint2*>(dst + (long long)row * cols);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = lane + 64 * i;
+        const uint2 code = e4m3_codes8(v[i], scale);
+        if (c < nvec) q[c] = code;
+      }
+    }
+  }
+}
+
 // dst[((k/16)*H + h)*16 + k%16] = W[h][k]: each output column's 16 consecutive k-values form
 // one 16-byte matrix-core operand.  One thread per (k-group, column).
 __global__ void prepare_weight_fp8_out_in_kernel(const uint8_t* __restrict__ W,
@@ -179,11 +232,26 @@ int check(const char* what) {
 
 }  // namespace
 
+bool quantize_fp8_single_pass(int cols, int group_rows) {
+  // Rows of up to 8192 columns: 16 vectors per lane leave room for three waves per SIMD; with 32
+  // (rows of 14336 columns) one wave per SIMD made the pass slower than the two kernels.
+  return (group_rows == 1 || group_rows == 2 || group_rows == 4) && cols <= 64 * 8 * 16;
+}
+
 int launch_quantize_fp8(const uint16_t* src, uint8_t* dst, float* scales, float* row_amax,
                         int rows, int cols, int group_rows, void* stream) {
   if (rows <= 0) return PR_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const unsigned grid = (unsigned)std::min((rows + 3) / 4, 16 * kNumCUs);
+  if (quantize_fp8_single_pass(cols, group_rows)) {
+    if (cols <= 64 * 8 * 8)
+      hipLaunchKernelGGL(fp8_quantize_rows_kernel<8>, dim3(grid), dim3(256), 0, s, src, dst,
+                         scales, rows, cols, group_rows);
+    else
+      hipLaunchKernelGGL(fp8_quantize_rows_kernel<16>, dim3(grid), dim3(256), 0, s, src, dst,
+                         scales, rows, cols, group_rows);
+    return check("fp8_quantize_rows_kernel");
+  }
   hipLaunchKernelGGL(fp8_row_amax_kernel, dim3(grid), dim3(256), 0, s, src, row_amax, rows, cols);
   const int rc = check("fp8_row_amax_kernel");
   if (rc != PR_OK) return rc;

@@ -155,6 +155,9 @@ int noalloc_workspace(SingleWs* ws);
 // FP8 quantisation (pr_fp8.hip): codes [rows][cols] E4M3 of the bf16 src by groups of
 // group_rows rows, scales[g] = amax / 448 (1 for an all-zero group); row_amax is a workspace of
 // `rows` floats.  cols % 16 == 0.
+// Groups of 1, 2 or 4 rows of at most 8192 columns are quantised in one pass, with no
+// row-maximum workspace (row_amax may then be null).
+bool quantize_fp8_single_pass(int cols, int group_rows);
 int launch_quantize_fp8(const uint16_t* src, uint8_t* dst, float* scales, float* row_amax,
                         int rows, int cols, int group_rows, void* stream);
 // FP8 weight layout: dst[((k/16)*H + h)*16 + k%16] = W[h][k] from [H][K] or [K][H] bytes.

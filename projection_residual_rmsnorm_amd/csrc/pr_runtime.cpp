@@ -755,6 +755,8 @@ int pr_quantize_fp8(const uint16_t* src, uint8_t* dst, float* scales, int rows, 
   if ((d0 < s1 && s0 < d1) || (c0 < s1 && s0 < c1) || (c0 < d1 && d0 < c1))
     return fail(PR_ERR_INVALID_ARG, "src, dst and scales must not overlap");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (quantize_fp8_single_pass(cols, group_rows))
+    return launch_quantize_fp8(src, dst, scales, nullptr, rows, cols, group_rows, s);
   bool capturing = false;
   PR_TRY(stream_capturing(s, &capturing));
   c->capturing = capturing;

@@ -41,10 +41,12 @@ def _quantize_dev(bits16, group_rows):
 
 
 @pytest.mark.parametrize("R,C,G", [(300, 512, 128), (64, 4096, 64), (1, 64, 1), (37, 1024, 5),
-                                   (2048, 4096, 2048)])
+                                   (2048, 4096, 2048), (130, 1024, 4), (37, 8192, 2),
+                                   (45, 16384, 4), (9, 16400, 1), (3, 4096, 1)])
 def test_quantize_codes_and_scales_bitwise(R, C, G):
     """Several magnitude ranges per row (so groups differ), a ragged last group, an all-zero
-    group and exact ties."""
+    group and exact ties.  Groups of 1, 2 or 4 rows up to 8192 columns take the one-pass
+    kernel (rows in registers, 8 or 16 vectors per lane), the others two passes."""
     rng = np.random.default_rng(R + C + G)
     x = rng.standard_normal((R, C)).astype(np.float32)
     x *= np.exp2(rng.integers(-12, 8, (R, 1))).astype(np.float32)
