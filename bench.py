@@ -63,6 +63,11 @@ def parse():
                     help="comma-separated CU counts reserved for the add/norm stream (0 = the "
                          "ping-pong schedule): time the pipeline of the workload at each chunk "
                          "size and split, round-robin, and print the table")
+    ap.add_argument("--phases", default="",
+                    help="comma-separated workloads: in-kernel phase and clock stamps of the single "
+                         "launch, from the diagnostic library libprojaddnorm_stamps.so (same "
+                         "kernels with stamps); writes the summary to --phases-out")
+    ap.add_argument("--phases-out", default="", help="markdown summary of --phases (else stdout)")
     ap.add_argument("--tp-share", default="",
                     help="comma-separated tensor-parallel degrees P: time one rank's share of "
                          "the workload (projection over K/P, add/norm of T/P rows with P fp32 "
@@ -682,8 +687,66 @@ def tp_share(pr, torch, args) -> int:
     return 0
 
 
+def phases(pr, torch, args) -> int:
+    """In-kernel phase and clock stamps of the single launch on each workload (the diagnostic
+    library, selected by PR_PHASE_STAMPS=1 before the first library call)."""
+    import synth
+    from projection_residual_rmsnorm_amd import profiling
+    results = {}
+    dev = "cuda:0"
+    for name in args.phases.split(","):
+        wl = synth.WORKLOADS[name]
+        T, K, H = wl.T, wl.K, wl.H
+        d = synth.make_inputs(wl, seed=0)
+        x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+        Wp = torch.empty(K * H, dtype=torch.int16, device=dev)
+        pr.pr_prepare_weight(torch.from_numpy(d["W"].view(np.int16)).to(dev),
+                             pr.PR_WEIGHT_OUT_IN, Wp, K, H)
+        r = torch.from_numpy(d["residual"]).to(dev)
+        w = torch.from_numpy(d["norm_w"]).to(dev)
+        out = torch.empty((T, H), dtype=torch.int16, device=dev)
+        torch.cuda.synchronize()
+        assert pr.loaded_library_path() == pr.STAMPS_LIB_PATH, pr.loaded_library_path()
+        c = pr.pr_select(T, K, H, pr.PR_SINGLE_LAUNCH)
+        cfg = (f"{c['gemm_bm']}x{c['gemm_bn']} tiles, {c['gemm_waves']} waves"
+               + (f" in {c['gemm_kgroups']} K groups" if c["gemm_kgroups"] > 1 else ""))
+        stream = torch.cuda.Stream()
+        call = lambda: pr.proj_add_rmsnorm_single_launch(x, Wp, r, w, d["eps"], T, K, H,
+                                                         wl.norm_kind, out, stream=stream)
+        for _ in range(max(args.warmup, 1)):
+            call()
+        trials = []
+        for _ in range(5):
+            pr.pr_phase_stamps(clear=True)
+            for _ in range(3):
+                call()
+            a = pr.pr_phase_stamps()  # synchronises the device
+            a = a[a[:, 1] != 0]
+            tiles = -(-T // c["gemm_bm"]) * (H // c["gemm_bn"])
+            # the matrix cores' share is derived only for one-round grids (every workgroup one
+            # whole tile)
+            fpg = 2.0 * c["gemm_bm"] * c["gemm_bn"] * K if a.shape[0] == tiles else 0.0
+            trials.append(profiling.phase_stats(a, fpg))
+        assert pr.pr_device_status(stream) == 0
+        results[name] = {"shape": f"T={T}, K={K}, H={H}", "config": cfg, "trials": trials,
+                         "rounds": -(-tiles // trials[0]["workgroups"])}
+        ph = trials[-1]["phases_us"]
+        log(f"{name}: main loop {ph[0]:.1f} us at {trials[-1]['clock_mhz']:.0f} MHz, "
+            f"span {trials[-1]['span_us']:.1f} us")
+    text = profiling.phases_summary(results, "python bench.py " + " ".join(sys.argv[1:]))
+    if args.phases_out:
+        with open(args.phases_out, "w") as f:
+            f.write(text)
+    else:
+        print(text)
+    return 0
+
+
 def main() -> int:
     args = parse()
+    if args.phases:
+        # the diagnostic library with in-kernel stamps (selected before any library call)
+        os.environ["PR_PHASE_STAMPS"] = "1"
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
               "inter-GPU step", file=sys.stderr)
@@ -695,6 +758,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.phases:
+        return phases(pr, torch, args)
     if args.tune_sweep:
         return tune_sweep(pr, torch, args)
     if args.tp_share:

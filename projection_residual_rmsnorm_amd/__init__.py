@@ -14,6 +14,10 @@ from typing import List, Optional, Sequence, Tuple
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libprojaddnorm.so")
+# The diagnostic build: the same sources and ABI, with in-kernel phase and clock stamps of the
+# single launch (and pr_phase_stamps_{layout,read,clear} to read them).  PR_PHASE_STAMPS=1 in
+# the environment when the library is first used selects it.
+STAMPS_LIB_PATH = os.path.join(_PKG_DIR, "libprojaddnorm_stamps.so")
 
 PR_OK = 0
 PR_ERR_INVALID_ARG = -1
@@ -118,14 +122,23 @@ class PRError(RuntimeError):
 
 
 _LIB = None
+_LIB_LOADED = None
+_STAMP_SIGNATURES = {
+    "pr_phase_stamps_layout": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int),
+                                              ctypes.POINTER(ctypes.c_int)]),
+    "pr_phase_stamps_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
+    "pr_phase_stamps_clear": (ctypes.c_int, []),
+}
 
 
 def _lib():
-    global _LIB
+    global _LIB, _LIB_LOADED
     if _LIB is None:
-        if not os.path.exists(LIB_PATH):
+        stamps = os.environ.get("PR_PHASE_STAMPS") == "1"
+        path = STAMPS_LIB_PATH if stamps else LIB_PATH
+        if not os.path.exists(path):
             raise RuntimeError(
-                f"HIP library {LIB_PATH} is missing; build it with "
+                f"HIP library {path} is missing; build it with "
                 "`python -m projection_residual_rmsnorm_amd.build`")
         # torch ships its own HIP runtime; importing it first makes the library bind to that one
         # runtime (same soname) instead of loading a second copy from /opt/rocm.
@@ -133,13 +146,42 @@ def _lib():
             import torch  # noqa: F401
         except ImportError:
             pass
-        lib = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in {**SIGNATURES, **(_STAMP_SIGNATURES if stamps else {})}.items():
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
         _LIB = lib
+        _LIB_LOADED = path
     return _LIB
+
+
+def loaded_library_path() -> Optional[str]:
+    """Path of the library this process loaded (None before the first call)."""
+    return _LIB_LOADED
+
+
+def pr_phase_stamps(clear: bool = False):
+    """The diagnostic library's phase stamps as a (workgroups, words) uint64 array (after
+    synchronising the device), or, with clear=True, zero them and return None.  Raises unless
+    the process loaded libprojaddnorm_stamps.so (PR_PHASE_STAMPS=1)."""
+    lib = _lib()
+    if _LIB_LOADED != STAMPS_LIB_PATH:
+        raise RuntimeError("phase stamps need the diagnostic library: set PR_PHASE_STAMPS=1 "
+                           "before the first library call")
+    def check(rc: int, name: str) -> None:
+        if rc != PR_OK:
+            raise PRError(rc, f"{name} failed")
+    if clear:
+        check(lib.pr_phase_stamps_clear(), "pr_phase_stamps_clear")
+        return None
+    import numpy as np
+    groups, words = ctypes.c_int(), ctypes.c_int()
+    check(lib.pr_phase_stamps_layout(ctypes.byref(groups), ctypes.byref(words)),
+          "pr_phase_stamps_layout")
+    buf = np.zeros(groups.value * words.value, dtype=np.uint64)
+    check(lib.pr_phase_stamps_read(buf.ctypes.data, buf.size), "pr_phase_stamps_read")
+    return buf.reshape(groups.value, words.value)
 
 
 def library():

@@ -695,6 +695,39 @@ __device__ __forceinline__ float lane_group_sum(float q) {
   return q;
 }
 
+#ifdef PR_PHASE_STAMPS
+// Phase stamps, compiled only into the diagnostic library libprojaddnorm_stamps.so (the
+// default library contains none of this).  Thread 0 of each of the first kStampGroups
+// workgroups of a single launch records, in its first round:
+//   [0]      its XCC id,
+//   [1 + p]  the constant 100 MHz clock (s_memrealtime) at phase boundary p of
+//            gemm_add_rmsnorm_kernel: 0 tile start, 1 main loop done, 2 K groups combined,
+//            3 r + y and row sums staged, 4 row partials published, 5 row counter complete,
+//            6 row slots read, 7 the wave's residual and output stores acknowledged,
+//   [10], [11] the shader clock (s_memtime) at boundaries 0 and 1, so that their difference
+//            over that of [1] and [2] is the clock the main loop ran at.
+// Every launch overwrites the same words.
+constexpr int kStampGroups = 4096;
+constexpr int kStampWords = 12;
+__device__ unsigned long long pr_phase_stamps[kStampGroups * kStampWords];
+
+__device__ __forceinline__ void phase_stamp(int round, int p) {
+  if (threadIdx.x != 0 || round != 0 || blockIdx.x >= kStampGroups) return;
+  unsigned long long* s = pr_phase_stamps + blockIdx.x * kStampWords;
+  if (p == 7) __builtin_amdgcn_s_waitcnt(0);  // this wave's stores acknowledged
+  s[1 + p] = __builtin_amdgcn_s_memrealtime();
+  if (p <= 1) s[10 + p] = __builtin_amdgcn_s_memtime();
+  if (p == 0) {
+    unsigned xcc = 0;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    s[0] = xcc & 0xff;
+  }
+}
+#define PR_PHASE(p) phase_stamp(round, p)
+#else
+#define PR_PHASE(p) ((void)0)
+#endif
+
 // FP8: A and Bp point at E4M3 bytes (see tile_mainloop) and y = acc * x_scales[(scale_row0 +
 // row) / scale_rows] * w_scale[0] in fp32 before the residual add; otherwise those arguments
 // are unused.
@@ -778,6 +811,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     tm += round * rows_per_round;
     const int m0 = tm * BM;
     const int n0 = tn * BN;
+    PR_PHASE(0);
 
     // Lane position in the staged layout: row lrow + RPI * rr of each 16-row slice, columns
     // rcol .. rcol+3 of the wave's WTN (lane id l).
@@ -818,6 +852,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     // last fragment read before the stage buffers are reused below.
     __builtin_amdgcn_s_waitcnt(PR_VMCNT(0));
     __syncthreads();
+    PR_PHASE(1);
     // The epilogue's per-lane offsets are formed here, from an opaque copy of the lane id, so
     // that they are not hoisted out of the round loop and kept live across the main loop.
     int el = lane;
@@ -887,6 +922,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
       if (kgrp == 0) combine(0); else combine(ETM);
       __syncthreads();  // hand-over regions read before the epilogue reuses the buffers
     }
+    PR_PHASE(2);
     if constexpr (FP8) {
       // One scale per tile row: the row's activation-group scale times the weight scale (in the
       // third ring buffer, after the K groups' hand-over has released it).
@@ -933,6 +969,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
       }
     }
     __syncthreads();
+    PR_PHASE(3);
     const unsigned long long tag = (unsigned long long)epoch << 32;
     if (threadIdx.x < BM) {
       float p = 0.0f;
@@ -947,12 +984,14 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     if (threadIdx.x == 0) {
       unsigned* cnt = sync + 3 + tm;
       __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      PR_PHASE(4);
       unsigned polls = 0;
       while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                  (unsigned)tiles_n &&
              polls++ < spin_limit)
         __builtin_amdgcn_s_sleep(1);
       *sflag = 1;
+      PR_PHASE(5);
     }
     __syncthreads();
     {
@@ -993,6 +1032,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
       sred[trow * TPR + part] = ss;
     }
     __syncthreads();
+    PR_PHASE(6);
     if (threadIdx.x < BM && m0 + threadIdx.x < M) {
       float ss = 0.0f;
 #pragma unroll
@@ -1030,6 +1070,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
             }
           }
     }
+    PR_PHASE(7);
     __syncthreads();  // LDS is refilled by the next tile's prologue
   }
 
@@ -2152,3 +2193,36 @@ int launch_fill_f32_hash(float* p, size_t n, uint32_t seed, float scale, float o
 }
 
 }  // namespace pr
+
+#ifdef PR_PHASE_STAMPS
+// Host access to the phase stamps of the diagnostic library (not part of the default
+// library's ABI).  pr_phase_stamps_layout gives the workgroups covered and the 64-bit words per
+// workgroup; pr_phase_stamps_read copies `words` words of the current device's stamps to host
+// memory after synchronising the device; pr_phase_stamps_clear synchronises the device and
+// zeroes them.
+// Each returns 0 or PR_ERR_HIP.
+extern "C" int pr_phase_stamps_layout(int* groups, int* words_per_group) {
+  *groups = pr::kStampGroups;
+  *words_per_group = pr::kStampWords;
+  return PR_OK;
+}
+
+extern "C" int pr_phase_stamps_read(unsigned long long* dst, int words) {
+  if (words < 0 || words > pr::kStampGroups * pr::kStampWords) return PR_ERR_INVALID_ARG;
+  if (hipDeviceSynchronize() != hipSuccess) return PR_ERR_HIP;
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(pr::pr_phase_stamps),
+                             (size_t)words * sizeof(unsigned long long)) == hipSuccess
+             ? PR_OK
+             : PR_ERR_HIP;
+}
+
+extern "C" int pr_phase_stamps_clear(void) {
+  void* p = nullptr;
+  if (hipDeviceSynchronize() != hipSuccess) return PR_ERR_HIP;  // no launch still stamping
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(pr::pr_phase_stamps)) != hipSuccess) return PR_ERR_HIP;
+  if (hipMemset(p, 0, sizeof(unsigned long long) * pr::kStampGroups * pr::kStampWords) !=
+      hipSuccess)
+    return PR_ERR_HIP;
+  return hipDeviceSynchronize() == hipSuccess ? PR_OK : PR_ERR_HIP;
+}
+#endif

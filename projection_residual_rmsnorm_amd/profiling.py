@@ -14,6 +14,9 @@
     python -m projection_residual_rmsnorm_amd.profiling runs <kernel_trace.csv> <out.md> \
         --kernel "<kernel name prefix>" --per-run N --labels "a,b,..." --command "<command>"
 
+`phases_summary` turns the in-kernel phase stamps of the diagnostic library (read by
+`bench.py --phases`) into a markdown table.
+
 `traffic` calibrates FETCH_SIZE and WRITE_SIZE (KiB per dispatch) against the plain 1 GiB
 device copies that `bench.py --copy-calibration` runs in the same process: the factor that
 turns each counter into bytes is (1 GiB) / (the counter's reading for one such copy).
@@ -280,10 +283,116 @@ def _code_only(text: str) -> str:
     return re.sub(r"\s+", " ", "".join(out)).strip()
 
 
+PHASES = ["main loop", "K groups' hand-over", "staging: r + y and row sums", "publish",
+          "row wait", "slot reads", "residual and output stores acknowledged"]
+
+
+def phase_stats(trial, flops_per_group: float = 0.0) -> dict:
+    """One launch's stamps (rows: workgroups of round 0; words as pr_phase_stamps documents)
+    reduced to medians over workgroups.  Times in µs from the 100 MHz constant clock; the main
+    loop's shader clock in MHz; with flops_per_group, the matrix cores' busy fraction of the
+    main loop at that clock (4096 dense bf16 flops per CU and clock)."""
+    import numpy as np
+    a = np.asarray(trial, dtype=np.uint64)
+    rt = a[:, 1:9].astype(np.int64)
+    t = (rt - rt[:, 0].min()) / 100.0
+    dur = np.diff(t, axis=1)
+    clock = (a[:, 11].astype(np.int64) - a[:, 10].astype(np.int64)) / dur[:, 0]
+    res = {
+        "workgroups": int(a.shape[0]),
+        "phases_us": [float(np.median(dur[:, p])) for p in range(dur.shape[1])],
+        "clock_mhz": float(np.median(clock)),
+        "clock_mhz_p10_p90": [float(np.percentile(clock, 10)), float(np.percentile(clock, 90))],
+        "span_us": float(t[:, 7].max()),
+        "main_loop_end_spread_us": float(t[:, 1].max() - t[:, 1].min()),
+        "after_last_main_loop_us": float(t[:, 7].max() - t[:, 1].max()),
+        "xcd": {},
+    }
+    if flops_per_group:
+        busy = flops_per_group / (4096.0 * clock * 1e6 * dur[:, 0] * 1e-6)
+        res["mfma_busy_main_loop"] = float(np.median(busy))
+    xcc = a[:, 0].astype(int)
+    for x in sorted(set(xcc.tolist())):
+        m = xcc == x
+        res["xcd"][x] = {"main_loop_us": float(np.median(dur[m, 0])),
+                         "clock_mhz": float(np.median(clock[m])),
+                         "main_loop_end_us": [float(t[m, 1].min()), float(t[m, 1].max())]}
+    return res
+
+
+def phases_summary(results: Dict[str, dict], command: str) -> str:
+    """results: workload -> {"shape": str, "config": str, "rounds": int (tile rounds of the
+    launch; only the first is stamped), "trials": [phase_stats(...), ...]}."""
+    import numpy as np
+    lines = ["# Single launch: in-kernel phase and clock stamps", "",
+             f"Command: `{command}`", "",
+             "Thread 0 of every workgroup stamps the constant 100 MHz clock at each phase "
+             "boundary of the single launch, and the shader clock around the main loop "
+             "(`libprojaddnorm_stamps.so`, the default sources compiled with "
+             "`PR_PHASE_STAMPS`). Each trial is the last of three back-to-back calls. Per "
+             "phase: the median over the launch's workgroups, as the median over trials [min–max "
+             "over trials], µs.", ""]
+    for name, r in results.items():
+        tr = r["trials"]
+        lines += [f"## {name}: {r['shape']}, {r['config']}", "",
+                  "| phase | µs |", "|---|---|"]
+        for p, ph in enumerate(PHASES):
+            v = [x["phases_us"][p] for x in tr]
+            lines.append(f"| {ph} | {np.median(v):.1f} [{min(v):.1f}–{max(v):.1f}] |")
+
+        def agg(key, fmt=".1f"):
+            v = [x[key] for x in tr]
+            return f"{np.median(v):{fmt}} [{min(v):{fmt}}–{max(v):{fmt}}]"
+        rounds = r.get("rounds", 1)
+        span = ("launch span" if rounds == 1 else
+                f"span of the first of {rounds} rounds (only it is stamped)")
+        lines += ["", f"- workgroups stamped per launch: {tr[0]['workgroups']}",
+                  f"- {span}, first start to last stores acknowledged: {agg('span_us')} µs",
+                  f"- spread of main-loop end times over workgroups: "
+                  f"{agg('main_loop_end_spread_us')} µs",
+                  f"- last stores acknowledged after the slowest main loop: "
+                  f"{agg('after_last_main_loop_us')} µs",
+                  f"- shader clock during the main loop: {agg('clock_mhz')} MHz (median over "
+                  f"workgroups; p10–p90 of the last trial "
+                  f"{tr[-1]['clock_mhz_p10_p90'][0]:.0f}–{tr[-1]['clock_mhz_p10_p90'][1]:.0f})"]
+        if "mfma_busy_main_loop" in tr[0]:
+            lines.append(f"- matrix cores busy during the main loop, at that clock: "
+                         f"{agg('mfma_busy_main_loop', '.2f')} (fraction; "
+                         "flops per workgroup ÷ (4096 × clock × main-loop time))")
+        lines += ["", "Per XCD, last trial:", "",
+                  "| XCC | main loop µs | clock MHz | main loops end at µs |", "|---|---|---|---|"]
+        for x, v in tr[-1]["xcd"].items():
+            lines.append(f"| {x} | {v['main_loop_us']:.1f} | {v['clock_mhz']:.0f} | "
+                         f"{v['main_loop_end_us'][0]:.1f}–{v['main_loop_end_us'][1]:.1f} |")
+        lines.append("")
+    return "\n".join(lines)
+
+
+def _without_stamps(text: str) -> str:
+    """The source without its diagnostic phase stamps: every #ifdef PR_PHASE_STAMPS block
+    (both branches: the stamp code, and the no-op PR_PHASE macro of the default build) and the
+    PR_PHASE(n) statements removed.  The default library's code is what remains."""
+    out, depth = [], 0  # depth > 0: inside a PR_PHASE_STAMPS block (counting nested #ifs)
+    for line in text.splitlines():
+        d = line.strip()
+        if depth:
+            if d.startswith("#if"):
+                depth += 1
+            elif d.startswith("#endif"):
+                depth -= 1
+            continue
+        if d == "#ifdef PR_PHASE_STAMPS":
+            depth = 1
+            continue
+        out.append(line)
+    return re.sub(r"\bPR_PHASE\(\d+\);", "", "\n".join(out))
+
+
 def source_digest(path: str) -> str:
-    """sha256 of a kernel source file's code (comments and whitespace do not count): counter
-    readings are void once the kernels' code changes."""
-    return hashlib.sha256(_code_only(open(path).read()).encode()).hexdigest()
+    """sha256 of a kernel source file's code as the default library compiles it (comments,
+    whitespace and the diagnostic phase stamps do not count): counter readings are void once
+    the kernels' code changes."""
+    return hashlib.sha256(_code_only(_without_stamps(open(path).read())).encode()).hexdigest()
 
 
 def main() -> None:

@@ -43,6 +43,57 @@ def test_library_exports_every_declared_symbol():
     assert pr.pr_strerror(pr.PR_ERR_SHAPE) == "unsupported shape"
 
 
+def test_phase_stamp_library_exports_the_same_abi():
+    """The diagnostic build (in-kernel phase stamps) exports every declared entry point and the
+    three stamp functions; the default library exports none of the latter.  Loaded in its own
+    handle, without touching a GPU."""
+    assert os.path.exists(pr.STAMPS_LIB_PATH), "build() makes both libraries"
+    lib = ctypes.CDLL(pr.STAMPS_LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    layout = lib.pr_phase_stamps_layout
+    layout.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    g, w = ctypes.c_int(), ctypes.c_int()
+    assert layout(ctypes.byref(g), ctypes.byref(w)) == 0 and (g.value, w.value) == (4096, 12)
+    for n in ("pr_phase_stamps_read", "pr_phase_stamps_clear"):
+        assert hasattr(lib, n), n
+    default = ctypes.CDLL(pr.LIB_PATH)
+    for n in ("pr_phase_stamps_layout", "pr_phase_stamps_read", "pr_phase_stamps_clear"):
+        assert not hasattr(default, n), n
+
+
+def test_phase_summary_from_synthetic_stamps():
+    """The phase table's arithmetic on stamps whose phases, clocks and XCDs are known."""
+    import numpy as np
+    from projection_residual_rmsnorm_amd import profiling
+    n = 16
+    a = np.zeros((n, 12), dtype=np.uint64)
+    base = 10_000
+    steps = [5000, 170, 340, 20, 450, 210, 480]  # 10 ns ticks: 50, 1.7, 3.4, ... µs
+    for g in range(n):
+        a[g, 0] = g % 8
+        t = base + g  # starts 10 ns apart
+        a[g, 1] = t
+        for p, dt in enumerate(steps):
+            t += dt + (g if p == 0 else 0)  # main loops differ by g ticks
+            a[g, 2 + p] = t
+        a[g, 10] = 1_000_000
+        a[g, 11] = 1_000_000 + int(round(1650.0 * (steps[0] + g) / 100.0))  # 1650 MHz
+    st = profiling.phase_stats(a, flops_per_group=2.0 * 256 * 128 * 4096)
+    assert st["workgroups"] == n
+    assert abs(st["phases_us"][0] - (5000 + 7.5) / 100) < 1e-9
+    assert [round(v, 6) for v in st["phases_us"][1:]] == [d / 100 for d in steps[1:]]
+    assert abs(st["clock_mhz"] - 1650.0) < 0.1
+    assert abs(st["main_loop_end_spread_us"] - 2 * (n - 1) / 100) < 1e-9
+    busy = 2.0 * 256 * 128 * 4096 / (4096 * 1650e6 * 50.075e-6)
+    assert abs(st["mfma_busy_main_loop"] - busy) < 1e-3
+    assert sorted(st["xcd"]) == list(range(8))
+    text = profiling.phases_summary({"o_proj": {"shape": "T=2048, K=4096, H=4096",
+                                                "config": "256x128 tiles", "trials": [st, st]}},
+                                    "python bench.py --phases o_proj")
+    assert "| main loop | 50.1 [50.1–50.1] |" in text and "1650" in text
+
+
 def test_validate():
     ok = dict(x=A, W=A * 2, residual_inout=A * 3, norm_w=A * 4, eps=1e-5, T=64, K=512, H=512,
               microchunk=16, norm_kind=0, out=A * 5)
@@ -569,6 +620,25 @@ def test_traffic_digest_ignores_comments_only(tmp_path):
     c.write_text('int f(int x) { return x + 2; }\nconst char* s = "//";\n')
     assert source_digest(str(a)) == source_digest(str(b))
     assert source_digest(str(a)) != source_digest(str(c))
+
+
+def test_traffic_digest_ignores_phase_stamps(tmp_path):
+    """The diagnostic phase stamps (PR_PHASE_STAMPS blocks, nested #ifs included, and the
+    PR_PHASE(n) statements), which the default library does not compile, leave the digest
+    unchanged; code outside them still counts."""
+    from projection_residual_rmsnorm_amd.profiling import source_digest
+    plain = "int f(int x) {\n  int y = x + 1;\n  return y;\n}\n"
+    stamped = ("#ifdef PR_PHASE_STAMPS\n__device__ int s[4];\n#if 1\nint g();\n#endif\n"
+               "#define PR_PHASE(p) g()\n#else\n#define PR_PHASE(p) ((void)0)\n#endif\n"
+               "int f(int x) {\n  PR_PHASE(0);\n  int y = x + 1;\n  PR_PHASE(12);\n"
+               "  return y;\n}\n")
+    changed = stamped.replace("x + 1", "x + 2")
+    paths = []
+    for i, text in enumerate((plain, stamped, changed)):
+        paths.append(tmp_path / f"{i}.hip")
+        paths[-1].write_text(text)
+    assert source_digest(str(paths[0])) == source_digest(str(paths[1]))
+    assert source_digest(str(paths[0])) != source_digest(str(paths[2]))
 
 
 def test_counter_summary_derivations(tmp_path):
