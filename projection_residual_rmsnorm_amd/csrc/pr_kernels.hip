@@ -798,13 +798,19 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     if ((rows_here * XG) % kNumXCDs == 0 && tiles_n % XG == 0) {
       // Each pair of XCDs computes whole tile rows, each XCD half of every row's columns
       // (workgroup b runs on XCD b % 8): a row's tiles finish together, an XCD that runs
-      // slower delays only its pair's rows, and each XCD reads half of the weight.
+      // slower delays only its pair's rows, and each XCD reads half of the weight.  The pairs
+      // are {0, 2}, {4, 6}, {1, 3}, {5, 7}: under MFMA load the odd-numbered XCDs ran a 3-7%
+      // lower clock than the even ones in every measurement on MI355X (in-kernel clock
+      // stamps on three GPUs), so like is paired with like and the faster pairs do not wait
+      // for a slower partner (their rows then finish, and write, before the slower pairs' do).
       const int xcd = blockIdx.x % kNumXCDs;
-      const int rows_g = rows_here * XG / kNumXCDs;  // tile rows of this XCD pair
-      const int cols_x = tiles_n / XG;               // column tiles per XCD
-      const int j = blockIdx.x / kNumXCDs;            // 0 .. rows_g * cols_x - 1
-      tm = (xcd / XG) * rows_g + j / cols_x;
-      tn = (xcd % XG) * cols_x + j % cols_x;
+      const int rows_g = rows_here * XG / kNumXCDs;   // tile rows of this XCD pair
+      const int cols_x = tiles_n / XG;                // column tiles per XCD
+      const int j = blockIdx.x / kNumXCDs;             // 0 .. rows_g * cols_x - 1
+      const int pair = ((xcd & 1) << 1) | (xcd >> 2);  // 0 .. 3
+      const int member = (xcd >> 1) & 1;               // which half of the row's columns
+      tm = pair * rows_g + j / cols_x;
+      tn = member * cols_x + j % cols_x;
     } else {
       tile_coords(xcd_logical(blockIdx.x, count), rows_here, tiles_n, &tm, &tn);
     }
