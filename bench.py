@@ -689,30 +689,52 @@ def tp_share(pr, torch, args) -> int:
 
 def phases(pr, torch, args) -> int:
     """In-kernel phase and clock stamps of the single launch on each workload (the diagnostic
-    library, selected by PR_PHASE_STAMPS=1 before the first library call)."""
+    library, selected by PR_PHASE_STAMPS=1 before the first library call).  A workload named
+    W:fp8 runs the FP8 single launch (activations quantised once, 256-token scale groups)."""
     import synth
     from projection_residual_rmsnorm_amd import profiling
     results = {}
     dev = "cuda:0"
-    for name in args.phases.split(","):
+    for spec in args.phases.split(","):
+        name, _, form = spec.partition(":")
+        fp8 = form == "fp8"
         wl = synth.WORKLOADS[name]
         T, K, H = wl.T, wl.K, wl.H
         d = synth.make_inputs(wl, seed=0)
         x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
-        Wp = torch.empty(K * H, dtype=torch.int16, device=dev)
-        pr.pr_prepare_weight(torch.from_numpy(d["W"].view(np.int16)).to(dev),
-                             pr.PR_WEIGHT_OUT_IN, Wp, K, H)
+        W_src = torch.from_numpy(d["W"].view(np.int16)).to(dev)
         r = torch.from_numpy(d["residual"]).to(dev)
         w = torch.from_numpy(d["norm_w"]).to(dev)
         out = torch.empty((T, H), dtype=torch.int16, device=dev)
+        stream = torch.cuda.Stream()
+        if fp8:
+            scale_rows = 256
+            wq = torch.empty((H, K), dtype=torch.uint8, device=dev)
+            sw = torch.empty(1, dtype=torch.float32, device=dev)
+            pr.pr_quantize_fp8(W_src, wq, sw, H, K, H, stream)
+            Wp = torch.empty(K * H, dtype=torch.uint8, device=dev)
+            pr.pr_prepare_weight_fp8(wq, pr.PR_WEIGHT_OUT_IN, Wp, K, H, stream)
+            xq = torch.empty((T, K), dtype=torch.uint8, device=dev)
+            sx = torch.empty(((T - 1) // scale_rows + 1,), dtype=torch.float32, device=dev)
+            pr.pr_quantize_fp8(x, xq, sx, T, K, scale_rows, stream)
+            call = lambda: pr.proj_add_rmsnorm_fp8(xq, sx, scale_rows, Wp, sw, r, w, d["eps"], T,
+                                                   K, H, wl.norm_kind, out, stream)
+        else:
+            Wp = torch.empty(K * H, dtype=torch.int16, device=dev)
+            pr.pr_prepare_weight(W_src, pr.PR_WEIGHT_OUT_IN, Wp, K, H)
+            call = lambda: pr.proj_add_rmsnorm_single_launch(x, Wp, r, w, d["eps"], T, K, H,
+                                                             wl.norm_kind, out, stream=stream)
         torch.cuda.synchronize()
         assert pr.loaded_library_path() == pr.STAMPS_LIB_PATH, pr.loaded_library_path()
+        # The FP8 launch takes the bf16 single launch's tile, with 8 waves, in two K groups
+        # where the bf16 launch uses them and K holds whole 128-deep stages.
         c = pr.pr_select(T, K, H, pr.PR_SINGLE_LAUNCH)
-        cfg = (f"{c['gemm_bm']}x{c['gemm_bn']} tiles, {c['gemm_waves']} waves"
-               + (f" in {c['gemm_kgroups']} K groups" if c["gemm_kgroups"] > 1 else ""))
-        stream = torch.cuda.Stream()
-        call = lambda: pr.proj_add_rmsnorm_single_launch(x, Wp, r, w, d["eps"], T, K, H,
-                                                         wl.norm_kind, out, stream=stream)
+        bm, bn = c["gemm_bm"], c["gemm_bn"]
+        waves = 8 if fp8 else c["gemm_waves"]
+        kgroups = c["gemm_kgroups"] if not fp8 or K % 128 == 0 else 1
+        cfg = (f"{bm}x{bn} tiles, {waves} waves"
+               + (f" in {kgroups} K groups" if kgroups > 1 else ""))
+        tiles = -(-T // bm) * (H // bn)
         for _ in range(max(args.warmup, 1)):
             call()
         trials = []
@@ -722,16 +744,16 @@ def phases(pr, torch, args) -> int:
                 call()
             a = pr.pr_phase_stamps()  # synchronises the device
             a = a[a[:, 1] != 0]
-            tiles = -(-T // c["gemm_bm"]) * (H // c["gemm_bn"])
             # the matrix cores' share is derived only for one-round grids (every workgroup one
             # whole tile)
-            fpg = 2.0 * c["gemm_bm"] * c["gemm_bn"] * K if a.shape[0] == tiles else 0.0
-            trials.append(profiling.phase_stats(a, fpg))
+            fpg = 2.0 * bm * bn * K if a.shape[0] == tiles else 0.0
+            trials.append(profiling.phase_stats(a, fpg, 8192.0 if fp8 else 4096.0))
         assert pr.pr_device_status(stream) == 0
-        results[name] = {"shape": f"T={T}, K={K}, H={H}", "config": cfg, "trials": trials,
+        results[spec] = {"shape": f"T={T}, K={K}, H={H}" + (", FP8 E4M3" if fp8 else ""),
+                         "config": cfg, "trials": trials,
                          "rounds": -(-tiles // trials[0]["workgroups"])}
         ph = trials[-1]["phases_us"]
-        log(f"{name}: main loop {ph[0]:.1f} us at {trials[-1]['clock_mhz']:.0f} MHz, "
+        log(f"{spec}: main loop {ph[0]:.1f} us at {trials[-1]['clock_mhz']:.0f} MHz, "
             f"span {trials[-1]['span_us']:.1f} us")
     text = profiling.phases_summary(results, "python bench.py " + " ".join(sys.argv[1:]))
     if args.phases_out:

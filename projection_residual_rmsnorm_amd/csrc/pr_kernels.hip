@@ -73,9 +73,11 @@ __device__ __forceinline__ void barrier_no_fence() {
 // LDS stage layouts (bytes).  Every direct global->LDS load writes 1 KiB contiguously (lane
 // l at offset 16 l), so the global side chooses which 16 bytes land where:
 //   A stage: [BM rows][4 slots][16 B], row r's slot p holding k-group p ^ f(r) with
-//            f(r) = ((r >> 1) ^ (r >> 3)) & 3.  One load fills 16 rows (64 B of each row, a
-//            coalesced read); the swizzle spreads the 32 rows of a fragment read over all
-//            banks both for 8-lane (32-bank) and for 16-lane (64-bank) LDS passes.
+//            f(r) = (r >> 2) & 3.  One load fills 16 rows (64 B of each row, a coalesced
+//            read).  The swizzle was chosen by measurement on gfx950: a 64-lane ds_read_b128
+//            of a fragment (rows l % 32, k-group 2s + l / 32) takes 4.4 cycles per CU with it,
+//            as a contiguous 1 KiB read does, against 8 with ((r >> 1) ^ (r >> 3)) & 3 and 16
+//            with no swizzle.
 //   B stage: [4 k-groups][BN columns][16 B] (lane-linear on both sides: the prepared weight
 //            already has this layout).
 // A 32x32x16 MFMA takes, per lane l, A[row l%32][k 8*(l/32)..+8] and B[k 8*(l/32)..+8][col l%32],
@@ -238,7 +240,7 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   for (int i = 0; i < A_LPW; ++i) {
     const int q = wave + NW * i;
     const int trow = q * 16 + (lane >> 2);
-    const int kg = (lane & 3) ^ (((trow >> 1) ^ (trow >> 3)) & 3);
+    const int kg = (lane & 3) ^ ((trow >> 2) & 3);
     int row = m0 + trow;
     row = row < M ? row : M - 1;
     if constexpr (FP8)
@@ -292,7 +294,7 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   // A fragment read: lane l reads tile row 32 rb + l%32, k-group 2s + l/32, i.e. slot
   // (2s + l/32) ^ f(row); f(row) depends only on l%32 (32 rb is a multiple of 16).
   const int a_r = lane & 31;
-  const int a_f = ((a_r >> 1) ^ (a_r >> 3)) & 3;
+  const int a_f = (a_r >> 2) & 3;
   const int a_lane0 = a_r * 64 + (((lane >> 5)) ^ a_f) * 16;      // substep 0
   const int a_lane1 = a_r * 64 + ((2 + (lane >> 5)) ^ a_f) * 16;  // substep 1
   auto load_frags = [&](const char* stage, int s, bf16x8_t* af, bf16x8_t* bfr) {

@@ -287,11 +287,12 @@ PHASES = ["main loop", "K groups' hand-over", "staging: r + y and row sums", "pu
           "row wait", "slot reads", "residual and output stores acknowledged"]
 
 
-def phase_stats(trial, flops_per_group: float = 0.0) -> dict:
+def phase_stats(trial, flops_per_group: float = 0.0, flops_per_clock: float = 4096.0) -> dict:
     """One launch's stamps (rows: workgroups of round 0; words as pr_phase_stamps documents)
     reduced to medians over workgroups.  Times in µs from the 100 MHz constant clock; the main
     loop's shader clock in MHz; with flops_per_group, the matrix cores' busy fraction of the
-    main loop at that clock (4096 dense bf16 flops per CU and clock)."""
+    main loop at that clock (flops_per_clock dense flops per CU and clock: 4096 for bf16, 8192
+    for fp8)."""
     import numpy as np
     a = np.asarray(trial, dtype=np.uint64)
     rt = a[:, 1:9].astype(np.int64)
@@ -309,8 +310,9 @@ def phase_stats(trial, flops_per_group: float = 0.0) -> dict:
         "xcd": {},
     }
     if flops_per_group:
-        busy = flops_per_group / (4096.0 * clock * 1e6 * dur[:, 0] * 1e-6)
+        busy = flops_per_group / (flops_per_clock * clock * 1e6 * dur[:, 0] * 1e-6)
         res["mfma_busy_main_loop"] = float(np.median(busy))
+        res["flops_per_clock"] = flops_per_clock
     xcc = a[:, 0].astype(int)
     for x in sorted(set(xcc.tolist())):
         m = xcc == x
@@ -358,7 +360,8 @@ def phases_summary(results: Dict[str, dict], command: str) -> str:
         if "mfma_busy_main_loop" in tr[0]:
             lines.append(f"- matrix cores busy during the main loop, at that clock: "
                          f"{agg('mfma_busy_main_loop', '.2f')} (fraction; "
-                         "flops per workgroup ÷ (4096 × clock × main-loop time))")
+                         f"flops per workgroup ÷ ({tr[0]['flops_per_clock']:.0f} × clock × "
+                         "main-loop time))")
         lines += ["", "Per XCD, last trial:", "",
                   "| XCC | main loop µs | clock MHz | main loops end at µs |", "|---|---|---|---|"]
         for x, v in tr[-1]["xcd"].items():
