@@ -278,6 +278,54 @@ def proj_add_rmsnorm_chunked(x_bits, W_bits, residual, norm_w, eps, norm_kind, m
 
 
 # --------------------------------------------------------------------------------------------
+# the conventional mode's rounding as a device takes it
+# --------------------------------------------------------------------------------------------
+FP32_UNIT_ROUNDOFF = 2.0 ** -24
+
+
+def conventional_roundings(x_bits, W_bits):
+    """The bf16 values a conventional projection may correctly emit for y = x . W^T.
+
+    The projection layer rounds its own fp32 sum of the K products to bf16, not the exact y
+    ("TPSP Design" section 1: the conventional region's projection emits the model dtype).
+    The products of two bf16 values are exact in fp32, and an fp32 sum of K terms, in any
+    order, differs from the exact sum by at most K * 2^-24 * sum_k |x_k w_k|.  So every bf16
+    value that rounds (to nearest) some number within that distance of y is a correct
+    result: the range [round(y - bound), round(y + bound)].  Returns (y, lo, hi), float64.
+    """
+    x = widen_bf16(x_bits)
+    W = widen_bf16(W_bits)
+    y = projection(x, W)
+    bound = W.shape[1] * FP32_UNIT_ROUNDOFF * projection(np.abs(x), np.abs(W))
+    return y, round_bf16(y - bound), round_bf16(y + bound)
+
+
+def proj_add_rmsnorm_conventional_taken(x_bits, W_bits, residual, norm_w, eps, norm_kind,
+                                        r_dev):
+    """The conventional mode with each element's bf16 y taken as the device rounded it, where
+    that rounding is a correct one (``conventional_roundings``).
+
+    The device adds its bf16 y to the fp32 residual in fp32, so its residual is fl32(r + yhat).
+    Its yhat is read back as the bf16 rounding of (r_dev - r) and kept where it lies in
+    [lo, hi] and fl32(r + yhat) reproduces r_dev exactly; every other element keeps the
+    round-to-nearest value of y, and the comparison then shows the device's error there.
+    Returns (r_new, out) in float64, as ``proj_add_rmsnorm``.
+    """
+    y, lo, hi = conventional_roundings(x_bits, W_bits)
+    r32 = np.asarray(residual, dtype=np.float32)
+    r = r32.astype(np.float64)
+    rd32 = np.asarray(r_dev, dtype=np.float32)
+    with np.errstate(invalid="ignore"):
+        taken = round_bf16(rd32.astype(np.float64) - r)
+        ok = ((taken >= lo) & (taken <= hi)
+              & ((r32 + taken.astype(np.float32)) == rd32))
+    yhat = np.where(ok, taken, round_bf16(y))
+    rp = residual_add(r, yhat)
+    g = norm_gain(widen_f32(norm_w), norm_kind)
+    return rp, rms_norm(rp, g, float(np.float32(eps)))
+
+
+# --------------------------------------------------------------------------------------------
 # comparison against a device result
 # --------------------------------------------------------------------------------------------
 OUT_MAX_ABS = 2e-2      # bf16 output: max |delta|

@@ -50,16 +50,19 @@ def test_random_shape_every_path(i, T, K, H, kind, mc, G):
     print(f"random case {i}: T={T} K={K} H={H} kind={kind} mc={mc} G={G}", flush=True)
     d = synth.make_custom(T, K, H, seed=1000 + i, norm_kind=kind, eps=1e-5 if i % 2 else 1e-6)
     dev = Device(d)
-    refs = {}
-    for mode in ("conventional", "fused"):
-        refs[mode] = oracle.proj_add_rmsnorm(d["x"], d["W"], d["residual"], d["norm_w"],
-                                             d["eps"], kind, mode)
+    fused_ref = oracle.proj_add_rmsnorm(d["x"], d["W"], d["residual"], d["norm_w"], d["eps"],
+                                        kind, "fused")
     for path in ("conventional", "pipeline", "single"):
         dev.reset()
         r_dev, out_bits = dev.run({"conventional": None, "pipeline": mc,
                                    "single": "single"}[path])
-        mode = "conventional" if path == "conventional" else "fused"
-        err = oracle.compare(r_dev, out_bits, *refs[mode])
+        if path == "conventional":
+            # the device's bf16 rounding of y, where it is a correct one
+            ref = oracle.proj_add_rmsnorm_conventional_taken(d["x"], d["W"], d["residual"],
+                                                             d["norm_w"], d["eps"], kind, r_dev)
+        else:
+            ref = fused_ref
+        err = oracle.compare(r_dev, out_bits, *ref)
         assert oracle.within_tolerance(err), (path, err)
 
     # FP8: the device's codes and scales equal the oracle's, then the region against the

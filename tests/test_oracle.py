@@ -299,6 +299,94 @@ def test_compare_accepts_own_rounding_and_rejects_planted_errors():
     assert not oracle.within_tolerance(oracle.compare(r_noy, out_bits, r_ref, out_ref))
 
 
+# ------------------------------------------------- conventional rounding as the device takes it
+def _fp32_sum(products, order):
+    """The fp32 sum of exact products, added one at a time in the given order."""
+    acc = np.float32(0.0)
+    for i in order:
+        acc = np.float32(acc + np.float32(products[i]))
+    return float(acc)
+
+
+def test_conventional_roundings_bound_holds_for_any_fp32_order():
+    """Brute force: fp32 sums of the K exact bf16 products, in sequential, reversed, pairwise
+    and random orders, always round (to bf16, nearest) into [lo, hi], and lie within the
+    bound of the exact y.  Cancellation-heavy rows (x and -x halves) are included."""
+    rng = np.random.default_rng(77)
+    T, K, H = 6, 96, 5
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    x[3, K // 2:] = -x[3, :K // 2]          # a row that nearly cancels
+    W = (rng.standard_normal((H, K)) / 8).astype(np.float32)
+    xb, Wb = _bits(x), _bits(W)
+    y, lo, hi = oracle.conventional_roundings(xb, Wb)
+    xw, Ww = oracle.widen_bf16(xb), oracle.widen_bf16(Wb)
+    bound = K * 2.0 ** -24 * (np.abs(xw) @ np.abs(Ww).T)
+    for t in range(T):
+        for h in range(H):
+            p = xw[t] * Ww[h]
+            assert math.fsum(p) == pytest.approx(y[t, h], abs=1e-12)
+            orders = [range(K), range(K - 1, -1, -1)] + [rng.permutation(K) for _ in range(20)]
+            sums = [_fp32_sum(p, o) for o in orders]
+            # pairwise (tree) order
+            level = [np.float32(v) for v in p]
+            while len(level) > 1:
+                level = [np.float32(level[i] + level[i + 1]) if i + 1 < len(level) else level[i]
+                         for i in range(0, len(level), 2)]
+            sums.append(float(level[0]))
+            for v in sums:
+                assert abs(v - y[t, h]) <= bound[t, h]
+                rb = oracle.round_bf16(np.array([v]))[0]
+                assert lo[t, h] <= rb <= hi[t, h]
+            assert lo[t, h] <= oracle.round_bf16(y[t, h:h + 1])[0] <= hi[t, h]
+
+
+def test_conventional_taken_equals_round_to_nearest_when_the_device_rounds_so():
+    d = synth.make_custom(24, 128, 64, seed=21)
+    r_ref, out_ref = oracle.proj_add_rmsnorm(d["x"], d["W"], d["residual"], d["norm_w"], d["eps"],
+                                             0, "conventional")
+    # the device's residual: fp32 add of the round-to-nearest bf16 y
+    y = oracle.round_bf16(oracle.projection(oracle.widen_bf16(d["x"]), oracle.widen_bf16(d["W"])))
+    r_dev = d["residual"].astype(np.float32) + y.astype(np.float32)
+    r2, out2 = oracle.proj_add_rmsnorm_conventional_taken(d["x"], d["W"], d["residual"],
+                                                          d["norm_w"], d["eps"], 0, r_dev)
+    np.testing.assert_array_equal(r2, r_ref)
+    np.testing.assert_array_equal(out2, out_ref)
+
+
+def test_conventional_taken_accepts_the_other_neighbour_only_near_a_midpoint():
+    """One element's y is placed a hair below the midpoint between two bf16 values: a device
+    that rounded up (its fp32 sum landed past the midpoint) is accepted and its output is
+    recomputed from its choice; a device two bf16 steps away is not, and the comparison then
+    fails; an element far from any midpoint admits only the nearest value."""
+    K = 4
+    # y[0,0] = 1 + 2^-8 - 2^-25: the midpoint of 1 and 1 + 2^-7 minus less than the fp32
+    # summation bound (4 * 2^-24 * (1 + 2^-8 + 2^-25), about 2^-22)
+    x = np.array([[1.0, 2.0 ** -8, -(2.0 ** -25), 0.0], [0.75, 0.0, 0.0, 0.0]], np.float32)
+    W = np.array([[1.0, 1.0, 1.0, 1.0], [1.0, 0.0, 0.0, 0.0]], np.float32)
+    xb, Wb = _bits(x), _bits(W)
+    y, lo, hi = oracle.conventional_roundings(xb, Wb)
+    assert y[0, 0] == 1.0 + 2.0 ** -8 - 2.0 ** -25
+    assert lo[0, 0] == 1.0 and hi[0, 0] == 1.0 + 2.0 ** -7     # both neighbours are correct
+    assert lo[1, 0] == hi[1, 0] == 0.75                       # exact: only one
+    r = np.array([[0.5, -0.25], [2.0, 1.0]], np.float32)
+    w = np.array([1.0, 1.0], np.float32)
+    eps = 1e-6
+    up = np.array([[1.0 + 2.0 ** -7, y[0, 1]], [0.75, y[1, 1]]])
+    r_dev = (r.astype(np.float64) + oracle.round_bf16(up)).astype(np.float32)
+    rp, out = oracle.proj_add_rmsnorm_conventional_taken(xb, Wb, r, w, eps, 0, r_dev)
+    assert rp[0, 0] == 0.5 + 1.0 + 2.0 ** -7
+    expect = rp[0] / math.sqrt((rp[0, 0] ** 2 + rp[0, 1] ** 2) / 2 + float(np.float32(eps)))
+    np.testing.assert_allclose(out[0], expect, rtol=1e-15)
+    # two steps up: not a correct rounding, so the nearest value is kept and the residual
+    # comparison shows the device's error
+    far = r_dev.copy()
+    far[0, 0] = np.float32(0.5 + 1.0 + 2 * 2.0 ** -7)
+    rp2, out2 = oracle.proj_add_rmsnorm_conventional_taken(xb, Wb, r, w, eps, 0, far)
+    assert rp2[0, 0] == 0.5 + 1.0
+    out_bits = oracle.bf16_bits_of(oracle.round_bf16(out2))
+    assert not oracle.within_tolerance(oracle.compare(far, out_bits, rp2, out2))
+
+
 # -------------------------------------------------------------------------------- SiluAndMul
 def test_silu_mul_hand_worked():
     """Hand-derived values.  silu(1) * 2 = 2 / (1 + e^-1) = 1.46211715...; bf16 spacing in [1, 2)
