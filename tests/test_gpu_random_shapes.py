@@ -90,3 +90,46 @@ def test_random_shape_every_path(i, T, K, H, kind, mc, G):
                                                  d["residual"], d["norm_w"], d["eps"], kind)
     err = oracle.compare(r.cpu().numpy(), bits(out), r_ref, out_ref)
     assert oracle.within_tolerance(err), ("fp8", err)
+
+
+def _hard_inputs(i, T, K, H, kind, mix):
+    d = synth.make_custom(T, K, H, seed=3000 + i, norm_kind=kind, eps=1e-6)
+    rng = np.random.default_rng(4000 + i)
+    if mix == "wide":      # x spread over 2^-8 .. 2^8
+        xf = (rng.standard_normal((T, K)) * np.exp2(rng.integers(-8, 9, (T, K)))).astype(np.float32)
+        d["x"] = synth.f32_to_bf16_bits(xf)
+    elif mix == "large_residual":
+        d["residual"] = (d["residual"] * np.float32(1000.0)).astype(np.float32)
+    elif mix == "zero_rows":  # all-zero x rows, and all-zero residual rows
+        d["x"][rng.random(T) < 0.2] = 0
+        d["residual"][rng.random(T) < 0.1] = 0.0
+    return d
+
+
+HARD = [(0, 700, 1024, 1536, 0, "wide"), (1, 1300, 512, 2048, 1, "wide"),
+        (2, 513, 2048, 768, 0, "large_residual"), (3, 2048, 1024, 1024, 1, "large_residual"),
+        (4, 999, 768, 1280, 0, "zero_rows"), (5, 257, 4096, 512, 1, "zero_rows")]
+
+
+@pytest.mark.parametrize("i,T,K,H,kind,mix", HARD)
+def test_hard_value_mixes(i, T, K, H, kind, mix):
+    """Every path against the oracle on value mixes beyond the workloads' normal draws: x spread
+    over sixteen binades, a residual a thousand times larger, and all-zero x and residual rows
+    (a zero row of x leaves y = 0; a zero residual row too gives r' = 0 and the norm's output
+    0 through eps)."""
+    print(f"hard case {i}: T={T} K={K} H={H} kind={kind} mix={mix}", flush=True)
+    d = _hard_inputs(i, T, K, H, kind, mix)
+    dev = Device(d)
+    fused_ref = oracle.proj_add_rmsnorm(d["x"], d["W"], d["residual"], d["norm_w"], d["eps"],
+                                        kind, "fused")
+    for path, mc in (("conventional", None), ("pipeline", 256), ("pipeline", 1000),
+                     ("single", "single")):
+        dev.reset()
+        r_dev, out_bits = dev.run(mc)
+        if path == "conventional":
+            ref = oracle.proj_add_rmsnorm_conventional_taken(d["x"], d["W"], d["residual"],
+                                                             d["norm_w"], d["eps"], kind, r_dev)
+        else:
+            ref = fused_ref
+        err = oracle.compare(r_dev, out_bits, *ref)
+        assert oracle.within_tolerance(err), (path, mc, err)
