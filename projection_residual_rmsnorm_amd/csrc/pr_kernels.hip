@@ -139,19 +139,22 @@ struct NoTail {
   __device__ void operator()(int, char*) const {}
 };
 
-// Tail hook that keeps the loop's load count exact with loads that cost next to nothing: every
-// lane of a refill reads the same 16 bytes (one cache line for the whole wave) into the buffer
-// being refilled, which is never read again.  The default refills re-read the last stage, a
-// stage's worth of L2 reads per refill that the wait after the loop has to drain.
-template <int LOADS, int NW>
+// Thin tail: the refills past the last stage keep the loop's load count exact with loads that
+// cost next to nothing, every lane of a refill reading the same 16 bytes (one cache line for
+// the whole wave) into the buffer being refilled, which is never read again.  The default
+// refills re-read the last stage, a stage's worth of L2 reads per refill that the wait after
+// the loop has to drain.  The main loop issues these refills itself (issue_stage_sel), with no
+// branch between them and the stage refills, so that all of them can be scheduled among the
+// step's MFMAs.
+template <typename T, typename = void>
+struct IsThin : std::false_type {};
+template <typename T>
+struct IsThin<T, std::void_t<decltype(T::kThin)>> : std::true_type {};
+
+template <int LOADS>
 struct ThinTail {
   static constexpr int kLoads = LOADS;
-  const char* src;
-  int wave;
-  __device__ void operator()(int, char* buf) const {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) load_to_lds16(src, 0u, buf + (wave + NW * i) * 1024);
-  }
+  static constexpr bool kThin = true;
 };
 
 // Main loop of one output tile: the product of A[m0 .. m0+BM)[k_begin .. k_begin + 32 KG nk)
@@ -262,6 +265,28 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
       FP8 ? reinterpret_cast<const char*>(Bp) + (long long)(k_begin / 16) * N * 16
           : reinterpret_cast<const char*>(Bp + (long long)(k_begin / 8) * N * 8);
   const long long b_half_bytes = (long long)(kBK / 8) * N * 16;
+  // With a thin tail: a stage's loads, or (thin) its thin refill, with no branch around the
+  // loads, so that they can be scheduled between the step's MFMAs.  A thin refill reads the
+  // first 16 bytes of stage 0 with every lane (the stage offset zeroed, the lane offsets
+  // masked) into the buffer being refilled, which is never read again.
+  auto issue_stage_sel = [&](int kt, char* buf, bool thin) {
+    const uint32_t keep = thin ? 0u : 0xFFFFFFFFu;  // wave-uniform
+    const long long ks = thin ? 0 : (long long)kt;
+#pragma unroll
+    for (int h = 0; h < KG; ++h) {
+      const long long hs = ks * KG + (thin ? 0 : h);
+      const char* a_base = a_base0 + hs * (kBK * 2);
+      const char* b_base = b_base0 + hs * b_half_bytes;
+      char* hb = buf + h * HALF;
+#pragma unroll
+      for (int i = 0; i < A_LPW; ++i)
+        load_to_lds16(a_base, a_off[i] & keep, hb + (wave + NW * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < B_LPW; ++i)
+        load_to_lds16(b_base, (b_lane_off + i * b_step) & keep,
+                      hb + A_RAW + (wave + NW * i) * 1024);
+    }
+  };
   auto issue_stage = [&](int kt, char* buf) {
 #pragma unroll
     for (int h = 0; h < KG; ++h) {
@@ -326,6 +351,17 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
+  };
+  // The same with the step's refill loads placed one after each of the first MFMAs (used with
+  // a thin tail: 3% faster on o_proj's two-K-group tile in ten alternating rounds, neutral to
+  // slightly slower on the 256 x 256 tiles, which keep all loads ahead of the MFMAs).
+  auto interleave_v = [&]() {
+#pragma unroll
+    for (int g = 0; g < TM * TN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (g < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (g < LPW) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
   };
 
   bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
@@ -478,18 +514,26 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   // every step; past the last stage it re-reads the last stage (an L2 hit) into the buffer
   // being refilled, which is never read again, or runs the tail hook.
   auto step = [&](int kt, char* cur, char* next, char* refill) {
-    if constexpr (Tail::kLoads >= 0) {
-      if (kt + P >= nk)
-        tail(kt + P - nk, refill);
-      else
-        issue_stage(kt + P, refill);
+    if constexpr (IsThin<Tail>::value) {
+      const bool thin = kt + P >= nk;
+      issue_stage_sel(thin ? 0 : kt + P, refill, thin);
+      load_frags(cur, 1, fa1, fb1);
+      mfmas(fa0, fb0);
+      interleave_v();
     } else {
-      issue_stage(min(kt + P, nk - 1), refill);
+      if constexpr (Tail::kLoads >= 0) {
+        if (kt + P >= nk)
+          tail(kt + P - nk, refill);
+        else
+          issue_stage(kt + P, refill);
+      } else {
+        issue_stage(min(kt + P, nk - 1), refill);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(cur, 1, fa1, fb1);
+      mfmas(fa0, fb0);
+      interleave();
     }
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(cur, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    interleave();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(PR_VMCNT(LPW * (P - 1)));  // stage kt+1 landed
     __builtin_amdgcn_s_waitcnt(PR_LGKMCNT0);
@@ -848,12 +892,8 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     // Two K groups: the last refills read one line (1.9% faster on o_proj in an interleaved
     // A/B); with one K group the tail's branch in every step cost 2-5% on 256 x 256 tiles.
     constexpr int LPW_ = KG * ((BM + BN) * kBK * 2 / 1024 / NW);
-    using TailT = std::conditional_t<(FP8 || SILU || KG == 1), NoTail, ThinTail<LPW_, NW>>;
-    TailT tail_hook{};
-    if constexpr (!(FP8 || SILU || KG == 1)) {
-      tail_hook.src = reinterpret_cast<const char*>(A);
-      tail_hook.wave = wave;
-    }
+    using TailT = std::conditional_t<(FP8 || SILU || KG == 1), NoTail, ThinTail<LPW_>>;
+    const TailT tail_hook{};
     const TileAcc<TM, TN> part_acc = tile_mainloop<BM, BN, NB, WM, WN, KG, TailT, FP8, SILU>(
         A, Bp, M, N, K, m0, n0, 0, FP8 ? K / (2 * kBK * KG) : K / (kBK * KG), tail_hook);
     // The ring's trailing refills (direct-to-LDS loads) have landed and every wave is past its
