@@ -80,6 +80,13 @@ __device__ __forceinline__ void barrier_no_fence() {
 //            with no swizzle.
 //   B stage: [4 k-groups][BN columns][16 B] (lane-linear on both sides: the prepared weight
 //            already has this layout).
+//   With two K groups (a stage of two 32-deep halves, bf16 or FP8) the x rows are loaded as
+//   whole 128-byte lines instead: one load fills 8 rows x 128 B into one [BM rows][8 slots]
+//   [16 B] block for both halves, row r's slot p holding k-group p ^ ((r >> 1) & 7) of the
+//   stage, and the two halves' B blocks follow it.  Measured on gfx950 with the o_proj tiles'
+//   real access pattern on every CU (a load-only probe): 42 B per clock per CU against 31 for
+//   two 16-row x 64-byte loads per 128-byte line; the swizzle reads a fragment in 4.25 cycles
+//   per CU, as a contiguous 1 KiB read does (8 with r & 7, 24 unswizzled).
 // A 32x32x16 MFMA takes, per lane l, A[row l%32][k 8*(l/32)..+8] and B[k 8*(l/32)..+8][col l%32],
 // one 16-byte read each.
 //
@@ -213,6 +220,11 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
 
   constexpr int HALF = A_RAW + B_BYTES;  // one 32-deep half of a stage
   constexpr int STAGE = KG * HALF;
+  // Whole-line x (two K groups): one [BM][8 slots][16 B] x block per stage, then the weight
+  // block of half h at WL_B0 + h * B_BYTES.
+  constexpr bool WL = KG == 2 && !SILU;
+  constexpr int WL_B0 = KG * A_BYTES;
+  constexpr int WL_ALPW = KG * A_LPW;  // whole-line x loads per wave per stage
   char* const sb0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
   char* const sb1 = ring_buffer<1, STAGE, BM, BN, NB, WM, WN>();
   // u is a compile-time constant at every call (unrolled loops), so this folds to one object.
@@ -253,6 +265,20 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
     else
       a_off[i] = (uint32_t)(row * K + kg * 8) * 2u;
   }
+  // Whole-line x loads: load i of wave w fills LDS kilobyte q = w + NW*i, rows 8q .. 8q+7 (lane
+  // l: tile row 8q + l/8, slot l%8, i.e. k-group (l%8) ^ ((row >> 1) & 7) of the stage).
+  uint32_t aw_off[WL ? WL_ALPW : 1];
+  if constexpr (WL) {
+#pragma unroll
+    for (int i = 0; i < WL_ALPW; ++i) {
+      const int q = wave + NW * i;
+      const int trow = q * 8 + (lane >> 3);
+      const int kg = (lane & 7) ^ ((trow >> 1) & 7);
+      int row = m0 + trow;
+      row = row < M ? row : M - 1;
+      aw_off[i] = FP8 ? (uint32_t)(row * K + kg * 16) : (uint32_t)(row * K + kg * 8) * 2u;
+    }
+  }
   int b_col = n0 + (wave % CG) * 64 + lane;
   b_col = b_col < N ? b_col : N - 1;
   const uint32_t b_lane_off = (uint32_t)(((wave / CG) * N + b_col) * 8) * 2u;
@@ -272,6 +298,21 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   auto issue_stage_sel = [&](int kt, char* buf, bool thin) {
     const uint32_t keep = thin ? 0u : 0xFFFFFFFFu;  // wave-uniform
     const long long ks = thin ? 0 : (long long)kt;
+    if constexpr (WL) {
+      const char* a_base = a_base0 + ks * (KG * kBK * 2);
+#pragma unroll
+      for (int i = 0; i < WL_ALPW; ++i)
+        load_to_lds16(a_base, aw_off[i] & keep, buf + (wave + NW * i) * 1024);
+#pragma unroll
+      for (int h = 0; h < KG; ++h) {
+        const char* b_base = b_base0 + (ks * KG + (thin ? 0 : h)) * b_half_bytes;
+#pragma unroll
+        for (int i = 0; i < B_LPW; ++i)
+          load_to_lds16(b_base, (b_lane_off + i * b_step) & keep,
+                        buf + WL_B0 + h * B_BYTES + (wave + NW * i) * 1024);
+      }
+      return;
+    }
 #pragma unroll
     for (int h = 0; h < KG; ++h) {
       const long long hs = ks * KG + (thin ? 0 : h);
@@ -288,6 +329,21 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
     }
   };
   auto issue_stage = [&](int kt, char* buf) {
+    if constexpr (WL) {
+      const char* a_base = a_base0 + (long long)kt * (KG * kBK * 2);
+#pragma unroll
+      for (int i = 0; i < WL_ALPW; ++i)
+        load_to_lds16(a_base, aw_off[i], buf + (wave + NW * i) * 1024);
+#pragma unroll
+      for (int h = 0; h < KG; ++h) {
+        const char* b_base = b_base0 + (kt * KG + h) * b_half_bytes;
+#pragma unroll
+        for (int i = 0; i < B_LPW; ++i)
+          load_to_lds16(b_base, b_lane_off + i * b_step,
+                        buf + WL_B0 + h * B_BYTES + (wave + NW * i) * 1024);
+      }
+      return;
+    }
 #pragma unroll
     for (int h = 0; h < KG; ++h) {
       const char* a_base = a_base0 + (kt * KG + h) * (kBK * 2);
@@ -322,7 +378,26 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   const int a_f = (a_r >> 2) & 3;
   const int a_lane0 = a_r * 64 + (((lane >> 5)) ^ a_f) * 16;      // substep 0
   const int a_lane1 = a_r * 64 + ((2 + (lane >> 5)) ^ a_f) * 16;  // substep 1
+  // Whole-line x: group g's half is slots 4g .. 4g+3 of the stage's 128-byte rows.
+  const int w_f = (a_r >> 1) & 7;
+  const int aw_lane0 = a_r * 128 + ((4 * kgrp + (lane >> 5)) ^ w_f) * 16;      // substep 0
+  const int aw_lane1 = a_r * 128 + ((4 * kgrp + 2 + (lane >> 5)) ^ w_f) * 16;  // substep 1
   auto load_frags = [&](const char* stage, int s, bf16x8_t* af, bf16x8_t* bfr) {
+    if constexpr (WL) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int rb = wm * TM + i;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(stage + rb * 4096 +
+                                                   (s == 0 ? aw_lane0 : aw_lane1));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = wn * WTN + j * 32;
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(
+            stage + WL_B0 + kgrp * B_BYTES + ((2 * s + (lane >> 5)) * BN + col + (lane & 31)) * 16);
+      }
+      return;
+    }
     const char* buf = KG == 1 ? stage : stage + kgrp * HALF;  // this group's half
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -372,21 +447,22 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
     // all of B's blocks of its wave tile).
     i32x8_t f8a[TM], f8b[TN];
     auto load_frags8 = [&](const char* stage) {
-      const char* buf = KG == 1 ? stage : stage + kgrp * HALF;  // this group's 64-deep half
+      // this group's 64-deep half: its B block, and its x slots (whole-line) or x block
+      const char* buf = KG == 1 ? stage : stage + kgrp * HALF;
+      const char* bblk = WL ? stage + WL_B0 + kgrp * B_BYTES : buf + A_RAW;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int col = wn * WTN + j * 32 + (lane & 31);
-        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(buf + A_RAW +
-                                                             ((lane >> 5) * BN + col) * 16);
-        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(buf + A_RAW +
-                                                             ((2 + (lane >> 5)) * BN + col) * 16);
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(bblk + ((lane >> 5) * BN + col) * 16);
+        const i32x4_t hi =
+            *reinterpret_cast<const i32x4_t*>(bblk + ((2 + (lane >> 5)) * BN + col) * 16);
         f8b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const char* rowp = buf + (wm * TM + i) * 2048;
-        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(rowp + a_lane0);
-        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(rowp + a_lane1);
+        const char* rowp = WL ? stage + (wm * TM + i) * 4096 : buf + (wm * TM + i) * 2048;
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(rowp + (WL ? aw_lane0 : a_lane0));
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(rowp + (WL ? aw_lane1 : a_lane1));
         f8a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     };
