@@ -178,8 +178,9 @@ int proj_add_rmsnorm_unfused(const uint16_t* x, const uint16_t* W, float* residu
  * synchronisation is involved).
  *
  * Same arguments and ownership as proj_add_rmsnorm_unfused.  Requires H = tile columns * n
- * with n <= 64 for one of the tiles the library instantiates (256 or 128 columns), else
- * PR_ERR_SHAPE.  The result agrees with the fused pipeline within rounding (the sum of squares
+ * with n <= 64 for one of the tiles the library instantiates (256, 192 or 128 columns; the
+ * 192 x 192 tile is this bf16 entry point's only, the FP8 and SiluAndMul forms take 256 or
+ * 128 columns), else PR_ERR_SHAPE.  The result agrees with the fused pipeline within rounding (the sum of squares
  * is taken in another order).  Uses a device workspace of at most T * H / 128 64-bit slots
  * and 3 + T / 128 words (status, completion counters, and the launch epoch, which the kernel
  * itself advances), shared by all calls on the device (calls on one device are sequential,

@@ -90,7 +90,7 @@ static int apply_forced_tile(int K, GemmCfg* g) {
   if (t != nullptr && t[0] != '\0') {
     int bm = 0, bn = 0;
     bool ok = std::sscanf(t, "%dx%d", &bm, &bn) == 2;
-    bool known = false;
+    bool known = bm == 192 && bn == 192;  // the single launch's 12-wave tile
     for (int c = 0; c < kNumTileCfgs; ++c) known |= (kTileBM[c] == bm && kTileBN[c] == bn);
     if (!ok || !known) return fail(PR_ERR_INVALID_ARG, "PR_FORCE_TILE=\"%s\" is not a tile", t);
     g->bm = bm;
@@ -99,8 +99,8 @@ static int apply_forced_tile(int K, GemmCfg* g) {
   const char* wv = std::getenv("PR_FORCE_WAVES");
   if (wv != nullptr && wv[0] != '\0') {
     const int waves = std::atoi(wv);
-    if (waves != 4 && waves != 8)
-      return fail(PR_ERR_INVALID_ARG, "PR_FORCE_WAVES=%s must be 4 or 8", wv);
+    if (waves != 4 && waves != 8 && waves != 12)
+      return fail(PR_ERR_INVALID_ARG, "PR_FORCE_WAVES=%s must be 4, 8 or 12", wv);
     g->waves = waves;
   }
   const char* st = std::getenv("PR_FORCE_STAGES");
@@ -147,19 +147,24 @@ constexpr double kWriteBW = 6.0e12;
 constexpr double kReadBW = 5.5e12;
 }  // namespace
 
-double model_gemm_time(int M, int N, int K, int c, int split, bool fp32_out, int cus) {
-  const int bm = kTileBM[c], bn = kTileBN[c];
+static double model_tile_time(int M, int N, int K, int bm, int bn, double eff, double rmax,
+                              int split, bool fp32_out, int cus) {
   const long long units = (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn) * split;
   const long long full = units / cus, rem = units % cus;
   const double tile_flops = 2.0 * bm * bn * ((double)K / split + kFixedK);
   const double chip = kChipRate * cus / kNumCUs;  // the share of the chip's rate
   auto round_t = [&](long long active) {
-    return tile_flops / std::min(kTileRmax[c], kTileEff[c] * chip / (double)active);
+    return tile_flops / std::min(rmax, eff * chip / (double)active);
   };
   double t = (double)full * round_t(cus) + (rem > 0 ? round_t(rem) : 0.0);
   const bool planes = fp32_out || split > 1;
   const double y_bytes = (planes ? 4.0 * split : 2.0) * M * (double)N;
   return t + y_bytes / kWriteBW + y_bytes / kReadBW;
+}
+
+double model_gemm_time(int M, int N, int K, int c, int split, bool fp32_out, int cus) {
+  return model_tile_time(M, N, K, kTileBM[c], kTileBN[c], kTileEff[c], kTileRmax[c], split,
+                         fp32_out, cus);
 }
 
 GemmCfg choose_gemm(int M, int N, int K, bool fp32_out, int cus) {
@@ -203,7 +208,13 @@ GemmCfg choose_gemm_unsplit(int M, int N, int K) {
 // keeping the 128 x 64 wave tile; on 2048 x 4096 x 4096, same box, three alternating rounds:
 // 0.0858-0.0861 ms against 0.0875-0.0886 ms for 4 waves and 0.0868-0.0887 ms for 8 waves in
 // one group, with every tile storing its residual after the row wait).
-GemmCfg choose_single(int M, int N, int K) {
+//
+// The single launch alone also has a 192 x 192 tile with 12 waves (three per SIMD, 96 x 32 wave
+// tiles), for widths that are a multiple of 192 where the 256-row tiles would leave CUs idle:
+// on 3000 x 3072 x 16384 it has 256 tiles against 144 of 256 x 256.  The model takes it with
+// efficiency 0.9 of the chip rate and a 5.5 TFLOP/s per-CU ceiling; with_192 = false keeps to
+// the tiles every form of the single launch has (the FP8 and SiluAndMul main loops).
+GemmCfg choose_single(int M, int N, int K, bool with_192) {
   GemmCfg best;
   best.bm = best.bn = 0;
   best.waves = 8;
@@ -216,6 +227,12 @@ GemmCfg choose_single(int M, int N, int K) {
       best.bm = kTileBM[c];
       best.bn = kTileBN[c];
     }
+  }
+  if (with_192 && N % 192 == 0 && N / 192 <= 64 &&
+      model_tile_time(M, N, K, 192, 192, 0.9, 5.5e12, 1, false, kNumCUs) < best_t * 0.999) {
+    best.bm = best.bn = 192;
+    best.waves = 12;
+    return best;
   }
   if (best.bm == 256 && best.bn == 128 &&
       (long long)((M + 255) / 256) * (N / 128) <= kNumCUs)
@@ -335,10 +352,10 @@ int decide(int T, int K, int H, int microchunk, pr_decision* d) {
     d->microchunk = T;
     d->n_chunks = T > 0 ? 1 : 0;
     d->last_valid = T;
-    g = choose_single(std::max(T, 1), H, K);
+    g = choose_single(std::max(T, 1), H, K, true);
     if (g.bm == 0)
-      return fail(PR_ERR_SHAPE, "single launch: H=%d is not a multiple of 128 with at most 64 "
-                  "tile columns", H);
+      return fail(PR_ERR_SHAPE, "single launch: H=%d is not a multiple of 128 or 192 with at "
+                  "most 64 tile columns", H);
   } else {
     d->microchunk = T;
     d->n_chunks = T > 0 ? 1 : 0;

@@ -39,6 +39,9 @@ GemmCfg choose_gemm_unsplit(int M, int N, int K);
 // kTileBM/kTileBN) and K split, including the add/norm's read of its output, when it has `cus`
 // CUs and that share of the chip's power to itself (kNumCUs: alone on the GPU).
 double model_gemm_time(int M, int N, int K, int c, int split, bool fp32_out, int cus);
+// Tile of the single launch for an M x N x K region (bm = 0 if N fits none); with_192 = false
+// keeps to the tiles that every single-launch form instantiates (FP8, SiluAndMul).
+GemmCfg choose_single(int M, int N, int K, bool with_192);
 
 // Error reporting: stores the message for pr_last_error() and returns `code`.
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

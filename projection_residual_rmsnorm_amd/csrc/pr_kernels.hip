@@ -189,6 +189,11 @@ struct ThinTail {
 // once a stage has landed, the workgroup converts it in place (each thread a few 16-byte
 // groups: x = gate / (1 + e^-gate) * up in fp32, rounded once to bf16, the arithmetic of the
 // stand-alone SiluAndMul kernel) and meets at a second barrier before any fragment read.
+// 32-deep halves per LDS stage: two for the K-group tiles (one half per group) and for the
+// 12-wave tile (three waves per SIMD, each running all four 16-deep substeps of a stage, so
+// that its x rows load as whole lines), one otherwise.
+constexpr int stage_halves(int kg, int nw) { return kg == 2 || nw == 12 ? 2 : 1; }
+
 template <int BM, int BN, int NB, int WM, int WN, int KG = 1, typename Tail = NoTail,
           bool FP8 = false, bool SILU = false>
 __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
@@ -205,26 +210,29 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   constexpr int B_BYTES = BN * kBK * 2;
   constexpr int A_LPW = A_BYTES / 1024 / NW;  // 1 KiB loads per wave per 32-deep half
   constexpr int B_LPW = B_BYTES / 1024 / NW;
-  constexpr int LPW = KG * ((SILU ? 2 : 1) * A_LPW + B_LPW);  // per stage
+  constexpr int HS = stage_halves(KG, NW);  // 32-deep halves per stage
+  constexpr int SUBS = 2 * HS / KG;         // 16-deep substeps per wave per stage
+  constexpr int LPW = HS * ((SILU ? 2 : 1) * A_LPW + B_LPW);  // per stage
   constexpr int P = NB - 1;  // stages in flight ahead of the one being computed
   constexpr int CG = BN / 64;
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "load split");
   static_assert(NW % CG == 0, "B loads: waves must cover whole k-groups");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
-  static_assert(NB >= 2 && NB <= 8 && NB * KG * (A_RAW + B_BYTES) <= 160 * 1024, "LDS budget");
+  static_assert(NB >= 2 && NB <= 8 && NB * HS * (A_RAW + B_BYTES) <= 160 * 1024, "LDS budget");
   static_assert(LPW * (P - 1) < 64, "vmcnt range");
   static_assert(KG == 1 || KG == 2, "one or two K groups");
   static_assert(Tail::kLoads < 0 || Tail::kLoads == LPW, "a tail refill issues a stage's loads");
   static_assert(!FP8 || Tail::kLoads < 0, "FP8: no tail hook");
-  static_assert(!SILU || (KG == 1 && Tail::kLoads < 0 && !FP8), "SILU: bf16, one K group");
+  static_assert(!SILU || (HS == 1 && Tail::kLoads < 0 && !FP8), "SILU: bf16, 32-deep stages");
+  static_assert(!FP8 || HS == KG, "FP8: one 64-deep half per K group");
 
   constexpr int HALF = A_RAW + B_BYTES;  // one 32-deep half of a stage
-  constexpr int STAGE = KG * HALF;
-  // Whole-line x (two K groups): one [BM][8 slots][16 B] x block per stage, then the weight
-  // block of half h at WL_B0 + h * B_BYTES.
-  constexpr bool WL = KG == 2 && !SILU;
-  constexpr int WL_B0 = KG * A_BYTES;
-  constexpr int WL_ALPW = KG * A_LPW;  // whole-line x loads per wave per stage
+  constexpr int STAGE = HS * HALF;
+  // Whole-line x (two halves per stage): one [BM][8 slots][16 B] x block per stage, then the
+  // weight block of half h at WL_B0 + h * B_BYTES.
+  constexpr bool WL = HS == 2 && !SILU;
+  constexpr int WL_B0 = HS * A_BYTES;
+  constexpr int WL_ALPW = HS * A_LPW;  // whole-line x loads per wave per stage
   char* const sb0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
   char* const sb1 = ring_buffer<1, STAGE, BM, BN, NB, WM, WN>();
   // u is a compile-time constant at every call (unrolled loops), so this folds to one object.
@@ -299,13 +307,13 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
     const uint32_t keep = thin ? 0u : 0xFFFFFFFFu;  // wave-uniform
     const long long ks = thin ? 0 : (long long)kt;
     if constexpr (WL) {
-      const char* a_base = a_base0 + ks * (KG * kBK * 2);
+      const char* a_base = a_base0 + ks * (HS * kBK * 2);
 #pragma unroll
       for (int i = 0; i < WL_ALPW; ++i)
         load_to_lds16(a_base, aw_off[i] & keep, buf + (wave + NW * i) * 1024);
 #pragma unroll
-      for (int h = 0; h < KG; ++h) {
-        const char* b_base = b_base0 + (ks * KG + (thin ? 0 : h)) * b_half_bytes;
+      for (int h = 0; h < HS; ++h) {
+        const char* b_base = b_base0 + (ks * HS + (thin ? 0 : h)) * b_half_bytes;
 #pragma unroll
         for (int i = 0; i < B_LPW; ++i)
           load_to_lds16(b_base, (b_lane_off + i * b_step) & keep,
@@ -314,8 +322,8 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
       return;
     }
 #pragma unroll
-    for (int h = 0; h < KG; ++h) {
-      const long long hs = ks * KG + (thin ? 0 : h);
+    for (int h = 0; h < HS; ++h) {
+      const long long hs = ks * HS + (thin ? 0 : h);
       const char* a_base = a_base0 + hs * (kBK * 2);
       const char* b_base = b_base0 + hs * b_half_bytes;
       char* hb = buf + h * HALF;
@@ -330,13 +338,13 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   };
   auto issue_stage = [&](int kt, char* buf) {
     if constexpr (WL) {
-      const char* a_base = a_base0 + (long long)kt * (KG * kBK * 2);
+      const char* a_base = a_base0 + (long long)kt * (HS * kBK * 2);
 #pragma unroll
       for (int i = 0; i < WL_ALPW; ++i)
         load_to_lds16(a_base, aw_off[i], buf + (wave + NW * i) * 1024);
 #pragma unroll
-      for (int h = 0; h < KG; ++h) {
-        const char* b_base = b_base0 + (kt * KG + h) * b_half_bytes;
+      for (int h = 0; h < HS; ++h) {
+        const char* b_base = b_base0 + (kt * HS + h) * b_half_bytes;
 #pragma unroll
         for (int i = 0; i < B_LPW; ++i)
           load_to_lds16(b_base, b_lane_off + i * b_step,
@@ -345,9 +353,9 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
       return;
     }
 #pragma unroll
-    for (int h = 0; h < KG; ++h) {
-      const char* a_base = a_base0 + (kt * KG + h) * (kBK * 2);
-      const char* b_base = b_base0 + (kt * KG + h) * b_half_bytes;
+    for (int h = 0; h < HS; ++h) {
+      const char* a_base = a_base0 + (kt * HS + h) * (kBK * 2);
+      const char* b_base = b_base0 + (kt * HS + h) * b_half_bytes;
       char* hb = buf + h * HALF;
 #pragma unroll
       for (int i = 0; i < A_LPW; ++i) load_to_lds16(a_base, a_off[i], hb + (wave + NW * i) * 1024);
@@ -378,23 +386,28 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   const int a_f = (a_r >> 2) & 3;
   const int a_lane0 = a_r * 64 + (((lane >> 5)) ^ a_f) * 16;      // substep 0
   const int a_lane1 = a_r * 64 + ((2 + (lane >> 5)) ^ a_f) * 16;  // substep 1
-  // Whole-line x: group g's half is slots 4g .. 4g+3 of the stage's 128-byte rows.
+  // Whole-line x: half h of a stage is slots 4h .. 4h+3 of its 128-byte rows.  With two K
+  // groups group g reads half g (substeps 0, 1); with one group a wave reads both halves
+  // (substeps 0 .. 3, substep s in half s / 2), and half 1's slot differs from half 0's in bit
+  // 2, which the swizzle leaves an XOR of 64 bytes.
   const int w_f = (a_r >> 1) & 7;
   const int aw_lane0 = a_r * 128 + ((4 * kgrp + (lane >> 5)) ^ w_f) * 16;      // substep 0
   const int aw_lane1 = a_r * 128 + ((4 * kgrp + 2 + (lane >> 5)) ^ w_f) * 16;  // substep 1
   auto load_frags = [&](const char* stage, int s, bf16x8_t* af, bf16x8_t* bfr) {
     if constexpr (WL) {
+      const int hs = s >> 1, sh = s & 1;  // (compile-time) half and substep within it
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int rb = wm * TM + i;
         af[i] = *reinterpret_cast<const bf16x8_t*>(stage + rb * 4096 +
-                                                   (s == 0 ? aw_lane0 : aw_lane1));
+                                                   ((sh == 0 ? aw_lane0 : aw_lane1) ^ (hs * 64)));
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int col = wn * WTN + j * 32;
         bfr[j] = *reinterpret_cast<const bf16x8_t*>(
-            stage + WL_B0 + kgrp * B_BYTES + ((2 * s + (lane >> 5)) * BN + col + (lane & 31)) * 16);
+            stage + WL_B0 + (kgrp + hs) * B_BYTES +
+            ((2 * sh + (lane >> 5)) * BN + col + (lane & 31)) * 16);
       }
       return;
     }
@@ -418,14 +431,17 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
-  // One LDS fragment read after each of the first TM+TN MFMAs, then the rest of the MFMAs.
+  // One LDS fragment read after each MFMA while both last (wave tiles with fewer MFMAs than
+  // fragments, such as 3 x 1 blocks, end with reads), then the rest.
   auto interleave = [&]() {
+    constexpr int NMF = TM * TN, NRD = TM + TN;
 #pragma unroll
-    for (int g = 0; g < TM + TN; ++g) {
+    for (int g = 0; g < (NMF < NRD ? NMF : NRD); ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
+    if constexpr (NMF >= NRD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
+    else __builtin_amdgcn_sched_group_barrier(0x100, NRD - NMF, 0);
   };
   // The same with the step's refill loads placed one after each of the first MFMAs (used with
   // a thin tail: 3% faster on o_proj's two-K-group tile in ten alternating rounds, neutral to
@@ -590,7 +606,22 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
   // every step; past the last stage it re-reads the last stage (an L2 hit) into the buffer
   // being refilled, which is never read again, or runs the tail hook.
   auto step = [&](int kt, char* cur, char* next, char* refill) {
-    if constexpr (IsThin<Tail>::value) {
+    if constexpr (SUBS == 4) {
+      // 12-wave tile: four substeps per stage, fragments double-buffered across them.
+      issue_stage(min(kt + P, nk - 1), refill);
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(cur, 1, fa1, fb1);
+      mfmas(fa0, fb0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(cur, 2, fa0, fb0);
+      mfmas(fa1, fb1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(cur, 3, fa1, fb1);
+      mfmas(fa0, fb0);
+      interleave();
+    } else if constexpr (IsThin<Tail>::value) {
       const bool thin = kt + P >= nk;
       issue_stage_sel(thin ? 0 : kt + P, refill, thin);
       load_frags(cur, 1, fa1, fb1);
@@ -878,7 +909,8 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
   constexpr int WTN = BN / WN;
   constexpr int ETM = WTM / 32;
   constexpr int TN = WTN / 32;
-  constexpr int STAGE = KG * ((SILU ? 2 * BM : BM) + BN) * kBK * 2;
+  constexpr int HS = stage_halves(KG, NW);  // 32-deep halves per stage of the main loop
+  constexpr int STAGE = HS * ((SILU ? 2 * BM : BM) + BN) * kBK * 2;
   static_assert(NB >= 3, "the norm epilogue uses the third ring buffer");
   static_assert((BM * WN + 2 * BM + 4) * 4 <= STAGE, "row partials fit in one stage buffer");
   char* const sb0 = ring_buffer<0, STAGE, BM, BN, NB, WM, WN>();
@@ -967,11 +999,11 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
 
     // Two K groups: the last refills read one line (1.9% faster on o_proj in an interleaved
     // A/B); with one K group the tail's branch in every step cost 2-5% on 256 x 256 tiles.
-    constexpr int LPW_ = KG * ((BM + BN) * kBK * 2 / 1024 / NW);
+    constexpr int LPW_ = HS * ((BM + BN) * kBK * 2 / 1024 / NW);
     using TailT = std::conditional_t<(FP8 || SILU || KG == 1), NoTail, ThinTail<LPW_>>;
     const TailT tail_hook{};
     const TileAcc<TM, TN> part_acc = tile_mainloop<BM, BN, NB, WM, WN, KG, TailT, FP8, SILU>(
-        A, Bp, M, N, K, m0, n0, 0, FP8 ? K / (2 * kBK * KG) : K / (kBK * KG), tail_hook);
+        A, Bp, M, N, K, m0, n0, 0, FP8 ? K / (2 * kBK * KG) : K / (kBK * HS), tail_hook);
     // The ring's trailing refills (direct-to-LDS loads) have landed and every wave is past its
     // last fragment read before the stage buffers are reused below.
     __builtin_amdgcn_s_waitcnt(PR_VMCNT(0));
@@ -2127,8 +2159,10 @@ int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, con
     return launch_pair(x, Wp, r, w, out, ws, M, N, K, eps, gemma, s, t0, t1);
   }
   const bool r256x128 = cfg.bm == 256 && cfg.bn == 128;
+  const bool r192 = cfg.bm == 192 && cfg.bn == 192;
   if (K % (2 * kBK) != 0 || N % cfg.bn != 0 || N / cfg.bn > 64 || cfg.split != 1 ||
-      (cfg.waves != 8 && !(cfg.waves == 4 && r256x128)) ||
+      (cfg.waves != 8 && !(cfg.waves == 4 && r256x128) && !(cfg.waves == 12 && r192)) ||
+      (r192 && cfg.waves != 12) ||
       (cfg.kgroups != 1 && !(cfg.kgroups == 2 && cfg.waves == 8 && r256x128)))
     return fail(PR_ERR_SHAPE, "single launch: N=%d K=%d with tile %dx%d split %d, %d waves, %d K "
                 "groups not supported", N, K, cfg.bm, cfg.bn, cfg.split, cfg.waves, cfg.kgroups);
@@ -2146,6 +2180,9 @@ int launch_gemm_add_rmsnorm(const uint16_t* x, const uint16_t* Wp, float* r, con
                                                  t0, t1);
   if (cfg.bm == 128 && cfg.bn == 128)
     return launch_single_t<128, 128, 4, 2, 4, 1>(x, Wp, r, w, out, ws, M, N, K, eps, gemma, s,
+                                                 t0, t1);
+  if (r192)
+    return launch_single_t<192, 192, 3, 2, 6, 1>(x, Wp, r, w, out, ws, M, N, K, eps, gemma, s,
                                                  t0, t1);
   return fail(PR_ERR_INVALID_ARG, "single launch: no tile %dx%d", cfg.bm, cfg.bn);
 }

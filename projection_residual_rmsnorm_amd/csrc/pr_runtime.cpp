@@ -807,6 +807,15 @@ int proj_add_rmsnorm_fp8(const uint8_t* x_q, const float* x_scales, int scale_ro
   GemmCfg g = cfg_of(d);
   if (g.split != 1)
     return fail(PR_ERR_UNSUPPORTED, "the K-split pair form has no FP8 variant");
+  if (g.bm == 192 && g.bn == 192) {  // the bf16 launch's 12-wave tile has no FP8 form
+    const GemmCfg b = choose_single(std::max(T, 1), H, K, false);
+    if (b.bm == 0)
+      return fail(PR_ERR_SHAPE, "single launch (FP8): H=%d is not a multiple of 128 with at "
+                  "most 64 tile columns", H);
+    g.bm = b.bm;
+    g.bn = b.bn;
+    g.kgroups = b.kgroups;
+  }
   g.waves = 8;
   if (!(g.bm == 256 && g.bn == 128 && g.kgroups == 2 && K % 128 == 0)) g.kgroups = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -920,6 +929,14 @@ int proj_add_rmsnorm_silu(const uint16_t* gate_up, const uint16_t* W, float* res
   GemmCfg g = cfg_of(d);
   if (g.split != 1)
     return fail(PR_ERR_UNSUPPORTED, "the K-split pair form has no SiluAndMul variant");
+  if (g.bm == 192 && g.bn == 192) {  // the bf16 launch's 12-wave tile has no SiluAndMul form
+    const GemmCfg b = choose_single(std::max(T, 1), H, K, false);
+    if (b.bm == 0)
+      return fail(PR_ERR_SHAPE, "single launch (SiluAndMul): H=%d is not a multiple of 128 with at "
+                  "most 64 tile columns", H);
+    g.bm = b.bm;
+    g.bn = b.bn;
+  }
   g.waves = 8;
   g.kgroups = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -107,7 +107,8 @@ def test_random_parity_small(T, K, H, kind):
 # (tile, waves per workgroup, K groups, K split) of every single-launch instantiation; split 2
 # is the pair form (each 256x256 tile's K halves on two workgroups)
 SINGLE_CFGS = [("256x256", 8, 1, 1), ("256x128", 8, 1, 1), ("256x128", 4, 1, 1),
-               ("256x128", 8, 2, 1), ("128x128", 8, 1, 1), ("256x256", 8, 1, 2)]
+               ("256x128", 8, 2, 1), ("128x128", 8, 1, 1), ("256x256", 8, 1, 2),
+               ("192x192", 12, 1, 1)]
 
 
 def _force_single(monkeypatch, tile, waves, kgroups, split):
@@ -166,8 +167,9 @@ def _identity_inputs(T, H, kind):
 def test_identity_weight_residual_is_x_bitwise(monkeypatch, path, kind):
     """W = I and r = 0: each output's projection has one nonzero product, so every path (any
     tile, K split or chunking) returns x exactly and the updated residual equals x bitwise;
-    the output is RMSNorm(x).  T = 300 leaves ragged tile rows and chunks."""
-    T, H = 300, 512
+    the output is RMSNorm(x).  T = 300 leaves ragged tile rows and chunks; H = 768 is a whole
+    number of tile columns for every tile."""
+    T, H = 300, 768
     if path.startswith("single "):
         _force_single(monkeypatch, *SINGLE_CFGS[[f"single {c[0]} {c[1]}w kg{c[2]} split{c[3]}"
                                                  for c in SINGLE_CFGS].index(path)])
@@ -201,13 +203,15 @@ def test_single_launch_random_parity_small(monkeypatch, tile, waves, kgroups, sp
                                                           ("256x256", 8, 1, 1, 4100, 8192),
                                                           ("256x256", 8, 1, 2, 4100, 8192),
                                                           ("256x256", 8, 1, 2, 1000, 1280),
-                                                          ("256x256", 8, 1, 2, 2048, 4096)])
+                                                          ("256x256", 8, 1, 2, 2048, 4096),
+                                                          ("192x192", 12, 1, 1, 4000, 3072)])
 def test_single_launch_several_rounds(monkeypatch, tile, waves, kgroups, split, T, H):
     """More tiles than resident workgroups: the launch runs several rounds of whole tile rows
     (256x128: 512 tiles in 2 rounds; 128x128: 1024 tiles in 2; 256x256: 17 x 32 tiles, the
     last round one ragged tile row).  Pairs: 17 x 32 tiles in 5 rounds of 4 tile rows (both
     exchange-region parities); 4 x 5 tiles in one round with 32 workgroups in same-XCD pairs and
-    8 in neighbour pairs; the o_proj shape in one full round."""
+    8 in neighbour pairs; the o_proj shape in one full round.  192x192: 21 x 16 tiles, a round
+    of 16 tile rows and one of 5."""
     _force_single(monkeypatch, tile, waves, kgroups, split)
     print(f"T={T} H={H}", flush=True)
     d = synth.make_custom(T, 256, H, seed=11)
@@ -284,7 +288,7 @@ def test_single_launch_agrees_with_pipeline():
 
 
 @pytest.mark.parametrize("tile,waves,split", [("256x128", 4, 1), ("256x256", 8, 1),
-                                              ("256x256", 8, 2)])
+                                              ("256x256", 8, 2), ("192x192", 12, 1)])
 def test_single_launch_wait_limit_reports(monkeypatch, tile, waves, split):
     """Row reads that look for an epoch no slot carries (set from the host) give up after 64
     polls each; every kernel still ends.  The call leaves no state behind: no output row is
@@ -297,7 +301,7 @@ def test_single_launch_wait_limit_reports(monkeypatch, tile, waves, split):
     _force_single(monkeypatch, tile, waves, 1, split)
     monkeypatch.setenv("PR_FAULT_INJECT", "wait")
     monkeypatch.setenv("PR_SPIN_LIMIT", "64")
-    d = synth.make_custom(600, 256, 1024, seed=4)
+    d = synth.make_custom(600, 256, 1536, seed=4)
     dev = Device(d)
     print(f"forced give-up: tile {tile}, {waves} waves, split {split}", flush=True)
     pr.proj_add_rmsnorm_single_launch(dev.x, dev.Wp, dev.r, dev.w, d["eps"], dev.T, dev.K, dev.H,

@@ -255,7 +255,14 @@ def test_select_single_launch():
         d = pr.pr_select(T, K, H, pr.PR_SINGLE_LAUNCH)
         assert d["path"] == pr.PR_PATH_SINGLE
         assert H % d["gemm_bn"] == 0 and H // d["gemm_bn"] <= 64
-        assert d["gemm_waves"] in (4, 8)
+        assert d["gemm_waves"] in (4, 8) or (d["gemm_bm"], d["gemm_bn"], d["gemm_waves"]) == (
+            192, 192, 12)
+    # 3000 x 3072: 144 tiles of 256 x 256 would leave 112 CUs idle; 16 x 16 tiles of 192 x 192
+    # with 12 waves fill the GPU in one round
+    d = pr.pr_select(3000, 16384, 3072, pr.PR_SINGLE_LAUNCH)
+    assert (d["gemm_bm"], d["gemm_bn"], d["gemm_waves"], d["gemm_kgroups"]) == (192, 192, 12, 1)
+    # a width only the 192-column tile divides (H = 576) is accepted
+    assert pr.pr_select(1000, 4096, 576, pr.PR_SINGLE_LAUNCH)["gemm_bn"] == 192
     with pytest.MonkeyPatch.context() as mp:
         mp.setenv("PR_FORCE_WAVES", "4")
         d = pr.pr_select(2048, 4096, 4096, pr.PR_SINGLE_LAUNCH)
