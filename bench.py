@@ -209,14 +209,14 @@ def clock_settings() -> dict:
             "xcds": len(gfx), "mclk_MHz": mhz(mem.get("clk"))}
 
 
-def tune_sweep(pr, torch, args) -> int:
-    """Token-threshold search over the long-prefill sweep (K = H = 8192): every chunk size is
-    checked against the conventional path, then timed; prints the table and the crossover."""
+def threshold_sweep(pr, args) -> dict:
+    """Token-threshold search over the long-prefill sweep (K = H = 8192, T in the sweep grid):
+    the library's tuner checks every fused candidate (each chunk size and the single launch)
+    against the conventional path on its own uniform synthetic data, times all of them
+    round-robin, and derives the crossover token count.  Times are the tuner's medians."""
     import synth
     grid = list(synth.SWEEP_T)
     mcs = [512, 1024, 2048]
-    stream = torch.cuda.Stream()
-    torch.cuda.set_stream(stream)
     t0 = time.perf_counter()
     rep = pr.pr_tune([8192], [8192], pr.PR_NORM_STANDARD, grid, mcs, reps=max(args.steps // 5, 5))
     rows = []
@@ -228,11 +228,21 @@ def tune_sweep(pr, torch, args) -> int:
                                   for j, m in enumerate(mcs)},
                      "single_launch_ms": t[2 + len(mcs)] * 1e3 if t[2 + len(mcs)] > 0 else None})
     thr = rep["threshold_tokens"]
-    print(json.dumps({"tune_sweep": {"K": 8192, "H": 8192, "T_grid": grid, "microchunks": mcs,
-                                     "rows": rows, "n_checked": rep["n_checked"],
-                                     "n_rejected": rep["n_rejected"],
-                                     "threshold_tokens": None if thr == pr.INT32_MAX else thr,
-                                     "seconds": time.perf_counter() - t0}}), flush=True)
+    res = {"K": 8192, "H": 8192, "T_grid": grid, "microchunks": mcs, "rows": rows,
+           "n_checked": rep["n_checked"], "n_rejected": rep["n_rejected"],
+           "threshold_tokens": None if thr == pr.INT32_MAX else thr,
+           "seconds": time.perf_counter() - t0}
+    log(f"threshold sweep (K=H=8192): crossover T = {res['threshold_tokens']} "
+        f"({res['n_checked']} candidates checked, {res['n_rejected']} rejected, "
+        f"{res['seconds']:.1f} s)")
+    return res
+
+
+def tune_sweep(pr, torch, args) -> int:
+    """The threshold sweep alone: prints its table as one JSON line."""
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    print(json.dumps({"tune_sweep": threshold_sweep(pr, args)}), flush=True)
     return 0
 
 
@@ -960,6 +970,8 @@ def main() -> int:
                                   min(wl.microchunks), args, stream)
         if wl.name == "o_proj":
             result["down_proj"] = down_proj_entry(pr, torch, args, stream)
+            # the fused-or-conventional crossover of the long-prefill sweep (a few seconds)
+            result["threshold_sweep"] = threshold_sweep(pr, args)
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
