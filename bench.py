@@ -750,8 +750,8 @@ def phases(pr, torch, args) -> int:
             pr.pr_phase_stamps(clear=True)
             call()
             n_wg = int(np.count_nonzero(pr.pr_phase_stamps()[:, 1]))
-            bm, bn = next((m, n) for m, n in ((256, 256), (256, 128), (128, 128))
-                          if H % n == 0 and -(-T // m) * (H // n) == n_wg)
+            bm, bn = next(((m, n) for m, n in ((256, 256), (256, 128), (128, 128))
+                           if H % n == 0 and -(-T // m) * (H // n) == n_wg), (bm, bn))
             kgroups = 2 if (bm, bn) == (256, 128) and K % 128 == 0 else 1
         cfg = (f"{bm}x{bn} tiles, {waves} waves"
                + (f" in {kgroups} K groups" if kgroups > 1 else ""))
