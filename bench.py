@@ -970,8 +970,11 @@ def main() -> int:
                                   min(wl.microchunks), args, stream)
         if wl.name == "o_proj":
             result["down_proj"] = down_proj_entry(pr, torch, args, stream)
-            # the fused-or-conventional crossover of the long-prefill sweep (a few seconds)
-            result["threshold_sweep"] = threshold_sweep(pr, args)
+            # the fused-or-conventional crossover of the long-prefill sweep (a few seconds; it
+            # tunes, so not with --no-tune, which the profiled runs pass: the tuner's CU-masked
+            # streams make rocprofv3 crash in its exit handler before it writes its files)
+            if not args.no_tune:
+                result["threshold_sweep"] = threshold_sweep(pr, args)
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
