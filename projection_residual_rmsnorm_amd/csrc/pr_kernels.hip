@@ -27,10 +27,14 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void global_cvoid_t;
 
 constexpr int kBK = 32;  // K depth of one LDS stage (4 groups of 8 bf16 = 64 bytes per row)
+// Word 3 of a gfx9 buffer resource for raw (untyped) accesses: data format 32 bits, so the
+// hardware range-checks each access against the resource's byte count.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 // The builtin (unlike inline asm) is understood by the compiler's own wait insertion, which
@@ -424,12 +428,17 @@ __device__ __forceinline__ TileAcc<BM / WM / 32, BN / WN / 32> tile_mainloop(
           buf + A_RAW + ((2 * s + (lane >> 5)) * BN + col + (lane & 31)) * 16);
     }
   };
+  // Blocks in snake order: each MFMA shares an operand with the one before it, so fewer
+  // matrix-core inputs toggle (the clock under MFMA load is power-limited).  Every accumulator
+  // still takes its k-steps in the same order, so results are unchanged.
   auto mfmas = [&](const bf16x8_t* af, const bf16x8_t* bfr) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int jj = 0; jj < TN; ++jj) {
+        const int j = (i & 1) ? TN - 1 - jj : jj;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
   };
   // One LDS fragment read after each MFMA while both last (wave tiles with fewer MFMAs than
   // fragments, such as 3 x 1 blocks, end with reads), then the rest.
@@ -1216,6 +1225,16 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
     } else {
       const float4 g = *reinterpret_cast<const float4*>(w + col);
       const float gx = g.x + g0, gy = g.y + g0, gz = g.z + g0, gw = g.w + g0;
+      // Tiles narrower than 256 columns store at device scope (sc1): the lines go through the
+      // XCD's L2 to memory as they are written, so the launch's end has fewer dirty lines to
+      // write back.  256x256 tiles, whose rows finish further apart, keep streaming stores.
+      constexpr bool kDeviceScopeStores = BN < 256;
+      constexpr int kSc1 = 16;  // cache-policy operand of a buffer store: sc1
+      const int vrows = min(BM, M - m0);
+      const __amdgpu_buffer_rsrc_t rs_r = __builtin_amdgcn_make_buffer_rsrc(
+          R + (long long)m0 * N, 0, vrows * N * 4, kBufferRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rs_o = __builtin_amdgcn_make_buffer_rsrc(
+          out + (long long)m0 * N, 0, vrows * N * 2, kBufferRsrcWord3);
 #pragma unroll
       for (int i = 0; i < ETM; ++i)
 #pragma unroll
@@ -1226,18 +1245,28 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
             const int row = m0 + trow;
             if (row < M) {
               const float4 v = keep[(i * 2 + h) * NR + rr];
-              // Streaming stores: the updated residual and the output are not read again here.
-              __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
-                                          reinterpret_cast<f32x4_t*>(R + (long long)row * N + col));
+              // The updated residual and the output are not read again here.
+              if constexpr (kDeviceScopeStores)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4_t, f32x4_t{v.x, v.y, v.z, v.w}), rs_r,
+                    (trow * N + col) * 4, 0, kSc1);
+              else
+                __builtin_nontemporal_store(
+                    f32x4_t{v.x, v.y, v.z, v.w},
+                    reinterpret_cast<f32x4_t*>(R + (long long)row * N + col));
               const float inv = sinv[trow];
               const uint32_t o0 = f32_to_bf16_rne(v.x * inv * gx);
               const uint32_t o1 = f32_to_bf16_rne(v.y * inv * gy);
               const uint32_t o2 = f32_to_bf16_rne(v.z * inv * gz);
               const uint32_t o3 = f32_to_bf16_rne(v.w * inv * gw);
-              __builtin_nontemporal_store(
-                  (unsigned long long)(o0 | (o1 << 16)) |
-                      ((unsigned long long)(o2 | (o3 << 16)) << 32),
-                  reinterpret_cast<unsigned long long*>(out + (long long)row * N + col));
+              if constexpr (kDeviceScopeStores)
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{o0 | (o1 << 16), o2 | (o3 << 16)},
+                                                      rs_o, (trow * N + col) * 2, 0, kSc1);
+              else
+                __builtin_nontemporal_store(
+                    (unsigned long long)(o0 | (o1 << 16)) |
+                        ((unsigned long long)(o2 | (o3 << 16)) << 32),
+                    reinterpret_cast<unsigned long long*>(out + (long long)row * N + col));
             }
           }
     }
