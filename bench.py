@@ -774,7 +774,10 @@ def phases(pr, torch, args) -> int:
         ph = trials[-1]["phases_us"]
         log(f"{spec}: main loop {ph[0]:.1f} us at {trials[-1]['clock_mhz']:.0f} MHz, "
             f"span {trials[-1]['span_us']:.1f} us")
-    text = profiling.phases_summary(results, "python bench.py " + " ".join(sys.argv[1:]))
+    # The command as run from the repository root (the output path made relative to it).
+    argv = [os.path.relpath(a, ROOT) if os.path.isabs(a) and a.startswith(ROOT) else a
+            for a in sys.argv[1:]]
+    text = profiling.phases_summary(results, "python bench.py " + " ".join(argv))
     if args.phases_out:
         with open(args.phases_out, "w") as f:
             f.write(text)
