@@ -35,6 +35,8 @@ constexpr int kBK = 32;  // K depth of one LDS stage (4 groups of 8 bf16 = 64 by
 // Word 3 of a gfx9 buffer resource for raw (untyped) accesses: data format 32 bits, so the
 // hardware range-checks each access against the resource's byte count.
 constexpr int kBufferRsrcWord3 = 0x00020000;
+// Cache-policy operand of a buffer store: sc1 (device scope).
+constexpr int kStoreSc1 = 16;
 
 // s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 // The builtin (unlike inline asm) is understood by the compiler's own wait insertion, which
@@ -1229,7 +1231,6 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
       // XCD's L2 to memory as they are written, so the launch's end has fewer dirty lines to
       // write back.  256x256 tiles, whose rows finish further apart, keep streaming stores.
       constexpr bool kDeviceScopeStores = BN < 256;
-      constexpr int kSc1 = 16;  // cache-policy operand of a buffer store: sc1
       const int vrows = min(BM, M - m0);
       const __amdgpu_buffer_rsrc_t rs_r = __builtin_amdgcn_make_buffer_rsrc(
           R + (long long)m0 * N, 0, vrows * N * 4, kBufferRsrcWord3);
@@ -1249,7 +1250,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
               if constexpr (kDeviceScopeStores)
                 __builtin_amdgcn_raw_buffer_store_b128(
                     __builtin_bit_cast(u32x4_t, f32x4_t{v.x, v.y, v.z, v.w}), rs_r,
-                    (trow * N + col) * 4, 0, kSc1);
+                    (trow * N + col) * 4, 0, kStoreSc1);
               else
                 __builtin_nontemporal_store(
                     f32x4_t{v.x, v.y, v.z, v.w},
@@ -1261,7 +1262,7 @@ __global__ void __launch_bounds__(WM* WN * KG * 64, 1)
               const uint32_t o3 = f32_to_bf16_rne(v.w * inv * gw);
               if constexpr (kDeviceScopeStores)
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{o0 | (o1 << 16), o2 | (o3 << 16)},
-                                                      rs_o, (trow * N + col) * 2, 0, kSc1);
+                                                      rs_o, (trow * N + col) * 2, 0, kStoreSc1);
               else
                 __builtin_nontemporal_store(
                     (unsigned long long)(o0 | (o1 << 16)) |
@@ -1744,7 +1745,7 @@ __global__ void __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR)
   // iterations later, after every wave has passed the barrier of the iteration in between
   // (and so has finished reading it).
   __shared__ float part[2][RPB][S];
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // row bases are uniform
   const int lane = threadIdx.x & 63;
   const int row_in = wave / WPR;
   const int wr = wave % WPR;
@@ -1814,10 +1815,16 @@ __global__ void __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR)
                              rv[i].w + v[i].w);
         }
       }
+      // The residual and the output are stored at device scope (sc1): the lines go through the
+      // L2 to memory as they are written instead of staying dirty until the launch's end.
+      const __amdgpu_buffer_rsrc_t rs_r =
+          __builtin_amdgcn_make_buffer_rsrc(r + base, 0, (H / WPR) * 4, kBufferRsrcWord3);
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int c = (i * 64 + lane) * 4;
-        *reinterpret_cast<float4*>(r + base + c) = v[i];
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4_t, f32x4_t{v[i].x, v[i].y, v[i].z, v[i].w}), rs_r, c * 4, 0,
+            kStoreSc1);
       }
 #pragma unroll
       for (int j = 0; j < SW; ++j) {
@@ -1843,7 +1850,8 @@ __global__ void __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR)
     }
     if (live) {
       const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-      uint16_t* oc = out + base;
+      const __amdgpu_buffer_rsrc_t rs_o =
+          __builtin_amdgcn_make_buffer_rsrc(out + base, 0, (H / WPR) * 2, kBufferRsrcWord3);
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int c = (i * 64 + lane) * 4;
@@ -1852,7 +1860,8 @@ __global__ void __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR)
         const uint32_t o1 = f32_to_bf16_rne(v[i].y * inv * (g.y + g0));
         const uint32_t o2 = f32_to_bf16_rne(v[i].z * inv * (g.z + g0));
         const uint32_t o3 = f32_to_bf16_rne(v[i].w * inv * (g.w + g0));
-        *reinterpret_cast<uint2*>(oc + c) = make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{o0 | (o1 << 16), o2 | (o3 << 16)}, rs_o,
+                                              c * 2, 0, kStoreSc1);
       }
     }
   }
