@@ -24,8 +24,9 @@ __device__ __forceinline__ float bf16_f32(uint32_t b) { return __uint_as_float(b
 // HBM-bound (6 bytes per element of x).  Workgroups stride over rows and threads over a row's
 // 16-byte vectors of 8 columns, U vectors per step with all their loads issued before any use,
 // so no index needs a division.  gate and up are read once, with streaming loads, so that
-// they do not evict the projection's weight from the Infinity Cache (x, which the projection
-// reads next, is stored normally).  The exponential is the device's native one (__expf, a
+// they do not evict the projection's weight from the Infinity Cache.  x is stored at device
+// scope (sc1 buffer stores), so its lines go through the L2 to memory as they are written
+// instead of staying dirty until the launch's end.  The exponential is the device's native one (__expf, a
 // scaled v_exp_f32: relative error near 1e-6, far below the half ulp of the bf16 result) and
 // the quotient an ordinary IEEE division.  Zero columns of the load-time padding give zeros.
 // --------------------------------------------------------------------------------------------
@@ -40,7 +41,9 @@ __global__ void __launch_bounds__(kSiluThreads) silu_mul_kernel(const uint16_t* 
   for (int t = blockIdx.x; t < T; t += gridDim.x) {
     const uint4* grow = reinterpret_cast<const uint4*>(gu + (long long)t * 2 * K);
     const uint4* urow = grow + kvec;
-    uint4* xrow = reinterpret_cast<uint4*>(x + (long long)t * K);
+    // Word 3 of a gfx9 buffer resource for raw accesses (data format 32 bits: range-checked).
+    const __amdgpu_buffer_rsrc_t rs_x =
+        __builtin_amdgcn_make_buffer_rsrc(x + (long long)t * K, 0, K * 2, 0x00020000);
     for (int c0 = threadIdx.x; c0 < kvec; c0 += kSiluThreads * U) {
       uint4 g[U], u[U];
 #pragma unroll
@@ -68,7 +71,8 @@ __global__ void __launch_bounds__(kSiluThreads) silu_mul_kernel(const uint16_t* 
             const float x1 = g1 / (1.0f + __expf(-g1)) * u1;
             o[j] = bf16_rne(x0) | (bf16_rne(x1) << 16);
           }
-          xrow[c] = make_uint4(o[0], o[1], o[2], o[3]);
+          __builtin_amdgcn_raw_buffer_store_b128(v4u{o[0], o[1], o[2], o[3]}, rs_x, c * 16, 0,
+                                                 16 /* sc1 */);
         }
       }
     }
