@@ -241,9 +241,17 @@ def test_largest_workload_every_path():
         assert np.all(np.isfinite(r_dev[rows]))
 
 
-def test_single_launch_padded_rows_untouched():
+@pytest.mark.parametrize("cfg", [None] + SINGLE_CFGS, ids=lambda c: "auto" if c is None else
+                         f"{c[0]}-{c[1]}w-{c[2]}kg-s{c[3]}")
+def test_single_launch_padded_rows_untouched(monkeypatch, cfg):
+    """Rows past T (sentinel-filled, NaN in x) stay untouched in every tile configuration: T =
+    300 leaves a ragged last tile row for 256- and 192-row tiles, whose residual and output
+    stores are bounded by the tile row's valid rows."""
     T = 300
-    d = synth.make_custom(T, 512, 384, seed=5)
+    H = 384 if cfg is None else 768
+    if cfg is not None:
+        _force_single(monkeypatch, *cfg)
+    d = synth.make_custom(T, 512, H, seed=5)
     dev = Device(d, extra_rows=212, pad_x_nan=True)
     dev.reset(sentinel=12345.0)
     r_dev, out_bits = dev.run("single")
